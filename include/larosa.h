@@ -1,0 +1,187 @@
+/*
+ * larosa.h — C ABI of the rotated Top-K sparse linear library (liblarosa.so)
+ *
+ * The method (LaRoSA; "La RoSA: Enhancing LLM Efficiency via Layerwise
+ * Rotated Sparse Activation", abstract on the PMLR 267 proceedings page, and
+ * the LaRoSA summary page, 方法详解 · 技术框架 "technical framework"):
+ * every linear layer's input activation x is rotated by a layerwise
+ * orthogonal matrix Q, then only the K entries of largest magnitude of the
+ * rotated vector are kept and the rest set to zero. Because Q·Qᵀ = I, the
+ * product (x·Q)·(Qᵀ·W) equals x·W; with Qᵀ folded offline into the weight
+ * (W' = Qᵀ·W) the online work is
+ *
+ *     x_rot = x·Q                       (rotate)
+ *     S     = Top-K of |x_rot|          (select; per token)
+ *     y     = Σ_{i∈S} x_rot[i]·W'[i,:]  (gather: read only the K rows of W')
+ *
+ * Conventions for every call below
+ *  - Matrices are row-major. W and W' are [d_in, d_out] (the x·W form), so
+ *    one input channel owns one contiguous row.
+ *  - The rotation argument is always the *prepared* rotation Qt = Qᵀ, packed
+ *    block-diagonal: Qt is [d, q_block] row-major, rows c·q_block … (c+1)·
+ *    q_block−1 holding block c transposed (q_block == d: one dense block).
+ *    larosa_prepare_rotation writes it from Q.
+ *  - All tensor pointers are device pointers owned by the caller. The library
+ *    allocates no memory and never synchronises the host; each call only
+ *    enqueues kernels on `stream` (a hipStream_t; NULL = default stream).
+ *  - Every call checks its arguments on the host before any HIP call; on an
+ *    error it enqueues nothing and returns the status, leaving outputs as
+ *    they were. Nothing is thrown across the ABI.
+ *  - Device pointers must be 16-byte aligned. Rows must be whole 16-byte
+ *    units: d_out and q_block multiples of 8 (bf16) or 4 (fp32); d a
+ *    multiple of 4. Sizes: 1 <= d <= 32768, 1 <= k <= d, B <= 64; B == 0 is
+ *    an empty batch and returns LAROSA_OK without work.
+ *  - Workspace: calls that take `ws` need at least larosa_workspace_bytes(…)
+ *    bytes. The workspace must be zero-filled once before first use
+ *    (larosa_workspace_init does it on the device); every call leaves it
+ *    ready for the next call on the same stream. Calls that share one
+ *    workspace must not run concurrently.
+ */
+#ifndef LAROSA_H
+#define LAROSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LAROSA_ABI_VERSION 1
+
+typedef void *larosa_stream_t; /* hipStream_t */
+
+/* Element types. */
+enum { LAROSA_F32 = 0, LAROSA_BF16 = 1 };
+
+/* Status codes. */
+enum {
+  LAROSA_OK = 0,
+  LAROSA_ERR_INVALID_ARG = 1, /* null pointer, B < 0, k outside [1, d] … */
+  LAROSA_ERR_SHAPE = 2,       /* q_block does not divide d, d too large … */
+  LAROSA_ERR_ALIGNMENT = 3,   /* pointer not 16-byte aligned, ragged rows */
+  LAROSA_ERR_DTYPE = 4,       /* unsupported element type or combination */
+  LAROSA_ERR_WORKSPACE = 5,   /* workspace missing or too small */
+  LAROSA_ERR_NO_DEVICE = 6,   /* no HIP device visible */
+  LAROSA_ERR_LAUNCH = 7       /* a kernel launch failed */
+};
+
+/* Execution modes of larosa_layer_forward. */
+enum { LAROSA_UNFUSED = 0, LAROSA_FUSED = 1 };
+
+/* LAROSA_ABI_VERSION of the loaded library. */
+int larosa_abi_version(void);
+
+/* A static, human-readable name for a status code (never NULL). */
+const char *larosa_status_string(int status);
+
+/* Bytes of workspace needed by larosa_layer_forward with these sizes in the
+ * given mode. It also covers larosa_topk_select, larosa_sparse_gemv and
+ * larosa_dense_gemv on the same (B, d_in, d_out, k). Returns 0 for invalid
+ * sizes. */
+size_t larosa_workspace_bytes(int64_t B, int64_t d_in, int64_t d_out,
+                              int64_t k, int mode);
+
+/* Zero-fills `bytes` of workspace with a device kernel (no memset node). */
+int larosa_workspace_init(void *ws, size_t bytes, larosa_stream_t stream);
+
+/* Prepared rotation: Qt = Qᵀ block by block. Q is packed [d/q_block,
+ * q_block, q_block] (block c of the block-diagonal rotation, row-major);
+ * Qt is written as [d, q_block] with Qt[c·q_block + j][i] = Q[c][i][j].
+ * Exact (a transpose). Q and Qt must not overlap. dtype: F32 or BF16.
+ * The rotation is the method's per-layer orthogonal matrix (LaRoSA summary
+ * page, 方法详解 · 关键设计: random or learned). Offline; not on the hot path. */
+int larosa_prepare_rotation(const void *Q, void *Qt, int64_t d,
+                            int64_t q_block, int dtype,
+                            larosa_stream_t stream);
+
+/* Folded weight W' = Qᵀ·W (= Qt·W), formed in fp32 and rounded to nearest
+ * even in w_dtype. Qt: prepared rotation [d_in, q_block]; W, W_folded:
+ * [d_in, d_out]; all three in w_dtype (F32 or BF16). W_folded must not
+ * overlap W or Qt. Offline; not on the hot path. Folding follows from the
+ * orthogonality the LaRoSA abstract names: (x·Q)·(Qᵀ·W) = x·W. */
+int larosa_fold_weights(const void *Qt, int64_t q_block, const void *W,
+                        void *W_folded, int64_t d_in, int64_t d_out,
+                        int w_dtype, larosa_stream_t stream);
+
+/* Rotation, stage 1 of the method (LaRoSA summary page, 技术框架):
+ * x_rot[b, :] = x[b, :]·Q for b < B, accumulated in fp32.
+ * x: [B, d] in x_dtype (F32 or BF16); Qt: prepared rotation [d, q_block] in
+ * q_dtype (F32 or BF16); x_rot: [B, d] fp32. */
+int larosa_rotate(const void *x, int x_dtype, const void *Qt, int64_t q_block,
+                  int q_dtype, float *x_rot, int64_t B, int64_t d,
+                  larosa_stream_t stream);
+
+/* Top-K selection, stage 2 of the method (LaRoSA summary page, 技术框架;
+ * the abstract's fixed-K "consistent model-level sparsity"): for each token
+ * b, the k entries of x_rot[b, :] with the largest magnitude. Magnitude is
+ * the fp32 value with the sign dropped (−0 equals +0); among equal
+ * magnitudes the lower index is kept. NaN inputs give an unspecified but
+ * in-bounds selection.
+ *   idx  [B, k] int32: kept indices of each token, ascending (required)
+ *   val  [B, k] fp32:  x_rot at those indices, unscaled (required)
+ *   xs   [B, d] fp32:  x_rot with unkept entries set to 0 (may be NULL
+ *                      when B == 1 and no union is asked for)
+ * Row union (B > 1, optional: pass union_idx == NULL to skip):
+ *   union_idx   [d] int32: ascending union of the tokens' kept indices
+ *   union_count [1] int32: its length |U| (written on the device)
+ *   union_coef  [d, B] fp32: union_coef[j·B + b] = xs[b, union_idx[j]]
+ * When the union is asked for, xs is required. ws: workspace. */
+int larosa_topk_select(const float *x_rot, int64_t B, int64_t d, int64_t k,
+                       int32_t *idx, float *val, float *xs, int32_t *union_idx,
+                       int32_t *union_count, float *union_coef, void *ws,
+                       size_t ws_bytes, larosa_stream_t stream);
+
+/* Gather product (the saving the LaRoSA abstract names: computation and
+ * memory transfers of zeroed channels are skipped):
+ *   y[b, :] = Σ_{j < n} coef[j·B + b] · W'[rows[j], :]
+ * rows: [max_rows] int32 row indices (entries outside [0, d_in) contribute
+ * nothing); n_rows: device int32 holding n (clamped to max_rows), or NULL
+ * for n = max_rows; coef: [max_rows, B] fp32; W_folded: [d_in, d_out] in
+ * w_dtype; y: [B, d_out] in y_dtype, fp32 accumulation. Only the n listed
+ * rows of W' are read. For B == 1 pass (idx, NULL, k, val) from
+ * larosa_topk_select; for B > 1 pass (union_idx, union_count, d_in,
+ * union_coef). */
+int larosa_sparse_gemv(const int32_t *rows, const int32_t *n_rows,
+                       int64_t max_rows, const float *coef,
+                       const void *W_folded, int w_dtype, void *y,
+                       int y_dtype, int64_t B, int64_t d_in, int64_t d_out,
+                       void *ws, size_t ws_bytes, larosa_stream_t stream);
+
+/* One rotated sparse linear: rotate → select → (row union when B > 1) →
+ * gather, for every projection that shares the input x. W_folded is the
+ * column concatenation of those projections' folded weights
+ * ([W'_q | W'_k | W'_v] or [W'_gate | W'_up]), [d_in, d_out] in w_dtype.
+ * x: [B, d_in] and y: [B, d_out] in act_dtype; Qt: prepared rotation
+ * [d_in, q_block] in w_dtype. idx_out [B, k] and xrot_out [B, d_in] (fp32)
+ * are optional copies of the selection and the rotated input (NULL skips
+ * them). mode: LAROSA_UNFUSED (one kernel per step) or LAROSA_FUSED (one
+ * persistent launch for B == 1; other B fall back to the unfused steps). */
+int larosa_layer_forward(const void *x, int act_dtype, const void *Qt,
+                         int64_t q_block, const void *W_folded, int w_dtype,
+                         int64_t B, int64_t d_in, int64_t d_out, int64_t k,
+                         void *y, int32_t *idx_out, float *xrot_out, int mode,
+                         void *ws, size_t ws_bytes, larosa_stream_t stream);
+
+/* Dense reference product y = x·W over every row of W, with the same
+ * streaming and fp32 accumulation as larosa_sparse_gemv. x: [B, d_in] and
+ * y: [B, d_out] in act_dtype; W: [d_in, d_out] in w_dtype. The baseline that
+ * the sparse product is compared against; not a step of the method. */
+int larosa_dense_gemv(const void *x, int act_dtype, const void *W,
+                      int w_dtype, void *y, int64_t B, int64_t d_in,
+                      int64_t d_out, void *ws, size_t ws_bytes,
+                      larosa_stream_t stream);
+
+/* SwiGLU between the two linears of an MLP (LLaMA-style; the method
+ * sparsifies the input of the down projection, which is this output):
+ *   h[b, i] = SiLU(gu[b, i]) · gu[b, f + i],  SiLU(z) = z / (1 + e^−z)
+ * gu: [B, 2f] ([gate | up]); h: [B, f]; both in dtype (F32 or BF16);
+ * arithmetic in fp32, rounded to nearest even. f a multiple of 8. */
+int larosa_swiglu(const void *gu, void *h, int64_t B, int64_t f, int dtype,
+                  larosa_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LAROSA_H */

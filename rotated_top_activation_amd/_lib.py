@@ -1,0 +1,177 @@
+"""ctypes binding of liblarosa.so — argument marshalling only.
+
+Each ``larosa_*`` function here has the name and argument order of the C
+entry point in ``include/larosa.h``. Tensor arguments are torch tensors on
+the GPU (their ``data_ptr()`` is passed); dtypes are taken from the tensors;
+``stream`` defaults to torch's current stream. A non-zero status raises
+``LarosaError``. No step of the computation happens here.
+
+The library must be built (``python -m rotated_top_activation_amd.build``);
+importing a function does not load it, calling one does, and a missing
+library raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblarosa.so")
+
+F32, BF16 = 0, 1
+UNFUSED, FUSED = 0, 1
+ABI_VERSION = 1
+
+_c_i64 = ctypes.c_int64
+_c_int = ctypes.c_int
+_c_vp = ctypes.c_void_p
+_c_sz = ctypes.c_size_t
+
+# (restype, argtypes) of every exported entry point.
+SIGNATURES = {
+    "larosa_abi_version": (_c_int, []),
+    "larosa_status_string": (ctypes.c_char_p, [_c_int]),
+    "larosa_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i64, _c_int]),
+    "larosa_workspace_init": (_c_int, [_c_vp, _c_sz, _c_vp]),
+    "larosa_prepare_rotation": (_c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_vp]),
+    "larosa_fold_weights": (_c_int, [_c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_vp]),
+    "larosa_rotate": (_c_int, [_c_vp, _c_int, _c_vp, _c_i64, _c_int, _c_vp, _c_i64, _c_i64, _c_vp]),
+    "larosa_topk_select": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp,
+                                    _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
+    "larosa_sparse_gemv": (_c_int, [_c_vp, _c_vp, _c_i64, _c_vp, _c_vp, _c_int, _c_vp, _c_int,
+                                    _c_i64, _c_i64, _c_i64, _c_vp, _c_sz, _c_vp]),
+    "larosa_layer_forward": (_c_int, [_c_vp, _c_int, _c_vp, _c_i64, _c_vp, _c_int, _c_i64,
+                                      _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_int,
+                                      _c_vp, _c_sz, _c_vp]),
+    "larosa_dense_gemv": (_c_int, [_c_vp, _c_int, _c_vp, _c_int, _c_vp, _c_i64, _c_i64, _c_i64,
+                                   _c_vp, _c_sz, _c_vp]),
+    "larosa_swiglu": (_c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_vp]),
+}
+
+_lib = None
+
+
+class LarosaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)} (status {status})")
+
+
+def load() -> ctypes.CDLL:
+    """Load liblarosa.so once and declare its entry points."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run "
+                               "`python -m rotated_top_activation_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        if lib.larosa_abi_version() != ABI_VERSION:
+            raise RuntimeError("liblarosa.so ABI version mismatch")
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load().larosa_status_string(status).decode()
+
+
+def _check(name: str, status: int) -> None:
+    if status != 0:
+        raise LarosaError(name, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dt(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream)
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+# ----------------------------------------------------------------------------
+
+def larosa_abi_version() -> int:
+    return load().larosa_abi_version()
+
+
+def larosa_workspace_bytes(B: int, d_in: int, d_out: int, k: int, mode: int = UNFUSED) -> int:
+    return load().larosa_workspace_bytes(B, d_in, d_out, k, mode)
+
+
+def larosa_workspace_init(ws, stream=None) -> None:
+    _check("larosa_workspace_init",
+           load().larosa_workspace_init(_ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def larosa_prepare_rotation(Q, Qt, d: int, q_block: int, stream=None) -> None:
+    _check("larosa_prepare_rotation",
+           load().larosa_prepare_rotation(_ptr(Q), _ptr(Qt), d, q_block, _dt(Q), _stream(stream)))
+
+
+def larosa_fold_weights(Qt, q_block: int, W, W_folded, d_in: int, d_out: int,
+                        stream=None) -> None:
+    _check("larosa_fold_weights",
+           load().larosa_fold_weights(_ptr(Qt), q_block, _ptr(W), _ptr(W_folded), d_in, d_out,
+                                      _dt(W), _stream(stream)))
+
+
+def larosa_rotate(x, Qt, q_block: int, x_rot, B: int, d: int, stream=None) -> None:
+    _check("larosa_rotate",
+           load().larosa_rotate(_ptr(x), _dt(x), _ptr(Qt), q_block, _dt(Qt), _ptr(x_rot), B, d,
+                                _stream(stream)))
+
+
+def larosa_topk_select(x_rot, B: int, d: int, k: int, idx, val, xs=None, union_idx=None,
+                       union_count=None, union_coef=None, ws=None, stream=None) -> None:
+    _check("larosa_topk_select",
+           load().larosa_topk_select(_ptr(x_rot), B, d, k, _ptr(idx), _ptr(val), _ptr(xs),
+                                     _ptr(union_idx), _ptr(union_count), _ptr(union_coef),
+                                     _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def larosa_sparse_gemv(rows, n_rows, max_rows: int, coef, W_folded, y, B: int, d_in: int,
+                       d_out: int, ws=None, stream=None) -> None:
+    _check("larosa_sparse_gemv",
+           load().larosa_sparse_gemv(_ptr(rows), _ptr(n_rows), max_rows, _ptr(coef),
+                                     _ptr(W_folded), _dt(W_folded), _ptr(y), _dt(y), B, d_in,
+                                     d_out, _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def larosa_layer_forward(x, Qt, q_block: int, W_folded, B: int, d_in: int, d_out: int, k: int,
+                         y, idx_out=None, xrot_out=None, mode: int = UNFUSED, ws=None,
+                         stream=None) -> None:
+    _check("larosa_layer_forward",
+           load().larosa_layer_forward(_ptr(x), _dt(x), _ptr(Qt), q_block, _ptr(W_folded),
+                                       _dt(W_folded), B, d_in, d_out, k, _ptr(y), _ptr(idx_out),
+                                       _ptr(xrot_out), mode, _ptr(ws), _nbytes(ws),
+                                       _stream(stream)))
+
+
+def larosa_dense_gemv(x, W, y, B: int, d_in: int, d_out: int, ws=None, stream=None) -> None:
+    _check("larosa_dense_gemv",
+           load().larosa_dense_gemv(_ptr(x), _dt(x), _ptr(W), _dt(W), _ptr(y), B, d_in, d_out,
+                                    _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def larosa_swiglu(gu, h, B: int, f: int, stream=None) -> None:
+    _check("larosa_swiglu",
+           load().larosa_swiglu(_ptr(gu), _ptr(h), B, f, _dt(gu), _stream(stream)))

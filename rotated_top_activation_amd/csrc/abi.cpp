@@ -1,0 +1,350 @@
+// C ABI of liblarosa: argument checks on the host, workspace carving, and
+// the step sequence of each call. Every argument is checked before any HIP
+// call, so an invalid call enqueues nothing and leaves outputs untouched.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+
+#include "../../include/larosa.h"
+#include "launch.hpp"
+
+using namespace larosa;
+
+namespace {
+
+constexpr int64_t kMaxD = 32768;  // select keeps a token's channels in one workgroup
+constexpr int64_t kMaxB = 64;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool dtype_ok(int dt) { return dt == LAROSA_F32 || dt == LAROSA_BF16; }
+int vec_of(int dt) { return dt == LAROSA_F32 ? 4 : 8; }
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+int device_status() {
+  static std::once_flag once;
+  static int status = LAROSA_OK;
+  std::call_once(once, [] {
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) status = LAROSA_ERR_NO_DEVICE;
+  });
+  return status;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? LAROSA_OK : LAROSA_ERR_LAUNCH; }
+
+hipStream_t stream_of(larosa_stream_t s) { return static_cast<hipStream_t>(s); }
+
+// Workspace carving for larosa_layer_forward and the standalone calls.
+struct Layout {
+  size_t x_rot = 0, idx = 0, val = 0, xs = 0, mask = 0, u_idx = 0, u_cnt = 0,
+         u_coef = 0, gather = 0, total = 0;
+};
+
+Layout layout_for(int64_t B, int64_t d_in, int64_t d_out, int64_t k, int w_dt) {
+  Layout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  L.x_rot = take(static_cast<size_t>(B) * d_in * 4);
+  L.idx = take(static_cast<size_t>(B) * k * 4);
+  L.val = take(static_cast<size_t>(B) * k * 4);
+  L.xs = take(static_cast<size_t>(B) * d_in * 4);
+  L.mask = take(static_cast<size_t>(B) * mask_words(static_cast<int>(d_in)) * 4);
+  L.u_idx = take(static_cast<size_t>(d_in) * 4);
+  L.u_cnt = take(4);
+  L.u_coef = take(static_cast<size_t>(d_in) * B * 4);
+  // The gather's reduction area covers both the sparse call (max_rows =
+  // min(d_in, B·k)) and the dense call (max_rows = d_in): the dense plan has
+  // at least as many splits.
+  const GatherPlan p = plan_gather(static_cast<int>(B), d_in, d_out, w_dt);
+  L.gather = take(gather_ws_bytes(p, static_cast<int>(B), d_out));
+  L.total = off;
+  return L;
+}
+
+size_t gather_need(int64_t B, int64_t max_rows, int64_t d_out, int w_dt) {
+  return gather_ws_bytes(plan_gather(static_cast<int>(B), max_rows, d_out, w_dt),
+                         static_cast<int>(B), d_out);
+}
+
+int check_sizes(int64_t B, int64_t d, int64_t k) {
+  if (B < 0 || B > kMaxB) return LAROSA_ERR_INVALID_ARG;
+  if (d < 1 || d > kMaxD) return LAROSA_ERR_SHAPE;
+  if (d % 4) return LAROSA_ERR_ALIGNMENT;
+  if (k < 1 || k > d) return LAROSA_ERR_INVALID_ARG;
+  return LAROSA_OK;
+}
+
+int check_rotation(int64_t d, int64_t qb, int q_dt) {
+  if (qb < 1 || qb > d || d % qb) return LAROSA_ERR_SHAPE;
+  if (qb % vec_of(q_dt)) return LAROSA_ERR_ALIGNMENT;
+  return LAROSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int larosa_abi_version(void) { return LAROSA_ABI_VERSION; }
+
+const char *larosa_status_string(int status) {
+  switch (status) {
+    case LAROSA_OK: return "ok";
+    case LAROSA_ERR_INVALID_ARG: return "invalid argument";
+    case LAROSA_ERR_SHAPE: return "unsupported shape";
+    case LAROSA_ERR_ALIGNMENT: return "misaligned pointer or row length";
+    case LAROSA_ERR_DTYPE: return "unsupported element type";
+    case LAROSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case LAROSA_ERR_NO_DEVICE: return "no HIP device";
+    case LAROSA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t larosa_workspace_bytes(int64_t B, int64_t d_in, int64_t d_out, int64_t k, int mode) {
+  if (check_sizes(B < 1 ? 1 : B, d_in, k) != LAROSA_OK || d_out < 1) return 0;
+  if (mode != LAROSA_UNFUSED && mode != LAROSA_FUSED) return 0;
+  // Sized for bf16 weights; fp32 weights have twice the column tiles but the
+  // same number of splits at most, and fit in the same bytes or fewer.
+  const Layout a = layout_for(B < 1 ? 1 : B, d_in, d_out, k, LAROSA_BF16);
+  const Layout b = layout_for(B < 1 ? 1 : B, d_in, d_out, k, LAROSA_F32);
+  return a.total > b.total ? a.total : b.total;
+}
+
+int larosa_workspace_init(void *ws, size_t bytes, larosa_stream_t stream) {
+  if (!ws && bytes) return LAROSA_ERR_INVALID_ARG;
+  if (bytes == 0) return LAROSA_OK;
+  if (!aligned16(ws)) return LAROSA_ERR_ALIGNMENT;
+  if (int st = device_status()) return st;
+  return launched(launch_fill_zero(ws, bytes, stream_of(stream)));
+}
+
+int larosa_prepare_rotation(const void *Q, void *Qt, int64_t d, int64_t q_block, int dtype,
+                            larosa_stream_t stream) {
+  if (!Q || !Qt) return LAROSA_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype)) return LAROSA_ERR_DTYPE;
+  if (d < 1) return LAROSA_ERR_SHAPE;
+  if (int st = check_rotation(d, q_block, dtype)) return st;
+  if (!aligned16(Q) || !aligned16(Qt)) return LAROSA_ERR_ALIGNMENT;
+  const size_t bytes = static_cast<size_t>(d) * q_block * dt_size(dtype);
+  const char *a = static_cast<const char *>(Q);
+  const char *b = static_cast<const char *>(Qt);
+  if (a < b + bytes && b < a + bytes) return LAROSA_ERR_INVALID_ARG;
+  if (int st = device_status()) return st;
+  return launched(launch_transpose_blocks(Q, Qt, d, q_block, dtype, stream_of(stream)));
+}
+
+int larosa_fold_weights(const void *Qt, int64_t q_block, const void *W, void *W_folded,
+                        int64_t d_in, int64_t d_out, int w_dtype, larosa_stream_t stream) {
+  if (!Qt || !W || !W_folded) return LAROSA_ERR_INVALID_ARG;
+  if (!dtype_ok(w_dtype)) return LAROSA_ERR_DTYPE;
+  if (d_in < 1 || d_out < 1) return LAROSA_ERR_SHAPE;
+  if (int st = check_rotation(d_in, q_block, w_dtype)) return st;
+  if (d_out % vec_of(w_dtype)) return LAROSA_ERR_ALIGNMENT;
+  if (!aligned16(Qt) || !aligned16(W) || !aligned16(W_folded)) return LAROSA_ERR_ALIGNMENT;
+  const size_t wb = static_cast<size_t>(d_in) * d_out * dt_size(w_dtype);
+  const size_t qbts = static_cast<size_t>(d_in) * q_block * dt_size(w_dtype);
+  const char *f = static_cast<const char *>(W_folded);
+  const char *w = static_cast<const char *>(W);
+  const char *q = static_cast<const char *>(Qt);
+  if ((f < w + wb && w < f + wb) || (f < q + qbts && q < f + wb)) return LAROSA_ERR_INVALID_ARG;
+  if (int st = device_status()) return st;
+  return launched(launch_fold(Qt, q_block, W, W_folded, d_in, d_out, w_dtype, stream_of(stream)));
+}
+
+int larosa_rotate(const void *x, int x_dtype, const void *Qt, int64_t q_block, int q_dtype,
+                  float *x_rot, int64_t B, int64_t d, larosa_stream_t stream) {
+  if (!dtype_ok(x_dtype) || !dtype_ok(q_dtype)) return LAROSA_ERR_DTYPE;
+  if (int st = check_sizes(B, d, 1)) return st;
+  if (B == 0) return LAROSA_OK;
+  if (!x || !Qt || !x_rot) return LAROSA_ERR_INVALID_ARG;
+  if (int st = check_rotation(d, q_block, q_dtype)) return st;
+  if (d % 8 && x_dtype == LAROSA_BF16) return LAROSA_ERR_ALIGNMENT;
+  if (!aligned16(x) || !aligned16(Qt) || !aligned16(x_rot)) return LAROSA_ERR_ALIGNMENT;
+  if (int st = device_status()) return st;
+  return launched(launch_rotate(x, x_dtype, Qt, q_dtype, x_rot, static_cast<int>(B),
+                                static_cast<int>(d), static_cast<int>(q_block),
+                                stream_of(stream)));
+}
+
+int larosa_topk_select(const float *x_rot, int64_t B, int64_t d, int64_t k, int32_t *idx,
+                       float *val, float *xs, int32_t *union_idx, int32_t *union_count,
+                       float *union_coef, void *ws, size_t ws_bytes, larosa_stream_t stream) {
+  if (int st = check_sizes(B, d, k)) return st;
+  if (B == 0) return LAROSA_OK;
+  if (!x_rot || !idx || !val) return LAROSA_ERR_INVALID_ARG;
+  const bool want_union = union_idx != nullptr;
+  if (want_union && (!union_count || !union_coef || !xs)) return LAROSA_ERR_INVALID_ARG;
+  if (!aligned16(x_rot)) return LAROSA_ERR_ALIGNMENT;
+  uint32_t *mask = nullptr;
+  if (want_union) {
+    const size_t need = static_cast<size_t>(B) * mask_words(static_cast<int>(d)) * 4;
+    if (!ws || ws_bytes < need) return LAROSA_ERR_WORKSPACE;
+    mask = static_cast<uint32_t *>(ws);
+  }
+  if (int st = device_status()) return st;
+  hipStream_t s = stream_of(stream);
+  hipError_t e = launch_select(x_rot, static_cast<int>(B), static_cast<int>(d),
+                               static_cast<int>(k), idx, val, xs, mask, s);
+  if (e == hipSuccess && want_union)
+    e = launch_union(mask, xs, static_cast<int>(B), static_cast<int>(d), union_idx,
+                     union_count, union_coef, s);
+  return launched(e);
+}
+
+int larosa_sparse_gemv(const int32_t *rows, const int32_t *n_rows, int64_t max_rows,
+                       const float *coef, const void *W_folded, int w_dtype, void *y,
+                       int y_dtype, int64_t B, int64_t d_in, int64_t d_out, void *ws,
+                       size_t ws_bytes, larosa_stream_t stream) {
+  if (!dtype_ok(w_dtype) || !dtype_ok(y_dtype)) return LAROSA_ERR_DTYPE;
+  if (w_dtype == LAROSA_F32 && y_dtype == LAROSA_BF16) return LAROSA_ERR_DTYPE;
+  if (B < 0 || B > kMaxB) return LAROSA_ERR_INVALID_ARG;
+  if (d_in < 1 || d_out < 1) return LAROSA_ERR_SHAPE;
+  if (max_rows < 0) return LAROSA_ERR_INVALID_ARG;
+  if (B == 0) return LAROSA_OK;
+  if (!rows || !coef || !W_folded || !y) return LAROSA_ERR_INVALID_ARG;
+  if (B > 8) return LAROSA_ERR_SHAPE;
+  if (d_out % vec_of(w_dtype)) return LAROSA_ERR_ALIGNMENT;
+  if (!aligned16(W_folded) || !aligned16(y)) return LAROSA_ERR_ALIGNMENT;
+  const int64_t mr = max_rows < 1 ? 1 : max_rows;
+  const size_t need = gather_need(B, mr, d_out, w_dtype);
+  if (need && (!ws || ws_bytes < need)) return LAROSA_ERR_WORKSPACE;
+  if (need && !aligned16(ws)) return LAROSA_ERR_ALIGNMENT;
+  if (int st = device_status()) return st;
+  GatherArgs a;
+  a.rows = rows;
+  a.n_rows = n_rows;
+  a.max_rows = max_rows;
+  a.coef = coef;
+  a.coef_mode = kCoefPacked;
+  a.w = W_folded;
+  a.w_dt = w_dtype;
+  a.d_in = d_in;
+  a.d_out = d_out;
+  a.y = y;
+  a.y_dt = y_dtype;
+  a.B = static_cast<int>(B);
+  a.ws = ws;
+  // max_rows == 0 still runs, so y is written (as zeros).
+  return launched(launch_gather(a, stream_of(stream)));
+}
+
+int larosa_dense_gemv(const void *x, int act_dtype, const void *W, int w_dtype, void *y,
+                      int64_t B, int64_t d_in, int64_t d_out, void *ws, size_t ws_bytes,
+                      larosa_stream_t stream) {
+  if (!dtype_ok(act_dtype) || !dtype_ok(w_dtype)) return LAROSA_ERR_DTYPE;
+  if (act_dtype != w_dtype) return LAROSA_ERR_DTYPE;
+  if (B < 0 || B > kMaxB) return LAROSA_ERR_INVALID_ARG;
+  if (d_in < 1 || d_out < 1) return LAROSA_ERR_SHAPE;
+  if (B == 0) return LAROSA_OK;
+  if (!x || !W || !y) return LAROSA_ERR_INVALID_ARG;
+  if (B > 8) return LAROSA_ERR_SHAPE;
+  if (d_out % vec_of(w_dtype)) return LAROSA_ERR_ALIGNMENT;
+  if (!aligned16(x) || !aligned16(W) || !aligned16(y)) return LAROSA_ERR_ALIGNMENT;
+  const size_t need = gather_need(B, d_in, d_out, w_dtype);
+  if (need && (!ws || ws_bytes < need)) return LAROSA_ERR_WORKSPACE;
+  if (need && !aligned16(ws)) return LAROSA_ERR_ALIGNMENT;
+  if (int st = device_status()) return st;
+  GatherArgs a;
+  a.rows = nullptr;
+  a.n_rows = nullptr;
+  a.max_rows = d_in;
+  a.coef = x;
+  a.coef_mode = act_dtype == LAROSA_F32 ? kCoefActF32 : kCoefActBF16;
+  a.w = W;
+  a.w_dt = w_dtype;
+  a.d_in = d_in;
+  a.d_out = d_out;
+  a.y = y;
+  a.y_dt = act_dtype;
+  a.B = static_cast<int>(B);
+  a.ws = ws;
+  return launched(launch_gather(a, stream_of(stream)));
+}
+
+int larosa_layer_forward(const void *x, int act_dtype, const void *Qt, int64_t q_block,
+                         const void *W_folded, int w_dtype, int64_t B, int64_t d_in,
+                         int64_t d_out, int64_t k, void *y, int32_t *idx_out, float *xrot_out,
+                         int mode, void *ws, size_t ws_bytes, larosa_stream_t stream) {
+  if (!dtype_ok(act_dtype) || !dtype_ok(w_dtype)) return LAROSA_ERR_DTYPE;
+  if (w_dtype == LAROSA_F32 && act_dtype == LAROSA_BF16) return LAROSA_ERR_DTYPE;
+  if (int st = check_sizes(B, d_in, k)) return st;
+  if (mode != LAROSA_UNFUSED && mode != LAROSA_FUSED) return LAROSA_ERR_INVALID_ARG;
+  if (d_out < 1) return LAROSA_ERR_SHAPE;
+  if (B == 0) return LAROSA_OK;
+  if (!x || !Qt || !W_folded || !y) return LAROSA_ERR_INVALID_ARG;
+  if (B > 8) return LAROSA_ERR_SHAPE;
+  if (int st = check_rotation(d_in, q_block, w_dtype)) return st;
+  if (d_in % vec_of(act_dtype) || d_out % vec_of(w_dtype)) return LAROSA_ERR_ALIGNMENT;
+  if (!aligned16(x) || !aligned16(Qt) || !aligned16(W_folded) || !aligned16(y))
+    return LAROSA_ERR_ALIGNMENT;
+  if ((xrot_out && !aligned16(xrot_out)) || !aligned16(ws)) return LAROSA_ERR_ALIGNMENT;
+  const Layout L = layout_for(B, d_in, d_out, k, w_dtype);
+  if (!ws || ws_bytes < L.total) return LAROSA_ERR_WORKSPACE;
+  if (int st = device_status()) return st;
+
+  hipStream_t s = stream_of(stream);
+  char *base = static_cast<char *>(ws);
+  float *x_rot = xrot_out ? xrot_out : reinterpret_cast<float *>(base + L.x_rot);
+  int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(base + L.idx);
+  float *val = reinterpret_cast<float *>(base + L.val);
+
+  hipError_t e = launch_rotate(x, act_dtype, Qt, w_dtype, x_rot, static_cast<int>(B),
+                               static_cast<int>(d_in), static_cast<int>(q_block), s);
+  if (e != hipSuccess) return LAROSA_ERR_LAUNCH;
+
+  GatherArgs a;
+  a.coef_mode = kCoefPacked;
+  a.w = W_folded;
+  a.w_dt = w_dtype;
+  a.d_in = d_in;
+  a.d_out = d_out;
+  a.y = y;
+  a.y_dt = act_dtype;
+  a.B = static_cast<int>(B);
+  a.ws = base + L.gather;
+  if (B == 1) {
+    e = launch_select(x_rot, 1, static_cast<int>(d_in), static_cast<int>(k), idx, val,
+                      nullptr, nullptr, s);
+    if (e != hipSuccess) return LAROSA_ERR_LAUNCH;
+    a.rows = idx;
+    a.n_rows = nullptr;
+    a.max_rows = k;
+    a.coef = val;
+  } else {
+    float *xs = reinterpret_cast<float *>(base + L.xs);
+    uint32_t *mask = reinterpret_cast<uint32_t *>(base + L.mask);
+    int32_t *u_idx = reinterpret_cast<int32_t *>(base + L.u_idx);
+    int32_t *u_cnt = reinterpret_cast<int32_t *>(base + L.u_cnt);
+    float *u_coef = reinterpret_cast<float *>(base + L.u_coef);
+    e = launch_select(x_rot, static_cast<int>(B), static_cast<int>(d_in), static_cast<int>(k),
+                      idx, val, xs, mask, s);
+    if (e == hipSuccess)
+      e = launch_union(mask, xs, static_cast<int>(B), static_cast<int>(d_in), u_idx, u_cnt,
+                       u_coef, s);
+    if (e != hipSuccess) return LAROSA_ERR_LAUNCH;
+    a.rows = u_idx;
+    a.n_rows = u_cnt;
+    const int64_t bk = B * k;
+    a.max_rows = bk < d_in ? bk : d_in;
+    a.coef = u_coef;
+  }
+  return launched(launch_gather(a, s));
+}
+
+int larosa_swiglu(const void *gu, void *h, int64_t B, int64_t f, int dtype,
+                  larosa_stream_t stream) {
+  if (!dtype_ok(dtype)) return LAROSA_ERR_DTYPE;
+  if (B < 0 || B > kMaxB || f < 1) return LAROSA_ERR_INVALID_ARG;
+  if (B == 0) return LAROSA_OK;
+  if (!gu || !h) return LAROSA_ERR_INVALID_ARG;
+  if (f % 8) return LAROSA_ERR_ALIGNMENT;
+  if (!aligned16(gu) || !aligned16(h)) return LAROSA_ERR_ALIGNMENT;
+  if (int st = device_status()) return st;
+  return launched(launch_swiglu(gu, h, B, f, dtype, stream_of(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,245 @@
+// Gather-rows product: y[b, :] = Σ_j coef(j, b) · W[row(j), :].
+//
+// This is the step where the method saves memory traffic: only the weight
+// rows of kept input channels are read (LaRoSA abstract, PMLR 267 page:
+// activation sparsity cuts computation and memory transfers). W is
+// [d_in, d_out] row-major, so each kept channel is one contiguous row.
+//
+// Layout of the work (vector path, B <= 8):
+//   * a workgroup owns one column tile of 64·V columns (V = 8 bf16 or 4 fp32
+//     per 16-byte load) and a contiguous range of the row list;
+//   * its waves take interleaved groups of kRows rows; every lane issues
+//     one 16-byte load per row, so a wave streams 1 KB of each row and keeps
+//     kRows loads in flight;
+//   * row index and coefficients are wave-uniform (scalar loads);
+//   * the waves' fp32 sums are combined in LDS, then either stored (one
+//     split) or written as a partial sum; the last workgroup of a tile to
+//     finish adds the partials in split order, so the result does not depend
+//     on arrival order and needs no float atomics.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace larosa {
+namespace {
+
+constexpr int kRows = 8;  // rows per wave group (loads in flight per lane)
+
+// Waves per workgroup: wide for few tokens, narrower as the per-lane
+// accumulators (B·V floats) and the LDS reduction buffer grow with B.
+constexpr int waves_for(int B) { return B <= 2 ? 8 : (B <= 4 ? 4 : 2); }
+template <int B> struct WavesFor { static constexpr int value = waves_for(B); };
+
+template <int B, typename WT, typename OT, int CMODE>
+__global__ __launch_bounds__(512) void gather_vec_kernel(
+    const int32_t *__restrict__ rows, const int32_t *__restrict__ n_rows_dev,
+    int64_t max_rows, const void *__restrict__ coef_v,
+    const WT *__restrict__ w, int64_t d_in, int64_t d_out,
+    OT *__restrict__ y, float *__restrict__ partials,
+    uint32_t *__restrict__ counters, int splits, int rows_per_split) {
+  constexpr int V = Elt<WT>::kVec;
+  constexpr int NW = WavesFor<B>::value;
+  constexpr int TILE = kWave * V;
+  __shared__ float red[NW][B][TILE];
+  __shared__ int s_last;
+
+  const int lane = threadIdx.x % kWave;
+  const int wave = wave_id();
+  const int tile = blockIdx.x;
+  const int split = blockIdx.y;
+  // Lanes past the last column read a valid column and store nothing.
+  const int64_t col_raw = static_cast<int64_t>(tile) * TILE + lane * V;
+  const int64_t col = col_raw < d_out ? col_raw : d_out - V;
+
+  int64_t n = max_rows;
+  if (n_rows_dev) {
+    int64_t nd = __builtin_amdgcn_readfirstlane(*n_rows_dev);
+    n = nd < n ? (nd < 0 ? 0 : nd) : n;
+  }
+  const int64_t r0 = static_cast<int64_t>(split) * rows_per_split;
+  const int64_t r1 = r0 + rows_per_split < n ? r0 + rows_per_split : n;
+
+  float acc[B][V];
+#pragma unroll
+  for (int b = 0; b < B; ++b)
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc[b][v] = 0.f;
+
+  for (int64_t base = r0 + static_cast<int64_t>(wave) * kRows; base < r1;
+       base += static_cast<int64_t>(NW) * kRows) {
+    // Index and coefficient loads are unconditional (clamped to the last
+    // valid list entry) so they issue back to back; rows past the end of the
+    // list or outside [0, d_in) are then masked out.
+    int32_t rr[kRows];
+    bool ok[kRows];
+    float c[kRows][B];
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) {
+      const int64_t jl = base + u < r1 ? base + u : r1 - 1;
+      rr[u] = rows ? rows[jl] : static_cast<int32_t>(jl);
+    }
+#pragma unroll
+    for (int u = 0; u < kRows; ++u)
+      ok[u] = base + u < r1 && static_cast<uint32_t>(rr[u]) < static_cast<uint64_t>(d_in);
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) {
+      const int64_t jl = base + u < r1 ? base + u : r1 - 1;
+      const int64_t ri = ok[u] ? rr[u] : 0;
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        float cv;
+        if (CMODE == kCoefPacked)
+          cv = static_cast<const float *>(coef_v)[jl * B + b];
+        else if (CMODE == kCoefActF32)
+          cv = static_cast<const float *>(coef_v)[b * d_in + ri];
+        else
+          cv = bf16_to_f32(static_cast<const uint16_t *>(coef_v)[b * d_in + ri]);
+        c[u][b] = ok[u] ? cv : 0.f;
+      }
+    }
+    uint4 q[kRows];
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) {
+      q[u] = make_uint4(0, 0, 0, 0);
+      if (ok[u]) q[u] = load16(w + static_cast<int64_t>(rr[u]) * d_out + col);
+    }
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) {
+      float f[V];
+      Elt<WT>::unpack(q[u], f);
+#pragma unroll
+      for (int b = 0; b < B; ++b)
+#pragma unroll
+        for (int v = 0; v < V; ++v) acc[b][v] = fmaf(c[u][b], f[v], acc[b][v]);
+    }
+  }
+
+  // Combine the waves of this workgroup.
+#pragma unroll
+  for (int b = 0; b < B; ++b)
+#pragma unroll
+    for (int v = 0; v < V; ++v) red[wave][b][lane * V + v] = acc[b][v];
+  __syncthreads();
+
+  const int64_t tile_col0 = static_cast<int64_t>(tile) * TILE;
+  constexpr int ENTRIES = B * TILE;
+  float *part = partials + static_cast<int64_t>(split) * B * d_out;
+  for (int e = threadIdx.x; e < ENTRIES; e += NW * kWave) {
+    const int b = e / TILE, cl = e % TILE;
+    const int64_t cg = tile_col0 + cl;
+    if (cg >= d_out) continue;
+    float s = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) s += red[ww][b][cl];
+    if (splits == 1)
+      Elt<OT>::store(y, b * d_out + cg, s);
+    else
+      part[b * d_out + cg] = s;
+  }
+  if (splits == 1) return;
+
+  // Last workgroup of this tile to arrive adds the partials in split order.
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = atomicAdd(&counters[tile], 1u);
+    s_last = prev == static_cast<uint32_t>(splits - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  for (int e = threadIdx.x; e < ENTRIES; e += NW * kWave) {
+    const int b = e / TILE, cl = e % TILE;
+    const int64_t cg = tile_col0 + cl;
+    if (cg >= d_out) continue;
+    float s = 0.f;
+    for (int r = 0; r < splits; ++r)
+      s += partials[(static_cast<int64_t>(r) * B + b) * d_out + cg];
+    Elt<OT>::store(y, b * d_out + cg, s);
+  }
+  if (threadIdx.x == 0) counters[tile] = 0u;
+}
+
+template <int B, typename WT, typename OT, int CMODE>
+hipError_t launch_t(const GatherArgs &a, const GatherPlan &p, hipStream_t s) {
+  float *partials = static_cast<float *>(a.ws);
+  uint32_t *counters = nullptr;
+  if (p.splits > 1) {
+    const size_t pbytes = static_cast<size_t>(p.splits) * B * a.d_out * sizeof(float);
+    counters = reinterpret_cast<uint32_t *>(static_cast<char *>(a.ws) + ((pbytes + 255) / 256) * 256);
+  }
+  dim3 grid(p.tiles, p.splits);
+  dim3 block(WavesFor<B>::value * kWave);
+  hipLaunchKernelGGL((gather_vec_kernel<B, WT, OT, CMODE>), grid, block, 0, s,
+                     a.rows, a.n_rows, a.max_rows, a.coef,
+                     static_cast<const WT *>(a.w), a.d_in, a.d_out,
+                     static_cast<OT *>(a.y), partials, counters, p.splits,
+                     p.rows_per_split);
+  return hipGetLastError();
+}
+
+template <int B>
+hipError_t dispatch_types(const GatherArgs &a, const GatherPlan &p, hipStream_t s) {
+  if (a.coef_mode == kCoefPacked) {
+    if (a.w_dt == kBF16 && a.y_dt == kBF16) return launch_t<B, uint16_t, uint16_t, kCoefPacked>(a, p, s);
+    if (a.w_dt == kBF16 && a.y_dt == kF32) return launch_t<B, uint16_t, float, kCoefPacked>(a, p, s);
+    if (a.w_dt == kF32 && a.y_dt == kF32) return launch_t<B, float, float, kCoefPacked>(a, p, s);
+    return hipErrorInvalidValue;
+  }
+  if (a.coef_mode == kCoefActBF16 && a.w_dt == kBF16 && a.y_dt == kBF16)
+    return launch_t<B, uint16_t, uint16_t, kCoefActBF16>(a, p, s);
+  if (a.coef_mode == kCoefActF32 && a.w_dt == kF32 && a.y_dt == kF32)
+    return launch_t<B, float, float, kCoefActF32>(a, p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+GatherPlan plan_gather(int B, int64_t max_rows, int64_t d_out, int w_dt) {
+  GatherPlan p;
+  p.vec = w_dt == kF32 ? 4 : 8;
+  p.waves = waves_for(B);
+  const int64_t tile_cols = static_cast<int64_t>(kWave) * p.vec;
+  p.tiles = static_cast<int>((d_out + tile_cols - 1) / tile_cols);
+  // Aim for about four workgroups per CU (256 CUs) while keeping at least
+  // two row groups per wave; more splits cost partial-sum traffic.
+  const int64_t target_wgs = 1024;
+  int64_t splits = (target_wgs + p.tiles - 1) / p.tiles;
+  const int64_t min_rows = static_cast<int64_t>(p.waves) * kRows * 2;
+  int64_t max_splits = max_rows / min_rows;
+  if (max_splits < 1) max_splits = 1;
+  if (splits > max_splits) splits = max_splits;
+  if (splits < 1) splits = 1;
+  int64_t rps = (max_rows + splits - 1) / splits;
+  // Round the split length to whole row groups of the workgroup.
+  const int64_t unit = static_cast<int64_t>(p.waves) * kRows;
+  rps = ((rps + unit - 1) / unit) * unit;
+  if (rps < 1) rps = 1;
+  splits = (max_rows + rps - 1) / rps;
+  if (splits < 1) splits = 1;
+  p.splits = static_cast<int>(splits);
+  p.rows_per_split = static_cast<int>(rps);
+  return p;
+}
+
+size_t gather_ws_bytes(const GatherPlan &p, int B, int64_t d_out) {
+  if (p.splits <= 1) return 0;
+  const size_t pbytes = static_cast<size_t>(p.splits) * B * d_out * sizeof(float);
+  return ((pbytes + 255) / 256) * 256 + ((static_cast<size_t>(p.tiles) * 4 + 255) / 256) * 256;
+}
+
+hipError_t launch_gather(const GatherArgs &a, hipStream_t s) {
+  const GatherPlan p = plan_gather(a.B, a.max_rows, a.d_out, a.w_dt);
+  switch (a.B) {
+    case 1: return dispatch_types<1>(a, p, s);
+    case 2: return dispatch_types<2>(a, p, s);
+    case 3: return dispatch_types<3>(a, p, s);
+    case 4: return dispatch_types<4>(a, p, s);
+    case 5: return dispatch_types<5>(a, p, s);
+    case 6: return dispatch_types<6>(a, p, s);
+    case 7: return dispatch_types<7>(a, p, s);
+    case 8: return dispatch_types<8>(a, p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace larosa

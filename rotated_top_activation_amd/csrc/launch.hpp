@@ -1,0 +1,71 @@
+// Host-side launch interface between the C ABI (abi.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace larosa {
+
+enum Dt { kF32 = 0, kBF16 = 1 };
+
+inline int dt_size(int dt) { return dt == kF32 ? 4 : 2; }
+
+// --- rotation (dot product per output channel against the prepared Qt) ---
+hipError_t launch_rotate(const void *x, int x_dt, const void *qt, int q_dt,
+                         float *x_rot, int B, int d, int qb, hipStream_t s);
+
+// --- Top-K selection (one workgroup per token) ---
+hipError_t launch_select(const float *x_rot, int B, int d, int k, int32_t *idx,
+                         float *val, float *xs, uint32_t *mask, hipStream_t s);
+
+// --- row union of B > 1 selections (from the per-token bit masks) ---
+hipError_t launch_union(const uint32_t *mask, const float *xs, int B, int d,
+                        int32_t *u_idx, int32_t *u_count, float *u_coef,
+                        hipStream_t s);
+
+inline int mask_words(int d) { return (d + 31) / 32; }
+
+// --- gather-rows product y[b,:] = Σ_j coef(j,b)·W[row(j),:] ---
+enum CoefMode { kCoefPacked = 0, kCoefActF32 = 1, kCoefActBF16 = 2 };
+
+struct GatherPlan {
+  int vec;             // columns per lane (one 16-byte load)
+  int waves;           // waves per workgroup, all on one column tile
+  int tiles;           // column tiles of 64·vec columns
+  int splits;          // row splits per tile (R); partial sums when R > 1
+  int rows_per_split;  // rows of the row list handled by one workgroup
+};
+GatherPlan plan_gather(int B, int64_t max_rows, int64_t d_out, int w_dt);
+// Workspace for the split-row reduction: partial sums, then one counter per
+// column tile. Counters must start at zero; the kernel leaves them at zero.
+size_t gather_ws_bytes(const GatherPlan &p, int B, int64_t d_out);
+
+struct GatherArgs {
+  const int32_t *rows;     // NULL: row j is row j
+  const int32_t *n_rows;   // device count, NULL: max_rows
+  int64_t max_rows;
+  const void *coef;        // packed [max_rows, B] fp32, or activation [B, d_in]
+  int coef_mode;
+  const void *w;
+  int w_dt;
+  int64_t d_in, d_out;
+  void *y;
+  int y_dt;
+  int B;
+  void *ws;                // gather_ws_bytes(plan) bytes
+};
+hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
+
+// --- offline preparation ---
+hipError_t launch_transpose_blocks(const void *q, void *qt, int64_t d, int64_t qb,
+                                   int dt, hipStream_t s);
+hipError_t launch_fold(const void *qt, int64_t qb, const void *w, void *wf,
+                       int64_t d_in, int64_t d_out, int dt, hipStream_t s);
+
+// --- glue ---
+hipError_t launch_swiglu(const void *gu, void *h, int64_t B, int64_t f, int dt,
+                         hipStream_t s);
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
+
+}  // namespace larosa

@@ -1,0 +1,175 @@
+// Offline preparation and glue kernels:
+//   * transpose of the rotation blocks into the prepared form Qt = Qᵀ;
+//   * folding W' = Qᵀ·W (the orthogonality in the LaRoSA abstract makes
+//     (x·Q)·(Qᵀ·W) = x·W, so the rotated input multiplies the folded weight);
+//   * SwiGLU between the two linears of an MLP;
+//   * a zero fill for workspaces (a kernel rather than a memset node).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace larosa {
+namespace {
+
+// Qt[c·qb + j][i] = Q[c][i][j], through a 32×33 LDS tile.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_blocks_kernel(
+    const T *__restrict__ q, T *__restrict__ qt, int64_t qb) {
+  __shared__ T tile[32][33];
+  const int64_t c = blockIdx.z;
+  const int64_t i0 = static_cast<int64_t>(blockIdx.y) * 32;  // rows of Q[c]
+  const int64_t j0 = static_cast<int64_t>(blockIdx.x) * 32;  // cols of Q[c]
+  const T *src = q + c * qb * qb;
+  T *dst = qt + c * qb * qb;
+  for (int r = threadIdx.y; r < 32; r += 8) {
+    const int64_t i = i0 + r, j = j0 + threadIdx.x;
+    if (i < qb && j < qb) tile[r][threadIdx.x] = src[i * qb + j];
+  }
+  __syncthreads();
+  for (int r = threadIdx.y; r < 32; r += 8) {
+    const int64_t j = j0 + r, i = i0 + threadIdx.x;
+    if (i < qb && j < qb) dst[j * qb + i] = tile[threadIdx.x][r];
+  }
+}
+
+// W'[c·qb + i, n] = Σ_kk Qt[c·qb + i, kk] · W[c·qb + kk, n], fp32 accumulation,
+// one rounding to T at the end. A workgroup computes a 64×64 output tile whose
+// rows all lie in one rotation block.
+template <typename T>
+__global__ __launch_bounds__(256) void fold_kernel(const T *__restrict__ qt,
+                                                   const T *__restrict__ w,
+                                                   T *__restrict__ wf, int64_t qb,
+                                                   int64_t d_out, int tiles_per_block) {
+  constexpr int TM = 64, TN = 64, TK = 16;
+  __shared__ float as[TK][TM + 4];
+  __shared__ float bs[TK][TN + 4];
+  const int64_t c = blockIdx.y / tiles_per_block;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.y % tiles_per_block) * TM;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * TN;
+  const int t = threadIdx.x, tx = t % 16, ty = t / 16;
+  const T *a_base = qt + (c * qb + r0) * qb;  // rows r0.. of block c of Qt
+  const T *b_base = w + c * qb * d_out;       // rows of W in block c
+  float acc[4][4] = {};
+  for (int64_t k0 = 0; k0 < qb; k0 += TK) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int e = t + 256 * m;
+      const int row = e / TK, kk = e % TK;
+      float av = 0.f;
+      if (r0 + row < qb && k0 + kk < qb) av = Elt<T>::load(a_base, row * qb + k0 + kk);
+      as[kk][row] = av;
+      const int kb = e / TN, col = e % TN;
+      float bv = 0.f;
+      if (k0 + kb < qb && n0 + col < d_out) bv = Elt<T>::load(b_base, (k0 + kb) * d_out + n0 + col);
+      bs[kb][col] = bv;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < TK; ++kk) {
+      float a[4], bb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = as[kk][ty + 16 * i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bb[j] = bs[kk][tx + 16 * j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], bb[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t r = r0 + ty + 16 * i;
+    if (r >= qb) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t n = n0 + tx + 16 * j;
+      if (n < d_out) Elt<T>::store(wf, (c * qb + r) * d_out + n, acc[i][j]);
+    }
+  }
+}
+
+// h[b, i] = SiLU(gu[b, i]) · gu[b, f + i]; V elements per thread.
+template <typename T>
+__global__ __launch_bounds__(256) void swiglu_kernel(const T *__restrict__ gu,
+                                                     T *__restrict__ h, int64_t B,
+                                                     int64_t f) {
+  constexpr int V = Elt<T>::kVec;
+  const int64_t e = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * V;
+  if (e >= B * f) return;
+  const int64_t b = e / f, i = e % f;  // f % V == 0: a vector stays in one row
+  float g[V], u[V], o[V];
+  Elt<T>::unpack(load16(gu + b * 2 * f + i), g);
+  Elt<T>::unpack(load16(gu + b * 2 * f + f + i), u);
+#pragma unroll
+  for (int v = 0; v < V; ++v) o[v] = g[v] / (1.0f + expf(-g[v])) * u[v];
+#pragma unroll
+  for (int v = 0; v < V; ++v) Elt<T>::store(h, b * f + i + v, o[v]);
+}
+
+__global__ void fill_zero_kernel(uint8_t *__restrict__ p, size_t bytes) {
+  const size_t n16 = bytes / 16;
+  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride)
+    reinterpret_cast<uint4 *>(p)[i] = make_uint4(0, 0, 0, 0);
+  const size_t tail = bytes - n16 * 16;
+  if (blockIdx.x == 0 && threadIdx.x < tail) p[n16 * 16 + threadIdx.x] = 0;
+}
+
+}  // namespace
+
+hipError_t launch_transpose_blocks(const void *q, void *qt, int64_t d, int64_t qb,
+                                   int dt, hipStream_t s) {
+  const int64_t nb = d / qb;
+  dim3 grid(static_cast<unsigned>((qb + 31) / 32), static_cast<unsigned>((qb + 31) / 32),
+            static_cast<unsigned>(nb));
+  dim3 block(32, 8);
+  if (dt == kF32)
+    hipLaunchKernelGGL(transpose_blocks_kernel<float>, grid, block, 0, s,
+                       static_cast<const float *>(q), static_cast<float *>(qt), qb);
+  else
+    hipLaunchKernelGGL(transpose_blocks_kernel<uint16_t>, grid, block, 0, s,
+                       static_cast<const uint16_t *>(q), static_cast<uint16_t *>(qt), qb);
+  return hipGetLastError();
+}
+
+hipError_t launch_fold(const void *qt, int64_t qb, const void *w, void *wf, int64_t d_in,
+                       int64_t d_out, int dt, hipStream_t s) {
+  const int tiles_per_block = static_cast<int>((qb + 63) / 64);
+  const int64_t nb = d_in / qb;
+  dim3 grid(static_cast<unsigned>((d_out + 63) / 64), static_cast<unsigned>(nb * tiles_per_block));
+  if (dt == kF32)
+    hipLaunchKernelGGL(fold_kernel<float>, grid, dim3(256), 0, s, static_cast<const float *>(qt),
+                       static_cast<const float *>(w), static_cast<float *>(wf), qb, d_out,
+                       tiles_per_block);
+  else
+    hipLaunchKernelGGL(fold_kernel<uint16_t>, grid, dim3(256), 0, s,
+                       static_cast<const uint16_t *>(qt), static_cast<const uint16_t *>(w),
+                       static_cast<uint16_t *>(wf), qb, d_out, tiles_per_block);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu(const void *gu, void *h, int64_t B, int64_t f, int dt, hipStream_t s) {
+  const int V = dt == kF32 ? 4 : 8;
+  const int64_t threads = (B * f + V - 1) / V;
+  dim3 grid(static_cast<unsigned>((threads + 255) / 256));
+  if (dt == kF32)
+    hipLaunchKernelGGL(swiglu_kernel<float>, grid, dim3(256), 0, s,
+                       static_cast<const float *>(gu), static_cast<float *>(h), B, f);
+  else
+    hipLaunchKernelGGL(swiglu_kernel<uint16_t>, grid, dim3(256), 0, s,
+                       static_cast<const uint16_t *>(gu), static_cast<uint16_t *>(h), B, f);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s) {
+  if (bytes == 0) return hipSuccess;
+  size_t blocks = (bytes / 16 + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                     static_cast<uint8_t *>(p), bytes);
+  return hipGetLastError();
+}
+
+}  // namespace larosa

@@ -1,0 +1,142 @@
+// Rotation of the layer input, stage 1 of the method (LaRoSA summary page,
+// 方法详解 · 技术框架): x_rot[b, :] = x[b, :]·Q, accumulated in fp32.
+//
+// The kernel reads the prepared rotation Qt = Qᵀ ([d, q_block], block rows
+// transposed), so output channel j is the dot product of x's block segment
+// with the contiguous row Qt[j, :]. Each wave owns J consecutive outputs of
+// one block and streams their rows with 16-byte loads per lane (1 KB per
+// wave per load, J loads in flight per step); the lane sums are folded
+// across the wave at the end. No partial sums leave the wave, so the result
+// needs no second pass and is the same on every run.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace larosa {
+namespace {
+
+constexpr int kWavesPerBlock = 4;
+
+// Load V consecutive activations starting at element i as floats.
+template <typename XT, int V> struct XLoad;
+template <int V> struct XLoad<float, V> {
+  __device__ __forceinline__ static void run(const float *x, int64_t i, float *o) {
+#pragma unroll
+    for (int c = 0; c < V; c += 4) {
+      const uint4 q = load16(x + i + c);
+      o[c] = __uint_as_float(q.x); o[c + 1] = __uint_as_float(q.y);
+      o[c + 2] = __uint_as_float(q.z); o[c + 3] = __uint_as_float(q.w);
+    }
+  }
+};
+template <> struct XLoad<uint16_t, 8> {
+  __device__ __forceinline__ static void run(const uint16_t *x, int64_t i, float *o) {
+    Elt<uint16_t>::unpack(load16(x + i), o);
+  }
+};
+template <> struct XLoad<uint16_t, 4> {
+  __device__ __forceinline__ static void run(const uint16_t *x, int64_t i, float *o) {
+    const uint2 q = *reinterpret_cast<const uint2 *>(x + i);
+    o[0] = bf16_lo(q.x); o[1] = bf16_hi(q.x); o[2] = bf16_lo(q.y); o[3] = bf16_hi(q.y);
+  }
+};
+
+template <int B, int J, typename XT, typename QT>
+__global__ __launch_bounds__(kWavesPerBlock * kWave) void rotate_vec_kernel(
+    const XT *__restrict__ x, const QT *__restrict__ qt, float *__restrict__ x_rot,
+    int d, int qb) {
+  constexpr int V = Elt<QT>::kVec;
+  const int lane = threadIdx.x % kWave;
+  const int wave = wave_id();
+  const int j0 = (blockIdx.x * kWavesPerBlock + wave) * J;
+  if (j0 >= d) return;
+  // qb % J == 0 (host-checked), so the J outputs share one block.
+  const int64_t xoff = static_cast<int64_t>(j0 / qb) * qb;
+  const int chunks = qb / V;
+
+  float acc[J][B];
+#pragma unroll
+  for (int jj = 0; jj < J; ++jj)
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[jj][b] = 0.f;
+
+#pragma unroll 2
+  for (int c = lane; c < chunks; c += kWave) {
+    uint4 q[J];
+#pragma unroll
+    for (int jj = 0; jj < J; ++jj)
+      q[jj] = load16(qt + static_cast<int64_t>(j0 + jj) * qb + c * V);
+    float xf[B][V];
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+      XLoad<XT, V>::run(x, static_cast<int64_t>(b) * d + xoff + c * V, xf[b]);
+#pragma unroll
+    for (int jj = 0; jj < J; ++jj) {
+      float qf[V];
+      Elt<QT>::unpack(q[jj], qf);
+#pragma unroll
+      for (int b = 0; b < B; ++b)
+#pragma unroll
+        for (int v = 0; v < V; ++v) acc[jj][b] = fmaf(xf[b][v], qf[v], acc[jj][b]);
+    }
+  }
+#pragma unroll
+  for (int jj = 0; jj < J; ++jj)
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const float s = wave_sum(acc[jj][b]);
+      if (lane == 0) x_rot[static_cast<int64_t>(b) * d + j0 + jj] = s;
+    }
+}
+
+template <int B, int J, typename XT, typename QT>
+hipError_t launch_t(const void *x, const void *qt, float *x_rot, int d, int qb,
+                    hipStream_t s) {
+  const int outs_per_block = kWavesPerBlock * J;
+  dim3 grid((d + outs_per_block - 1) / outs_per_block);
+  hipLaunchKernelGGL((rotate_vec_kernel<B, J, XT, QT>), grid, dim3(kWavesPerBlock * kWave),
+                     0, s, static_cast<const XT *>(x), static_cast<const QT *>(qt), x_rot,
+                     d, qb);
+  return hipGetLastError();
+}
+
+template <int B, typename XT, typename QT>
+hipError_t launch_j(const void *x, const void *qt, float *x_rot, int d, int qb,
+                    hipStream_t s) {
+  // Two outputs per wave keeps about eight waves per CU at d = 4096.
+  if (qb % 2 == 0) return launch_t<B, 2, XT, QT>(x, qt, x_rot, d, qb, s);
+  return launch_t<B, 1, XT, QT>(x, qt, x_rot, d, qb, s);
+}
+
+template <int B>
+hipError_t launch_b(const void *x, int x_dt, const void *qt, int q_dt, float *x_rot,
+                    int d, int qb, hipStream_t s) {
+  if (x_dt == kBF16 && q_dt == kBF16) return launch_j<B, uint16_t, uint16_t>(x, qt, x_rot, d, qb, s);
+  if (x_dt == kF32 && q_dt == kF32) return launch_j<B, float, float>(x, qt, x_rot, d, qb, s);
+  if (x_dt == kF32 && q_dt == kBF16) return launch_j<B, float, uint16_t>(x, qt, x_rot, d, qb, s);
+  if (x_dt == kBF16 && q_dt == kF32) return launch_j<B, uint16_t, float>(x, qt, x_rot, d, qb, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_rotate(const void *x, int x_dt, const void *qt, int q_dt,
+                         float *x_rot, int B, int d, int qb, hipStream_t s) {
+  // Tokens are processed four at a time; each group re-reads Qt.
+  const int xs = dt_size(x_dt);
+  for (int b0 = 0; b0 < B; b0 += 4) {
+    const int nb = B - b0 < 4 ? B - b0 : 4;
+    const void *xb = static_cast<const char *>(x) + static_cast<int64_t>(b0) * d * xs;
+    float *xr = x_rot + static_cast<int64_t>(b0) * d;
+    hipError_t e;
+    switch (nb) {
+      case 1: e = launch_b<1>(xb, x_dt, qt, q_dt, xr, d, qb, s); break;
+      case 2: e = launch_b<2>(xb, x_dt, qt, q_dt, xr, d, qb, s); break;
+      case 3: e = launch_b<3>(xb, x_dt, qt, q_dt, xr, d, qb, s); break;
+      default: e = launch_b<4>(xb, x_dt, qt, q_dt, xr, d, qb, s); break;
+    }
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace larosa

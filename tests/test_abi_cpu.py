@@ -1,0 +1,119 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point that
+include/larosa.h declares, and rejects invalid arguments before touching a
+device. Nothing here launches a kernel. Pointers below are fake addresses
+that the library must never dereference (it checks arguments on the host
+and returns before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from rotated_top_activation_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "larosa.h")
+
+OK, INVALID, SHAPE, ALIGN, DTYPE, WS, NODEV, LAUNCH = range(8)
+P = 0x10000          # a fake, 16-byte aligned device address
+PM = 0x10008         # a fake, misaligned one
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(larosa_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from rotated_top_activation_amd import build
+        build.build()
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported_and_bound(lib):
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, f"{n} has no binding"
+    assert set(_lib.SIGNATURES) == set(names)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.larosa_abi_version() == _lib.ABI_VERSION
+    for code in range(8):
+        assert lib.larosa_status_string(code)
+    assert lib.larosa_status_string(99) == b"unknown status"
+
+
+def test_workspace_bytes(lib):
+    f = lib.larosa_workspace_bytes
+    assert f(1, 4096, 22016, 2457, 0) > 0
+    assert f(1, 4096, 22016, 0, 0) == 0          # k out of range
+    assert f(1, 4096, 22016, 4097, 0) == 0
+    assert f(1, 40000, 128, 10, 0) == 0          # d above 32768
+    assert f(1, 4096, 22016, 2457, 7) == 0       # unknown mode
+    assert f(8, 4096, 22016, 2457, 0) >= f(1, 4096, 22016, 2457, 0)
+
+
+def _lf(lib, x=P, act=1, qt=P, qb=64, wf=P, wdt=1, B=1, d_in=128, d_out=64, k=32, y=P,
+        idx=None, xr=None, mode=0, ws=P, wsb=1 << 30):
+    return lib.larosa_layer_forward(x, act, qt, qb, wf, wdt, B, d_in, d_out, k, y, idx, xr,
+                                    mode, ws, wsb, None)
+
+
+def test_layer_forward_validation(lib):
+    assert _lf(lib, k=0) == INVALID
+    assert _lf(lib, k=129) == INVALID
+    assert _lf(lib, B=-1) == INVALID
+    assert _lf(lib, B=65) == INVALID
+    assert _lf(lib, mode=3) == INVALID
+    assert _lf(lib, x=None) == INVALID
+    assert _lf(lib, y=None) == INVALID
+    assert _lf(lib, qb=48) == SHAPE             # does not divide 128
+    assert _lf(lib, d_in=40000, k=10) == SHAPE
+    assert _lf(lib, d_in=130, qb=130, k=10) == ALIGN   # d % 4
+    assert _lf(lib, d_out=60) == ALIGN          # bf16 rows of 60 are not 16-byte units
+    assert _lf(lib, x=PM) == ALIGN
+    assert _lf(lib, wf=PM) == ALIGN
+    assert _lf(lib, act=5) == DTYPE
+    assert _lf(lib, act=1, wdt=0) == DTYPE      # bf16 activations need bf16 weights
+    assert _lf(lib, ws=None) == WS
+    assert _lf(lib, wsb=16) == WS
+    assert _lf(lib, B=0) == OK                   # empty batch: nothing to do
+
+
+def test_standalone_calls_validation(lib):
+    assert lib.larosa_rotate(P, 1, P, 48, 1, P, 1, 128, None) == SHAPE
+    assert lib.larosa_rotate(P, 9, P, 64, 1, P, 1, 128, None) == DTYPE
+    assert lib.larosa_rotate(None, 1, P, 64, 1, P, 1, 128, None) == INVALID
+    assert lib.larosa_rotate(P, 1, P, 64, 1, PM, 1, 128, None) == ALIGN
+    assert lib.larosa_topk_select(P, 1, 128, 0, P, P, None, None, None, None, None, 0,
+                                  None) == INVALID
+    assert lib.larosa_topk_select(P, 2, 128, 5, P, P, P, P, None, P, P, 1 << 20,
+                                  None) == INVALID   # union without its count
+    assert lib.larosa_topk_select(P, 2, 128, 5, P, P, P, P, P, P, P, 4, None) == WS
+    assert lib.larosa_sparse_gemv(P, None, 10, P, P, 1, P, 1, 1, 128, 60, P, 1 << 20,
+                                  None) == ALIGN
+    assert lib.larosa_sparse_gemv(P, None, 10, P, P, 0, P, 1, 1, 128, 64, P, 1 << 20,
+                                  None) == DTYPE     # fp32 weights into bf16 output
+    assert lib.larosa_sparse_gemv(P, None, -1, P, P, 1, P, 1, 1, 128, 64, P, 1 << 20,
+                                  None) == INVALID
+    assert lib.larosa_dense_gemv(P, 1, P, 0, P, 1, 128, 64, P, 1 << 20, None) == DTYPE
+    assert lib.larosa_fold_weights(P, 64, P, P, 128, 64, 1, None) == INVALID   # aliasing
+    assert lib.larosa_prepare_rotation(P, P + 16, 128, 64, 1, None) == INVALID  # overlap
+    assert lib.larosa_prepare_rotation(P, P + (1 << 20), 128, 48, 1, None) == SHAPE
+    assert lib.larosa_swiglu(P, P, 1, 12, 1, None) == ALIGN
+    assert lib.larosa_workspace_init(PM, 64, None) == ALIGN
+
+
+def test_no_device_is_reported_not_crashed(lib):
+    """Valid arguments on a machine without a GPU give NO_DEVICE."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    assert _lf(lib) == NODEV
+    assert lib.larosa_swiglu(P, P + (1 << 20), 1, 64, 1, None) == NODEV

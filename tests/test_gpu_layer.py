@@ -1,0 +1,115 @@
+"""GPU parity of the whole rotated sparse linear (larosa_layer_forward) and of
+the SwiGLU MLP built from two of them, on the workload shapes, teacher-forced
+against the oracle (see test_gpu_parity for the tolerance rules)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import larosa_ref as ref
+from rotated_top_activation_amd import _lib
+from rotated_top_activation_amd import workloads as wl
+from rotated_top_activation_amd.device import RotatedLinear
+
+from gpu_helpers import dev, guarded, host, host_f32
+from test_gpu_parity import rotation_bound
+
+pytestmark = pytest.mark.gpu
+
+
+def check_linear(lin: RotatedLinear, x: np.ndarray, q: np.ndarray, mode=_lib.UNFUSED,
+                 tol=None, report=None):
+    """Run one layer_forward on x and check every stage against the oracle.
+
+    Returns the GPU output (float64 values of its dtype)."""
+    B = x.shape[0]
+    act = lin.dtype
+    tdt = torch.float32 if act == "f32" else torch.bfloat16
+    y, ok_y = guarded((B, lin.d_out), tdt)
+    idx, ok_i = guarded((B, lin.k), torch.int32, fill=-3)
+    xr, ok_x = guarded((B, lin.d_in), torch.float32)
+    ws = lin.workspace(B, mode)
+    x_d = dev(x, act)
+    lin.forward(x_d, y, ws, idx_out=idx, xrot_out=xr, mode=mode)
+    y2 = torch.empty_like(y)
+    lin.forward(x_d, y2, ws, mode=mode)
+    torch.cuda.synchronize()
+    assert ok_y() and ok_i() and ok_x()
+    assert torch.equal(y, y2), "two runs differ"
+
+    xr_g = host_f32(xr)
+    # stage 1: rotation within the rigorous fp32 bound of the exact product
+    bound, exact = rotation_bound(x, q)
+    assert np.all(np.abs(xr_g.astype(np.float64) - exact) <= bound)
+    # stage 2: the GPU's selection on its own x_rot is the oracle's, bit for bit
+    want_idx = ref.select(xr_g, lin.k)
+    np.testing.assert_array_equal(host(idx), want_idx)
+    # stage 3: the product over the kept rows of the GPU's folded weight
+    wf = host(lin.Wf)
+    want_y = ref.round_to(ref.gather_product(xr_g, want_idx, wf), lin.dtype)
+    tol = tol if tol is not None else (1e-5 if lin.dtype == "f32" else 2e-2)
+    err = ref.rel_error(host(y), want_y)
+    assert err <= tol, err
+    if report is not None:
+        # end to end (not teacher-forced): sets from the oracle's own x_rot;
+        # any difference must be a near-tie within the rotation error bound
+        own = ref.select(ref.rotate(x, q), lin.k)
+        mism = 0
+        for b in range(B):
+            a, c = set(own[b].tolist()), set(want_idx[b].tolist())
+            if a != c:
+                mism += 1
+                key = np.abs(exact[b])
+                kth = np.sort(key)[::-1][lin.k - 1]
+                for i in a ^ c:
+                    assert abs(key[i] - kth) <= 2 * bound[b, i] + 2 * bound[b].max()
+        report.append((B, mism, err))
+    return host(y), xr_g, want_idx
+
+
+def test_single_linear_f32_512x1536():
+    case, x, q, w = wl.single_linear_f32()
+    lin = RotatedLinear(q, w, "f32", case.k)
+    rep = []
+    check_linear(lin, x, q, report=rep)
+    assert case.k == 307
+
+
+@pytest.mark.parametrize("B,sp", [(2, 25), (4, 40), (8, 50), (3, 40)])
+def test_batched_linear_union_4096_to_qkv(B, sp):
+    d, n = 4096, 12288
+    case = wl.LinearCase(cfg=3, batch=B, d_in=d, d_out=n, q_block=d, sparsity_pct=sp,
+                         dtype="bf16", role="attn_in")
+    x, q, w = wl.linear_case_inputs(case, w_std=0.02)
+    lin = RotatedLinear(q, w, "bf16", case.k)
+    check_linear(lin, x, q)
+
+
+@pytest.mark.parametrize("k", [1, 4096])
+def test_linear_extreme_k(k):
+    case = wl.LinearCase(cfg=3, batch=2, d_in=4096, d_out=1032, q_block=4096, sparsity_pct=40,
+                         dtype="bf16")
+    x, q, w = wl.linear_case_inputs(case, w_std=0.02)
+    lin = RotatedLinear(q, w, "bf16", k)
+    y, xr, idx = check_linear(lin, x, q)
+    if k == 4096:
+        # K = d keeps every channel: the dense x·W within bf16 tolerance
+        dense = ref.round_to(x @ w, "bf16")
+        assert ref.rel_error(y, dense) <= 2e-2
+
+
+def test_llama7b_mlp_decode_b1():
+    """The 7B-shaped SwiGLU MLP at batch 1, 40%: gate|up (4096→22016),
+    SiLU(gate)·up, down (11008→4096) with the 4×2752 block rotation."""
+    case = wl.llama7b_mlp()
+    x, q1, wgu, q2, wd = wl.mlp_case_inputs(case)
+    l1 = RotatedLinear(q1, wgu, "bf16", case.k1)
+    l2 = RotatedLinear(q2, wd, "bf16", case.k2)
+    gu, _, _ = check_linear(l1, x, q1)
+    h = torch.empty((1, case.f), dtype=torch.bfloat16, device="cuda")
+    _lib.larosa_swiglu(dev(gu, "bf16"), h, 1, case.f)
+    torch.cuda.synchronize()
+    h_g = host(h)
+    h_ref = ref.swiglu(gu, case.f, "bf16")
+    assert ref.rel_error(h_g, h_ref) <= 2e-2
+    check_linear(l2, h_g, q2)
+    assert (case.k1, case.k2) == (2457, 6604)
