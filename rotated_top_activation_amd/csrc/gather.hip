@@ -23,21 +23,20 @@ namespace larosa {
 namespace {
 
 constexpr int kRows = 8;  // rows per wave group (loads in flight per lane)
+constexpr int kMaxSplitLoads = 16;  // partial sums fetched per round trip
 
-// Waves per workgroup: wide for few tokens, narrower as the per-lane
-// accumulators (B·V floats) and the LDS reduction buffer grow with B.
-constexpr int waves_for(int B) { return B <= 2 ? 8 : (B <= 4 ? 4 : 2); }
-template <int B> struct WavesFor { static constexpr int value = waves_for(B); };
+// Largest waves per workgroup for B tokens: the LDS reduction buffer holds
+// NW·B·TILE floats (at most 32 KB).
+constexpr int max_waves_for(int B) { return B == 1 ? 16 : (B == 2 ? 8 : (B <= 4 ? 4 : 2)); }
 
-template <int B, typename WT, typename OT, int CMODE>
-__global__ __launch_bounds__(512) void gather_vec_kernel(
+template <int B, int NW, typename WT, typename OT, int CMODE>
+__global__ __launch_bounds__(NW * 64) void gather_vec_kernel(
     const int32_t *__restrict__ rows, const int32_t *__restrict__ n_rows_dev,
     int64_t max_rows, const void *__restrict__ coef_v,
     const WT *__restrict__ w, int64_t d_in, int64_t d_out,
     OT *__restrict__ y, float *__restrict__ partials,
     uint32_t *__restrict__ counters, int splits, int rows_per_split) {
   constexpr int V = Elt<WT>::kVec;
-  constexpr int NW = WavesFor<B>::value;
   constexpr int TILE = kWave * V;
   __shared__ float red[NW][B][TILE];
   __shared__ int s_last;
@@ -130,37 +129,60 @@ __global__ __launch_bounds__(512) void gather_vec_kernel(
     float s = 0.f;
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) s += red[ww][b][cl];
-    if (splits == 1)
+    if (splits == 1) {
       Elt<OT>::store(y, b * d_out + cg, s);
-    else
-      part[b * d_out + cg] = s;
+    } else {
+      // Written with an agent-scope atomic exchange, so the value lands at
+      // the same device-coherent point as the arrival counter below.
+      const float old = __hip_atomic_exchange(part + b * d_out + cg, s, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+      (void)old;
+    }
   }
   if (splits == 1) return;
 
-  // Last workgroup of this tile to arrive adds the partials in split order.
-  __threadfence();
+  // Last workgroup of this tile to arrive adds the partials in split order,
+  // so the sum does not depend on arrival order. Every partial write above
+  // has completed (waitcnt) before this workgroup's counter increment; the
+  // reads below are agent-scope atomic loads, which do not hit stale cache
+  // lines. No L2 write-back or invalidate is involved.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t prev = atomicAdd(&counters[tile], 1u);
+    const uint32_t prev =
+        __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = prev == static_cast<uint32_t>(splits - 1);
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
+  const int64_t stride = static_cast<int64_t>(B) * d_out;
   for (int e = threadIdx.x; e < ENTRIES; e += NW * kWave) {
     const int b = e / TILE, cl = e % TILE;
     const int64_t cg = tile_col0 + cl;
     if (cg >= d_out) continue;
+    const float *p = partials + b * d_out + cg;
     float s = 0.f;
-    for (int r = 0; r < splits; ++r)
-      s += partials[(static_cast<int64_t>(r) * B + b) * d_out + cg];
+    // All loads of a chunk are issued before any is used: one round trip
+    // per kMaxSplitLoads splits.
+    for (int r0 = 0; r0 < splits; r0 += kMaxSplitLoads) {
+      float v[kMaxSplitLoads];
+#pragma unroll
+      for (int i = 0; i < kMaxSplitLoads; ++i)
+        v[i] = r0 + i < splits ? __hip_atomic_load(p + (r0 + i) * stride, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT)
+                               : 0.f;
+#pragma unroll
+      for (int i = 0; i < kMaxSplitLoads; ++i)
+        if (r0 + i < splits) s += v[i];
+    }
     Elt<OT>::store(y, b * d_out + cg, s);
   }
-  if (threadIdx.x == 0) counters[tile] = 0u;
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int B, typename WT, typename OT, int CMODE>
-hipError_t launch_t(const GatherArgs &a, const GatherPlan &p, hipStream_t s) {
+template <int B, int NW, typename WT, typename OT, int CMODE>
+hipError_t launch_nw(const GatherArgs &a, const GatherPlan &p, hipStream_t s) {
   float *partials = static_cast<float *>(a.ws);
   uint32_t *counters = nullptr;
   if (p.splits > 1) {
@@ -168,13 +190,22 @@ hipError_t launch_t(const GatherArgs &a, const GatherPlan &p, hipStream_t s) {
     counters = reinterpret_cast<uint32_t *>(static_cast<char *>(a.ws) + ((pbytes + 255) / 256) * 256);
   }
   dim3 grid(p.tiles, p.splits);
-  dim3 block(WavesFor<B>::value * kWave);
-  hipLaunchKernelGGL((gather_vec_kernel<B, WT, OT, CMODE>), grid, block, 0, s,
+  dim3 block(NW * kWave);
+  hipLaunchKernelGGL((gather_vec_kernel<B, NW, WT, OT, CMODE>), grid, block, 0, s,
                      a.rows, a.n_rows, a.max_rows, a.coef,
                      static_cast<const WT *>(a.w), a.d_in, a.d_out,
                      static_cast<OT *>(a.y), partials, counters, p.splits,
                      p.rows_per_split);
   return hipGetLastError();
+}
+
+template <int B, typename WT, typename OT, int CMODE>
+hipError_t launch_t(const GatherArgs &a, const GatherPlan &p, hipStream_t s) {
+  constexpr int M = max_waves_for(B);
+  if (p.waves >= 16 && M >= 16) return launch_nw<B, (M >= 16 ? 16 : M), WT, OT, CMODE>(a, p, s);
+  if (p.waves >= 8 && M >= 8) return launch_nw<B, (M >= 8 ? 8 : M), WT, OT, CMODE>(a, p, s);
+  if (p.waves >= 4 && M >= 4) return launch_nw<B, (M >= 4 ? 4 : M), WT, OT, CMODE>(a, p, s);
+  return launch_nw<B, M, WT, OT, CMODE>(a, p, s);
 }
 
 template <int B>
@@ -194,30 +225,44 @@ hipError_t dispatch_types(const GatherArgs &a, const GatherPlan &p, hipStream_t 
 
 }  // namespace
 
-GatherPlan plan_gather(int B, int64_t max_rows, int64_t d_out, int w_dt) {
+namespace {
+
+GatherPlan plan_with_waves(int waves, int64_t max_rows, int64_t d_out, int w_dt) {
   GatherPlan p;
   p.vec = w_dt == kF32 ? 4 : 8;
-  p.waves = waves_for(B);
+  p.waves = waves;
   const int64_t tile_cols = static_cast<int64_t>(kWave) * p.vec;
   p.tiles = static_cast<int>((d_out + tile_cols - 1) / tile_cols);
-  // Aim for about four workgroups per CU (256 CUs) while keeping at least
-  // two row groups per wave; more splits cost partial-sum traffic.
-  const int64_t target_wgs = 1024;
+  // Aim for about 32 waves per CU (256 CUs) while keeping at least two row
+  // groups per wave; more splits cost partial-sum traffic and reduction time.
+  const int64_t target_wgs = (256 * 32) / waves;
   int64_t splits = (target_wgs + p.tiles - 1) / p.tiles;
-  const int64_t min_rows = static_cast<int64_t>(p.waves) * kRows * 2;
-  int64_t max_splits = max_rows / min_rows;
+  const int64_t unit = static_cast<int64_t>(waves) * kRows;
+  int64_t max_splits = max_rows / (2 * unit);
   if (max_splits < 1) max_splits = 1;
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
   int64_t rps = (max_rows + splits - 1) / splits;
-  // Round the split length to whole row groups of the workgroup.
-  const int64_t unit = static_cast<int64_t>(p.waves) * kRows;
-  rps = ((rps + unit - 1) / unit) * unit;
+  rps = ((rps + unit - 1) / unit) * unit;  // whole row groups per workgroup
   if (rps < 1) rps = 1;
   splits = (max_rows + rps - 1) / rps;
   if (splits < 1) splits = 1;
   p.splits = static_cast<int>(splits);
   p.rows_per_split = static_cast<int>(rps);
+  return p;
+}
+
+}  // namespace
+
+GatherPlan plan_gather(int B, int64_t max_rows, int64_t d_out, int w_dt) {
+  // The widest workgroup that still yields at least 256 workgroups (one per
+  // CU); otherwise the narrowest allowed.
+  const int m = max_waves_for(B);
+  GatherPlan p = plan_with_waves(m, max_rows, d_out, w_dt);
+  for (int w = m; w >= 4; w /= 2) {
+    p = plan_with_waves(w, max_rows, d_out, w_dt);
+    if (static_cast<int64_t>(p.tiles) * p.splits >= 256) break;
+  }
   return p;
 }
 

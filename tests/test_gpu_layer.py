@@ -113,3 +113,58 @@ def test_llama7b_mlp_decode_b1():
     assert ref.rel_error(h_g, h_ref) <= 2e-2
     check_linear(l2, h_g, q2)
     assert (case.k1, case.k2) == (2457, 6604)
+
+
+@pytest.mark.parametrize("B", [1, 4])
+def test_graph_replay_matches_eager(B):
+    """A captured layer_forward replays to the eager result every time, with
+    eager work and synchronisations between replays."""
+    case = wl.LinearCase(cfg=3, batch=B, d_in=2048, d_out=4104, q_block=512, sparsity_pct=40,
+                         dtype="bf16")
+    x, q, w = wl.linear_case_inputs(case, w_std=0.02)
+    lin = RotatedLinear(q, w, "bf16", case.k)
+    ws = lin.workspace(B)
+    x_d = dev(x, "bf16")
+    y_eager = torch.empty((B, case.d_out), dtype=torch.bfloat16, device="cuda")
+    lin.forward(x_d, y_eager, ws)
+    torch.cuda.synchronize()
+    y_g = torch.zeros_like(y_eager)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        lin.forward(x_d, y_g, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lin.forward(x_d, y_g, ws)
+    for rep in range(4):
+        y_g.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_g, y_eager), f"replay {rep} differs"
+        other = torch.empty_like(y_eager)
+        lin.forward(x_d, other, ws)          # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(other, y_eager)
+
+
+def test_changing_inputs_through_one_workspace():
+    """Different inputs through one workspace, call after call: every output
+    matches the oracle (a stale partial sum from an earlier call would not)."""
+    case = wl.LinearCase(cfg=3, batch=1, d_in=4096, d_out=22016, q_block=4096,
+                         sparsity_pct=40, dtype="bf16")
+    _, q, w = wl.linear_case_inputs(case, w_std=0.02)
+    lin = RotatedLinear(q, w, "bf16", case.k)
+    ws = lin.workspace(1)
+    wf = host(lin.Wf)
+    rng = np.random.default_rng(77)
+    for it in range(6):
+        x = wl.quantize(rng.standard_normal((1, 4096)) * (it + 1), "bf16")
+        y = torch.empty((1, case.d_out), dtype=torch.bfloat16, device="cuda")
+        xr = torch.empty((1, 4096), device="cuda")
+        lin.forward(dev(x, "bf16"), y, ws, xrot_out=xr)
+        torch.cuda.synchronize()
+        xr_g = host_f32(xr)
+        idx = ref.select(xr_g, case.k)
+        want = ref.round_to(ref.gather_product(xr_g, idx, wf), "bf16")
+        assert ref.rel_error(host(y), want) <= 2e-2, it
