@@ -37,7 +37,7 @@ hipStream_t stream_of(larosa_stream_t s) { return static_cast<hipStream_t>(s); }
 // Workspace carving for larosa_layer_forward and the standalone calls.
 struct Layout {
   size_t x_rot = 0, idx = 0, val = 0, xs = 0, mask = 0, u_idx = 0, u_cnt = 0,
-         u_coef = 0, gather = 0, total = 0;
+         u_coef = 0, gather = 0, fused = 0, total = 0;
 };
 
 Layout layout_for(int64_t B, int64_t d_in, int64_t d_out, int64_t k, int w_dt) {
@@ -62,6 +62,15 @@ Layout layout_for(int64_t B, int64_t d_in, int64_t d_out, int64_t k, int w_dt) {
   const GatherPlan p = plan_gather(static_cast<int>(B), d_in, d_out, w_dt);
   L.gather = take(gather_ws_bytes(p, static_cast<int>(B), d_out));
   L.total = off;
+  return L;
+}
+
+// The fused kernel's region follows the unfused layout, so calls in either
+// mode can share one workspace.
+Layout layout_with_fused(int64_t B, int64_t d_in, int64_t d_out, int64_t k, int w_dt) {
+  Layout L = layout_for(B, d_in, d_out, k, w_dt);
+  L.fused = L.total;
+  L.total += align256(plan_fused(d_in, d_out, k, w_dt, kFusedMaxGrid).bytes);
   return L;
 }
 
@@ -109,8 +118,11 @@ size_t larosa_workspace_bytes(int64_t B, int64_t d_in, int64_t d_out, int64_t k,
   if (mode != LAROSA_UNFUSED && mode != LAROSA_FUSED) return 0;
   // Sized for bf16 weights; fp32 weights have twice the column tiles but the
   // same number of splits at most, and fit in the same bytes or fewer.
-  const Layout a = layout_for(B < 1 ? 1 : B, d_in, d_out, k, LAROSA_BF16);
-  const Layout b = layout_for(B < 1 ? 1 : B, d_in, d_out, k, LAROSA_F32);
+  const int64_t b1 = B < 1 ? 1 : B;
+  const Layout a = mode == LAROSA_FUSED ? layout_with_fused(b1, d_in, d_out, k, LAROSA_BF16)
+                                        : layout_for(b1, d_in, d_out, k, LAROSA_BF16);
+  const Layout b = mode == LAROSA_FUSED ? layout_with_fused(b1, d_in, d_out, k, LAROSA_F32)
+                                        : layout_for(b1, d_in, d_out, k, LAROSA_F32);
   return a.total > b.total ? a.total : b.total;
 }
 
@@ -282,12 +294,30 @@ int larosa_layer_forward(const void *x, int act_dtype, const void *Qt, int64_t q
   if (!aligned16(x) || !aligned16(Qt) || !aligned16(W_folded) || !aligned16(y))
     return LAROSA_ERR_ALIGNMENT;
   if ((xrot_out && !aligned16(xrot_out)) || !aligned16(ws)) return LAROSA_ERR_ALIGNMENT;
-  const Layout L = layout_for(B, d_in, d_out, k, w_dtype);
+  const bool fused = mode == LAROSA_FUSED && fused_supported(B, d_in, act_dtype, w_dtype);
+  const Layout L = fused ? layout_with_fused(B, d_in, d_out, k, w_dtype)
+                         : layout_for(B, d_in, d_out, k, w_dtype);
   if (!ws || ws_bytes < L.total) return LAROSA_ERR_WORKSPACE;
   if (int st = device_status()) return st;
 
   hipStream_t s = stream_of(stream);
   char *base = static_cast<char *>(ws);
+  if (fused) {
+    FusedArgs f;
+    f.x = x;
+    f.qt = Qt;
+    f.wf = W_folded;
+    f.y = y;
+    f.w_dt = w_dtype;
+    f.d_in = static_cast<int>(d_in);
+    f.q_block = static_cast<int>(q_block);
+    f.k = static_cast<int>(k);
+    f.d_out = d_out;
+    f.idx_out = idx_out;
+    f.xrot_out = xrot_out;
+    f.ws = base + L.fused;
+    return launched(launch_fused_linear(f, s));
+  }
   float *x_rot = xrot_out ? xrot_out : reinterpret_cast<float *>(base + L.x_rot);
   int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(base + L.idx);
   float *val = reinterpret_cast<float *>(base + L.val);

@@ -57,6 +57,31 @@ struct GatherArgs {
 };
 hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
 
+// --- fused rotate → select → gather for one token (persistent launch) ---
+constexpr int kFusedMaxD = 16384;          // 32 channels per thread of 512
+constexpr int kFusedMaxRowsPerUnit = 1024;  // LDS row list of one work unit
+constexpr int kFusedMaxGrid = 2048;         // bound used to size the workspace
+
+struct FusedPlan {
+  int grid, tiles, splits, chans_per_split;
+  // workspace layout: synchronisation words at 0, then these regions
+  size_t tile_off, flags_off, xrot_off, partial_off, bytes;
+};
+FusedPlan plan_fused(int64_t d_in, int64_t d_out, int64_t k, int w_dt, int grid);
+bool fused_supported(int64_t B, int64_t d_in, int act_dt, int w_dt);
+
+struct FusedArgs {
+  const void *x, *qt, *wf;
+  void *y;
+  int w_dt;
+  int d_in, q_block, k;
+  int64_t d_out;
+  int32_t *idx_out;   // may be NULL
+  float *xrot_out;    // may be NULL (x_rot then lives in the workspace)
+  void *ws;           // plan_fused(..., kFusedMaxGrid).bytes, zeroed before first use
+};
+hipError_t launch_fused_linear(const FusedArgs &a, hipStream_t s);
+
 // --- offline preparation ---
 hipError_t launch_transpose_blocks(const void *q, void *qt, int64_t d, int64_t qb,
                                    int dt, hipStream_t s);

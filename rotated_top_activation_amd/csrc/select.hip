@@ -2,9 +2,9 @@
 // 技术框架: keep the K largest-magnitude entries of the rotated activation,
 // zero the rest; the abstract's fixed K gives consistent sparsity).
 //
-// One 1024-thread workgroup per token. Thread t owns the E = ceil(d/1024)
-// consecutive channels [t·E, t·E + E) and keeps their values and keys in
-// registers. The key of a channel is its fp32 bit pattern with the sign bit
+// One 1024-thread workgroup per token. Thread t owns the E consecutive
+// channels [t·E, t·E + E) (E = ceil(d/1024) rounded up to a multiple of 4,
+// read with 16-byte loads) and keeps their values and keys in registers. The key of a channel is its fp32 bit pattern with the sign bit
 // cleared, which orders like |x|. An exact radix select over the 31 key bits
 // (digits of 11, 11 and 9 bits, LDS histograms) finds the K-th largest key
 // T and how many channels equal to T are still to be taken; those go to the
@@ -18,35 +18,19 @@
 // coefficient for every union row.
 #include "common.hpp"
 #include "launch.hpp"
+#include "select_core.hpp"
 
 namespace larosa {
 namespace {
 
 constexpr int kThreads = 1024;
-constexpr int kNumWaves = kThreads / kWave;
-constexpr int kBins = 2048;
-
-// Inclusive scan over the 1024 threads of the workgroup (thread order).
-__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t *wave_tot) {
-  const int lane = threadIdx.x % kWave;
-  const int w = threadIdx.x / kWave;
-  uint32_t x = wave_incl_scan(v, lane);
-  if (lane == kWave - 1) wave_tot[w] = x;
-  __syncthreads();
-  uint32_t off = 0;
-  for (int i = 0; i < w; ++i) off += wave_tot[i];
-  __syncthreads();  // wave_tot may be rewritten by the next scan
-  return x + off;
-}
 
 template <int EMAX>
 __global__ __launch_bounds__(kThreads) void topk_select_kernel(
     const float *__restrict__ x_rot, int d, int k, int E, int32_t *__restrict__ idx,
     float *__restrict__ val, float *__restrict__ xs, uint32_t *__restrict__ mask) {
-  __shared__ uint32_t hist[kBins];
-  __shared__ uint32_t wave_tot[kNumWaves];
+  __shared__ SelectSmem<kThreads> sm;
   __shared__ uint32_t bitmap[kThreads];  // up to 32768 channels
-  __shared__ uint32_t s_bin, s_above;
 
   const int b = blockIdx.x;
   const int t = threadIdx.x;
@@ -54,93 +38,29 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
   const int i0 = t * E;
 
   float v[EMAX];
-  uint32_t key[EMAX];  // bit 31 set marks "no channel here"
-#pragma unroll
-  for (int e = 0; e < EMAX; ++e) {
-    const int i = i0 + e;
-    if (e < E && i < d) {
-      v[e] = xr[i];
-      key[e] = __float_as_uint(v[e]) & 0x7FFFFFFFu;
-    } else {
-      v[e] = 0.f;
-      key[e] = 0x80000000u;
-    }
-  }
+  uint32_t key[EMAX];
+  load_keys4<EMAX>(xr, d, E, key, v);
   if (mask) bitmap[t] = 0u;
 
-  // Radix select: after the three passes, prefix == T and krem is the number
-  // of channels with key == T that still belong to the top K.
-  uint32_t prefix = 0u, pmask = 0x80000000u;
-  uint32_t krem = static_cast<uint32_t>(k);
-#pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 20 : (pass == 1 ? 9 : 0);
-    const uint32_t dmask = pass == 2 ? 0x1FFu : 0x7FFu;
-    hist[t] = 0u;
-    hist[t + kThreads] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < EMAX; ++e)
-      if ((key[e] & pmask) == prefix) atomicAdd(&hist[(key[e] >> shift) & dmask], 1u);
-    __syncthreads();
-    // Thread t looks at the bin pair q = 1023 − t, so thread order runs from
-    // the highest bins down and the inclusive scan counts keys at or above.
-    const int q = kThreads - 1 - t;
-    const uint32_t h_hi = hist[2 * q + 1], h_lo = hist[2 * q];
-    const uint32_t pair = h_hi + h_lo;
-    const uint32_t incl = block_incl_scan(pair, wave_tot);
-    const uint32_t above = incl - pair;  // keys in bins above 2q+1
-    if (above < krem && above + h_hi >= krem) {
-      s_bin = 2 * q + 1;
-      s_above = above;
-    } else if (above + h_hi < krem && incl >= krem) {
-      s_bin = 2 * q;
-      s_above = above + h_hi;
-    }
-    __syncthreads();
-    prefix |= s_bin << shift;
-    pmask |= dmask << shift;
-    krem -= s_above;
-    __syncthreads();  // s_bin / s_above are rewritten by the next pass
-  }
-  const uint32_t T = prefix;
+  uint32_t T, krem, n_eq;
+  radix_threshold<kThreads, EMAX>(key, static_cast<uint32_t>(k), sm, T, krem, n_eq);
+  bool kept[EMAX];
+  uint32_t pos;
+  kept_flags<kThreads, EMAX>(key, T, krem, sm, kept, pos);
 
-  // Positions: kept = key > T, plus the first krem channels with key == T.
-  uint32_t gt = 0, eq = 0;
-#pragma unroll
-  for (int e = 0; e < EMAX; ++e) {
-    if (key[e] & 0x80000000u) continue;
-    gt += key[e] > T;
-    eq += key[e] == T;
-  }
-  const uint32_t packed = (gt << 16) | eq;  // each count <= 32768
-  const uint32_t excl = block_incl_scan(packed, wave_tot) - packed;
-  uint32_t g = excl >> 16, qe = excl & 0xFFFFu;
   int32_t *idx_b = idx + static_cast<int64_t>(b) * k;
   float *val_b = val + static_cast<int64_t>(b) * k;
 #pragma unroll
   for (int e = 0; e < EMAX; ++e) {
-    if (key[e] & 0x80000000u) continue;
+    if (key[e] & kNoKey) continue;
     const int i = i0 + e;
-    bool kept = false;
-    uint32_t pos = 0;
-    if (key[e] > T) {
-      pos = g + (qe < krem ? qe : krem);
-      kept = true;
-      ++g;
-    } else if (key[e] == T) {
-      if (qe < krem) {
-        pos = g + qe;
-        kept = true;
-      }
-      ++qe;
-    }
-    if (kept) {
+    if (kept[e]) {
       idx_b[pos] = i;
       val_b[pos] = v[e];
+      ++pos;
       if (mask) atomicOr(&bitmap[i >> 5], 1u << (i & 31));
     }
-    if (xs) xs[static_cast<int64_t>(b) * d + i] = kept ? v[e] : 0.f;
+    if (xs) xs[static_cast<int64_t>(b) * d + i] = kept[e] ? v[e] : 0.f;
   }
   if (mask) {
     __syncthreads();
@@ -153,14 +73,14 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
 __global__ __launch_bounds__(kThreads) void union_list_kernel(
     const uint32_t *__restrict__ mask, int B, int d, int32_t *__restrict__ u_idx,
     int32_t *__restrict__ u_count) {
-  __shared__ uint32_t wave_tot[kNumWaves];
+  __shared__ uint32_t wave_tot[kThreads / kWave];
   const int t = threadIdx.x;
   const int nw = (d + 31) / 32;
   uint32_t word = 0u;
   if (t < nw)
     for (int b = 0; b < B; ++b) word |= mask[static_cast<int64_t>(b) * nw + t];
   const uint32_t c = __popc(word);
-  const uint32_t incl = block_incl_scan(c, wave_tot);
+  const uint32_t incl = block_incl_scan<kThreads>(c, wave_tot);
   uint32_t pos = incl - c;
   while (word) {
     const int bit = __ffs(word) - 1;
@@ -195,7 +115,7 @@ hipError_t launch_sel(const float *x_rot, int B, int d, int k, int E, int32_t *i
 
 hipError_t launch_select(const float *x_rot, int B, int d, int k, int32_t *idx,
                          float *val, float *xs, uint32_t *mask, hipStream_t s) {
-  const int E = (d + kThreads - 1) / kThreads;
+  const int E = slots_per_thread(d, kThreads);
   if (E <= 4) return launch_sel<4>(x_rot, B, d, k, E, idx, val, xs, mask, s);
   if (E <= 8) return launch_sel<8>(x_rot, B, d, k, E, idx, val, xs, mask, s);
   if (E <= 16) return launch_sel<16>(x_rot, B, d, k, E, idx, val, xs, mask, s);

@@ -66,12 +66,28 @@ def check_linear(lin: RotatedLinear, x: np.ndarray, q: np.ndarray, mode=_lib.UNF
     return host(y), xr_g, want_idx
 
 
-def test_single_linear_f32_512x1536():
+MODES = [pytest.param(_lib.UNFUSED, id="unfused"), pytest.param(_lib.FUSED, id="fused")]
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_single_linear_f32_512x1536(mode):
     case, x, q, w = wl.single_linear_f32()
     lin = RotatedLinear(q, w, "f32", case.k)
     rep = []
-    check_linear(lin, x, q, report=rep)
+    check_linear(lin, x, q, mode=mode, report=rep)
     assert case.k == 307
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("d,qb,n,sp", [(4096, 4096, 12288, 25), (11008, 2752, 4096, 40),
+                                       (1024, 256, 1032, 50), (16384, 4096, 520, 40),
+                                       (2048, 2048, 22016, 40)])
+def test_single_token_linear_shapes(mode, d, qb, n, sp):
+    case = wl.LinearCase(cfg=3, batch=1, d_in=d, d_out=n, q_block=qb, sparsity_pct=sp,
+                         dtype="bf16", role="o_in")
+    x, q, w = wl.linear_case_inputs(case, w_std=0.02)
+    lin = RotatedLinear(q, w, "bf16", case.k)
+    check_linear(lin, x, q, mode=mode)
 
 
 @pytest.mark.parametrize("B,sp", [(2, 25), (4, 40), (8, 50), (3, 40)])
@@ -84,87 +100,114 @@ def test_batched_linear_union_4096_to_qkv(B, sp):
     check_linear(lin, x, q)
 
 
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("B", [1, 2])
 @pytest.mark.parametrize("k", [1, 4096])
-def test_linear_extreme_k(k):
-    case = wl.LinearCase(cfg=3, batch=2, d_in=4096, d_out=1032, q_block=4096, sparsity_pct=40,
+def test_linear_extreme_k(k, B, mode):
+    case = wl.LinearCase(cfg=3, batch=B, d_in=4096, d_out=1032, q_block=4096, sparsity_pct=40,
                          dtype="bf16")
     x, q, w = wl.linear_case_inputs(case, w_std=0.02)
     lin = RotatedLinear(q, w, "bf16", k)
-    y, xr, idx = check_linear(lin, x, q)
+    y, xr, idx = check_linear(lin, x, q, mode=mode)
     if k == 4096:
         # K = d keeps every channel: the dense x·W within bf16 tolerance
         dense = ref.round_to(x @ w, "bf16")
         assert ref.rel_error(y, dense) <= 2e-2
 
 
-def test_llama7b_mlp_decode_b1():
+@pytest.mark.parametrize("mode", MODES)
+def test_llama7b_mlp_decode_b1(mode):
     """The 7B-shaped SwiGLU MLP at batch 1, 40%: gate|up (4096→22016),
     SiLU(gate)·up, down (11008→4096) with the 4×2752 block rotation."""
     case = wl.llama7b_mlp()
     x, q1, wgu, q2, wd = wl.mlp_case_inputs(case)
     l1 = RotatedLinear(q1, wgu, "bf16", case.k1)
     l2 = RotatedLinear(q2, wd, "bf16", case.k2)
-    gu, _, _ = check_linear(l1, x, q1)
+    gu, _, _ = check_linear(l1, x, q1, mode=mode)
     h = torch.empty((1, case.f), dtype=torch.bfloat16, device="cuda")
     _lib.larosa_swiglu(dev(gu, "bf16"), h, 1, case.f)
     torch.cuda.synchronize()
     h_g = host(h)
     h_ref = ref.swiglu(gu, case.f, "bf16")
     assert ref.rel_error(h_g, h_ref) <= 2e-2
-    check_linear(l2, h_g, q2)
+    check_linear(l2, h_g, q2, mode=mode)
     assert (case.k1, case.k2) == (2457, 6604)
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("B", [1, 4])
-def test_graph_replay_matches_eager(B):
+def test_graph_replay_matches_eager(B, mode):
     """A captured layer_forward replays to the eager result every time, with
     eager work and synchronisations between replays."""
     case = wl.LinearCase(cfg=3, batch=B, d_in=2048, d_out=4104, q_block=512, sparsity_pct=40,
                          dtype="bf16")
     x, q, w = wl.linear_case_inputs(case, w_std=0.02)
     lin = RotatedLinear(q, w, "bf16", case.k)
-    ws = lin.workspace(B)
+    ws = lin.workspace(B, mode)
     x_d = dev(x, "bf16")
     y_eager = torch.empty((B, case.d_out), dtype=torch.bfloat16, device="cuda")
-    lin.forward(x_d, y_eager, ws)
+    lin.forward(x_d, y_eager, ws, mode=mode)
     torch.cuda.synchronize()
     y_g = torch.zeros_like(y_eager)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        lin.forward(x_d, y_g, ws)
+        lin.forward(x_d, y_g, ws, mode=mode)
     torch.cuda.current_stream().wait_stream(side)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        lin.forward(x_d, y_g, ws)
+        lin.forward(x_d, y_g, ws, mode=mode)
     for rep in range(4):
         y_g.zero_()
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(y_g, y_eager), f"replay {rep} differs"
         other = torch.empty_like(y_eager)
-        lin.forward(x_d, other, ws)          # eager work between replays
+        lin.forward(x_d, other, ws, mode=mode)   # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(other, y_eager)
 
 
-def test_changing_inputs_through_one_workspace():
+@pytest.mark.parametrize("mode", MODES)
+def test_changing_inputs_through_one_workspace(mode):
     """Different inputs through one workspace, call after call: every output
     matches the oracle (a stale partial sum from an earlier call would not)."""
     case = wl.LinearCase(cfg=3, batch=1, d_in=4096, d_out=22016, q_block=4096,
                          sparsity_pct=40, dtype="bf16")
     _, q, w = wl.linear_case_inputs(case, w_std=0.02)
     lin = RotatedLinear(q, w, "bf16", case.k)
-    ws = lin.workspace(1)
+    ws = lin.workspace(1, mode)
     wf = host(lin.Wf)
     rng = np.random.default_rng(77)
     for it in range(6):
         x = wl.quantize(rng.standard_normal((1, 4096)) * (it + 1), "bf16")
         y = torch.empty((1, case.d_out), dtype=torch.bfloat16, device="cuda")
         xr = torch.empty((1, 4096), device="cuda")
-        lin.forward(dev(x, "bf16"), y, ws, xrot_out=xr)
+        lin.forward(dev(x, "bf16"), y, ws, xrot_out=xr, mode=mode)
         torch.cuda.synchronize()
         xr_g = host_f32(xr)
         idx = ref.select(xr_g, case.k)
         want = ref.round_to(ref.gather_product(xr_g, idx, wf), "bf16")
         assert ref.rel_error(host(y), want) <= 2e-2, it
+
+
+def test_fused_and_unfused_share_one_workspace():
+    """Alternating modes on one workspace: both stay correct and agree on the
+    kept index sets."""
+    case = wl.LinearCase(cfg=3, batch=1, d_in=4096, d_out=4104, q_block=1024, sparsity_pct=40,
+                         dtype="bf16")
+    x, q, w = wl.linear_case_inputs(case, w_std=0.02)
+    lin = RotatedLinear(q, w, "bf16", case.k)
+    ws = lin.workspace(1, _lib.FUSED)
+    x_d = dev(x, "bf16")
+    outs = []
+    for it in range(6):
+        mode = _lib.FUSED if it % 2 else _lib.UNFUSED
+        y = torch.empty((1, case.d_out), dtype=torch.bfloat16, device="cuda")
+        idx = torch.empty((1, case.k), dtype=torch.int32, device="cuda")
+        lin.forward(x_d, y, ws, idx_out=idx, mode=mode)
+        torch.cuda.synchronize()
+        outs.append((mode, host(y), host(idx)))
+    for mode, y, idx in outs:
+        np.testing.assert_array_equal(idx, outs[0][2])
+        assert ref.rel_error(y, outs[0][1]) <= 2e-2
