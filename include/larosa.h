@@ -34,8 +34,9 @@
  *  - Workspace: calls that take `ws` need at least larosa_workspace_bytes(…)
  *    bytes. The workspace must be zero-filled once before first use
  *    (larosa_workspace_init does it on the device); every call leaves it
- *    ready for the next call on the same stream. Calls that share one
- *    workspace must not run concurrently.
+ *    ready for the next call of the same shape (B, d_in, d_out, k) on the
+ *    same stream. To use it for another shape, zero it again first. Calls
+ *    that share one workspace must not run concurrently.
  */
 #ifndef LAROSA_H
 #define LAROSA_H
@@ -179,6 +180,44 @@ int larosa_dense_gemv(const void *x, int act_dtype, const void *W,
  * arithmetic in fp32, rounded to nearest even. f a multiple of 8. */
 int larosa_swiglu(const void *gu, void *h, int64_t B, int64_t f, int dtype,
                   larosa_stream_t stream);
+
+/* ---- The decoder layer around the rotated linears ----------------------
+ * The pages apply the rotated Top-K sparsification to every linear layer of a
+ * pretrained decoder (LaRoSA summary page, 方法详解 · 技术框架) and describe no
+ * other part of the layer. These calls implement the LLaMA-style layer used
+ * by the decoder workloads; they are not steps of the method. fp32 inside,
+ * one rounding to dtype (F32 or BF16) per output. */
+
+/* RMSNorm with unit gain: out[b, :] = h[b, :] / sqrt(mean(h[b, :]²) + eps).
+ * h, out: [B, d]; they may be the same buffer. */
+int larosa_rmsnorm(const void *h, void *out, int64_t B, int64_t d, float eps, int dtype,
+                   larosa_stream_t stream);
+
+/* Rotate-half rotary embedding at position pos: for each head, channel i
+ * (i < d_head/2) pairs with i + d_head/2 and both turn by
+ * pos · theta^(−2i/d_head). Row b of qk holds n_heads query heads, then
+ * n_kv_heads key heads (d_head channels each) at qk + b·qk_stride; the
+ * results go to q_out [B, n_heads·d_head] and k_out [B, n_kv_heads·d_head],
+ * which must not overlap qk. */
+int larosa_rope(const void *qk, int64_t qk_stride, void *q_out, void *k_out, int64_t B,
+                int64_t n_heads, int64_t n_kv_heads, int64_t d_head, int64_t pos, float theta,
+                int dtype, larosa_stream_t stream);
+
+/* Single-query softmax attention of every query head over its key/value
+ * head's T cached positions plus the new token's own key and value:
+ *   out[b, h] = Σ_t softmax_t(q[b,h]·k_t / sqrt(d_head)) · v_t,
+ * with key/value head h / (n_heads / n_kv_heads). q, out: [B, n_heads·128];
+ * the new key and value of token b start at k_new + b·k_stride and
+ * v_new + b·v_stride (n_kv_heads·128 channels each); caches are
+ * [B, n_kv_heads, T, 128] (head-major). d_head must be 128; T <= 16384. */
+int larosa_decode_attention(const void *q, const void *k_new, int64_t k_stride,
+                            const void *v_new, int64_t v_stride, const void *k_cache,
+                            const void *v_cache, void *out, int64_t B, int64_t T,
+                            int64_t n_heads, int64_t n_kv_heads, int64_t d_head, int dtype,
+                            larosa_stream_t stream);
+
+/* Residual add in place: h[i] = h[i] + o[i] for i < n. */
+int larosa_residual_add(void *h, const void *o, int64_t n, int dtype, larosa_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -45,6 +45,12 @@ SIGNATURES = {
     "larosa_dense_gemv": (_c_int, [_c_vp, _c_int, _c_vp, _c_int, _c_vp, _c_i64, _c_i64, _c_i64,
                                    _c_vp, _c_sz, _c_vp]),
     "larosa_swiglu": (_c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_vp]),
+    "larosa_rmsnorm": (_c_int, [_c_vp, _c_vp, _c_i64, _c_i64, ctypes.c_float, _c_int, _c_vp]),
+    "larosa_rope": (_c_int, [_c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                             ctypes.c_float, _c_int, _c_vp]),
+    "larosa_decode_attention": (_c_int, [_c_vp, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp, _c_vp, _c_vp,
+                                         _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_int, _c_vp]),
+    "larosa_residual_add": (_c_int, [_c_vp, _c_vp, _c_i64, _c_int, _c_vp]),
 }
 
 _lib = None
@@ -175,3 +181,29 @@ def larosa_dense_gemv(x, W, y, B: int, d_in: int, d_out: int, ws=None, stream=No
 def larosa_swiglu(gu, h, B: int, f: int, stream=None) -> None:
     _check("larosa_swiglu",
            load().larosa_swiglu(_ptr(gu), _ptr(h), B, f, _dt(gu), _stream(stream)))
+
+
+def larosa_rmsnorm(h, out, B: int, d: int, eps: float = 1e-5, stream=None) -> None:
+    _check("larosa_rmsnorm", load().larosa_rmsnorm(_ptr(h), _ptr(out), B, d, eps, _dt(h),
+                                                   _stream(stream)))
+
+
+def larosa_rope(qk, qk_stride: int, q_out, k_out, B: int, n_heads: int, n_kv_heads: int,
+                d_head: int, pos: int, theta: float = 10000.0, stream=None) -> None:
+    _check("larosa_rope", load().larosa_rope(_ptr(qk), qk_stride, _ptr(q_out), _ptr(k_out), B,
+                                             n_heads, n_kv_heads, d_head, pos, theta, _dt(qk),
+                                             _stream(stream)))
+
+
+def larosa_decode_attention(q, k_new, k_stride: int, v_new, v_stride: int, k_cache, v_cache,
+                            out, B: int, T: int, n_heads: int, n_kv_heads: int,
+                            d_head: int = 128, stream=None) -> None:
+    _check("larosa_decode_attention",
+           load().larosa_decode_attention(_ptr(q), _ptr(k_new), k_stride, _ptr(v_new), v_stride,
+                                          _ptr(k_cache), _ptr(v_cache), _ptr(out), B, T, n_heads,
+                                          n_kv_heads, d_head, _dt(q), _stream(stream)))
+
+
+def larosa_residual_add(h, o, n: int, stream=None) -> None:
+    _check("larosa_residual_add", load().larosa_residual_add(_ptr(h), _ptr(o), n, _dt(h),
+                                                             _stream(stream)))

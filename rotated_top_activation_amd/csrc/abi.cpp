@@ -59,8 +59,7 @@ Layout layout_for(int64_t B, int64_t d_in, int64_t d_out, int64_t k, int w_dt) {
   // The gather's reduction area covers both the sparse call (max_rows =
   // min(d_in, B·k)) and the dense call (max_rows = d_in): the dense plan has
   // at least as many splits.
-  const GatherPlan p = plan_gather(static_cast<int>(B), d_in, d_out, w_dt);
-  L.gather = take(gather_ws_bytes(p, static_cast<int>(B), d_out));
+  L.gather = take(gather_batch_ws_bytes(static_cast<int>(B), d_in, d_out, w_dt));
   L.total = off;
   return L;
 }
@@ -75,8 +74,7 @@ Layout layout_with_fused(int64_t B, int64_t d_in, int64_t d_out, int64_t k, int 
 }
 
 size_t gather_need(int64_t B, int64_t max_rows, int64_t d_out, int w_dt) {
-  return gather_ws_bytes(plan_gather(static_cast<int>(B), max_rows, d_out, w_dt),
-                         static_cast<int>(B), d_out);
+  return gather_batch_ws_bytes(static_cast<int>(B), max_rows, d_out, w_dt);
 }
 
 int check_sizes(int64_t B, int64_t d, int64_t k) {
@@ -218,7 +216,6 @@ int larosa_sparse_gemv(const int32_t *rows, const int32_t *n_rows, int64_t max_r
   if (max_rows < 0) return LAROSA_ERR_INVALID_ARG;
   if (B == 0) return LAROSA_OK;
   if (!rows || !coef || !W_folded || !y) return LAROSA_ERR_INVALID_ARG;
-  if (B > 8) return LAROSA_ERR_SHAPE;
   if (d_out % vec_of(w_dtype)) return LAROSA_ERR_ALIGNMENT;
   if (!aligned16(W_folded) || !aligned16(y)) return LAROSA_ERR_ALIGNMENT;
   const int64_t mr = max_rows < 1 ? 1 : max_rows;
@@ -253,7 +250,6 @@ int larosa_dense_gemv(const void *x, int act_dtype, const void *W, int w_dtype, 
   if (d_in < 1 || d_out < 1) return LAROSA_ERR_SHAPE;
   if (B == 0) return LAROSA_OK;
   if (!x || !W || !y) return LAROSA_ERR_INVALID_ARG;
-  if (B > 8) return LAROSA_ERR_SHAPE;
   if (d_out % vec_of(w_dtype)) return LAROSA_ERR_ALIGNMENT;
   if (!aligned16(x) || !aligned16(W) || !aligned16(y)) return LAROSA_ERR_ALIGNMENT;
   const size_t need = gather_need(B, d_in, d_out, w_dtype);
@@ -288,7 +284,6 @@ int larosa_layer_forward(const void *x, int act_dtype, const void *Qt, int64_t q
   if (d_out < 1) return LAROSA_ERR_SHAPE;
   if (B == 0) return LAROSA_OK;
   if (!x || !Qt || !W_folded || !y) return LAROSA_ERR_INVALID_ARG;
-  if (B > 8) return LAROSA_ERR_SHAPE;
   if (int st = check_rotation(d_in, q_block, w_dtype)) return st;
   if (d_in % vec_of(act_dtype) || d_out % vec_of(w_dtype)) return LAROSA_ERR_ALIGNMENT;
   if (!aligned16(x) || !aligned16(Qt) || !aligned16(W_folded) || !aligned16(y))
@@ -375,6 +370,63 @@ int larosa_swiglu(const void *gu, void *h, int64_t B, int64_t f, int dtype,
   if (!aligned16(gu) || !aligned16(h)) return LAROSA_ERR_ALIGNMENT;
   if (int st = device_status()) return st;
   return launched(launch_swiglu(gu, h, B, f, dtype, stream_of(stream)));
+}
+
+int larosa_rmsnorm(const void *h, void *out, int64_t B, int64_t d, float eps, int dtype,
+                   larosa_stream_t stream) {
+  if (!dtype_ok(dtype)) return LAROSA_ERR_DTYPE;
+  if (B < 0 || B > kMaxB || d < 1 || !(eps >= 0.f)) return LAROSA_ERR_INVALID_ARG;
+  if (B == 0) return LAROSA_OK;
+  if (!h || !out) return LAROSA_ERR_INVALID_ARG;
+  if (int st = device_status()) return st;
+  return launched(launch_rmsnorm(h, out, B, d, eps, dtype, stream_of(stream)));
+}
+
+int larosa_rope(const void *qk, int64_t qk_stride, void *q_out, void *k_out, int64_t B,
+                int64_t n_heads, int64_t n_kv_heads, int64_t d_head, int64_t pos, float theta,
+                int dtype, larosa_stream_t stream) {
+  if (!dtype_ok(dtype)) return LAROSA_ERR_DTYPE;
+  if (B < 0 || B > kMaxB || n_heads < 1 || n_kv_heads < 1 || pos < 0 || !(theta > 0.f))
+    return LAROSA_ERR_INVALID_ARG;
+  if (d_head < 2 || d_head % 2 || qk_stride < (n_heads + n_kv_heads) * d_head)
+    return LAROSA_ERR_SHAPE;
+  if (B == 0) return LAROSA_OK;
+  if (!qk || !q_out || !k_out) return LAROSA_ERR_INVALID_ARG;
+  if (int st = device_status()) return st;
+  return launched(launch_rope(qk, qk_stride, q_out, k_out, B, n_heads, n_kv_heads, d_head, pos,
+                              static_cast<double>(theta), dtype, stream_of(stream)));
+}
+
+int larosa_decode_attention(const void *q, const void *k_new, int64_t k_stride,
+                            const void *v_new, int64_t v_stride, const void *k_cache,
+                            const void *v_cache, void *out, int64_t B, int64_t T,
+                            int64_t n_heads, int64_t n_kv_heads, int64_t d_head, int dtype,
+                            larosa_stream_t stream) {
+  if (!dtype_ok(dtype)) return LAROSA_ERR_DTYPE;
+  if (B < 0 || B > kMaxB || T < 0 || n_heads < 1 || n_kv_heads < 1) return LAROSA_ERR_INVALID_ARG;
+  if (d_head != 128 || n_heads % n_kv_heads || T > 16384) return LAROSA_ERR_SHAPE;
+  if (k_stride < n_kv_heads * d_head || v_stride < n_kv_heads * d_head) return LAROSA_ERR_SHAPE;
+  if ((k_stride * dt_size(dtype)) % 16 || (v_stride * dt_size(dtype)) % 16)
+    return LAROSA_ERR_ALIGNMENT;
+  if (B == 0) return LAROSA_OK;
+  if (!q || !k_new || !v_new || !out || (T > 0 && (!k_cache || !v_cache)))
+    return LAROSA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || !aligned16(out))
+    return LAROSA_ERR_ALIGNMENT;
+  if (int st = device_status()) return st;
+  return launched(launch_decode_attention(q, k_new, k_stride, v_new, v_stride, k_cache, v_cache,
+                                          out, B, T, n_heads, n_kv_heads, dtype,
+                                          stream_of(stream)));
+}
+
+int larosa_residual_add(void *h, const void *o, int64_t n, int dtype, larosa_stream_t stream) {
+  if (!dtype_ok(dtype)) return LAROSA_ERR_DTYPE;
+  if (n < 0) return LAROSA_ERR_INVALID_ARG;
+  if (n == 0) return LAROSA_OK;
+  if (!h || !o) return LAROSA_ERR_INVALID_ARG;
+  if (int st = device_status()) return st;
+  return launched(launch_residual_add(h, o, n, dtype, stream_of(stream)));
 }
 
 }  // extern "C"

@@ -23,6 +23,8 @@ namespace larosa {
 namespace {
 
 constexpr int kRows = 8;  // rows per wave group (loads in flight per lane)
+
+size_t counter_bytes(int tiles) { return (static_cast<size_t>(tiles) * 4 + 255) / 256 * 256; }
 constexpr int kMaxSplitLoads = 16;  // partial sums fetched per round trip
 
 // Largest waves per workgroup for B tokens: the LDS reduction buffer holds
@@ -33,7 +35,7 @@ template <int B, int NW, typename WT, typename OT, int CMODE>
 __global__ __launch_bounds__(NW * 64) void gather_vec_kernel(
     const int32_t *__restrict__ rows, const int32_t *__restrict__ n_rows_dev,
     int64_t max_rows, const void *__restrict__ coef_v,
-    const WT *__restrict__ w, int64_t d_in, int64_t d_out,
+    int64_t coef_stride, const WT *__restrict__ w, int64_t d_in, int64_t d_out,
     OT *__restrict__ y, float *__restrict__ partials,
     uint32_t *__restrict__ counters, int splits, int rows_per_split) {
   constexpr int V = Elt<WT>::kVec;
@@ -87,11 +89,11 @@ __global__ __launch_bounds__(NW * 64) void gather_vec_kernel(
       for (int b = 0; b < B; ++b) {
         float cv;
         if (CMODE == kCoefPacked)
-          cv = static_cast<const float *>(coef_v)[jl * B + b];
+          cv = static_cast<const float *>(coef_v)[jl * coef_stride + b];
         else if (CMODE == kCoefActF32)
-          cv = static_cast<const float *>(coef_v)[b * d_in + ri];
+          cv = static_cast<const float *>(coef_v)[b * coef_stride + ri];
         else
-          cv = bf16_to_f32(static_cast<const uint16_t *>(coef_v)[b * d_in + ri]);
+          cv = bf16_to_f32(static_cast<const uint16_t *>(coef_v)[b * coef_stride + ri]);
         c[u][b] = ok[u] ? cv : 0.f;
       }
     }
@@ -183,18 +185,25 @@ __global__ __launch_bounds__(NW * 64) void gather_vec_kernel(
 
 template <int B, int NW, typename WT, typename OT, int CMODE>
 hipError_t launch_nw(const GatherArgs &a, const GatherPlan &p, hipStream_t s) {
-  float *partials = static_cast<float *>(a.ws);
-  uint32_t *counters = nullptr;
-  if (p.splits > 1) {
-    const size_t pbytes = static_cast<size_t>(p.splits) * B * a.d_out * sizeof(float);
-    counters = reinterpret_cast<uint32_t *>(static_cast<char *>(a.ws) + ((pbytes + 255) / 256) * 256);
-  }
+  // Token group [b0, b0 + B) of a batch of a.B: coefficients and outputs are
+  // offset to the group; the stride between tokens (activation coefficients)
+  // or between rows (packed coefficients) is that of the whole batch.
+  const int64_t b0 = a.b0;
+  const int64_t cstride = a.coef_mode == kCoefPacked ? a.B : a.d_in;
+  const char *coef = static_cast<const char *>(a.coef) +
+                     (a.coef_mode == kCoefPacked ? b0 * 4
+                                                 : b0 * a.d_in * (a.coef_mode == kCoefActF32 ? 4 : 2));
+  char *yb = static_cast<char *>(a.y) + b0 * a.d_out * (a.y_dt == kF32 ? 4 : 2);
+  // Counters first (their place depends only on the column tiles, so every
+  // token group of a batch finds them at zero), partial sums after them.
+  uint32_t *counters = static_cast<uint32_t *>(a.ws);
+  float *partials = reinterpret_cast<float *>(static_cast<char *>(a.ws) + counter_bytes(p.tiles));
   dim3 grid(p.tiles, p.splits);
   dim3 block(NW * kWave);
   hipLaunchKernelGGL((gather_vec_kernel<B, NW, WT, OT, CMODE>), grid, block, 0, s,
-                     a.rows, a.n_rows, a.max_rows, a.coef,
+                     a.rows, a.n_rows, a.max_rows, static_cast<const void *>(coef), cstride,
                      static_cast<const WT *>(a.w), a.d_in, a.d_out,
-                     static_cast<OT *>(a.y), partials, counters, p.splits,
+                     reinterpret_cast<OT *>(yb), partials, counters, p.splits,
                      p.rows_per_split);
   return hipGetLastError();
 }
@@ -269,22 +278,40 @@ GatherPlan plan_gather(int B, int64_t max_rows, int64_t d_out, int w_dt) {
 size_t gather_ws_bytes(const GatherPlan &p, int B, int64_t d_out) {
   if (p.splits <= 1) return 0;
   const size_t pbytes = static_cast<size_t>(p.splits) * B * d_out * sizeof(float);
-  return ((pbytes + 255) / 256) * 256 + ((static_cast<size_t>(p.tiles) * 4 + 255) / 256) * 256;
+  return counter_bytes(p.tiles) + pbytes;
+}
+
+size_t gather_batch_ws_bytes(int B, int64_t max_rows, int64_t d_out, int w_dt) {
+  size_t need = 0;
+  for (int nb = 1; nb <= (B < 8 ? B : 8); ++nb) {
+    const size_t n = gather_ws_bytes(plan_gather(nb, max_rows, d_out, w_dt), nb, d_out);
+    need = n > need ? n : need;
+  }
+  return need;
 }
 
 hipError_t launch_gather(const GatherArgs &a, hipStream_t s) {
-  const GatherPlan p = plan_gather(a.B, a.max_rows, a.d_out, a.w_dt);
-  switch (a.B) {
-    case 1: return dispatch_types<1>(a, p, s);
-    case 2: return dispatch_types<2>(a, p, s);
-    case 3: return dispatch_types<3>(a, p, s);
-    case 4: return dispatch_types<4>(a, p, s);
-    case 5: return dispatch_types<5>(a, p, s);
-    case 6: return dispatch_types<6>(a, p, s);
-    case 7: return dispatch_types<7>(a, p, s);
-    case 8: return dispatch_types<8>(a, p, s);
-    default: return hipErrorInvalidValue;
+  // Up to eight tokens per launch; larger batches run in groups of eight
+  // over the same row list (each group re-reads the rows).
+  for (int b0 = 0; b0 < a.B; b0 += 8) {
+    GatherArgs g = a;
+    g.b0 = b0;
+    const int nb = a.B - b0 < 8 ? a.B - b0 : 8;
+    const GatherPlan p = plan_gather(nb, a.max_rows, a.d_out, a.w_dt);
+    hipError_t e;
+    switch (nb) {
+      case 1: e = dispatch_types<1>(g, p, s); break;
+      case 2: e = dispatch_types<2>(g, p, s); break;
+      case 3: e = dispatch_types<3>(g, p, s); break;
+      case 4: e = dispatch_types<4>(g, p, s); break;
+      case 5: e = dispatch_types<5>(g, p, s); break;
+      case 6: e = dispatch_types<6>(g, p, s); break;
+      case 7: e = dispatch_types<7>(g, p, s); break;
+      default: e = dispatch_types<8>(g, p, s); break;
+    }
+    if (e != hipSuccess) return e;
   }
+  return hipSuccess;
 }
 
 }  // namespace larosa

@@ -40,6 +40,9 @@ GatherPlan plan_gather(int B, int64_t max_rows, int64_t d_out, int w_dt);
 // Workspace for the split-row reduction: partial sums, then one counter per
 // column tile. Counters must start at zero; the kernel leaves them at zero.
 size_t gather_ws_bytes(const GatherPlan &p, int B, int64_t d_out);
+// Workspace for a launch_gather call over a batch of B tokens (groups of at
+// most eight tokens run one after another and reuse the area).
+size_t gather_batch_ws_bytes(int B, int64_t max_rows, int64_t d_out, int w_dt);
 
 struct GatherArgs {
   const int32_t *rows;     // NULL: row j is row j
@@ -52,7 +55,8 @@ struct GatherArgs {
   int64_t d_in, d_out;
   void *y;
   int y_dt;
-  int B;
+  int B;                   // tokens in the batch
+  int b0 = 0;              // first token of this launch's group (set internally)
   void *ws;                // gather_ws_bytes(plan) bytes
 };
 hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
@@ -92,5 +96,17 @@ hipError_t launch_fold(const void *qt, int64_t qb, const void *w, void *wf,
 hipError_t launch_swiglu(const void *gu, void *h, int64_t B, int64_t f, int dt,
                          hipStream_t s);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
+
+// --- decoder layer around the rotated linears ---
+hipError_t launch_rmsnorm(const void *h, void *out, int64_t B, int64_t d, float eps, int dt,
+                          hipStream_t s);
+hipError_t launch_rope(const void *qk, int64_t stride, void *q_out, void *k_out, int64_t B,
+                       int64_t n_heads, int64_t n_kv, int64_t dh, int64_t pos, double theta,
+                       int dt, hipStream_t s);
+hipError_t launch_decode_attention(const void *q, const void *k_new, int64_t k_stride,
+                                   const void *v_new, int64_t v_stride, const void *kc,
+                                   const void *vc, void *out, int64_t B, int64_t Tlen,
+                                   int64_t n_heads, int64_t n_kv, int dt, hipStream_t s);
+hipError_t launch_residual_add(void *h, const void *o, int64_t n, int dt, hipStream_t s);
 
 }  // namespace larosa

@@ -15,23 +15,28 @@ from .workloads import to_torch
 class RotatedLinear:
     """One rotated sparse linear on the GPU.
 
-    q_blocks: packed rotation [d_in // q_block, q_block, q_block] (float64
-    values of the stored dtype); w: [d_in, d_out] (float64 values of the
-    stored dtype). Keeps Q, the prepared Qt, W and the folded W'.
+    q_blocks: packed rotation [d_in // q_block, q_block, q_block]; w:
+    [d_in, d_out]; either float64 arrays of stored values or device tensors
+    of the storage dtype. Keeps Q, the prepared Qt, W (unless keep_w is
+    False) and the folded W'.
     """
 
-    def __init__(self, q_blocks: np.ndarray, w: np.ndarray, dtype: str, k: int,
-                 device: str = "cuda", keep_w: bool = True):
+    def __init__(self, q_blocks, w, dtype: str, k: int, device: str = "cuda",
+                 keep_w: bool = True):
+        import torch
         nb, qb, _ = q_blocks.shape
         self.d_in = nb * qb
         self.q_block = qb
         self.d_out = w.shape[1]
         self.k = k
         self.dtype = dtype
-        self.Q = to_torch(q_blocks.reshape(self.d_in, qb), dtype, device)
+        if isinstance(q_blocks, torch.Tensor):  # already on the device
+            self.Q = q_blocks.reshape(self.d_in, qb).contiguous()
+        else:
+            self.Q = to_torch(q_blocks.reshape(self.d_in, qb), dtype, device)
         self.Qt = self.Q.new_empty(self.Q.shape)
         _lib.larosa_prepare_rotation(self.Q, self.Qt, self.d_in, qb)
-        W = to_torch(w, dtype, device)
+        W = w.contiguous() if isinstance(w, torch.Tensor) else to_torch(w, dtype, device)
         self.Wf = W.new_empty(W.shape)
         _lib.larosa_fold_weights(self.Qt, qb, W, self.Wf, self.d_in, self.d_out)
         self.W = W if keep_w else None

@@ -265,3 +265,99 @@ def to_torch(a: np.ndarray, dtype: str, device="cuda"):
     elif dtype != "f32":
         raise ValueError(dtype)
     return t.to(device)
+
+
+# ----------------------------------------------------------------------------
+# Decoder-scale workloads. Drawing tens of fresh 4096² random orthogonal
+# matrices and gigabytes of Gaussian weights per run would dominate the test
+# time, so a layer's tensors are seeded signed permutations of one draw per
+# role: for a random orthogonal Q and permutation/sign matrices P, D, the
+# matrix P·Q·D is again random orthogonal with the same (Haar) law, and a
+# row/column permutation of an i.i.d. Gaussian matrix is again i.i.d.
+# Gaussian. The permutations are inputs like everything else here.
+
+@dataclasses.dataclass(frozen=True)
+class DecoderShape:
+    """A LLaMA-shaped decoder layer."""
+    d: int = 4096
+    f: int = 11008
+    n_heads: int = 32
+    n_kv_heads: int = 32
+    d_head: int = 128
+    ctx: int = 2048
+    q2_block: int = 2752
+    w_std: float = 0.02
+
+    @property
+    def qkv_out(self) -> int:
+        return (self.n_heads + 2 * self.n_kv_heads) * self.d_head
+
+
+LLAMA7B = DecoderShape()
+
+
+def base_decoder_tensors(cfg: int, shape: DecoderShape, dtype: str = "bf16",
+                         run_seed: int = 0) -> dict:
+    """One draw per role: rotations (packed blocks) and Gaussian weights."""
+    d, f = shape.d, shape.f
+    out = {
+        "q_attn": rotation(cfg, 0, "attn_in", d, d, dtype, run_seed),
+        "q_o": rotation(cfg, 0, "o_in", d, d, dtype, run_seed),
+        "q_mlp": rotation(cfg, 0, "mlp_in", d, d, dtype, run_seed),
+        "q_down": rotation(cfg, 0, "down_in", f, shape.q2_block, dtype, run_seed),
+        "w_qkv": gaussian_weight(cfg, 0, "attn_in", d, shape.qkv_out, shape.w_std, dtype, run_seed),
+        "w_o": gaussian_weight(cfg, 0, "o_in", d, d, shape.w_std, dtype, run_seed),
+        "w_gu": np.concatenate(
+            [gaussian_weight(cfg, 0, "mlp_in", d, f, shape.w_std, dtype, run_seed, 0),
+             gaussian_weight(cfg, 0, "mlp_in", d, f, shape.w_std, dtype, run_seed, 1)], axis=1),
+        "w_down": gaussian_weight(cfg, 0, "down_in", f, d, shape.w_std, dtype, run_seed),
+    }
+    return out
+
+
+ROLE_TENSORS = {"attn_in": ("q_attn", "w_qkv"), "o_in": ("q_o", "w_o"),
+                "mlp_in": ("q_mlp", "w_gu"), "down_in": ("q_down", "w_down")}
+
+
+def layer_tensor_indices(cfg: int, layer: int, role: str, shape: DecoderShape,
+                         run_seed: int = 0):
+    """For layer `layer` and `role`: (rot_rows, rot_signs, w_rows, w_cols), the
+    index arrays that turn the role's base draw into this layer's tensors:
+    Q_l = base[:, rot_rows, :] · diag(rot_signs) per block, W_l = base[w_rows][:, w_cols].
+    Layer 0 uses the base draw itself."""
+    d_in = shape.f if role == "down_in" else shape.d
+    qb = shape.q2_block if role == "down_in" else shape.d
+    n_out = {"attn_in": shape.qkv_out, "o_in": shape.d, "mlp_in": 2 * shape.f,
+             "down_in": shape.d}[role]
+    if layer == 0:
+        return (np.arange(qb), np.ones(qb), np.arange(d_in), np.arange(n_out))
+    rng = rng_for(cfg, layer, role, "perm", run_seed)
+    rot_rows, rot_signs = signed_permutation(rng, qb)
+    return rot_rows, rot_signs, rng.permutation(d_in), rng.permutation(n_out)
+
+
+def layer_rotation(base_q: np.ndarray, idx) -> np.ndarray:
+    rot_rows, rot_signs = idx[0], idx[1]
+    return base_q[:, rot_rows, :] * rot_signs[None, None, :]
+
+
+def layer_weight(base_w: np.ndarray, idx) -> np.ndarray:
+    return base_w[idx[2]][:, idx[3]]
+
+
+def kv_cache_base(cfg: int, shape: DecoderShape, dtype: str = "bf16", run_seed: int = 0):
+    """One seeded N(0,1) key and value cache [n_kv_heads, ctx, d_head]; token b
+    of layer l reads it rolled by a seeded offset along the positions."""
+    rng = rng_for(cfg, 0, "attn_in", "kv", run_seed)
+    k = rng.standard_normal((shape.n_kv_heads, shape.ctx, shape.d_head), dtype=np.float32)
+    v = rng.standard_normal((shape.n_kv_heads, shape.ctx, shape.d_head), dtype=np.float32)
+    return quantize(k, dtype), quantize(v, dtype)
+
+
+def kv_offsets(cfg: int, layer: int, batch: int, ctx: int, run_seed: int = 0) -> np.ndarray:
+    return rng_for(cfg, layer, "o_in", "kv", run_seed).integers(0, ctx, size=batch)
+
+
+def decoder_hidden(cfg: int, batch: int, d: int, dtype: str = "bf16", run_seed: int = 0):
+    """The decode step's input hidden state: heavy-tailed channel scales."""
+    return heavy_tailed_activations(cfg, 0, "attn_in", batch, d, dtype, run_seed)

@@ -90,7 +90,7 @@ def test_single_token_linear_shapes(mode, d, qb, n, sp):
     check_linear(lin, x, q, mode=mode)
 
 
-@pytest.mark.parametrize("B,sp", [(2, 25), (4, 40), (8, 50), (3, 40)])
+@pytest.mark.parametrize("B,sp", [(2, 25), (4, 40), (8, 50), (3, 40), (16, 40), (16, 25)])
 def test_batched_linear_union_4096_to_qkv(B, sp):
     d, n = 4096, 12288
     case = wl.LinearCase(cfg=3, batch=B, d_in=d, d_out=n, q_block=d, sparsity_pct=sp,
@@ -211,3 +211,13 @@ def test_fused_and_unfused_share_one_workspace():
     for mode, y, idx in outs:
         np.testing.assert_array_equal(idx, outs[0][2])
         assert ref.rel_error(y, outs[0][1]) <= 2e-2
+
+
+@pytest.mark.parametrize("B,d,qb,n", [(32, 2048, 512, 2056), (64, 1024, 1024, 1032),
+                                      (11, 4096, 4096, 520)])
+def test_large_batches(B, d, qb, n):
+    case = wl.LinearCase(cfg=5, batch=B, d_in=d, d_out=n, q_block=qb, sparsity_pct=50,
+                         dtype="bf16", role="mlp_in")
+    x, q, w = wl.linear_case_inputs(case, w_std=0.01)
+    lin = RotatedLinear(q, w, "bf16", case.k)
+    check_linear(lin, x, q)
