@@ -31,6 +31,34 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+COPY_BYTES = 512 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "gather_vec_kernel": ["gather.hip", "common.hpp"],
+    "fused_linear_kernel": ["fused.hip", "select_core.hpp", "common.hpp"],
+}
+
+
+def source_digest(kernel: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "rotated_top_activation_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed counter runs, or None when the
+    kernel's sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256") != source_digest(kernel):
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def parse():
@@ -44,7 +72,7 @@ def parse():
     p.add_argument("--q2-block", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--kernel-only", choices=["", "gather", "step"], default="",
+    p.add_argument("--kernel-only", choices=["", "gather", "fused1", "step", "copy"], default="",
                    help="only launch that work (for profiler runs)")
     return p.parse_args()
 
@@ -65,6 +93,15 @@ def main():
     _lib.load()
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
+    if a.kernel_only == "copy":
+        # A plain device copy of a known size (512 MiB read + 512 MiB written
+        # per launch): the calibration for the HBM traffic counters.
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(a.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        return
     case = wl.llama7b_mlp(batch=1, sparsity_pct=a.sparsity, q2_block=a.q2_block or None)
     t0 = time.time()
     x, q1, wgu, q2, wd = wl.mlp_case_inputs(case)
@@ -143,7 +180,8 @@ def main():
             graph_ms[name] = timed(lambda i, g=gs: g[i % copies].replay(), a.steps, a.warmup)
             step_ms[name] = min(eager_ms[name], graph_ms[name])
 
-    # The dominant kernel alone: the gate|up gather product over the kept rows.
+    # The dominant kernels alone, gate|up (the larger linear): the unfused
+    # gather product over the kept rows, and the fused rotate-select-gather.
     xr1 = torch.empty((1, d), dtype=torch.float32, device=dev)
     idx1 = torch.empty((1, case.k1), dtype=torch.int32, device=dev)
     val1 = torch.empty((1, case.k1), dtype=torch.float32, device=dev)
@@ -153,14 +191,23 @@ def main():
     def gather(i):
         _lib.larosa_sparse_gemv(idx1, None, case.k1, val1, wf1[i % copies], gu, 1, d, 2 * f,
                                 ws=ws1)
-    if a.kernel_only == "gather":
+
+    def fused1(i):
+        c = i % copies
+        _lib.larosa_layer_forward(x_d, qt1[c], l1.q_block, wf1[c], 1, d, 2 * f, case.k1, gu,
+                                  mode=_lib.FUSED, ws=ws1)
+    if a.kernel_only in ("gather", "fused1"):
+        fn = gather if a.kernel_only == "gather" else fused1
         for i in range(a.steps):
-            gather(i)
+            fn(i)
         torch.cuda.synchronize()
         return
     gather_ms = timed(gather, a.steps, a.warmup)
     gather_bytes = case.k1 * 2 * f * 2 + case.k1 * 8 + 2 * f * 2
     gather_gbs = gather_bytes / (gather_ms * 1e-3) / 1e9
+    fused1_ms = timed(fused1, a.steps, a.warmup)
+    fused1_bytes = l1.Qt.numel() * 2 + d * 2 + case.k1 * 2 * f * 2 + 2 * f * 2
+    fused1_gbs = fused1_bytes / (fused1_ms * 1e-3) / 1e9
 
     # Dense product over all rows of the same folded weight.
     def dense(i):
@@ -197,6 +244,14 @@ def main():
     dense_mlp_bytes = (d * 2 * f + f * d) * 2
     best = min(step_ms, key=step_ms.get)
     ms = step_ms[best]
+    kernels = {
+        "gather_vec_kernel": dict(achieved=gather_gbs, bytes=gather_bytes, us=gather_ms * 1e3,
+                                  what="unfused gather product, gate|up kept rows"),
+        "fused_linear_kernel": dict(achieved=fused1_gbs, bytes=fused1_bytes, us=fused1_ms * 1e3,
+                                    what="fused rotate-select-gather, gate|up"),
+    }
+    dom = "fused_linear_kernel" if best == "fused" else "gather_vec_kernel"
+    kd = kernels[dom]
 
     cpu = None
     if not a.no_cpu_baseline:
@@ -223,10 +278,10 @@ def main():
             "launch": "hip graph" if graph_ms.get(best, 1e9) <= eager_ms.get(best, 1e9) else "eager",
         },
         "roofline": {
-            "bound": "hbm", "kernel": "gather_vec_kernel (gate|up rows)",
-            "achieved": round(gather_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(gather_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-            "bytes_per_launch": gather_bytes, "avg_us": round(gather_ms * 1e3, 3),
+            "bound": "hbm", "kernel": f"{dom} ({kd['what']})",
+            "achieved": round(kd["achieved"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(kd["achieved"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dom),
+            "bytes_per_launch": kd["bytes"], "avg_us": round(kd["us"], 3),
         },
         "cpu_baseline": cpu,
         "detail": {
@@ -237,6 +292,9 @@ def main():
             "mlp_dense_weight_bytes": dense_mlp_bytes,
             "mlp_achieved_GBs": round(sparse_bytes / (ms * 1e-3) / 1e9, 1),
             "stage_us": {k: round(v * 1e3, 2) for k, v in stage.items()},
+            "kernels": {k: {"achieved_GBs": round(v["achieved"], 1), "bytes_per_launch": v["bytes"],
+                            "avg_us": round(v["us"], 3), "frac": round(v["achieved"] / HBM_PEAK_GBS, 4),
+                            "traffic": measured_traffic(k)} for k, v in kernels.items()},
             "gate_up_dense_us": {"larosa_dense_gemv": round(dense_ms * 1e3, 2),
                                  "torch.matmul": round(torch_ms * 1e3, 2)},
             "gate_up_dense_GBs": round(dense_bytes / (dense_ms * 1e-3) / 1e9, 1),
