@@ -6,24 +6,39 @@
 // Every workgroup of the grid is resident at once (the grid is sized from
 // the occupancy of this kernel), and the phases hand over through memory:
 //   1. rotate: output channel j is owned by one wave, which writes x_rot[j]
-//      with an agent-scope atomic store;
-//   2. arrival: hierarchical counters (16 groups, then one) find the last
-//      workgroup to finish rotating. That workgroup alone selects: an exact
-//      radix select over all of x_rot gives the K-th key T, and a scan gives
-//      the index cut-off among channels equal to T (lower index first). It
-//      then writes (flag, T, cut-off) as one 64-bit word into every other
-//      workgroup's own release line, so no two workgroups poll the same
-//      address;
-//   3. gather: a work unit is (column tile, channel range). It reads its
-//      range of x_rot, keeps channel i iff key > T or (key == T and i <=
-//      cut-off), lists those rows in LDS, streams them from W', and the last
-//      unit of a tile to finish adds the tile's partial sums in split order.
-// All counters and flags return to zero, so the workspace is ready for the
-// next call. Waits are bounded: a wait that runs past the limit sets an
-// error word in the workspace and continues instead of hanging.
+//      with an agent-scope atomic store. Every workgroup takes part.
+//   2. select: workgroup 0 is the selector. It waits until the other
+//      workgroups have counted themselves in (16 group counters) and tells
+//      them so, then copies the magnitude keys of x_rot into LDS and runs an
+//      exact radix select over them. After the first digit it already knows
+//      the bin B0 (key bits 30..20) holding the K-th largest key: every
+//      channel in a higher bin is kept whatever the rest of the select
+//      finds. It releases that preliminary rule at once, then finishes the
+//      select (the K-th key T, and the index cut-off among channels equal to
+//      T, lower index first) and releases the exact rule. Each release is
+//      one 64-bit word written into every workgroup's own 128-byte line, so
+//      no two workgroups poll the same address. The selector's code runs
+//      once per launch on one workgroup, so it is kept short (rolled loops
+//      over LDS) to limit cold instruction fetches.
+//   3. gather (workgroups 1..G-1): a work unit is (column tile, channel
+//      range). A workgroup loads its first unit's slice of x_rot as soon as
+//      every rotation is in, and lists on the preliminary rule the channels
+//      of the range above bin B0 and those inside it; it streams the first
+//      list's rows of W' at once, and appends the kept channels of B0 to the
+//      list when the exact rule is in (the first wave to run out of certain
+//      rows does that for the workgroup). The last unit of a tile to finish
+//      adds the tile's partial sums in split order.
+// The bin-B0 rows go last in every unit's accumulation whatever the timing,
+// so results do not depend on when the exact rule arrives. All counters and
+// flags return to zero, so the workspace is ready for the next call. Waits
+// are bounded: a wait that runs past the limit sets an error word in the
+// workspace and continues instead of hanging.
 #include "common.hpp"
 #include "launch.hpp"
 #include "select_core.hpp"
+
+#include <cstddef>
+#include <mutex>
 
 namespace larosa {
 namespace {
@@ -32,47 +47,251 @@ constexpr int kFT = 512;              // threads per workgroup
 constexpr int kFW = kFT / kWave;      // waves per workgroup
 constexpr int kFRows = 8;             // rows per wave group
 constexpr int kFSplitLoads = 32;      // partial sums fetched per round trip
-constexpr int kGroups = 16;           // arrival sub-counters
+constexpr int kGroups = 16;           // arrival counters
+constexpr int kChunks = kFusedMaxD / (4 * kFT);  // 16-byte key chunks per selector thread
 constexpr uint32_t kSpinLimit = 1u << 22;
 
 // Word offsets inside the synchronisation block (each on its own 128-byte
-// line): [0] top arrival count, [32·(1+g)] arrival count of group g, [32·17]
-// error word.
+// line): [32·(1+g)] arrival count of group g, [32·17] error word.
 constexpr int kErrWord = 32 * (kGroups + 1);
 
-struct FusedSmem {
-  SelectSmem<kFT> sel;
+// Release words: bit 63 marks a word, bits 62..61 its stage.
+//   stage 0 (all rotations are in): nothing else
+//   stage 1 (preliminary rule):     bits 10..0 = B0
+//   stage 2 (exact rule):           bits 46..16 = T, bits 15..0 = cut-off
+//                                   (0xFFFF: every channel equal to T)
+constexpr uint64_t kWord = 1ull << 63;
+constexpr int kStageShift = 61;
+constexpr uint32_t kCutAll = 0xFFFFu;
+
+struct WorkerSmem {
   float red[kFW][kWave * 8];
-  int32_t rows[kFusedMaxRowsPerUnit];
+  int32_t rows[kFusedMaxRowsPerUnit];     // kept rows: certain ones, then bin B0's
   float coef[kFusedMaxRowsPerUnit];
-  uint32_t T, cut;
-  int flag;
+  int32_t crow[kFusedMaxRowsPerUnit];     // channels of bin B0
+  float ccoef[kFusedMaxRowsPerUnit];
+  uint32_t wave_tot[kFW];
 };
 
-// Arrival at the grid barrier; true in exactly one workgroup (the last).
-__device__ __forceinline__ bool arrive_last(uint32_t *sync, int *s_flag) {
-  const uint32_t G = gridDim.x;
-  __builtin_amdgcn_s_waitcnt(0);  // this workgroup's stores and atomics have completed
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t g = blockIdx.x % kGroups;
-    const uint32_t members = (G - g + kGroups - 1) / kGroups;
-    const uint32_t groups = G < kGroups ? G : kGroups;
-    bool last = false;
-    const uint32_t prev = __hip_atomic_fetch_add(&sync[32 * (1 + g)], 1u, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    if (prev == members - 1) {
-      const uint32_t top =
-          __hip_atomic_fetch_add(&sync[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      last = top == groups - 1;
-    }
-    *s_flag = last;
-  }
-  __syncthreads();
-  return *s_flag != 0;
+struct SelectorSmem {
+  SelectSmem<kFT> sel;
+  alignas(16) uint32_t key[4];  // d keys (the launch's dynamic LDS extends the array)
+};
+
+struct FusedSmem {
+  uint32_t ns, nc;          // certain rows / bin-B0 channels of the unit
+  uint32_t claim, tail;     // bin-B0 compaction: claimed; done (count + 1)
+  uint32_t last;            // this unit is the last of its tile
+  uint32_t b0, T, cut, stage;
+  alignas(16) union {
+    SelectorSmem s;
+    WorkerSmem w;
+  };
+};
+
+// LDS bytes of one workgroup: the worker's lists or the selector's
+// histogram and keys, whichever is larger.
+size_t fused_lds_bytes(int d) {
+  const size_t sel = offsetof(FusedSmem, s) + offsetof(SelectorSmem, key) + 4 * static_cast<size_t>(d);
+  return sel > sizeof(FusedSmem) ? sel : sizeof(FusedSmem);
 }
 
-template <int EMAX, typename T>
+__device__ __forceinline__ uint32_t lds_load(uint32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_store(uint32_t *p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Decodes a release word into sm.
+__device__ __forceinline__ void take_word(uint64_t w, FusedSmem &sm) {
+  const uint32_t stage = static_cast<uint32_t>(w >> kStageShift) & 3u;
+  if (stage == 2) {
+    const uint32_t T = static_cast<uint32_t>(w >> 16) & 0x7FFFFFFFu;
+    const uint32_t c = static_cast<uint32_t>(w) & 0xFFFFu;
+    sm.T = T;
+    sm.cut = c == kCutAll ? 0xFFFFFFFFu : c;
+    sm.b0 = T >> 20;
+  } else if (stage == 1) {
+    sm.b0 = static_cast<uint32_t>(w) & 0x7FFu;
+  }
+  lds_store(&sm.stage, stage);
+}
+
+// Polls this workgroup's release line until a word of at least `stage`
+// arrives (bounded); decodes it into sm.
+__device__ __forceinline__ void wait_word(uint64_t *line, uint32_t stage, uint32_t *err,
+                                          FusedSmem &sm) {
+  uint32_t spins = 0;
+  uint64_t w;
+  for (;;) {
+    w = __hip_atomic_load(line, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((w & kWord) && (static_cast<uint32_t>(w >> kStageShift) & 3u) >= stage) break;
+    __builtin_amdgcn_s_sleep(1);
+    if (++spins > kSpinLimit) {
+      __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      w = kWord | (2ull << kStageShift);  // T = 0, cut = 0: keeps every channel of a unit
+      break;
+    }
+  }
+  take_word(w, sm);
+}
+
+__device__ __forceinline__ void release_all(uint64_t *flags, uint64_t w) {
+  for (uint32_t b = 1 + threadIdx.x; b < gridDim.x; b += kFT)
+    __hip_atomic_store(&flags[b * 16], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One radix pass over the selector's LDS keys (rolled loop: 16-byte reads,
+// consecutive across the workgroup).
+__device__ __forceinline__ uint32_t selector_pass(int pass, const uint32_t *key, int d,
+                                                  uint32_t &prefix, uint32_t &pmask,
+                                                  uint32_t &krem, SelectSmem<kFT> &sel) {
+  radix_clear<kFT>(sel);
+  __syncthreads();
+#pragma unroll 1
+  for (int i = 4 * static_cast<int>(threadIdx.x); i < d; i += 4 * kFT) {
+    const uint4 q = *reinterpret_cast<const uint4 *>(key + i);
+    radix_count<kFT>(q.x, pass, prefix, pmask, sel);
+    radix_count<kFT>(q.y, pass, prefix, pmask, sel);
+    radix_count<kFT>(q.z, pass, prefix, pmask, sel);
+    radix_count<kFT>(q.w, pass, prefix, pmask, sel);
+  }
+  __syncthreads();
+  return radix_resolve<kFT>(pass, prefix, pmask, krem, sel);
+}
+
+// Selector (workgroup 0): waits for the arrivals, selects, releases.
+__device__ __forceinline__ void select_and_release(const float *x_rot, int d, int k,
+                                                   uint32_t *sync, uint64_t *flags,
+                                                   int32_t *idx_out, FusedSmem &sm) {
+  const int t = threadIdx.x;
+  const uint32_t G = gridDim.x;
+  SelectSmem<kFT> &sel = sm.s.sel;
+  uint32_t *key = sm.s.key;
+  if (t < kWave) {
+    uint32_t spins = 0;
+    for (;;) {
+      const uint32_t c = t < kGroups ? __hip_atomic_load(&sync[32 * (1 + t)], __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT)
+                                     : 0u;
+      if (wave_sum_u32(c) >= G - 1) break;
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kSpinLimit) {
+        if (t == 0)
+          __hip_atomic_store(&sync[kErrWord], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+    // every worker has arrived: the counters are free for the next call
+    if (t < kGroups)
+      __hip_atomic_store(&sync[32 * (1 + t)], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  release_all(flags, kWord);  // stage 0: x_rot is complete
+  // the acquire fence makes the workers' x_rot stores visible to ordinary
+  // (vector) loads here
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  {
+    // keys into LDS: every 16-byte load in flight before any is used
+    float4 f[kChunks];
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int i = 4 * (c * kFT + t);
+      if (i < d) f[c] = *reinterpret_cast<const float4 *>(x_rot + i);
+    }
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int i = 4 * (c * kFT + t);
+      if (i < d)
+        *reinterpret_cast<uint4 *>(key + i) =
+            make_uint4(__float_as_uint(f[c].x) & 0x7FFFFFFFu, __float_as_uint(f[c].y) & 0x7FFFFFFFu,
+                       __float_as_uint(f[c].z) & 0x7FFFFFFFu, __float_as_uint(f[c].w) & 0x7FFFFFFFu);
+    }
+  }
+
+  // first digit: bin B0 of the K-th largest key; release the preliminary rule
+  uint32_t prefix = 0, pmask = kNoKey, krem = static_cast<uint32_t>(k);
+  selector_pass(0, key, d, prefix, pmask, krem, sel);  // its first barrier covers the key stores
+  release_all(flags, kWord | (1ull << kStageShift) | (prefix >> 20));
+
+  // remaining digits: T, and the count of keys equal to T
+  uint32_t n_eq = 0;
+#pragma unroll 1
+  for (int pass = 1; pass < 3; ++pass) n_eq = selector_pass(pass, key, d, prefix, pmask, krem, sel);
+  const uint32_t T = prefix;
+
+  // Thread t owns the E consecutive channels [t·E, t·E + E) for the index-
+  // order steps below.
+  const int E = (d + kFT - 1) / kFT;
+  const int i0 = t * E;
+  const int i1 = i0 + E < d ? i0 + E : d;
+  // index cut-off among the channels equal to T: the krem-th of them
+  uint32_t cut = kCutAll;
+  if (n_eq != krem) {
+    uint32_t eq = 0;
+#pragma unroll 1
+    for (int i = i0; i < i1; ++i) eq += key[i] == T;
+    const uint32_t incl = block_incl_scan<kFT>(eq, sel.wave_tot);
+    uint32_t r = incl - eq;
+    if (r < krem && incl >= krem) {
+#pragma unroll 1
+      for (int i = i0; i < i1; ++i)
+        if (key[i] == T && ++r == krem) sel.bin = static_cast<uint32_t>(i);
+    }
+    __syncthreads();
+    cut = sel.bin;
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // earlier words are out first
+  release_all(flags, kWord | (2ull << kStageShift) | (static_cast<uint64_t>(T) << 16) | cut);
+
+  // optional copy of the kept indices, ascending
+  if (idx_out) {
+    const uint32_t cut32 = cut == kCutAll ? 0xFFFFFFFFu : cut;
+    uint32_t n = 0;
+#pragma unroll 1
+    for (int i = i0; i < i1; ++i)
+      n += key[i] > T || (key[i] == T && static_cast<uint32_t>(i) <= cut32);
+    uint32_t p = block_incl_scan<kFT>(n, sel.wave_tot) - n;
+#pragma unroll 1
+    for (int i = i0; i < i1; ++i)
+      if (key[i] > T || (key[i] == T && static_cast<uint32_t>(i) <= cut32)) idx_out[p++] = i;
+  }
+}
+
+// Streams rows[base .. base + kFRows) (clamped to n) of W' into acc.
+template <typename T>
+__device__ __forceinline__ void gather_group(const T *__restrict__ wf, int64_t d_out, int64_t col,
+                                             const int32_t *rows, const float *coef, int base,
+                                             int n, float (&acc)[Elt<T>::kVec]) {
+  constexpr int V = Elt<T>::kVec;
+  int rr[kFRows];
+  float c[kFRows];
+#pragma unroll
+  for (int r = 0; r < kFRows; ++r) {
+    const int jl = base + r < n ? base + r : n - 1;
+    rr[r] = __builtin_amdgcn_readfirstlane(rows[jl]);
+    c[r] = base + r < n ? coef[jl] : 0.f;
+  }
+  uint4 q[kFRows];
+#pragma unroll
+  for (int r = 0; r < kFRows; ++r) q[r] = load16(wf + static_cast<int64_t>(rr[r]) * d_out + col);
+#pragma unroll
+  for (int r = 0; r < kFRows; ++r) {
+    float f[V];
+    Elt<T>::unpack(q[r], f);
+#pragma unroll
+    for (int w = 0; w < V; ++w) acc[w] = fmaf(c[r], f[w], acc[w]);
+  }
+}
+
+template <typename T>
 __global__ __launch_bounds__(kFT) void fused_linear_kernel(
     const T *__restrict__ x, const T *__restrict__ qt, const T *__restrict__ wf,
     T *__restrict__ y, int d, int qb, int64_t d_out, int k, float *__restrict__ x_rot,
@@ -81,7 +300,8 @@ __global__ __launch_bounds__(kFT) void fused_linear_kernel(
     int32_t *__restrict__ idx_out, int tiles, int splits, int chans_per_split) {
   constexpr int V = Elt<T>::kVec;
   constexpr int TILE = kWave * V;
-  __shared__ FusedSmem sm;
+  extern __shared__ __align__(16) unsigned char fused_lds[];
+  FusedSmem &sm = *reinterpret_cast<FusedSmem *>(fused_lds);
   const int t = threadIdx.x;
   const int lane = t % kWave;
   const int wave = wave_id();
@@ -103,141 +323,141 @@ __global__ __launch_bounds__(kFT) void fused_linear_kernel(
     acc = wave_sum(acc);
     if (lane == 0) __hip_atomic_store(x_rot + j, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  __builtin_amdgcn_s_waitcnt(0);  // this workgroup's x_rot stores have completed
+  __syncthreads();
 
-  // ---- 2. arrival; the last workgroup selects and releases the others ----
-  if (arrive_last(sync, &sm.flag)) {
-    // exact selection over all of x_rot; the acquire fence makes the other
-    // workgroups' x_rot stores visible to ordinary (vector) loads here
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    const int E = slots_per_thread(d, kFT);
-    const int i0 = t * E;
-    uint32_t key[EMAX];
-    float vv[EMAX];
-    load_keys4<EMAX>(x_rot, d, E, key, vv);
-    uint32_t T_, krem, n_eq;
-    radix_threshold<kFT, EMAX>(key, static_cast<uint32_t>(k), sm.sel, T_, krem, n_eq);
-    // channels equal to T are all kept unless there are more than krem
-    const uint32_t cut =
-        n_eq == krem ? 0xFFFFFFFFu : tie_cutoff<kFT, EMAX>(key, i0, T_, krem, sm.sel);
-    // reset the arrival counters: every workgroup has arrived
-    if (t <= kGroups)
-      __hip_atomic_store(&sync[32 * t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // release: one 64-bit word per workgroup carries the flag bit, T and the
-    // cut-off together
-    const uint64_t word = (1ull << 63) | (static_cast<uint64_t>(T_) << 32) | cut;
-    for (uint32_t b = t; b < G; b += kFT)
-      if (b != blockIdx.x)
-        __hip_atomic_store(&flags[b * 16], word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (t == 0) {
-      sm.T = T_;
-      sm.cut = cut;
-    }
-  } else if (t == 0) {
-    uint64_t *line = &flags[blockIdx.x * 16];
-    uint32_t spins = 0;
-    uint64_t word;
-    while ((word = __hip_atomic_load(line, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0u) {
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > kSpinLimit) {
-        __hip_atomic_store(&sync[kErrWord], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-    }
-    sm.T = static_cast<uint32_t>(word >> 32) & 0x7FFFFFFFu;
-    sm.cut = static_cast<uint32_t>(word);
-    __hip_atomic_store(line, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // ---- 2. selector ---------------------------------------------------------
+  if (blockIdx.x == 0) {
+    select_and_release(x_rot, d, k, sync, flags, idx_out, sm);
+    return;
+  }
+
+  // ---- arrival; the first unit's slice of x_rot once every rotation is in,
+  // then the preliminary (or already the exact) rule ------------------------
+  uint64_t *line = &flags[blockIdx.x * 16];
+  if (t == 0) {
+    __hip_atomic_fetch_add(&sync[32 * (1 + blockIdx.x % kGroups)], 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    wait_word(line, 0, &sync[kErrWord], sm);
   }
   __syncthreads();
-  const uint32_t Tk = sm.T, cut = sm.cut;
-
-  // ---- optional copy of the kept indices (ascending), by workgroup 0 ------
-  if (idx_out && blockIdx.x == 0) {
-    const int E = (d + kFT - 1) / kFT;
-    const int i0 = t * E;
-    uint32_t n = 0;
-    for (int e = 0; e < E; ++e) {
-      const int i = i0 + e;
-      if (i >= d) break;
-      const uint32_t kk =
-          __float_as_uint(__hip_atomic_load(x_rot + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) &
-          0x7FFFFFFFu;
-      n += kk > Tk || (kk == Tk && static_cast<uint32_t>(i) <= cut);
-    }
-    uint32_t p = block_incl_scan<kFT>(n, sm.sel.wave_tot) - n;
-    for (int e = 0; e < E; ++e) {
-      const int i = i0 + e;
-      if (i >= d) break;
-      const uint32_t kk =
-          __float_as_uint(__hip_atomic_load(x_rot + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) &
-          0x7FFFFFFFu;
-      if (kk > Tk || (kk == Tk && static_cast<uint32_t>(i) <= cut)) idx_out[p++] = i;
-    }
-  }
-
-  // ---- 3. gather over units (column tile, channel range) -----------------
+  const uint32_t W = G - 1;
   const int units = tiles * splits;
-  for (int u = blockIdx.x; u < units; u += G) {
-    const int tile = u % tiles, split = u / tiles;
-    const int c0 = split * chans_per_split;
+  constexpr int kPer = kFusedMaxRowsPerUnit / kFT;
+  float cv[kPer];
+  auto load_slice = [&](int u) {
+    const int c0 = (u / tiles) * chans_per_split;
     const int c1 = c0 + chans_per_split < d ? c0 + chans_per_split : d;
-    // kept channels of the range, listed in index order
-    constexpr int kPer = kFusedMaxRowsPerUnit / kFT;
-    float cv[kPer];
-    bool kp[kPer];
-    uint32_t n = 0;
 #pragma unroll
     for (int m = 0; m < kPer; ++m) {
       const int i = c0 + t * kPer + m;
       const int ic = i < c1 ? i : c1 - 1;
       cv[m] = __hip_atomic_load(x_rot + ic, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+  };
+  if (static_cast<int>(blockIdx.x) - 1 < units) load_slice(blockIdx.x - 1);
+  if (t == 0 && lds_load(&sm.stage) < 1) wait_word(line, 1, &sync[kErrWord], sm);
+  __syncthreads();
+
+  // ---- 3. gather over units (column tile, channel range) -----------------
+  for (int u = blockIdx.x - 1; u < units; u += W) {
+    const int tile = u % tiles, split = u / tiles;
+    const int c0 = split * chans_per_split;
+    const int c1 = c0 + chans_per_split < d ? c0 + chans_per_split : d;
+    const uint32_t b0 = sm.b0;
+    if (u != static_cast<int>(blockIdx.x) - 1) load_slice(u);
+    // certain rows (bin above B0) and bin-B0 channels of the range, in index
+    // order
+    uint32_t cls[kPer];  // 2: certain, 1: bin B0, 0: dropped
+    uint32_t cnt = 0;    // certain count (low half) and bin-B0 count (high half)
 #pragma unroll
     for (int m = 0; m < kPer; ++m) {
       const int i = c0 + t * kPer + m;
-      const uint32_t kk = __float_as_uint(cv[m]) & 0x7FFFFFFFu;
-      kp[m] = i < c1 && (kk > Tk || (kk == Tk && static_cast<uint32_t>(i) <= cut));
-      n += kp[m];
+      const uint32_t bin = (__float_as_uint(cv[m]) & 0x7FFFFFFFu) >> 20;
+      cls[m] = i >= c1 ? 0u : (bin > b0 ? 2u : (bin == b0 ? 1u : 0u));
+      cnt += cls[m] == 2u ? 1u : (cls[m] == 1u ? 0x10000u : 0u);
     }
-    const uint32_t incl = block_incl_scan<kFT>(n, sm.sel.wave_tot);
-    uint32_t p = incl - n;
+    const uint32_t incl = block_incl_scan<kFT>(cnt, sm.w.wave_tot);
+    uint32_t ps = (incl - cnt) & 0xFFFFu, pc = (incl - cnt) >> 16;
 #pragma unroll
     for (int m = 0; m < kPer; ++m) {
-      if (kp[m]) {
-        sm.rows[p] = c0 + t * kPer + m;
-        sm.coef[p] = cv[m];
-        ++p;
+      const int i = c0 + t * kPer + m;
+      if (cls[m] == 2u) {
+        sm.w.rows[ps] = i;
+        sm.w.coef[ps] = cv[m];
+        ++ps;
+      } else if (cls[m] == 1u) {
+        sm.w.crow[pc] = i;
+        sm.w.ccoef[pc] = cv[m];
+        ++pc;
       }
     }
-    if (t == kFT - 1) sm.flag = static_cast<int>(incl);
+    if (t == kFT - 1) {
+      sm.ns = incl & 0xFFFFu;
+      sm.nc = incl >> 16;
+      sm.claim = 0;
+      sm.tail = 0;
+    }
     __syncthreads();
-    const int nrows = sm.flag;
+    const int ns = static_cast<int>(sm.ns), nc = static_cast<int>(sm.nc);
     const int64_t col_raw = static_cast<int64_t>(tile) * TILE + lane * V;
     const int64_t col = col_raw < d_out ? col_raw : d_out - V;
     float acc[V];
 #pragma unroll
     for (int q = 0; q < V; ++q) acc[q] = 0.f;
-    for (int base = wave * kFRows; base < nrows; base += kFW * kFRows) {
-      int rr[kFRows];
-      float c[kFRows];
-#pragma unroll
-      for (int r = 0; r < kFRows; ++r) {
-        const int jl = base + r < nrows ? base + r : nrows - 1;
-        rr[r] = __builtin_amdgcn_readfirstlane(sm.rows[jl]);
-        c[r] = base + r < nrows ? sm.coef[jl] : 0.f;
+
+    // full groups of certain rows: group g goes to wave g mod kFW
+    const int full = ns / kFRows;
+    for (int g = wave; g < full; g += kFW)
+      gather_group<T>(wf, d_out, col, sm.w.rows, sm.w.coef, g * kFRows, ns, acc);
+
+    // tail: the last partial group of certain rows, then the kept bin-B0
+    // channels, appended after them by the first wave to get here
+    int n = ns;
+    if (nc > 0) {
+      uint32_t won = 0;
+      if (lane == 0) {
+        uint32_t expected = 0;
+        won = __hip_atomic_compare_exchange_strong(&sm.claim, &expected, 1u, __ATOMIC_RELAXED,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
-      uint4 q[kFRows];
-#pragma unroll
-      for (int r = 0; r < kFRows; ++r) q[r] = load16(wf + static_cast<int64_t>(rr[r]) * d_out + col);
-#pragma unroll
-      for (int r = 0; r < kFRows; ++r) {
-        float f[V];
-        Elt<T>::unpack(q[r], f);
-#pragma unroll
-        for (int w = 0; w < V; ++w) acc[w] = fmaf(c[r], f[w], acc[w]);
+      won = __shfl(won, 0, kWave);
+      if (won) {
+        if (lane == 0 && lds_load(&sm.stage) < 2) wait_word(line, 2, &sync[kErrWord], sm);
+        __builtin_amdgcn_wave_barrier();
+        const uint32_t Tk = __shfl(lane == 0 ? sm.T : 0u, 0, kWave);
+        const uint32_t cut = __shfl(lane == 0 ? sm.cut : 0u, 0, kWave);
+        uint32_t m = static_cast<uint32_t>(ns);
+        for (int b = 0; b < nc; b += kWave) {
+          const int i = b + lane;
+          const int ic = i < nc ? i : nc - 1;
+          const int32_t row = sm.w.crow[ic];
+          const float v = sm.w.ccoef[ic];
+          const uint32_t kk = __float_as_uint(v) & 0x7FFFFFFFu;
+          const bool kp = i < nc && (kk > Tk || (kk == Tk && static_cast<uint32_t>(row) <= cut));
+          const uint64_t mask = __ballot(kp);
+          const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
+              static_cast<uint32_t>(mask >> 32),
+              __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
+          if (kp) {
+            sm.w.rows[m + rank] = row;
+            sm.w.coef[m + rank] = v;
+          }
+          m += static_cast<uint32_t>(__popcll(mask));
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        if (lane == 0) lds_store(&sm.tail, m + 1);
       }
+      uint32_t tn, spins = 0;
+      while ((tn = lds_load(&sm.tail)) == 0u && ++spins < kSpinLimit) __builtin_amdgcn_s_sleep(1);
+      n = tn > 0 ? static_cast<int>(tn - 1) : ns;
     }
+    const int ng = (n + kFRows - 1) / kFRows;
+    for (int g = full + ((wave - full % kFW) + kFW) % kFW; g < ng; g += kFW)
+      gather_group<T>(wf, d_out, col, sm.w.rows, sm.w.coef, g * kFRows, n, acc);
+
 #pragma unroll
-    for (int w = 0; w < V; ++w) sm.red[wave][lane * V + w] = acc[w];
+    for (int w = 0; w < V; ++w) sm.w.red[wave][lane * V + w] = acc[w];
     __syncthreads();
     const int64_t tile_col0 = static_cast<int64_t>(tile) * TILE;
     for (int e = t; e < TILE; e += kFT) {
@@ -245,7 +465,7 @@ __global__ __launch_bounds__(kFT) void fused_linear_kernel(
       if (cg >= d_out) continue;
       float s = 0.f;
 #pragma unroll
-      for (int w = 0; w < kFW; ++w) s += sm.red[w][e];
+      for (int w = 0; w < kFW; ++w) s += sm.w.red[w][e];
       if (splits == 1) {
         Elt<T>::store(y, cg, s);
       } else {
@@ -260,10 +480,10 @@ __global__ __launch_bounds__(kFT) void fused_linear_kernel(
       if (t == 0) {
         const uint32_t prev =
             __hip_atomic_fetch_add(&tile_ctr[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        sm.flag = prev == static_cast<uint32_t>(splits - 1);
+        sm.last = prev == static_cast<uint32_t>(splits - 1);
       }
       __syncthreads();
-      if (sm.flag) {
+      if (sm.last) {
         for (int e = t; e < TILE; e += kFT) {
           const int64_t cg = tile_col0 + e;
           if (cg >= d_out) continue;
@@ -288,28 +508,48 @@ __global__ __launch_bounds__(kFT) void fused_linear_kernel(
     }
     __syncthreads();  // LDS lists and reduction buffer are reused by the next unit
   }
-}
 
-template <int EMAX, typename T>
-int resident_blocks() {
-  static int cached = -1;
-  if (cached < 0) {
-    int per_cu = 0, dev = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void *>(&fused_linear_kernel<EMAX, T>), kFT, 0) !=
-            hipSuccess ||
-        hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return 0;
-    cached = per_cu * cus;
+  // the exact rule always follows the preliminary one: take it before
+  // clearing the line for the next call
+  if (t == 0) {
+    if (lds_load(&sm.stage) < 2) wait_word(line, 2, &sync[kErrWord], sm);
+    __hip_atomic_store(line, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  return cached;
 }
 
-template <int EMAX, typename T>
-hipError_t launch_e(const FusedArgs &a, hipStream_t s) {
-  int capacity = resident_blocks<EMAX, T>();
-  if (capacity <= 0) return hipErrorLaunchFailure;
+// Workgroups of the kernel resident at once on the current device, for a
+// given LDS size (cached; a few sizes are in use at a time).
+template <typename T>
+int resident_blocks(size_t lds) {
+  struct Entry {
+    int dev;
+    size_t lds;
+    int n;
+  };
+  static std::mutex mu;
+  static Entry cache[16];
+  static int used = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < used; ++i)
+    if (cache[i].dev == dev && cache[i].lds == lds) return cache[i].n;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, reinterpret_cast<const void *>(&fused_linear_kernel<T>), kFT, lds) !=
+          hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  const int n = per_cu * cus;
+  if (used < 16) cache[used++] = Entry{dev, lds, n};
+  return n;
+}
+
+template <typename T>
+hipError_t launch_t(const FusedArgs &a, hipStream_t s) {
+  const size_t lds = fused_lds_bytes(a.d_in);
+  int capacity = resident_blocks<T>(lds);
+  if (capacity < 2) return hipErrorLaunchFailure;
   if (capacity > kFusedMaxGrid) capacity = kFusedMaxGrid;
   const FusedPlan p = plan_fused(a.d_in, a.d_out, a.k, a.w_dt, capacity);
   char *ws = static_cast<char *>(a.ws);
@@ -318,21 +558,12 @@ hipError_t launch_e(const FusedArgs &a, hipStream_t s) {
   uint64_t *flags = reinterpret_cast<uint64_t *>(ws + p.flags_off);
   float *x_rot = a.xrot_out ? a.xrot_out : reinterpret_cast<float *>(ws + p.xrot_off);
   float *partials = reinterpret_cast<float *>(ws + p.partial_off);
-  hipLaunchKernelGGL((fused_linear_kernel<EMAX, T>), dim3(p.grid), dim3(kFT), 0, s,
+  hipLaunchKernelGGL((fused_linear_kernel<T>), dim3(p.grid), dim3(kFT), lds, s,
                      static_cast<const T *>(a.x), static_cast<const T *>(a.qt),
                      static_cast<const T *>(a.wf), static_cast<T *>(a.y), a.d_in, a.q_block,
                      a.d_out, a.k, x_rot, sync, flags, tile_ctr, partials, a.idx_out,
                      p.tiles, p.splits, p.chans_per_split);
   return hipGetLastError();
-}
-
-template <typename T>
-hipError_t launch_t(const FusedArgs &a, hipStream_t s) {
-  const int E = slots_per_thread(a.d_in, kFT);
-  if (E <= 8) return launch_e<8, T>(a, s);
-  if (E <= 16) return launch_e<16, T>(a, s);
-  if (E <= 32) return launch_e<32, T>(a, s);
-  return hipErrorInvalidValue;
 }
 
 size_t up256(size_t n) { return (n + 255) / 256 * 256; }
@@ -346,9 +577,9 @@ FusedPlan plan_fused(int64_t d_in, int64_t d_out, int64_t k, int w_dt, int grid)
   const int64_t tile_cols = static_cast<int64_t>(kWave) * V;
   p.grid = grid;
   p.tiles = static_cast<int>((d_out + tile_cols - 1) / tile_cols);
-  // One unit per workgroup where possible; a unit's channel range must fit
-  // its LDS row list.
-  int64_t splits = grid / p.tiles;
+  // One unit per gathering workgroup (all but the selector) where possible;
+  // a unit's channel range must fit its LDS row list.
+  int64_t splits = (grid - 1) / p.tiles;
   if (splits < 1) splits = 1;
   const int64_t min_split = (d_in + kFusedMaxRowsPerUnit - 1) / kFusedMaxRowsPerUnit;
   if (splits < min_split) splits = min_split;

@@ -281,10 +281,33 @@ size_t gather_ws_bytes(const GatherPlan &p, int B, int64_t d_out) {
   return counter_bytes(p.tiles) + pbytes;
 }
 
+// Most splits any plan_gather(nb, rows, ...) with rows <= max_rows can
+// choose. For a fixed wave count the split count is at most
+// min(ceil(target / tiles), max(1, rows / (2 · waves · kRows))), which grows
+// with rows; but fewer rows can move the choice to narrower workgroups with
+// more splits, so every wave count the planner may pick is bounded.
+int64_t gather_split_bound(int nb, int64_t max_rows, int64_t d_out, int w_dt) {
+  const int m = max_waves_for(nb);
+  int64_t bound = 1;
+  for (int w = m; w >= (m < 4 ? m : 4); w /= 2) {
+    const GatherPlan p = plan_with_waves(w, max_rows, d_out, w_dt);
+    const int64_t target_wgs = (256 * 32) / w;
+    int64_t by_rows = max_rows / (2 * static_cast<int64_t>(w) * kRows);
+    if (by_rows < 1) by_rows = 1;
+    const int64_t by_target = (target_wgs + p.tiles - 1) / p.tiles;
+    const int64_t sb = by_rows < by_target ? by_rows : by_target;
+    if (sb > bound) bound = sb;
+  }
+  return bound;
+}
+
 size_t gather_batch_ws_bytes(int B, int64_t max_rows, int64_t d_out, int w_dt) {
   size_t need = 0;
   for (int nb = 1; nb <= (B < 8 ? B : 8); ++nb) {
-    const size_t n = gather_ws_bytes(plan_gather(nb, max_rows, d_out, w_dt), nb, d_out);
+    const GatherPlan p = plan_gather(nb, max_rows, d_out, w_dt);
+    const int64_t splits = gather_split_bound(nb, max_rows, d_out, w_dt);
+    if (splits <= 1) continue;
+    const size_t n = counter_bytes(p.tiles) + static_cast<size_t>(splits) * nb * d_out * sizeof(float);
     need = n > need ? n : need;
   }
   return need;

@@ -77,6 +77,38 @@ __device__ __forceinline__ void suffix_search(uint32_t krem, SelectSmem<NT> &sm)
   __syncthreads();
 }
 
+// Radix digits: pass 0 takes key bits 30..20, pass 1 bits 19..9, pass 2
+// bits 8..0 (key bit 31 is the no-key mark).
+__host__ __device__ constexpr int radix_shift(int pass) { return pass == 0 ? 20 : (pass == 1 ? 9 : 0); }
+__host__ __device__ constexpr uint32_t radix_dmask(int pass) { return pass == 2 ? 0x1FFu : 0x7FFu; }
+
+// A radix pass taken in steps, for callers that hold their keys in another
+// layout: radix_clear, then radix_count for every key (both followed by a
+// barrier), then radix_resolve, which finds the bin holding the krem-th
+// largest key among those matching (prefix, pmask), updates prefix, pmask
+// and krem, and returns that bin's count.
+template <int NT>
+__device__ __forceinline__ void radix_clear(SelectSmem<NT> &sm) {
+  for (int i = threadIdx.x; i < 2048 + 64; i += NT) sm.hist[i] = 0u;
+}
+template <int NT>
+__device__ __forceinline__ void radix_count(uint32_t key, int pass, uint32_t prefix, uint32_t pmask,
+                                            SelectSmem<NT> &sm) {
+  if ((key & pmask) == prefix)
+    atomicAdd(&sm.hist[pad_bin(static_cast<int>((key >> radix_shift(pass)) & radix_dmask(pass)))], 1u);
+}
+template <int NT>
+__device__ __forceinline__ uint32_t radix_resolve(int pass, uint32_t &prefix, uint32_t &pmask,
+                                                  uint32_t &krem, SelectSmem<NT> &sm) {
+  suffix_search<NT>(krem, sm);
+  prefix |= sm.bin << radix_shift(pass);
+  pmask |= radix_dmask(pass) << radix_shift(pass);
+  krem -= sm.above;
+  const uint32_t count = sm.count;
+  __syncthreads();  // bin / above are rewritten by the next pass
+  return count;
+}
+
 // Radix passes first_pass..2 over the keys matching (prefix, pmask): finds T
 // and krem for the krem-th largest key among them; eq_count is the number of
 // keys equal to T (the last digit's bin count).

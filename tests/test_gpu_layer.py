@@ -116,6 +116,31 @@ def test_linear_extreme_k(k, B, mode):
 
 
 @pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("d,qb,n,levels,k", [
+    (4096, 512, 22016, 5, 2457),    # five magnitudes: the K-th key is tied many times
+    (4096, 512, 4104, 1, 1000),     # one magnitude: every channel ties with the K-th
+    (8192, 1024, 4096, 5, 7000),    # K past the nonzero channels: the K-th key is 0
+    (16384, 1024, 22016, 1, 9000),  # ranges of 1024 channels, all tied
+])
+def test_single_token_ties(mode, d, qb, n, levels, k):
+    """Exact ties at the K-th key: a signed-permutation rotation keeps x's
+    few integer magnitudes exactly, so the lowest-index rule decides which of
+    the tied channels are kept."""
+    rng = np.random.default_rng(d + 10 * levels + k)
+    q = np.zeros((d // qb, qb, qb))
+    for b in range(d // qb):
+        perm, sign = wl.signed_permutation(rng, qb)
+        q[b, np.arange(qb), perm] = sign
+    mag = rng.integers(0, levels, (1, d)) if levels > 1 else np.ones((1, d))
+    x = mag * np.where(rng.random((1, d)) < 0.5, -1.0, 1.0)
+    w = wl.quantize(rng.standard_normal((d, n)) * 0.02, "bf16")
+    lin = RotatedLinear(q, w, "bf16", k)
+    _, xr, _ = check_linear(lin, x, q, mode=mode)
+    key = np.abs(xr[0])
+    assert np.sum(key == np.sort(key)[::-1][k - 1]) > 1  # the case really ties
+
+
+@pytest.mark.parametrize("mode", MODES)
 def test_llama7b_mlp_decode_b1(mode):
     """The 7B-shaped SwiGLU MLP at batch 1, 40%: gate|up (4096→22016),
     SiLU(gate)·up, down (11008→4096) with the 4×2752 block rotation."""
@@ -221,3 +246,31 @@ def test_large_batches(B, d, qb, n):
     x, q, w = wl.linear_case_inputs(case, w_std=0.01)
     lin = RotatedLinear(q, w, "bf16", case.k)
     check_linear(lin, x, q)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("B,d,qb,n", [(1, 8192, 1024, 4096), (1, 4096, 4096, 22016),
+                                      (3, 4096, 1024, 4104), (16, 2048, 512, 2056)])
+def test_workspace_stays_in_bounds(mode, B, d, qb, n):
+    """K from 1 to d, each on a fresh workspace of exactly the advertised size
+    with canaries on both sides: no call writes outside it. (Fewer kept rows
+    can make the gather plan choose more splits than the all-rows plan.)"""
+    case = wl.LinearCase(cfg=3, batch=B, d_in=d, d_out=n, q_block=qb, sparsity_pct=40,
+                         dtype="bf16")
+    x, q, w = wl.linear_case_inputs(case, w_std=0.02)
+    lin = RotatedLinear(q, w, "bf16", case.k, keep_w=False)
+    x_d = dev(x, "bf16")
+    ks = {1, 2, 63, 64, 65, d // 7, d // 3, d - 1, d} | set(range(d // 16, d, d // 16))
+    pad = 4096
+    for k in sorted(ks):
+        nbytes = _lib.larosa_workspace_bytes(B, d, n, k, mode)
+        buf = torch.full((nbytes + 2 * pad,), 0xA5, dtype=torch.uint8, device="cuda")
+        ws = buf[pad:pad + nbytes]
+        _lib.larosa_workspace_init(ws)
+        y = torch.empty((B, n), dtype=torch.bfloat16, device="cuda")
+        for _ in range(2):
+            _lib.larosa_layer_forward(x_d, lin.Qt, qb, lin.Wf, B, d, n, k, y, mode=mode, ws=ws)
+        torch.cuda.synchronize()
+        b = buf.cpu()
+        assert bool((b[:pad] == 0xA5).all() and (b[pad + nbytes:] == 0xA5).all()), k
+        assert bool(torch.isfinite(y).all()), k
