@@ -34,15 +34,56 @@ int launched(hipError_t e) { return e == hipSuccess ? LAROSA_OK : LAROSA_ERR_LAU
 
 hipStream_t stream_of(larosa_stream_t s) { return static_cast<hipStream_t>(s); }
 
-// Workspace carving for larosa_layer_forward and the standalone calls.
+// Workspace carving. Every call that takes a workspace uses the same prefix,
+// computed from (B, d_in, d_out) only, so calls of one shape can share one
+// workspace in any order:
+//   mask   B per-token bit masks of the selection (rewritten by each select)
+//   gather the vector product's tile counters (must stay zero between
+//          calls) and split partial sums
+//   mfma   transposed coefficients and split partial sums of the matrix-core
+//          forms (B >= 16, bf16 weights; rewritten by each call)
+// larosa_layer_forward then adds its own areas, and the fused kernel's region
+// (whose synchronisation words must also stay zero) comes last.
+struct Prefix {
+  size_t mask = 0, gather = 0, mfma_coef = 0, mfma_parts = 0, end = 0;
+};
+
+bool mfma_region(int64_t B, int w_dt) { return w_dt == LAROSA_BF16 && B >= kMfmaMinB && B <= kMaxB; }
+
+// rows_bound: the longest row list a product over this workspace takes.
+Prefix prefix_for(int64_t B, int64_t d_in, int64_t d_out, int64_t rows_bound, int w_dt) {
+  Prefix P;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  P.mask = take(static_cast<size_t>(B) * mask_words(static_cast<int>(d_in)) * 4);
+  P.gather = take(gather_batch_ws_bytes(static_cast<int>(B), rows_bound, d_out, w_dt));
+  if (mfma_region(B, w_dt)) {
+    P.mfma_coef = take(static_cast<size_t>(B) * mfma_coef_ld(rows_bound) * 4);
+    size_t parts = rotate_mfma_ws_bound(B, d_in);
+    const size_t g = gather_mfma_ws_bound(B, d_out);
+    P.mfma_parts = take(parts > g ? parts : g);
+  }
+  P.end = off;
+  return P;
+}
+
 struct Layout {
-  size_t x_rot = 0, idx = 0, val = 0, xs = 0, mask = 0, u_idx = 0, u_cnt = 0,
-         u_coef = 0, gather = 0, fused = 0, total = 0;
+  Prefix p;
+  size_t x_rot = 0, idx = 0, val = 0, xs = 0, u_idx = 0, u_cnt = 0, u_coef = 0, fused = 0,
+         total = 0;
 };
 
 Layout layout_for(int64_t B, int64_t d_in, int64_t d_out, int64_t k, int w_dt) {
   Layout L;
-  size_t off = 0;
+  // The vector product's area covers both the sparse call (max_rows =
+  // min(d_in, B·k)) and the dense call (max_rows = d_in): the dense plan has
+  // at least as many splits.
+  L.p = prefix_for(B, d_in, d_out, d_in, w_dt);
+  size_t off = L.p.end;
   auto take = [&](size_t bytes) {
     const size_t at = off;
     off += align256(bytes);
@@ -52,14 +93,9 @@ Layout layout_for(int64_t B, int64_t d_in, int64_t d_out, int64_t k, int w_dt) {
   L.idx = take(static_cast<size_t>(B) * k * 4);
   L.val = take(static_cast<size_t>(B) * k * 4);
   L.xs = take(static_cast<size_t>(B) * d_in * 4);
-  L.mask = take(static_cast<size_t>(B) * mask_words(static_cast<int>(d_in)) * 4);
   L.u_idx = take(static_cast<size_t>(d_in) * 4);
   L.u_cnt = take(4);
   L.u_coef = take(static_cast<size_t>(d_in) * B * 4);
-  // The gather's reduction area covers both the sparse call (max_rows =
-  // min(d_in, B·k)) and the dense call (max_rows = d_in): the dense plan has
-  // at least as many splits.
-  L.gather = take(gather_batch_ws_bytes(static_cast<int>(B), d_in, d_out, w_dt));
   L.total = off;
   return L;
 }
@@ -71,10 +107,6 @@ Layout layout_with_fused(int64_t B, int64_t d_in, int64_t d_out, int64_t k, int 
   L.fused = L.total;
   L.total += align256(plan_fused(d_in, d_out, k, w_dt, kFusedMaxGrid).bytes);
   return L;
-}
-
-size_t gather_need(int64_t B, int64_t max_rows, int64_t d_out, int w_dt) {
-  return gather_batch_ws_bytes(static_cast<int>(B), max_rows, d_out, w_dt);
 }
 
 int check_sizes(int64_t B, int64_t d, int64_t k) {
@@ -175,6 +207,10 @@ int larosa_rotate(const void *x, int x_dtype, const void *Qt, int64_t q_block, i
   if (d % 8 && x_dtype == LAROSA_BF16) return LAROSA_ERR_ALIGNMENT;
   if (!aligned16(x) || !aligned16(Qt) || !aligned16(x_rot)) return LAROSA_ERR_ALIGNMENT;
   if (int st = device_status()) return st;
+  // Without a workspace the matrix-core form runs unsplit over each block.
+  if (mfma_supported(B, x_dtype, q_dtype) && q_block % 32 == 0)
+    return launched(launch_rotate_mfma(x, Qt, x_rot, static_cast<int>(B), static_cast<int>(d),
+                                       static_cast<int>(q_block), nullptr, stream_of(stream)));
   return launched(launch_rotate(x, x_dtype, Qt, q_dtype, x_rot, static_cast<int>(B),
                                 static_cast<int>(d), static_cast<int>(q_block),
                                 stream_of(stream)));
@@ -212,17 +248,30 @@ int larosa_sparse_gemv(const int32_t *rows, const int32_t *n_rows, int64_t max_r
   if (!dtype_ok(w_dtype) || !dtype_ok(y_dtype)) return LAROSA_ERR_DTYPE;
   if (w_dtype == LAROSA_F32 && y_dtype == LAROSA_BF16) return LAROSA_ERR_DTYPE;
   if (B < 0 || B > kMaxB) return LAROSA_ERR_INVALID_ARG;
-  if (d_in < 1 || d_out < 1) return LAROSA_ERR_SHAPE;
-  if (max_rows < 0) return LAROSA_ERR_INVALID_ARG;
+  if (d_in < 1 || d_in > kMaxD || d_out < 1) return LAROSA_ERR_SHAPE;
+  if (max_rows < 0 || max_rows > INT32_MAX / 2) return LAROSA_ERR_INVALID_ARG;
   if (B == 0) return LAROSA_OK;
   if (!rows || !coef || !W_folded || !y) return LAROSA_ERR_INVALID_ARG;
   if (d_out % vec_of(w_dtype)) return LAROSA_ERR_ALIGNMENT;
   if (!aligned16(W_folded) || !aligned16(y)) return LAROSA_ERR_ALIGNMENT;
   const int64_t mr = max_rows < 1 ? 1 : max_rows;
-  const size_t need = gather_need(B, mr, d_out, w_dtype);
-  if (need && (!ws || ws_bytes < need)) return LAROSA_ERR_WORKSPACE;
-  if (need && !aligned16(ws)) return LAROSA_ERR_ALIGNMENT;
+  const Prefix P = prefix_for(B, d_in, d_out, mr > d_in ? mr : d_in, w_dtype);
+  const bool mf = mfma_supported(B, y_dtype, w_dtype);
+  if (!ws || ws_bytes < P.end) return LAROSA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return LAROSA_ERR_ALIGNMENT;
   if (int st = device_status()) return st;
+  hipStream_t s = stream_of(stream);
+  char *base = static_cast<char *>(ws);
+  if (mf) {
+    // max_rows == 0 still runs, so y is written (as zeros).
+    const int64_t ldc = mfma_coef_ld(mr);
+    float *coefT = reinterpret_cast<float *>(base + P.mfma_coef);
+    hipError_t e = launch_coef_transpose(coef, static_cast<int>(B), max_rows, ldc, coefT, s);
+    if (e == hipSuccess)
+      e = launch_gather_mfma(rows, n_rows, max_rows, d_in, coefT, ldc, W_folded, y,
+                             static_cast<int>(B), d_out, base + P.mfma_parts, s);
+    return launched(e);
+  }
   GatherArgs a;
   a.rows = rows;
   a.n_rows = n_rows;
@@ -236,9 +285,9 @@ int larosa_sparse_gemv(const int32_t *rows, const int32_t *n_rows, int64_t max_r
   a.y = y;
   a.y_dt = y_dtype;
   a.B = static_cast<int>(B);
-  a.ws = ws;
+  a.ws = base + P.gather;
   // max_rows == 0 still runs, so y is written (as zeros).
-  return launched(launch_gather(a, stream_of(stream)));
+  return launched(launch_gather(a, s));
 }
 
 int larosa_dense_gemv(const void *x, int act_dtype, const void *W, int w_dtype, void *y,
@@ -247,15 +296,26 @@ int larosa_dense_gemv(const void *x, int act_dtype, const void *W, int w_dtype, 
   if (!dtype_ok(act_dtype) || !dtype_ok(w_dtype)) return LAROSA_ERR_DTYPE;
   if (act_dtype != w_dtype) return LAROSA_ERR_DTYPE;
   if (B < 0 || B > kMaxB) return LAROSA_ERR_INVALID_ARG;
-  if (d_in < 1 || d_out < 1) return LAROSA_ERR_SHAPE;
+  if (d_in < 1 || d_in > kMaxD || d_out < 1) return LAROSA_ERR_SHAPE;
   if (B == 0) return LAROSA_OK;
   if (!x || !W || !y) return LAROSA_ERR_INVALID_ARG;
   if (d_out % vec_of(w_dtype)) return LAROSA_ERR_ALIGNMENT;
   if (!aligned16(x) || !aligned16(W) || !aligned16(y)) return LAROSA_ERR_ALIGNMENT;
-  const size_t need = gather_need(B, d_in, d_out, w_dtype);
-  if (need && (!ws || ws_bytes < need)) return LAROSA_ERR_WORKSPACE;
-  if (need && !aligned16(ws)) return LAROSA_ERR_ALIGNMENT;
+  const Prefix P = prefix_for(B, d_in, d_out, d_in, w_dtype);
+  if (!ws || ws_bytes < P.end) return LAROSA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return LAROSA_ERR_ALIGNMENT;
   if (int st = device_status()) return st;
+  hipStream_t s = stream_of(stream);
+  char *base = static_cast<char *>(ws);
+  if (mfma_supported(B, act_dtype, w_dtype)) {
+    const int64_t ldc = mfma_coef_ld(d_in);
+    float *coefT = reinterpret_cast<float *>(base + P.mfma_coef);
+    hipError_t e = launch_act_to_coef_t(x, static_cast<int>(B), d_in, ldc, coefT, s);
+    if (e == hipSuccess)
+      e = launch_gather_mfma(nullptr, nullptr, d_in, d_in, coefT, ldc, W, y,
+                             static_cast<int>(B), d_out, base + P.mfma_parts, s);
+    return launched(e);
+  }
   GatherArgs a;
   a.rows = nullptr;
   a.n_rows = nullptr;
@@ -269,8 +329,8 @@ int larosa_dense_gemv(const void *x, int act_dtype, const void *W, int w_dtype, 
   a.y = y;
   a.y_dt = act_dtype;
   a.B = static_cast<int>(B);
-  a.ws = ws;
-  return launched(launch_gather(a, stream_of(stream)));
+  a.ws = base + P.gather;
+  return launched(launch_gather(a, s));
 }
 
 int larosa_layer_forward(const void *x, int act_dtype, const void *Qt, int64_t q_block,
@@ -317,8 +377,16 @@ int larosa_layer_forward(const void *x, int act_dtype, const void *Qt, int64_t q
   int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(base + L.idx);
   float *val = reinterpret_cast<float *>(base + L.val);
 
-  hipError_t e = launch_rotate(x, act_dtype, Qt, w_dtype, x_rot, static_cast<int>(B),
-                               static_cast<int>(d_in), static_cast<int>(q_block), s);
+  // Batches of 16 to 64 tokens in bf16 run the matrix-core forms of the
+  // rotation and the product, which read Qt and the union rows once for the
+  // whole batch.
+  const bool mf = mfma_supported(B, act_dtype, w_dtype);
+  hipError_t e =
+      mf && q_block % 32 == 0
+          ? launch_rotate_mfma(x, Qt, x_rot, static_cast<int>(B), static_cast<int>(d_in),
+                               static_cast<int>(q_block), base + L.p.mfma_parts, s)
+          : launch_rotate(x, act_dtype, Qt, w_dtype, x_rot, static_cast<int>(B),
+                          static_cast<int>(d_in), static_cast<int>(q_block), s);
   if (e != hipSuccess) return LAROSA_ERR_LAUNCH;
 
   GatherArgs a;
@@ -330,7 +398,7 @@ int larosa_layer_forward(const void *x, int act_dtype, const void *Qt, int64_t q
   a.y = y;
   a.y_dt = act_dtype;
   a.B = static_cast<int>(B);
-  a.ws = base + L.gather;
+  a.ws = base + L.p.gather;
   if (B == 1) {
     e = launch_select(x_rot, 1, static_cast<int>(d_in), static_cast<int>(k), idx, val,
                       nullptr, nullptr, s);
@@ -341,7 +409,7 @@ int larosa_layer_forward(const void *x, int act_dtype, const void *Qt, int64_t q
     a.coef = val;
   } else {
     float *xs = reinterpret_cast<float *>(base + L.xs);
-    uint32_t *mask = reinterpret_cast<uint32_t *>(base + L.mask);
+    uint32_t *mask = reinterpret_cast<uint32_t *>(base + L.p.mask);
     int32_t *u_idx = reinterpret_cast<int32_t *>(base + L.u_idx);
     int32_t *u_cnt = reinterpret_cast<int32_t *>(base + L.u_cnt);
     float *u_coef = reinterpret_cast<float *>(base + L.u_coef);
@@ -349,12 +417,23 @@ int larosa_layer_forward(const void *x, int act_dtype, const void *Qt, int64_t q
                       idx, val, xs, mask, s);
     if (e == hipSuccess)
       e = launch_union(mask, xs, static_cast<int>(B), static_cast<int>(d_in), u_idx, u_cnt,
-                       u_coef, s);
+                       mf ? nullptr : u_coef, s);
     if (e != hipSuccess) return LAROSA_ERR_LAUNCH;
+    const int64_t bk = B * k;
+    const int64_t max_rows = bk < d_in ? bk : d_in;
+    if (mf) {
+      const int64_t ldc = mfma_coef_ld(max_rows);
+      float *coefT = reinterpret_cast<float *>(base + L.p.mfma_coef);
+      e = launch_union_coef_t(u_idx, u_cnt, xs, static_cast<int>(B), static_cast<int>(d_in), ldc,
+                              coefT, s);
+      if (e == hipSuccess)
+        e = launch_gather_mfma(u_idx, u_cnt, max_rows, d_in, coefT, ldc, W_folded, y,
+                               static_cast<int>(B), d_out, base + L.p.mfma_parts, s);
+      return launched(e);
+    }
     a.rows = u_idx;
     a.n_rows = u_cnt;
-    const int64_t bk = B * k;
-    a.max_rows = bk < d_in ? bk : d_in;
+    a.max_rows = max_rows;
     a.coef = u_coef;
   }
   return launched(launch_gather(a, s));

@@ -103,6 +103,29 @@ __global__ void union_coef_kernel(const int32_t *__restrict__ u_idx,
   coef[e] = j < n ? xs[static_cast<int64_t>(b) * d + u_idx[j]] : 0.f;
 }
 
+// coefT[b·ldc + j] = xs[b, u_idx[j]] for j < |U|; zero for j in [|U|, ldc).
+__global__ void union_coef_t_kernel(const int32_t *__restrict__ u_idx,
+                                    const int32_t *__restrict__ u_count,
+                                    const float *__restrict__ xs, int B, int d, int64_t ldc,
+                                    float *__restrict__ coefT) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (e >= ldc * B) return;
+  const int b = static_cast<int>(e / ldc);
+  const int64_t j = e % ldc;
+  const int n = *u_count;
+  coefT[e] = j < n ? xs[static_cast<int64_t>(b) * d + u_idx[j]] : 0.f;
+}
+
+// coefT[b·ldc + j] = coef[j·B + b] for j < rows; zero for j in [rows, ldc).
+__global__ void coef_transpose_kernel(const float *__restrict__ coef, int B, int64_t rows,
+                                      int64_t ldc, float *__restrict__ coefT) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (e >= ldc * B) return;
+  const int b = static_cast<int>(e / ldc);
+  const int64_t j = e % ldc;
+  coefT[e] = j < rows ? coef[j * B + b] : 0.f;
+}
+
 template <int EMAX>
 hipError_t launch_sel(const float *x_rot, int B, int d, int k, int E, int32_t *idx,
                       float *val, float *xs, uint32_t *mask, hipStream_t s) {
@@ -129,10 +152,26 @@ hipError_t launch_union(const uint32_t *mask, const float *xs, int B, int d,
   hipLaunchKernelGGL(union_list_kernel, dim3(1), dim3(kThreads), 0, s, mask, B, d,
                      u_idx, u_count);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !u_coef) return e;
   const int64_t n = static_cast<int64_t>(d) * B;
   hipLaunchKernelGGL(union_coef_kernel, dim3(static_cast<unsigned>((n + 255) / 256)),
                      dim3(256), 0, s, u_idx, u_count, xs, B, d, u_coef);
+  return hipGetLastError();
+}
+
+hipError_t launch_union_coef_t(const int32_t *u_idx, const int32_t *u_count, const float *xs,
+                               int B, int d, int64_t ldc, float *coefT, hipStream_t s) {
+  const int64_t n = ldc * B;
+  hipLaunchKernelGGL(union_coef_t_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
+                     0, s, u_idx, u_count, xs, B, d, ldc, coefT);
+  return hipGetLastError();
+}
+
+hipError_t launch_coef_transpose(const float *coef, int B, int64_t max_rows, int64_t ldc,
+                                 float *coefT, hipStream_t s) {
+  const int64_t n = ldc * B;
+  hipLaunchKernelGGL(coef_transpose_kernel, dim3(static_cast<unsigned>((n + 255) / 256)),
+                     dim3(256), 0, s, coef, B, max_rows, ldc, coefT);
   return hipGetLastError();
 }
 

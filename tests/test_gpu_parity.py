@@ -115,6 +115,9 @@ ROTATE_CASES = [
     ("f32", "f32", 512, 512, 1), ("bf16", "bf16", 4096, 4096, 1),
     ("bf16", "bf16", 11008, 2752, 1), ("bf16", "bf16", 1024, 256, 5),
     ("f32", "bf16", 768, 768, 2), ("bf16", "f32", 256, 64, 3), ("bf16", "bf16", 13824, 3456, 8),
+    # batches of 16 and more in bf16 take the matrix-core form
+    ("bf16", "bf16", 4096, 4096, 16), ("bf16", "bf16", 11008, 2752, 33),
+    ("bf16", "bf16", 8192, 8192, 64), ("bf16", "bf16", 1152, 96, 17),
 ]
 
 
@@ -231,18 +234,56 @@ def test_sparse_gemv_parity(dt, d_in, d_out, k):
     assert ok()
 
 
-def test_sparse_gemv_small_integers_are_bit_exact_and_bounds_checked():
+@pytest.mark.parametrize("B,d_in,d_out,k", [(16, 4096, 22016, 2457), (40, 4096, 1032, 1000),
+                                             (64, 2048, 4104, 1024), (17, 11008, 4096, 6604)])
+def test_sparse_gemv_batched_union_parity(B, d_in, d_out, k):
+    """The product over the row union of a batch (packed coefficients, the
+    count on the device), against each token's product over its own kept
+    rows."""
+    rng = np.random.default_rng(B * d_out + k)
+    w = wl.quantize(rng.standard_normal((d_in, d_out)) * 0.02, "bf16")
+    xr = make_x_rot("heavy", B, d_in, seed=k + B)
+    idx = ref.select(xr, k)
+    u = ref.row_union(idx)
+    xs = ref.sparsify(xr, idx)
+    coef = np.ascontiguousarray(xs[:, u].T.astype(np.float32))
+    max_rows = min(d_in, B * k)
+    rows = np.full(max_rows, -7, dtype=np.int32)
+    rows[:len(u)] = u
+    coef_full = np.zeros((max_rows, B), dtype=np.float32)
+    coef_full[:len(u)] = coef
+    n_dev = torch.tensor([len(u)], dtype=torch.int32, device="cuda")
+    y, ok = guarded((B, d_out), torch.bfloat16)
+    ws = _gather_ws(B, d_in, d_out, k)
+    args = (torch.from_numpy(rows).cuda(), n_dev, max_rows, torch.from_numpy(coef_full).cuda(),
+            dev(w, "bf16"))
+    _lib.larosa_sparse_gemv(*args, y, B, d_in, d_out, ws)
+    y2 = torch.empty_like(y)
+    _lib.larosa_sparse_gemv(*args, y2, B, d_in, d_out, ws)
+    torch.cuda.synchronize()
+    want = ref.round_to(ref.gather_product(xr, idx, w), "bf16")
+    assert ref.rel_error(host(y), want) <= 2e-2
+    assert torch.equal(y, y2)
+    assert ok()
+
+
+@pytest.mark.parametrize("B", [3, 16, 64])
+def test_sparse_gemv_small_integers_are_bit_exact_and_bounds_checked(B):
     """Integer weights and coefficients make every summation order exact, so
     the fp32 output must equal the oracle exactly. Row entries outside
     [0, d_in) and entries past the device-side count contribute nothing."""
-    rng = np.random.default_rng(21)
-    d_in, d_out, B = 700, 2056, 3
+    rng = np.random.default_rng(21 + B)
+    d_in, d_out = 700, 2056
     w = rng.integers(-64, 65, (d_in, d_out)).astype(np.float64)
     rows = np.array(sorted(rng.choice(d_in, 200, replace=False)), dtype=np.int32)
     rows_bad = np.concatenate([rows[:150], [-1, d_in, 10 ** 6], rows[150:]]).astype(np.int32)
     coef = rng.integers(-9, 10, (len(rows_bad), B)).astype(np.float32)
     n_dev = torch.tensor([len(rows_bad) - 10], dtype=torch.int32, device="cuda")
-    y = torch.empty((B, d_out), device="cuda")
+    # The vector form (B < 16) is checked on an fp32 output. The matrix-core
+    # form writes bf16 only: its fp32 sums are exact too (integers below 2^24),
+    # so the output must be the bf16 rounding of the exact sum.
+    ydt = torch.float32 if B < 16 else torch.bfloat16
+    y = torch.empty((B, d_out), device="cuda", dtype=ydt)
     ws = _gather_ws(B, d_in, d_out, d_in)
     _lib.larosa_sparse_gemv(torch.from_numpy(rows_bad).cuda(), n_dev, len(rows_bad),
                             torch.from_numpy(coef).cuda(), dev(w, "bf16"), y, B, d_in, d_out, ws)
@@ -253,11 +294,12 @@ def test_sparse_gemv_small_integers_are_bit_exact_and_bounds_checked():
         r = rows_bad[j]
         if 0 <= r < d_in:
             want += coef[j][:, None].astype(np.float64) * w[r][None, :]
-    np.testing.assert_array_equal(host(y), want)
+    np.testing.assert_array_equal(host(y), want if B < 16 else ref.round_to(want, "bf16"))
 
 
 @pytest.mark.parametrize("dt,B,d_in,d_out", [("bf16", 1, 4096, 11008), ("f32", 2, 512, 1536),
-                                              ("bf16", 8, 1024, 520)])
+                                              ("bf16", 8, 1024, 520), ("bf16", 16, 1024, 520),
+                                              ("bf16", 64, 4096, 1032), ("bf16", 33, 300, 8)])
 def test_dense_gemv_parity(dt, B, d_in, d_out):
     rng = np.random.default_rng(B * d_in)
     w = wl.quantize(rng.standard_normal((d_in, d_out)) * 0.02, dt)
