@@ -60,7 +60,13 @@ Prefix prefix_for(int64_t B, int64_t d_in, int64_t d_out, int64_t rows_bound, in
     return at;
   };
   P.mask = take(static_cast<size_t>(B) * mask_words(static_cast<int>(d_in)) * 4);
-  P.gather = take(gather_batch_ws_bytes(static_cast<int>(B), rows_bound, d_out, w_dt));
+  size_t g = gather_batch_ws_bytes(static_cast<int>(B), rows_bound, d_out, w_dt);
+  if (B == 1) {
+    // the one-token product with the selection folded in (same counters)
+    const size_t sg = select_gather_ws_bytes(d_in, d_out, w_dt);
+    g = sg > g ? sg : g;
+  }
+  P.gather = take(g);
   if (mfma_region(B, w_dt)) {
     P.mfma_coef = take(static_cast<size_t>(B) * mfma_coef_ld(rows_bound) * 4);
     size_t parts = rotate_mfma_ws_bound(B, d_in);
@@ -399,6 +405,22 @@ int larosa_layer_forward(const void *x, int act_dtype, const void *Qt, int64_t q
   a.y_dt = act_dtype;
   a.B = static_cast<int>(B);
   a.ws = base + L.p.gather;
+  if (B == 1 && select_gather_supported(d_in)) {
+    // One token: every workgroup of the product computes the exact Top-K rule
+    // itself, so selection and product are one launch.
+    SelectGatherArgs g;
+    g.x_rot = x_rot;
+    g.d_in = static_cast<int>(d_in);
+    g.k = static_cast<int>(k);
+    g.w = W_folded;
+    g.w_dt = w_dtype;
+    g.d_out = d_out;
+    g.y = y;
+    g.y_dt = act_dtype;
+    g.idx_out = idx_out;
+    g.ws = base + L.p.gather;
+    return launched(launch_select_gather(g, s));
+  }
   if (B == 1) {
     e = launch_select(x_rot, 1, static_cast<int>(d_in), static_cast<int>(k), idx, val,
                       nullptr, nullptr, s);

@@ -62,6 +62,30 @@ struct GatherArgs {
 };
 hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
 
+// --- selection folded into the product, one token ---
+struct SelectGatherPlan {
+  int tiles;   // column tiles of 64·V columns
+  int splits;  // channel ranges per tile (partial sums when > 1)
+  int cps;     // channels per range
+};
+SelectGatherPlan plan_select_gather(int64_t d_in, int64_t d_out, int w_dt);
+// Counters (one per column tile, at offset 0, zero between calls) and
+// partial sums.
+size_t select_gather_ws_bytes(int64_t d_in, int64_t d_out, int w_dt);
+bool select_gather_supported(int64_t d_in);
+struct SelectGatherArgs {
+  const float *x_rot;  // [d_in] fp32
+  int d_in, k;
+  const void *w;       // [d_in, d_out]
+  int w_dt;
+  int64_t d_out;
+  void *y;             // [d_out]
+  int y_dt;
+  int32_t *idx_out;    // [k] ascending kept indices, or NULL
+  void *ws;
+};
+hipError_t launch_select_gather(const SelectGatherArgs &a, hipStream_t s);
+
 // --- matrix-core forms for batches of 16..64 tokens in bf16 ---
 constexpr int kMfmaMinB = 16;
 bool mfma_supported(int64_t B, int act_dt, int w_dt);
