@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define LAROSA_ABI_VERSION 1
+#define LAROSA_ABI_VERSION 2
 
 typedef void *larosa_stream_t; /* hipStream_t */
 
@@ -77,7 +77,7 @@ int larosa_abi_version(void);
 const char *larosa_status_string(int status);
 
 /* Bytes of workspace needed by larosa_layer_forward with these sizes in the
- * given mode. It also covers larosa_topk_select, larosa_sparse_gemv and
+ * given mode. It also covers larosa_topk_select, larosa_topk_gemv, larosa_sparse_gemv and
  * larosa_dense_gemv on the same (B, d_in, d_out, k). Returns 0 for invalid
  * sizes. */
 size_t larosa_workspace_bytes(int64_t B, int64_t d_in, int64_t d_out,
@@ -148,6 +148,22 @@ int larosa_sparse_gemv(const int32_t *rows, const int32_t *n_rows,
                        const void *W_folded, int w_dtype, void *y,
                        int y_dtype, int64_t B, int64_t d_in, int64_t d_out,
                        void *ws, size_t ws_bytes, larosa_stream_t stream);
+
+/* Selection folded into the product, for one token (LaRoSA summary page,
+ * 方法详解 · 技术框架: keep the k largest-magnitude rotated entries, set the
+ * rest to zero, so only their rows of the folded weight are read):
+ *   y = Σ_{i ∈ S} x_rot[i] · W'[i, :],  S = Top-k of |x_rot| (the rule of
+ *   larosa_topk_select: fp32 magnitude, equal magnitudes keep the lower index)
+ * x_rot: [d_in] fp32 (one token); W_folded: [d_in, d_out] in w_dtype;
+ * y: [d_out] in y_dtype (F32, or BF16 with BF16 weights), fp32 accumulation.
+ * idx_out: [k] int32, the kept indices ascending, or NULL. One launch:
+ * every workgroup of the product computes the exact rule itself, so no index
+ * list goes through memory. d_in <= 16384 (LAROSA_ERR_SHAPE above). ws:
+ * workspace of larosa_workspace_bytes(1, d_in, d_out, k, …). */
+int larosa_topk_gemv(const float *x_rot, int64_t d_in, int64_t k,
+                     const void *W_folded, int w_dtype, void *y, int y_dtype,
+                     int64_t d_out, int32_t *idx_out, void *ws, size_t ws_bytes,
+                     larosa_stream_t stream);
 
 /* One rotated sparse linear: rotate → select → (row union when B > 1) →
  * gather, for every projection that shares the input x. W_folded is the

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblarosa.s
 
 F32, BF16 = 0, 1
 UNFUSED, FUSED = 0, 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _c_i64 = ctypes.c_int64
 _c_int = ctypes.c_int
@@ -39,6 +39,8 @@ SIGNATURES = {
                                     _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
     "larosa_sparse_gemv": (_c_int, [_c_vp, _c_vp, _c_i64, _c_vp, _c_vp, _c_int, _c_vp, _c_int,
                                     _c_i64, _c_i64, _c_i64, _c_vp, _c_sz, _c_vp]),
+    "larosa_topk_gemv": (_c_int, [_c_vp, _c_i64, _c_i64, _c_vp, _c_int, _c_vp, _c_int, _c_i64,
+                                  _c_vp, _c_vp, _c_sz, _c_vp]),
     "larosa_layer_forward": (_c_int, [_c_vp, _c_int, _c_vp, _c_i64, _c_vp, _c_int, _c_i64,
                                       _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_int,
                                       _c_vp, _c_sz, _c_vp]),
@@ -160,6 +162,14 @@ def larosa_sparse_gemv(rows, n_rows, max_rows: int, coef, W_folded, y, B: int, d
            load().larosa_sparse_gemv(_ptr(rows), _ptr(n_rows), max_rows, _ptr(coef),
                                      _ptr(W_folded), _dt(W_folded), _ptr(y), _dt(y), B, d_in,
                                      d_out, _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def larosa_topk_gemv(x_rot, d_in: int, k: int, W_folded, y, d_out: int, idx_out=None, ws=None,
+                     stream=None) -> None:
+    _check("larosa_topk_gemv",
+           load().larosa_topk_gemv(_ptr(x_rot), d_in, k, _ptr(W_folded), _dt(W_folded), _ptr(y),
+                                   _dt(y), d_out, _ptr(idx_out), _ptr(ws), _nbytes(ws),
+                                   _stream(stream)))
 
 
 def larosa_layer_forward(x, Qt, q_block: int, W_folded, B: int, d_in: int, d_out: int, k: int,

@@ -296,6 +296,35 @@ int larosa_sparse_gemv(const int32_t *rows, const int32_t *n_rows, int64_t max_r
   return launched(launch_gather(a, s));
 }
 
+int larosa_topk_gemv(const float *x_rot, int64_t d_in, int64_t k, const void *W_folded,
+                     int w_dtype, void *y, int y_dtype, int64_t d_out, int32_t *idx_out,
+                     void *ws, size_t ws_bytes, larosa_stream_t stream) {
+  if (!dtype_ok(w_dtype) || !dtype_ok(y_dtype)) return LAROSA_ERR_DTYPE;
+  if (w_dtype == LAROSA_F32 && y_dtype == LAROSA_BF16) return LAROSA_ERR_DTYPE;
+  if (int st = check_sizes(1, d_in, k)) return st;
+  if (!select_gather_supported(d_in)) return LAROSA_ERR_SHAPE;
+  if (d_out < 1) return LAROSA_ERR_SHAPE;
+  if (!x_rot || !W_folded || !y) return LAROSA_ERR_INVALID_ARG;
+  if (d_out % vec_of(w_dtype)) return LAROSA_ERR_ALIGNMENT;
+  if (!aligned16(x_rot) || !aligned16(W_folded) || !aligned16(y)) return LAROSA_ERR_ALIGNMENT;
+  const Prefix P = prefix_for(1, d_in, d_out, d_in, w_dtype);
+  if (!ws || ws_bytes < P.end) return LAROSA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return LAROSA_ERR_ALIGNMENT;
+  if (int st = device_status()) return st;
+  SelectGatherArgs g;
+  g.x_rot = x_rot;
+  g.d_in = static_cast<int>(d_in);
+  g.k = static_cast<int>(k);
+  g.w = W_folded;
+  g.w_dt = w_dtype;
+  g.d_out = d_out;
+  g.y = y;
+  g.y_dt = y_dtype;
+  g.idx_out = idx_out;
+  g.ws = static_cast<char *>(ws) + P.gather;
+  return launched(launch_select_gather(g, stream_of(stream)));
+}
+
 int larosa_dense_gemv(const void *x, int act_dtype, const void *W, int w_dtype, void *y,
                       int64_t B, int64_t d_in, int64_t d_out, void *ws, size_t ws_bytes,
                       larosa_stream_t stream) {

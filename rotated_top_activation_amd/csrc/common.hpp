@@ -57,13 +57,19 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Inclusive prefix sum over the lanes of a wave (lane order).
+// Inclusive prefix sum over the lanes of a wave (lane order), with DPP
+// lane moves (register to register, no LDS round trip): shifts by 1, 2, 4
+// and 8 lanes within each 16-lane row (lanes shifted in from outside the row
+// read 0), then the last lane of row 0 added to row 1 and of row 2 to row 3
+// (row_bcast:15), then lane 31 added to rows 2 and 3 (row_bcast:31).
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    uint32_t t = __shfl_up(v, off, kWave);
-    if (lane >= off) v += t;
-  }
+  (void)lane;
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x111, 0xF, 0xF, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x112, 0xF, 0xF, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x114, 0xF, 0xF, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x118, 0xF, 0xF, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x142, 0xA, 0xF, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x143, 0xC, 0xF, false));
   return v;
 }
 

@@ -23,15 +23,21 @@ constexpr uint32_t kNoKey = 0x80000000u;
 // so 64 lanes reading 32 consecutive bins each hit distinct banks.
 __device__ __forceinline__ int pad_bin(int b) { return b + (b >> 5); }
 
+// Bin counted for slots that hold no channel (never searched).
+constexpr int kDummyBin = 2048;
+
 template <int NT> struct SelectSmem {
-  uint32_t hist[2048 + 64];
+  uint32_t hist[2048 + 64 + 4];  // 2048 padded bins, then the dummy bin
   uint32_t wave_tot[NT / kWave];
   uint32_t bin, above, count;
 };
 
-// Inclusive scan over the NT threads of the block (thread order).
+// Inclusive scan over the NT threads of the block (thread order). With
+// trailing_barrier == false the caller must place a barrier before wave_tot
+// is written again.
 template <int NT>
-__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t *wave_tot) {
+__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t *wave_tot,
+                                                    bool trailing_barrier = true) {
   const int lane = threadIdx.x % kWave;
   const int w = threadIdx.x / kWave;
   uint32_t x = wave_incl_scan(v, lane);
@@ -40,38 +46,48 @@ __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t *wave_t
   uint32_t off = 0;
 #pragma unroll
   for (int i = 0; i < NT / kWave; ++i) off += i < w ? wave_tot[i] : 0u;
-  __syncthreads();  // wave_tot may be rewritten by the next scan
+  if (trailing_barrier) __syncthreads();  // wave_tot may be rewritten by the next scan
   return x + off;
 }
 
-// Suffix search over the 2048 bins in sm.hist, done by wave 0 alone (the
-// other waves wait at the closing barrier): the bin holding the krem-th
-// largest key and the number of keys in higher bins, left in sm.bin and
-// sm.above. Lane l first sums chunk 63 − l (32 bins), so lane order runs
-// from the highest chunk down; a wave scan finds the chunk that crosses
-// krem, then a second scan over that chunk's bins (highest first) finds the
-// bin.
+// Suffix search over the 2048 bins in sm.hist by the whole block: the bin
+// holding the krem-th largest key and the number of keys in higher bins,
+// left in sm.bin and sm.above (sm.count: that bin's count). Thread t owns
+// the 2048/NT consecutive bins just below bin 2048 − t·(2048/NT), so thread
+// order runs from the highest bin down; one block scan of the per-thread
+// sums finds the thread whose bins cross krem (exactly one thread has
+// excl < krem <= incl when 1 <= krem <= total), which then walks its own
+// bins. Requires 1 <= krem <= the number of counted keys; otherwise the
+// result is bin 0 with nothing above it (in range, but meaningless).
 template <int NT>
 __device__ __forceinline__ void suffix_search(uint32_t krem, SelectSmem<NT> &sm) {
-  if (threadIdx.x < kWave) {
-    const int lane = threadIdx.x;
-    const int chunk = 63 - lane;
-    uint32_t s = 0;
+  static_assert(2048 % NT == 0 && NT <= 2048, "block size must divide 2048");
+  constexpr int BP = 2048 / NT;
+  const int top = 2047 - static_cast<int>(threadIdx.x) * BP;  // highest bin of this thread
+  if (threadIdx.x == 0) {  // ordered before the crossing thread's write by the scan's barriers
+    sm.bin = 0u;
+    sm.above = 0u;
+    sm.count = 0u;
+  }
+  uint32_t h[BP];
+  uint32_t s = 0;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) s += sm.hist[pad_bin(chunk * 32 + i)];
-    const uint32_t incl = wave_incl_scan(s, lane);
-    const uint64_t cross = __ballot(incl >= krem);
-    const int L = __ffsll(static_cast<unsigned long long>(cross)) - 1;  // krem <= total
-    const uint32_t above_chunk = __shfl(incl - s, L, kWave);
-    const int c = 63 - L;
-    const uint32_t v = lane < 32 ? sm.hist[pad_bin(c * 32 + 31 - lane)] : 0u;
-    const uint32_t incl2 = wave_incl_scan(v, lane);
-    const uint64_t cross2 = __ballot(lane < 32 && above_chunk + incl2 >= krem);
-    const int L2 = __ffsll(static_cast<unsigned long long>(cross2)) - 1;
-    if (lane == L2) {
-      sm.bin = static_cast<uint32_t>(c * 32 + 31 - lane);
-      sm.above = above_chunk + incl2 - v;
-      sm.count = v;
+  for (int i = 0; i < BP; ++i) {
+    h[i] = sm.hist[pad_bin(top - i)];
+    s += h[i];
+  }
+  // no trailing barrier: the one closing this function comes first
+  const uint32_t incl = block_incl_scan<NT>(s, sm.wave_tot, false);
+  uint32_t above = incl - s;
+  if (above < krem && incl >= krem) {
+#pragma unroll
+    for (int i = 0; i < BP; ++i) {
+      if (above < krem && above + h[i] >= krem) {
+        sm.bin = static_cast<uint32_t>(top - i);
+        sm.above = above;
+        sm.count = h[i];
+      }
+      above += h[i];
     }
   }
   __syncthreads();
@@ -240,6 +256,133 @@ __device__ __forceinline__ void kept_flags(const uint32_t (&key)[EMAX], uint32_t
     }
     kept[e] = kp;
   }
+}
+
+// ---- Exact rule from a short candidate list ------------------------------
+// After the first digit, only the channels whose first digit equals the
+// boundary digit can still be in or out; on typical activations they are a
+// few hundred. They are compacted (in index order) into LDS, and the later
+// digits and the tie cut-off are resolved on that list with one or two
+// entries per thread instead of every slot of every thread.
+constexpr int kCandMax = 2048;
+
+struct CandSmem {
+  uint32_t key[kCandMax];
+  uint32_t idx[kCandMax];
+};
+
+// The exact Top-k rule of the keys held by the block (slots [0, E) of each
+// thread hold channels i0 + e; other slots and slots past d hold kNoKey):
+// channel i with key κ is kept iff κ > T, or κ == T and i <= cut. Requires
+// 1 <= k <= the number of channels. Taken in two steps so that a caller can
+// act on the first digit (every channel whose first digit is above the
+// boundary digit is kept) before the rest is resolved.
+struct RuleState {
+  uint32_t prefix, pmask, krem, n_cand;
+};
+
+// Step 1: the first digit (key bits 30..20) over every slot. The boundary
+// digit is st.prefix >> 20; st.n_cand channels share it.
+template <int NT, int EMAX>
+__device__ __forceinline__ RuleState rule_first_digit(const uint32_t (&key)[EMAX], int E,
+                                                      uint32_t k, SelectSmem<NT> &sm) {
+  radix_clear<NT>(sm);
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) {
+    if (e < E) {  // empty slots go to the dummy bin
+      const int b = (key[e] & kNoKey) ? kDummyBin : static_cast<int>(key[e] >> radix_shift(0));
+      atomicAdd(&sm.hist[pad_bin(b)], 1u);
+    }
+  }
+  __syncthreads();
+  RuleState st{0u, kNoKey, k, 0u};
+  st.n_cand = radix_resolve<NT>(0, st.prefix, st.pmask, st.krem, sm);
+  return st;
+}
+
+// Step 2: the later digits and the tie cut-off. Every thread gets T and cut.
+template <int NT, int EMAX>
+__device__ __forceinline__ void rule_finish(const uint32_t (&key)[EMAX], int E, int i0,
+                                            RuleState st, SelectSmem<NT> &sm, CandSmem &cs,
+                                            uint32_t &T, uint32_t &cut) {
+  static_assert(kCandMax % NT == 0, "candidates per thread must be whole");
+  constexpr int CPT = kCandMax / NT;
+  const int t = threadIdx.x;
+  uint32_t prefix = st.prefix, pmask = st.pmask, krem = st.krem;
+  const uint32_t n_cand = st.n_cand;
+  const uint32_t digit0 = prefix >> radix_shift(0);
+  if (n_cand > static_cast<uint32_t>(kCandMax)) {
+    // many equal first digits (tie-heavy data): the later digits on the slots
+    uint32_t n_eq;
+    radix_threshold_from<NT, EMAX>(key, 1, prefix, pmask, krem, sm, T, krem, n_eq);
+    cut = tie_cutoff<NT, EMAX>(key, i0, T, krem, sm);
+    return;
+  }
+  // compact the candidates in index order; an empty slot has first digit 0x800
+  uint32_t nc = 0;
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e)
+    if (e < E) nc += (key[e] >> radix_shift(0)) == digit0;
+  {
+    uint32_t p = block_incl_scan<NT>(nc, sm.wave_tot) - nc;
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) {
+      if (e < E && (key[e] >> radix_shift(0)) == digit0) {
+        cs.key[p] = key[e];
+        cs.idx[p] = static_cast<uint32_t>(i0 + e);
+        ++p;
+      }
+    }
+  }
+  __syncthreads();
+  // the later digits over the candidates
+  for (int pass = 1; pass < 3; ++pass) {
+    radix_clear<NT>(sm);
+    __syncthreads();
+    for (int j = t; j < static_cast<int>(n_cand); j += NT) radix_count<NT>(cs.key[j], pass, prefix, pmask, sm);
+    __syncthreads();
+    radix_resolve<NT>(pass, prefix, pmask, krem, sm);
+  }
+  T = prefix;
+  // the krem-th candidate equal to T in index order is the last one kept
+  uint32_t eq = 0;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int j = t * CPT + c;
+    eq += j < static_cast<int>(n_cand) && cs.key[j] == T;
+  }
+  const uint32_t incl = block_incl_scan<NT>(eq, sm.wave_tot);
+  uint32_t before = incl - eq;
+  if (before < krem && incl >= krem) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int j = t * CPT + c;
+      if (j < static_cast<int>(n_cand) && cs.key[j] == T) {
+        ++before;
+        if (before == krem) sm.bin = cs.idx[j];
+      }
+    }
+  }
+  __syncthreads();
+  cut = sm.bin;
+  __syncthreads();
+}
+
+template <int NT, int EMAX>
+__device__ __forceinline__ void topk_rule(const uint32_t (&key)[EMAX], int E, int i0, uint32_t k,
+                                          SelectSmem<NT> &sm, CandSmem &cs, uint32_t &T,
+                                          uint32_t &cut) {
+  const RuleState st = rule_first_digit<NT, EMAX>(key, E, k, sm);
+  rule_finish<NT, EMAX>(key, E, i0, st, sm, cs, T, cut);
+}
+
+// Whether slot e (channel i0 + e) is kept under the rule (T, cut).
+template <int EMAX>
+__device__ __forceinline__ bool rule_keeps(const uint32_t (&key)[EMAX], int e, int E, int i0,
+                                           uint32_t T, uint32_t cut) {
+  return e < E && !(key[e] & kNoKey) &&
+         (key[e] > T || (key[e] == T && static_cast<uint32_t>(i0 + e) <= cut));
 }
 
 }  // namespace larosa

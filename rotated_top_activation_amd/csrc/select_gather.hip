@@ -31,6 +31,7 @@ constexpr int kSgWaves = 16;
 constexpr int kSgThreads = kSgWaves * kWave;
 constexpr int kSgRows = 8;        // kept rows per wave group (loads in flight per lane)
 constexpr int kSgListMax = 4096;  // channels of one split (LDS row list)
+constexpr int kSgKeysMax = 16384; // channels of the LDS copy of the rotated vector
 constexpr int kSgMaxSplitLoads = 16;
 
 size_t sg_counter_bytes(int tiles) { return (static_cast<size_t>(tiles) * 4 + 255) / 256 * 256; }
@@ -42,11 +43,18 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
     uint32_t *__restrict__ counters, int32_t *__restrict__ idx_out) {
   constexpr int V = Elt<WT>::kVec;
   constexpr int TILE = kWave * V;
+  constexpr int R = kSgRows;
+  static_assert(kSgListMax % R == 0, "row groups must not straddle the list's end");
   __shared__ SelectSmem<kSgThreads> sm;
+  __shared__ CandSmem cs;
   __shared__ int32_t l_idx[kSgListMax];
   __shared__ float l_val[kSgListMax];
-  __shared__ float red[kSgWaves][TILE];
-  __shared__ uint32_t s_p0, s_p1;
+  // The rotated vector as loaded (fp32 bits, sign included), for the list
+  // build; after that the same bytes hold the waves' sums.
+  constexpr int KV_WORDS = kSgKeysMax > kSgWaves * TILE ? kSgKeysMax : kSgWaves * TILE;
+  __shared__ __align__(16) uint32_t kv[KV_WORDS];
+  float(*red)[TILE] = reinterpret_cast<float(*)[TILE]>(kv);
+  __shared__ uint32_t s_carry;
   __shared__ int s_last;
 
   const int t = threadIdx.x;
@@ -56,76 +64,138 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
   const int split = blockIdx.x / tiles;
   const int c0 = split * cps < d ? split * cps : d;
   const int c1 = c0 + cps < d ? c0 + cps : d;
-
-  // 1. The exact rule over all d channels: T, and krem channels equal to T
-  //    kept in index order. kept_flags also gives each thread the number of
-  //    kept channels below its first slot.
-  float v[EMAX];
-  uint32_t key[EMAX];
-  load_keys4<EMAX>(x_rot, d, E, key, v);
-  uint32_t T, krem, n_eq;
-  radix_threshold<kSgThreads, EMAX>(key, static_cast<uint32_t>(k), sm, T, krem, n_eq);
-  bool kept[EMAX];
-  uint32_t pos;
-  kept_flags<kSgThreads, EMAX>(key, T, krem, sm, kept, pos);
-
-  // 2. Positions of this split's first and last kept channel in the global
-  //    ascending list, then its kept channels into LDS (and, from tile 0, the
-  //    global index list when asked for).
   const int i0 = t * E;
-  if (t == 0) {
-    if (c0 >= d) s_p0 = static_cast<uint32_t>(k);
-    if (c1 >= d) s_p1 = static_cast<uint32_t>(k);
-  }
-  {
-    uint32_t p = pos;
-#pragma unroll
-    for (int e = 0; e < EMAX; ++e) {
-      const int i = i0 + e;
-      if (e < E && i < d && i == c0) s_p0 = p;
-      if (e < E && i < d && i == c1) s_p1 = p;
-      if (kept[e]) ++p;
-    }
-  }
-  __syncthreads();
-  const uint32_t p0 = s_p0;
-  const int n_list = static_cast<int>(s_p1 - p0);
-  {
-    uint32_t p = pos;
-#pragma unroll
-    for (int e = 0; e < EMAX; ++e) {
-      if (!kept[e]) continue;
-      const int i = i0 + e;
-      if (i >= c0 && i < c1) {
-        l_idx[p - p0] = i;
-        l_val[p - p0] = v[e];
-      }
-      if (idx_out && tile == 0 && i >= c0 && i < c1) idx_out[p] = i;
-      ++p;
-    }
-  }
-  __syncthreads();
 
-  // 3. Stream the kept rows of this column tile. Lanes past the last column
-  //    read a valid column and store nothing.
+  // Keys in registers; the signs are kept as one bit per slot (the value of
+  // a slot is its key with the sign bit put back), which saves registers.
+  uint32_t key[EMAX];
+  {
+    float v[EMAX];
+    load_keys4<EMAX>(x_rot, d, E, key, v);
+    // whole 16-byte quads: E and d are multiples of 4
+#pragma unroll
+    for (int q = 0; q < EMAX / 4; ++q)
+      if (4 * q < E && i0 + 4 * q < d)
+        *reinterpret_cast<uint4 *>(&kv[i0 + 4 * q]) =
+            make_uint4(__float_as_uint(v[4 * q]), __float_as_uint(v[4 * q + 1]),
+                       __float_as_uint(v[4 * q + 2]), __float_as_uint(v[4 * q + 3]));
+  }
+
+  // A chunked ordered compaction over the LDS copy: emit(i, pos) for every
+  // channel i of [a, b) with pred(i), pos counting from 0 in index order, one
+  // channel per thread and chunk. Returns the count.
+  auto compact = [&](int a, int b, auto pred, auto emit) {
+    uint32_t carry = 0;
+    for (int b0 = a; b0 < b; b0 += kSgThreads) {
+      const int i = b0 + t;
+      const uint32_t kp = i < b && pred(i);
+      const uint32_t incl = block_incl_scan<kSgThreads>(kp, sm.wave_tot);
+      if (kp) emit(i, carry + incl - 1);
+      if (t == kSgThreads - 1) s_carry = incl;
+      __syncthreads();
+      carry += s_carry;
+      __syncthreads();  // s_carry is rewritten by the next chunk
+    }
+    return carry;
+  };
+  auto key_of = [&](int i) { return kv[i] & 0x7FFFFFFFu; };
+
+  // 1. First digit of the rule over all d channels (the same in every
+  //    workgroup). A channel whose first digit is above the boundary digit
+  //    is kept whatever its later digits.
+  const RuleState st = rule_first_digit<kSgThreads, EMAX>(key, E, static_cast<uint32_t>(k), sm);
+  const uint32_t digit0 = st.prefix >> radix_shift(0);
+
+  // 2. This split's certain rows, ascending, at the head of the LDS list.
+  const int n_cert = static_cast<int>(compact(
+      c0, c1, [&](int i) { return (key_of(i) >> radix_shift(0)) > digit0; },
+      [&](int i, uint32_t pos) {
+        l_idx[pos] = i;
+        l_val[pos] = __uint_as_float(kv[i]);
+      }));
+
+  // 3. Start streaming: this wave's first group of certain rows is loaded
+  //    now, so the rest of the rule is resolved while they are in flight.
+  //    Lanes past the last column read a valid column and store nothing.
   const int64_t col_raw = static_cast<int64_t>(tile) * TILE + lane * V;
   const int64_t col = col_raw < d_out ? col_raw : d_out - V;
+  uint4 q0[R];
+  float cf0[R];
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    const int j = wave * R + u;  // wave-uniform
+    const bool ok = j < n_cert;
+    const int row = ok ? l_idx[j] : 0;
+    cf0[u] = ok ? l_val[j] : 0.f;
+    q0[u] = ok ? load16(w + static_cast<int64_t>(row) * d_out + col) : make_uint4(0, 0, 0, 0);
+  }
+
+  // 4. The rest of the rule: T, and channels equal to T kept up to `cut`.
+  uint32_t T, cut;
+  rule_finish<kSgThreads, EMAX>(key, E, i0, st, sm, cs, T, cut);
+  auto keeps = [&](int i) {
+    const uint32_t kk = key_of(i);
+    return kk > T || (kk == T && static_cast<uint32_t>(i) <= cut);
+  };
+
+  // 5. The split's kept channels of the boundary digit follow the certain
+  //    ones; tile 0 also writes the global ascending index list (parity
+  //    checks): the positions of this split's channels follow from the
+  //    channels below c1.
+  const int n_list = n_cert + static_cast<int>(compact(
+      c0, c1, [&](int i) { return (key_of(i) >> radix_shift(0)) == digit0 && keeps(i); },
+      [&](int i, uint32_t pos) {
+        l_idx[n_cert + pos] = i;
+        l_val[n_cert + pos] = __uint_as_float(kv[i]);
+      }));
+  if (idx_out != nullptr && tile == 0)
+    compact(0, c1, keeps, [&](int i, uint32_t pos) {
+      if (i >= c0) idx_out[pos] = i;
+    });
+  __syncthreads();  // the vector's LDS copy becomes the waves' sum area
+
+  // 6. Stream the split's kept rows of this column tile: the first group
+  //    (completed from the list where the certain rows ran out), then
+  //    interleaved groups of R rows per wave, all R loads in flight.
   float acc[V];
 #pragma unroll
   for (int q = 0; q < V; ++q) acc[q] = 0.f;
-  for (int base = wave * kSgRows; base < n_list; base += kSgWaves * kSgRows) {
-    uint4 q[kSgRows];
-    float c[kSgRows];
+  {
 #pragma unroll
-    for (int u = 0; u < kSgRows; ++u) {
-      const int j = base + u;  // wave-uniform
-      const bool ok = j < n_list;
-      const int row = ok ? l_idx[j] : 0;
-      c[u] = ok ? l_val[j] : 0.f;
-      q[u] = ok ? load16(w + static_cast<int64_t>(row) * d_out + col) : make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < R; ++u) {
+      const int j = wave * R + u;
+      if (j >= n_cert && j < n_list) {
+        cf0[u] = l_val[j];
+        q0[u] = load16(w + static_cast<int64_t>(l_idx[j]) * d_out + col);
+      }
     }
 #pragma unroll
-    for (int u = 0; u < kSgRows; ++u) {
+    for (int u = 0; u < R; ++u) {
+      float f[V];
+      Elt<WT>::unpack(q0[u], f);
+#pragma unroll
+      for (int qq = 0; qq < V; ++qq) acc[qq] = fmaf(cf0[u], f[qq], acc[qq]);
+    }
+  }
+  for (int base = (kSgWaves + wave) * R; base < n_list; base += kSgWaves * R) {
+    // base is a multiple of R below n_list <= kSgListMax, so the R list
+    // entries read here are in bounds (entries past n_list are not used).
+    int rows[R];
+    float c[R];
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      rows[u] = l_idx[base + u];
+      c[u] = l_val[base + u];
+    }
+    uint4 q[R];
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const bool ok = base + u < n_list;  // wave-uniform
+      c[u] = ok ? c[u] : 0.f;
+      q[u] = ok ? load16(w + static_cast<int64_t>(rows[u]) * d_out + col) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
       float f[V];
       Elt<WT>::unpack(q[u], f);
 #pragma unroll
@@ -207,7 +277,6 @@ hipError_t launch_sg_t(const SelectGatherArgs &a, const SelectGatherPlan &p, hip
   if (E <= 4) LAROSA_SG(4);
   else if (E <= 8) LAROSA_SG(8);
   else if (E <= 16) LAROSA_SG(16);
-  else if (E <= 32) LAROSA_SG(32);
   else return hipErrorInvalidValue;
 #undef LAROSA_SG
   return hipGetLastError();
@@ -237,7 +306,7 @@ size_t select_gather_ws_bytes(int64_t d_in, int64_t d_out, int w_dt) {
   return sg_counter_bytes(p.tiles) + static_cast<size_t>(p.splits) * d_out * sizeof(float);
 }
 
-bool select_gather_supported(int64_t d_in) { return d_in >= 1 && d_in <= 32768; }
+bool select_gather_supported(int64_t d_in) { return d_in >= 1 && d_in <= kSgKeysMax; }
 
 hipError_t launch_select_gather(const SelectGatherArgs &a, hipStream_t s) {
   const SelectGatherPlan p = plan_select_gather(a.d_in, a.d_out, a.w_dt);

@@ -103,6 +103,15 @@ def test_standalone_calls_validation(lib):
     assert lib.larosa_sparse_gemv(P, None, -1, P, P, 1, P, 1, 1, 128, 64, P, 1 << 20,
                                   None) == INVALID
     assert lib.larosa_dense_gemv(P, 1, P, 0, P, 1, 128, 64, P, 1 << 20, None) == DTYPE
+    # selection folded into the product (one token)
+    assert lib.larosa_topk_gemv(P, 128, 0, P, 1, P, 1, 64, None, P, 1 << 20, None) == INVALID
+    assert lib.larosa_topk_gemv(P, 128, 129, P, 1, P, 1, 64, None, P, 1 << 20, None) == INVALID
+    assert lib.larosa_topk_gemv(P, 20000, 10, P, 1, P, 1, 64, None, P, 1 << 20, None) == SHAPE
+    assert lib.larosa_topk_gemv(P, 128, 10, P, 0, P, 1, 64, None, P, 1 << 20, None) == DTYPE
+    assert lib.larosa_topk_gemv(P, 128, 10, P, 1, P, 1, 60, None, P, 1 << 20, None) == ALIGN
+    assert lib.larosa_topk_gemv(PM, 128, 10, P, 1, P, 1, 64, None, P, 1 << 20, None) == ALIGN
+    assert lib.larosa_topk_gemv(P, 128, 10, P, 1, P, 1, 64, None, P, 16, None) == WS
+    assert lib.larosa_topk_gemv(None, 128, 10, P, 1, P, 1, 64, None, P, 1 << 20, None) == INVALID
     assert lib.larosa_fold_weights(P, 64, P, P, 128, 64, 1, None) == INVALID   # aliasing
     assert lib.larosa_prepare_rotation(P, P + 16, 128, 64, 1, None) == INVALID  # overlap
     assert lib.larosa_prepare_rotation(P, P + (1 << 20), 128, 48, 1, None) == SHAPE
@@ -117,3 +126,4 @@ def test_no_device_is_reported_not_crashed(lib):
         pytest.skip("a GPU is visible")
     assert _lf(lib) == NODEV
     assert lib.larosa_swiglu(P, P + (1 << 20), 1, 64, 1, None) == NODEV
+    assert lib.larosa_topk_gemv(P, 128, 10, P, 1, P, 1, 64, None, P, 1 << 20, None) == NODEV

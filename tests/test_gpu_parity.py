@@ -234,6 +234,43 @@ def test_sparse_gemv_parity(dt, d_in, d_out, k):
     assert ok()
 
 
+TOPK_GEMV_CASES = [
+    # (weight dtype, d_in, d_out, k, activation kind)
+    ("bf16", 4096, 22016, 2457, "heavy"), ("bf16", 11008, 4096, 6604, "gauss"),
+    ("f32", 512, 1536, 307, "heavy"), ("bf16", 16384, 520, 9000, "heavy"),
+    ("bf16", 1000, 1544, 1, "gauss"), ("bf16", 300, 8, 300, "heavy"),
+    ("bf16", 4100, 2056, 1700, "ties"), ("bf16", 12288, 1032, 6000, "ties"),
+    ("bf16", 2048, 11008, 2047, "gauss"),
+]
+
+
+@pytest.mark.parametrize("dt,d_in,d_out,k,kind", TOPK_GEMV_CASES)
+def test_topk_gemv_selection_exact_and_product_within_tolerance(dt, d_in, d_out, k, kind):
+    """The one-token selection folded into the product: the kept index list
+    equals the oracle's selection bit for bit (ties included), the output is
+    within tolerance of the oracle's product over those rows, and a second
+    call on the same workspace gives identical bits."""
+    rng = np.random.default_rng(d_in * 7 + k)
+    w = wl.quantize(rng.standard_normal((d_in, d_out)) * 0.02, dt)
+    xr = make_x_rot(kind, 1, d_in, seed=d_in + k)
+    ydt = torch.float32 if dt == "f32" else torch.bfloat16
+    y, ok_y = guarded((d_out,), ydt)
+    idx, ok_i = guarded((k,), torch.int32, fill=-5)
+    ws = _gather_ws(1, d_in, d_out, k)
+    xr_d = torch.from_numpy(xr[0]).cuda()
+    w_d = dev(w, dt)
+    _lib.larosa_topk_gemv(xr_d, d_in, k, w_d, y, d_out, idx_out=idx, ws=ws)
+    y2 = torch.empty_like(y)
+    _lib.larosa_topk_gemv(xr_d, d_in, k, w_d, y2, d_out, ws=ws)
+    torch.cuda.synchronize()
+    assert ok_y() and ok_i()
+    want_idx = ref.select(xr, k)
+    np.testing.assert_array_equal(host(idx)[None, :], want_idx)
+    want = ref.round_to(ref.gather_product(xr, want_idx, w), dt)
+    assert ref.rel_error(host(y)[None, :], want) <= (1e-5 if dt == "f32" else 2e-2)
+    assert torch.equal(y, y2)
+
+
 @pytest.mark.parametrize("B,d_in,d_out,k", [(16, 4096, 22016, 2457), (40, 4096, 1032, 1000),
                                              (64, 2048, 4104, 1024), (17, 11008, 4096, 6604)])
 def test_sparse_gemv_batched_union_parity(B, d_in, d_out, k):
