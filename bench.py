@@ -119,6 +119,13 @@ def main():
     copies = a.copies or max(2, math.ceil((5 << 29) / per_copy) + 1)
     qt1 = [l1.Qt] + [l1.Qt.clone() for _ in range(copies - 1)]
     wf1 = [l1.Wf] + [l1.Wf.clone() for _ in range(copies - 1)]
+    # gate|up folded weight with gate and up columns interleaved, so the
+    # product writes SiLU(gate)·up directly
+    wil1 = []
+    for c in range(copies):
+        t = torch.empty_like(l1.Wf)
+        _lib.larosa_interleave_gate_up(wf1[c], t, case.d, case.f)
+        wil1.append(t)
     qt2 = [l2.Qt] + [l2.Qt.clone() for _ in range(copies - 1)]
     wf2 = [l2.Wf] + [l2.Wf.clone() for _ in range(copies - 1)]
 
@@ -129,12 +136,13 @@ def main():
     y = torch.empty((1, d), dtype=torch.bfloat16, device=dev)
     ws1 = l1.workspace(1, _lib.FUSED)
     ws2 = l2.workspace(1, _lib.FUSED)
+    ws1s = torch.zeros(_lib.larosa_swiglu_workspace_bytes(1, d, f, case.k1, _lib.FUSED),
+                       dtype=torch.uint8, device=dev)
 
     def step(i, mode):
         c = i % copies
-        _lib.larosa_layer_forward(x_d, qt1[c], l1.q_block, wf1[c], 1, d, 2 * f, case.k1, gu,
-                                  mode=mode, ws=ws1)
-        _lib.larosa_swiglu(gu, h, 1, f)
+        _lib.larosa_swiglu_layer_forward(x_d, qt1[c], l1.q_block, wil1[c], 1, d, f, case.k1, h,
+                                         mode=mode, ws=ws1s)
         _lib.larosa_layer_forward(h, qt2[c], l2.q_block, wf2[c], 1, f, d, case.k2, y,
                                   mode=mode, ws=ws2)
 
@@ -194,7 +202,7 @@ def main():
     _lib.larosa_rotate(x_d, l1.Qt, l1.q_block, xr1, 1, d)
     _lib.larosa_topk_select(xr1, 1, d, case.k1, idx1, val1)
     xr2 = torch.empty((1, f), dtype=torch.float32, device=dev)
-    step(0, _lib.UNFUSED)
+    step(0, _lib.UNFUSED)  # h of this input
     _lib.larosa_rotate(h, l2.Qt, l2.q_block, xr2, 1, f)
     torch.cuda.synchronize()
 
@@ -241,7 +249,7 @@ def main():
     stage["rotate1"] = timed(lambda i: _lib.larosa_rotate(x_d, qt1[i % copies], l1.q_block, xr1,
                                                           1, d), a.steps, a.warmup)
     stage["select_gather1"] = topk1_ms
-    stage["swiglu"] = timed(lambda i: _lib.larosa_swiglu(gu, h, 1, f), a.steps, a.warmup)
+    stage["swiglu_alone"] = timed(lambda i: _lib.larosa_swiglu(gu, h, 1, f), a.steps, a.warmup)
     stage["rotate2"] = timed(lambda i: _lib.larosa_rotate(h, qt2[i % copies], l2.q_block, xr2,
                                                           1, f), a.steps, a.warmup)
     stage["select_gather2"] = timed(topk2, a.steps, a.warmup)

@@ -197,6 +197,42 @@ int larosa_dense_gemv(const void *x, int act_dtype, const void *W,
 int larosa_swiglu(const void *gu, void *h, int64_t B, int64_t f, int dtype,
                   larosa_stream_t stream);
 
+/* ---- The gate|up linear of a SwiGLU MLP with SiLU(gate)·up folded in ----
+ * The method sparsifies the input of every linear (LaRoSA summary page,
+ * 方法详解 · 技术框架); in a SwiGLU MLP the gate and up projections share one
+ * input, and their outputs meet only in h = SiLU(gate)·up, which is the
+ * input of the down projection. Storing the folded [W'_gate | W'_up] with
+ * the two halves' columns interleaved in blocks (256 columns for bf16
+ * weights, 128 for fp32: half a product column tile) lets the product write
+ * h directly. */
+
+/* W_il[r, (i / b)·2b + i mod b] = W[r, i] (gate) and W_il[r, (i / b)·2b + b
+ * + i mod b] = W[r, f + i] (up) for the block b above; W: [d_in, 2f] =
+ * [gate | up] (folded or not: the permutation acts on columns only). f must
+ * be a multiple of b (LAROSA_ERR_SHAPE otherwise); W and W_il must not
+ * overlap. Offline; not on the hot path. */
+int larosa_interleave_gate_up(const void *W, void *W_il, int64_t d_in, int64_t f, int dtype,
+                              larosa_stream_t stream);
+
+/* Workspace for larosa_swiglu_layer_forward: the layer's own
+ * (larosa_workspace_bytes(B, d_in, 2f, k, mode)) plus room for the gate|up
+ * rows. 0 for invalid sizes. */
+size_t larosa_swiglu_workspace_bytes(int64_t B, int64_t d_in, int64_t f, int64_t k, int mode);
+
+/* h[b, i] = SiLU(g[b, i])·u[b, i] with [g | u] = larosa_layer_forward of x
+ * over the interleaved folded weight W_il ([d_in, 2f], see above): g and u
+ * are rounded to act_dtype first, exactly as larosa_layer_forward followed by
+ * larosa_swiglu would see them. h: [B, f] in act_dtype. For one token in
+ * LAROSA_UNFUSED mode the selection, product and SwiGLU are one launch
+ * after the rotation; other cases run the layer into the workspace and then
+ * the SwiGLU step. Other arguments as for larosa_layer_forward; ws: at least
+ * larosa_swiglu_workspace_bytes(B, d_in, f, k, mode) bytes, zero-filled once. */
+int larosa_swiglu_layer_forward(const void *x, int act_dtype, const void *Qt, int64_t q_block,
+                                const void *W_il, int w_dtype, int64_t B, int64_t d_in,
+                                int64_t f, int64_t k, void *h, int32_t *idx_out,
+                                float *xrot_out, int mode, void *ws, size_t ws_bytes,
+                                larosa_stream_t stream);
+
 /* ---- The decoder layer around the rotated linears ----------------------
  * The pages apply the rotated Top-K sparsification to every linear layer of a
  * pretrained decoder (LaRoSA summary page, 方法详解 · 技术框架) and describe no

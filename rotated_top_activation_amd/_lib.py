@@ -47,6 +47,11 @@ SIGNATURES = {
     "larosa_dense_gemv": (_c_int, [_c_vp, _c_int, _c_vp, _c_int, _c_vp, _c_i64, _c_i64, _c_i64,
                                    _c_vp, _c_sz, _c_vp]),
     "larosa_swiglu": (_c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_vp]),
+    "larosa_interleave_gate_up": (_c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_vp]),
+    "larosa_swiglu_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i64, _c_int]),
+    "larosa_swiglu_layer_forward": (_c_int, [_c_vp, _c_int, _c_vp, _c_i64, _c_vp, _c_int, _c_i64,
+                                             _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_int,
+                                             _c_vp, _c_sz, _c_vp]),
     "larosa_rmsnorm": (_c_int, [_c_vp, _c_vp, _c_i64, _c_i64, ctypes.c_float, _c_int, _c_vp]),
     "larosa_rope": (_c_int, [_c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                              ctypes.c_float, _c_int, _c_vp]),
@@ -191,6 +196,25 @@ def larosa_dense_gemv(x, W, y, B: int, d_in: int, d_out: int, ws=None, stream=No
 def larosa_swiglu(gu, h, B: int, f: int, stream=None) -> None:
     _check("larosa_swiglu",
            load().larosa_swiglu(_ptr(gu), _ptr(h), B, f, _dt(gu), _stream(stream)))
+
+
+def larosa_interleave_gate_up(W, W_il, d_in: int, f: int, stream=None) -> None:
+    _check("larosa_interleave_gate_up",
+           load().larosa_interleave_gate_up(_ptr(W), _ptr(W_il), d_in, f, _dt(W), _stream(stream)))
+
+
+def larosa_swiglu_workspace_bytes(B: int, d_in: int, f: int, k: int, mode: int = UNFUSED) -> int:
+    return int(load().larosa_swiglu_workspace_bytes(B, d_in, f, k, mode))
+
+
+def larosa_swiglu_layer_forward(x, Qt, q_block: int, W_il, B: int, d_in: int, f: int, k: int,
+                                h, idx_out=None, xrot_out=None, mode: int = UNFUSED, ws=None,
+                                stream=None) -> None:
+    _check("larosa_swiglu_layer_forward",
+           load().larosa_swiglu_layer_forward(_ptr(x), _dt(x), _ptr(Qt), q_block, _ptr(W_il),
+                                              _dt(W_il), B, d_in, f, k, _ptr(h), _ptr(idx_out),
+                                              _ptr(xrot_out), mode, _ptr(ws), _nbytes(ws),
+                                              _stream(stream)))
 
 
 def larosa_rmsnorm(h, out, B: int, d: int, eps: float = 1e-5, stream=None) -> None:

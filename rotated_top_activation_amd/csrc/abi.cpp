@@ -490,6 +490,89 @@ int larosa_layer_forward(const void *x, int act_dtype, const void *Qt, int64_t q
   return launched(launch_gather(a, s));
 }
 
+size_t larosa_swiglu_workspace_bytes(int64_t B, int64_t d_in, int64_t f, int64_t k, int mode) {
+  if (f < 1) return 0;
+  const size_t base = larosa_workspace_bytes(B, d_in, 2 * f, k, mode);
+  if (base == 0) return 0;
+  const int64_t b1 = B < 1 ? 1 : B;
+  return base + align256(static_cast<size_t>(b1) * 2 * f * 4);  // the gate|up rows
+}
+
+int larosa_interleave_gate_up(const void *W, void *W_il, int64_t d_in, int64_t f, int dtype,
+                              larosa_stream_t stream) {
+  if (!W || !W_il) return LAROSA_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype)) return LAROSA_ERR_DTYPE;
+  if (d_in < 1 || f < 1 || f % interleave_block(dtype)) return LAROSA_ERR_SHAPE;
+  if (!aligned16(W) || !aligned16(W_il)) return LAROSA_ERR_ALIGNMENT;
+  const size_t bytes = static_cast<size_t>(d_in) * 2 * f * dt_size(dtype);
+  const char *a = static_cast<const char *>(W);
+  const char *b = static_cast<const char *>(W_il);
+  if (a < b + bytes && b < a + bytes) return LAROSA_ERR_INVALID_ARG;
+  if (int st = device_status()) return st;
+  return launched(launch_interleave(W, W_il, d_in, f, interleave_block(dtype), dtype,
+                                    stream_of(stream)));
+}
+
+int larosa_swiglu_layer_forward(const void *x, int act_dtype, const void *Qt, int64_t q_block,
+                                const void *W_il, int w_dtype, int64_t B, int64_t d_in,
+                                int64_t f, int64_t k, void *h, int32_t *idx_out,
+                                float *xrot_out, int mode, void *ws, size_t ws_bytes,
+                                larosa_stream_t stream) {
+  if (!dtype_ok(act_dtype) || !dtype_ok(w_dtype)) return LAROSA_ERR_DTYPE;
+  if (f < 1 || f % interleave_block(w_dtype)) return LAROSA_ERR_SHAPE;
+  if (mode != LAROSA_UNFUSED && mode != LAROSA_FUSED) return LAROSA_ERR_INVALID_ARG;
+  const size_t need = larosa_swiglu_workspace_bytes(B, d_in, f, k, mode);
+  if (need == 0 && B != 0) {  // invalid sizes: let the layer call name the error
+    return larosa_layer_forward(x, act_dtype, Qt, q_block, W_il, w_dtype, B, d_in, 2 * f, k, h,
+                                idx_out, xrot_out, mode, ws, ws_bytes, stream);
+  }
+  if (B == 0) return LAROSA_OK;
+  if (!h) return LAROSA_ERR_INVALID_ARG;
+  if (!aligned16(h)) return LAROSA_ERR_ALIGNMENT;
+  if (!ws || ws_bytes < need) return LAROSA_ERR_WORKSPACE;
+  const size_t layer_bytes = larosa_workspace_bytes(B, d_in, 2 * f, k, mode);
+  const bool one_launch = mode == LAROSA_UNFUSED && B == 1 && select_gather_supported(d_in) &&
+                          !(w_dtype == LAROSA_F32 && act_dtype == LAROSA_BF16);
+  if (one_launch) {
+    // rotation, then the selection, product and SiLU(gate)·up in one launch
+    if (int st = check_sizes(B, d_in, k)) return st;
+    if (!x || !Qt || !W_il) return LAROSA_ERR_INVALID_ARG;
+    if (int st = check_rotation(d_in, q_block, w_dtype)) return st;
+    if (d_in % vec_of(act_dtype)) return LAROSA_ERR_ALIGNMENT;
+    if (!aligned16(x) || !aligned16(Qt) || !aligned16(W_il) || !aligned16(ws))
+      return LAROSA_ERR_ALIGNMENT;
+    if (xrot_out && !aligned16(xrot_out)) return LAROSA_ERR_ALIGNMENT;
+    if (int st = device_status()) return st;
+    const Layout L = layout_for(B, d_in, 2 * f, k, w_dtype);
+    char *base = static_cast<char *>(ws);
+    float *x_rot = xrot_out ? xrot_out : reinterpret_cast<float *>(base + L.x_rot);
+    hipStream_t s = stream_of(stream);
+    if (launch_rotate(x, act_dtype, Qt, w_dtype, x_rot, 1, static_cast<int>(d_in),
+                      static_cast<int>(q_block), s) != hipSuccess)
+      return LAROSA_ERR_LAUNCH;
+    SelectGatherArgs g;
+    g.x_rot = x_rot;
+    g.d_in = static_cast<int>(d_in);
+    g.k = static_cast<int>(k);
+    g.w = W_il;
+    g.w_dt = w_dtype;
+    g.d_out = 2 * f;
+    g.y = h;
+    g.y_dt = act_dtype;
+    g.idx_out = idx_out;
+    g.ws = base + L.p.gather;
+    g.swiglu = true;
+    return launched(launch_select_gather(g, s));
+  }
+  // otherwise the gate|up rows into the workspace, then SiLU(gate)·up
+  void *gu = static_cast<char *>(ws) + layer_bytes;
+  const int st = larosa_layer_forward(x, act_dtype, Qt, q_block, W_il, w_dtype, B, d_in, 2 * f,
+                                      k, gu, idx_out, xrot_out, mode, ws, layer_bytes, stream);
+  if (st != LAROSA_OK) return st;
+  return launched(launch_swiglu_il(gu, h, B, f, interleave_block(w_dtype), act_dtype,
+                                   stream_of(stream)));
+}
+
 int larosa_swiglu(const void *gu, void *h, int64_t B, int64_t f, int dtype,
                   larosa_stream_t stream) {
   if (!dtype_ok(dtype)) return LAROSA_ERR_DTYPE;

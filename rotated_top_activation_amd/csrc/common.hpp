@@ -24,10 +24,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// SiLU(g)·u = g / (1 + e^-g) · u in fp32 (one definition for every kernel
+// that applies it, so they agree bit for bit).
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
 // Element access by type tag: float or uint16_t (bf16).
 template <typename T> struct Elt;
 template <> struct Elt<float> {
   static constexpr int kVec = 4;  // elements per 16-byte load
+  __device__ __forceinline__ static float round(float v) { return v; }
   __device__ __forceinline__ static float load(const float *p, int64_t i) { return p[i]; }
   __device__ __forceinline__ static void store(float *p, int64_t i, float v) { p[i] = v; }
   // Unpack one 16-byte chunk into kVec floats.
@@ -38,6 +43,8 @@ template <> struct Elt<float> {
 };
 template <> struct Elt<uint16_t> {
   static constexpr int kVec = 8;
+  // the value after one rounding to this type
+  __device__ __forceinline__ static float round(float v) { return bf16_to_f32(f32_to_bf16(v)); }
   __device__ __forceinline__ static float load(const uint16_t *p, int64_t i) { return bf16_to_f32(p[i]); }
   __device__ __forceinline__ static void store(uint16_t *p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
   __device__ __forceinline__ static void unpack(const uint4 &q, float *o) {

@@ -83,6 +83,9 @@ struct SelectGatherArgs {
   int y_dt;
   int32_t *idx_out;    // [k] ascending kept indices, or NULL
   void *ws;
+  // swiglu: W's columns are gate|up interleaved in blocks of half a tile and
+  // y is h [d_out / 2] = SiLU(gate)·up of the sums rounded to y's type.
+  bool swiglu = false;
 };
 hipError_t launch_select_gather(const SelectGatherArgs &a, hipStream_t s);
 
@@ -158,6 +161,14 @@ hipError_t launch_fold(const void *qt, int64_t qb, const void *w, void *wf,
 hipError_t launch_swiglu(const void *gu, void *h, int64_t B, int64_t f, int dt,
                          hipStream_t s);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
+// Gate|up columns interleaved in blocks of ib (half a product column tile:
+// 256 bf16 or 128 fp32 columns), so one tile holds matching gate and up
+// columns.
+inline int64_t interleave_block(int w_dt) { return w_dt == kF32 ? 128 : 256; }
+hipError_t launch_swiglu_il(const void *gu, void *h, int64_t B, int64_t f, int64_t ib, int dt,
+                            hipStream_t s);
+hipError_t launch_interleave(const void *w, void *out, int64_t d_in, int64_t f, int64_t ib,
+                             int dt, hipStream_t s);
 
 // --- decoder layer around the rotated linears ---
 hipError_t launch_rmsnorm(const void *h, void *out, int64_t B, int64_t d, float eps, int dt,

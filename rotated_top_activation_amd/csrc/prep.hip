@@ -102,9 +102,43 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const T *__restrict__ gu,
   Elt<T>::unpack(load16(gu + b * 2 * f + i), g);
   Elt<T>::unpack(load16(gu + b * 2 * f + f + i), u);
 #pragma unroll
-  for (int v = 0; v < V; ++v) o[v] = g[v] / (1.0f + expf(-g[v])) * u[v];
+  for (int v = 0; v < V; ++v) o[v] = silu_mul(g[v], u[v]);
 #pragma unroll
   for (int v = 0; v < V; ++v) Elt<T>::store(h, b * f + i + v, o[v]);
+}
+
+// The same over gate|up columns interleaved in blocks of ib: gate column i
+// sits at (i / ib)·2ib + i mod ib, its up column ib further.
+template <typename T>
+__global__ __launch_bounds__(256) void swiglu_il_kernel(const T *__restrict__ gu,
+                                                        T *__restrict__ h, int64_t B,
+                                                        int64_t f, int64_t ib) {
+  constexpr int V = Elt<T>::kVec;
+  const int64_t e = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * V;
+  if (e >= B * f) return;
+  const int64_t b = e / f, i = e % f;  // ib % V == 0: a vector stays in one block
+  const int64_t gc = (i / ib) * 2 * ib + i % ib;
+  float g[V], u[V];
+  Elt<T>::unpack(load16(gu + b * 2 * f + gc), g);
+  Elt<T>::unpack(load16(gu + b * 2 * f + gc + ib), u);
+#pragma unroll
+  for (int v = 0; v < V; ++v) Elt<T>::store(h, b * f + i + v, silu_mul(g[v], u[v]));
+}
+
+// out[r, (i / ib)·2ib + i mod ib] = w[r, i] and out[r, … + ib] = w[r, f + i]:
+// gate and up columns of a [d_in, 2f] weight interleaved in blocks of ib.
+template <typename T>
+__global__ __launch_bounds__(256) void interleave_kernel(const T *__restrict__ w,
+                                                         T *__restrict__ out, int64_t d_in,
+                                                         int64_t f, int64_t ib) {
+  constexpr int V = Elt<T>::kVec;
+  const int64_t e = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * V;
+  if (e >= d_in * 2 * f) return;
+  const int64_t r = e / (2 * f), c = e % (2 * f);  // source column; f % V == 0
+  const bool up = c >= f;
+  const int64_t i = up ? c - f : c;
+  const int64_t oc = (i / ib) * 2 * ib + i % ib + (up ? ib : 0);
+  *reinterpret_cast<uint4 *>(out + r * 2 * f + oc) = load16(w + e);
 }
 
 __global__ void fill_zero_kernel(uint8_t *__restrict__ p, size_t bytes) {
@@ -159,6 +193,35 @@ hipError_t launch_swiglu(const void *gu, void *h, int64_t B, int64_t f, int dt, 
   else
     hipLaunchKernelGGL(swiglu_kernel<uint16_t>, grid, dim3(256), 0, s,
                        static_cast<const uint16_t *>(gu), static_cast<uint16_t *>(h), B, f);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_il(const void *gu, void *h, int64_t B, int64_t f, int64_t ib, int dt,
+                            hipStream_t s) {
+  const int V = dt == kF32 ? 4 : 8;
+  const int64_t threads = (B * f + V - 1) / V;
+  dim3 grid(static_cast<unsigned>((threads + 255) / 256));
+  if (dt == kF32)
+    hipLaunchKernelGGL(swiglu_il_kernel<float>, grid, dim3(256), 0, s,
+                       static_cast<const float *>(gu), static_cast<float *>(h), B, f, ib);
+  else
+    hipLaunchKernelGGL(swiglu_il_kernel<uint16_t>, grid, dim3(256), 0, s,
+                       static_cast<const uint16_t *>(gu), static_cast<uint16_t *>(h), B, f, ib);
+  return hipGetLastError();
+}
+
+hipError_t launch_interleave(const void *w, void *out, int64_t d_in, int64_t f, int64_t ib,
+                             int dt, hipStream_t s) {
+  const int V = dt == kF32 ? 4 : 8;
+  const int64_t threads = (d_in * 2 * f + V - 1) / V;
+  dim3 grid(static_cast<unsigned>((threads + 255) / 256));
+  if (dt == kF32)
+    hipLaunchKernelGGL(interleave_kernel<float>, grid, dim3(256), 0, s,
+                       static_cast<const float *>(w), static_cast<float *>(out), d_in, f, ib);
+  else
+    hipLaunchKernelGGL(interleave_kernel<uint16_t>, grid, dim3(256), 0, s,
+                       static_cast<const uint16_t *>(w), static_cast<uint16_t *>(out), d_in, f,
+                       ib);
   return hipGetLastError();
 }
 

@@ -88,6 +88,57 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void rotate_vec_kernel(
     }
 }
 
+// One token, x and Qt of one element type: each wave computes one output
+// channel and issues every load of its row (NC 16-byte chunks per lane, the
+// matching x chunks alongside) before using any, so a wave's life is about
+// one memory round trip plus its share of the transfer.
+template <int NC, typename T>
+__global__ __launch_bounds__(kWavesPerBlock * kWave) void rotate_row_kernel(
+    const T *__restrict__ x, const T *__restrict__ qt, float *__restrict__ x_rot, int d,
+    int qb) {
+  constexpr int V = Elt<T>::kVec;
+  const int lane = threadIdx.x % kWave;
+  const int j = blockIdx.x * kWavesPerBlock + wave_id();
+  if (j >= d) return;
+  const int64_t xoff = static_cast<int64_t>(j / qb) * qb;
+  const T *row = qt + static_cast<int64_t>(j) * qb;
+  const int chunks = qb / V;
+  uint4 xq[NC], q[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = lane + kWave * i;
+    const bool ok = c < chunks;
+    xq[i] = ok ? load16(x + xoff + c * V) : make_uint4(0, 0, 0, 0);
+    q[i] = ok ? load16(row + c * V) : make_uint4(0, 0, 0, 0);
+  }
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    float xf[V], qf[V];
+    Elt<T>::unpack(xq[i], xf);
+    Elt<T>::unpack(q[i], qf);
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc = fmaf(xf[v], qf[v], acc);
+  }
+  const float sum = wave_sum(acc);
+  if (lane == 0) x_rot[j] = sum;
+}
+
+template <typename T>
+bool launch_row(const void *x, const void *qt, float *x_rot, int d, int qb, hipStream_t s) {
+  constexpr int V = Elt<T>::kVec;
+  const int nc = (qb / V + kWave - 1) / kWave;
+  const dim3 grid((d + kWavesPerBlock - 1) / kWavesPerBlock), block(kWavesPerBlock * kWave);
+  const auto *xp = static_cast<const T *>(x);
+  const auto *qp = static_cast<const T *>(qt);
+  if (nc <= 2) hipLaunchKernelGGL((rotate_row_kernel<2, T>), grid, block, 0, s, xp, qp, x_rot, d, qb);
+  else if (nc <= 4) hipLaunchKernelGGL((rotate_row_kernel<4, T>), grid, block, 0, s, xp, qp, x_rot, d, qb);
+  else if (nc <= 8) hipLaunchKernelGGL((rotate_row_kernel<8, T>), grid, block, 0, s, xp, qp, x_rot, d, qb);
+  else if (nc <= 16) hipLaunchKernelGGL((rotate_row_kernel<16, T>), grid, block, 0, s, xp, qp, x_rot, d, qb);
+  else return false;
+  return true;
+}
+
 template <int B, int J, typename XT, typename QT>
 hipError_t launch_t(const void *x, const void *qt, float *x_rot, int d, int qb,
                     hipStream_t s) {
@@ -121,6 +172,11 @@ hipError_t launch_b(const void *x, int x_dt, const void *qt, int q_dt, float *x_
 
 hipError_t launch_rotate(const void *x, int x_dt, const void *qt, int q_dt,
                          float *x_rot, int B, int d, int qb, hipStream_t s) {
+  if (B == 1 && x_dt == q_dt) {
+    const bool done = x_dt == kBF16 ? launch_row<uint16_t>(x, qt, x_rot, d, qb, s)
+                                    : launch_row<float>(x, qt, x_rot, d, qb, s);
+    if (done) return hipGetLastError();
+  }
   // Tokens are processed four at a time; each group re-reads Qt.
   const int xs = dt_size(x_dt);
   for (int b0 = 0; b0 < B; b0 += 4) {

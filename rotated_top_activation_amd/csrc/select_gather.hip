@@ -36,7 +36,7 @@ constexpr int kSgMaxSplitLoads = 16;
 
 size_t sg_counter_bytes(int tiles) { return (static_cast<size_t>(tiles) * 4 + 255) / 256 * 256; }
 
-template <typename WT, typename OT, int EMAX>
+template <typename WT, typename OT, int EMAX, bool SWIGLU>
 __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
     const float *__restrict__ x_rot, int d, int k, int E, int tiles, int splits, int cps,
     const WT *__restrict__ w, int64_t d_out, OT *__restrict__ y, float *__restrict__ partials,
@@ -56,6 +56,7 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
   float(*red)[TILE] = reinterpret_cast<float(*)[TILE]>(kv);
   __shared__ uint32_t s_carry;
   __shared__ int s_last;
+  __shared__ float ep[SWIGLU ? TILE : 1];  // the tile's sums, for the SwiGLU epilogue
 
   const int t = threadIdx.x;
   const int lane = t % kWave;
@@ -203,29 +204,46 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
     }
   }
 
-  // 4. Combine the waves; with one split store y, else partial sums.
+  // 4. Combine the waves; with one split finish the tile, else partial sums.
 #pragma unroll
   for (int q = 0; q < V; ++q) red[wave][lane * V + q] = acc[q];
   __syncthreads();
   const int64_t tile_col0 = static_cast<int64_t>(tile) * TILE;
+  // A finished column sum: stored, or staged for the SwiGLU epilogue, which
+  // pairs gate column e with up column e + TILE/2 of the tile (rounded to
+  // the output type first, as a separate SwiGLU step would see them).
+  auto finish = [&](int e, float v) {
+    if (SWIGLU) ep[e] = v;
+    else Elt<OT>::store(y, tile_col0 + e, v);
+  };
+  auto epilogue = [&]() {
+    if (!SWIGLU) return;
+    __syncthreads();
+    for (int e = t; e < TILE / 2; e += kSgThreads)
+      Elt<OT>::store(y, static_cast<int64_t>(tile) * (TILE / 2) + e,
+                     silu_mul(Elt<OT>::round(ep[e]), Elt<OT>::round(ep[TILE / 2 + e])));
+  };
   float *part = partials + static_cast<int64_t>(split) * d_out;
   for (int e = t; e < TILE; e += kSgThreads) {
     const int64_t cg = tile_col0 + e;
     if (cg >= d_out) continue;
-    float s = 0.f;
+    float sum = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < kSgWaves; ++ww) s += red[ww][e];
+    for (int ww = 0; ww < kSgWaves; ++ww) sum += red[ww][e];
     if (splits == 1) {
-      Elt<OT>::store(y, cg, s);
+      finish(e, sum);
     } else {
       // Agent-scope atomic exchange: the value lands at the device-coherent
       // point, like the arrival counter below.
-      const float old = __hip_atomic_exchange(part + cg, s, __ATOMIC_RELAXED,
+      const float old = __hip_atomic_exchange(part + cg, sum, __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_AGENT);
       (void)old;
     }
   }
-  if (splits == 1) return;
+  if (splits == 1) {
+    epilogue();
+    return;
+  }
 
   // The tile's last workgroup to arrive adds the partial sums in split
   // order (the result does not depend on arrival order) and resets the
@@ -243,7 +261,7 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
     const int64_t cg = tile_col0 + e;
     if (cg >= d_out) continue;
     const float *p = partials + cg;
-    float s = 0.f;
+    float sum = 0.f;
     for (int r0 = 0; r0 < splits; r0 += kSgMaxSplitLoads) {
       float pv[kSgMaxSplitLoads];
 #pragma unroll
@@ -253,32 +271,40 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
                                 : 0.f;
 #pragma unroll
       for (int i = 0; i < kSgMaxSplitLoads; ++i)
-        if (r0 + i < splits) s += pv[i];
+        if (r0 + i < splits) sum += pv[i];
     }
-    Elt<OT>::store(y, cg, s);
+    finish(e, sum);
   }
+  epilogue();
   if (t == 0)
     __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename WT, typename OT, int EM>
+void launch_sg_em(const SelectGatherArgs &a, const SelectGatherPlan &p, int E, hipStream_t s) {
+  uint32_t *counters = static_cast<uint32_t *>(a.ws);
+  float *partials =
+      reinterpret_cast<float *>(static_cast<char *>(a.ws) + sg_counter_bytes(p.tiles));
+  const dim3 grid(static_cast<unsigned>(p.tiles * p.splits)), block(kSgThreads);
+  const auto *w = static_cast<const WT *>(a.w);
+  auto *y = static_cast<OT *>(a.y);
+  if (a.swiglu)
+    hipLaunchKernelGGL((select_gather_kernel<WT, OT, EM, true>), grid, block, 0, s, a.x_rot,
+                       a.d_in, a.k, E, p.tiles, p.splits, p.cps, w, a.d_out, y, partials,
+                       counters, a.idx_out);
+  else
+    hipLaunchKernelGGL((select_gather_kernel<WT, OT, EM, false>), grid, block, 0, s, a.x_rot,
+                       a.d_in, a.k, E, p.tiles, p.splits, p.cps, w, a.d_out, y, partials,
+                       counters, a.idx_out);
 }
 
 template <typename WT, typename OT>
 hipError_t launch_sg_t(const SelectGatherArgs &a, const SelectGatherPlan &p, hipStream_t s) {
   const int E = slots_per_thread(a.d_in, kSgThreads);
-  uint32_t *counters = static_cast<uint32_t *>(a.ws);
-  float *partials =
-      reinterpret_cast<float *>(static_cast<char *>(a.ws) + sg_counter_bytes(p.tiles));
-  const dim3 grid(static_cast<unsigned>(p.tiles * p.splits));
-  const auto *w = static_cast<const WT *>(a.w);
-  auto *y = static_cast<OT *>(a.y);
-#define LAROSA_SG(EM)                                                                       \
-  hipLaunchKernelGGL((select_gather_kernel<WT, OT, EM>), grid, dim3(kSgThreads), 0, s,     \
-                     a.x_rot, a.d_in, a.k, E, p.tiles, p.splits, p.cps, w, a.d_out, y,      \
-                     partials, counters, a.idx_out)
-  if (E <= 4) LAROSA_SG(4);
-  else if (E <= 8) LAROSA_SG(8);
-  else if (E <= 16) LAROSA_SG(16);
+  if (E <= 4) launch_sg_em<WT, OT, 4>(a, p, E, s);
+  else if (E <= 8) launch_sg_em<WT, OT, 8>(a, p, E, s);
+  else if (E <= 16) launch_sg_em<WT, OT, 16>(a, p, E, s);
   else return hipErrorInvalidValue;
-#undef LAROSA_SG
   return hipGetLastError();
 }
 

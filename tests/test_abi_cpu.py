@@ -116,6 +116,12 @@ def test_standalone_calls_validation(lib):
     assert lib.larosa_prepare_rotation(P, P + 16, 128, 64, 1, None) == INVALID  # overlap
     assert lib.larosa_prepare_rotation(P, P + (1 << 20), 128, 48, 1, None) == SHAPE
     assert lib.larosa_swiglu(P, P, 1, 12, 1, None) == ALIGN
+    assert lib.larosa_interleave_gate_up(P, P + (1 << 24), 64, 300, 1, None) == SHAPE
+    assert lib.larosa_interleave_gate_up(P, P + 64, 64, 256, 1, None) == INVALID  # overlap
+    assert lib.larosa_swiglu_workspace_bytes(1, 4096, 11008, 2457, 0) > \
+        lib.larosa_workspace_bytes(1, 4096, 22016, 2457, 0)
+    assert lib.larosa_swiglu_layer_forward(P, 1, P, 64, P, 1, 1, 128, 300, 10, P, None, None, 0,
+                                           P, 1 << 24, None) == SHAPE
     assert lib.larosa_workspace_init(PM, 64, None) == ALIGN
 
 
