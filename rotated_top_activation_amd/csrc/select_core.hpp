@@ -342,7 +342,24 @@ __device__ __forceinline__ void rule_finish(const uint32_t (&key)[EMAX], int E, 
     __syncthreads();
     for (int j = t; j < static_cast<int>(n_cand); j += NT) radix_count<NT>(cs.key[j], pass, prefix, pmask, sm);
     __syncthreads();
-    radix_resolve<NT>(pass, prefix, pmask, krem, sm);
+    const uint32_t in_bin = radix_resolve<NT>(pass, prefix, pmask, krem, sm);
+    if (pass == 1 && in_bin == 1) {
+      // One candidate carries the boundary's first two digits (the usual
+      // case): its key is T and no other channel has that key, so it is the
+      // last one kept (krem == 1) and the third digit and the tie cut-off are
+      // not needed.
+      for (int j = t; j < static_cast<int>(n_cand); j += NT) {
+        if ((cs.key[j] & pmask) == prefix) {
+          sm.bin = cs.key[j];
+          sm.above = cs.idx[j];
+        }
+      }
+      __syncthreads();
+      T = sm.bin;
+      cut = sm.above;
+      __syncthreads();
+      return;
+    }
   }
   T = prefix;
   // the krem-th candidate equal to T in index order is the last one kept

@@ -32,7 +32,7 @@ constexpr int kSgThreads = kSgWaves * kWave;
 constexpr int kSgRows = 8;        // kept rows per wave group (loads in flight per lane)
 constexpr int kSgListMax = 4096;  // channels of one split (LDS row list)
 constexpr int kSgKeysMax = 16384; // channels of the LDS copy of the rotated vector
-constexpr int kSgMaxSplitLoads = 16;
+constexpr int kSgMaxSplitLoads = 32;  // partial sums fetched per round trip
 
 size_t sg_counter_bytes(int tiles) { return (static_cast<size_t>(tiles) * 4 + 255) / 256 * 256; }
 
