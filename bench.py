@@ -73,7 +73,11 @@ def parse():
     p.add_argument("--q2-block", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--kernel-only", choices=["", "gather", "topk1", "fused1", "step", "copy"],
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the other workloads (single linear, decoder step, layer slices)")
+    p.add_argument("--config-steps", type=int, default=20)
+    p.add_argument("--kernel-only", choices=["", "gather", "topk1", "fused1", "step", "copy",
+                                             "configs"],
                    default="",
                    help="only launch that work (for profiler runs)")
     return p.parse_args()
@@ -103,6 +107,9 @@ def main():
         for _ in range(a.steps):
             dst.copy_(src)
         torch.cuda.synchronize()
+        return
+    if a.kernel_only == "configs":
+        print(json.dumps(other_configs(a, dev)), flush=True)
         return
     case = wl.llama7b_mlp(batch=1, sparsity_pct=a.sparsity, q2_block=a.q2_block or None)
     t0 = time.time()
@@ -277,6 +284,13 @@ def main():
     dom = "fused_linear_kernel" if best == "fused" else "select_gather_kernel"
     kd = kernels[dom]
 
+    configs = None
+    if not a.no_configs:
+        # the MLP's copies are no longer needed
+        del qt1, wf1, wil1, qt2, wf2
+        torch.cuda.empty_cache()
+        configs = other_configs(a, dev)
+
     cpu = None
     if not a.no_cpu_baseline:
         cpu = cpu_baseline(case, x, q1, wgu, q2, wd, a.cpu_seconds)
@@ -325,9 +339,200 @@ def main():
             "gate_up_speedup_vs_dense": round(min(dense_ms, torch_ms) / topk1_ms, 3),
             "gate_up_gather_only_speedup_vs_dense": round(min(dense_ms, torch_ms) / gather_ms, 3),
             "input_gen_s": round(gen_s, 1),
+            "configs": configs,
         },
     }
     print(json.dumps(out), flush=True)
+
+
+# ---------------------------------------------------------------- other workloads --
+# The single fp32 linear, the 32-layer decoder step and the 13B / 70B layer
+# slices, timed with HIP events like the MLP. Their rotations and weights are
+# drawn on the device (QR of a seeded N(0,1) matrix, sign-fixed; seeded
+# Gaussian weights): the same distributions as the test inputs, without the
+# host QR of 8192² matrices. Bytes per step are what the path must read: the
+# rotations, the union rows of every folded weight (union sizes from one
+# traced step) and, for the decoder, the key/value cache.
+
+def _dev_haar(gen, n: int, nb: int, device):
+    import torch
+    out = []
+    for _ in range(nb):
+        g = torch.randn((n, n), generator=gen, device=device, dtype=torch.float32)
+        q, r = torch.linalg.qr(g)
+        sg = torch.sign(torch.diagonal(r))
+        sg[sg == 0] = 1.0
+        out.append((q * sg[None, :]).to(torch.bfloat16))
+    return torch.stack(out)
+
+
+def _dev_weight(gen, d_in: int, d_out: int, std: float, device):
+    import torch
+    return (torch.randn((d_in, d_out), generator=gen, device=device) * std).to(torch.bfloat16)
+
+
+def _timed_ms(fn, steps: int, warmup: int) -> float:
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def _union_rows(idx) -> int:
+    import torch
+    return int(torch.unique(idx.reshape(-1)).numel())
+
+
+def _entry(B, ms, nbytes, extra=None):
+    out = {"tokens_per_s": round(B / (ms * 1e-3), 1), "us_per_step": round(ms * 1e3, 2),
+           "bytes_per_step": int(nbytes), "GBs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+           "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    if extra:
+        out.update(extra)
+    return out
+
+
+def other_configs(a, device):
+    import torch
+    from rotated_top_activation_amd import _lib, decoder as dec, workloads as wl
+    from rotated_top_activation_amd.device import RotatedLinear
+    steps, warm = a.config_steps, 3
+    res = {}
+
+    # single linear, fp32, 512 -> 1536, batch 1, 40%
+    case, x, q, w = wl.single_linear_f32()
+    lin = RotatedLinear(q, w, "f32", case.k)
+    x_d = wl.to_torch(x, "f32")
+    y = torch.empty((1, 1536), dtype=torch.float32, device=device)
+    best = None
+    for mode, name in ((_lib.UNFUSED, "unfused"), (_lib.FUSED, "fused")):
+        ws = lin.workspace(1, mode)
+        ms = _timed_ms(lambda: lin.forward(x_d, y, ws, mode=mode), 200, 20)
+        if best is None or ms < best[0]:
+            best = (ms, name)
+    nbytes = 512 * 512 * 4 + case.k * 1536 * 4
+    res["single_linear_f32_512x1536_b1_s40"] = _entry(1, best[0], nbytes, {"mode": best[1]})
+    del lin
+
+    # 32-layer 7B decoder step
+    shape = wl.LLAMA7B
+    gen = torch.Generator(device=device)
+    gen.manual_seed(3)
+    d, f = shape.d, shape.f
+    base = {
+        "q_attn": _dev_haar(gen, d, 1, device), "q_o": _dev_haar(gen, d, 1, device),
+        "q_mlp": _dev_haar(gen, d, 1, device),
+        "q_down": _dev_haar(gen, shape.q2_block, f // shape.q2_block, device),
+        "w_qkv": _dev_weight(gen, d, shape.qkv_out, shape.w_std, device),
+        "w_o": _dev_weight(gen, d, d, shape.w_std, device),
+        "w_gu": _dev_weight(gen, d, 2 * f, shape.w_std, device),
+        "w_down": _dev_weight(gen, f, d, shape.w_std, device),
+    }
+    kv_base = tuple(torch.randn((shape.n_kv_heads, shape.ctx, shape.d_head), generator=gen,
+                                device=device).to(torch.bfloat16) for _ in range(2))
+    n_layers = 32
+    for B, sps in ((1, (25, 40, 50)), (4, (40,)), (16, (40,))):
+        layers = [dec.build_layer(3, l, shape, base, kv_base, B, sps[0])[0]
+                  for l in range(n_layers)]
+        buf = dec.DecoderBuffers(shape, B)
+        h0 = wl.to_torch(wl.decoder_hidden(3, B, d), "bf16")
+        h = h0.clone()
+        for sp in sps:
+            for L in layers:
+                for role in dec.ROLES:
+                    lin = L.lin[role]
+                    lin.k = wl.k_for(lin.d_in, sp)
+                L.ws = {}
+
+            def step():
+                h.copy_(h0)
+                for L in layers:
+                    dec.layer_forward(L, h, buf, _lib.UNFUSED)
+            ms = _timed_ms(step, steps, warm)
+            # bytes: rotations + union rows (one traced step) + key/value cache
+            nbytes = 0
+            h.copy_(h0)
+            for L in layers:
+                trace = {}
+                dec.layer_forward(L, h, buf, _lib.UNFUSED, trace=trace)
+                for role in dec.ROLES:
+                    lin = L.lin[role]
+                    nbytes += lin.Qt.numel() * 2 + _union_rows(trace[role][1]) * lin.d_out * 2
+                nbytes += B * 2 * shape.n_kv_heads * shape.ctx * shape.d_head * 2
+            res[f"decoder32_7b_b{B}_s{sp}"] = _entry(B, ms, nbytes, {"layers": n_layers})
+        del layers, buf
+        torch.cuda.empty_cache()
+    del base, kv_base
+    torch.cuda.empty_cache()
+
+    # layer slices: the four rotated linears of one layer (no attention core)
+    slices = (("13b", 4, 5120, 13824, 40, 40, 0.02, "outlier", 40, (8,)),
+              ("70b", 5, 8192, 28672, 64, 8, 0.01, "heavy", 50, (32, 64)))
+    for name, cfg, d, f, H, Hkv, wstd, act, sp, Bs in slices:
+        q2 = wl.ffn_q_block(f)
+        qkv_out = (H + 2 * Hkv) * 128
+        gen.manual_seed(cfg)
+        lins = {
+            "attn_in": RotatedLinear(_dev_haar(gen, d, 1, device),
+                                     _dev_weight(gen, d, qkv_out, wstd, device), "bf16",
+                                     wl.k_for(d, sp), keep_w=False),
+            "o_in": RotatedLinear(_dev_haar(gen, d, 1, device), _dev_weight(gen, d, d, wstd, device),
+                                  "bf16", wl.k_for(d, sp), keep_w=False),
+            "mlp_in": RotatedLinear(_dev_haar(gen, d, 1, device),
+                                    _dev_weight(gen, d, 2 * f, wstd, device), "bf16",
+                                    wl.k_for(d, sp), keep_w=False),
+            "down_in": RotatedLinear(_dev_haar(gen, q2, f // q2, device),
+                                     _dev_weight(gen, f, d, wstd, device), "bf16",
+                                     wl.k_for(f, sp), keep_w=False),
+        }
+        for B in Bs:
+            def acts(role):
+                if act == "outlier":
+                    return wl.to_torch(wl.outlier_activations(cfg, 0, role, B, d, d // 100, 30.0,
+                                                              "bf16"), "bf16")
+                return wl.to_torch(wl.heavy_tailed_activations(cfg, 0, role, B, d, "bf16"), "bf16")
+            xa, xo, xm = acts("attn_in"), acts("o_in"), acts("mlp_in")
+            ya = torch.empty((B, qkv_out), dtype=torch.bfloat16, device=device)
+            yo = torch.empty((B, d), dtype=torch.bfloat16, device=device)
+            gu = torch.empty((B, 2 * f), dtype=torch.bfloat16, device=device)
+            hh = torch.empty((B, f), dtype=torch.bfloat16, device=device)
+            yd = torch.empty((B, d), dtype=torch.bfloat16, device=device)
+            wss = {r: lins[r].workspace(B) for r in lins}
+
+            def step(trace=None):
+                outs = {}
+                for role, xin, yout in (("attn_in", xa, ya), ("o_in", xo, yo),
+                                        ("mlp_in", xm, gu)):
+                    idx = None
+                    if trace is not None:
+                        idx = torch.empty((B, lins[role].k), dtype=torch.int32, device=device)
+                        trace[role] = idx
+                    lins[role].forward(xin, yout, wss[role], idx_out=idx)
+                _lib.larosa_swiglu(gu, hh, B, f)
+                idx = None
+                if trace is not None:
+                    idx = torch.empty((B, lins["down_in"].k), dtype=torch.int32, device=device)
+                    trace["down_in"] = idx
+                lins["down_in"].forward(hh, yd, wss["down_in"], idx_out=idx)
+            ms = _timed_ms(step, steps, warm)
+            trace = {}
+            step(trace)
+            torch.cuda.synchronize()
+            nbytes = sum(lins[r].Qt.numel() * 2 + _union_rows(trace[r]) * lins[r].d_out * 2
+                         for r in lins)
+            rows = {r: _union_rows(trace[r]) for r in lins}
+            res[f"slice_{name}_b{B}_s{sp}"] = _entry(
+                B, ms, nbytes, {"union_rows": rows, "d_in": {r: lins[r].d_in for r in lins}})
+        del lins
+        torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(case, x, q1, wgu, q2, wd, seconds):

@@ -87,70 +87,145 @@ __global__ __launch_bounds__(kGT) void rope_kernel(const T *__restrict__ qk, int
 // One workgroup per (query head, token). The cache is [B, n_kv, T, 128];
 // the new token's key and value sit at k_new + b·k_stride + kv·128 and
 // v_new + b·v_stride + kv·128.
-// Scores for the T cached positions and the new one go to LDS; then a max,
-// the exponentials and their sum; then each wave accumulates p·v over a
-// quarter of the positions (two channels per lane) and the waves are added.
+// Single-query attention, one 1024-thread workgroup per (token, head). A key
+// or value row (one position's 128 channels) is read by LPR lanes with
+// 16-byte loads, so one wave instruction covers 64/LPR rows; the 16 waves
+// take interleaved row groups and keep kAttBatch instructions in flight.
+// Pass 1 writes the scores of the T cached positions and the new one to LDS;
+// then one max and one sum of the exponentials; pass 2 accumulates p·v per
+// lane and folds the row slots and the waves.
+constexpr int kAT = 1024;
+constexpr int kAW = kAT / kWave;
+constexpr int kAttBatch = 8;
+
+template <int NW>
+__device__ __forceinline__ float block_sum_w(float v, float *red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) red[w] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) s += red[i];
+  return s;
+}
+
+template <int NW>
+__device__ __forceinline__ float block_max_w(float v, float *red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) red[w] = v;
+  __syncthreads();
+  float m = red[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) m = fmaxf(m, red[i]);
+  return m;
+}
+
 template <typename T>
-__global__ __launch_bounds__(kGT) void decode_attention_kernel(
+__global__ __launch_bounds__(kAT) void decode_attention_kernel(
     const T *__restrict__ q, const T *__restrict__ k_new, int64_t k_stride,
     const T *__restrict__ v_new, int64_t v_stride, const T *__restrict__ kc,
     const T *__restrict__ vc, T *__restrict__ out, int Tlen, int n_heads, int n_kv) {
   constexpr int DH = 128;
-  extern __shared__ float smem[];
-  float *qs = smem;             // [DH]
-  float *sc = smem + DH;        // [Tlen + 1]
-  __shared__ float red[kGW];
-  __shared__ float accs[kGW][DH];
+  constexpr int V = Elt<T>::kVec;      // channels per 16-byte load
+  constexpr int LPR = DH / V;          // lanes per row
+  constexpr int RPI = kWave / LPR;     // rows per wave instruction
+  constexpr int ROWS = RPI * kAW;      // rows per round of the workgroup
+  extern __shared__ float sc[];        // [Tlen + 1] scores, then p
+  __shared__ float red[kAW];
+  __shared__ float accs[kAW][DH];
   const int h = blockIdx.x, b = blockIdx.y;
   const int g = h / (n_heads / n_kv);
-  const T *qrow = q + (static_cast<int64_t>(b) * n_heads + h) * DH;
-  for (int i = threadIdx.x; i < DH; i += kGT) qs[i] = Elt<T>::load(qrow, i);
-  __syncthreads();
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int slot = lane / LPR, c = lane % LPR;
   const T *kbase = kc + (static_cast<int64_t>(b) * n_kv + g) * Tlen * DH;
   const T *vbase = vc + (static_cast<int64_t>(b) * n_kv + g) * Tlen * DH;
   const T *kn = k_new + b * k_stride + static_cast<int64_t>(g) * DH;
   const T *vn = v_new + b * v_stride + static_cast<int64_t>(g) * DH;
+  const int n = Tlen + 1;  // positions, the new token last
+  auto row_of = [&](const T *base, const T *nw, int t) {
+    return t < Tlen ? base + static_cast<int64_t>(t) * DH : nw;
+  };
+  // this lane's query channels
+  float qf[V];
+  Elt<T>::unpack(load16(q + (static_cast<int64_t>(b) * n_heads + h) * DH + c * V), qf);
   const float scale = 1.0f / sqrtf(static_cast<float>(DH));
-  constexpr int V = Elt<T>::kVec;
+
+  // pass 1: scores
   float mx = -INFINITY;
-  for (int t = threadIdx.x; t <= Tlen; t += kGT) {
-    const T *krow = t < Tlen ? kbase + static_cast<int64_t>(t) * DH : kn;
-    float s = 0.f;
+  for (int r0 = wave * RPI; r0 < n; r0 += ROWS * kAttBatch) {
+    uint4 kq[kAttBatch];
 #pragma unroll
-    for (int c = 0; c < DH; c += V) {
-      float f[V];
-      Elt<T>::unpack(load16(krow + c), f);
-#pragma unroll
-      for (int v = 0; v < V; ++v) s = fmaf(qs[c + v], f[v], s);
+    for (int i = 0; i < kAttBatch; ++i) {
+      const int t = r0 + i * ROWS + slot;
+      kq[i] = t < n ? load16(row_of(kbase, kn, t) + c * V) : make_uint4(0, 0, 0, 0);
     }
-    s *= scale;
-    sc[t] = s;
-    mx = fmaxf(mx, s);
+#pragma unroll
+    for (int i = 0; i < kAttBatch; ++i) {
+      float kf[V];
+      Elt<T>::unpack(kq[i], kf);
+      float s = 0.f;
+#pragma unroll
+      for (int v = 0; v < V; ++v) s = fmaf(qf[v], kf[v], s);
+#pragma unroll
+      for (int off = LPR / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, kWave);
+      const int t = r0 + i * ROWS + slot;
+      if (t < n) {
+        s *= scale;
+        if (c == 0) sc[t] = s;
+        mx = fmaxf(mx, s);
+      }
+    }
   }
-  mx = block_max(mx, red);
+  mx = block_max_w<kAW>(mx, red);  // its barriers also order the sc[] writes
   float sum = 0.f;
-  for (int t = threadIdx.x; t <= Tlen; t += kGT) {
+  for (int t = threadIdx.x; t < n; t += kAT) {
     const float p = expf(sc[t] - mx);
     sc[t] = p;
     sum += p;
   }
-  sum = block_sum(sum, red);  // also orders the sc[] writes before the reads below
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  float a0 = 0.f, a1 = 0.f;
-  for (int t = wave; t <= Tlen; t += kGW) {
-    const T *vrow = t < Tlen ? vbase + static_cast<int64_t>(t) * DH : vn;
-    const float p = sc[t];
-    a0 = fmaf(p, Elt<T>::load(vrow, 2 * lane), a0);
-    a1 = fmaf(p, Elt<T>::load(vrow, 2 * lane + 1), a1);
+  sum = block_sum_w<kAW>(sum, red);
+
+  // pass 2: Σ p·v, V channels per lane for its row slot
+  float acc[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) acc[v] = 0.f;
+  for (int r0 = wave * RPI; r0 < n; r0 += ROWS * kAttBatch) {
+    uint4 vq[kAttBatch];
+#pragma unroll
+    for (int i = 0; i < kAttBatch; ++i) {
+      const int t = r0 + i * ROWS + slot;
+      vq[i] = t < n ? load16(row_of(vbase, vn, t) + c * V) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kAttBatch; ++i) {
+      const int t = r0 + i * ROWS + slot;
+      const float p = t < n ? sc[t] : 0.f;
+      float vf[V];
+      Elt<T>::unpack(vq[i], vf);
+#pragma unroll
+      for (int v = 0; v < V; ++v) acc[v] = fmaf(p, vf[v], acc[v]);
+    }
   }
-  accs[wave][2 * lane] = a0;
-  accs[wave][2 * lane + 1] = a1;
+  // fold the row slots (lanes c, c + LPR, …), then the waves
+#pragma unroll
+  for (int v = 0; v < V; ++v)
+#pragma unroll
+    for (int off = LPR; off < kWave; off <<= 1) acc[v] += __shfl_xor(acc[v], off, kWave);
+  if (slot == 0) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) accs[wave][c * V + v] = acc[v];
+  }
   __syncthreads();
   T *orow = out + (static_cast<int64_t>(b) * n_heads + h) * DH;
-  for (int i = threadIdx.x; i < DH; i += kGT) {
+  for (int i = threadIdx.x; i < DH; i += kAT) {
     float s = 0.f;
 #pragma unroll
-    for (int w = 0; w < kGW; ++w) s += accs[w][i];
+    for (int w = 0; w < kAW; ++w) s += accs[w][i];
     Elt<T>::store(orow, i, s / sum);
   }
 }
@@ -203,17 +278,17 @@ hipError_t launch_decode_attention(const void *q, const void *k_new, int64_t k_s
                                    const void *v_new, int64_t v_stride, const void *kc,
                                    const void *vc, void *out, int64_t B, int64_t Tlen,
                                    int64_t n_heads, int64_t n_kv, int dt, hipStream_t s) {
-  const size_t lds = (128 + static_cast<size_t>(Tlen) + 1) * sizeof(float);
+  const size_t lds = (static_cast<size_t>(Tlen) + 1) * sizeof(float);
   dim3 grid(static_cast<unsigned>(n_heads), static_cast<unsigned>(B));
   if (dt == kF32)
-    hipLaunchKernelGGL(decode_attention_kernel<float>, grid, dim3(kGT), lds, s,
+    hipLaunchKernelGGL(decode_attention_kernel<float>, grid, dim3(kAT), lds, s,
                        static_cast<const float *>(q), static_cast<const float *>(k_new), k_stride,
                        static_cast<const float *>(v_new), v_stride,
                        static_cast<const float *>(kc), static_cast<const float *>(vc),
                        static_cast<float *>(out), static_cast<int>(Tlen),
                        static_cast<int>(n_heads), static_cast<int>(n_kv));
   else
-    hipLaunchKernelGGL(decode_attention_kernel<uint16_t>, grid, dim3(kGT), lds, s,
+    hipLaunchKernelGGL(decode_attention_kernel<uint16_t>, grid, dim3(kAT), lds, s,
                        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k_new),
                        k_stride, static_cast<const uint16_t *>(v_new), v_stride,
                        static_cast<const uint16_t *>(kc), static_cast<const uint16_t *>(vc),
