@@ -271,7 +271,7 @@ int larosa_sparse_gemv(const int32_t *rows, const int32_t *n_rows, int64_t max_r
   if (mf) {
     // max_rows == 0 still runs, so y is written (as zeros).
     const int64_t ldc = mfma_coef_ld(mr);
-    float *coefT = reinterpret_cast<float *>(base + P.mfma_coef);
+    void *coefT = base + P.mfma_coef;
     hipError_t e = launch_coef_transpose(coef, static_cast<int>(B), max_rows, ldc, coefT, s);
     if (e == hipSuccess)
       e = launch_gather_mfma(rows, n_rows, max_rows, d_in, coefT, ldc, W_folded, y,
@@ -344,7 +344,7 @@ int larosa_dense_gemv(const void *x, int act_dtype, const void *W, int w_dtype, 
   char *base = static_cast<char *>(ws);
   if (mfma_supported(B, act_dtype, w_dtype)) {
     const int64_t ldc = mfma_coef_ld(d_in);
-    float *coefT = reinterpret_cast<float *>(base + P.mfma_coef);
+    void *coefT = base + P.mfma_coef;
     hipError_t e = launch_act_to_coef_t(x, static_cast<int>(B), d_in, ldc, coefT, s);
     if (e == hipSuccess)
       e = launch_gather_mfma(nullptr, nullptr, d_in, d_in, coefT, ldc, W, y,
@@ -474,7 +474,7 @@ int larosa_layer_forward(const void *x, int act_dtype, const void *Qt, int64_t q
     const int64_t max_rows = bk < d_in ? bk : d_in;
     if (mf) {
       const int64_t ldc = mfma_coef_ld(max_rows);
-      float *coefT = reinterpret_cast<float *>(base + L.p.mfma_coef);
+      void *coefT = base + L.p.mfma_coef;
       e = launch_union_coef_t(u_idx, u_cnt, xs, static_cast<int>(B), static_cast<int>(d_in), ldc,
                               coefT, s);
       if (e == hipSuccess)

@@ -53,6 +53,19 @@ template <> struct Elt<uint16_t> {
   }
 };
 
+// Coefficients of the matrix-core product, stored split: for token b and
+// list position k, the bf16 truncation hi of c and lo = bf16(c − hi) sit in
+// 16-element groups [b][k / 8] of (8 hi, 8 lo), so one lane's eight
+// consecutive positions are one 16-byte hi load and one 16-byte lo load.
+// ldc (a multiple of 8) is the padded list length.
+__device__ __forceinline__ void store_coef_hl(uint16_t *base, int64_t ldc, int64_t b, int64_t k,
+                                              float c) {
+  const uint32_t u = __float_as_uint(c) & 0xFFFF0000u;
+  const int64_t at = (b * (ldc / 8) + k / 8) * 16 + k % 8;
+  base[at] = static_cast<uint16_t>(u >> 16);
+  base[at + 8] = f32_to_bf16(c - __uint_as_float(u));
+}
+
 __device__ __forceinline__ uint4 load16(const void *p) {
   return *reinterpret_cast<const uint4 *>(p);
 }

@@ -89,8 +89,8 @@ struct SelectGatherArgs {
 };
 hipError_t launch_select_gather(const SelectGatherArgs &a, hipStream_t s);
 
-// --- matrix-core forms for batches of 16..64 tokens in bf16 ---
-constexpr int kMfmaMinB = 16;
+// --- matrix-core forms for batches of 2..64 tokens in bf16 ---
+constexpr int kMfmaMinB = 2;
 bool mfma_supported(int64_t B, int act_dt, int w_dt);
 // Rotation; qb % 32 == 0. With ws == NULL the k-range is not split (one
 // launch, x_rot written directly); otherwise ws holds rotate_mfma_ws_bytes.
@@ -98,9 +98,10 @@ int rotate_mfma_splits(int64_t B, int64_t d, int64_t qb);
 size_t rotate_mfma_ws_bytes(int64_t B, int64_t d, int64_t qb);
 hipError_t launch_rotate_mfma(const void *x, const void *qt, float *x_rot, int B, int d, int qb,
                               void *ws, hipStream_t s);
-// Product over a row list with transposed coefficients coefT[b · ldc + j]
-// (ldc = mfma_coef_ld(max_rows); entries past the list's end must be finite,
-// normally zero). ws holds gather_mfma_ws_bytes.
+// Product over a row list with coefficients stored split and transposed
+// (store_coef_hl in common.hpp; B · ldc · 4 bytes, ldc = mfma_coef_ld(max_rows);
+// entries past the list's end must be finite, normally zero). ws holds
+// gather_mfma_ws_bytes.
 struct MfmaGatherPlan {
   int col_groups;      // workgroups across the columns (256 columns each)
   int splits;          // row splits, summed by a second kernel when > 1
@@ -110,16 +111,16 @@ MfmaGatherPlan plan_gather_mfma(int64_t B, int64_t max_rows, int64_t d_out);
 size_t gather_mfma_ws_bytes(int64_t B, int64_t max_rows, int64_t d_out);
 int64_t mfma_coef_ld(int64_t max_rows);
 hipError_t launch_gather_mfma(const int32_t *rows, const int32_t *n_rows, int64_t max_rows,
-                              int64_t d_in, const float *coefT, int64_t ldc, const void *w,
+                              int64_t d_in, const void *coef_hl, int64_t ldc, const void *w,
                               void *y, int B, int64_t d_out, void *ws, hipStream_t s);
-// coefT[b · ldc + j] = xs[b, u_idx[j]] for j < |U|, zero for j in [|U|, ldc).
+// Split coefficients of xs[b, u_idx[j]] for j < |U|, zero for j in [|U|, ldc).
 hipError_t launch_union_coef_t(const int32_t *u_idx, const int32_t *u_count, const float *xs,
-                               int B, int d, int64_t ldc, float *coefT, hipStream_t s);
-// coefT[b · ldc + j] = coef[j · B + b] for j < max_rows, zero up to ldc.
+                               int B, int d, int64_t ldc, void *coef_hl, hipStream_t s);
+// Split coefficients of coef[j · B + b] for j < max_rows, zero up to ldc.
 hipError_t launch_coef_transpose(const float *coef, int B, int64_t max_rows, int64_t ldc,
-                                 float *coefT, hipStream_t s);
-// coefT[b · ldc + j] = x[b, j] for a bf16 activation x [B, d_in], zero up to ldc.
-hipError_t launch_act_to_coef_t(const void *x, int B, int64_t d_in, int64_t ldc, float *coefT,
+                                 void *coef_hl, hipStream_t s);
+// Split coefficients of a bf16 activation x [B, d_in], zero up to ldc.
+hipError_t launch_act_to_coef_t(const void *x, int B, int64_t d_in, int64_t ldc, void *coef_hl,
                                 hipStream_t s);
 // Upper bound of gather_mfma_ws_bytes over every row-list length.
 size_t gather_mfma_ws_bound(int64_t B, int64_t d_out);

@@ -21,9 +21,9 @@
 // W'[row_j, :]. Rows of W' are contiguous along the output columns, so a
 // wave stages 32 rows × 64 columns in its own LDS area and reads the B
 // operand back with the gfx950 transpose read (ds_read_b64_tr_b16). The
-// fp32 coefficients are split into bf16 hi + lo parts (two MFMAs), which
+// fp32 coefficients arrive split into bf16 hi + lo parts (two MFMAs), which
 // keeps about 16 significant bits of each coefficient; products and sums
-// stay in fp32.
+// stay in fp32. Weight rows and coefficients are requested two steps ahead.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -47,20 +47,6 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) {
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// bf16 hi part (truncation) and the rounded remainder: c = hi + lo to about
-// 2^-16 relative.
-__device__ __forceinline__ void split_hi_lo(const float (&c)[8], bf16x8 &hi, bf16x8 &lo) {
-  uint16_t h[8], o[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t u = __float_as_uint(c[i]) & 0xFFFF0000u;
-    h[i] = static_cast<uint16_t>(u >> 16);
-    o[i] = f32_to_bf16(c[i] - __uint_as_float(u));
-  }
-  __builtin_memcpy(&hi, h, 16);
-  __builtin_memcpy(&lo, o, 16);
 }
 
 // ---- rotation --------------------------------------------------------------
@@ -118,13 +104,13 @@ __global__ __launch_bounds__(kMW * kWave) void rotate_mfma_kernel(
 // ---- product over kept rows ------------------------------------------------
 // Grid: (ceil(d_out / 256) column groups of four waves, splits). Split s
 // covers list positions [s·rps, s·rps + rps) (rps a multiple of 32). Coefficients
-// come transposed: coefT[b · ldc + j] for list position j (zero past the
+// come split and transposed (store_coef_hl) for list position j (zero past the
 // list's end, ldc a multiple of 32 and at least the list length rounded up
 // to 32). Split s writes out + s·B·d_out (fp32), or y when there is one split.
 template <int MT>
 __global__ __launch_bounds__(kMW * kWave) void gather_mfma_kernel(
     const int32_t *__restrict__ rows, const int32_t *__restrict__ n_rows_dev, int max_rows,
-    int d_in, const float *__restrict__ coefT, int ldc, const uint16_t *__restrict__ w,
+    int d_in, const uint16_t *__restrict__ coef_hl, int ldc, const uint16_t *__restrict__ w,
     int64_t d_out, float *__restrict__ out, uint16_t *__restrict__ y, int B, int rps) {
   __shared__ __align__(16) uint16_t tile[kMW][kMK * kPitch];
   const int lane = threadIdx.x % kWave;
@@ -144,13 +130,14 @@ __global__ __launch_bounds__(kMW * kWave) void gather_mfma_kernel(
   // s / 4, column 16·ns + 4·(s mod 4)
   const int g = lane / 16, s = lane % 16;
   const int tr_off = (g * 8 + s / 4) * kPitch + 4 * (s % 4);
-  // coefficients: lane l takes token 16·m + l mod 16, list positions
-  // k0 + 8·(l div 16) .. + 7
-  const float *crow[MT];
+  // coefficients (split hi/lo, see store_coef_hl): lane l takes token
+  // 16·m + l mod 16, list positions k0 + 8·(l div 16) .. + 7, whose hi and
+  // lo halves are 16 bytes each at crow[m] + 2·k0
+  const uint16_t *crow[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     const int b = m * 16 + lane % 16;
-    crow[m] = coefT + static_cast<int64_t>(b < B ? b : 0) * ldc + g * 8;
+    crow[m] = coef_hl + (static_cast<int64_t>(b < B ? b : 0) * ldc + g * 8) * 2;
   }
   f32x4 acc[4][MT];
 #pragma unroll
@@ -158,8 +145,10 @@ __global__ __launch_bounds__(kMW * kWave) void gather_mfma_kernel(
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[n][m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  uint4 nxt[4];
-  auto fetch = [&](int k0, uint4 (&v)[4]) {
+  // Two-deep software pipeline: the weight rows and the coefficients of
+  // step k + 2 are requested while step k is computed (the loop body is
+  // unrolled by two so both buffers stay in registers).
+  auto fetch = [&](int k0, uint4 (&v)[4], uint4 (&cv)[MT][2]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int r = k0 + srow + 8 * q;
@@ -168,23 +157,21 @@ __global__ __launch_bounds__(kMW * kWave) void gather_mfma_kernel(
       v[q] = row >= 0 && row < d_in ? load16(w + static_cast<int64_t>(row) * d_out + scol)
                                     : make_uint4(0, 0, 0, 0);
     }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      cv[m][0] = load16(crow[m] + 2 * k0);
+      cv[m][1] = load16(crow[m] + 2 * k0 + 8);
+    }
   };
-  if (r_begin < r_end) fetch(r_begin, nxt);
-  for (int k0 = r_begin; k0 < r_end; k0 += kMK) {
-    // stage this step's rows, then start fetching the next step's
+  auto step = [&](const uint4 (&v)[4], const uint4 (&cv)[MT][2]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<uint4 *>(my + (srow + 8 * q) * kPitch + (lane % 8) * 8) = nxt[q];
-    if (k0 + kMK < r_end) fetch(k0 + kMK, nxt);
+      *reinterpret_cast<uint4 *>(my + (srow + 8 * q) * kPitch + (lane % 8) * 8) = v[q];
     bf16x8 ahi[MT], alo[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      float c[8];
-      const float4 c0 = *reinterpret_cast<const float4 *>(crow[m] + k0);
-      const float4 c1 = *reinterpret_cast<const float4 *>(crow[m] + k0 + 4);
-      c[0] = c0.x; c[1] = c0.y; c[2] = c0.z; c[3] = c0.w;
-      c[4] = c1.x; c[5] = c1.y; c[6] = c1.z; c[7] = c1.w;
-      split_hi_lo(c, ahi[m], alo[m]);
+      ahi[m] = as_bf16x8(cv[m][0]);
+      alo[m] = as_bf16x8(cv[m][1]);
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS stores are done
     __builtin_amdgcn_wave_barrier();
@@ -206,6 +193,20 @@ __global__ __launch_bounds__(kMW * kWave) void gather_mfma_kernel(
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next step's stores
     __builtin_amdgcn_wave_barrier();
+  };
+  uint4 v0[4], v1[4];
+  uint4 c0[MT][2], c1[MT][2];
+  // coefficient reads past the split stay below ldc (a multiple of the step
+  // above the list length), so only the first fetch of each buffer is guarded
+  if (r_begin < r_end) fetch(r_begin, v0, c0);
+  if (r_begin + kMK < r_end) fetch(r_begin + kMK, v1, c1);
+  for (int k0 = r_begin; k0 < r_end; k0 += 2 * kMK) {
+    step(v0, c0);
+    if (k0 + 2 * kMK < r_end) fetch(k0 + 2 * kMK, v0, c0);
+    if (k0 + kMK < r_end) {
+      step(v1, c1);
+      if (k0 + 3 * kMK < r_end) fetch(k0 + 3 * kMK, v1, c1);
+    }
   }
   // lane l holds tokens 16·m + 4·(l div 16) + i of column col0 + 16·n + l mod 16
 #pragma unroll
@@ -246,13 +247,14 @@ __global__ void sum_parts_kernel(const float *__restrict__ part, int parts, int6
   Elt<OT>::store(dst, i + 3, s.w);
 }
 
-// coefT[b·ldc + j] = x[b, j] (bf16 → fp32) for j < d_in; zero up to ldc.
+// Split coefficients (store_coef_hl) of the bf16 activation x[b, j] for
+// j < d_in; zero up to ldc.
 __global__ void act_to_coef_t_kernel(const uint16_t *__restrict__ x, int B, int64_t d_in,
-                                     int64_t ldc, float *__restrict__ coefT) {
+                                     int64_t ldc, uint16_t *__restrict__ coef_hl) {
   const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (e >= ldc * B) return;
   const int64_t b = e / ldc, j = e % ldc;
-  coefT[e] = j < d_in ? bf16_to_f32(x[b * d_in + j]) : 0.f;
+  store_coef_hl(coef_hl, ldc, b, j, j < d_in ? bf16_to_f32(x[b * d_in + j]) : 0.f);
 }
 
 template <typename OT>
@@ -336,7 +338,7 @@ size_t gather_mfma_ws_bytes(int64_t B, int64_t max_rows, int64_t d_out) {
 int64_t mfma_coef_ld(int64_t max_rows) { return (max_rows + kMK - 1) / kMK * kMK; }
 
 hipError_t launch_gather_mfma(const int32_t *rows, const int32_t *n_rows, int64_t max_rows,
-                              int64_t d_in, const float *coefT, int64_t ldc, const void *w,
+                              int64_t d_in, const void *coef_hl, int64_t ldc, const void *w,
                               void *y, int B, int64_t d_out, void *ws, hipStream_t s) {
   const MfmaGatherPlan p = plan_gather_mfma(B, max_rows, d_out);
   float *out = static_cast<float *>(ws);
@@ -345,12 +347,13 @@ hipError_t launch_gather_mfma(const int32_t *rows, const int32_t *n_rows, int64_
   const int MT = (B + 15) / 16;
   const auto *wp = static_cast<const uint16_t *>(w);
   const int mr = static_cast<int>(max_rows), ld = static_cast<int>(ldc);
+  const auto *ch = static_cast<const uint16_t *>(coef_hl);
   const int di = static_cast<int>(d_in);
   switch (MT) {
-    case 1: hipLaunchKernelGGL(gather_mfma_kernel<1>, grid, dim3(kMW * kWave), 0, s, rows, n_rows, mr, di, coefT, ld, wp, d_out, out, yy, B, p.rows_per_split); break;
-    case 2: hipLaunchKernelGGL(gather_mfma_kernel<2>, grid, dim3(kMW * kWave), 0, s, rows, n_rows, mr, di, coefT, ld, wp, d_out, out, yy, B, p.rows_per_split); break;
-    case 3: hipLaunchKernelGGL(gather_mfma_kernel<3>, grid, dim3(kMW * kWave), 0, s, rows, n_rows, mr, di, coefT, ld, wp, d_out, out, yy, B, p.rows_per_split); break;
-    default: hipLaunchKernelGGL(gather_mfma_kernel<4>, grid, dim3(kMW * kWave), 0, s, rows, n_rows, mr, di, coefT, ld, wp, d_out, out, yy, B, p.rows_per_split); break;
+    case 1: hipLaunchKernelGGL(gather_mfma_kernel<1>, grid, dim3(kMW * kWave), 0, s, rows, n_rows, mr, di, ch, ld, wp, d_out, out, yy, B, p.rows_per_split); break;
+    case 2: hipLaunchKernelGGL(gather_mfma_kernel<2>, grid, dim3(kMW * kWave), 0, s, rows, n_rows, mr, di, ch, ld, wp, d_out, out, yy, B, p.rows_per_split); break;
+    case 3: hipLaunchKernelGGL(gather_mfma_kernel<3>, grid, dim3(kMW * kWave), 0, s, rows, n_rows, mr, di, ch, ld, wp, d_out, out, yy, B, p.rows_per_split); break;
+    default: hipLaunchKernelGGL(gather_mfma_kernel<4>, grid, dim3(kMW * kWave), 0, s, rows, n_rows, mr, di, ch, ld, wp, d_out, out, yy, B, p.rows_per_split); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
@@ -358,11 +361,12 @@ hipError_t launch_gather_mfma(const int32_t *rows, const int32_t *n_rows, int64_
                              static_cast<uint16_t *>(y), s);
 }
 
-hipError_t launch_act_to_coef_t(const void *x, int B, int64_t d_in, int64_t ldc, float *coefT,
+hipError_t launch_act_to_coef_t(const void *x, int B, int64_t d_in, int64_t ldc, void *coefT,
                                 hipStream_t s) {
   const int64_t n = ldc * B;
   hipLaunchKernelGGL(act_to_coef_t_kernel, dim3(static_cast<unsigned>((n + 255) / 256)),
-                     dim3(256), 0, s, static_cast<const uint16_t *>(x), B, d_in, ldc, coefT);
+                     dim3(256), 0, s, static_cast<const uint16_t *>(x), B, d_in, ldc,
+                     static_cast<uint16_t *>(coefT));
   return hipGetLastError();
 }
 

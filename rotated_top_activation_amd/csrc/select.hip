@@ -103,27 +103,28 @@ __global__ void union_coef_kernel(const int32_t *__restrict__ u_idx,
   coef[e] = j < n ? xs[static_cast<int64_t>(b) * d + u_idx[j]] : 0.f;
 }
 
-// coefT[b·ldc + j] = xs[b, u_idx[j]] for j < |U|; zero for j in [|U|, ldc).
+// Split coefficients (store_coef_hl) of xs[b, u_idx[j]] for j < |U|; zero
+// for j in [|U|, ldc).
 __global__ void union_coef_t_kernel(const int32_t *__restrict__ u_idx,
                                     const int32_t *__restrict__ u_count,
                                     const float *__restrict__ xs, int B, int d, int64_t ldc,
-                                    float *__restrict__ coefT) {
+                                    uint16_t *__restrict__ coef_hl) {
   const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (e >= ldc * B) return;
   const int b = static_cast<int>(e / ldc);
   const int64_t j = e % ldc;
   const int n = *u_count;
-  coefT[e] = j < n ? xs[static_cast<int64_t>(b) * d + u_idx[j]] : 0.f;
+  store_coef_hl(coef_hl, ldc, b, j, j < n ? xs[static_cast<int64_t>(b) * d + u_idx[j]] : 0.f);
 }
 
-// coefT[b·ldc + j] = coef[j·B + b] for j < rows; zero for j in [rows, ldc).
+// Split coefficients of coef[j·B + b] for j < rows; zero for j in [rows, ldc).
 __global__ void coef_transpose_kernel(const float *__restrict__ coef, int B, int64_t rows,
-                                      int64_t ldc, float *__restrict__ coefT) {
+                                      int64_t ldc, uint16_t *__restrict__ coef_hl) {
   const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (e >= ldc * B) return;
   const int b = static_cast<int>(e / ldc);
   const int64_t j = e % ldc;
-  coefT[e] = j < rows ? coef[j * B + b] : 0.f;
+  store_coef_hl(coef_hl, ldc, b, j, j < rows ? coef[j * B + b] : 0.f);
 }
 
 template <int EMAX>
@@ -160,18 +161,18 @@ hipError_t launch_union(const uint32_t *mask, const float *xs, int B, int d,
 }
 
 hipError_t launch_union_coef_t(const int32_t *u_idx, const int32_t *u_count, const float *xs,
-                               int B, int d, int64_t ldc, float *coefT, hipStream_t s) {
+                               int B, int d, int64_t ldc, void *coefT, hipStream_t s) {
   const int64_t n = ldc * B;
   hipLaunchKernelGGL(union_coef_t_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
-                     0, s, u_idx, u_count, xs, B, d, ldc, coefT);
+                     0, s, u_idx, u_count, xs, B, d, ldc, static_cast<uint16_t *>(coefT));
   return hipGetLastError();
 }
 
 hipError_t launch_coef_transpose(const float *coef, int B, int64_t max_rows, int64_t ldc,
-                                 float *coefT, hipStream_t s) {
+                                 void *coefT, hipStream_t s) {
   const int64_t n = ldc * B;
   hipLaunchKernelGGL(coef_transpose_kernel, dim3(static_cast<unsigned>((n + 255) / 256)),
-                     dim3(256), 0, s, coef, B, max_rows, ldc, coefT);
+                     dim3(256), 0, s, coef, B, max_rows, ldc, static_cast<uint16_t *>(coefT));
   return hipGetLastError();
 }
 
