@@ -145,14 +145,20 @@ __global__ __launch_bounds__(kMW * kWave) void gather_mfma_kernel(
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[n][m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Two-deep software pipeline: the weight rows and the coefficients of
-  // step k + 2 are requested while step k is computed (the loop body is
-  // unrolled by two so both buffers stay in registers).
-  auto fetch = [&](int k0, uint4 (&v)[4], uint4 (&cv)[MT][2]) {
+  // Software pipeline: the row indices of step k + 4, and the weight rows
+  // and coefficients of step k + 2, are requested while step k is computed
+  // (the loop body is unrolled by two so every buffer stays in registers).
+  auto fetch_idx = [&](int k0, int (&ix)[4]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int r = k0 + srow + 8 * q;
-      const int row = r < r_end ? (rows ? rows[r] : r) : -1;
+      ix[q] = r < r_end ? (rows ? rows[r] : r) : -1;
+    }
+  };
+  auto fetch = [&](int k0, const int (&ix)[4], uint4 (&v)[4], uint4 (&cv)[MT][2]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = ix[q];
       // rows outside [0, d_in) contribute nothing
       v[q] = row >= 0 && row < d_in ? load16(w + static_cast<int64_t>(row) * d_out + scol)
                                     : make_uint4(0, 0, 0, 0);
@@ -196,16 +202,31 @@ __global__ __launch_bounds__(kMW * kWave) void gather_mfma_kernel(
   };
   uint4 v0[4], v1[4];
   uint4 c0[MT][2], c1[MT][2];
-  // coefficient reads past the split stay below ldc (a multiple of the step
-  // above the list length), so only the first fetch of each buffer is guarded
-  if (r_begin < r_end) fetch(r_begin, v0, c0);
-  if (r_begin + kMK < r_end) fetch(r_begin + kMK, v1, c1);
+  int i0[4], i1[4];
+  // every fetch is guarded by its step being below r_end, so coefficient
+  // reads stay below ldc (a multiple of the step above the list length)
+  if (r_begin < r_end) {
+    fetch_idx(r_begin, i0);
+    fetch(r_begin, i0, v0, c0);
+    fetch_idx(r_begin + 2 * kMK, i0);
+  }
+  if (r_begin + kMK < r_end) {
+    fetch_idx(r_begin + kMK, i1);
+    fetch(r_begin + kMK, i1, v1, c1);
+    fetch_idx(r_begin + 3 * kMK, i1);
+  }
   for (int k0 = r_begin; k0 < r_end; k0 += 2 * kMK) {
     step(v0, c0);
-    if (k0 + 2 * kMK < r_end) fetch(k0 + 2 * kMK, v0, c0);
+    if (k0 + 2 * kMK < r_end) {
+      fetch(k0 + 2 * kMK, i0, v0, c0);
+      fetch_idx(k0 + 4 * kMK, i0);
+    }
     if (k0 + kMK < r_end) {
       step(v1, c1);
-      if (k0 + 3 * kMK < r_end) fetch(k0 + 3 * kMK, v1, c1);
+      if (k0 + 3 * kMK < r_end) {
+        fetch(k0 + 3 * kMK, i1, v1, c1);
+        fetch_idx(k0 + 5 * kMK, i1);
+      }
     }
   }
   // lane l holds tokens 16·m + 4·(l div 16) + i of column col0 + 16·n + l mod 16
