@@ -251,6 +251,9 @@ def main():
         torch.matmul(x_d, wf1[i % copies], out=out_t)
     torch_ms = timed(tmm, a.steps, a.warmup)
 
+    def gbs(nbytes, ms_):
+        return nbytes / (ms_ * 1e-3) / 1e9
+
     # Per-stage times of the unfused step (each stage alone, cycling copies).
     stage = {}
     stage["rotate1"] = timed(lambda i: _lib.larosa_rotate(x_d, qt1[i % copies], l1.q_block, xr1,
@@ -264,13 +267,28 @@ def main():
                                                                      val1), a.steps, a.warmup)
     stage["gather1_alone"] = gather_ms
 
+    # The fp64-accumulating rotation beside the fp32 one, for both rotations
+    # of the MLP at 1, 4 and 8 tokens, and the one-token step with it.
+    exact_rot = {}
+    for nb in (1, 4, 8):
+        for tag, src, lin, dd, dst_d in (("q1", x_d, l1, d, xr1), ("q2", h, l2, f, xr2)):
+            xb = src.expand(nb, dd).contiguous()
+            dst = dst_d if nb == 1 else torch.empty((nb, dd), dtype=torch.float32, device=dev)
+            qts = qt1 if tag == "q1" else qt2
+            for prec, fn in (("fp32", _lib.larosa_rotate), ("fp64", _lib.larosa_rotate_fp64)):
+                t = timed(lambda i, fn=fn, xb=xb, dst=dst, qts=qts, lin=lin, nb=nb, dd=dd:
+                          fn(xb, qts[i % copies], lin.q_block, dst, nb, dd), a.steps, a.warmup)
+                nbytes = lin.Qt.numel() * 2 + nb * dd * (2 + 4)
+                exact_rot[f"{tag}_b{nb}_{prec}"] = {"us": round(t * 1e3, 2),
+                                                    "GBs": round(gbs(nbytes, t), 1)}
+    exact_rot["step_ms_unfused_fp64_rotation"] = round(
+        timed(lambda i: step(i, _lib.UNFUSED | _lib.ROTATE_FP64), a.steps, a.warmup), 5)
+
     q_bytes = (l1.Qt.numel() + l2.Qt.numel()) * 2
     sparse_bytes = q_bytes + (case.k1 * 2 * f + case.k2 * d) * 2
     dense_mlp_bytes = (d * 2 * f + f * d) * 2
     best = min(step_ms, key=step_ms.get)
     ms = step_ms[best]
-    def gbs(nbytes, ms_):
-        return nbytes / (ms_ * 1e-3) / 1e9
     kernels = {
         "select_gather_kernel": dict(achieved=gbs(topk1_bytes, topk1_ms), bytes=topk1_bytes,
                                      us=topk1_ms * 1e3,
@@ -330,6 +348,7 @@ def main():
             "mlp_dense_weight_bytes": dense_mlp_bytes,
             "mlp_achieved_GBs": round(sparse_bytes / (ms * 1e-3) / 1e9, 1),
             "stage_us": {k: round(v * 1e3, 2) for k, v in stage.items()},
+            "rotation_fp32_vs_fp64": exact_rot,
             "kernels": {k: {"achieved_GBs": round(v["achieved"], 1), "bytes_per_launch": v["bytes"],
                             "avg_us": round(v["us"], 3), "frac": round(v["achieved"] / HBM_PEAK_GBS, 4),
                             "traffic": measured_traffic(k)} for k, v in kernels.items()},

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define LAROSA_ABI_VERSION 2
+#define LAROSA_ABI_VERSION 3
 
 typedef void *larosa_stream_t; /* hipStream_t */
 
@@ -69,6 +69,13 @@ enum {
 
 /* Execution modes of larosa_layer_forward. */
 enum { LAROSA_UNFUSED = 0, LAROSA_FUSED = 1 };
+
+/* Mode flag, OR-ed into the mode of larosa_layer_forward,
+ * larosa_swiglu_layer_forward and their workspace-size calls: the rotation
+ * accumulates in fp64 and rounds once to fp32 (larosa_rotate_fp64), so the
+ * selected index sets follow the exactly rounded x·Q. With this flag
+ * LAROSA_FUSED runs the unfused steps. Any other bit is an invalid mode. */
+enum { LAROSA_ROTATE_FP64 = 2 };
 
 /* LAROSA_ABI_VERSION of the loaded library. */
 int larosa_abi_version(void);
@@ -112,6 +119,20 @@ int larosa_fold_weights(const void *Qt, int64_t q_block, const void *W,
 int larosa_rotate(const void *x, int x_dtype, const void *Qt, int64_t q_block,
                   int q_dtype, float *x_rot, int64_t B, int64_t d,
                   larosa_stream_t stream);
+
+/* The same rotation with fp64 accumulation: every product x[b, i]·Q[i, j]
+ * of two bf16 or two fp32 values is exact in fp64, the sum is kept in fp64
+ * and rounded to nearest even fp32 once. x_rot then equals fp32(x·Q) of the
+ * exact product except where that product lies within about 2^-53·√q_block
+ * (relative) of an fp32 rounding midpoint, so the Top-K sets taken from it
+ * match the exact rotation's (the fixed-K selection of stage 2 depends on
+ * the rotated magnitudes only). Arguments, layout and errors as
+ * larosa_rotate. Qt is read once per 8 tokens. One token costs about what
+ * the fp32 form does (both read Qt once); from a few tokens on, the fp64
+ * conversions and FMAs, not HBM, bound it. */
+int larosa_rotate_fp64(const void *x, int x_dtype, const void *Qt,
+                       int64_t q_block, int q_dtype, float *x_rot, int64_t B,
+                       int64_t d, larosa_stream_t stream);
 
 /* Top-K selection, stage 2 of the method (LaRoSA summary page, 技术框架;
  * the abstract's fixed-K "consistent model-level sparsity"): for each token
@@ -173,7 +194,8 @@ int larosa_topk_gemv(const float *x_rot, int64_t d_in, int64_t k,
  * [d_in, q_block] in w_dtype. idx_out [B, k] and xrot_out [B, d_in] (fp32)
  * are optional copies of the selection and the rotated input (NULL skips
  * them). mode: LAROSA_UNFUSED (one kernel per step) or LAROSA_FUSED (one
- * persistent launch for B == 1; other B fall back to the unfused steps). */
+ * persistent launch for B == 1; other B fall back to the unfused steps),
+ * optionally OR-ed with LAROSA_ROTATE_FP64. */
 int larosa_layer_forward(const void *x, int act_dtype, const void *Qt,
                          int64_t q_block, const void *W_folded, int w_dtype,
                          int64_t B, int64_t d_in, int64_t d_out, int64_t k,

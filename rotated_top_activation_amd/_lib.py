@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblarosa.s
 
 F32, BF16 = 0, 1
 UNFUSED, FUSED = 0, 1
-ABI_VERSION = 2
+ROTATE_FP64 = 2  # mode flag: fp64-accumulating rotation, OR-ed into UNFUSED or FUSED
+ABI_VERSION = 3
 
 _c_i64 = ctypes.c_int64
 _c_int = ctypes.c_int
@@ -35,6 +36,8 @@ SIGNATURES = {
     "larosa_prepare_rotation": (_c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_vp]),
     "larosa_fold_weights": (_c_int, [_c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_vp]),
     "larosa_rotate": (_c_int, [_c_vp, _c_int, _c_vp, _c_i64, _c_int, _c_vp, _c_i64, _c_i64, _c_vp]),
+    "larosa_rotate_fp64": (_c_int, [_c_vp, _c_int, _c_vp, _c_i64, _c_int, _c_vp, _c_i64, _c_i64,
+                                    _c_vp]),
     "larosa_topk_select": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp,
                                     _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
     "larosa_sparse_gemv": (_c_int, [_c_vp, _c_vp, _c_i64, _c_vp, _c_vp, _c_int, _c_vp, _c_int,
@@ -151,6 +154,12 @@ def larosa_rotate(x, Qt, q_block: int, x_rot, B: int, d: int, stream=None) -> No
     _check("larosa_rotate",
            load().larosa_rotate(_ptr(x), _dt(x), _ptr(Qt), q_block, _dt(Qt), _ptr(x_rot), B, d,
                                 _stream(stream)))
+
+
+def larosa_rotate_fp64(x, Qt, q_block: int, x_rot, B: int, d: int, stream=None) -> None:
+    _check("larosa_rotate_fp64",
+           load().larosa_rotate_fp64(_ptr(x), _dt(x), _ptr(Qt), q_block, _dt(Qt), _ptr(x_rot), B,
+                                     d, _stream(stream)))
 
 
 def larosa_topk_select(x_rot, B: int, d: int, k: int, idx, val, xs=None, union_idx=None,

@@ -129,6 +129,15 @@ int check_rotation(int64_t d, int64_t qb, int q_dt) {
   return LAROSA_OK;
 }
 
+// The execution mode without the LAROSA_ROTATE_FP64 flag, or -1 when the
+// mode holds any other bit.
+int base_mode(int mode) {
+  const int m = mode & ~LAROSA_ROTATE_FP64;
+  return m == LAROSA_UNFUSED || m == LAROSA_FUSED ? m : -1;
+}
+
+bool fp64_rotation(int mode) { return (mode & LAROSA_ROTATE_FP64) != 0; }
+
 }  // namespace
 
 extern "C" {
@@ -151,7 +160,8 @@ const char *larosa_status_string(int status) {
 
 size_t larosa_workspace_bytes(int64_t B, int64_t d_in, int64_t d_out, int64_t k, int mode) {
   if (check_sizes(B < 1 ? 1 : B, d_in, k) != LAROSA_OK || d_out < 1) return 0;
-  if (mode != LAROSA_UNFUSED && mode != LAROSA_FUSED) return 0;
+  if (base_mode(mode) < 0) return 0;
+  mode = base_mode(mode);
   // Sized for bf16 weights; fp32 weights have twice the column tiles but the
   // same number of splits at most, and fit in the same bytes or fewer.
   const int64_t b1 = B < 1 ? 1 : B;
@@ -220,6 +230,21 @@ int larosa_rotate(const void *x, int x_dtype, const void *Qt, int64_t q_block, i
   return launched(launch_rotate(x, x_dtype, Qt, q_dtype, x_rot, static_cast<int>(B),
                                 static_cast<int>(d), static_cast<int>(q_block),
                                 stream_of(stream)));
+}
+
+int larosa_rotate_fp64(const void *x, int x_dtype, const void *Qt, int64_t q_block,
+                       int q_dtype, float *x_rot, int64_t B, int64_t d, larosa_stream_t stream) {
+  if (!dtype_ok(x_dtype) || !dtype_ok(q_dtype)) return LAROSA_ERR_DTYPE;
+  if (int st = check_sizes(B, d, 1)) return st;
+  if (B == 0) return LAROSA_OK;
+  if (!x || !Qt || !x_rot) return LAROSA_ERR_INVALID_ARG;
+  if (int st = check_rotation(d, q_block, q_dtype)) return st;
+  if (d % 8 && x_dtype == LAROSA_BF16) return LAROSA_ERR_ALIGNMENT;
+  if (!aligned16(x) || !aligned16(Qt) || !aligned16(x_rot)) return LAROSA_ERR_ALIGNMENT;
+  if (int st = device_status()) return st;
+  return launched(launch_rotate_f64(x, x_dtype, Qt, q_dtype, x_rot, static_cast<int>(B),
+                                    static_cast<int>(d), static_cast<int>(q_block),
+                                    stream_of(stream)));
 }
 
 int larosa_topk_select(const float *x_rot, int64_t B, int64_t d, int64_t k, int32_t *idx,
@@ -375,7 +400,7 @@ int larosa_layer_forward(const void *x, int act_dtype, const void *Qt, int64_t q
   if (!dtype_ok(act_dtype) || !dtype_ok(w_dtype)) return LAROSA_ERR_DTYPE;
   if (w_dtype == LAROSA_F32 && act_dtype == LAROSA_BF16) return LAROSA_ERR_DTYPE;
   if (int st = check_sizes(B, d_in, k)) return st;
-  if (mode != LAROSA_UNFUSED && mode != LAROSA_FUSED) return LAROSA_ERR_INVALID_ARG;
+  if (base_mode(mode) < 0) return LAROSA_ERR_INVALID_ARG;
   if (d_out < 1) return LAROSA_ERR_SHAPE;
   if (B == 0) return LAROSA_OK;
   if (!x || !Qt || !W_folded || !y) return LAROSA_ERR_INVALID_ARG;
@@ -384,7 +409,9 @@ int larosa_layer_forward(const void *x, int act_dtype, const void *Qt, int64_t q
   if (!aligned16(x) || !aligned16(Qt) || !aligned16(W_folded) || !aligned16(y))
     return LAROSA_ERR_ALIGNMENT;
   if ((xrot_out && !aligned16(xrot_out)) || !aligned16(ws)) return LAROSA_ERR_ALIGNMENT;
-  const bool fused = mode == LAROSA_FUSED && fused_supported(B, d_in, act_dtype, w_dtype);
+  const bool f64 = fp64_rotation(mode);
+  const bool fused = base_mode(mode) == LAROSA_FUSED && !f64 &&
+                     fused_supported(B, d_in, act_dtype, w_dtype);
   const Layout L = fused ? layout_with_fused(B, d_in, d_out, k, w_dtype)
                          : layout_for(B, d_in, d_out, k, w_dtype);
   if (!ws || ws_bytes < L.total) return LAROSA_ERR_WORKSPACE;
@@ -417,7 +444,9 @@ int larosa_layer_forward(const void *x, int act_dtype, const void *Qt, int64_t q
   // whole batch.
   const bool mf = mfma_supported(B, act_dtype, w_dtype);
   hipError_t e =
-      mf && q_block % 32 == 0
+      f64   ? launch_rotate_f64(x, act_dtype, Qt, w_dtype, x_rot, static_cast<int>(B),
+                                static_cast<int>(d_in), static_cast<int>(q_block), s)
+      : mf && q_block % 32 == 0
           ? launch_rotate_mfma(x, Qt, x_rot, static_cast<int>(B), static_cast<int>(d_in),
                                static_cast<int>(q_block), base + L.p.mfma_parts, s)
           : launch_rotate(x, act_dtype, Qt, w_dtype, x_rot, static_cast<int>(B),
@@ -520,7 +549,7 @@ int larosa_swiglu_layer_forward(const void *x, int act_dtype, const void *Qt, in
                                 larosa_stream_t stream) {
   if (!dtype_ok(act_dtype) || !dtype_ok(w_dtype)) return LAROSA_ERR_DTYPE;
   if (f < 1 || f % interleave_block(w_dtype)) return LAROSA_ERR_SHAPE;
-  if (mode != LAROSA_UNFUSED && mode != LAROSA_FUSED) return LAROSA_ERR_INVALID_ARG;
+  if (base_mode(mode) < 0) return LAROSA_ERR_INVALID_ARG;
   const size_t need = larosa_swiglu_workspace_bytes(B, d_in, f, k, mode);
   if (need == 0 && B != 0) {  // invalid sizes: let the layer call name the error
     return larosa_layer_forward(x, act_dtype, Qt, q_block, W_il, w_dtype, B, d_in, 2 * f, k, h,
@@ -531,7 +560,8 @@ int larosa_swiglu_layer_forward(const void *x, int act_dtype, const void *Qt, in
   if (!aligned16(h)) return LAROSA_ERR_ALIGNMENT;
   if (!ws || ws_bytes < need) return LAROSA_ERR_WORKSPACE;
   const size_t layer_bytes = larosa_workspace_bytes(B, d_in, 2 * f, k, mode);
-  const bool one_launch = mode == LAROSA_UNFUSED && B == 1 && select_gather_supported(d_in) &&
+  const bool one_launch = (base_mode(mode) == LAROSA_UNFUSED || fp64_rotation(mode)) && B == 1 &&
+                          select_gather_supported(d_in) &&
                           !(w_dtype == LAROSA_F32 && act_dtype == LAROSA_BF16);
   if (one_launch) {
     // rotation, then the selection, product and SiLU(gate)·up in one launch
@@ -547,9 +577,13 @@ int larosa_swiglu_layer_forward(const void *x, int act_dtype, const void *Qt, in
     char *base = static_cast<char *>(ws);
     float *x_rot = xrot_out ? xrot_out : reinterpret_cast<float *>(base + L.x_rot);
     hipStream_t s = stream_of(stream);
-    if (launch_rotate(x, act_dtype, Qt, w_dtype, x_rot, 1, static_cast<int>(d_in),
-                      static_cast<int>(q_block), s) != hipSuccess)
-      return LAROSA_ERR_LAUNCH;
+    const hipError_t er =
+        fp64_rotation(mode)
+            ? launch_rotate_f64(x, act_dtype, Qt, w_dtype, x_rot, 1, static_cast<int>(d_in),
+                                static_cast<int>(q_block), s)
+            : launch_rotate(x, act_dtype, Qt, w_dtype, x_rot, 1, static_cast<int>(d_in),
+                            static_cast<int>(q_block), s);
+    if (er != hipSuccess) return LAROSA_ERR_LAUNCH;
     SelectGatherArgs g;
     g.x_rot = x_rot;
     g.d_in = static_cast<int>(d_in);

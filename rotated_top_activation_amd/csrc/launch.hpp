@@ -14,6 +14,9 @@ inline int dt_size(int dt) { return dt == kF32 ? 4 : 2; }
 // --- rotation (dot product per output channel against the prepared Qt) ---
 hipError_t launch_rotate(const void *x, int x_dt, const void *qt, int q_dt,
                          float *x_rot, int B, int d, int qb, hipStream_t s);
+// fp64 accumulation, one rounding to fp32 (any B; one pass per 8 tokens)
+hipError_t launch_rotate_f64(const void *x, int x_dt, const void *qt, int q_dt, float *x_rot,
+                             int B, int d, int qb, hipStream_t s);
 
 // --- Top-K selection (one workgroup per token) ---
 hipError_t launch_select(const float *x_rot, int B, int d, int k, int32_t *idx,

@@ -168,6 +168,158 @@ hipError_t launch_b(const void *x, int x_dt, const void *qt, int q_dt, float *x_
   return hipErrorInvalidValue;
 }
 
+// fp64-accumulating rotation. Each product of two bf16 values, or of two
+// fp32 values, is exact in fp64, and the fp64 sum carries a relative error
+// near 2^-53·√qb, so rounding it once to fp32 gives the correctly rounded
+// x·Q except when that product lies within the fp64 error of an fp32
+// rounding midpoint. Index sets taken from this x_rot therefore agree with
+// the ones taken from the exact product, not just up to legitimate fp32
+// summation-order ties at the K boundary (the method's Top-K, stage 2).
+// One wave per output channel and up to NB tokens. For one token this reads
+// Qt at about the fp32 form's rate; with more tokens the per-element fp64
+// conversions and FMAs (full rate on CDNA4, 16 lanes per clock per SIMD)
+// become the bound.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int off = kWave / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+template <int NC, int NB, typename XT, typename QT>
+__global__ __launch_bounds__(kWavesPerBlock * kWave) void rotate_f64_kernel(
+    const XT *__restrict__ x, const QT *__restrict__ qt, float *__restrict__ x_rot, int B,
+    int d, int qb) {
+  constexpr int V = Elt<QT>::kVec;
+  const int lane = threadIdx.x % kWave;
+  const int j = blockIdx.x * kWavesPerBlock + wave_id();
+  if (j >= d) return;
+  const int b0 = blockIdx.y * NB;
+  const int64_t xoff = static_cast<int64_t>(j / qb) * qb;
+  const QT *row = qt + static_cast<int64_t>(j) * qb;
+  const int chunks = qb / V;
+  const XT *xrow[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int bb = b0 + b < B ? b0 + b : B - 1;  // tokens past B: loaded, not stored
+    xrow[b] = x + static_cast<int64_t>(bb) * d + xoff;
+  }
+  double acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = 0.0;
+  // NC·64 chunks of the Qt row in flight at once (the whole row up to
+  // q_block = 8192 in bf16); x (shared by every wave of the block, so
+  // cache-resident) is read per chunk, one load per token
+  for (int seg = 0; seg < chunks; seg += NC * kWave) {
+    uint4 q[NC];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c = seg + lane + kWave * i;
+      q[i] = c < chunks ? load16(row + c * V) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c = seg + lane + kWave * i;
+      if (c >= chunks) break;
+      float qf[V];
+      Elt<QT>::unpack(q[i], qf);
+      double qd[V];
+#pragma unroll
+      for (int v = 0; v < V; ++v) qd[v] = static_cast<double>(qf[v]);
+      float xf[NB][V];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) XLoad<XT, V>::run(xrow[b], static_cast<int64_t>(c) * V, xf[b]);
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int v = 0; v < V; ++v) acc[b] = fma(static_cast<double>(xf[b][v]), qd[v], acc[b]);
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const double s = wave_sum_f64(acc[b]);
+    if (lane == 0 && b0 + b < B) x_rot[static_cast<int64_t>(b0 + b) * d + j] = static_cast<float>(s);
+  }
+}
+
+// One token, x and Qt of one element type: every load of the row is issued
+// before any is used, as in the fp32 one-token form above.
+template <int NC, typename T>
+__global__ __launch_bounds__(kWavesPerBlock * kWave) void rotate_row_f64_kernel(
+    const T *__restrict__ x, const T *__restrict__ qt, float *__restrict__ x_rot, int d,
+    int qb) {
+  constexpr int V = Elt<T>::kVec;
+  const int lane = threadIdx.x % kWave;
+  const int j = blockIdx.x * kWavesPerBlock + wave_id();
+  if (j >= d) return;
+  const int64_t xoff = static_cast<int64_t>(j / qb) * qb;
+  const T *row = qt + static_cast<int64_t>(j) * qb;
+  const int chunks = qb / V;
+  uint4 xq[NC], q[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = lane + kWave * i;
+    const bool ok = c < chunks;
+    xq[i] = ok ? load16(x + xoff + c * V) : make_uint4(0, 0, 0, 0);
+    q[i] = ok ? load16(row + c * V) : make_uint4(0, 0, 0, 0);
+  }
+  double acc = 0.0;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    float xf[V], qf[V];
+    Elt<T>::unpack(xq[i], xf);
+    Elt<T>::unpack(q[i], qf);
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      acc = fma(static_cast<double>(xf[v]), static_cast<double>(qf[v]), acc);
+  }
+  const double s = wave_sum_f64(acc);
+  if (lane == 0) x_rot[j] = static_cast<float>(s);
+}
+
+template <typename T>
+bool launch_row_f64(const void *x, const void *qt, float *x_rot, int d, int qb, hipStream_t s) {
+  constexpr int V = Elt<T>::kVec;
+  const int nc = (qb / V + kWave - 1) / kWave;
+  const dim3 grid((d + kWavesPerBlock - 1) / kWavesPerBlock), block(kWavesPerBlock * kWave);
+  const auto *xp = static_cast<const T *>(x);
+  const auto *qp = static_cast<const T *>(qt);
+  if (nc <= 2) hipLaunchKernelGGL((rotate_row_f64_kernel<2, T>), grid, block, 0, s, xp, qp, x_rot, d, qb);
+  else if (nc <= 4) hipLaunchKernelGGL((rotate_row_f64_kernel<4, T>), grid, block, 0, s, xp, qp, x_rot, d, qb);
+  else if (nc <= 8) hipLaunchKernelGGL((rotate_row_f64_kernel<8, T>), grid, block, 0, s, xp, qp, x_rot, d, qb);
+  else if (nc <= 16) hipLaunchKernelGGL((rotate_row_f64_kernel<16, T>), grid, block, 0, s, xp, qp, x_rot, d, qb);
+  else return false;
+  return true;
+}
+
+template <int NC, int NB, typename XT, typename QT>
+hipError_t launch_f64_t(const void *x, const void *qt, float *x_rot, int B, int d, int qb,
+                        hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((d + kWavesPerBlock - 1) / kWavesPerBlock),
+                  static_cast<unsigned>((B + NB - 1) / NB));
+  hipLaunchKernelGGL((rotate_f64_kernel<NC, NB, XT, QT>), grid, dim3(kWavesPerBlock * kWave), 0,
+                     s, static_cast<const XT *>(x), static_cast<const QT *>(qt), x_rot, B, d, qb);
+  return hipGetLastError();
+}
+
+template <int NB, typename XT, typename QT>
+hipError_t launch_f64_nc(const void *x, const void *qt, float *x_rot, int B, int d, int qb,
+                         hipStream_t s) {
+  const int nc = (qb / Elt<QT>::kVec + kWave - 1) / kWave;
+  if (nc <= 2) return launch_f64_t<2, NB, XT, QT>(x, qt, x_rot, B, d, qb, s);
+  if (nc <= 4) return launch_f64_t<4, NB, XT, QT>(x, qt, x_rot, B, d, qb, s);
+  if (nc <= 8) return launch_f64_t<8, NB, XT, QT>(x, qt, x_rot, B, d, qb, s);
+  return launch_f64_t<16, NB, XT, QT>(x, qt, x_rot, B, d, qb, s);  // looped past 16
+}
+
+template <typename XT, typename QT>
+hipError_t launch_f64_nb(const void *x, const void *qt, float *x_rot, int B, int d, int qb,
+                         hipStream_t s) {
+  if (B == 1) return launch_f64_nc<1, XT, QT>(x, qt, x_rot, B, d, qb, s);
+  if (B == 2) return launch_f64_nc<2, XT, QT>(x, qt, x_rot, B, d, qb, s);
+  if (B <= 4) return launch_f64_nc<4, XT, QT>(x, qt, x_rot, B, d, qb, s);
+  return launch_f64_nc<8, XT, QT>(x, qt, x_rot, B, d, qb, s);
+}
+
 }  // namespace
 
 hipError_t launch_rotate(const void *x, int x_dt, const void *qt, int q_dt,
@@ -193,6 +345,20 @@ hipError_t launch_rotate(const void *x, int x_dt, const void *qt, int q_dt,
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+hipError_t launch_rotate_f64(const void *x, int x_dt, const void *qt, int q_dt, float *x_rot,
+                             int B, int d, int qb, hipStream_t s) {
+  if (B == 1 && x_dt == q_dt) {
+    const bool done = x_dt == kBF16 ? launch_row_f64<uint16_t>(x, qt, x_rot, d, qb, s)
+                                    : launch_row_f64<float>(x, qt, x_rot, d, qb, s);
+    if (done) return hipGetLastError();
+  }
+  if (x_dt == kBF16 && q_dt == kBF16) return launch_f64_nb<uint16_t, uint16_t>(x, qt, x_rot, B, d, qb, s);
+  if (x_dt == kF32 && q_dt == kF32) return launch_f64_nb<float, float>(x, qt, x_rot, B, d, qb, s);
+  if (x_dt == kF32 && q_dt == kBF16) return launch_f64_nb<float, uint16_t>(x, qt, x_rot, B, d, qb, s);
+  if (x_dt == kBF16 && q_dt == kF32) return launch_f64_nb<uint16_t, float>(x, qt, x_rot, B, d, qb, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace larosa

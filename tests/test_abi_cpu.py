@@ -55,7 +55,11 @@ def test_workspace_bytes(lib):
     assert f(1, 4096, 22016, 0, 0) == 0          # k out of range
     assert f(1, 4096, 22016, 4097, 0) == 0
     assert f(1, 40000, 128, 10, 0) == 0          # d above 32768
-    assert f(1, 4096, 22016, 2457, 7) == 0       # unknown mode
+    assert f(1, 4096, 22016, 2457, 7) == 0       # unknown mode bit
+    assert f(1, 4096, 22016, 2457, 4) == 0
+    # the fp64-rotation flag needs no extra workspace
+    assert f(1, 4096, 22016, 2457, 2) == f(1, 4096, 22016, 2457, 0)
+    assert f(4, 4096, 22016, 2457, 3) == f(4, 4096, 22016, 2457, 1)
     assert f(8, 4096, 22016, 2457, 0) >= f(1, 4096, 22016, 2457, 0)
 
 
@@ -70,7 +74,9 @@ def test_layer_forward_validation(lib):
     assert _lf(lib, k=129) == INVALID
     assert _lf(lib, B=-1) == INVALID
     assert _lf(lib, B=65) == INVALID
-    assert _lf(lib, mode=3) == INVALID
+    assert _lf(lib, mode=4) == INVALID
+    assert _lf(lib, mode=6) == INVALID
+    assert _lf(lib, mode=2, k=0) == INVALID      # the flag does not skip the checks
     assert _lf(lib, x=None) == INVALID
     assert _lf(lib, y=None) == INVALID
     assert _lf(lib, qb=48) == SHAPE             # does not divide 128
@@ -91,6 +97,15 @@ def test_standalone_calls_validation(lib):
     assert lib.larosa_rotate(P, 9, P, 64, 1, P, 1, 128, None) == DTYPE
     assert lib.larosa_rotate(None, 1, P, 64, 1, P, 1, 128, None) == INVALID
     assert lib.larosa_rotate(P, 1, P, 64, 1, PM, 1, 128, None) == ALIGN
+    assert lib.larosa_rotate_fp64(P, 1, P, 48, 1, P, 1, 128, None) == SHAPE
+    assert lib.larosa_rotate_fp64(P, 1, P, 64, 3, P, 1, 128, None) == DTYPE
+    assert lib.larosa_rotate_fp64(P, 1, None, 64, 1, P, 1, 128, None) == INVALID
+    assert lib.larosa_rotate_fp64(P, 1, P, 64, 1, P, 65, 128, None) == INVALID
+    assert lib.larosa_rotate_fp64(PM, 1, P, 64, 1, P, 1, 128, None) == ALIGN
+    assert lib.larosa_rotate_fp64(P, 1, P, 60, 1, P, 1, 120, None) == ALIGN  # d % 8, bf16
+    assert lib.larosa_rotate_fp64(P, 1, P, 64, 1, P, 0, 128, None) == OK     # empty batch
+    assert lib.larosa_swiglu_layer_forward(P, 1, P, 64, P, 1, 1, 128, 256, 10, P, None, None, 5,
+                                           P, 1 << 24, None) == INVALID
     assert lib.larosa_topk_select(P, 1, 128, 0, P, P, None, None, None, None, None, 0,
                                   None) == INVALID
     assert lib.larosa_topk_select(P, 2, 128, 5, P, P, P, P, None, P, P, 1 << 20,
@@ -131,5 +146,7 @@ def test_no_device_is_reported_not_crashed(lib):
     if torch.cuda.is_available():
         pytest.skip("a GPU is visible")
     assert _lf(lib) == NODEV
+    assert _lf(lib, mode=3) == NODEV
+    assert lib.larosa_rotate_fp64(P, 1, P, 64, 1, P + (1 << 20), 1, 128, None) == NODEV
     assert lib.larosa_swiglu(P, P + (1 << 20), 1, 64, 1, None) == NODEV
     assert lib.larosa_topk_gemv(P, 128, 10, P, 1, P, 1, 64, None, P, 1 << 20, None) == NODEV

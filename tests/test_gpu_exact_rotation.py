@@ -1,0 +1,205 @@
+"""The fp64-accumulating rotation (larosa_rotate_fp64, and the
+LAROSA_ROTATE_FP64 mode flag of the layer calls) against the oracle.
+
+With the fp32 rotation the index sets are checked teacher-forced, because
+two correct fp32 summation orders can swap a near-tie at the K boundary. The
+fp64 rotation removes that freedom. Every product of two bf16 (or two fp32)
+values is exact in fp64, and the sum is rounded to fp32 once. So x_rot must
+equal the oracle's once-rounded x·Q bit for bit. The only allowed exception
+is an element whose exact value lies within the fp64 error bound of an fp32
+rounding midpoint. That exception is certified here and counted; none is
+expected. The index sets are then compared end to end: the GPU's selection
+against the oracle's selection on the oracle's own x_rot.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import larosa_ref as ref
+from rotated_top_activation_amd import _lib
+from rotated_top_activation_amd import workloads as wl
+from rotated_top_activation_amd.device import RotatedLinear
+
+from gpu_helpers import dev, guarded, host, host_f32
+
+pytestmark = pytest.mark.gpu
+
+U64 = 2.0 ** -53
+
+
+def gamma64(n):
+    return n * U64 / (1 - n * U64)
+
+
+def check_correctly_rounded(got: np.ndarray, x, q_blocks):
+    """got (fp32) must be the oracle's fp32(x·Q) except at certified midpoint
+    cases. Returns (oracle x_rot, boolean mask of certified exceptions)."""
+    want = ref.rotate(x, q_blocks)
+    diff = got != want
+    if not diff.any():
+        return want, diff
+    b = q_blocks.shape[1]
+    exact = ref.rotate_exact(x, q_blocks)
+    absum = ref.rotate_exact(np.abs(x), np.abs(q_blocks))
+    g = got[diff].astype(np.float64)
+    w = want[diff].astype(np.float64)
+    # adjacent fp32 values, and the midpoint between them within twice the
+    # fp64 bound of the oracle's product (its error plus the kernel's)
+    assert np.all(np.nextafter(want[diff], got[diff]) == got[diff]), "more than one ulp apart"
+    mid = (g + w) / 2
+    assert np.all(np.abs(mid - exact[diff]) <= 2 * gamma64(b) * absum[diff]), \
+        "differs from the correctly rounded product away from a rounding midpoint"
+    return want, diff
+
+
+ROTATE_CASES = [
+    # (x dtype, Q dtype, d, q_block, B)
+    ("f32", "f32", 512, 512, 1), ("bf16", "bf16", 4096, 4096, 1),
+    ("bf16", "bf16", 4096, 4096, 8), ("bf16", "bf16", 11008, 2752, 3),
+    ("bf16", "bf16", 13824, 3456, 4), ("f32", "bf16", 768, 768, 2),
+    ("bf16", "f32", 256, 64, 5), ("bf16", "bf16", 8192, 8192, 9),
+    ("bf16", "bf16", 1152, 96, 17), ("f32", "f32", 1024, 256, 2),
+    # fp32 rows of 8192: more chunks per lane than one load batch holds
+    ("f32", "f32", 8192, 8192, 1), ("f32", "f32", 8192, 8192, 3),
+]
+
+
+@pytest.mark.parametrize("xdt,qdt,d,qb,B", ROTATE_CASES)
+def test_rotate_fp64_is_the_once_rounded_product(xdt, qdt, d, qb, B):
+    q = wl.rotation(4, 2, "single", d, qb, qdt)
+    x = wl.heavy_tailed_activations(4, 2, "single", B, d, xdt)
+    q_d = dev(q.reshape(d, qb), qdt)
+    qt = torch.empty_like(q_d)
+    _lib.larosa_prepare_rotation(q_d, qt, d, qb)
+    xr, ok = guarded((B, d), torch.float32)
+    _lib.larosa_rotate_fp64(dev(x, xdt), qt, qb, xr, B, d)
+    torch.cuda.synchronize()
+    assert ok()
+    _, certified = check_correctly_rounded(host_f32(xr), x, q)
+    assert certified.sum() <= 2
+
+
+def test_rotate_fp64_exact_for_signed_permutation_and_identity():
+    rng = np.random.default_rng(5)
+    d = 1024
+    x = wl.quantize(rng.standard_normal((3, d)), "bf16")
+    perm, sign = wl.signed_permutation(rng, d)
+    p = np.zeros((d, d))
+    p[np.arange(d), perm] = sign
+    for q in (p, np.eye(d)):
+        q_d = dev(q, "bf16")
+        qt = torch.empty_like(q_d)
+        _lib.larosa_prepare_rotation(q_d, qt, d, d)
+        xr = torch.empty((3, d), device="cuda")
+        _lib.larosa_rotate_fp64(dev(x, "bf16"), qt, d, xr, 3, d)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host_f32(xr), ref.rotate(x, q[None]))
+
+
+def _end_to_end(lin, x, q, mode, tol):
+    B = x.shape[0]
+    tdt = torch.float32 if lin.dtype == "f32" else torch.bfloat16
+    y, ok_y = guarded((B, lin.d_out), tdt)
+    idx, ok_i = guarded((B, lin.k), torch.int32, fill=-3)
+    xr, ok_x = guarded((B, lin.d_in), torch.float32)
+    ws = lin.workspace(B, mode)
+    lin.forward(dev(x, lin.dtype), y, ws, idx_out=idx, xrot_out=xr, mode=mode)
+    torch.cuda.synchronize()
+    assert ok_y() and ok_i() and ok_x()
+    want_xr, certified = check_correctly_rounded(host_f32(xr), x, q)
+    got_idx = host(idx)
+    # teacher-forced: always exact
+    np.testing.assert_array_equal(got_idx, ref.select(host_f32(xr), lin.k))
+    # end to end: the oracle's own sets, for every token whose x_rot matched
+    own = ref.select(want_xr, lin.k)
+    rows = ~certified.any(axis=1)
+    np.testing.assert_array_equal(got_idx[rows], own[rows])
+    want_y = ref.round_to(ref.gather_product(want_xr, own, host(lin.Wf)), lin.dtype)
+    err = ref.rel_error(host(y), want_y)
+    assert err <= tol, err
+    return y
+
+
+LAYER_CASES = [
+    # (d_in, q_block, d_out, B, sparsity %)
+    (4096, 4096, 1032, 1, 40), (4096, 4096, 1032, 4, 40), (4096, 4096, 1032, 8, 25),
+    (11008, 2752, 520, 1, 40), (11008, 2752, 520, 3, 50), (2048, 512, 4104, 2, 40),
+]
+
+
+@pytest.mark.parametrize("d,qb,n,B,sp", LAYER_CASES)
+def test_layer_forward_fp64_rotation_index_sets_end_to_end(d, qb, n, B, sp):
+    case = wl.LinearCase(cfg=3, batch=B, d_in=d, d_out=n, q_block=qb, sparsity_pct=sp,
+                         dtype="bf16", role="down_in")
+    x, q, w = wl.linear_case_inputs(case, w_std=0.02)
+    lin = RotatedLinear(q, w, "bf16", case.k)
+    y = _end_to_end(lin, x, q, _lib.UNFUSED | _lib.ROTATE_FP64, 2e-2)
+    if B == 1:
+        # with the flag the fused mode runs the same unfused steps
+        y2 = _end_to_end(lin, x, q, _lib.FUSED | _lib.ROTATE_FP64, 2e-2)
+        assert torch.equal(y, y2)
+
+
+def test_layer_forward_fp64_rotation_f32_single_linear():
+    case, x, q, w = wl.single_linear_f32()
+    lin = RotatedLinear(q, w, "f32", case.k)
+    _end_to_end(lin, x, q, _lib.UNFUSED | _lib.ROTATE_FP64, 1e-5)
+
+
+@pytest.mark.parametrize("B", [1, 4])
+def test_swiglu_layer_fp64_rotation_index_sets_end_to_end(B):
+    d, f, sp = 4096, 2816, 40
+    case = wl.LinearCase(cfg=2, batch=B, d_in=d, d_out=2 * f, q_block=d, sparsity_pct=sp,
+                         dtype="bf16", role="mlp_in")
+    x, q, w = wl.linear_case_inputs(case, w_std=0.02)
+    lin = RotatedLinear(q, w, "bf16", case.k)
+    w_il = torch.empty_like(lin.Wf)
+    _lib.larosa_interleave_gate_up(lin.Wf, w_il, d, f)
+    mode = _lib.UNFUSED | _lib.ROTATE_FP64
+    ws = torch.zeros(_lib.larosa_swiglu_workspace_bytes(B, d, f, case.k, mode),
+                     dtype=torch.uint8, device="cuda")
+    h, ok_h = guarded((B, f), torch.bfloat16)
+    idx = torch.empty((B, case.k), dtype=torch.int32, device="cuda")
+    xr = torch.empty((B, d), dtype=torch.float32, device="cuda")
+    _lib.larosa_swiglu_layer_forward(dev(x, "bf16"), lin.Qt, d, w_il, B, d, f, case.k, h,
+                                     idx_out=idx, xrot_out=xr, mode=mode, ws=ws)
+    torch.cuda.synchronize()
+    assert ok_h()
+    want_xr, certified = check_correctly_rounded(host_f32(xr), x, q)
+    assert not certified.any()
+    own = ref.select(want_xr, case.k)
+    np.testing.assert_array_equal(host(idx), own)
+    g_u = ref.round_to(ref.gather_product(want_xr, own, host(lin.Wf)), "bf16")
+    assert ref.rel_error(host(h), ref.swiglu(g_u, f, "bf16")) <= 2e-2
+
+
+def test_fp64_rotation_removes_boundary_swaps_over_many_tokens():
+    """Over 1024 tokens at d = 4096, s = .4, the Top-K sets taken from the fp64
+    rotation equal the oracle's own sets for every token. The fp32 rotation
+    may differ on a few tokens (legitimate near-ties). That count is printed,
+    not gated."""
+    d, k, B, reps = 4096, wl.k_for(4096, 40), 64, 16
+    q = wl.rotation(3, 7, "mlp_in", d, d, "bf16")
+    q_d = dev(q.reshape(d, d), "bf16")
+    qt = torch.empty_like(q_d)
+    _lib.larosa_prepare_rotation(q_d, qt, d, d)
+    xr = torch.empty((B, d), dtype=torch.float32, device="cuda")
+    idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    val = torch.empty((B, k), dtype=torch.float32, device="cuda")
+    diff32 = diff64 = 0
+    for r in range(reps):
+        x = wl.heavy_tailed_activations(3, 7, "mlp_in", B, d, "bf16", run_seed=r)
+        own = ref.select(ref.rotate(x, q), k)
+        x_d = dev(x, "bf16")
+        for fn in (_lib.larosa_rotate, _lib.larosa_rotate_fp64):
+            fn(x_d, qt, d, xr, B, d)
+            _lib.larosa_topk_select(xr, B, d, k, idx, val)
+            torch.cuda.synchronize()
+            n = int((host(idx) != own).any(axis=1).sum())
+            if fn is _lib.larosa_rotate:
+                diff32 += n
+            else:
+                diff64 += n
+    print(f"tokens whose sets differ from the exact rotation's: fp32 {diff32}, "
+          f"fp64 {diff64} of {B * reps}")
+    assert diff64 == 0
