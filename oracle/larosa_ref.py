@@ -19,6 +19,13 @@ Sources:
               K entries of largest magnitude and sets the rest to zero.
   [design]    same page, 方法详解 · 关键设计 (key design): the rotation may be
               random or learned; the Top-K ratio sets the sparsity.
+  [rsparse]   the R-Sparse summary page (R-Sparse: Rank-Aware Activation
+              Sparsity, 研究流程与方法 · R-Sparse框架设计 (framework design)):
+              input channels whose magnitude is below a threshold t(s) set by
+              a sparsity budget s are masked; the masked remainder goes
+              through a rank-r factorisation A_r·B_r of the weight taken from
+              its SVD (A_r = U_r·Σ_r^½, B_r = Σ_r^½·V_rᵀ); the output is the
+              sparse part plus that low-rank part.
 
 Readings where the pages are silent (each is listed with its reason in the
 design notes of the repository):
@@ -225,6 +232,71 @@ def mlp(x, q1, w_gu_folded, q2, w_down_folded, k1: int, k2: int, f: int,
     h = swiglu(gu, f, act_dtype)
     y, xr2, idx2 = linear(h, q2, w_down_folded, k2, act_dtype)
     return y, dict(gu=gu, h=h, x_rot1=xr1, idx1=idx1, x_rot2=xr2, idx2=idx2)
+
+
+# ----------------------------------------------------------------------------
+# Variants next to the method's fixed Top-K (the contrast the pages draw).
+
+
+def threshold_key(t) -> np.uint32:
+    """The key a magnitude threshold t is compared with: fp32(t)'s bit
+    pattern. t must be a non-negative number (−0 counts as 0)."""
+    t32 = np.float32(t)
+    if np.isnan(t32) or t32 < 0:
+        raise ValueError(f"threshold {t!r} must be a non-negative number")
+    return np.uint32(np.array(t32).view(np.uint32) & np.uint32(0x7FFFFFFF))
+
+
+def calibrate_threshold(x_rot_calib: np.ndarray, sparsity_pct: int) -> np.float32:
+    """t(s) [rsparse] from calibration activations: the K_total-th largest
+    magnitude over all n entries, K_total = ⌊n·(100 − p)/100⌋ (the same floor
+    rule as K). Keeping |x| ≥ t keeps K_total of the calibration entries, or
+    more when the K_total-th magnitude is tied. Returned as the fp32 value."""
+    key = magnitude_key(np.asarray(x_rot_calib, dtype=np.float32).reshape(-1))
+    n = key.size
+    k_total = n * (100 - int(sparsity_pct)) // 100
+    if not 1 <= k_total <= n:
+        raise ValueError(f"sparsity {sparsity_pct}% keeps {k_total} of {n} entries")
+    kth = np.sort(key)[::-1][k_total - 1]
+    return np.array(kth, dtype=np.uint32).view(np.float32)[()]
+
+
+def threshold_select_row(x_rot_row: np.ndarray, t) -> np.ndarray:
+    """Magnitude-threshold selection [rsparse]: the indices i with
+    |x_rot[i]| ≥ t, ascending. How many are kept varies from token to token
+    (the fluctuating sparsity [abstract] attributes to magnitude pruning)."""
+    key = magnitude_key(x_rot_row)
+    return np.nonzero(key >= threshold_key(t))[0].astype(np.int32)
+
+
+def threshold_select(x_rot: np.ndarray, t) -> list:
+    """Per-token threshold selections (a list of ascending index arrays)."""
+    x_rot = np.asarray(x_rot, dtype=np.float32)
+    return [threshold_select_row(x_rot[b], t) for b in range(x_rot.shape[0])]
+
+
+def lowrank_factors(w_folded: np.ndarray, r: int):
+    """A_r = U_r·Σ_r^½ [d_in, r] and B_r = Σ_r^½·V_rᵀ [r, d_out] from the SVD
+    W' = U·Σ·Vᵀ [rsparse], so that A_r·B_r is the best rank-r approximation
+    of W' (in the x·W orientation used here)."""
+    w = np.asarray(w_folded, dtype=np.float64)
+    if not 0 <= r <= min(w.shape):
+        raise ValueError(f"rank {r} outside [0, {min(w.shape)}]")
+    u, sv, vt = np.linalg.svd(w, full_matrices=False)
+    root = np.sqrt(sv[:r])
+    return u[:, :r] * root[None, :], root[:, None] * vt[:r]
+
+
+def lowrank_compensated_product(x_rot: np.ndarray, idx, w_folded: np.ndarray,
+                                a_r: np.ndarray, b_r: np.ndarray) -> np.ndarray:
+    """y = xs·W' + (x_rot − xs)·(A_r·B_r) in float64 [rsparse]: the sparse
+    product over the kept rows, plus the dropped remainder of the rotated
+    input through the low-rank factors (first (x_rot − xs)·A_r, then ·B_r)."""
+    xs = sparsify(x_rot, idx)
+    dropped = np.asarray(x_rot, dtype=np.float32).astype(np.float64) - xs
+    y_s = gather_product(x_rot, idx, w_folded)
+    y_r = (dropped @ np.asarray(a_r, dtype=np.float64)) @ np.asarray(b_r, dtype=np.float64)
+    return y_s + y_r
 
 
 def rel_error(y_hat, y) -> float:

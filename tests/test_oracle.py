@@ -329,3 +329,153 @@ def test_pins_catch_planted_mistakes():
     # a sign slip in SiLU
     ln3 = math.log(3.0)
     assert abs(ln3 / (1 + math.exp(ln3)) - 0.75 * ln3) > 0.1
+
+
+# ------------------------------------------------- threshold and low rank ----
+
+def test_threshold_worked_example():
+    g = _load("threshold_lowrank_example.json")
+    x = _f32(g["threshold"]["x_rot"])
+    for t, kept in g["threshold"]["kept"].items():
+        assert list(ref.threshold_select_row(x, float(t))) == kept, t
+    c = g["calibration"]
+    xc = np.array(c["x_rot"], dtype=np.float32)
+    for p, t in c["t"].items():
+        assert ref.calibrate_threshold(xc, int(p)) == np.float32(t), p
+    sel = ref.threshold_select(xc, ref.calibrate_threshold(xc, 50))
+    assert [list(s) for s in sel] == c["kept_at_p50"]
+
+
+def test_calibrated_threshold_brute_force_and_top_k_agreement():
+    rng = np.random.default_rng(11)
+    for trial in range(40):
+        n_tok, d = int(rng.integers(1, 4)), int(rng.integers(1, 40))
+        # small integers: many ties
+        xc = rng.integers(-4, 5, (n_tok, d)).astype(np.float32)
+        for p in (0, 10, 40, 50, 90):
+            n = n_tok * d
+            k_total = n * (100 - p) // 100
+            if k_total < 1:
+                with pytest.raises(ValueError):
+                    ref.calibrate_threshold(xc, p)
+                continue
+            t = ref.calibrate_threshold(xc, p)
+            mags = np.abs(xc.astype(np.float64)).reshape(-1)
+            # characterisation: fewer than K_total entries are above t, and
+            # at least K_total are at or above it; t is one of the magnitudes
+            assert (mags > t).sum() < k_total <= (mags >= t).sum()
+            assert t in mags
+            kept = sum(len(s) for s in ref.threshold_select(xc, t))
+            assert kept == (mags >= t).sum()
+            if n_tok == 1:
+                # one calibration token: the threshold keeps the Top-K set,
+                # plus every channel tied with the K-th magnitude
+                topk = set(ref.select_row(xc[0], k_total).tolist())
+                thr = set(ref.threshold_select_row(xc[0], t).tolist())
+                assert topk <= thr
+                assert all(abs(xc[0, i]) == t for i in thr - topk)
+    # without ties the two selections coincide
+    x = rng.standard_normal(4096).astype(np.float32)
+    t = ref.calibrate_threshold(x[None], 40)
+    np.testing.assert_array_equal(ref.threshold_select_row(x, t), ref.select_row(x, 2457))
+
+
+def test_threshold_special_cases():
+    x = np.array([0.0, -0.0, 1.0, -np.inf, np.inf, 3.0], dtype=np.float32)
+    assert list(ref.threshold_select_row(x, 0.0)) == [0, 1, 2, 3, 4, 5]
+    assert list(ref.threshold_select_row(x, -0.0)) == [0, 1, 2, 3, 4, 5]
+    assert list(ref.threshold_select_row(x, np.inf)) == [3, 4]
+    assert list(ref.threshold_select_row(x, 3.0)) == [3, 4, 5]
+    assert list(ref.threshold_select_row(x[:3], 2.0)) == []
+    for bad in (-1.0, np.nan):
+        with pytest.raises(ValueError):
+            ref.threshold_select_row(x, bad)
+    # a larger threshold keeps a subset
+    rng = np.random.default_rng(2)
+    y = rng.standard_normal(500).astype(np.float32)
+    a = set(ref.threshold_select_row(y, 0.5).tolist())
+    b = set(ref.threshold_select_row(y, 0.8).tolist())
+    assert b <= a and len(a) > len(b)
+
+
+def test_lowrank_worked_example():
+    g = _load("threshold_lowrank_example.json")["lowrank"]
+    w = np.array(g["W_folded"])
+    a1, b1 = ref.lowrank_factors(w, 1)
+    np.testing.assert_allclose(a1 @ b1, g["rank1_product"], atol=1e-15)
+    xr = _f32(g["x_rot"])[None]
+    for r, y in g["y"].items():
+        a, b = ref.lowrank_factors(w, int(r))
+        got = ref.lowrank_compensated_product(xr, [np.array(g["kept"])], w, a, b)
+        np.testing.assert_allclose(got[0], y, atol=1e-14)
+
+
+def test_lowrank_factors_closed_forms():
+    rng = np.random.default_rng(4)
+    w = rng.standard_normal((48, 30))
+    sv = np.linalg.svd(w, compute_uv=False)
+    for r in (0, 1, 7, 30):
+        a, b = ref.lowrank_factors(w, r)
+        assert a.shape == (48, r) and b.shape == (r, 30)
+        # Eckart–Young: the residual's energy is the dropped singular values'
+        res = np.sum((w - a @ b) ** 2)
+        assert abs(res - np.sum(sv[r:] ** 2)) <= 1e-10 * np.sum(sv ** 2)
+        # balanced factors: AᵀA = B·Bᵀ = Σ_r
+        np.testing.assert_allclose(a.T @ a, np.diag(sv[:r]), atol=1e-10)
+        np.testing.assert_allclose(b @ b.T, np.diag(sv[:r]), atol=1e-10)
+    with pytest.raises(ValueError):
+        ref.lowrank_factors(w, 31)
+
+
+def test_lowrank_compensation_limits():
+    rng = np.random.default_rng(8)
+    d, n, k = 64, 40, 25
+    w = rng.standard_normal((d, n))
+    xr = rng.standard_normal((3, d)).astype(np.float32)
+    idx = ref.select(xr, k)
+    plain = ref.gather_product(xr, idx, w)
+    dense = xr.astype(np.float64) @ w
+    a0, b0 = ref.lowrank_factors(w, 0)
+    np.testing.assert_array_equal(ref.lowrank_compensated_product(xr, idx, w, a0, b0), plain)
+    af, bf = ref.lowrank_factors(w, n)  # full rank: the dense product
+    np.testing.assert_allclose(ref.lowrank_compensated_product(xr, idx, w, af, bf), dense,
+                               rtol=1e-12, atol=1e-12)
+    # nothing dropped (K = d): the compensation adds exactly zero
+    all_idx = ref.select(xr, d)
+    a5, b5 = ref.lowrank_factors(w, 5)
+    np.testing.assert_array_equal(ref.lowrank_compensated_product(xr, all_idx, w, a5, b5),
+                                  ref.gather_product(xr, all_idx, w))
+    # an exactly rank-5 weight is recovered by rank 5 for any selection
+    w5 = rng.standard_normal((d, 5)) @ rng.standard_normal((5, n))
+    a, b = ref.lowrank_factors(w5, 5)
+    np.testing.assert_allclose(ref.lowrank_compensated_product(xr, idx, w5, a, b),
+                               xr.astype(np.float64) @ w5, rtol=1e-10, atol=1e-10)
+    # the error shrinks as the rank grows
+    errs = [np.abs(ref.lowrank_compensated_product(xr, idx, w, *ref.lowrank_factors(w, r))
+                   - dense).max() for r in (0, 10, 20, 40)]
+    assert errs[0] > errs[1] > errs[2] > errs[3]
+
+
+def test_threshold_and_lowrank_pins_catch_planted_mistakes():
+    g = _load("threshold_lowrank_example.json")
+    x = _f32(g["threshold"]["x_rot"])
+    # strict > instead of >= drops the channels equal to t
+    key = ref.magnitude_key(x)
+    tk = ref.threshold_key(1.0)
+    assert list(np.nonzero(key > tk)[0]) != g["threshold"]["kept"]["1.0"]
+    # calibration taking the K_total-th smallest instead of largest
+    xc = np.array(g["calibration"]["x_rot"], dtype=np.float32)
+    mk = np.sort(ref.magnitude_key(xc.reshape(-1)))
+    wrong = np.array(mk[2 - 1], dtype=np.uint32).view(np.float32)  # p = 75: K_total = 2
+    assert wrong != np.float32(g["calibration"]["t"]["75"])
+    # compensating the kept part instead of the dropped one
+    lr = g["lowrank"]
+    w = np.array(lr["W_folded"])
+    a, b = ref.lowrank_factors(w, 1)
+    xr = _f32(lr["x_rot"])[None]
+    xs = ref.sparsify(xr, [np.array(lr["kept"])])
+    bad = ref.gather_product(xr, [np.array(lr["kept"])], w) + (xs @ a) @ b
+    assert not np.allclose(bad[0], lr["y"]["1"])
+    # B_r taken without the Σ^½ weight (U_r·V_rᵀ)
+    u, sv, vt = np.linalg.svd(w)
+    assert not np.allclose(u[:, :1] @ vt[:1], lr["rank1_product"])
