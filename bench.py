@@ -284,6 +284,8 @@ def main():
     exact_rot["step_ms_unfused_fp64_rotation"] = round(
         timed(lambda i: step(i, _lib.UNFUSED | _lib.ROTATE_FP64), a.steps, a.warmup), 5)
 
+    thr = threshold_mlp(a, case, x_d, l1, l2, qt1, wil1, qt2, wf2, copies, h, y, timed, gbs)
+
     q_bytes = (l1.Qt.numel() + l2.Qt.numel()) * 2
     sparse_bytes = q_bytes + (case.k1 * 2 * f + case.k2 * d) * 2
     dense_mlp_bytes = (d * 2 * f + f * d) * 2
@@ -349,6 +351,7 @@ def main():
             "mlp_achieved_GBs": round(sparse_bytes / (ms * 1e-3) / 1e9, 1),
             "stage_us": {k: round(v * 1e3, 2) for k, v in stage.items()},
             "rotation_fp32_vs_fp64": exact_rot,
+            "threshold_select": thr,
             "kernels": {k: {"achieved_GBs": round(v["achieved"], 1), "bytes_per_launch": v["bytes"],
                             "avg_us": round(v["us"], 3), "frac": round(v["achieved"] / HBM_PEAK_GBS, 4),
                             "traffic": measured_traffic(k)} for k, v in kernels.items()},
@@ -362,6 +365,114 @@ def main():
         },
     }
     print(json.dumps(out), flush=True)
+
+
+def threshold_mlp(a, case, x_d, l1, l2, qt1, wil1, qt2, wf2, copies, h, y, timed, gbs):
+    """The same one-token MLP with the magnitude-threshold selection in place
+    of the Top-K: t1 and t2 are calibrated on the device from 64 synthetic
+    calibration tokens (t2 on the h those tokens produce), then one decode
+    step is timed, and the kept counts of 64 further tokens are reported
+    (the per-token sparsity that a threshold lets fluctuate)."""
+    import torch
+    from rotated_top_activation_amd import _lib, workloads as wl
+    dev = x_d.device
+    d, f, p = case.d, case.f, a.sparsity
+    n_cal = 64
+    cal_ws = torch.empty(_lib.larosa_calibrate_workspace_bytes(), dtype=torch.uint8, device=dev)
+    t_d = torch.empty(2, dtype=torch.float32, device=dev)
+
+    def batch_ws(B, d_in, f_):
+        return torch.zeros(_lib.larosa_swiglu_workspace_bytes(B, d_in, f_, d_in, _lib.UNFUSED),
+                           dtype=torch.uint8, device=dev)
+
+    def down_ws(B):
+        return torch.zeros(_lib.larosa_workspace_bytes(B, f, d, f, _lib.UNFUSED),
+                           dtype=torch.uint8, device=dev)
+
+    def run_batch(xb, t1, t2):
+        B = xb.shape[0]
+        hb = torch.empty((B, f), dtype=torch.bfloat16, device=dev)
+        yb = torch.empty((B, d), dtype=torch.bfloat16, device=dev)
+        c1 = torch.empty(B, dtype=torch.int32, device=dev)
+        c2 = torch.empty(B, dtype=torch.int32, device=dev)
+        _lib.larosa_threshold_swiglu_layer_forward(xb, l1.Qt, l1.q_block, wil1[0], B, d, f, t1,
+                                                   hb, count_out=c1, ws=batch_ws(B, d, f))
+        if t2 is not None:
+            _lib.larosa_threshold_layer_forward(hb, l2.Qt, l2.q_block, wf2[0], B, f, d, t2, yb,
+                                                count_out=c2, ws=down_ws(B))
+        return hb, c1, c2
+
+    # calibration
+    x_cal = wl.to_torch(wl.heavy_tailed_activations(2, 0, "mlp_in", n_cal, d, "bf16",
+                                                    run_seed=17), "bf16")
+    xr_cal = torch.empty((n_cal, d), dtype=torch.float32, device=dev)
+    _lib.larosa_rotate(x_cal, l1.Qt, l1.q_block, xr_cal, n_cal, d)
+    _lib.larosa_calibrate_threshold(xr_cal, n_cal * d, n_cal * d * (100 - p) // 100, t_d[0:1],
+                                    cal_ws)
+    t1 = float(t_d[0].item())
+    h_cal, _, _ = run_batch(x_cal, t1, None)
+    hr_cal = torch.empty((n_cal, f), dtype=torch.float32, device=dev)
+    _lib.larosa_rotate(h_cal, l2.Qt, l2.q_block, hr_cal, n_cal, f)
+    _lib.larosa_calibrate_threshold(hr_cal, n_cal * f, n_cal * f * (100 - p) // 100, t_d[1:2],
+                                    cal_ws)
+    t2 = float(t_d[1].item())
+
+    # one decode step
+    ws1 = batch_ws(1, d, f)
+    ws2 = down_ws(1)
+    cnt = torch.empty(2, dtype=torch.int32, device=dev)
+
+    def step(i, counts=False):
+        c = i % copies
+        _lib.larosa_threshold_swiglu_layer_forward(x_d, qt1[c], l1.q_block, wil1[c], 1, d, f, t1,
+                                                   h, count_out=cnt[0:1] if counts else None,
+                                                   ws=ws1)
+        _lib.larosa_threshold_layer_forward(h, qt2[c], l2.q_block, wf2[c], 1, f, d, t2, y,
+                                            count_out=cnt[1:2] if counts else None, ws=ws2)
+    step(0, counts=True)
+    torch.cuda.synchronize()
+    k1, k2 = (int(v) for v in cnt.tolist())
+    step_ms = timed(step, a.steps, a.warmup)
+    xr1 = torch.empty((1, d), dtype=torch.float32, device=dev)
+    _lib.larosa_rotate(x_d, l1.Qt, l1.q_block, xr1, 1, d)
+    gu = torch.empty((1, 2 * f), dtype=torch.bfloat16, device=dev)
+    ws_g = torch.zeros(_lib.larosa_workspace_bytes(1, d, 2 * f, d, _lib.UNFUSED),
+                       dtype=torch.uint8, device=dev)
+    # the folded selection + product alone (gate|up, without SwiGLU): the
+    # threshold form of the Top-K kernel timed in stage_us["select_gather1"]
+    sg_ms = timed(lambda i: _lib.larosa_threshold_layer_forward(
+        x_d, qt1[i % copies], l1.q_block, wil1[i % copies], 1, d, 2 * f, t1, gu, ws=ws_g),
+        a.steps, a.warmup)
+    rot_ms = timed(lambda i: _lib.larosa_rotate(x_d, qt1[i % copies], l1.q_block, xr1, 1, d),
+                   a.steps, a.warmup)
+    sg_only_ms = max(sg_ms - rot_ms, 1e-6)
+    sg_bytes = k1 * 2 * f * 2 + d * 4 + 2 * f * 2
+
+    # kept counts of 64 more tokens
+    x_test = wl.to_torch(wl.heavy_tailed_activations(2, 0, "mlp_in", 64, d, "bf16",
+                                                     run_seed=18), "bf16")
+    _, c1, c2 = run_batch(x_test, t1, t2)
+    c1 = c1.cpu().numpy()
+    c2 = c2.cpu().numpy()
+    q_bytes = (l1.Qt.numel() + l2.Qt.numel()) * 2
+    step_bytes = q_bytes + (k1 * 2 * f + k2 * d) * 2
+    return {
+        "calibration": f"t = the floor(n*(100-p)/100)-th largest |x_rot| over {n_cal} synthetic "
+                       f"tokens (n = {n_cal}*d), on the device; t2 on those tokens' h",
+        "t1": t1, "t2": t2,
+        "step_ms": round(step_ms, 5),
+        "step_tokens_per_s": round(1.0 / (step_ms * 1e-3), 2),
+        "step_kept": {"gate_up_in": k1, "down_in": k2},
+        "step_GBs": round(gbs(step_bytes, step_ms), 1),
+        "gate_up_select_gather_us_layer_minus_rotation": round(sg_only_ms * 1e3, 2),
+        "gate_up_select_gather_GBs": round(gbs(sg_bytes, sg_only_ms), 1),
+        "kept_64_tokens": {
+            "gate_up_in": {"min": int(c1.min()), "mean": round(float(c1.mean()), 1),
+                           "max": int(c1.max()), "top_k": case.k1},
+            "down_in": {"min": int(c2.min()), "mean": round(float(c2.mean()), 1),
+                        "max": int(c2.max()), "top_k": case.k2},
+        },
+    }
 
 
 # ---------------------------------------------------------------- other workloads --

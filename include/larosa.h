@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define LAROSA_ABI_VERSION 3
+#define LAROSA_ABI_VERSION 4
 
 typedef void *larosa_stream_t; /* hipStream_t */
 
@@ -254,6 +254,66 @@ int larosa_swiglu_layer_forward(const void *x, int act_dtype, const void *Qt, in
                                 int64_t f, int64_t k, void *h, int32_t *idx_out,
                                 float *xrot_out, int mode, void *ws, size_t ws_bytes,
                                 larosa_stream_t stream);
+
+/* ---- Magnitude-threshold selection (the contrast to the fixed Top-K) ----
+ * The R-Sparse summary page (研究流程与方法 · R-Sparse框架设计) masks every
+ * input channel whose magnitude is below a threshold t(s) chosen for a
+ * sparsity budget s; the LaRoSA abstract names such magnitude pruning as the
+ * source of fluctuating sparsity that its fixed K avoids. These calls run
+ * that selection on the rotated activation: channel i of a token is kept iff
+ * |x_rot[i]| >= t, compared on the same keys as the Top-K (fp32 bits with the
+ * sign cleared, so −0 equals +0 and ±inf rank highest). The number kept
+ * varies per token and is written to device memory. t must be a
+ * non-negative number (LAROSA_ERR_INVALID_ARG for negative or NaN). */
+
+/* Workspace bytes of larosa_calibrate_threshold (a few KB). */
+size_t larosa_calibrate_workspace_bytes(void);
+
+/* *t_out (device fp32) = the keep-th largest magnitude |x_rot[i]| over the
+ * n entries x_rot[0 .. n) (e.g. the rotated activations of N calibration
+ * tokens, n = N·d). Keeping |x| >= t then keeps keep of those entries, or
+ * more when the keep-th magnitude is tied. For a sparsity of p percent use
+ * keep = floor(n·(100 − p)/100). Exact radix select on the keys
+ * (deterministic). 1 <= keep <= n < 2^31; ws: at least
+ * larosa_calibrate_workspace_bytes() bytes, 16-byte aligned, overwritten.
+ * Offline: not on the decode path. */
+int larosa_calibrate_threshold(const float *x_rot, int64_t n, int64_t keep, float *t_out,
+                               void *ws, size_t ws_bytes, larosa_stream_t stream);
+
+/* Per-token threshold selection: for each token b the indices i with
+ * |x_rot[b, i]| >= t, ascending, in idx[b·d .. b·d + count[b]) (rows of
+ * capacity d; entries past count[b] are not written), their values in val
+ * (same layout; may be NULL), count [B] (device), and xs [B, d] (the kept
+ * values, zero elsewhere; may be NULL). The union outputs, workspace and
+ * errors are as for larosa_topk_select. */
+int larosa_threshold_select(const float *x_rot, int64_t B, int64_t d, float t, int32_t *idx,
+                            int32_t *count, float *val, float *xs, int32_t *union_idx,
+                            int32_t *union_count, float *union_coef, void *ws, size_t ws_bytes,
+                            larosa_stream_t stream);
+
+/* larosa_layer_forward with the threshold selection in place of the Top-K:
+ * rotate, keep |x_rot| >= t per token, (row union for B > 1), product over
+ * the kept rows of W_folded. idx_out ([B, d_in], rows of capacity d_in),
+ * count_out ([B] kept channels per token) and xrot_out may be NULL. mode:
+ * LAROSA_UNFUSED, optionally with LAROSA_ROTATE_FP64 (LAROSA_FUSED runs the
+ * same unfused steps). For one token the selection and the product are one
+ * launch after the rotation. ws: larosa_workspace_bytes(B, d_in, d_out,
+ * d_in, mode) bytes, zero-filled once. Other arguments and errors as
+ * larosa_layer_forward. */
+int larosa_threshold_layer_forward(const void *x, int act_dtype, const void *Qt,
+                                   int64_t q_block, const void *W_folded, int w_dtype, int64_t B,
+                                   int64_t d_in, int64_t d_out, float t, void *y,
+                                   int32_t *idx_out, int32_t *count_out, float *xrot_out,
+                                   int mode, void *ws, size_t ws_bytes, larosa_stream_t stream);
+
+/* larosa_swiglu_layer_forward with the threshold selection (see above);
+ * ws: larosa_swiglu_workspace_bytes(B, d_in, f, d_in, mode) bytes. */
+int larosa_threshold_swiglu_layer_forward(const void *x, int act_dtype, const void *Qt,
+                                          int64_t q_block, const void *W_il, int w_dtype,
+                                          int64_t B, int64_t d_in, int64_t f, float t, void *h,
+                                          int32_t *idx_out, int32_t *count_out, float *xrot_out,
+                                          int mode, void *ws, size_t ws_bytes,
+                                          larosa_stream_t stream);
 
 /* ---- The decoder layer around the rotated linears ----------------------
  * The pages apply the rotated Top-K sparsification to every linear layer of a

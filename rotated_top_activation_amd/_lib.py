@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblarosa.s
 F32, BF16 = 0, 1
 UNFUSED, FUSED = 0, 1
 ROTATE_FP64 = 2  # mode flag: fp64-accumulating rotation, OR-ed into UNFUSED or FUSED
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 _c_i64 = ctypes.c_int64
 _c_int = ctypes.c_int
@@ -55,6 +55,19 @@ SIGNATURES = {
     "larosa_swiglu_layer_forward": (_c_int, [_c_vp, _c_int, _c_vp, _c_i64, _c_vp, _c_int, _c_i64,
                                              _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_int,
                                              _c_vp, _c_sz, _c_vp]),
+    "larosa_calibrate_workspace_bytes": (_c_sz, []),
+    "larosa_calibrate_threshold": (_c_int, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_sz, _c_vp]),
+    "larosa_threshold_select": (_c_int, [_c_vp, _c_i64, _c_i64, ctypes.c_float, _c_vp, _c_vp,
+                                         _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz,
+                                         _c_vp]),
+    "larosa_threshold_layer_forward": (_c_int, [_c_vp, _c_int, _c_vp, _c_i64, _c_vp, _c_int,
+                                                _c_i64, _c_i64, _c_i64, ctypes.c_float, _c_vp,
+                                                _c_vp, _c_vp, _c_vp, _c_int, _c_vp, _c_sz,
+                                                _c_vp]),
+    "larosa_threshold_swiglu_layer_forward": (_c_int, [_c_vp, _c_int, _c_vp, _c_i64, _c_vp,
+                                                       _c_int, _c_i64, _c_i64, _c_i64,
+                                                       ctypes.c_float, _c_vp, _c_vp, _c_vp,
+                                                       _c_vp, _c_int, _c_vp, _c_sz, _c_vp]),
     "larosa_rmsnorm": (_c_int, [_c_vp, _c_vp, _c_i64, _c_i64, ctypes.c_float, _c_int, _c_vp]),
     "larosa_rope": (_c_int, [_c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                              ctypes.c_float, _c_int, _c_vp]),
@@ -224,6 +237,49 @@ def larosa_swiglu_layer_forward(x, Qt, q_block: int, W_il, B: int, d_in: int, f:
                                               _dt(W_il), B, d_in, f, k, _ptr(h), _ptr(idx_out),
                                               _ptr(xrot_out), mode, _ptr(ws), _nbytes(ws),
                                               _stream(stream)))
+
+
+def larosa_calibrate_workspace_bytes() -> int:
+    return int(load().larosa_calibrate_workspace_bytes())
+
+
+def larosa_calibrate_threshold(x_rot, n: int, keep: int, t_out, ws, stream=None) -> None:
+    _check("larosa_calibrate_threshold",
+           load().larosa_calibrate_threshold(_ptr(x_rot), n, keep, _ptr(t_out), _ptr(ws),
+                                             _nbytes(ws), _stream(stream)))
+
+
+def larosa_threshold_select(x_rot, B: int, d: int, t: float, idx, count, val=None, xs=None,
+                            union_idx=None, union_count=None, union_coef=None, ws=None,
+                            stream=None) -> None:
+    _check("larosa_threshold_select",
+           load().larosa_threshold_select(_ptr(x_rot), B, d, t, _ptr(idx), _ptr(count), _ptr(val),
+                                          _ptr(xs), _ptr(union_idx), _ptr(union_count),
+                                          _ptr(union_coef), _ptr(ws), _nbytes(ws),
+                                          _stream(stream)))
+
+
+def larosa_threshold_layer_forward(x, Qt, q_block: int, W_folded, B: int, d_in: int, d_out: int,
+                                   t: float, y, idx_out=None, count_out=None, xrot_out=None,
+                                   mode: int = UNFUSED, ws=None, stream=None) -> None:
+    _check("larosa_threshold_layer_forward",
+           load().larosa_threshold_layer_forward(_ptr(x), _dt(x), _ptr(Qt), q_block,
+                                                 _ptr(W_folded), _dt(W_folded), B, d_in, d_out, t,
+                                                 _ptr(y), _ptr(idx_out), _ptr(count_out),
+                                                 _ptr(xrot_out), mode, _ptr(ws), _nbytes(ws),
+                                                 _stream(stream)))
+
+
+def larosa_threshold_swiglu_layer_forward(x, Qt, q_block: int, W_il, B: int, d_in: int, f: int,
+                                          t: float, h, idx_out=None, count_out=None,
+                                          xrot_out=None, mode: int = UNFUSED, ws=None,
+                                          stream=None) -> None:
+    _check("larosa_threshold_swiglu_layer_forward",
+           load().larosa_threshold_swiglu_layer_forward(_ptr(x), _dt(x), _ptr(Qt), q_block,
+                                                        _ptr(W_il), _dt(W_il), B, d_in, f, t,
+                                                        _ptr(h), _ptr(idx_out), _ptr(count_out),
+                                                        _ptr(xrot_out), mode, _ptr(ws),
+                                                        _nbytes(ws), _stream(stream)))
 
 
 def larosa_rmsnorm(h, out, B: int, d: int, eps: float = 1e-5, stream=None) -> None:

@@ -140,6 +140,227 @@ bool fp64_rotation(int mode) { return (mode & LAROSA_ROTATE_FP64) != 0; }
 
 }  // namespace
 
+namespace {
+
+// What the selection step keeps: each token's Top-k, or (thr) every
+// channel whose magnitude is at least a threshold, with room for d_in per
+// token and the number kept written to count_out when it is not NULL.
+struct Sel {
+  bool thr = false;
+  int64_t k = 0;
+  uint32_t thr_key = 0;
+  int32_t *count_out = nullptr;
+};
+
+int layer_entry(const void *x, int act_dtype, const void *Qt, int64_t q_block,
+                const void *W_folded, int w_dtype, int64_t B, int64_t d_in, int64_t d_out,
+                const Sel &sel, void *y, int32_t *idx_out, float *xrot_out, int mode, void *ws,
+                size_t ws_bytes, larosa_stream_t stream) {
+  const int64_t k = sel.k;
+  if (!dtype_ok(act_dtype) || !dtype_ok(w_dtype)) return LAROSA_ERR_DTYPE;
+  if (w_dtype == LAROSA_F32 && act_dtype == LAROSA_BF16) return LAROSA_ERR_DTYPE;
+  if (int st = check_sizes(B, d_in, k)) return st;
+  if (base_mode(mode) < 0) return LAROSA_ERR_INVALID_ARG;
+  if (d_out < 1) return LAROSA_ERR_SHAPE;
+  if (B == 0) return LAROSA_OK;
+  if (!x || !Qt || !W_folded || !y) return LAROSA_ERR_INVALID_ARG;
+  if (int st = check_rotation(d_in, q_block, w_dtype)) return st;
+  if (d_in % vec_of(act_dtype) || d_out % vec_of(w_dtype)) return LAROSA_ERR_ALIGNMENT;
+  if (!aligned16(x) || !aligned16(Qt) || !aligned16(W_folded) || !aligned16(y))
+    return LAROSA_ERR_ALIGNMENT;
+  if ((xrot_out && !aligned16(xrot_out)) || !aligned16(ws)) return LAROSA_ERR_ALIGNMENT;
+  const bool f64 = fp64_rotation(mode);
+  const bool fused = base_mode(mode) == LAROSA_FUSED && !f64 && !sel.thr &&
+                     fused_supported(B, d_in, act_dtype, w_dtype);
+  const Layout L = fused ? layout_with_fused(B, d_in, d_out, k, w_dtype)
+                         : layout_for(B, d_in, d_out, k, w_dtype);
+  if (!ws || ws_bytes < L.total) return LAROSA_ERR_WORKSPACE;
+  if (int st = device_status()) return st;
+
+  hipStream_t s = stream_of(stream);
+  char *base = static_cast<char *>(ws);
+  if (fused) {
+    FusedArgs f;
+    f.x = x;
+    f.qt = Qt;
+    f.wf = W_folded;
+    f.y = y;
+    f.w_dt = w_dtype;
+    f.d_in = static_cast<int>(d_in);
+    f.q_block = static_cast<int>(q_block);
+    f.k = static_cast<int>(k);
+    f.d_out = d_out;
+    f.idx_out = idx_out;
+    f.xrot_out = xrot_out;
+    f.ws = base + L.fused;
+    return launched(launch_fused_linear(f, s));
+  }
+  float *x_rot = xrot_out ? xrot_out : reinterpret_cast<float *>(base + L.x_rot);
+  int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(base + L.idx);
+  float *val = reinterpret_cast<float *>(base + L.val);
+
+  // Batches of 16 to 64 tokens in bf16 run the matrix-core forms of the
+  // rotation and the product, which read Qt and the union rows once for the
+  // whole batch.
+  const bool mf = mfma_supported(B, act_dtype, w_dtype);
+  hipError_t e =
+      f64   ? launch_rotate_f64(x, act_dtype, Qt, w_dtype, x_rot, static_cast<int>(B),
+                                static_cast<int>(d_in), static_cast<int>(q_block), s)
+      : mf && q_block % 32 == 0
+          ? launch_rotate_mfma(x, Qt, x_rot, static_cast<int>(B), static_cast<int>(d_in),
+                               static_cast<int>(q_block), base + L.p.mfma_parts, s)
+          : launch_rotate(x, act_dtype, Qt, w_dtype, x_rot, static_cast<int>(B),
+                          static_cast<int>(d_in), static_cast<int>(q_block), s);
+  if (e != hipSuccess) return LAROSA_ERR_LAUNCH;
+
+  GatherArgs a;
+  a.coef_mode = kCoefPacked;
+  a.w = W_folded;
+  a.w_dt = w_dtype;
+  a.d_in = d_in;
+  a.d_out = d_out;
+  a.y = y;
+  a.y_dt = act_dtype;
+  a.B = static_cast<int>(B);
+  a.ws = base + L.p.gather;
+  if (B == 1 && select_gather_supported(d_in)) {
+    // One token: every workgroup of the product computes the exact Top-K rule
+    // itself, so selection and product are one launch.
+    SelectGatherArgs g;
+    g.x_rot = x_rot;
+    g.d_in = static_cast<int>(d_in);
+    g.k = static_cast<int>(k);
+    g.w = W_folded;
+    g.w_dt = w_dtype;
+    g.d_out = d_out;
+    g.y = y;
+    g.y_dt = act_dtype;
+    g.idx_out = idx_out;
+    g.ws = base + L.p.gather;
+    g.by_threshold = sel.thr;
+    g.thr_key = sel.thr_key;
+    g.count_out = sel.count_out;
+    return launched(launch_select_gather(g, s));
+  }
+  if (B == 1) {
+    if (sel.thr) {
+      int32_t *cnt = sel.count_out ? sel.count_out : reinterpret_cast<int32_t *>(base + L.u_cnt);
+      e = launch_threshold_select(x_rot, 1, static_cast<int>(d_in), sel.thr_key, idx, cnt, val,
+                                  nullptr, nullptr, s);
+      a.n_rows = cnt;
+    } else {
+      e = launch_select(x_rot, 1, static_cast<int>(d_in), static_cast<int>(k), idx, val,
+                        nullptr, nullptr, s);
+      a.n_rows = nullptr;
+    }
+    if (e != hipSuccess) return LAROSA_ERR_LAUNCH;
+    a.rows = idx;
+    a.max_rows = k;
+    a.coef = val;
+  } else {
+    float *xs = reinterpret_cast<float *>(base + L.xs);
+    uint32_t *mask = reinterpret_cast<uint32_t *>(base + L.p.mask);
+    int32_t *u_idx = reinterpret_cast<int32_t *>(base + L.u_idx);
+    int32_t *u_cnt = reinterpret_cast<int32_t *>(base + L.u_cnt);
+    float *u_coef = reinterpret_cast<float *>(base + L.u_coef);
+    e = sel.thr ? launch_threshold_select(x_rot, static_cast<int>(B), static_cast<int>(d_in),
+                                          sel.thr_key, idx, sel.count_out, val, xs, mask, s)
+                : launch_select(x_rot, static_cast<int>(B), static_cast<int>(d_in),
+                                static_cast<int>(k), idx, val, xs, mask, s);
+    if (e == hipSuccess)
+      e = launch_union(mask, xs, static_cast<int>(B), static_cast<int>(d_in), u_idx, u_cnt,
+                       mf ? nullptr : u_coef, s);
+    if (e != hipSuccess) return LAROSA_ERR_LAUNCH;
+    const int64_t bk = B * k;  // the threshold form's k is d_in
+    const int64_t max_rows = bk < d_in ? bk : d_in;
+    if (mf) {
+      const int64_t ldc = mfma_coef_ld(max_rows);
+      void *coefT = base + L.p.mfma_coef;
+      e = launch_union_coef_t(u_idx, u_cnt, xs, static_cast<int>(B), static_cast<int>(d_in), ldc,
+                              coefT, s);
+      if (e == hipSuccess)
+        e = launch_gather_mfma(u_idx, u_cnt, max_rows, d_in, coefT, ldc, W_folded, y,
+                               static_cast<int>(B), d_out, base + L.p.mfma_parts, s);
+      return launched(e);
+    }
+    a.rows = u_idx;
+    a.n_rows = u_cnt;
+    a.max_rows = max_rows;
+    a.coef = u_coef;
+  }
+  return launched(launch_gather(a, s));
+}
+
+int swiglu_entry(const void *x, int act_dtype, const void *Qt, int64_t q_block,
+                 const void *W_il, int w_dtype, int64_t B, int64_t d_in, int64_t f,
+                 const Sel &sel, void *h, int32_t *idx_out, float *xrot_out, int mode, void *ws,
+                 size_t ws_bytes, larosa_stream_t stream) {
+  const int64_t k = sel.k;
+  if (!dtype_ok(act_dtype) || !dtype_ok(w_dtype)) return LAROSA_ERR_DTYPE;
+  if (f < 1 || f % interleave_block(w_dtype)) return LAROSA_ERR_SHAPE;
+  if (base_mode(mode) < 0) return LAROSA_ERR_INVALID_ARG;
+  const size_t need = larosa_swiglu_workspace_bytes(B, d_in, f, k, mode);
+  if (need == 0 && B != 0) {  // invalid sizes: let the layer call name the error
+    return layer_entry(x, act_dtype, Qt, q_block, W_il, w_dtype, B, d_in, 2 * f, sel, h, idx_out,
+                       xrot_out, mode, ws, ws_bytes, stream);
+  }
+  if (B == 0) return LAROSA_OK;
+  if (!h) return LAROSA_ERR_INVALID_ARG;
+  if (!aligned16(h)) return LAROSA_ERR_ALIGNMENT;
+  if (!ws || ws_bytes < need) return LAROSA_ERR_WORKSPACE;
+  const size_t layer_bytes = larosa_workspace_bytes(B, d_in, 2 * f, k, mode);
+  const bool one_launch = (base_mode(mode) == LAROSA_UNFUSED || fp64_rotation(mode)) && B == 1 &&
+                          select_gather_supported(d_in) &&
+                          !(w_dtype == LAROSA_F32 && act_dtype == LAROSA_BF16);
+  if (one_launch) {
+    // rotation, then the selection, product and SiLU(gate)·up in one launch
+    if (int st = check_sizes(B, d_in, k)) return st;
+    if (!x || !Qt || !W_il) return LAROSA_ERR_INVALID_ARG;
+    if (int st = check_rotation(d_in, q_block, w_dtype)) return st;
+    if (d_in % vec_of(act_dtype)) return LAROSA_ERR_ALIGNMENT;
+    if (!aligned16(x) || !aligned16(Qt) || !aligned16(W_il) || !aligned16(ws))
+      return LAROSA_ERR_ALIGNMENT;
+    if (xrot_out && !aligned16(xrot_out)) return LAROSA_ERR_ALIGNMENT;
+    if (int st = device_status()) return st;
+    const Layout L = layout_for(B, d_in, 2 * f, k, w_dtype);
+    char *base = static_cast<char *>(ws);
+    float *x_rot = xrot_out ? xrot_out : reinterpret_cast<float *>(base + L.x_rot);
+    hipStream_t s = stream_of(stream);
+    const hipError_t er =
+        fp64_rotation(mode)
+            ? launch_rotate_f64(x, act_dtype, Qt, w_dtype, x_rot, 1, static_cast<int>(d_in),
+                                static_cast<int>(q_block), s)
+            : launch_rotate(x, act_dtype, Qt, w_dtype, x_rot, 1, static_cast<int>(d_in),
+                            static_cast<int>(q_block), s);
+    if (er != hipSuccess) return LAROSA_ERR_LAUNCH;
+    SelectGatherArgs g;
+    g.x_rot = x_rot;
+    g.d_in = static_cast<int>(d_in);
+    g.k = static_cast<int>(k);
+    g.w = W_il;
+    g.w_dt = w_dtype;
+    g.d_out = 2 * f;
+    g.y = h;
+    g.y_dt = act_dtype;
+    g.idx_out = idx_out;
+    g.ws = base + L.p.gather;
+    g.swiglu = true;
+    g.by_threshold = sel.thr;
+    g.thr_key = sel.thr_key;
+    g.count_out = sel.count_out;
+    return launched(launch_select_gather(g, s));
+  }
+  // otherwise the gate|up rows into the workspace, then SiLU(gate)·up
+  void *gu = static_cast<char *>(ws) + layer_bytes;
+  const int st = layer_entry(x, act_dtype, Qt, q_block, W_il, w_dtype, B, d_in, 2 * f, sel, gu,
+                             idx_out, xrot_out, mode, ws, layer_bytes, stream);
+  if (st != LAROSA_OK) return st;
+  return launched(launch_swiglu_il(gu, h, B, f, interleave_block(w_dtype), act_dtype,
+                                   stream_of(stream)));
+}
+
+}  // namespace
+
 extern "C" {
 
 int larosa_abi_version(void) { return LAROSA_ABI_VERSION; }
@@ -272,6 +493,47 @@ int larosa_topk_select(const float *x_rot, int64_t B, int64_t d, int64_t k, int3
   return launched(e);
 }
 
+int larosa_threshold_select(const float *x_rot, int64_t B, int64_t d, float t, int32_t *idx,
+                            int32_t *count, float *val, float *xs, int32_t *union_idx,
+                            int32_t *union_count, float *union_coef, void *ws, size_t ws_bytes,
+                            larosa_stream_t stream) {
+  if (int st = check_sizes(B, d, 1)) return st;
+  if (!(t >= 0.f)) return LAROSA_ERR_INVALID_ARG;  // negative or NaN
+  if (B == 0) return LAROSA_OK;
+  if (!x_rot || !idx || !count) return LAROSA_ERR_INVALID_ARG;
+  const bool want_union = union_idx != nullptr;
+  if (want_union && (!union_count || !union_coef || !xs)) return LAROSA_ERR_INVALID_ARG;
+  if (!aligned16(x_rot)) return LAROSA_ERR_ALIGNMENT;
+  uint32_t *mask = nullptr;
+  if (want_union) {
+    const size_t need = static_cast<size_t>(B) * mask_words(static_cast<int>(d)) * 4;
+    if (!ws || ws_bytes < need) return LAROSA_ERR_WORKSPACE;
+    mask = static_cast<uint32_t *>(ws);
+  }
+  if (int st = device_status()) return st;
+  hipStream_t s = stream_of(stream);
+  hipError_t e = launch_threshold_select(x_rot, static_cast<int>(B), static_cast<int>(d),
+                                         threshold_key_of(t), idx, count, val, xs, mask, s);
+  if (e == hipSuccess && want_union)
+    e = launch_union(mask, xs, static_cast<int>(B), static_cast<int>(d), union_idx,
+                     union_count, union_coef, s);
+  return launched(e);
+}
+
+size_t larosa_calibrate_workspace_bytes(void) { return calibrate_ws_bytes(); }
+
+int larosa_calibrate_threshold(const float *x_rot, int64_t n, int64_t keep, float *t_out,
+                               void *ws, size_t ws_bytes, larosa_stream_t stream) {
+  if (n < 1 || n > INT32_MAX) return LAROSA_ERR_SHAPE;
+  if (keep < 1 || keep > n) return LAROSA_ERR_INVALID_ARG;
+  if (!x_rot || !t_out) return LAROSA_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < calibrate_ws_bytes()) return LAROSA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return LAROSA_ERR_ALIGNMENT;
+  if (int st = device_status()) return st;
+  return launched(launch_calibrate(x_rot, n, static_cast<uint32_t>(keep), t_out, ws,
+                                   stream_of(stream)));
+}
+
 int larosa_sparse_gemv(const int32_t *rows, const int32_t *n_rows, int64_t max_rows,
                        const float *coef, const void *W_folded, int w_dtype, void *y,
                        int y_dtype, int64_t B, int64_t d_in, int64_t d_out, void *ws,
@@ -397,126 +659,25 @@ int larosa_layer_forward(const void *x, int act_dtype, const void *Qt, int64_t q
                          const void *W_folded, int w_dtype, int64_t B, int64_t d_in,
                          int64_t d_out, int64_t k, void *y, int32_t *idx_out, float *xrot_out,
                          int mode, void *ws, size_t ws_bytes, larosa_stream_t stream) {
-  if (!dtype_ok(act_dtype) || !dtype_ok(w_dtype)) return LAROSA_ERR_DTYPE;
-  if (w_dtype == LAROSA_F32 && act_dtype == LAROSA_BF16) return LAROSA_ERR_DTYPE;
-  if (int st = check_sizes(B, d_in, k)) return st;
-  if (base_mode(mode) < 0) return LAROSA_ERR_INVALID_ARG;
-  if (d_out < 1) return LAROSA_ERR_SHAPE;
-  if (B == 0) return LAROSA_OK;
-  if (!x || !Qt || !W_folded || !y) return LAROSA_ERR_INVALID_ARG;
-  if (int st = check_rotation(d_in, q_block, w_dtype)) return st;
-  if (d_in % vec_of(act_dtype) || d_out % vec_of(w_dtype)) return LAROSA_ERR_ALIGNMENT;
-  if (!aligned16(x) || !aligned16(Qt) || !aligned16(W_folded) || !aligned16(y))
-    return LAROSA_ERR_ALIGNMENT;
-  if ((xrot_out && !aligned16(xrot_out)) || !aligned16(ws)) return LAROSA_ERR_ALIGNMENT;
-  const bool f64 = fp64_rotation(mode);
-  const bool fused = base_mode(mode) == LAROSA_FUSED && !f64 &&
-                     fused_supported(B, d_in, act_dtype, w_dtype);
-  const Layout L = fused ? layout_with_fused(B, d_in, d_out, k, w_dtype)
-                         : layout_for(B, d_in, d_out, k, w_dtype);
-  if (!ws || ws_bytes < L.total) return LAROSA_ERR_WORKSPACE;
-  if (int st = device_status()) return st;
+  Sel sel;
+  sel.k = k;
+  return layer_entry(x, act_dtype, Qt, q_block, W_folded, w_dtype, B, d_in, d_out, sel, y,
+                     idx_out, xrot_out, mode, ws, ws_bytes, stream);
+}
 
-  hipStream_t s = stream_of(stream);
-  char *base = static_cast<char *>(ws);
-  if (fused) {
-    FusedArgs f;
-    f.x = x;
-    f.qt = Qt;
-    f.wf = W_folded;
-    f.y = y;
-    f.w_dt = w_dtype;
-    f.d_in = static_cast<int>(d_in);
-    f.q_block = static_cast<int>(q_block);
-    f.k = static_cast<int>(k);
-    f.d_out = d_out;
-    f.idx_out = idx_out;
-    f.xrot_out = xrot_out;
-    f.ws = base + L.fused;
-    return launched(launch_fused_linear(f, s));
-  }
-  float *x_rot = xrot_out ? xrot_out : reinterpret_cast<float *>(base + L.x_rot);
-  int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(base + L.idx);
-  float *val = reinterpret_cast<float *>(base + L.val);
-
-  // Batches of 16 to 64 tokens in bf16 run the matrix-core forms of the
-  // rotation and the product, which read Qt and the union rows once for the
-  // whole batch.
-  const bool mf = mfma_supported(B, act_dtype, w_dtype);
-  hipError_t e =
-      f64   ? launch_rotate_f64(x, act_dtype, Qt, w_dtype, x_rot, static_cast<int>(B),
-                                static_cast<int>(d_in), static_cast<int>(q_block), s)
-      : mf && q_block % 32 == 0
-          ? launch_rotate_mfma(x, Qt, x_rot, static_cast<int>(B), static_cast<int>(d_in),
-                               static_cast<int>(q_block), base + L.p.mfma_parts, s)
-          : launch_rotate(x, act_dtype, Qt, w_dtype, x_rot, static_cast<int>(B),
-                          static_cast<int>(d_in), static_cast<int>(q_block), s);
-  if (e != hipSuccess) return LAROSA_ERR_LAUNCH;
-
-  GatherArgs a;
-  a.coef_mode = kCoefPacked;
-  a.w = W_folded;
-  a.w_dt = w_dtype;
-  a.d_in = d_in;
-  a.d_out = d_out;
-  a.y = y;
-  a.y_dt = act_dtype;
-  a.B = static_cast<int>(B);
-  a.ws = base + L.p.gather;
-  if (B == 1 && select_gather_supported(d_in)) {
-    // One token: every workgroup of the product computes the exact Top-K rule
-    // itself, so selection and product are one launch.
-    SelectGatherArgs g;
-    g.x_rot = x_rot;
-    g.d_in = static_cast<int>(d_in);
-    g.k = static_cast<int>(k);
-    g.w = W_folded;
-    g.w_dt = w_dtype;
-    g.d_out = d_out;
-    g.y = y;
-    g.y_dt = act_dtype;
-    g.idx_out = idx_out;
-    g.ws = base + L.p.gather;
-    return launched(launch_select_gather(g, s));
-  }
-  if (B == 1) {
-    e = launch_select(x_rot, 1, static_cast<int>(d_in), static_cast<int>(k), idx, val,
-                      nullptr, nullptr, s);
-    if (e != hipSuccess) return LAROSA_ERR_LAUNCH;
-    a.rows = idx;
-    a.n_rows = nullptr;
-    a.max_rows = k;
-    a.coef = val;
-  } else {
-    float *xs = reinterpret_cast<float *>(base + L.xs);
-    uint32_t *mask = reinterpret_cast<uint32_t *>(base + L.p.mask);
-    int32_t *u_idx = reinterpret_cast<int32_t *>(base + L.u_idx);
-    int32_t *u_cnt = reinterpret_cast<int32_t *>(base + L.u_cnt);
-    float *u_coef = reinterpret_cast<float *>(base + L.u_coef);
-    e = launch_select(x_rot, static_cast<int>(B), static_cast<int>(d_in), static_cast<int>(k),
-                      idx, val, xs, mask, s);
-    if (e == hipSuccess)
-      e = launch_union(mask, xs, static_cast<int>(B), static_cast<int>(d_in), u_idx, u_cnt,
-                       mf ? nullptr : u_coef, s);
-    if (e != hipSuccess) return LAROSA_ERR_LAUNCH;
-    const int64_t bk = B * k;
-    const int64_t max_rows = bk < d_in ? bk : d_in;
-    if (mf) {
-      const int64_t ldc = mfma_coef_ld(max_rows);
-      void *coefT = base + L.p.mfma_coef;
-      e = launch_union_coef_t(u_idx, u_cnt, xs, static_cast<int>(B), static_cast<int>(d_in), ldc,
-                              coefT, s);
-      if (e == hipSuccess)
-        e = launch_gather_mfma(u_idx, u_cnt, max_rows, d_in, coefT, ldc, W_folded, y,
-                               static_cast<int>(B), d_out, base + L.p.mfma_parts, s);
-      return launched(e);
-    }
-    a.rows = u_idx;
-    a.n_rows = u_cnt;
-    a.max_rows = max_rows;
-    a.coef = u_coef;
-  }
-  return launched(launch_gather(a, s));
+int larosa_threshold_layer_forward(const void *x, int act_dtype, const void *Qt,
+                                   int64_t q_block, const void *W_folded, int w_dtype, int64_t B,
+                                   int64_t d_in, int64_t d_out, float t, void *y,
+                                   int32_t *idx_out, int32_t *count_out, float *xrot_out,
+                                   int mode, void *ws, size_t ws_bytes, larosa_stream_t stream) {
+  if (!(t >= 0.f)) return LAROSA_ERR_INVALID_ARG;  // negative or NaN
+  Sel sel;
+  sel.thr = true;
+  sel.k = d_in;
+  sel.thr_key = threshold_key_of(t);
+  sel.count_out = count_out;
+  return layer_entry(x, act_dtype, Qt, q_block, W_folded, w_dtype, B, d_in, d_out, sel, y,
+                     idx_out, xrot_out, mode, ws, ws_bytes, stream);
 }
 
 size_t larosa_swiglu_workspace_bytes(int64_t B, int64_t d_in, int64_t f, int64_t k, int mode) {
@@ -547,64 +708,26 @@ int larosa_swiglu_layer_forward(const void *x, int act_dtype, const void *Qt, in
                                 int64_t f, int64_t k, void *h, int32_t *idx_out,
                                 float *xrot_out, int mode, void *ws, size_t ws_bytes,
                                 larosa_stream_t stream) {
-  if (!dtype_ok(act_dtype) || !dtype_ok(w_dtype)) return LAROSA_ERR_DTYPE;
-  if (f < 1 || f % interleave_block(w_dtype)) return LAROSA_ERR_SHAPE;
-  if (base_mode(mode) < 0) return LAROSA_ERR_INVALID_ARG;
-  const size_t need = larosa_swiglu_workspace_bytes(B, d_in, f, k, mode);
-  if (need == 0 && B != 0) {  // invalid sizes: let the layer call name the error
-    return larosa_layer_forward(x, act_dtype, Qt, q_block, W_il, w_dtype, B, d_in, 2 * f, k, h,
-                                idx_out, xrot_out, mode, ws, ws_bytes, stream);
-  }
-  if (B == 0) return LAROSA_OK;
-  if (!h) return LAROSA_ERR_INVALID_ARG;
-  if (!aligned16(h)) return LAROSA_ERR_ALIGNMENT;
-  if (!ws || ws_bytes < need) return LAROSA_ERR_WORKSPACE;
-  const size_t layer_bytes = larosa_workspace_bytes(B, d_in, 2 * f, k, mode);
-  const bool one_launch = (base_mode(mode) == LAROSA_UNFUSED || fp64_rotation(mode)) && B == 1 &&
-                          select_gather_supported(d_in) &&
-                          !(w_dtype == LAROSA_F32 && act_dtype == LAROSA_BF16);
-  if (one_launch) {
-    // rotation, then the selection, product and SiLU(gate)·up in one launch
-    if (int st = check_sizes(B, d_in, k)) return st;
-    if (!x || !Qt || !W_il) return LAROSA_ERR_INVALID_ARG;
-    if (int st = check_rotation(d_in, q_block, w_dtype)) return st;
-    if (d_in % vec_of(act_dtype)) return LAROSA_ERR_ALIGNMENT;
-    if (!aligned16(x) || !aligned16(Qt) || !aligned16(W_il) || !aligned16(ws))
-      return LAROSA_ERR_ALIGNMENT;
-    if (xrot_out && !aligned16(xrot_out)) return LAROSA_ERR_ALIGNMENT;
-    if (int st = device_status()) return st;
-    const Layout L = layout_for(B, d_in, 2 * f, k, w_dtype);
-    char *base = static_cast<char *>(ws);
-    float *x_rot = xrot_out ? xrot_out : reinterpret_cast<float *>(base + L.x_rot);
-    hipStream_t s = stream_of(stream);
-    const hipError_t er =
-        fp64_rotation(mode)
-            ? launch_rotate_f64(x, act_dtype, Qt, w_dtype, x_rot, 1, static_cast<int>(d_in),
-                                static_cast<int>(q_block), s)
-            : launch_rotate(x, act_dtype, Qt, w_dtype, x_rot, 1, static_cast<int>(d_in),
-                            static_cast<int>(q_block), s);
-    if (er != hipSuccess) return LAROSA_ERR_LAUNCH;
-    SelectGatherArgs g;
-    g.x_rot = x_rot;
-    g.d_in = static_cast<int>(d_in);
-    g.k = static_cast<int>(k);
-    g.w = W_il;
-    g.w_dt = w_dtype;
-    g.d_out = 2 * f;
-    g.y = h;
-    g.y_dt = act_dtype;
-    g.idx_out = idx_out;
-    g.ws = base + L.p.gather;
-    g.swiglu = true;
-    return launched(launch_select_gather(g, s));
-  }
-  // otherwise the gate|up rows into the workspace, then SiLU(gate)·up
-  void *gu = static_cast<char *>(ws) + layer_bytes;
-  const int st = larosa_layer_forward(x, act_dtype, Qt, q_block, W_il, w_dtype, B, d_in, 2 * f,
-                                      k, gu, idx_out, xrot_out, mode, ws, layer_bytes, stream);
-  if (st != LAROSA_OK) return st;
-  return launched(launch_swiglu_il(gu, h, B, f, interleave_block(w_dtype), act_dtype,
-                                   stream_of(stream)));
+  Sel sel;
+  sel.k = k;
+  return swiglu_entry(x, act_dtype, Qt, q_block, W_il, w_dtype, B, d_in, f, sel, h, idx_out,
+                      xrot_out, mode, ws, ws_bytes, stream);
+}
+
+int larosa_threshold_swiglu_layer_forward(const void *x, int act_dtype, const void *Qt,
+                                          int64_t q_block, const void *W_il, int w_dtype,
+                                          int64_t B, int64_t d_in, int64_t f, float t, void *h,
+                                          int32_t *idx_out, int32_t *count_out, float *xrot_out,
+                                          int mode, void *ws, size_t ws_bytes,
+                                          larosa_stream_t stream) {
+  if (!(t >= 0.f)) return LAROSA_ERR_INVALID_ARG;
+  Sel sel;
+  sel.thr = true;
+  sel.k = d_in;
+  sel.thr_key = threshold_key_of(t);
+  sel.count_out = count_out;
+  return swiglu_entry(x, act_dtype, Qt, q_block, W_il, w_dtype, B, d_in, f, sel, h, idx_out,
+                      xrot_out, mode, ws, ws_bytes, stream);
 }
 
 int larosa_swiglu(const void *gu, void *h, int64_t B, int64_t f, int dtype,

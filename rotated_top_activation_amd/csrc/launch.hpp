@@ -14,6 +14,18 @@ inline int dt_size(int dt) { return dt == kF32 ? 4 : 2; }
 // --- rotation (dot product per output channel against the prepared Qt) ---
 hipError_t launch_rotate(const void *x, int x_dt, const void *qt, int q_dt,
                          float *x_rot, int B, int d, int qb, hipStream_t s);
+// --- magnitude-threshold selection and its calibration ---
+uint32_t threshold_key_of(float t);  // fp32 bits of t with the sign cleared
+// idx/val rows have capacity d; count[b] = kept channels of token b; val,
+// xs, count and mask may be NULL.
+hipError_t launch_threshold_select(const float *x_rot, int B, int d, uint32_t thr_key,
+                                   int32_t *idx, int32_t *count, float *val, float *xs,
+                                   uint32_t *mask, hipStream_t s);
+size_t calibrate_ws_bytes();
+// t_out = the keep-th largest magnitude of x[0 .. n); 1 <= keep <= n < 2^31.
+hipError_t launch_calibrate(const float *x, int64_t n, uint32_t keep, float *t_out, void *ws,
+                            hipStream_t s);
+
 // fp64 accumulation, one rounding to fp32 (any B; one pass per 8 tokens)
 hipError_t launch_rotate_f64(const void *x, int x_dt, const void *qt, int q_dt, float *x_rot,
                              int B, int d, int qb, hipStream_t s);
@@ -89,6 +101,12 @@ struct SelectGatherArgs {
   // swiglu: W's columns are gate|up interleaved in blocks of half a tile and
   // y is h [d_out / 2] = SiLU(gate)·up of the sums rounded to y's type.
   bool swiglu = false;
+  // by_threshold: keep the channels whose key (fp32 bits, sign cleared) is
+  // >= thr_key instead of the Top-k; idx_out then has capacity d_in and the
+  // number kept goes to count_out (either may be NULL).
+  bool by_threshold = false;
+  uint32_t thr_key = 0;
+  int32_t *count_out = nullptr;
 };
 hipError_t launch_select_gather(const SelectGatherArgs &a, hipStream_t s);
 

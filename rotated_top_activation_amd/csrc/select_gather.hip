@@ -20,6 +20,11 @@
 //
 // The grid is sized to at most one workgroup per CU (256 on MI355X), which
 // keeps every workgroup resident for the whole launch.
+//
+// Threshold form (THR): the kept channels are those with |x_rot| >= t (the
+// magnitude threshold of the R-Sparse summary page, 研究流程与方法 ·
+// R-Sparse框架设计). No rule has to be found: every workgroup compacts its
+// split's kept channels at once, and tile 0 also writes how many there are.
 #include "common.hpp"
 #include "launch.hpp"
 #include "select_core.hpp"
@@ -36,11 +41,12 @@ constexpr int kSgMaxSplitLoads = 32;  // partial sums fetched per round trip
 
 size_t sg_counter_bytes(int tiles) { return (static_cast<size_t>(tiles) * 4 + 255) / 256 * 256; }
 
-template <typename WT, typename OT, int EMAX, bool SWIGLU>
+template <typename WT, typename OT, int EMAX, bool SWIGLU, bool THR>
 __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
-    const float *__restrict__ x_rot, int d, int k, int E, int tiles, int splits, int cps,
-    const WT *__restrict__ w, int64_t d_out, OT *__restrict__ y, float *__restrict__ partials,
-    uint32_t *__restrict__ counters, int32_t *__restrict__ idx_out) {
+    const float *__restrict__ x_rot, int d, int k, uint32_t thr_key, int E, int tiles,
+    int splits, int cps, const WT *__restrict__ w, int64_t d_out, OT *__restrict__ y,
+    float *__restrict__ partials, uint32_t *__restrict__ counters,
+    int32_t *__restrict__ idx_out, int32_t *__restrict__ count_out) {
   constexpr int V = Elt<WT>::kVec;
   constexpr int TILE = kWave * V;
   constexpr int R = kSgRows;
@@ -103,13 +109,24 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
 
   // 1. First digit of the rule over all d channels (the same in every
   //    workgroup). A channel whose first digit is above the boundary digit
-  //    is kept whatever its later digits.
-  const RuleState st = rule_first_digit<kSgThreads, EMAX>(key, E, static_cast<uint32_t>(k), sm);
-  const uint32_t digit0 = st.prefix >> radix_shift(0);
+  //    is kept whatever its later digits. (The threshold form has no rule:
+  //    every kept channel is certain.)
+  RuleState st{};
+  uint32_t digit0 = 0;
+  if constexpr (!THR) {
+    st = rule_first_digit<kSgThreads, EMAX>(key, E, static_cast<uint32_t>(k), sm);
+    digit0 = st.prefix >> radix_shift(0);
+  } else {
+    __syncthreads();  // the LDS copy of the vector is complete
+  }
+  auto certain = [&](int i) {
+    if constexpr (THR) return key_of(i) >= thr_key;
+    else return (key_of(i) >> radix_shift(0)) > digit0;
+  };
 
   // 2. This split's certain rows, ascending, at the head of the LDS list.
   const int n_cert = static_cast<int>(compact(
-      c0, c1, [&](int i) { return (key_of(i) >> radix_shift(0)) > digit0; },
+      c0, c1, certain,
       [&](int i, uint32_t pos) {
         l_idx[pos] = i;
         l_val[pos] = __uint_as_float(kv[i]);
@@ -132,27 +149,33 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
   }
 
   // 4. The rest of the rule: T, and channels equal to T kept up to `cut`.
-  uint32_t T, cut;
-  rule_finish<kSgThreads, EMAX>(key, E, i0, st, sm, cs, T, cut);
+  uint32_t T = 0, cut = 0;
+  if constexpr (!THR) rule_finish<kSgThreads, EMAX>(key, E, i0, st, sm, cs, T, cut);
   auto keeps = [&](int i) {
     const uint32_t kk = key_of(i);
-    return kk > T || (kk == T && static_cast<uint32_t>(i) <= cut);
+    if constexpr (THR) return kk >= thr_key;
+    else return kk > T || (kk == T && static_cast<uint32_t>(i) <= cut);
   };
 
   // 5. The split's kept channels of the boundary digit follow the certain
   //    ones; tile 0 also writes the global ascending index list (parity
   //    checks): the positions of this split's channels follow from the
   //    channels below c1.
-  const int n_list = n_cert + static_cast<int>(compact(
-      c0, c1, [&](int i) { return (key_of(i) >> radix_shift(0)) == digit0 && keeps(i); },
-      [&](int i, uint32_t pos) {
-        l_idx[n_cert + pos] = i;
-        l_val[n_cert + pos] = __uint_as_float(kv[i]);
-      }));
-  if (idx_out != nullptr && tile == 0)
-    compact(0, c1, keeps, [&](int i, uint32_t pos) {
-      if (i >= c0) idx_out[pos] = i;
+  int n_list = n_cert;
+  if constexpr (!THR)
+    n_list += static_cast<int>(compact(
+        c0, c1, [&](int i) { return (key_of(i) >> radix_shift(0)) == digit0 && keeps(i); },
+        [&](int i, uint32_t pos) {
+          l_idx[n_cert + pos] = i;
+          l_val[n_cert + pos] = __uint_as_float(kv[i]);
+        }));
+  if ((idx_out != nullptr || (THR && count_out != nullptr && c1 == d)) && tile == 0) {
+    const uint32_t below = compact(0, c1, keeps, [&](int i, uint32_t pos) {
+      if (idx_out != nullptr && i >= c0) idx_out[pos] = i;
     });
+    // the last split counts every kept channel
+    if (THR && count_out != nullptr && c1 == d && t == 0) *count_out = static_cast<int32_t>(below);
+  }
   __syncthreads();  // the vector's LDS copy becomes the waves' sum area
 
   // 6. Stream the split's kept rows of this column tile: the first group
@@ -280,22 +303,27 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
     __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <typename WT, typename OT, int EM>
-void launch_sg_em(const SelectGatherArgs &a, const SelectGatherPlan &p, int E, hipStream_t s) {
+template <typename WT, typename OT, int EM, bool SW, bool TH>
+void launch_sg_k(const SelectGatherArgs &a, const SelectGatherPlan &p, int E, hipStream_t s) {
   uint32_t *counters = static_cast<uint32_t *>(a.ws);
   float *partials =
       reinterpret_cast<float *>(static_cast<char *>(a.ws) + sg_counter_bytes(p.tiles));
   const dim3 grid(static_cast<unsigned>(p.tiles * p.splits)), block(kSgThreads);
-  const auto *w = static_cast<const WT *>(a.w);
-  auto *y = static_cast<OT *>(a.y);
-  if (a.swiglu)
-    hipLaunchKernelGGL((select_gather_kernel<WT, OT, EM, true>), grid, block, 0, s, a.x_rot,
-                       a.d_in, a.k, E, p.tiles, p.splits, p.cps, w, a.d_out, y, partials,
-                       counters, a.idx_out);
-  else
-    hipLaunchKernelGGL((select_gather_kernel<WT, OT, EM, false>), grid, block, 0, s, a.x_rot,
-                       a.d_in, a.k, E, p.tiles, p.splits, p.cps, w, a.d_out, y, partials,
-                       counters, a.idx_out);
+  hipLaunchKernelGGL((select_gather_kernel<WT, OT, EM, SW, TH>), grid, block, 0, s, a.x_rot,
+                     a.d_in, a.k, a.thr_key, E, p.tiles, p.splits, p.cps,
+                     static_cast<const WT *>(a.w), a.d_out, static_cast<OT *>(a.y), partials,
+                     counters, a.idx_out, a.count_out);
+}
+
+template <typename WT, typename OT, int EM>
+void launch_sg_em(const SelectGatherArgs &a, const SelectGatherPlan &p, int E, hipStream_t s) {
+  if (a.by_threshold) {
+    if (a.swiglu) launch_sg_k<WT, OT, EM, true, true>(a, p, E, s);
+    else launch_sg_k<WT, OT, EM, false, true>(a, p, E, s);
+  } else {
+    if (a.swiglu) launch_sg_k<WT, OT, EM, true, false>(a, p, E, s);
+    else launch_sg_k<WT, OT, EM, false, false>(a, p, E, s);
+  }
 }
 
 template <typename WT, typename OT>

@@ -140,6 +140,43 @@ def test_standalone_calls_validation(lib):
     assert lib.larosa_workspace_init(PM, 64, None) == ALIGN
 
 
+def test_threshold_calls_validation(lib):
+    nan = float("nan")
+    ts = lib.larosa_threshold_select
+    assert ts(P, 1, 128, -1.0, P, P, None, None, None, None, None, None, 0, None) == INVALID
+    assert ts(P, 1, 128, nan, P, P, None, None, None, None, None, None, 0, None) == INVALID
+    assert ts(P, 1, 128, 0.5, P, None, None, None, None, None, None, None, 0, None) == INVALID
+    assert ts(P, 65, 128, 0.5, P, P, None, None, None, None, None, None, 0, None) == INVALID
+    assert ts(P, 1, 40000, 0.5, P, P, None, None, None, None, None, None, 0, None) == SHAPE
+    assert ts(P, 2, 128, 0.5, P, P, None, P, P, None, P, P, 1 << 20, None) == INVALID
+    assert ts(P, 2, 128, 0.5, P, P, None, P, P, P, P, P, 4, None) == WS
+    assert ts(PM, 1, 128, 0.5, P, P, None, None, None, None, None, None, 0, None) == ALIGN
+    assert ts(P, 0, 128, 0.5, P, P, None, None, None, None, None, None, 0, None) == OK
+    cw = lib.larosa_calibrate_workspace_bytes()
+    assert 0 < cw < 1 << 16
+    cal = lib.larosa_calibrate_threshold
+    assert cal(P, 0, 1, P, P, cw, None) == SHAPE
+    assert cal(P, 1 << 31, 1, P, P, cw, None) == SHAPE
+    assert cal(P, 100, 0, P, P, cw, None) == INVALID
+    assert cal(P, 100, 101, P, P, cw, None) == INVALID
+    assert cal(P, 100, 10, None, P, cw, None) == INVALID
+    assert cal(P, 100, 10, P, P, cw - 1, None) == WS
+    assert cal(P, 100, 10, P, PM, cw, None) == ALIGN
+    tl = lib.larosa_threshold_layer_forward
+    args = (P, 1, P, 64, P, 1, 1, 128, 64)
+    assert tl(*args, -0.5, P, None, None, None, 0, P, 1 << 30, None) == INVALID
+    assert tl(*args, nan, P, None, None, None, 0, P, 1 << 30, None) == INVALID
+    assert tl(*args, 0.5, P, None, None, None, 4, P, 1 << 30, None) == INVALID
+    assert tl(*args, 0.5, P, None, None, None, 0, P, 16, None) == WS
+    assert tl(P, 1, P, 48, P, 1, 1, 128, 64, 0.5, P, None, None, None, 0, P, 1 << 30,
+              None) == SHAPE
+    tsw = lib.larosa_threshold_swiglu_layer_forward
+    assert tsw(P, 1, P, 64, P, 1, 1, 128, 256, -1.0, P, None, None, None, 0, P, 1 << 24,
+               None) == INVALID
+    assert tsw(P, 1, P, 64, P, 1, 1, 128, 300, 0.5, P, None, None, None, 0, P, 1 << 24,
+               None) == SHAPE
+
+
 def test_no_device_is_reported_not_crashed(lib):
     """Valid arguments on a machine without a GPU give NO_DEVICE."""
     import torch
@@ -147,6 +184,9 @@ def test_no_device_is_reported_not_crashed(lib):
         pytest.skip("a GPU is visible")
     assert _lf(lib) == NODEV
     assert _lf(lib, mode=3) == NODEV
+    assert lib.larosa_threshold_layer_forward(P, 1, P, 64, P, 1, 1, 128, 64, 0.5, P, None, None,
+                                              None, 0, P, 1 << 30, None) == NODEV
+    assert lib.larosa_calibrate_threshold(P, 100, 10, P, P, 1 << 16, None) == NODEV
     assert lib.larosa_rotate_fp64(P, 1, P, 64, 1, P + (1 << 20), 1, 128, None) == NODEV
     assert lib.larosa_swiglu(P, P + (1 << 20), 1, 64, 1, None) == NODEV
     assert lib.larosa_topk_gemv(P, 128, 10, P, 1, P, 1, 64, None, P, 1 << 20, None) == NODEV
