@@ -285,6 +285,7 @@ def main():
         timed(lambda i: step(i, _lib.UNFUSED | _lib.ROTATE_FP64), a.steps, a.warmup), 5)
 
     thr = threshold_mlp(a, case, x_d, l1, l2, qt1, wil1, qt2, wf2, copies, h, y, timed, gbs)
+    lowr = lowrank_gate_up(a, case, x_d, l1, qt1, wf1, copies, timed, gbs)
 
     q_bytes = (l1.Qt.numel() + l2.Qt.numel()) * 2
     sparse_bytes = q_bytes + (case.k1 * 2 * f + case.k2 * d) * 2
@@ -352,6 +353,7 @@ def main():
             "stage_us": {k: round(v * 1e3, 2) for k, v in stage.items()},
             "rotation_fp32_vs_fp64": exact_rot,
             "threshold_select": thr,
+            "lowrank_compensation": lowr,
             "kernels": {k: {"achieved_GBs": round(v["achieved"], 1), "bytes_per_launch": v["bytes"],
                             "avg_us": round(v["us"], 3), "frac": round(v["achieved"] / HBM_PEAK_GBS, 4),
                             "traffic": measured_traffic(k)} for k, v in kernels.items()},
@@ -472,6 +474,43 @@ def threshold_mlp(a, case, x_d, l1, l2, qt1, wil1, qt2, wf2, copies, h, y, timed
             "down_in": {"min": int(c2.min()), "mean": round(float(c2.mean()), 1),
                         "max": int(c2.max()), "top_k": case.k2},
         },
+    }
+
+
+def lowrank_gate_up(a, case, x_d, l1, qt1, wf1, copies, timed, gbs, r=64):
+    """The gate|up linear with rank-r compensation of the dropped channels:
+    y = xs·W' + (x_rot − xs)·A_r·B_r, factors from a randomised SVD of the
+    folded weight on the device (offline, untimed), B_r stored below each
+    weight copy. Timed beside the plain Top-K layer on the same copies."""
+    import torch
+    from rotated_top_activation_amd import _lib
+    dev = x_d.device
+    d, n = case.d, 2 * case.f
+    torch.manual_seed(0)
+    u, sv, v = torch.svd_lowrank(l1.Wf.float(), q=r + 16, niter=3)
+    root = sv[:r].sqrt()
+    a_r = (u[:, :r] * root[None, :]).to(torch.bfloat16).contiguous()
+    b_r = (root[:, None] * v[:, :r].T).to(torch.bfloat16).contiguous()
+    w_ext = [torch.cat([wf1[c], b_r], dim=0).contiguous() for c in range(copies)]
+    gu = torch.empty((1, n), dtype=torch.bfloat16, device=dev)
+    ws = torch.zeros(_lib.larosa_lowrank_workspace_bytes(1, d, n, case.k1, r), dtype=torch.uint8,
+                     device=dev)
+    ws_plain = torch.zeros(_lib.larosa_workspace_bytes(1, d, n, case.k1, _lib.UNFUSED),
+                           dtype=torch.uint8, device=dev)
+    lr_ms = timed(lambda i: _lib.larosa_lowrank_layer_forward(
+        x_d, qt1[i % copies], l1.q_block, w_ext[i % copies], a_r, r, 1, d, n, case.k1, gu, ws=ws),
+        a.steps, a.warmup)
+    plain_ms = timed(lambda i: _lib.larosa_layer_forward(
+        x_d, qt1[i % copies], l1.q_block, wf1[i % copies], 1, d, n, case.k1, gu, ws=ws_plain),
+        a.steps, a.warmup)
+    nbytes = l1.Qt.numel() * 2 + (case.k1 + r) * n * 2 + d * r * 2
+    del w_ext
+    return {
+        "rank": r, "factors": "randomised SVD of W'_gate|up on the device (offline)",
+        "gate_up_layer_us": round(lr_ms * 1e3, 2),
+        "gate_up_layer_GBs": round(gbs(nbytes, lr_ms), 1),
+        "plain_top_k_layer_us": round(plain_ms * 1e3, 2),
+        "extra_bytes": (r * n + d * r) * 2,
     }
 
 

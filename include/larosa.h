@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define LAROSA_ABI_VERSION 4
+#define LAROSA_ABI_VERSION 5
 
 typedef void *larosa_stream_t; /* hipStream_t */
 
@@ -314,6 +314,37 @@ int larosa_threshold_swiglu_layer_forward(const void *x, int act_dtype, const vo
                                           int32_t *idx_out, int32_t *count_out, float *xrot_out,
                                           int mode, void *ws, size_t ws_bytes,
                                           larosa_stream_t stream);
+
+/* ---- Low-rank compensation of the dropped channels ---------------------
+ * The R-Sparse summary page (研究流程与方法 · R-Sparse框架设计) sends the
+ * masked remainder of the input through a rank-r factorisation of the
+ * weight taken from its SVD, A_r = U_r·Σ_r^½ and B_r = Σ_r^½·V_rᵀ, and adds
+ * that to the sparse output. Applied to the rotated layer (x·W convention,
+ * W' = U·Σ·Vᵀ):
+ *   y = xs·W' + (x_rot − xs)·A_r·B_r
+ * with xs the method's Top-K sparsified rotated input. The factors are
+ * inputs prepared offline (any SVD of W'); the caller stores B_r directly
+ * below W' as W_ext = [W'; B_r] ([d_in + r, d_out] in w_dtype), so the
+ * low-rank term is r more rows of the same product and both parts share one
+ * fp32 sum per output, rounded once to act_dtype. The first d_in rows of
+ * W_ext are W' itself and serve the other layer calls unchanged. */
+
+/* Workspace bytes of larosa_lowrank_layer_forward; 0 for invalid sizes. */
+size_t larosa_lowrank_workspace_bytes(int64_t B, int64_t d_in, int64_t d_out, int64_t k,
+                                      int64_t r);
+
+/* Rotate, keep each token's Top-k, then y [B, d_out] = xs·W' + (x_rot −
+ * xs)·A_r·B_r. A_r: [d_in, r] in w_dtype (row-major); 1 <= r <= min(256,
+ * d_in, d_out) (LAROSA_ERR_INVALID_ARG otherwise). mode: LAROSA_UNFUSED or
+ * LAROSA_FUSED (both run the separate steps), optionally with
+ * LAROSA_ROTATE_FP64. ws: larosa_lowrank_workspace_bytes(B, d_in, d_out, k,
+ * r) bytes, zero-filled once. Other arguments and errors as
+ * larosa_layer_forward. */
+int larosa_lowrank_layer_forward(const void *x, int act_dtype, const void *Qt, int64_t q_block,
+                                 const void *W_ext, const void *A_r, int64_t r, int w_dtype,
+                                 int64_t B, int64_t d_in, int64_t d_out, int64_t k, void *y,
+                                 int32_t *idx_out, float *xrot_out, int mode, void *ws,
+                                 size_t ws_bytes, larosa_stream_t stream);
 
 /* ---- The decoder layer around the rotated linears ----------------------
  * The pages apply the rotated Top-K sparsification to every linear layer of a

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblarosa.s
 F32, BF16 = 0, 1
 UNFUSED, FUSED = 0, 1
 ROTATE_FP64 = 2  # mode flag: fp64-accumulating rotation, OR-ed into UNFUSED or FUSED
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 _c_i64 = ctypes.c_int64
 _c_int = ctypes.c_int
@@ -68,6 +68,10 @@ SIGNATURES = {
                                                        _c_int, _c_i64, _c_i64, _c_i64,
                                                        ctypes.c_float, _c_vp, _c_vp, _c_vp,
                                                        _c_vp, _c_int, _c_vp, _c_sz, _c_vp]),
+    "larosa_lowrank_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64]),
+    "larosa_lowrank_layer_forward": (_c_int, [_c_vp, _c_int, _c_vp, _c_i64, _c_vp, _c_vp, _c_i64,
+                                              _c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp,
+                                              _c_vp, _c_vp, _c_int, _c_vp, _c_sz, _c_vp]),
     "larosa_rmsnorm": (_c_int, [_c_vp, _c_vp, _c_i64, _c_i64, ctypes.c_float, _c_int, _c_vp]),
     "larosa_rope": (_c_int, [_c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                              ctypes.c_float, _c_int, _c_vp]),
@@ -280,6 +284,20 @@ def larosa_threshold_swiglu_layer_forward(x, Qt, q_block: int, W_il, B: int, d_i
                                                         _ptr(h), _ptr(idx_out), _ptr(count_out),
                                                         _ptr(xrot_out), mode, _ptr(ws),
                                                         _nbytes(ws), _stream(stream)))
+
+
+def larosa_lowrank_workspace_bytes(B: int, d_in: int, d_out: int, k: int, r: int) -> int:
+    return int(load().larosa_lowrank_workspace_bytes(B, d_in, d_out, k, r))
+
+
+def larosa_lowrank_layer_forward(x, Qt, q_block: int, W_ext, A_r, r: int, B: int, d_in: int,
+                                 d_out: int, k: int, y, idx_out=None, xrot_out=None,
+                                 mode: int = UNFUSED, ws=None, stream=None) -> None:
+    _check("larosa_lowrank_layer_forward",
+           load().larosa_lowrank_layer_forward(_ptr(x), _dt(x), _ptr(Qt), q_block, _ptr(W_ext),
+                                               _ptr(A_r), r, _dt(W_ext), B, d_in, d_out, k,
+                                               _ptr(y), _ptr(idx_out), _ptr(xrot_out), mode,
+                                               _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def larosa_rmsnorm(h, out, B: int, d: int, eps: float = 1e-5, stream=None) -> None:

@@ -115,6 +115,32 @@ Layout layout_with_fused(int64_t B, int64_t d_in, int64_t d_out, int64_t k, int 
   return L;
 }
 
+// The low-rank compensated layer: the layer's areas sized for d_in + r rows
+// (the product runs over W_ext = [W'; B_r]), then the projection's partial
+// sums and the extended row list.
+struct LrLayout {
+  Layout l;
+  size_t part = 0, rows_ext = 0, n_ext = 0, total = 0;
+};
+
+LrLayout lowrank_layout(int64_t B, int64_t d_in, int64_t d_out, int64_t k, int64_t r, int w_dt) {
+  LrLayout L;
+  L.l = layout_for(B, d_in + r, d_out, k, w_dt);
+  size_t off = L.l.total;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  L.part = take(lowrank_part_bytes(B, d_in, r));
+  L.rows_ext = take(static_cast<size_t>(d_in + r) * 4);
+  L.n_ext = take(4);
+  L.total = off;
+  return L;
+}
+
+constexpr int64_t kMaxRank = 256;
+
 int check_sizes(int64_t B, int64_t d, int64_t k) {
   if (B < 0 || B > kMaxB) return LAROSA_ERR_INVALID_ARG;
   if (d < 1 || d > kMaxD) return LAROSA_ERR_SHAPE;
@@ -532,6 +558,105 @@ int larosa_calibrate_threshold(const float *x_rot, int64_t n, int64_t keep, floa
   if (int st = device_status()) return st;
   return launched(launch_calibrate(x_rot, n, static_cast<uint32_t>(keep), t_out, ws,
                                    stream_of(stream)));
+}
+
+size_t larosa_lowrank_workspace_bytes(int64_t B, int64_t d_in, int64_t d_out, int64_t k,
+                                      int64_t r) {
+  const int64_t b1 = B < 1 ? 1 : B;
+  if (check_sizes(b1, d_in, k) != LAROSA_OK || d_out < 1) return 0;
+  if (r < 1 || r > kMaxRank || r > d_in || r > d_out) return 0;
+  const size_t a = lowrank_layout(b1, d_in, d_out, k, r, LAROSA_BF16).total;
+  const size_t b = lowrank_layout(b1, d_in, d_out, k, r, LAROSA_F32).total;
+  return a > b ? a : b;
+}
+
+int larosa_lowrank_layer_forward(const void *x, int act_dtype, const void *Qt, int64_t q_block,
+                                 const void *W_ext, const void *A_r, int64_t r, int w_dtype,
+                                 int64_t B, int64_t d_in, int64_t d_out, int64_t k, void *y,
+                                 int32_t *idx_out, float *xrot_out, int mode, void *ws,
+                                 size_t ws_bytes, larosa_stream_t stream) {
+  if (!dtype_ok(act_dtype) || !dtype_ok(w_dtype)) return LAROSA_ERR_DTYPE;
+  if (w_dtype == LAROSA_F32 && act_dtype == LAROSA_BF16) return LAROSA_ERR_DTYPE;
+  if (int st = check_sizes(B, d_in, k)) return st;
+  if (base_mode(mode) < 0) return LAROSA_ERR_INVALID_ARG;
+  if (d_out < 1) return LAROSA_ERR_SHAPE;
+  if (r < 1 || r > kMaxRank || r > d_in || r > d_out) return LAROSA_ERR_INVALID_ARG;
+  if (B == 0) return LAROSA_OK;
+  if (!x || !Qt || !W_ext || !A_r || !y) return LAROSA_ERR_INVALID_ARG;
+  if (int st = check_rotation(d_in, q_block, w_dtype)) return st;
+  if (d_in % vec_of(act_dtype) || d_out % vec_of(w_dtype)) return LAROSA_ERR_ALIGNMENT;
+  if (!aligned16(x) || !aligned16(Qt) || !aligned16(W_ext) || !aligned16(y) || !aligned16(ws))
+    return LAROSA_ERR_ALIGNMENT;
+  if (xrot_out && !aligned16(xrot_out)) return LAROSA_ERR_ALIGNMENT;
+  const LrLayout L = lowrank_layout(B, d_in, d_out, k, r, w_dtype);
+  if (!ws || ws_bytes < L.total) return LAROSA_ERR_WORKSPACE;
+  if (int st = device_status()) return st;
+
+  hipStream_t s = stream_of(stream);
+  char *base = static_cast<char *>(ws);
+  float *x_rot = xrot_out ? xrot_out : reinterpret_cast<float *>(base + L.l.x_rot);
+  int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(base + L.l.idx);
+  float *val = reinterpret_cast<float *>(base + L.l.val);
+  float *xs = reinterpret_cast<float *>(base + L.l.xs);
+  const int Bi = static_cast<int>(B), di = static_cast<int>(d_in), ri = static_cast<int>(r);
+  const bool mf = mfma_supported(B, act_dtype, w_dtype);
+  hipError_t e =
+      fp64_rotation(mode)
+          ? launch_rotate_f64(x, act_dtype, Qt, w_dtype, x_rot, Bi, di, static_cast<int>(q_block), s)
+      : mf && q_block % 32 == 0
+          ? launch_rotate_mfma(x, Qt, x_rot, Bi, di, static_cast<int>(q_block),
+                               base + L.l.p.mfma_parts, s)
+          : launch_rotate(x, act_dtype, Qt, w_dtype, x_rot, Bi, di, static_cast<int>(q_block), s);
+  uint32_t *mask = B > 1 ? reinterpret_cast<uint32_t *>(base + L.l.p.mask) : nullptr;
+  if (e == hipSuccess)
+    e = launch_select(x_rot, Bi, di, static_cast<int>(k), idx, val, xs, mask, s);
+  // the base row list: the token's kept rows, or the batch's union
+  const int32_t *list = idx;
+  const int32_t *n_dev = nullptr;
+  int64_t max_rows = k;
+  if (e == hipSuccess && B > 1) {
+    int32_t *u_idx = reinterpret_cast<int32_t *>(base + L.l.u_idx);
+    int32_t *u_cnt = reinterpret_cast<int32_t *>(base + L.l.u_cnt);
+    e = launch_union(mask, xs, Bi, di, u_idx, u_cnt, nullptr, s);
+    list = u_idx;
+    n_dev = u_cnt;
+    max_rows = B * k < d_in ? B * k : d_in;
+  }
+  float *part = reinterpret_cast<float *>(base + L.part);
+  if (e == hipSuccess) e = launch_lowrank_proj(x_rot, xs, A_r, w_dtype, Bi, di, ri, part, s);
+  if (e != hipSuccess) return LAROSA_ERR_LAUNCH;
+  int32_t *rows_ext = reinterpret_cast<int32_t *>(base + L.rows_ext);
+  int32_t *n_ext = reinterpret_cast<int32_t *>(base + L.n_ext);
+  const int64_t max_ext = max_rows + r;
+  if (mf) {
+    const int64_t ldc = mfma_coef_ld(max_ext);
+    void *coefT = base + L.l.p.mfma_coef;
+    e = launch_lowrank_list(list, n_dev, static_cast<int>(k), di, ri, xs, part, Bi, ldc,
+                            rows_ext, n_ext, nullptr, coefT, s);
+    if (e == hipSuccess)
+      e = launch_gather_mfma(rows_ext, n_ext, max_ext, d_in + r, coefT, ldc, W_ext, y, Bi, d_out,
+                             base + L.l.p.mfma_parts, s);
+    return launched(e);
+  }
+  float *coef = reinterpret_cast<float *>(base + L.l.u_coef);
+  e = launch_lowrank_list(list, n_dev, static_cast<int>(k), di, ri, xs, part, Bi, max_ext,
+                          rows_ext, n_ext, coef, nullptr, s);
+  if (e != hipSuccess) return LAROSA_ERR_LAUNCH;
+  GatherArgs a;
+  a.rows = rows_ext;
+  a.n_rows = n_ext;
+  a.max_rows = max_ext;
+  a.coef = coef;
+  a.coef_mode = kCoefPacked;
+  a.w = W_ext;
+  a.w_dt = w_dtype;
+  a.d_in = d_in + r;
+  a.d_out = d_out;
+  a.y = y;
+  a.y_dt = act_dtype;
+  a.B = Bi;
+  a.ws = base + L.l.p.gather;
+  return launched(launch_gather(a, s));
 }
 
 int larosa_sparse_gemv(const int32_t *rows, const int32_t *n_rows, int64_t max_rows,

@@ -26,6 +26,20 @@ size_t calibrate_ws_bytes();
 hipError_t launch_calibrate(const float *x, int64_t n, uint32_t keep, float *t_out, void *ws,
                             hipStream_t s);
 
+// --- low-rank compensation of the dropped channels (r <= 256) ---
+size_t lowrank_part_bytes(int64_t B, int64_t d, int64_t r);
+// Partial sums of u [B, r] = (x_rot − xs)·A_r per row range, into part
+// (lowrank_part_bytes).
+hipError_t launch_lowrank_proj(const float *x_rot, const float *xs, const void *a_r, int w_dt,
+                               int B, int d, int r, float *part, hipStream_t s);
+// The kept rows (or union) followed by rows d_in .. d_in + r − 1 of W_ext,
+// with their coefficients (u summed from part): packed (coef, ld = list
+// capacity) or split and transposed (coef_hl, ld = ldc).
+hipError_t launch_lowrank_list(const int32_t *base, const int32_t *n_dev, int n_host, int d_in,
+                               int r, const float *xs, const float *part, int B, int64_t ld,
+                               int32_t *rows_ext, int32_t *n_ext, float *coef, void *coef_hl,
+                               hipStream_t s);
+
 // fp64 accumulation, one rounding to fp32 (any B; one pass per 8 tokens)
 hipError_t launch_rotate_f64(const void *x, int x_dt, const void *qt, int q_dt, float *x_rot,
                              int B, int d, int qb, hipStream_t s);

@@ -177,6 +177,27 @@ def test_threshold_calls_validation(lib):
                None) == SHAPE
 
 
+def test_lowrank_validation(lib):
+    wb = lib.larosa_lowrank_workspace_bytes
+    assert wb(1, 4096, 22016, 2457, 64) > lib.larosa_workspace_bytes(1, 4096, 22016, 2457, 0)
+    assert wb(1, 4096, 22016, 2457, 0) == 0       # r outside [1, 256]
+    assert wb(1, 4096, 22016, 2457, 257) == 0
+    assert wb(1, 128, 64, 10, 100) == 0           # r above d_out
+    lr = lib.larosa_lowrank_layer_forward
+
+    def call(r=16, a=P, wext=P, mode=0, wsb=1 << 30, k=32, qb=64):
+        return lr(P, 1, P, qb, wext, a, r, 1, 1, 128, 64, k, P, None, None, mode, P, wsb, None)
+    assert call(r=0) == INVALID
+    assert call(r=65) == INVALID                  # above d_out = 64
+    assert call(a=None) == INVALID
+    assert call(wext=None) == INVALID
+    assert call(mode=4) == INVALID
+    assert call(k=0) == INVALID
+    assert call(qb=48) == SHAPE
+    assert call(wext=PM) == ALIGN
+    assert call(wsb=16) == WS
+
+
 def test_no_device_is_reported_not_crashed(lib):
     """Valid arguments on a machine without a GPU give NO_DEVICE."""
     import torch
@@ -187,6 +208,8 @@ def test_no_device_is_reported_not_crashed(lib):
     assert lib.larosa_threshold_layer_forward(P, 1, P, 64, P, 1, 1, 128, 64, 0.5, P, None, None,
                                               None, 0, P, 1 << 30, None) == NODEV
     assert lib.larosa_calibrate_threshold(P, 100, 10, P, P, 1 << 16, None) == NODEV
+    assert lib.larosa_lowrank_layer_forward(P, 1, P, 64, P, P, 16, 1, 1, 128, 64, 32, P, None,
+                                            None, 0, P, 1 << 30, None) == NODEV
     assert lib.larosa_rotate_fp64(P, 1, P, 64, 1, P + (1 << 20), 1, 128, None) == NODEV
     assert lib.larosa_swiglu(P, P + (1 << 20), 1, 64, 1, None) == NODEV
     assert lib.larosa_topk_gemv(P, 128, 10, P, 1, P, 1, 64, None, P, 1 << 20, None) == NODEV

@@ -1,0 +1,114 @@
+"""GPU parity of the low-rank compensated layer (R-Sparse-style
+y = xs·W' + (x_rot − xs)·A_r·B_r on the method's Top-K selection) against the
+oracle, teacher-forced on the GPU's rotated input, folded weight and stored
+factors, with the method's tolerances (see test_gpu_parity)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import larosa_ref as ref
+from rotated_top_activation_amd import _lib
+from rotated_top_activation_amd import workloads as wl
+from rotated_top_activation_amd.device import RotatedLinear
+
+from gpu_helpers import dev, guarded, host, host_f32
+
+pytestmark = pytest.mark.gpu
+
+
+def _factors(lin, r):
+    """A_r [d_in, r] and W_ext = [W'; B_r] on the device, in the weight dtype
+    (the oracle's SVD of the GPU's folded weight, rounded once)."""
+    a, b = ref.lowrank_factors(host(lin.Wf), r)
+    a_d = dev(ref.round_to(a, lin.dtype), lin.dtype)
+    b_d = dev(ref.round_to(b, lin.dtype), lin.dtype)
+    return a_d, torch.cat([lin.Wf, b_d], dim=0).contiguous()
+
+
+def _run(lin, x, r, a_d, w_ext, mode=_lib.UNFUSED):
+    B = x.shape[0]
+    tdt = torch.float32 if lin.dtype == "f32" else torch.bfloat16
+    y, ok_y = guarded((B, lin.d_out), tdt)
+    idx, ok_i = guarded((B, lin.k), torch.int32, fill=-3)
+    xr = torch.empty((B, lin.d_in), dtype=torch.float32, device="cuda")
+    nbytes = _lib.larosa_lowrank_workspace_bytes(B, lin.d_in, lin.d_out, lin.k, r)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    x_d = dev(x, lin.dtype)
+    _lib.larosa_lowrank_layer_forward(x_d, lin.Qt, lin.q_block, w_ext, a_d, r, B, lin.d_in,
+                                      lin.d_out, lin.k, y, idx_out=idx, xrot_out=xr, mode=mode,
+                                      ws=ws)
+    y2 = torch.empty_like(y)
+    _lib.larosa_lowrank_layer_forward(x_d, lin.Qt, lin.q_block, w_ext, a_d, r, B, lin.d_in,
+                                      lin.d_out, lin.k, y2, mode=mode, ws=ws)
+    torch.cuda.synchronize()
+    assert ok_y() and ok_i()
+    assert torch.equal(y, y2), "two runs differ"
+    return host(y), host_f32(xr), host(idx)
+
+
+def _check(lin, x, r, tol, mode=_lib.UNFUSED):
+    a_d, w_ext = _factors(lin, r)
+    y, xr, idx = _run(lin, x, r, a_d, w_ext, mode)
+    want_idx = ref.select(xr, lin.k)
+    np.testing.assert_array_equal(idx, want_idx)
+    want = ref.round_to(ref.lowrank_compensated_product(xr, want_idx, host(lin.Wf), host(a_d),
+                                                        host(w_ext)[lin.d_in:]), lin.dtype)
+    err = ref.rel_error(y, want)
+    assert err <= tol, err
+    return y, xr
+
+
+CASES = [
+    # (d_in, q_block, d_out, B, sparsity %, r): B = 1 runs the vector
+    # product over the kept rows plus r; B >= 2 in bf16 the matrix-core one
+    (4096, 4096, 1032, 1, 40, 64), (4096, 4096, 22016, 1, 40, 64),
+    (11008, 2752, 4096, 1, 40, 128), (4096, 4096, 1032, 4, 40, 32),
+    (2048, 512, 4104, 40, 25, 256), (1024, 256, 1032, 16, 50, 1), (1024, 256, 520, 2, 50, 200),
+]
+
+
+@pytest.mark.parametrize("d,qb,n,B,sp,r", CASES)
+def test_lowrank_layer_parity(d, qb, n, B, sp, r):
+    case = wl.LinearCase(cfg=3, batch=B, d_in=d, d_out=n, q_block=qb, sparsity_pct=sp,
+                         dtype="bf16", role="o_in")
+    x, q, w = wl.linear_case_inputs(case, w_std=0.02)
+    lin = RotatedLinear(q, w, "bf16", case.k)
+    _check(lin, x, r, 2e-2)
+
+
+@pytest.mark.parametrize("B", [1, 3])
+def test_lowrank_layer_parity_f32(B):
+    case, x, q, w = wl.single_linear_f32(batch=B)
+    lin = RotatedLinear(q, w, "f32", case.k)
+    _check(lin, x, 100, 1e-5)
+
+
+def test_lowrank_layer_with_fp64_rotation():
+    case = wl.LinearCase(cfg=3, batch=2, d_in=4096, d_out=1032, q_block=4096, sparsity_pct=40,
+                         dtype="bf16", role="down_in")
+    x, q, w = wl.linear_case_inputs(case, w_std=0.02)
+    lin = RotatedLinear(q, w, "bf16", case.k)
+    _, xr = _check(lin, x, 48, 2e-2, mode=_lib.FUSED | _lib.ROTATE_FP64)
+    np.testing.assert_array_equal(xr, ref.rotate(x, q))
+
+
+def test_lowrank_recovers_a_low_rank_weight():
+    """With W' of rank 32, rank-32 compensation reproduces the dense x·W'
+    although 40% of the rotated channels are dropped; the plain sparse layer
+    does not."""
+    d, n, B, r = 2048, 1032, 2, 32
+    case = wl.LinearCase(cfg=3, batch=B, d_in=d, d_out=n, q_block=d, sparsity_pct=40,
+                         dtype="bf16", role="mlp_in")
+    x, q, _ = wl.linear_case_inputs(case, w_std=0.02)
+    rng = np.random.default_rng(12)
+    w = wl.quantize((rng.standard_normal((d, r)) @ rng.standard_normal((r, n))) * 0.004, "bf16")
+    lin = RotatedLinear(q, w, "bf16", case.k)
+    y_lr, xr = _check(lin, x, r, 2e-2)
+    dense = ref.round_to(xr.astype(np.float64) @ host(lin.Wf), "bf16")
+    y_plain = torch.empty((B, n), dtype=torch.bfloat16, device="cuda")
+    lin.forward(dev(x, "bf16"), y_plain, lin.workspace(B))
+    torch.cuda.synchronize()
+    err_lr = ref.rel_error(y_lr, dense)
+    err_plain = ref.rel_error(host(y_plain), dense)
+    print(f"rel. error vs dense: plain sparse {err_plain:.3e}, rank-{r} compensated {err_lr:.3e}")
+    assert err_lr <= 3e-2 and err_plain > 10 * err_lr
