@@ -286,6 +286,7 @@ def main():
 
     thr = threshold_mlp(a, case, x_d, l1, l2, qt1, wil1, qt2, wf2, copies, h, y, timed, gbs)
     lowr = lowrank_gate_up(a, case, x_d, l1, qt1, wf1, copies, timed, gbs)
+    sweep = q2_block_sweep(a, case, wd, l1, x_d, qt1, wil1, copies, h, y, timed, gbs)
 
     q_bytes = (l1.Qt.numel() + l2.Qt.numel()) * 2
     sparse_bytes = q_bytes + (case.k1 * 2 * f + case.k2 * d) * 2
@@ -354,6 +355,7 @@ def main():
             "rotation_fp32_vs_fp64": exact_rot,
             "threshold_select": thr,
             "lowrank_compensation": lowr,
+            "q2_block_sweep": sweep,
             "kernels": {k: {"achieved_GBs": round(v["achieved"], 1), "bytes_per_launch": v["bytes"],
                             "avg_us": round(v["us"], 3), "frac": round(v["achieved"] / HBM_PEAK_GBS, 4),
                             "traffic": measured_traffic(k)} for k, v in kernels.items()},
@@ -475,6 +477,64 @@ def threshold_mlp(a, case, x_d, l1, l2, qt1, wil1, qt2, wf2, copies, h, y, timed
                         "max": int(c2.max()), "top_k": case.k2},
         },
     }
+
+
+def q2_block_sweep(a, case, wd, l1, x_d, qt1, wil1, copies, h, y, timed, gbs,
+                   blocks=(256, 688, 1376, 2752, 5504, 11008)):
+    """The one-token MLP step with the down projection's rotation Q2 made of
+    f / b independent b×b Haar blocks, for block widths b that divide f =
+    11008 (the pages allow any orthogonal rotation, random or learned): the
+    Q2 bytes fall as b shrinks. Q2 drawn on the device (QR of a seeded N(0,1)
+    matrix, sign-fixed), folded into the same W_down; three copies per point
+    so the on-package cache serves none of a step's reads."""
+    import torch
+    from rotated_top_activation_amd import _lib
+    from rotated_top_activation_amd.device import RotatedLinear
+    dev = x_d.device
+    d, f = case.d, case.f
+    gen = torch.Generator(device=dev)
+    ws1 = torch.zeros(_lib.larosa_swiglu_workspace_bytes(1, d, f, case.k1, _lib.UNFUSED),
+                      dtype=torch.uint8, device=dev)
+    w_down = None
+    out = {}
+    for b in blocks:
+        if f % b:
+            continue
+        gen.manual_seed(1000 + b)
+        lins = []
+        for _ in range(3):
+            q = _dev_haar(gen, b, f // b, dev)
+            if w_down is None:
+                w_down = wl_to_dev(wd)
+            lins.append(RotatedLinear(q, w_down, "bf16", case.k2, keep_w=False))
+        ws2 = torch.zeros(_lib.larosa_workspace_bytes(1, f, d, case.k2, _lib.UNFUSED),
+                          dtype=torch.uint8, device=dev)
+        xr2 = torch.empty((1, f), dtype=torch.float32, device=dev)
+
+        def step(i, lins=lins, ws2=ws2, b=b):
+            c = i % copies
+            _lib.larosa_swiglu_layer_forward(x_d, qt1[c], l1.q_block, wil1[c], 1, d, f, case.k1,
+                                             h, ws=ws1)
+            l2 = lins[i % 3]
+            _lib.larosa_layer_forward(h, l2.Qt, b, l2.Wf, 1, f, d, case.k2, y, ws=ws2)
+        ms = timed(step, a.steps, a.warmup)
+        rot = timed(lambda i, lins=lins, b=b: _lib.larosa_rotate(h, lins[i % 3].Qt, b, xr2, 1, f),
+                    a.steps, a.warmup)
+        q_bytes = l1.Qt.numel() * 2 + f * b * 2
+        sparse = q_bytes + (case.k1 * 2 * f + case.k2 * d) * 2
+        dense = (d * 2 * f + f * d) * 2
+        out[str(b)] = {"step_ms": round(ms, 5), "tokens_per_s": round(1.0 / (ms * 1e-3), 1),
+                       "rotate2_us": round(rot * 1e3, 2), "q2_bytes": f * b * 2,
+                       "step_bytes": sparse, "step_GBs": round(gbs(sparse, ms), 1),
+                       "dense_over_sparse_bytes": round(dense / sparse, 3)}
+        del lins
+        torch.cuda.empty_cache()
+    return out
+
+
+def wl_to_dev(w):
+    from rotated_top_activation_amd import workloads as wl
+    return wl.to_torch(w, "bf16")
 
 
 def lowrank_gate_up(a, case, x_d, l1, qt1, wf1, copies, timed, gbs, r=64):

@@ -124,6 +124,34 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void rotate_row_kernel(
   if (lane == 0) x_rot[j] = sum;
 }
 
+// One token, short rotation blocks (a row of Qt is at most LPR 16-byte
+// chunks, LPR <= 32): each wave computes 64 / LPR output channels, LPR lanes
+// per channel, so every lane has a chunk to load; the lane groups are summed
+// with xor shuffles inside the group (a fixed order).
+template <int LPR, typename T>
+__global__ __launch_bounds__(kWavesPerBlock * kWave) void rotate_rows_short_kernel(
+    const T *__restrict__ x, const T *__restrict__ qt, float *__restrict__ x_rot, int d,
+    int qb) {
+  constexpr int V = Elt<T>::kVec;
+  constexpr int RPW = kWave / LPR;
+  const int lane = threadIdx.x % kWave;
+  const int j = (blockIdx.x * kWavesPerBlock + wave_id()) * RPW + lane / LPR;
+  const int c = lane % LPR;
+  const bool ok = j < d && c < qb / V;
+  float acc = 0.f;
+  if (ok) {
+    const int64_t xoff = static_cast<int64_t>(j / qb) * qb;
+    float xf[V], qf[V];
+    Elt<T>::unpack(load16(x + xoff + c * V), xf);
+    Elt<T>::unpack(load16(qt + static_cast<int64_t>(j) * qb + c * V), qf);
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc = fmaf(xf[v], qf[v], acc);
+  }
+#pragma unroll
+  for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, kWave);
+  if (c == 0 && j < d) x_rot[j] = acc;
+}
+
 template <typename T>
 bool launch_row(const void *x, const void *qt, float *x_rot, int d, int qb, hipStream_t s) {
   constexpr int V = Elt<T>::kVec;
@@ -131,6 +159,16 @@ bool launch_row(const void *x, const void *qt, float *x_rot, int d, int qb, hipS
   const dim3 grid((d + kWavesPerBlock - 1) / kWavesPerBlock), block(kWavesPerBlock * kWave);
   const auto *xp = static_cast<const T *>(x);
   const auto *qp = static_cast<const T *>(qt);
+  const int chunks = qb / V;
+  if (chunks <= 32) {
+    const int lpr = chunks <= 8 ? 8 : (chunks <= 16 ? 16 : 32);
+    const int per_block = kWavesPerBlock * (kWave / lpr);
+    const dim3 g((d + per_block - 1) / per_block);
+    if (lpr == 8) hipLaunchKernelGGL((rotate_rows_short_kernel<8, T>), g, block, 0, s, xp, qp, x_rot, d, qb);
+    else if (lpr == 16) hipLaunchKernelGGL((rotate_rows_short_kernel<16, T>), g, block, 0, s, xp, qp, x_rot, d, qb);
+    else hipLaunchKernelGGL((rotate_rows_short_kernel<32, T>), g, block, 0, s, xp, qp, x_rot, d, qb);
+    return true;
+  }
   if (nc <= 2) hipLaunchKernelGGL((rotate_row_kernel<2, T>), grid, block, 0, s, xp, qp, x_rot, d, qb);
   else if (nc <= 4) hipLaunchKernelGGL((rotate_row_kernel<4, T>), grid, block, 0, s, xp, qp, x_rot, d, qb);
   else if (nc <= 8) hipLaunchKernelGGL((rotate_row_kernel<8, T>), grid, block, 0, s, xp, qp, x_rot, d, qb);

@@ -118,6 +118,10 @@ ROTATE_CASES = [
     # batches of 16 and more in bf16 take the matrix-core form
     ("bf16", "bf16", 4096, 4096, 16), ("bf16", "bf16", 11008, 2752, 33),
     ("bf16", "bf16", 8192, 8192, 64), ("bf16", "bf16", 1152, 96, 17),
+    # one token, short blocks: several output channels per wave (8, 16 or 32
+    # lanes each, the last with idle lanes)
+    ("bf16", "bf16", 11008, 256, 1), ("bf16", "bf16", 1024, 64, 1), ("f32", "f32", 512, 64, 1),
+    ("bf16", "bf16", 1152, 96, 1), ("f32", "f32", 384, 128, 1), ("bf16", "bf16", 11008, 344, 1),
 ]
 
 
