@@ -113,14 +113,18 @@ __device__ __forceinline__ void radix_count(uint32_t key, int pass, uint32_t pre
   if ((key & pmask) == prefix)
     atomicAdd(&sm.hist[pad_bin(static_cast<int>((key >> radix_shift(pass)) & radix_dmask(pass)))], 1u);
 }
+// With clear_hist the histogram is also zeroed (before the closing barrier),
+// ready for the next pass's counts.
 template <int NT>
 __device__ __forceinline__ uint32_t radix_resolve(int pass, uint32_t &prefix, uint32_t &pmask,
-                                                  uint32_t &krem, SelectSmem<NT> &sm) {
+                                                  uint32_t &krem, SelectSmem<NT> &sm,
+                                                  bool clear_hist = false) {
   suffix_search<NT>(krem, sm);
   prefix |= sm.bin << radix_shift(pass);
   pmask |= radix_dmask(pass) << radix_shift(pass);
   krem -= sm.above;
   const uint32_t count = sm.count;
+  if (clear_hist) radix_clear<NT>(sm);
   __syncthreads();  // bin / above are rewritten by the next pass
   return count;
 }
@@ -297,7 +301,8 @@ __device__ __forceinline__ RuleState rule_first_digit(const uint32_t (&key)[EMAX
   }
   __syncthreads();
   RuleState st{0u, kNoKey, k, 0u};
-  st.n_cand = radix_resolve<NT>(0, st.prefix, st.pmask, st.krem, sm);
+  // the histogram comes back cleared for rule_finish's second digit
+  st.n_cand = radix_resolve<NT>(0, st.prefix, st.pmask, st.krem, sm, true);
   return st;
 }
 
@@ -311,7 +316,6 @@ __device__ __forceinline__ void rule_finish(const uint32_t (&key)[EMAX], int E, 
   const int t = threadIdx.x;
   uint32_t prefix = st.prefix, pmask = st.pmask, krem = st.krem;
   const uint32_t n_cand = st.n_cand;
-  const uint32_t digit0 = prefix >> radix_shift(0);
   if (n_cand > static_cast<uint32_t>(kCandMax)) {
     // many equal first digits (tie-heavy data): the later digits on the slots
     uint32_t n_eq;
@@ -319,55 +323,64 @@ __device__ __forceinline__ void rule_finish(const uint32_t (&key)[EMAX], int E, 
     cut = tie_cutoff<NT, EMAX>(key, i0, T, krem, sm);
     return;
   }
-  // compact the candidates in index order; an empty slot has first digit 0x800
+  // The second digit straight from the slots (sm.hist arrives cleared from
+  // rule_first_digit): no candidate list is needed in the usual case.
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e)
+    if (e < E) radix_count<NT>(key[e], 1, prefix, pmask, sm);
+  __syncthreads();
+  const uint32_t in_bin = radix_resolve<NT>(1, prefix, pmask, krem, sm);
+  if (in_bin == 1) {
+    // One channel carries the boundary's first two digits (the usual case):
+    // its key is T and no other channel has that key, so it is the last one
+    // kept (krem == 1) and the third digit and the tie cut-off are not needed.
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) {
+      if (e < E && (key[e] & pmask) == prefix) {
+        sm.bin = key[e];
+        sm.above = static_cast<uint32_t>(i0 + e);
+      }
+    }
+    __syncthreads();
+    T = sm.bin;
+    cut = sm.above;
+    __syncthreads();
+    return;
+  }
+  // Otherwise the channels with these two digits, compacted in index order
+  // (at most n_cand <= kCandMax of them), take the third digit and the cut.
   uint32_t nc = 0;
 #pragma unroll
   for (int e = 0; e < EMAX; ++e)
-    if (e < E) nc += (key[e] >> radix_shift(0)) == digit0;
+    if (e < E) nc += (key[e] & pmask) == prefix;
+  uint32_t n2;
   {
-    uint32_t p = block_incl_scan<NT>(nc, sm.wave_tot) - nc;
+    const uint32_t incl = block_incl_scan<NT>(nc, sm.wave_tot);
+    uint32_t p = incl - nc;
 #pragma unroll
     for (int e = 0; e < EMAX; ++e) {
-      if (e < E && (key[e] >> radix_shift(0)) == digit0) {
+      if (e < E && (key[e] & pmask) == prefix) {
         cs.key[p] = key[e];
         cs.idx[p] = static_cast<uint32_t>(i0 + e);
         ++p;
       }
     }
+    if (t == NT - 1) sm.count = incl;
   }
+  radix_clear<NT>(sm);
   __syncthreads();
-  // the later digits over the candidates
-  for (int pass = 1; pass < 3; ++pass) {
-    radix_clear<NT>(sm);
-    __syncthreads();
-    for (int j = t; j < static_cast<int>(n_cand); j += NT) radix_count<NT>(cs.key[j], pass, prefix, pmask, sm);
-    __syncthreads();
-    const uint32_t in_bin = radix_resolve<NT>(pass, prefix, pmask, krem, sm);
-    if (pass == 1 && in_bin == 1) {
-      // One candidate carries the boundary's first two digits (the usual
-      // case): its key is T and no other channel has that key, so it is the
-      // last one kept (krem == 1) and the third digit and the tie cut-off are
-      // not needed.
-      for (int j = t; j < static_cast<int>(n_cand); j += NT) {
-        if ((cs.key[j] & pmask) == prefix) {
-          sm.bin = cs.key[j];
-          sm.above = cs.idx[j];
-        }
-      }
-      __syncthreads();
-      T = sm.bin;
-      cut = sm.above;
-      __syncthreads();
-      return;
-    }
-  }
+  n2 = sm.count;
+  for (int j = t; j < static_cast<int>(n2); j += NT) radix_count<NT>(cs.key[j], 2, prefix, pmask, sm);
+  __syncthreads();
+  radix_resolve<NT>(2, prefix, pmask, krem, sm);
+  const uint32_t n_cand2 = n2;
   T = prefix;
   // the krem-th candidate equal to T in index order is the last one kept
   uint32_t eq = 0;
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     const int j = t * CPT + c;
-    eq += j < static_cast<int>(n_cand) && cs.key[j] == T;
+    eq += j < static_cast<int>(n_cand2) && cs.key[j] == T;
   }
   const uint32_t incl = block_incl_scan<NT>(eq, sm.wave_tot);
   uint32_t before = incl - eq;
@@ -375,7 +388,7 @@ __device__ __forceinline__ void rule_finish(const uint32_t (&key)[EMAX], int E, 
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int j = t * CPT + c;
-      if (j < static_cast<int>(n_cand) && cs.key[j] == T) {
+      if (j < static_cast<int>(n_cand2) && cs.key[j] == T) {
         ++before;
         if (before == krem) sm.bin = cs.idx[j];
       }
