@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define LAROSA_ABI_VERSION 5
+#define LAROSA_ABI_VERSION 6
 
 typedef void *larosa_stream_t; /* hipStream_t */
 
@@ -368,18 +368,26 @@ int larosa_rope(const void *qk, int64_t qk_stride, void *q_out, void *k_out, int
                 int64_t n_heads, int64_t n_kv_heads, int64_t d_head, int64_t pos, float theta,
                 int dtype, larosa_stream_t stream);
 
+/* Workspace bytes of larosa_decode_attention (per-chunk partial results of
+ * 256 positions); 0 for invalid sizes. */
+size_t larosa_decode_attention_workspace_bytes(int64_t B, int64_t T, int64_t n_heads);
+
 /* Single-query softmax attention of every query head over its key/value
  * head's T cached positions plus the new token's own key and value:
  *   out[b, h] = Σ_t softmax_t(q[b,h]·k_t / sqrt(d_head)) · v_t,
  * with key/value head h / (n_heads / n_kv_heads). q, out: [B, n_heads·128];
  * the new key and value of token b start at k_new + b·k_stride and
  * v_new + b·v_stride (n_kv_heads·128 channels each); caches are
- * [B, n_kv_heads, T, 128] (head-major). d_head must be 128; T <= 16384. */
+ * [B, n_kv_heads, T, 128] (head-major). d_head must be 128; T <= 16384.
+ * The positions are taken in chunks of 256 whose partial softmax results
+ * are combined in chunk order (deterministic); ws: at least
+ * larosa_decode_attention_workspace_bytes(B, T, n_heads) bytes, 16-byte
+ * aligned, overwritten by each call. */
 int larosa_decode_attention(const void *q, const void *k_new, int64_t k_stride,
                             const void *v_new, int64_t v_stride, const void *k_cache,
                             const void *v_cache, void *out, int64_t B, int64_t T,
                             int64_t n_heads, int64_t n_kv_heads, int64_t d_head, int dtype,
-                            larosa_stream_t stream);
+                            void *ws, size_t ws_bytes, larosa_stream_t stream);
 
 /* Residual add in place: h[i] = h[i] + o[i] for i < n. */
 int larosa_residual_add(void *h, const void *o, int64_t n, int dtype, larosa_stream_t stream);

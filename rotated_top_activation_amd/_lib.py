@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblarosa.s
 F32, BF16 = 0, 1
 UNFUSED, FUSED = 0, 1
 ROTATE_FP64 = 2  # mode flag: fp64-accumulating rotation, OR-ed into UNFUSED or FUSED
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 _c_i64 = ctypes.c_int64
 _c_int = ctypes.c_int
@@ -75,8 +75,10 @@ SIGNATURES = {
     "larosa_rmsnorm": (_c_int, [_c_vp, _c_vp, _c_i64, _c_i64, ctypes.c_float, _c_int, _c_vp]),
     "larosa_rope": (_c_int, [_c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                              ctypes.c_float, _c_int, _c_vp]),
+    "larosa_decode_attention_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64]),
     "larosa_decode_attention": (_c_int, [_c_vp, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp, _c_vp, _c_vp,
-                                         _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_int, _c_vp]),
+                                         _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_int, _c_vp,
+                                         _c_sz, _c_vp]),
     "larosa_residual_add": (_c_int, [_c_vp, _c_vp, _c_i64, _c_int, _c_vp]),
 }
 
@@ -312,13 +314,18 @@ def larosa_rope(qk, qk_stride: int, q_out, k_out, B: int, n_heads: int, n_kv_hea
                                              _stream(stream)))
 
 
+def larosa_decode_attention_workspace_bytes(B: int, T: int, n_heads: int) -> int:
+    return int(load().larosa_decode_attention_workspace_bytes(B, T, n_heads))
+
+
 def larosa_decode_attention(q, k_new, k_stride: int, v_new, v_stride: int, k_cache, v_cache,
                             out, B: int, T: int, n_heads: int, n_kv_heads: int,
-                            d_head: int = 128, stream=None) -> None:
+                            d_head: int = 128, ws=None, stream=None) -> None:
     _check("larosa_decode_attention",
            load().larosa_decode_attention(_ptr(q), _ptr(k_new), k_stride, _ptr(v_new), v_stride,
                                           _ptr(k_cache), _ptr(v_cache), _ptr(out), B, T, n_heads,
-                                          n_kv_heads, d_head, _dt(q), _stream(stream)))
+                                          n_kv_heads, d_head, _dt(q), _ptr(ws), _nbytes(ws),
+                                          _stream(stream)))
 
 
 def larosa_residual_add(h, o, n: int, stream=None) -> None:

@@ -892,11 +892,16 @@ int larosa_rope(const void *qk, int64_t qk_stride, void *q_out, void *k_out, int
                               static_cast<double>(theta), dtype, stream_of(stream)));
 }
 
+size_t larosa_decode_attention_workspace_bytes(int64_t B, int64_t T, int64_t n_heads) {
+  if (B < 1 || B > kMaxB || T < 0 || T > 16384 || n_heads < 1) return 0;
+  return decode_attention_ws_bytes(B, T, n_heads);
+}
+
 int larosa_decode_attention(const void *q, const void *k_new, int64_t k_stride,
                             const void *v_new, int64_t v_stride, const void *k_cache,
                             const void *v_cache, void *out, int64_t B, int64_t T,
                             int64_t n_heads, int64_t n_kv_heads, int64_t d_head, int dtype,
-                            larosa_stream_t stream) {
+                            void *ws, size_t ws_bytes, larosa_stream_t stream) {
   if (!dtype_ok(dtype)) return LAROSA_ERR_DTYPE;
   if (B < 0 || B > kMaxB || T < 0 || n_heads < 1 || n_kv_heads < 1) return LAROSA_ERR_INVALID_ARG;
   if (d_head != 128 || n_heads % n_kv_heads || T > 16384) return LAROSA_ERR_SHAPE;
@@ -907,11 +912,12 @@ int larosa_decode_attention(const void *q, const void *k_new, int64_t k_stride,
   if (!q || !k_new || !v_new || !out || (T > 0 && (!k_cache || !v_cache)))
     return LAROSA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
-      !aligned16(v_cache) || !aligned16(out))
+      !aligned16(v_cache) || !aligned16(out) || !aligned16(ws))
     return LAROSA_ERR_ALIGNMENT;
+  if (!ws || ws_bytes < decode_attention_ws_bytes(B, T, n_heads)) return LAROSA_ERR_WORKSPACE;
   if (int st = device_status()) return st;
   return launched(launch_decode_attention(q, k_new, k_stride, v_new, v_stride, k_cache, v_cache,
-                                          out, B, T, n_heads, n_kv_heads, dtype,
+                                          out, B, T, n_heads, n_kv_heads, dtype, ws,
                                           stream_of(stream)));
 }
 

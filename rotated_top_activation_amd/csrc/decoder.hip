@@ -87,16 +87,11 @@ __global__ __launch_bounds__(kGT) void rope_kernel(const T *__restrict__ qk, int
 // One workgroup per (query head, token). The cache is [B, n_kv, T, 128];
 // the new token's key and value sit at k_new + b·k_stride + kv·128 and
 // v_new + b·v_stride + kv·128.
-// Single-query attention, one 1024-thread workgroup per (token, head). A key
-// or value row (one position's 128 channels) is read by LPR lanes with
-// 16-byte loads, so one wave instruction covers 64/LPR rows; the 16 waves
-// take interleaved row groups and keep kAttBatch instructions in flight.
-// Pass 1 writes the scores of the T cached positions and the new one to LDS;
-// then one max and one sum of the exponentials; pass 2 accumulates p·v per
-// lane and folds the row slots and the waves.
-constexpr int kAT = 1024;
-constexpr int kAW = kAT / kWave;
-constexpr int kAttBatch = 8;
+// Single-query attention. A key or value row (one position's 128 channels)
+// is read by LPR lanes with 16-byte loads, so one wave instruction covers
+// 64/LPR rows. The scores go to LDS; then one max and one sum of the
+// exponentials; then p·v accumulates per lane and the row slots and the
+// waves are folded.
 
 template <int NW>
 __device__ __forceinline__ float block_sum_w(float v, float *red) {
@@ -125,20 +120,33 @@ __device__ __forceinline__ float block_max_w(float v, float *red) {
   return m;
 }
 
+// The positions are cut into chunks of kACh, one 256-thread workgroup per
+// (token, head, chunk), so a single token still spreads its heads' cache
+// reads over the whole chip (32 heads × 33 chunks at T = 2048), and a wave
+// issues all its key and value loads before using any (one memory round
+// trip per chunk). A chunk
+// writes its own maximum score m, Σ exp(s − m) and Σ exp(s − m)·v; a second
+// kernel rescales the chunks to the common maximum and adds them in chunk
+// order (softmax over the union of the chunks, deterministic).
+constexpr int kACT = 256;
+constexpr int kACW = kACT / kWave;
+constexpr int kACh = 64;  // positions per chunk: every key and value load of a wave in flight at once
+
 template <typename T>
-__global__ __launch_bounds__(kAT) void decode_attention_kernel(
+__global__ __launch_bounds__(kACT) void attn_chunk_kernel(
     const T *__restrict__ q, const T *__restrict__ k_new, int64_t k_stride,
     const T *__restrict__ v_new, int64_t v_stride, const T *__restrict__ kc,
-    const T *__restrict__ vc, T *__restrict__ out, int Tlen, int n_heads, int n_kv) {
+    const T *__restrict__ vc, float *__restrict__ part_m, float *__restrict__ part_l,
+    float *__restrict__ part_o, int Tlen, int n_heads, int n_kv, int S) {
   constexpr int DH = 128;
   constexpr int V = Elt<T>::kVec;      // channels per 16-byte load
   constexpr int LPR = DH / V;          // lanes per row
   constexpr int RPI = kWave / LPR;     // rows per wave instruction
-  constexpr int ROWS = RPI * kAW;      // rows per round of the workgroup
-  extern __shared__ float sc[];        // [Tlen + 1] scores, then p
-  __shared__ float red[kAW];
-  __shared__ float accs[kAW][DH];
-  const int h = blockIdx.x, b = blockIdx.y;
+  constexpr int ROWS = RPI * kACW;     // rows per round of the workgroup
+  __shared__ float sc[kACh];           // the chunk's scores, then p
+  __shared__ float red[kACW];
+  __shared__ float accs[kACW][DH];
+  const int h = blockIdx.x / S, ci = blockIdx.x % S, b = blockIdx.y;
   const int g = h / (n_heads / n_kv);
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int slot = lane / LPR, c = lane % LPR;
@@ -147,69 +155,64 @@ __global__ __launch_bounds__(kAT) void decode_attention_kernel(
   const T *kn = k_new + b * k_stride + static_cast<int64_t>(g) * DH;
   const T *vn = v_new + b * v_stride + static_cast<int64_t>(g) * DH;
   const int n = Tlen + 1;  // positions, the new token last
+  const int t0 = ci * kACh;
+  const int t1 = t0 + kACh < n ? t0 + kACh : n;  // S = ceil(n / kACh): never empty
   auto row_of = [&](const T *base, const T *nw, int t) {
     return t < Tlen ? base + static_cast<int64_t>(t) * DH : nw;
   };
-  // this lane's query channels
   float qf[V];
   Elt<T>::unpack(load16(q + (static_cast<int64_t>(b) * n_heads + h) * DH + c * V), qf);
   const float scale = 1.0f / sqrtf(static_cast<float>(DH));
 
-  // pass 1: scores
+  // every key and value row of this wave's share of the chunk, loaded at once
+  constexpr int NI = kACh / ROWS;  // wave instructions per pass (4 bf16, 8 fp32)
+  static_assert(NI * ROWS == kACh, "chunk must be whole rounds");
+  uint4 kq[NI], vq[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int t = t0 + wave * RPI + i * ROWS + slot;
+    const bool ok = t < t1;
+    kq[i] = ok ? load16(row_of(kbase, kn, t) + c * V) : make_uint4(0, 0, 0, 0);
+    vq[i] = ok ? load16(row_of(vbase, vn, t) + c * V) : make_uint4(0, 0, 0, 0);
+  }
+  // scores
   float mx = -INFINITY;
-  for (int r0 = wave * RPI; r0 < n; r0 += ROWS * kAttBatch) {
-    uint4 kq[kAttBatch];
 #pragma unroll
-    for (int i = 0; i < kAttBatch; ++i) {
-      const int t = r0 + i * ROWS + slot;
-      kq[i] = t < n ? load16(row_of(kbase, kn, t) + c * V) : make_uint4(0, 0, 0, 0);
-    }
+  for (int i = 0; i < NI; ++i) {
+    float kf[V];
+    Elt<T>::unpack(kq[i], kf);
+    float sdot = 0.f;
 #pragma unroll
-    for (int i = 0; i < kAttBatch; ++i) {
-      float kf[V];
-      Elt<T>::unpack(kq[i], kf);
-      float s = 0.f;
+    for (int v = 0; v < V; ++v) sdot = fmaf(qf[v], kf[v], sdot);
 #pragma unroll
-      for (int v = 0; v < V; ++v) s = fmaf(qf[v], kf[v], s);
-#pragma unroll
-      for (int off = LPR / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, kWave);
-      const int t = r0 + i * ROWS + slot;
-      if (t < n) {
-        s *= scale;
-        if (c == 0) sc[t] = s;
-        mx = fmaxf(mx, s);
-      }
+    for (int off = LPR / 2; off >= 1; off >>= 1) sdot += __shfl_xor(sdot, off, kWave);
+    const int t = t0 + wave * RPI + i * ROWS + slot;
+    if (t < t1) {
+      sdot *= scale;
+      if (c == 0) sc[t - t0] = sdot;
+      mx = fmaxf(mx, sdot);
     }
   }
-  mx = block_max_w<kAW>(mx, red);  // its barriers also order the sc[] writes
+  mx = block_max_w<kACW>(mx, red);  // its barriers also order the sc[] writes
   float sum = 0.f;
-  for (int t = threadIdx.x; t < n; t += kAT) {
+  for (int t = threadIdx.x; t < t1 - t0; t += kACT) {
     const float p = expf(sc[t] - mx);
     sc[t] = p;
     sum += p;
   }
-  sum = block_sum_w<kAW>(sum, red);
-
-  // pass 2: Σ p·v, V channels per lane for its row slot
+  sum = block_sum_w<kACW>(sum, red);
+  // Σ p·v, V channels per lane for its row slot
   float acc[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) acc[v] = 0.f;
-  for (int r0 = wave * RPI; r0 < n; r0 += ROWS * kAttBatch) {
-    uint4 vq[kAttBatch];
 #pragma unroll
-    for (int i = 0; i < kAttBatch; ++i) {
-      const int t = r0 + i * ROWS + slot;
-      vq[i] = t < n ? load16(row_of(vbase, vn, t) + c * V) : make_uint4(0, 0, 0, 0);
-    }
+  for (int i = 0; i < NI; ++i) {
+    const int t = t0 + wave * RPI + i * ROWS + slot;
+    const float p = t < t1 ? sc[t - t0] : 0.f;
+    float vf[V];
+    Elt<T>::unpack(vq[i], vf);
 #pragma unroll
-    for (int i = 0; i < kAttBatch; ++i) {
-      const int t = r0 + i * ROWS + slot;
-      const float p = t < n ? sc[t] : 0.f;
-      float vf[V];
-      Elt<T>::unpack(vq[i], vf);
-#pragma unroll
-      for (int v = 0; v < V; ++v) acc[v] = fmaf(p, vf[v], acc[v]);
-    }
+    for (int v = 0; v < V; ++v) acc[v] = fmaf(p, vf[v], acc[v]);
   }
   // fold the row slots (lanes c, c + LPR, …), then the waves
 #pragma unroll
@@ -221,13 +224,39 @@ __global__ __launch_bounds__(kAT) void decode_attention_kernel(
     for (int v = 0; v < V; ++v) accs[wave][c * V + v] = acc[v];
   }
   __syncthreads();
-  T *orow = out + (static_cast<int64_t>(b) * n_heads + h) * DH;
-  for (int i = threadIdx.x; i < DH; i += kAT) {
-    float s = 0.f;
+  const int64_t pi = (static_cast<int64_t>(b) * n_heads + h) * S + ci;
+  for (int i = threadIdx.x; i < DH; i += kACT) {
+    float o = 0.f;
 #pragma unroll
-    for (int w = 0; w < kAW; ++w) s += accs[w][i];
-    Elt<T>::store(orow, i, s / sum);
+    for (int w = 0; w < kACW; ++w) o += accs[w][i];
+    part_o[pi * DH + i] = o;
   }
+  if (threadIdx.x == 0) {
+    part_m[pi] = mx;
+    part_l[pi] = sum;
+  }
+}
+
+// out[b, h, i] = Σ_c e^{m_c − m}·o_c[i] / Σ_c e^{m_c − m}·l_c, chunks in order.
+template <typename T>
+__global__ __launch_bounds__(128) void attn_combine_kernel(const float *__restrict__ part_m,
+                                                           const float *__restrict__ part_l,
+                                                           const float *__restrict__ part_o,
+                                                           T *__restrict__ out, int n_heads,
+                                                           int S) {
+  const int h = blockIdx.x, b = blockIdx.y, i = threadIdx.x;
+  const int64_t base = (static_cast<int64_t>(b) * n_heads + h) * S;
+  float m = -INFINITY;
+#pragma unroll 8
+  for (int c = 0; c < S; ++c) m = fmaxf(m, part_m[base + c]);
+  float l = 0.f, o = 0.f;
+#pragma unroll 8
+  for (int c = 0; c < S; ++c) {
+    const float w = expf(part_m[base + c] - m);
+    l = fmaf(part_l[base + c], w, l);
+    o = fmaf(part_o[(base + c) * 128 + i], w, o);
+  }
+  Elt<T>::store(out, (static_cast<int64_t>(b) * n_heads + h) * 128 + i, o / l);
 }
 
 // h[i] = h[i] + o[i], rounded to T.
@@ -274,26 +303,45 @@ hipError_t launch_rope(const void *qk, int64_t stride, void *q_out, void *k_out,
   return hipGetLastError();
 }
 
+size_t decode_attention_ws_bytes(int64_t B, int64_t Tlen, int64_t n_heads) {
+  const int64_t S = (Tlen + 1 + kACh - 1) / kACh;
+  return static_cast<size_t>(B) * n_heads * S * (2 + 128) * sizeof(float);
+}
+
 hipError_t launch_decode_attention(const void *q, const void *k_new, int64_t k_stride,
                                    const void *v_new, int64_t v_stride, const void *kc,
                                    const void *vc, void *out, int64_t B, int64_t Tlen,
-                                   int64_t n_heads, int64_t n_kv, int dt, hipStream_t s) {
-  const size_t lds = (static_cast<size_t>(Tlen) + 1) * sizeof(float);
-  dim3 grid(static_cast<unsigned>(n_heads), static_cast<unsigned>(B));
-  if (dt == kF32)
-    hipLaunchKernelGGL(decode_attention_kernel<float>, grid, dim3(kAT), lds, s,
+                                   int64_t n_heads, int64_t n_kv, int dt, void *ws,
+                                   hipStream_t s) {
+  const int S = static_cast<int>((Tlen + 1 + kACh - 1) / kACh);
+  const int64_t parts = B * n_heads * S;
+  float *pm = static_cast<float *>(ws);
+  float *pl = pm + parts;
+  float *po = pl + parts;
+  const dim3 grid(static_cast<unsigned>(n_heads * S), static_cast<unsigned>(B));
+  const dim3 cgrid(static_cast<unsigned>(n_heads), static_cast<unsigned>(B));
+  const int T = static_cast<int>(Tlen), H = static_cast<int>(n_heads), K = static_cast<int>(n_kv);
+  if (dt == kF32) {
+    hipLaunchKernelGGL(attn_chunk_kernel<float>, grid, dim3(kACT), 0, s,
                        static_cast<const float *>(q), static_cast<const float *>(k_new), k_stride,
                        static_cast<const float *>(v_new), v_stride,
-                       static_cast<const float *>(kc), static_cast<const float *>(vc),
-                       static_cast<float *>(out), static_cast<int>(Tlen),
-                       static_cast<int>(n_heads), static_cast<int>(n_kv));
-  else
-    hipLaunchKernelGGL(decode_attention_kernel<uint16_t>, grid, dim3(kAT), lds, s,
+                       static_cast<const float *>(kc), static_cast<const float *>(vc), pm, pl, po,
+                       T, H, K, S);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_combine_kernel<float>, cgrid, dim3(128), 0, s, pm, pl, po,
+                       static_cast<float *>(out), H, S);
+  } else {
+    hipLaunchKernelGGL(attn_chunk_kernel<uint16_t>, grid, dim3(kACT), 0, s,
                        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k_new),
                        k_stride, static_cast<const uint16_t *>(v_new), v_stride,
-                       static_cast<const uint16_t *>(kc), static_cast<const uint16_t *>(vc),
-                       static_cast<uint16_t *>(out), static_cast<int>(Tlen),
-                       static_cast<int>(n_heads), static_cast<int>(n_kv));
+                       static_cast<const uint16_t *>(kc), static_cast<const uint16_t *>(vc), pm,
+                       pl, po, T, H, K, S);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_combine_kernel<uint16_t>, cgrid, dim3(128), 0, s, pm, pl, po,
+                       static_cast<uint16_t *>(out), H, S);
+  }
   return hipGetLastError();
 }
 

@@ -212,10 +212,13 @@ hipError_t launch_rmsnorm(const void *h, void *out, int64_t B, int64_t d, float 
 hipError_t launch_rope(const void *qk, int64_t stride, void *q_out, void *k_out, int64_t B,
                        int64_t n_heads, int64_t n_kv, int64_t dh, int64_t pos, double theta,
                        int dt, hipStream_t s);
+// ws: decode_attention_ws_bytes (per-chunk partial results)
+size_t decode_attention_ws_bytes(int64_t B, int64_t Tlen, int64_t n_heads);
 hipError_t launch_decode_attention(const void *q, const void *k_new, int64_t k_stride,
                                    const void *v_new, int64_t v_stride, const void *kc,
                                    const void *vc, void *out, int64_t B, int64_t Tlen,
-                                   int64_t n_heads, int64_t n_kv, int dt, hipStream_t s);
+                                   int64_t n_heads, int64_t n_kv, int dt, void *ws,
+                                   hipStream_t s);
 hipError_t launch_residual_add(void *h, const void *o, int64_t n, int dt, hipStream_t s);
 
 }  // namespace larosa

@@ -61,6 +61,8 @@ class DecoderBuffers:
         self.gu = torch.empty((B, 2 * s.f), **bf)
         self.hh = torch.empty((B, s.f), **bf)
         self.dn = torch.empty((B, s.d), **bf)
+        n = _lib.larosa_decode_attention_workspace_bytes(B, s.ctx, s.n_heads)
+        self.att_ws = torch.empty(max(n, 16), dtype=torch.uint8, device=device)
 
 
 def layer_forward(layer: DecoderLayer, h, buf: DecoderBuffers, mode: int = _lib.UNFUSED,
@@ -89,7 +91,7 @@ def layer_forward(layer: DecoderLayer, h, buf: DecoderBuffers, mode: int = _lib.
     v_new = buf.qkv[:, (s.n_heads + s.n_kv_heads) * s.d_head:]
     _lib.larosa_decode_attention(buf.q, buf.k, s.n_kv_heads * s.d_head, v_new, s.qkv_out,
                                  layer.k_cache, layer.v_cache, buf.att, B, s.ctx, s.n_heads,
-                                 s.n_kv_heads, s.d_head)
+                                 s.n_kv_heads, s.d_head, ws=buf.att_ws)
     lin("o_in", buf.att, buf.o)
     _lib.larosa_residual_add(h, buf.o, B * s.d)
     _lib.larosa_rmsnorm(h, buf.m, B, s.d)

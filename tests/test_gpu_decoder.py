@@ -66,7 +66,8 @@ def test_rope(B, H, Hkv):
 
 
 @pytest.mark.parametrize("B,H,Hkv,T", [(1, 32, 32, 2048), (4, 32, 32, 2048), (2, 64, 8, 300),
-                                       (2, 4, 4, 0)])
+                                       (2, 4, 4, 0), (1, 8, 8, 255), (3, 8, 2, 256),
+                                       (1, 4, 4, 4100)])
 def test_decode_attention(B, H, Hkv, T):
     dh = 128
     rng = np.random.default_rng(T + B)
@@ -78,8 +79,10 @@ def test_decode_attention(B, H, Hkv, T):
     out = torch.empty((B, H * dh), dtype=torch.bfloat16, device="cuda")
     kc_d = dev(kc.reshape(-1), "bf16") if T else torch.empty(8, dtype=torch.bfloat16, device="cuda")
     vc_d = dev(vc.reshape(-1), "bf16") if T else torch.empty(8, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(_lib.larosa_decode_attention_workspace_bytes(B, T, H), dtype=torch.uint8,
+                     device="cuda")
     _lib.larosa_decode_attention(dev(q, "bf16"), dev(kn, "bf16"), Hkv * dh, dev(vn, "bf16"),
-                                 Hkv * dh, kc_d, vc_d, out, B, T, H, Hkv, dh)
+                                 Hkv * dh, kc_d, vc_d, out, B, T, H, Hkv, dh, ws=ws)
     torch.cuda.synchronize()
     want = dec.decode_attention(q, kn, vn, kc, vc, H, Hkv, dh)
     assert ref.rel_error(host(out), want) <= TOL
