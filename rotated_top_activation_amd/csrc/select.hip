@@ -77,8 +77,18 @@ __global__ __launch_bounds__(kThreads) void union_list_kernel(
   const int t = threadIdx.x;
   const int nw = (d + 31) / 32;
   uint32_t word = 0u;
-  if (t < nw)
-    for (int b = 0; b < B; ++b) word |= mask[static_cast<int64_t>(b) * nw + t];
+  if (t < nw) {
+    // eight tokens' words in flight at a time
+    int b = 0;
+    for (; b + 8 <= B; b += 8) {
+      uint32_t w8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w8[i] = mask[static_cast<int64_t>(b + i) * nw + t];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) word |= w8[i];
+    }
+    for (; b < B; ++b) word |= mask[static_cast<int64_t>(b) * nw + t];
+  }
   const uint32_t c = __popc(word);
   const uint32_t incl = block_incl_scan<kThreads>(c, wave_tot);
   uint32_t pos = incl - c;

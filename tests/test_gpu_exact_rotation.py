@@ -61,6 +61,8 @@ ROTATE_CASES = [
     ("bf16", "bf16", 1152, 96, 17), ("f32", "f32", 1024, 256, 2),
     # fp32 rows of 8192: more chunks per lane than one load batch holds
     ("f32", "f32", 8192, 8192, 1), ("f32", "f32", 8192, 8192, 3),
+    # several groups of eight tokens, the last one ragged
+    ("bf16", "bf16", 2048, 512, 33),
 ]
 
 

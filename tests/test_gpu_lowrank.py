@@ -64,6 +64,7 @@ CASES = [
     (4096, 4096, 1032, 1, 40, 64), (4096, 4096, 22016, 1, 40, 64),
     (11008, 2752, 4096, 1, 40, 128), (4096, 4096, 1032, 4, 40, 32),
     (2048, 512, 4104, 40, 25, 256), (1024, 256, 1032, 16, 50, 1), (1024, 256, 520, 2, 50, 200),
+    (1024, 256, 2056, 64, 50, 64),  # 49-64 tokens: coefficients staged per workgroup
 ]
 
 

@@ -150,7 +150,7 @@ LAYER_CASES = [
     # selection + product below 16384 channels and the separate steps above
     (4096, 4096, 22016, 1, 40), (11008, 2752, 4096, 1, 40), (1024, 256, 1032, 1, 50),
     (20480, 2048, 1024, 1, 50), (4096, 4096, 1032, 3, 40), (4096, 4096, 1032, 16, 40),
-    (2048, 512, 4104, 40, 25),
+    (2048, 512, 4104, 40, 25), (1024, 256, 2056, 64, 40),
 ]
 
 
