@@ -49,8 +49,7 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
     int32_t *__restrict__ idx_out, int32_t *__restrict__ count_out) {
   constexpr int V = Elt<WT>::kVec;
   constexpr int TILE = kWave * V;
-  constexpr int R = kSgRows;
-  static_assert(kSgListMax % R == 0, "row groups must not straddle the list's end");
+  constexpr int R = kSgRows;  // loads in flight per lane, list positions per group
   __shared__ SelectSmem<kSgThreads> sm;
   __shared__ CandSmem cs;
   __shared__ int32_t l_idx[kSgListMax];
@@ -132,25 +131,57 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
         l_val[pos] = __uint_as_float(kv[i]);
       }));
 
-  // 3. Start streaming: this wave's first group of certain rows is loaded
-  //    now, so the rest of the rule is resolved while they are in flight.
-  //    Lanes past the last column read a valid column and store nothing.
+  // 3. Start streaming. The row list is read in groups of R positions:
+  //    first the certain rows (groups 0 .. CG − 1), then the boundary rows
+  //    (the tail, known once the rule is resolved); wave w takes groups w,
+  //    w + 16, w + 32, ... This wave's first group of certain rows is
+  //    requested now, so the rest of the rule is resolved while it is in
+  //    flight. Lanes past the last column read a valid column and store
+  //    nothing.
   const int64_t col_raw = static_cast<int64_t>(tile) * TILE + lane * V;
   const int64_t col = col_raw < d_out ? col_raw : d_out - V;
+  const int n_cg = (n_cert + R - 1) / R;  // CG
+  int n_list = n_cert;
+  auto load_group = [&](int G, uint4(&q)[R], float(&c)[R]) {
+    const int lo = G < n_cg ? G * R : n_cert + (G - n_cg) * R;
+    const int hi = G < n_cg ? (lo + R < n_cert ? lo + R : n_cert) : (lo + R < n_list ? lo + R : n_list);
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int j = lo + u;
+      const bool ok = j < hi;  // wave-uniform
+      const int row = ok ? l_idx[j] : 0;
+      c[u] = ok ? l_val[j] : 0.f;
+      q[u] = ok ? load16(w + static_cast<int64_t>(row) * d_out + col) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  float acc[V];
+#pragma unroll
+  for (int q = 0; q < V; ++q) acc[q] = 0.f;
+  auto consume = [&](const uint4(&q)[R], const float(&c)[R]) {
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      float f[V];
+      Elt<WT>::unpack(q[u], f);
+#pragma unroll
+      for (int qq = 0; qq < V; ++qq) acc[qq] = fmaf(c[u], f[qq], acc[qq]);
+    }
+  };
   uint4 q0[R];
   float cf0[R];
-#pragma unroll
-  for (int u = 0; u < R; ++u) {
-    const int j = wave * R + u;  // wave-uniform
-    const bool ok = j < n_cert;
-    const int row = ok ? l_idx[j] : 0;
-    cf0[u] = ok ? l_val[j] : 0.f;
-    q0[u] = ok ? load16(w + static_cast<int64_t>(row) * d_out + col) : make_uint4(0, 0, 0, 0);
-  }
+  if (wave < n_cg) load_group(wave, q0, cf0);
 
   // 4. The rest of the rule: T, and channels equal to T kept up to `cut`.
+  //    Then the first group has (nearly) arrived: it is added up and the
+  //    wave's next group of certain rows is requested before the boundary
+  //    list is built, so the memory pipe does not run dry meanwhile.
   uint32_t T = 0, cut = 0;
-  if constexpr (!THR) rule_finish<kSgThreads, EMAX>(key, E, i0, st, sm, cs, T, cut);
+  if constexpr (!THR) {
+    rule_finish<kSgThreads, EMAX>(key, E, i0, st, sm, cs, T, cut);
+    if (wave < n_cg) {
+      consume(q0, cf0);
+      if (wave + kSgWaves < n_cg) load_group(wave + kSgWaves, q0, cf0);
+    }
+  }
   auto keeps = [&](int i) {
     const uint32_t kk = key_of(i);
     if constexpr (THR) return kk >= thr_key;
@@ -161,7 +192,6 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
   //    ones; tile 0 also writes the global ascending index list (parity
   //    checks): the positions of this split's channels follow from the
   //    channels below c1.
-  int n_list = n_cert;
   if constexpr (!THR)
     n_list += static_cast<int>(compact(
         c0, c1, [&](int i) { return (key_of(i) >> radix_shift(0)) == digit0 && keeps(i); },
@@ -178,56 +208,29 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
   }
   __syncthreads();  // the vector's LDS copy becomes the waves' sum area
 
-  // 6. Stream the split's kept rows of this column tile: the first group
-  //    (completed from the list where the certain rows ran out), then
-  //    interleaved groups of R rows per wave, all R loads in flight.
-  float acc[V];
-#pragma unroll
-  for (int q = 0; q < V; ++q) acc[q] = 0.f;
-  {
-#pragma unroll
-    for (int u = 0; u < R; ++u) {
-      const int j = wave * R + u;
-      if (j >= n_cert && j < n_list) {
-        cf0[u] = l_val[j];
-        q0[u] = load16(w + static_cast<int64_t>(l_idx[j]) * d_out + col);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < R; ++u) {
-      float f[V];
-      Elt<WT>::unpack(q0[u], f);
-#pragma unroll
-      for (int qq = 0; qq < V; ++qq) acc[qq] = fmaf(cf0[u], f[qq], acc[qq]);
+  // 6. Stream the rest of this wave's groups: the one in flight (if any),
+  //    then one group of R rows at a time, all R loads in flight.
+  const int n_groups = n_cg + (n_list - n_cert + R - 1) / R;
+  int G = wave;
+  bool pending = wave < n_cg;  // THR: group `wave` is in flight
+  if constexpr (!THR) {
+    if (wave < n_cg) {  // group `wave` was added up after the rule
+      G = wave + kSgWaves;
+      pending = G < n_cg;
     }
   }
-  for (int base = (kSgWaves + wave) * R; base < n_list; base += kSgWaves * R) {
-    // base is a multiple of R below n_list <= kSgListMax, so the R list
-    // entries read here are in bounds (entries past n_list are not used).
-    int rows[R];
-    float c[R];
-#pragma unroll
-    for (int u = 0; u < R; ++u) {
-      rows[u] = l_idx[base + u];
-      c[u] = l_val[base + u];
-    }
+  if (pending) {
+    consume(q0, cf0);
+    G += kSgWaves;
+  }
+  for (; G < n_groups; G += kSgWaves) {
     uint4 q[R];
-#pragma unroll
-    for (int u = 0; u < R; ++u) {
-      const bool ok = base + u < n_list;  // wave-uniform
-      c[u] = ok ? c[u] : 0.f;
-      q[u] = ok ? load16(w + static_cast<int64_t>(rows[u]) * d_out + col) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < R; ++u) {
-      float f[V];
-      Elt<WT>::unpack(q[u], f);
-#pragma unroll
-      for (int qq = 0; qq < V; ++qq) acc[qq] = fmaf(c[u], f[qq], acc[qq]);
-    }
+    float c[R];
+    load_group(G, q, c);
+    consume(q, c);
   }
 
-  // 4. Combine the waves; with one split finish the tile, else partial sums.
+  // 7. Combine the waves; with one split finish the tile, else partial sums.
 #pragma unroll
   for (int q = 0; q < V; ++q) red[wave][lane * V + q] = acc[q];
   __syncthreads();
