@@ -142,17 +142,24 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
   const int64_t col = col_raw < d_out ? col_raw : d_out - V;
   const int n_cg = (n_cert + R - 1) / R;  // CG
   int n_list = n_cert;
+  // A group's list entries are all read first, then its R rows requested
+  // back to back. Positions past the group's end (the last group of a
+  // segment) repeat the group's last row with coefficient 0: the repeated
+  // request hits the same lines as the real one, so it costs no HBM
+  // traffic, and no load is conditional.
   auto load_group = [&](int G, uint4(&q)[R], float(&c)[R]) {
     const int lo = G < n_cg ? G * R : n_cert + (G - n_cg) * R;
     const int hi = G < n_cg ? (lo + R < n_cert ? lo + R : n_cert) : (lo + R < n_list ? lo + R : n_list);
+    int rows[R];
 #pragma unroll
     for (int u = 0; u < R; ++u) {
-      const int j = lo + u;
-      const bool ok = j < hi;  // wave-uniform
-      const int row = ok ? l_idx[j] : 0;
-      c[u] = ok ? l_val[j] : 0.f;
-      q[u] = ok ? load16(w + static_cast<int64_t>(row) * d_out + col) : make_uint4(0, 0, 0, 0);
+      const int j = lo + u < hi ? lo + u : hi - 1;  // hi > lo for every group read
+      rows[u] = l_idx[j];
+      const float cv = l_val[j];
+      c[u] = lo + u < hi ? cv : 0.f;
     }
+#pragma unroll
+    for (int u = 0; u < R; ++u) q[u] = load16(w + static_cast<int64_t>(rows[u]) * d_out + col);
   };
   float acc[V];
 #pragma unroll
@@ -166,20 +173,25 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
       for (int qq = 0; qq < V; ++qq) acc[qq] = fmaf(c[u], f[qq], acc[qq]);
     }
   };
-  uint4 q0[R];
-  float cf0[R];
-  if (wave < n_cg) load_group(wave, q0, cf0);
+  uint4 qa[R];
+  float ca[R];
+  const bool has_a = wave < n_cg;  // the early group
+  if (has_a) load_group(wave, qa, ca);
 
   // 4. The rest of the rule: T, and channels equal to T kept up to `cut`.
   //    Then the first group has (nearly) arrived: it is added up and the
   //    wave's next group of certain rows is requested before the boundary
   //    list is built, so the memory pipe does not run dry meanwhile.
   uint32_t T = 0, cut = 0;
+  uint4 qb[R];
+  float cb[R];
+  bool has_b = false;  // the group requested after the rule
   if constexpr (!THR) {
     rule_finish<kSgThreads, EMAX>(key, E, i0, st, sm, cs, T, cut);
-    if (wave < n_cg) {
-      consume(q0, cf0);
-      if (wave + kSgWaves < n_cg) load_group(wave + kSgWaves, q0, cf0);
+    if (has_a) {
+      consume(qa, ca);
+      has_b = wave + kSgWaves < n_cg;
+      if (has_b) load_group(wave + kSgWaves, qb, cb);
     }
   }
   auto keeps = [&](int i) {
@@ -212,16 +224,17 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
   //    then one group of R rows at a time, all R loads in flight.
   const int n_groups = n_cg + (n_list - n_cert + R - 1) / R;
   int G = wave;
-  bool pending = wave < n_cg;  // THR: group `wave` is in flight
-  if constexpr (!THR) {
-    if (wave < n_cg) {  // group `wave` was added up after the rule
-      G = wave + kSgWaves;
-      pending = G < n_cg;
+  if constexpr (THR) {
+    if (has_a) {  // still in flight
+      consume(qa, ca);
+      G += kSgWaves;
     }
-  }
-  if (pending) {
-    consume(q0, cf0);
+  } else if (has_a) {  // added up after the rule
     G += kSgWaves;
+    if (has_b) {
+      consume(qb, cb);
+      G += kSgWaves;
+    }
   }
   for (; G < n_groups; G += kSgWaves) {
     uint4 q[R];
