@@ -229,12 +229,17 @@ int layer_entry(const void *x, int act_dtype, const void *Qt, int64_t q_block,
   // rotation and the product, which read Qt and the union rows once for the
   // whole batch.
   const bool mf = mfma_supported(B, act_dtype, w_dtype);
+  // The matrix-core rotation may leave its k-range partial sums for the
+  // Top-K selection to add (one launch fewer); x_rot is then written there.
+  int n_parts = 1;
+  const float *parts = reinterpret_cast<const float *>(base + L.p.mfma_parts);
   hipError_t e =
       f64   ? launch_rotate_f64(x, act_dtype, Qt, w_dtype, x_rot, static_cast<int>(B),
                                 static_cast<int>(d_in), static_cast<int>(q_block), s)
       : mf && q_block % 32 == 0
           ? launch_rotate_mfma(x, Qt, x_rot, static_cast<int>(B), static_cast<int>(d_in),
-                               static_cast<int>(q_block), base + L.p.mfma_parts, s)
+                               static_cast<int>(q_block), base + L.p.mfma_parts, s,
+                               B > 1 && !sel.thr ? &n_parts : nullptr)
           : launch_rotate(x, act_dtype, Qt, w_dtype, x_rot, static_cast<int>(B),
                           static_cast<int>(d_in), static_cast<int>(q_block), s);
   if (e != hipSuccess) return LAROSA_ERR_LAUNCH;
@@ -292,7 +297,7 @@ int layer_entry(const void *x, int act_dtype, const void *Qt, int64_t q_block,
     e = sel.thr ? launch_threshold_select(x_rot, static_cast<int>(B), static_cast<int>(d_in),
                                           sel.thr_key, idx, sel.count_out, val, xs, mask, s)
                 : launch_select(x_rot, static_cast<int>(B), static_cast<int>(d_in),
-                                static_cast<int>(k), idx, val, xs, mask, s);
+                                static_cast<int>(k), idx, val, xs, mask, s, parts, n_parts);
     if (e == hipSuccess)
       e = launch_union(mask, xs, static_cast<int>(B), static_cast<int>(d_in), u_idx, u_cnt,
                        mf ? nullptr : u_coef, s);
@@ -511,8 +516,9 @@ int larosa_topk_select(const float *x_rot, int64_t B, int64_t d, int64_t k, int3
   }
   if (int st = device_status()) return st;
   hipStream_t s = stream_of(stream);
-  hipError_t e = launch_select(x_rot, static_cast<int>(B), static_cast<int>(d),
-                               static_cast<int>(k), idx, val, xs, mask, s);
+  // x_rot is only read (no partial sums are passed)
+  hipError_t e = launch_select(const_cast<float *>(x_rot), static_cast<int>(B),
+                               static_cast<int>(d), static_cast<int>(k), idx, val, xs, mask, s);
   if (e == hipSuccess && want_union)
     e = launch_union(mask, xs, static_cast<int>(B), static_cast<int>(d), union_idx,
                      union_count, union_coef, s);
@@ -600,16 +606,18 @@ int larosa_lowrank_layer_forward(const void *x, int act_dtype, const void *Qt, i
   float *xs = reinterpret_cast<float *>(base + L.l.xs);
   const int Bi = static_cast<int>(B), di = static_cast<int>(d_in), ri = static_cast<int>(r);
   const bool mf = mfma_supported(B, act_dtype, w_dtype);
+  int n_parts = 1;  // k-range partial sums left for the selection to add
+  const float *parts = reinterpret_cast<const float *>(base + L.l.p.mfma_parts);
   hipError_t e =
       fp64_rotation(mode)
           ? launch_rotate_f64(x, act_dtype, Qt, w_dtype, x_rot, Bi, di, static_cast<int>(q_block), s)
       : mf && q_block % 32 == 0
           ? launch_rotate_mfma(x, Qt, x_rot, Bi, di, static_cast<int>(q_block),
-                               base + L.l.p.mfma_parts, s)
+                               base + L.l.p.mfma_parts, s, &n_parts)
           : launch_rotate(x, act_dtype, Qt, w_dtype, x_rot, Bi, di, static_cast<int>(q_block), s);
   uint32_t *mask = B > 1 ? reinterpret_cast<uint32_t *>(base + L.l.p.mask) : nullptr;
   if (e == hipSuccess)
-    e = launch_select(x_rot, Bi, di, static_cast<int>(k), idx, val, xs, mask, s);
+    e = launch_select(x_rot, Bi, di, static_cast<int>(k), idx, val, xs, mask, s, parts, n_parts);
   // the base row list: the token's kept rows, or the batch's union
   const int32_t *list = idx;
   const int32_t *n_dev = nullptr;

@@ -45,8 +45,13 @@ hipError_t launch_rotate_f64(const void *x, int x_dt, const void *qt, int q_dt, 
                              int B, int d, int qb, hipStream_t s);
 
 // --- Top-K selection (one workgroup per token) ---
-hipError_t launch_select(const float *x_rot, int B, int d, int k, int32_t *idx,
-                         float *val, float *xs, uint32_t *mask, hipStream_t s);
+// With n_parts > 1, x_rot arrives as n_parts k-range partial sums of the
+// rotation (slice p at parts + p·B·d, added in order p = 0, 1, ...) and is
+// written here; select_takes_parts says whether this d allows n_parts.
+bool select_takes_parts(int d, int n_parts);
+hipError_t launch_select(float *x_rot, int B, int d, int k, int32_t *idx, float *val, float *xs,
+                         uint32_t *mask, hipStream_t s, const float *parts = nullptr,
+                         int n_parts = 1);
 
 // --- row union of B > 1 selections (from the per-token bit masks); with
 // u_coef == NULL only the list and its count are written ---
@@ -129,10 +134,12 @@ constexpr int kMfmaMinB = 2;
 bool mfma_supported(int64_t B, int act_dt, int w_dt);
 // Rotation; qb % 32 == 0. With ws == NULL the k-range is not split (one
 // launch, x_rot written directly); otherwise ws holds rotate_mfma_ws_bytes.
+// With parts_out, k-range partial sums that the selection can take are
+// left in ws unsummed and *parts_out is their count (1: x_rot written).
 int rotate_mfma_splits(int64_t B, int64_t d, int64_t qb);
 size_t rotate_mfma_ws_bytes(int64_t B, int64_t d, int64_t qb);
 hipError_t launch_rotate_mfma(const void *x, const void *qt, float *x_rot, int B, int d, int qb,
-                              void *ws, hipStream_t s);
+                              void *ws, hipStream_t s, int *parts_out = nullptr);
 // Product over a row list with coefficients stored split and transposed
 // (store_coef_hl in common.hpp; B · ldc · 4 bytes, ldc = mfma_coef_ld(max_rows);
 // entries past the list's end must be finite, normally zero). ws holds

@@ -612,8 +612,10 @@ size_t rotate_mfma_ws_bytes(int64_t B, int64_t d, int64_t qb) {
 }
 
 hipError_t launch_rotate_mfma(const void *x, const void *qt, float *x_rot, int B, int d, int qb,
-                              void *ws, hipStream_t s) {
+                              void *ws, hipStream_t s, int *parts_out) {
   const int ks = ws ? rotate_mfma_splits(B, d, qb) : 1;
+  const bool leave = parts_out != nullptr && ks > 1 && select_takes_parts(d, ks);
+  if (parts_out) *parts_out = leave ? ks : 1;
   const int steps = qb / kMK;
   const int kps = (steps + ks - 1) / ks * kMK;
   float *out = ks > 1 ? static_cast<float *>(ws) : x_rot;
@@ -629,7 +631,7 @@ hipError_t launch_rotate_mfma(const void *x, const void *qt, float *x_rot, int B
       default: hipLaunchKernelGGL(rotate_mfma_staged_kernel<4>, grid, dim3(kMW * kWave), 0, s, xp, qp, out, B, d, qb, kps); break;
     }
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || ks == 1) return e;
+    if (e != hipSuccess || ks == 1 || leave) return e;
     return sum_parts<float>(out, ks, static_cast<int64_t>(B) * d, x_rot, s);
   }
   switch (MT) {
@@ -639,7 +641,7 @@ hipError_t launch_rotate_mfma(const void *x, const void *qt, float *x_rot, int B
     default: hipLaunchKernelGGL(rotate_mfma_kernel<4>, grid, dim3(kMW * kWave), 0, s, xp, qp, out, B, d, qb, kps); break;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || ks == 1) return e;
+  if (e != hipSuccess || ks == 1 || leave) return e;
   return sum_parts<float>(out, ks, static_cast<int64_t>(B) * d, x_rot, s);
 }
 

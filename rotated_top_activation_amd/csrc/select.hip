@@ -25,21 +25,81 @@ namespace {
 
 constexpr int kThreads = 1024;
 
+// Partial sums of the rotation taken per thread at most: kMaxPartLoads
+// 16-byte loads (n_parts · EMAX / 4), all in flight at once.
+constexpr int kMaxPartLoads = 16;
+
+// The keys of slots [t·E, t·E + E) of row b when x_rot arrives as n_parts
+// k-range partial sums (slice p at parts + p·B·d): every partial is loaded
+// first, then the slices are added in order p = 0, 1, ... (the order of the
+// separate sum, so the bits are the same), and the sums are written to
+// x_rot.
+template <int EMAX>
+__device__ __forceinline__ void load_keys_parts(const float *parts, int64_t pstride, int n_parts,
+                                                float *x_rot_row, const float *part_row, int d,
+                                                int E, uint32_t (&key)[EMAX], float (&v)[EMAX]) {
+  constexpr int NQ = EMAX / 4;
+  constexpr int MAXP = kMaxPartLoads / NQ;
+  const int i0 = static_cast<int>(threadIdx.x) * E;
+  (void)parts;
+  float4 g[MAXP][NQ];
+#pragma unroll
+  for (int p = 0; p < MAXP; ++p)
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int i = i0 + 4 * q < d ? i0 + 4 * q : d - 4;
+      g[p][q] = p < n_parts ? *reinterpret_cast<const float4 *>(part_row + p * pstride + i)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    float4 a = g[0][q];
+#pragma unroll
+    for (int p = 1; p < MAXP; ++p) {
+      if (p < n_parts) {
+        a.x += g[p][q].x;
+        a.y += g[p][q].y;
+        a.z += g[p][q].z;
+        a.w += g[p][q].w;
+      }
+    }
+    v[4 * q] = a.x;
+    v[4 * q + 1] = a.y;
+    v[4 * q + 2] = a.z;
+    v[4 * q + 3] = a.w;
+    // whole 16-byte quads: E and d are multiples of 4
+    if (4 * q < E && i0 + 4 * q < d) *reinterpret_cast<float4 *>(x_rot_row + i0 + 4 * q) = a;
+  }
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) {
+    const bool here = e < E && i0 + e < d;
+    key[e] = here ? (__float_as_uint(v[e]) & 0x7FFFFFFFu) : kNoKey;
+    v[e] = here ? v[e] : 0.f;
+  }
+}
+
+// x_rot is either given (n_parts <= 1) or summed here from n_parts partial
+// sums (and written).
 template <int EMAX>
 __global__ __launch_bounds__(kThreads) void topk_select_kernel(
-    const float *__restrict__ x_rot, int d, int k, int E, int32_t *__restrict__ idx,
-    float *__restrict__ val, float *__restrict__ xs, uint32_t *__restrict__ mask) {
+    float *__restrict__ x_rot, int d, int k, int E, int32_t *__restrict__ idx,
+    float *__restrict__ val, float *__restrict__ xs, uint32_t *__restrict__ mask,
+    const float *__restrict__ parts, int n_parts) {
   __shared__ SelectSmem<kThreads> sm;
   __shared__ uint32_t bitmap[kThreads];  // up to 32768 channels
 
   const int b = blockIdx.x;
   const int t = threadIdx.x;
-  const float *xr = x_rot + static_cast<int64_t>(b) * d;
+  float *xr = x_rot + static_cast<int64_t>(b) * d;
   const int i0 = t * E;
 
   float v[EMAX];
   uint32_t key[EMAX];
-  load_keys4<EMAX>(xr, d, E, key, v);
+  if (n_parts > 1)
+    load_keys_parts<EMAX>(parts, static_cast<int64_t>(gridDim.x) * d, n_parts, xr,
+                          parts + static_cast<int64_t>(b) * d, d, E, key, v);
+  else
+    load_keys4<EMAX>(xr, d, E, key, v);
   if (mask) bitmap[t] = 0u;
 
   uint32_t T, krem, n_eq;
@@ -138,22 +198,34 @@ __global__ void coef_transpose_kernel(const float *__restrict__ coef, int B, int
 }
 
 template <int EMAX>
-hipError_t launch_sel(const float *x_rot, int B, int d, int k, int E, int32_t *idx,
-                      float *val, float *xs, uint32_t *mask, hipStream_t s) {
+hipError_t launch_sel(float *x_rot, int B, int d, int k, int E, int32_t *idx, float *val,
+                      float *xs, uint32_t *mask, const float *parts, int n_parts,
+                      hipStream_t s) {
+  if (n_parts > kMaxPartLoads / (EMAX / 4)) return hipErrorInvalidValue;
   hipLaunchKernelGGL((topk_select_kernel<EMAX>), dim3(B), dim3(kThreads), 0, s, x_rot,
-                     d, k, E, idx, val, xs, mask);
+                     d, k, E, idx, val, xs, mask, parts, n_parts);
   return hipGetLastError();
+}
+
+int select_emax(int d) {
+  const int E = slots_per_thread(d, kThreads);
+  return E <= 4 ? 4 : (E <= 8 ? 8 : (E <= 16 ? 16 : 32));
 }
 
 }  // namespace
 
-hipError_t launch_select(const float *x_rot, int B, int d, int k, int32_t *idx,
-                         float *val, float *xs, uint32_t *mask, hipStream_t s) {
+bool select_takes_parts(int d, int n_parts) {
+  return n_parts >= 1 && n_parts <= kMaxPartLoads / (select_emax(d) / 4);
+}
+
+hipError_t launch_select(float *x_rot, int B, int d, int k, int32_t *idx, float *val, float *xs,
+                         uint32_t *mask, hipStream_t s, const float *parts, int n_parts) {
   const int E = slots_per_thread(d, kThreads);
-  if (E <= 4) return launch_sel<4>(x_rot, B, d, k, E, idx, val, xs, mask, s);
-  if (E <= 8) return launch_sel<8>(x_rot, B, d, k, E, idx, val, xs, mask, s);
-  if (E <= 16) return launch_sel<16>(x_rot, B, d, k, E, idx, val, xs, mask, s);
-  if (E <= 32) return launch_sel<32>(x_rot, B, d, k, E, idx, val, xs, mask, s);
+  if (n_parts <= 1) parts = nullptr;
+  if (E <= 4) return launch_sel<4>(x_rot, B, d, k, E, idx, val, xs, mask, parts, n_parts, s);
+  if (E <= 8) return launch_sel<8>(x_rot, B, d, k, E, idx, val, xs, mask, parts, n_parts, s);
+  if (E <= 16) return launch_sel<16>(x_rot, B, d, k, E, idx, val, xs, mask, parts, n_parts, s);
+  if (E <= 32) return launch_sel<32>(x_rot, B, d, k, E, idx, val, xs, mask, parts, n_parts, s);
   return hipErrorInvalidValue;
 }
 

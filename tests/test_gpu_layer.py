@@ -336,3 +336,32 @@ def test_swiglu_layer_matches_layer_then_swiglu(B, mode):
     g_u = ref.round_to(ref.gather_product(xr_g, want_idx, host(lin.Wf)), "bf16")
     want_h = ref.swiglu(g_u, f, "bf16")
     assert ref.rel_error(host(h), want_h) <= 2e-2
+
+
+@pytest.mark.parametrize("B,d,qb,n", [(16, 4096, 4096, 1032), (64, 11008, 2752, 520),
+                                      (40, 2048, 512, 1032), (2, 5120, 5120, 1032)])
+def test_batched_selection_adds_the_rotation_parts_in_order(B, d, qb, n):
+    """From 2 tokens the matrix-core rotation's k-range partial sums are added
+    by the Top-K selection itself, with no separate summing launch. That
+    x_rot must equal, bit for bit, the threshold layer's, whose rotation runs
+    the same split and adds the partials in the separate step, and the kept
+    sets must be the oracle's selection of it."""
+    case = wl.LinearCase(cfg=3, batch=B, d_in=d, d_out=n, q_block=qb, sparsity_pct=40,
+                         dtype="bf16", role="mlp_in")
+    x, q, w = wl.linear_case_inputs(case, w_std=0.02)
+    lin = RotatedLinear(q, w, "bf16", case.k)
+    x_d = dev(x, "bf16")
+    y, ok_y = guarded((B, n), torch.bfloat16)
+    idx, ok_i = guarded((B, case.k), torch.int32, fill=-3)
+    xr, ok_x = guarded((B, d), torch.float32)
+    lin.forward(x_d, y, lin.workspace(B), idx_out=idx, xrot_out=xr)
+    y_t = torch.empty_like(y)
+    xr_t = torch.empty((B, d), dtype=torch.float32, device="cuda")
+    ws_t = torch.zeros(_lib.larosa_workspace_bytes(B, d, n, d, _lib.UNFUSED), dtype=torch.uint8,
+                       device="cuda")
+    _lib.larosa_threshold_layer_forward(x_d, lin.Qt, qb, lin.Wf, B, d, n, 1.0, y_t, xrot_out=xr_t,
+                                        ws=ws_t)
+    torch.cuda.synchronize()
+    assert ok_y() and ok_i() and ok_x()
+    assert torch.equal(xr, xr_t)
+    np.testing.assert_array_equal(host(idx), ref.select(host_f32(xr), case.k))
