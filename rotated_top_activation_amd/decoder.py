@@ -23,7 +23,9 @@ class DecoderLayer:
 
     Row layout of the q|k|v projection output: n_heads query heads, then
     n_kv_heads key heads, then n_kv_heads value heads (d_head channels each).
-    The cache is [B, n_kv_heads, ctx, d_head] (head-major)."""
+    The cache is [B, n_kv_heads, ctx, d_head] (head-major). The gate|up
+    linear also keeps its folded weight with gate and up columns interleaved
+    (w_il), which the SwiGLU-folded layer call reads."""
 
     def __init__(self, shape: wl.DecoderShape, tensors: dict, ks: dict, k_cache, v_cache,
                  dtype: str = "bf16"):
@@ -33,6 +35,9 @@ class DecoderLayer:
             qname, wname = wl.ROLE_TENSORS[role]
             self.lin[role] = RotatedLinear(tensors[qname], tensors[wname], dtype, ks[role],
                                            keep_w=False)
+        g = self.lin["mlp_in"]
+        self.w_il = g.Wf.new_empty(g.Wf.shape)
+        _lib.larosa_interleave_gate_up(g.Wf, self.w_il, g.d_in, shape.f)
         self.k_cache = k_cache
         self.v_cache = v_cache
         self.ws = {}
@@ -40,7 +45,12 @@ class DecoderLayer:
     def workspaces(self, B: int, mode: int):
         key = (B, mode)
         if key not in self.ws:
-            self.ws[key] = {r: self.lin[r].workspace(B, mode) for r in ROLES}
+            ws = {r: self.lin[r].workspace(B, mode) for r in ROLES if r != "mlp_in"}
+            g = self.lin["mlp_in"]
+            n = _lib.larosa_swiglu_workspace_bytes(B, g.d_in, self.shape.f, g.k, mode)
+            ws["mlp_in"] = torch.empty(max(n, 16), dtype=torch.uint8, device=g.Wf.device)
+            _lib.larosa_workspace_init(ws["mlp_in"])
+            self.ws[key] = ws
         return self.ws[key]
 
 
@@ -58,7 +68,6 @@ class DecoderBuffers:
         self.att = torch.empty((B, s.n_heads * s.d_head), **bf)
         self.o = torch.empty((B, s.d), **bf)
         self.m = torch.empty((B, s.d), **bf)
-        self.gu = torch.empty((B, 2 * s.f), **bf)
         self.hh = torch.empty((B, s.f), **bf)
         self.dn = torch.empty((B, s.d), **bf)
         n = _lib.larosa_decode_attention_workspace_bytes(B, s.ctx, s.n_heads)
@@ -76,13 +85,17 @@ def layer_forward(layer: DecoderLayer, h, buf: DecoderBuffers, mode: int = _lib.
 
     def lin(role, x, y):
         L = layer.lin[role]
+        xr = idx = None
         if trace is not None:
             xr = torch.empty((B, L.d_in), dtype=torch.float32, device=h.device)
             idx = torch.empty((B, L.k), dtype=torch.int32, device=h.device)
             trace[role] = (xr, idx)
-            L.forward(x, y, ws[role], idx_out=idx, xrot_out=xr, mode=mode)
+        if role == "mlp_in":  # y is h = SiLU(gate)·up, folded into the gate|up call
+            _lib.larosa_swiglu_layer_forward(x, L.Qt, L.q_block, layer.w_il, B, L.d_in, s.f, L.k,
+                                             y, idx_out=idx, xrot_out=xr, mode=mode,
+                                             ws=ws[role])
         else:
-            L.forward(x, y, ws[role], mode=mode)
+            L.forward(x, y, ws[role], idx_out=idx, xrot_out=xr, mode=mode)
 
     _lib.larosa_rmsnorm(h, buf.a, B, s.d)
     lin("attn_in", buf.a, buf.qkv)
@@ -95,8 +108,7 @@ def layer_forward(layer: DecoderLayer, h, buf: DecoderBuffers, mode: int = _lib.
     lin("o_in", buf.att, buf.o)
     _lib.larosa_residual_add(h, buf.o, B * s.d)
     _lib.larosa_rmsnorm(h, buf.m, B, s.d)
-    lin("mlp_in", buf.m, buf.gu)
-    _lib.larosa_swiglu(buf.gu, buf.hh, B, s.f)
+    lin("mlp_in", buf.m, buf.hh)
     lin("down_in", buf.hh, buf.dn)
     _lib.larosa_residual_add(h, buf.dn, B * s.d)
 

@@ -5,7 +5,8 @@ Each layer is checked teacher-forced on the GPU's own layer input and
 intermediates: RMSNorm, the four rotations (rigorous fp32 bound), the four
 kept index sets (bit-exact against the oracle's selection on the GPU's
 rotated activations), sampled output columns of the four products, rotary
-embedding, attention over the key/value cache, SwiGLU and both residual adds.
+embedding, attention over the key/value cache, the gate|up call's folded
+SwiGLU and both residual adds.
 """
 import functools
 
@@ -111,6 +112,21 @@ def _check_linear(x_in, q_blocks, xr_gpu, idx_gpu, y_gpu, wf_dev, k, cols):
     assert ref.rel_error(y_gpu[:, cols], want) <= TOL
 
 
+def _check_swiglu_linear(x_in, q_blocks, xr_gpu, idx_gpu, h_gpu, wf_dev, k, f, cols):
+    """The gate|up linear with SiLU(gate)·up folded in: h on gate columns
+    `cols` (each paired with up column f + c) against the oracle's SwiGLU of
+    the product over the GPU's kept rows, teacher-forced."""
+    bound, exact = rotation_bound(x_in, q_blocks)
+    assert np.all(np.abs(xr_gpu.astype(np.float64) - exact) <= bound), "rotation bound"
+    want_idx = ref.select(xr_gpu, k)
+    np.testing.assert_array_equal(idx_gpu, want_idx)
+    both = np.concatenate([cols, cols + f])
+    wf_cols = host(wf_dev[:, torch.from_numpy(both).cuda()])
+    gu = ref.round_to(ref.gather_product(xr_gpu, want_idx, wf_cols), "bf16")
+    want = ref.swiglu(gu, len(cols), "bf16")
+    assert ref.rel_error(h_gpu[:, cols], want) <= TOL
+
+
 @functools.lru_cache(maxsize=1)
 def _base(cfg):
     shape = wl.LLAMA7B
@@ -140,18 +156,23 @@ def run_decoder(B, sparsity, n_layers, mode, n_checked=None, seed_cols=0):
             del layer
             continue
         checked += 1
-        a, qkv, att, o, m, gu, hh, dn = (host(t) for t in (buf.a, buf.qkv, buf.att, buf.o, buf.m,
-                                                            buf.gu, buf.hh, buf.dn))
+        a, qkv, att, o, m, hh, dn = (host(t) for t in (buf.a, buf.qkv, buf.att, buf.o, buf.m,
+                                                        buf.hh, buf.dn))
         q, k = host(buf.q), host(buf.k)
         h_out = host(h)
         assert close_bf16(a, dec.rmsnorm(h_in), extra=1e-6), f"layer {l} rmsnorm"
         lin_in = {"attn_in": a, "o_in": att, "mlp_in": m, "down_in": hh}
-        lin_out = {"attn_in": qkv, "o_in": o, "mlp_in": gu, "down_in": dn}
+        lin_out = {"attn_in": qkv, "o_in": o, "mlp_in": hh, "down_in": dn}
         for role in D.ROLES:
             qn, _ = wl.ROLE_TENSORS[role]
             xr, idx = trace[role]
             L = layer.lin[role]
             q_host = wl.layer_rotation(base[qn], idxs[role])
+            if role == "mlp_in":  # h = SiLU(gate)·up straight from the gate|up call
+                cols = np.sort(rng.choice(shape.f, size=256, replace=False))
+                _check_swiglu_linear(m, q_host, host_f32(xr), host(idx), hh, L.Wf, L.k,
+                                     shape.f, cols)
+                continue
             cols = np.sort(rng.choice(L.d_out, size=min(256, L.d_out), replace=False))
             _check_linear(lin_in[role], q_host, host_f32(xr), host(idx), lin_out[role], L.Wf,
                           L.k, cols)
@@ -168,7 +189,6 @@ def run_decoder(B, sparsity, n_layers, mode, n_checked=None, seed_cols=0):
         assert ref.rel_error(att, want_att) <= TOL, f"layer {l} attention"
         h_mid = dec.residual_add(h_in, o)
         assert close_bf16(m, dec.rmsnorm(h_mid), extra=1e-6), f"layer {l} residual/rmsnorm"
-        assert ref.rel_error(hh, ref.swiglu(gu, shape.f, "bf16")) <= TOL, f"layer {l} swiglu"
         np.testing.assert_array_equal(h_out, dec.residual_add(h_mid, dn))
         del layer
     assert np.all(np.isfinite(host(h)))
