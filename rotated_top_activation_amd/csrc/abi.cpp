@@ -296,8 +296,11 @@ int layer_entry(const void *x, int act_dtype, const void *Qt, int64_t q_block,
     float *u_coef = reinterpret_cast<float *>(base + L.u_coef);
     e = sel.thr ? launch_threshold_select(x_rot, static_cast<int>(B), static_cast<int>(d_in),
                                           sel.thr_key, idx, sel.count_out, val, xs, mask, s)
+                // the union and the product read xs and the masks only: the
+                // index list is written when asked for, the values not at all
                 : launch_select(x_rot, static_cast<int>(B), static_cast<int>(d_in),
-                                static_cast<int>(k), idx, val, xs, mask, s, parts, n_parts);
+                                static_cast<int>(k), idx_out, nullptr, xs, mask, s, parts,
+                                n_parts);
     if (e == hipSuccess)
       e = launch_union(mask, xs, static_cast<int>(B), static_cast<int>(d_in), u_idx, u_cnt,
                        mf ? nullptr : u_coef, s);
@@ -602,7 +605,6 @@ int larosa_lowrank_layer_forward(const void *x, int act_dtype, const void *Qt, i
   char *base = static_cast<char *>(ws);
   float *x_rot = xrot_out ? xrot_out : reinterpret_cast<float *>(base + L.l.x_rot);
   int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(base + L.l.idx);
-  float *val = reinterpret_cast<float *>(base + L.l.val);
   float *xs = reinterpret_cast<float *>(base + L.l.xs);
   const int Bi = static_cast<int>(B), di = static_cast<int>(d_in), ri = static_cast<int>(r);
   const bool mf = mfma_supported(B, act_dtype, w_dtype);
@@ -617,7 +619,11 @@ int larosa_lowrank_layer_forward(const void *x, int act_dtype, const void *Qt, i
           : launch_rotate(x, act_dtype, Qt, w_dtype, x_rot, Bi, di, static_cast<int>(q_block), s);
   uint32_t *mask = B > 1 ? reinterpret_cast<uint32_t *>(base + L.l.p.mask) : nullptr;
   if (e == hipSuccess)
-    e = launch_select(x_rot, Bi, di, static_cast<int>(k), idx, val, xs, mask, s, parts, n_parts);
+    // one token: the kept rows are the product's base list; more: the union is,
+    // and the index list is written only when asked for. Coefficients come
+    // from xs, so the values are not written.
+    e = launch_select(x_rot, Bi, di, static_cast<int>(k), B == 1 ? idx : idx_out, nullptr, xs,
+                      mask, s, parts, n_parts);
   // the base row list: the token's kept rows, or the batch's union
   const int32_t *list = idx;
   const int32_t *n_dev = nullptr;

@@ -87,6 +87,7 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
     const float *__restrict__ parts, int n_parts) {
   __shared__ SelectSmem<kThreads> sm;
   __shared__ uint32_t bitmap[kThreads];  // up to 32768 channels
+  __shared__ __align__(16) uint32_t stage[EMAX * kThreads];  // one output row
 
   const int b = blockIdx.x;
   const int t = threadIdx.x;
@@ -108,19 +109,46 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
   uint32_t pos;
   kept_flags<kThreads, EMAX>(key, T, krem, sm, kept, pos);
 
-  int32_t *idx_b = idx + static_cast<int64_t>(b) * k;
-  float *val_b = val + static_cast<int64_t>(b) * k;
+  // Outputs go through LDS: a thread's slots are E consecutive channels, so
+  // storing them straight to memory would put a wave's 64 lanes 4·E bytes
+  // apart (64 partly written lines per store). Each row (xs, then idx, then
+  // val) is laid out in `stage` and copied out with consecutive lanes on
+  // consecutive words.
+  const int64_t row_xs = static_cast<int64_t>(b) * d;
+  const int64_t row_k = static_cast<int64_t>(b) * k;
 #pragma unroll
   for (int e = 0; e < EMAX; ++e) {
     if (key[e] & kNoKey) continue;
     const int i = i0 + e;
-    if (kept[e]) {
-      idx_b[pos] = i;
-      val_b[pos] = v[e];
-      ++pos;
-      if (mask) atomicOr(&bitmap[i >> 5], 1u << (i & 31));
-    }
-    if (xs) xs[static_cast<int64_t>(b) * d + i] = kept[e] ? v[e] : 0.f;
+    if (kept[e] && mask) atomicOr(&bitmap[i >> 5], 1u << (i & 31));
+  }
+  if (xs) {
+#pragma unroll
+    for (int q = 0; q < EMAX / 4; ++q)
+      if (4 * q < E && i0 + 4 * q < d)  // whole quads: E and d are multiples of 4
+        *reinterpret_cast<uint4 *>(&stage[i0 + 4 * q]) = make_uint4(
+            kept[4 * q] ? __float_as_uint(v[4 * q]) : 0u, kept[4 * q + 1] ? __float_as_uint(v[4 * q + 1]) : 0u,
+            kept[4 * q + 2] ? __float_as_uint(v[4 * q + 2]) : 0u, kept[4 * q + 3] ? __float_as_uint(v[4 * q + 3]) : 0u);
+    __syncthreads();
+    for (int j = t; j < d; j += kThreads) xs[row_xs + j] = __uint_as_float(stage[j]);
+    __syncthreads();
+  }
+  if (idx) {
+    uint32_t p = pos;
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e)
+      if (!(key[e] & kNoKey) && kept[e]) stage[p++] = static_cast<uint32_t>(i0 + e);
+    __syncthreads();
+    for (int j = t; j < k; j += kThreads) idx[row_k + j] = static_cast<int32_t>(stage[j]);
+    __syncthreads();
+  }
+  if (val) {
+    uint32_t p = pos;
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e)
+      if (!(key[e] & kNoKey) && kept[e]) stage[p++] = __float_as_uint(v[e]);
+    __syncthreads();
+    for (int j = t; j < k; j += kThreads) val[row_k + j] = __uint_as_float(stage[j]);
   }
   if (mask) {
     __syncthreads();
