@@ -162,6 +162,7 @@ __global__ __launch_bounds__(kThreads) void union_list_kernel(
     const uint32_t *__restrict__ mask, int B, int d, int32_t *__restrict__ u_idx,
     int32_t *__restrict__ u_count) {
   __shared__ uint32_t wave_tot[kThreads / kWave];
+  __shared__ uint32_t stage[32 * kThreads];  // the list, copied out coalesced
   const int t = threadIdx.x;
   const int nw = (d + 31) / 32;
   uint32_t word = 0u;
@@ -182,9 +183,16 @@ __global__ __launch_bounds__(kThreads) void union_list_kernel(
   uint32_t pos = incl - c;
   while (word) {
     const int bit = __ffs(word) - 1;
-    u_idx[pos++] = t * 32 + bit;
+    stage[pos++] = static_cast<uint32_t>(t * 32 + bit);
     word &= word - 1u;
   }
+  // the total: the wave totals left by the scan
+  uint32_t total = 0;
+#pragma unroll
+  for (int i = 0; i < kThreads / kWave; ++i) total += wave_tot[i];
+  __syncthreads();
+  for (int j = t; j < static_cast<int>(total); j += kThreads)
+    u_idx[j] = static_cast<int32_t>(stage[j]);
   if (t == kThreads - 1) *u_count = static_cast<int32_t>(incl);
 }
 

@@ -34,6 +34,8 @@ __global__ __launch_bounds__(kThreads) void threshold_select_kernel(
     uint32_t *__restrict__ mask) {
   __shared__ uint32_t wave_tot[kThreads / kWave];
   __shared__ uint32_t bitmap[kThreads];  // up to 32768 channels
+  __shared__ __align__(16) uint32_t stage[EMAX * kThreads];  // one output row
+  __shared__ uint32_t s_total;
   const int b = blockIdx.x;
   const int t = threadIdx.x;
   const float *xr = x_rot + static_cast<int64_t>(b) * d;
@@ -46,23 +48,49 @@ __global__ __launch_bounds__(kThreads) void threshold_select_kernel(
 #pragma unroll
   for (int e = 0; e < EMAX; ++e) n += !(key[e] & kNoKey) && key[e] >= thr_key;
   const uint32_t incl = block_incl_scan<kThreads>(n, wave_tot);
-  uint32_t pos = incl - n;
-  int32_t *idx_b = idx + static_cast<int64_t>(b) * d;
-  float *val_b = val ? val + static_cast<int64_t>(b) * d : nullptr;
+  const uint32_t pos = incl - n;
+  if (t == kThreads - 1) {
+    s_total = incl;
+    if (count) count[b] = static_cast<int32_t>(incl);
+  }
+  bool kept[EMAX];
 #pragma unroll
   for (int e = 0; e < EMAX; ++e) {
-    if (key[e] & kNoKey) continue;
-    const int i = i0 + e;
-    const bool kept = key[e] >= thr_key;
-    if (kept) {
-      idx_b[pos] = i;
-      if (val_b) val_b[pos] = v[e];
-      ++pos;
-      if (mask) atomicOr(&bitmap[i >> 5], 1u << (i & 31));
-    }
-    if (xs) xs[static_cast<int64_t>(b) * d + i] = kept ? v[e] : 0.f;
+    kept[e] = !(key[e] & kNoKey) && key[e] >= thr_key;
+    if (kept[e] && mask) atomicOr(&bitmap[(i0 + e) >> 5], 1u << ((i0 + e) & 31));
   }
-  if (t == kThreads - 1 && count) count[b] = static_cast<int32_t>(incl);
+  // Each output row is laid out in LDS and copied out with consecutive lanes
+  // on consecutive words (a thread's slots are E consecutive channels).
+  const int64_t row = static_cast<int64_t>(b) * d;
+  if (xs) {
+#pragma unroll
+    for (int q = 0; q < EMAX / 4; ++q)
+      if (4 * q < E && i0 + 4 * q < d)  // whole quads: E and d are multiples of 4
+        *reinterpret_cast<uint4 *>(&stage[i0 + 4 * q]) = make_uint4(
+            kept[4 * q] ? __float_as_uint(v[4 * q]) : 0u, kept[4 * q + 1] ? __float_as_uint(v[4 * q + 1]) : 0u,
+            kept[4 * q + 2] ? __float_as_uint(v[4 * q + 2]) : 0u, kept[4 * q + 3] ? __float_as_uint(v[4 * q + 3]) : 0u);
+    __syncthreads();
+    for (int j = t; j < d; j += kThreads) xs[row + j] = __uint_as_float(stage[j]);
+  }
+  __syncthreads();  // stage is free; s_total is visible
+  const int total = static_cast<int>(s_total);
+  {
+    uint32_t p = pos;
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e)
+      if (kept[e]) stage[p++] = static_cast<uint32_t>(i0 + e);
+    __syncthreads();
+    for (int j = t; j < total; j += kThreads) idx[row + j] = static_cast<int32_t>(stage[j]);
+  }
+  if (val) {
+    __syncthreads();
+    uint32_t p = pos;
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e)
+      if (kept[e]) stage[p++] = __float_as_uint(v[e]);
+    __syncthreads();
+    for (int j = t; j < total; j += kThreads) val[row + j] = __uint_as_float(stage[j]);
+  }
   if (mask) {
     __syncthreads();
     const int nw = (d + 31) / 32;
