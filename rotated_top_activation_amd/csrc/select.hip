@@ -167,14 +167,14 @@ __global__ __launch_bounds__(kThreads) void union_list_kernel(
   const int nw = (d + 31) / 32;
   uint32_t word = 0u;
   if (t < nw) {
-    // eight tokens' words in flight at a time
+    // sixteen tokens' words in flight at a time
     int b = 0;
-    for (; b + 8 <= B; b += 8) {
-      uint32_t w8[8];
+    for (; b + 16 <= B; b += 16) {
+      uint32_t w16[16];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) w8[i] = mask[static_cast<int64_t>(b + i) * nw + t];
+      for (int i = 0; i < 16; ++i) w16[i] = mask[static_cast<int64_t>(b + i) * nw + t];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) word |= w8[i];
+      for (int i = 0; i < 16; ++i) word |= w16[i];
     }
     for (; b < B; ++b) word |= mask[static_cast<int64_t>(b) * nw + t];
   }
