@@ -196,17 +196,33 @@ __global__ __launch_bounds__(kThreads) void union_list_kernel(
   if (t == kThreads - 1) *u_count = static_cast<int32_t>(incl);
 }
 
-// coef[j·B + b] = xs[b, u_idx[j]] for j < |U|; rows past |U| get zeros.
-__global__ void union_coef_kernel(const int32_t *__restrict__ u_idx,
-                                  const int32_t *__restrict__ u_count,
-                                  const float *__restrict__ xs, int B, int d,
-                                  float *__restrict__ coef) {
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (e >= static_cast<int64_t>(d) * B) return;
-  const int64_t j = e / B;
-  const int b = static_cast<int>(e % B);
+// coef[j·B + b] = xs[b, u_idx[j]] for j < |U|; rows past |U| get zeros
+// (j < d). A workgroup takes 64 consecutive j and every token: it reads
+// xs along j (consecutive lanes on consecutive union rows of one token),
+// turns the tile in LDS, and writes coef along b.
+constexpr int kUcRows = 64;
+constexpr int kUcThreads = 256;
+__global__ __launch_bounds__(kUcThreads) void union_coef_kernel(
+    const int32_t *__restrict__ u_idx, const int32_t *__restrict__ u_count,
+    const float *__restrict__ xs, int B, int d, float *__restrict__ coef) {
+  __shared__ float tile[kUcRows][kUcRows + 1];  // [j][b] for up to 64 tokens
+  const int t = threadIdx.x;
+  const int64_t j0 = static_cast<int64_t>(blockIdx.x) * kUcRows;
   const int n = *u_count;
-  coef[e] = j < n ? xs[static_cast<int64_t>(b) * d + u_idx[j]] : 0.f;
+  const int jj = t % kUcRows;
+  const int64_t j = j0 + jj;
+  const int row = j < n ? u_idx[j] : 0;
+  for (int b0 = 0; b0 < B; b0 += kUcRows) {
+    const int nb = B - b0 < kUcRows ? B - b0 : kUcRows;
+    for (int bb = t / kUcRows; bb < nb; bb += kUcThreads / kUcRows)
+      tile[jj][bb] = j < n ? xs[static_cast<int64_t>(b0 + bb) * d + row] : 0.f;
+    __syncthreads();
+    for (int e = t; e < kUcRows * nb; e += kUcThreads) {
+      const int r = e / nb, bb = e % nb;
+      if (j0 + r < d) coef[(j0 + r) * B + b0 + bb] = tile[r][bb];
+    }
+    __syncthreads();  // the tile is rewritten by the next token group
+  }
 }
 
 // Split coefficients (store_coef_hl) of xs[b, u_idx[j]] for j < |U|; zero
@@ -272,9 +288,8 @@ hipError_t launch_union(const uint32_t *mask, const float *xs, int B, int d,
                      u_idx, u_count);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !u_coef) return e;
-  const int64_t n = static_cast<int64_t>(d) * B;
-  hipLaunchKernelGGL(union_coef_kernel, dim3(static_cast<unsigned>((n + 255) / 256)),
-                     dim3(256), 0, s, u_idx, u_count, xs, B, d, u_coef);
+  hipLaunchKernelGGL(union_coef_kernel, dim3(static_cast<unsigned>((d + kUcRows - 1) / kUcRows)),
+                     dim3(kUcThreads), 0, s, u_idx, u_count, xs, B, d, u_coef);
   return hipGetLastError();
 }
 

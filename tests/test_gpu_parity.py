@@ -85,7 +85,9 @@ def test_select_bit_exact(d, k, B, kind):
 
 
 @pytest.mark.parametrize("d,k,B", [(512, 100, 2), (4100, 1700, 5), (11008, 6604, 8),
-                                   (64, 64, 3), (2048, 1, 6)])
+                                   (64, 64, 3), (2048, 1, 6),
+                                   # 64 tokens, and a ragged last group of union rows
+                                   (1000, 300, 64), (132, 100, 40)])
 def test_union_matches_set_union(d, k, B):
     xr = make_x_rot("heavy", B, d, seed=B * 1000 + d)
     xr_d = torch.from_numpy(xr).cuda()
