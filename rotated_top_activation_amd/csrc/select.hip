@@ -30,18 +30,18 @@ constexpr int kThreads = 1024;
 constexpr int kMaxPartLoads = 16;
 
 // The keys of slots [t·E, t·E + E) of row b when x_rot arrives as n_parts
-// k-range partial sums (slice p at parts + p·B·d): every partial is loaded
+// k-range partial sums (the row's slice p at part_row + p·pstride,
+// pstride = B·d): every partial is loaded
 // first, then the slices are added in order p = 0, 1, ... (the order of the
 // separate sum, so the bits are the same), and the sums are written to
 // x_rot.
 template <int EMAX>
-__device__ __forceinline__ void load_keys_parts(const float *parts, int64_t pstride, int n_parts,
-                                                float *x_rot_row, const float *part_row, int d,
-                                                int E, uint32_t (&key)[EMAX], float (&v)[EMAX]) {
+__device__ __forceinline__ void load_keys_parts(const float *part_row, int64_t pstride,
+                                                int n_parts, float *x_rot_row, int d, int E,
+                                                uint32_t (&key)[EMAX], float (&v)[EMAX]) {
   constexpr int NQ = EMAX / 4;
   constexpr int MAXP = kMaxPartLoads / NQ;
   const int i0 = static_cast<int>(threadIdx.x) * E;
-  (void)parts;
   float4 g[MAXP][NQ];
 #pragma unroll
   for (int p = 0; p < MAXP; ++p)
@@ -97,8 +97,8 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
   float v[EMAX];
   uint32_t key[EMAX];
   if (n_parts > 1)
-    load_keys_parts<EMAX>(parts, static_cast<int64_t>(gridDim.x) * d, n_parts, xr,
-                          parts + static_cast<int64_t>(b) * d, d, E, key, v);
+    load_keys_parts<EMAX>(parts + static_cast<int64_t>(b) * d, static_cast<int64_t>(gridDim.x) * d,
+                          n_parts, xr, d, E, key, v);
   else
     load_keys4<EMAX>(xr, d, E, key, v);
   if (mask) bitmap[t] = 0u;
