@@ -103,8 +103,13 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
     load_keys4<EMAX>(xr, d, E, key, v);
   if (mask) bitmap[t] = 0u;
 
+  // The first digit counts into histogram copies laid out in `stage`, which
+  // is free until the outputs; the later digits continue from it.
+  constexpr int kCopies = EMAX >= 8 ? hist_copies_for(EMAX * kThreads) : 1;
+  const RuleState st =
+      rule_first_digit<kThreads, EMAX, kCopies>(key, E, static_cast<uint32_t>(k), sm, stage);
   uint32_t T, krem, n_eq;
-  radix_threshold<kThreads, EMAX>(key, static_cast<uint32_t>(k), sm, T, krem, n_eq);
+  radix_threshold_from<kThreads, EMAX>(key, 1, st.prefix, st.pmask, st.krem, sm, T, krem, n_eq);
   bool kept[EMAX];
   uint32_t pos;
   kept_flags<kThreads, EMAX>(key, T, krem, sm, kept, pos);

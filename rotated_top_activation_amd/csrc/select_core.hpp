@@ -287,19 +287,54 @@ struct RuleState {
 
 // Step 1: the first digit (key bits 30..20) over every slot. The boundary
 // digit is st.prefix >> 20; st.n_cand channels share it.
-template <int NT, int EMAX>
+//
+// With COPIES > 1 the counts go to COPIES histograms in `copies` (LDS that
+// is free during this step, COPIES·kHistStride words, 16-byte aligned; lane
+// l counts into copy l % COPIES) and are then summed into sm.hist. Keys
+// crowd a few dozen first-digit bins, and an LDS atomic serialises the
+// lanes of a wave that hit one word; spread over the copies, those lanes
+// mostly hit different words in different banks.
+constexpr int kHistWords = 2048 + 64 + 4;  // the words of SelectSmem::hist
+constexpr int kHistStride = 2120;          // >= kHistWords, 8 (mod 32): a bin's copies in different banks
+
+// Copies (at most 4) that fit in `words` words of free LDS; 1 counts into
+// sm.hist alone.
+__host__ __device__ constexpr int hist_copies_for(int words) {
+  return words >= 4 * kHistStride ? 4 : (words >= 3 * kHistStride ? 3 : (words >= 2 * kHistStride ? 2 : 1));
+}
+
+template <int NT, int EMAX, int COPIES = 1>
 __device__ __forceinline__ RuleState rule_first_digit(const uint32_t (&key)[EMAX], int E,
-                                                      uint32_t k, SelectSmem<NT> &sm) {
-  radix_clear<NT>(sm);
+                                                      uint32_t k, SelectSmem<NT> &sm,
+                                                      uint32_t *copies = nullptr) {
+  static_assert(sizeof(sm.hist) == kHistWords * sizeof(uint32_t), "histogram size");
+  static_assert(kHistStride >= kHistWords && kHistStride % 4 == 0, "copy stride");
+  uint32_t *hist = sm.hist;
+  if constexpr (COPIES > 1) {
+    for (int i = threadIdx.x; i < COPIES * kHistStride / 4; i += NT)
+      reinterpret_cast<uint4 *>(copies)[i] = make_uint4(0u, 0u, 0u, 0u);
+    hist = copies + (threadIdx.x % COPIES) * kHistStride;
+  } else {
+    radix_clear<NT>(sm);
+  }
   __syncthreads();
 #pragma unroll
   for (int e = 0; e < EMAX; ++e) {
     if (e < E) {  // empty slots go to the dummy bin
       const int b = (key[e] & kNoKey) ? kDummyBin : static_cast<int>(key[e] >> radix_shift(0));
-      atomicAdd(&sm.hist[pad_bin(b)], 1u);
+      atomicAdd(&hist[pad_bin(b)], 1u);
     }
   }
   __syncthreads();
+  if constexpr (COPIES > 1) {
+    for (int i = threadIdx.x; i < kHistWords; i += NT) {
+      uint32_t s = 0;
+#pragma unroll
+      for (int c = 0; c < COPIES; ++c) s += copies[c * kHistStride + i];
+      sm.hist[i] = s;
+    }
+    __syncthreads();
+  }
   RuleState st{0u, kNoKey, k, 0u};
   // the histogram comes back cleared for rule_finish's second digit
   st.n_cand = radix_resolve<NT>(0, st.prefix, st.pmask, st.krem, sm, true);

@@ -52,8 +52,16 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
   constexpr int R = kSgRows;  // loads in flight per lane, list positions per group
   __shared__ SelectSmem<kSgThreads> sm;
   __shared__ CandSmem cs;
-  __shared__ int32_t l_idx[kSgListMax];
-  __shared__ float l_val[kSgListMax];
+  // The row list (indices, then coefficients). Before the list is built the
+  // same words hold the first digit's histogram copies.
+  // Copies only from 8 key slots per thread: with 4 keys per thread the
+  // clear and the sum of the copies cost more than the spread saves.
+  constexpr int COPIES = EMAX >= 8 ? 4 : 1;
+  constexpr int LIST_WORDS =
+      2 * kSgListMax > COPIES * kHistStride ? 2 * kSgListMax : COPIES * kHistStride;
+  __shared__ __align__(16) uint32_t lists[LIST_WORDS];
+  int32_t *const l_idx = reinterpret_cast<int32_t *>(lists);
+  float *const l_val = reinterpret_cast<float *>(lists + kSgListMax);
   // The rotated vector as loaded (fp32 bits, sign included), for the list
   // build; after that the same bytes hold the waves' sums.
   constexpr int KV_WORDS = kSgKeysMax > kSgWaves * TILE ? kSgKeysMax : kSgWaves * TILE;
@@ -113,7 +121,8 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
   RuleState st{};
   uint32_t digit0 = 0;
   if constexpr (!THR) {
-    st = rule_first_digit<kSgThreads, EMAX>(key, E, static_cast<uint32_t>(k), sm);
+    st = rule_first_digit<kSgThreads, EMAX, COPIES>(key, E, static_cast<uint32_t>(k), sm,
+                                                           lists);
     digit0 = st.prefix >> radix_shift(0);
   } else {
     __syncthreads();  // the LDS copy of the vector is complete
