@@ -162,6 +162,24 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
   }
 }
 
+// OR of word t over the B tokens' masks, C words in flight per round trip.
+// Positions past B repeat the last token's word (OR is idempotent), so the
+// loads are unconditional and a batch of up to C tokens takes one round trip.
+template <int C>
+__device__ __forceinline__ uint32_t or_words(const uint32_t *__restrict__ mask, int B, int nw,
+                                             int t) {
+  uint32_t word = 0u;
+  for (int b = 0; b < B; b += C) {
+    uint32_t w[C];
+#pragma unroll
+    for (int i = 0; i < C; ++i)
+      w[i] = mask[static_cast<int64_t>(b + i < B ? b + i : B - 1) * nw + t];
+#pragma unroll
+    for (int i = 0; i < C; ++i) word |= w[i];
+  }
+  return word;
+}
+
 // Union of the B masks: one workgroup, one mask word per thread (d <= 32768).
 __global__ __launch_bounds__(kThreads) void union_list_kernel(
     const uint32_t *__restrict__ mask, int B, int d, int32_t *__restrict__ u_idx,
@@ -171,18 +189,7 @@ __global__ __launch_bounds__(kThreads) void union_list_kernel(
   const int t = threadIdx.x;
   const int nw = (d + 31) / 32;
   uint32_t word = 0u;
-  if (t < nw) {
-    // sixteen tokens' words in flight at a time
-    int b = 0;
-    for (; b + 16 <= B; b += 16) {
-      uint32_t w16[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) w16[i] = mask[static_cast<int64_t>(b + i) * nw + t];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) word |= w16[i];
-    }
-    for (; b < B; ++b) word |= mask[static_cast<int64_t>(b) * nw + t];
-  }
+  if (t < nw) word = B <= 16 ? or_words<16>(mask, B, nw, t) : or_words<32>(mask, B, nw, t);
   const uint32_t c = __popc(word);
   const uint32_t incl = block_incl_scan<kThreads>(c, wave_tot);
   uint32_t pos = incl - c;
