@@ -297,6 +297,79 @@ def test_silu_closed_forms():
     np.testing.assert_allclose(h[0], [0.75 * ln3 * 2.0, 0.0], rtol=1e-7)
 
 
+def _mlp_fixture():
+    g = _load("mlp_worked_example.json")
+    x = np.array([g["x"]])
+    q1 = np.array(g["Q1"])[None]
+    q2 = np.array(g["Q2"])[None]
+    wgu = np.array(g["W_gate_up_folded"])
+    wd = np.array(g["W_down_folded"])
+    return g, x, q1, wgu, q2, wd
+
+
+def test_mlp_worked_example_f32():
+    """The MLP composition against the hand-worked closed forms (fp32
+    activations): every intermediate is a multiple of ln 3."""
+    g, x, q1, wgu, q2, wd = _mlp_fixture()
+    ln3 = math.log(3.0)
+    y, st = ref.mlp(x, q1, wgu, q2, wd, g["k1"], g["k2"], g["f"], act_dtype="f32")
+    c = g["f32"]
+    np.testing.assert_array_equal(st["x_rot1"][0], _f32(g["x_rot1"]))
+    assert list(st["idx1"][0]) == g["idx1"]
+    np.testing.assert_allclose(st["gu"][0, :2], np.array(c["gate_up_over_ln3"]) * ln3, rtol=1e-7)
+    np.testing.assert_array_equal(st["gu"][0, 2:], c["up"])
+    np.testing.assert_allclose(st["h"][0], np.array(c["h_over_ln3"]) * ln3, rtol=1e-6)
+    np.testing.assert_allclose(st["x_rot2"][0], np.array(c["x_rot2_over_ln3"]) * ln3, rtol=1e-6)
+    assert list(st["idx2"][0]) == g["idx2"]
+    np.testing.assert_allclose(y[0], np.array(c["y_over_ln3"]) * ln3, rtol=1e-6)
+
+
+def test_mlp_worked_example_bf16():
+    """bf16 activations: every value in the fixture is a bf16 number, so the
+    oracle must reproduce each exactly, including y[0], which depends on h
+    being rounded to bf16 before the down linear."""
+    g, x, q1, wgu, q2, wd = _mlp_fixture()
+    y, st = ref.mlp(x, q1, wgu, q2, wd, g["k1"], g["k2"], g["f"], act_dtype="bf16")
+    c = g["bf16"]
+    np.testing.assert_array_equal(st["gu"][0], c["gate_up"])
+    np.testing.assert_array_equal(st["h"][0], c["h"])
+    np.testing.assert_array_equal(st["x_rot2"][0], _f32(c["x_rot2"]))
+    assert list(st["idx1"][0]) == g["idx1"] and list(st["idx2"][0]) == g["idx2"]
+    np.testing.assert_array_equal(y[0], c["y"])
+
+
+def test_mlp_pins_catch_planted_mistakes():
+    """Plausible slips in the MLP composition each fail the bf16 fixture."""
+    g, x, q1, wgu, q2, wd = _mlp_fixture()
+    f, k1, k2 = g["f"], g["k1"], g["k2"]
+    want = np.array(g["bf16"]["y"])
+    gu, _, _ = ref.linear(x, q1, wgu, k1, "bf16")
+    h = ref.swiglu(gu, f, "bf16")
+    # gate|up rows fed to the down linear instead of h (the slice takes gate)
+    y_bad, _, _ = ref.linear(gu[:, :f], q2, wd, k2, "bf16")
+    assert not np.array_equal(y_bad[0], want)
+    # the gate|up linear's K reused for the down linear
+    y_bad, _, _ = ref.linear(h, q2, wd, k1, "bf16")
+    assert not np.array_equal(y_bad[0], want)
+    # h left unrounded between the linears
+    h_raw = ref.silu(gu[:, :f]) * gu[:, f:]
+    y_bad, _, _ = ref.linear(h_raw, q2, wd, k2, "bf16")
+    assert not np.array_equal(y_bad[0], want)
+    np.testing.assert_array_equal(y_bad[0], g["bf16"]["y_if_h_unrounded"])
+    # SiLU applied to up instead of gate
+    h_swap = ref.round_to(ref.silu(gu[:, f:]) * gu[:, :f], "bf16")
+    y_bad, _, _ = ref.linear(h_swap, q2, wd, k2, "bf16")
+    assert not np.array_equal(y_bad[0], want)
+    # the down linear run with the gate|up rotation's transpose convention (x·Qᵀ)
+    xr_bad = ref.round_f32(h @ q2[0].T)
+    idx_bad = ref.select(xr_bad, k2)
+    y_bad = ref.round_to(ref.gather_product(xr_bad, idx_bad, wd), "bf16")
+    assert not np.array_equal(y_bad[0], want)
+    # the correct composition, for contrast
+    y_ok, _, _ = ref.linear(h, q2, wd, k2, "bf16")
+    np.testing.assert_array_equal(y_ok[0], want)
+
+
 def test_rel_error_metric():
     y = np.array([1.0, -2.0, 0.0, 1e-9])
     assert ref.rel_error(y, y) == 0.0
