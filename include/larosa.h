@@ -48,7 +48,15 @@
 extern "C" {
 #endif
 
-#define LAROSA_ABI_VERSION 6
+#define LAROSA_ABI_VERSION 7
+
+/* Every entry point is a no-throw C function: exceptions never cross the
+ * ABI (a caught one is reported as LAROSA_ERR_INTERNAL). */
+#ifdef __cplusplus
+#define LAROSA_NOEXCEPT noexcept
+#else
+#define LAROSA_NOEXCEPT
+#endif
 
 typedef void *larosa_stream_t; /* hipStream_t */
 
@@ -64,7 +72,12 @@ enum {
   LAROSA_ERR_DTYPE = 4,       /* unsupported element type or combination */
   LAROSA_ERR_WORKSPACE = 5,   /* workspace missing or too small */
   LAROSA_ERR_NO_DEVICE = 6,   /* no HIP device visible */
-  LAROSA_ERR_LAUNCH = 7       /* a kernel launch failed */
+  LAROSA_ERR_LAUNCH = 7,      /* a kernel launch failed */
+  LAROSA_ERR_NONFINITE = 8,   /* LAROSA_VALIDATE: the rotated input holds NaN or ±inf */
+  LAROSA_ERR_TIMEOUT = 9,     /* a bounded device-side wait gave up (see
+                                 larosa_workspace_status) */
+  LAROSA_ERR_INTERNAL = 10    /* an unexpected host-side failure (e.g. an
+                                 exception) was caught at the ABI */
 };
 
 /* Execution modes of larosa_layer_forward. */
@@ -77,21 +90,52 @@ enum { LAROSA_UNFUSED = 0, LAROSA_FUSED = 1 };
  * LAROSA_FUSED runs the unfused steps. Any other bit is an invalid mode. */
 enum { LAROSA_ROTATE_FP64 = 2 };
 
+/* Debug flag, OR-ed into the mode like LAROSA_ROTATE_FP64: after the
+ * rotation the call checks every rotated entry on the device, waits for the
+ * stream (the one place the library synchronises the host) and, if any is
+ * NaN or ±inf, returns LAROSA_ERR_NONFINITE before the selection runs,
+ * leaving y as it was. The Top-K rule orders finite magnitudes and ±inf, and
+ * leaves NaN undefined (the oracle rejects it); this mode turns such input
+ * into a status. With it, LAROSA_FUSED runs the unfused steps, so that the
+ * check happens between the rotation and the selection. Not for graph
+ * capture (it waits on the stream). */
+enum { LAROSA_VALIDATE = 4 };
+
 /* LAROSA_ABI_VERSION of the loaded library. */
-int larosa_abi_version(void);
+int larosa_abi_version(void) LAROSA_NOEXCEPT;
 
 /* A static, human-readable name for a status code (never NULL). */
-const char *larosa_status_string(int status);
+const char *larosa_status_string(int status) LAROSA_NOEXCEPT;
 
 /* Bytes of workspace needed by larosa_layer_forward with these sizes in the
  * given mode. It also covers larosa_topk_select, larosa_topk_gemv, larosa_sparse_gemv and
  * larosa_dense_gemv on the same (B, d_in, d_out, k). Returns 0 for invalid
  * sizes. */
 size_t larosa_workspace_bytes(int64_t B, int64_t d_in, int64_t d_out,
-                              int64_t k, int mode);
+                              int64_t k, int mode) LAROSA_NOEXCEPT;
 
 /* Zero-fills `bytes` of workspace with a device kernel (no memset node). */
-int larosa_workspace_init(void *ws, size_t bytes, larosa_stream_t stream);
+int larosa_workspace_init(void *ws, size_t bytes, larosa_stream_t stream) LAROSA_NOEXCEPT;
+
+/* Device-side status of a workspace. The one-launch (LAROSA_FUSED) kernel
+ * waits on other workgroups of its grid; every such wait is bounded, and
+ * one that gives up (for instance when the grid is not all resident because
+ * other work holds the GPU) records LAROSA_ERR_TIMEOUT in the first word of
+ * the workspace, finishes without faulting and leaves the workspace ready
+ * for the next call; that call's outputs are then not to be trusted. This
+ * call enqueues a copy of the recorded status into *status_out (a device
+ * int32: LAROSA_OK or LAROSA_ERR_TIMEOUT) and clears it, in stream order;
+ * read status_out after the stream has reached it. ws: a workspace of
+ * larosa_workspace_bytes / larosa_swiglu_workspace_bytes size, 16-byte
+ * aligned. */
+int larosa_workspace_status(void *ws, int32_t *status_out, larosa_stream_t stream) LAROSA_NOEXCEPT;
+
+/* Spin limit of the bounded device-side waits above for launches enqueued
+ * after this call (process-wide; the default is 1 << 22 polls, far beyond
+ * any wait of a resident grid). A limit of 0 makes every such wait give up
+ * at once, which exercises the LAROSA_ERR_TIMEOUT path: every kernel still
+ * runs to its end and stays within its buffers. Returns the previous limit. */
+uint32_t larosa_set_spin_limit(uint32_t limit) LAROSA_NOEXCEPT;
 
 /* Prepared rotation: Qt = Qᵀ block by block. Q is packed [d/q_block,
  * q_block, q_block] (block c of the block-diagonal rotation, row-major);
@@ -101,7 +145,7 @@ int larosa_workspace_init(void *ws, size_t bytes, larosa_stream_t stream);
  * page, 方法详解 · 关键设计: random or learned). Offline; not on the hot path. */
 int larosa_prepare_rotation(const void *Q, void *Qt, int64_t d,
                             int64_t q_block, int dtype,
-                            larosa_stream_t stream);
+                            larosa_stream_t stream) LAROSA_NOEXCEPT;
 
 /* Folded weight W' = Qᵀ·W (= Qt·W), formed in fp32 and rounded to nearest
  * even in w_dtype. Qt: prepared rotation [d_in, q_block]; W, W_folded:
@@ -110,7 +154,7 @@ int larosa_prepare_rotation(const void *Q, void *Qt, int64_t d,
  * orthogonality the LaRoSA abstract names: (x·Q)·(Qᵀ·W) = x·W. */
 int larosa_fold_weights(const void *Qt, int64_t q_block, const void *W,
                         void *W_folded, int64_t d_in, int64_t d_out,
-                        int w_dtype, larosa_stream_t stream);
+                        int w_dtype, larosa_stream_t stream) LAROSA_NOEXCEPT;
 
 /* Rotation, stage 1 of the method (LaRoSA summary page, 技术框架):
  * x_rot[b, :] = x[b, :]·Q for b < B, accumulated in fp32.
@@ -118,7 +162,7 @@ int larosa_fold_weights(const void *Qt, int64_t q_block, const void *W,
  * q_dtype (F32 or BF16); x_rot: [B, d] fp32. */
 int larosa_rotate(const void *x, int x_dtype, const void *Qt, int64_t q_block,
                   int q_dtype, float *x_rot, int64_t B, int64_t d,
-                  larosa_stream_t stream);
+                  larosa_stream_t stream) LAROSA_NOEXCEPT;
 
 /* The same rotation with fp64 accumulation: every product x[b, i]·Q[i, j]
  * of two bf16 or two fp32 values is exact in fp64, the sum is kept in fp64
@@ -132,7 +176,7 @@ int larosa_rotate(const void *x, int x_dtype, const void *Qt, int64_t q_block,
  * conversions and FMAs, not HBM, bound it. */
 int larosa_rotate_fp64(const void *x, int x_dtype, const void *Qt,
                        int64_t q_block, int q_dtype, float *x_rot, int64_t B,
-                       int64_t d, larosa_stream_t stream);
+                       int64_t d, larosa_stream_t stream) LAROSA_NOEXCEPT;
 
 /* Top-K selection, stage 2 of the method (LaRoSA summary page, 技术框架;
  * the abstract's fixed-K "consistent model-level sparsity"): for each token
@@ -152,7 +196,7 @@ int larosa_rotate_fp64(const void *x, int x_dtype, const void *Qt,
 int larosa_topk_select(const float *x_rot, int64_t B, int64_t d, int64_t k,
                        int32_t *idx, float *val, float *xs, int32_t *union_idx,
                        int32_t *union_count, float *union_coef, void *ws,
-                       size_t ws_bytes, larosa_stream_t stream);
+                       size_t ws_bytes, larosa_stream_t stream) LAROSA_NOEXCEPT;
 
 /* Gather product (the saving the LaRoSA abstract names: computation and
  * memory transfers of zeroed channels are skipped):
@@ -168,7 +212,7 @@ int larosa_sparse_gemv(const int32_t *rows, const int32_t *n_rows,
                        int64_t max_rows, const float *coef,
                        const void *W_folded, int w_dtype, void *y,
                        int y_dtype, int64_t B, int64_t d_in, int64_t d_out,
-                       void *ws, size_t ws_bytes, larosa_stream_t stream);
+                       void *ws, size_t ws_bytes, larosa_stream_t stream) LAROSA_NOEXCEPT;
 
 /* Selection folded into the product, for one token (LaRoSA summary page,
  * 方法详解 · 技术框架: keep the k largest-magnitude rotated entries, set the
@@ -184,10 +228,16 @@ int larosa_sparse_gemv(const int32_t *rows, const int32_t *n_rows,
 int larosa_topk_gemv(const float *x_rot, int64_t d_in, int64_t k,
                      const void *W_folded, int w_dtype, void *y, int y_dtype,
                      int64_t d_out, int32_t *idx_out, void *ws, size_t ws_bytes,
-                     larosa_stream_t stream);
+                     larosa_stream_t stream) LAROSA_NOEXCEPT;
 
-/* One rotated sparse linear: rotate → select → (row union when B > 1) →
- * gather, for every projection that shares the input x. W_folded is the
+/* One rotated sparse linear layer of the method, both online stages of the
+ * LaRoSA summary page (方法详解 · 技术框架: stage 1 rotates the layer's input
+ * activation with its orthogonal matrix; stage 2 keeps the K entries of
+ * largest magnitude and sets the rest to zero) followed by the product that
+ * reads only the kept rows of the folded weight (the LaRoSA abstract: the
+ * zeroed channels cost neither computation nor memory transfer):
+ *   rotate → select → (row union when B > 1) → gather,
+ * for every projection that shares the input x. W_folded is the
  * column concatenation of those projections' folded weights
  * ([W'_q | W'_k | W'_v] or [W'_gate | W'_up]), [d_in, d_out] in w_dtype.
  * x: [B, d_in] and y: [B, d_out] in act_dtype; Qt: prepared rotation
@@ -195,12 +245,12 @@ int larosa_topk_gemv(const float *x_rot, int64_t d_in, int64_t k,
  * are optional copies of the selection and the rotated input (NULL skips
  * them). mode: LAROSA_UNFUSED (one kernel per step) or LAROSA_FUSED (one
  * persistent launch for B == 1; other B fall back to the unfused steps),
- * optionally OR-ed with LAROSA_ROTATE_FP64. */
+ * optionally OR-ed with LAROSA_ROTATE_FP64 and LAROSA_VALIDATE. */
 int larosa_layer_forward(const void *x, int act_dtype, const void *Qt,
                          int64_t q_block, const void *W_folded, int w_dtype,
                          int64_t B, int64_t d_in, int64_t d_out, int64_t k,
                          void *y, int32_t *idx_out, float *xrot_out, int mode,
-                         void *ws, size_t ws_bytes, larosa_stream_t stream);
+                         void *ws, size_t ws_bytes, larosa_stream_t stream) LAROSA_NOEXCEPT;
 
 /* Dense reference product y = x·W over every row of W, with the same
  * streaming and fp32 accumulation as larosa_sparse_gemv. x: [B, d_in] and
@@ -209,7 +259,7 @@ int larosa_layer_forward(const void *x, int act_dtype, const void *Qt,
 int larosa_dense_gemv(const void *x, int act_dtype, const void *W,
                       int w_dtype, void *y, int64_t B, int64_t d_in,
                       int64_t d_out, void *ws, size_t ws_bytes,
-                      larosa_stream_t stream);
+                      larosa_stream_t stream) LAROSA_NOEXCEPT;
 
 /* SwiGLU between the two linears of an MLP (LLaMA-style; the method
  * sparsifies the input of the down projection, which is this output):
@@ -217,7 +267,7 @@ int larosa_dense_gemv(const void *x, int act_dtype, const void *W,
  * gu: [B, 2f] ([gate | up]); h: [B, f]; both in dtype (F32 or BF16);
  * arithmetic in fp32, rounded to nearest even. f a multiple of 8. */
 int larosa_swiglu(const void *gu, void *h, int64_t B, int64_t f, int dtype,
-                  larosa_stream_t stream);
+                  larosa_stream_t stream) LAROSA_NOEXCEPT;
 
 /* ---- The gate|up linear of a SwiGLU MLP with SiLU(gate)·up folded in ----
  * The method sparsifies the input of every linear (LaRoSA summary page,
@@ -234,12 +284,12 @@ int larosa_swiglu(const void *gu, void *h, int64_t B, int64_t f, int dtype,
  * be a multiple of b (LAROSA_ERR_SHAPE otherwise); W and W_il must not
  * overlap. Offline; not on the hot path. */
 int larosa_interleave_gate_up(const void *W, void *W_il, int64_t d_in, int64_t f, int dtype,
-                              larosa_stream_t stream);
+                              larosa_stream_t stream) LAROSA_NOEXCEPT;
 
 /* Workspace for larosa_swiglu_layer_forward: the layer's own
  * (larosa_workspace_bytes(B, d_in, 2f, k, mode)) plus room for the gate|up
  * rows. 0 for invalid sizes. */
-size_t larosa_swiglu_workspace_bytes(int64_t B, int64_t d_in, int64_t f, int64_t k, int mode);
+size_t larosa_swiglu_workspace_bytes(int64_t B, int64_t d_in, int64_t f, int64_t k, int mode) LAROSA_NOEXCEPT;
 
 /* h[b, i] = SiLU(g[b, i])·u[b, i] with [g | u] = larosa_layer_forward of x
  * over the interleaved folded weight W_il ([d_in, 2f], see above): g and u
@@ -253,7 +303,7 @@ int larosa_swiglu_layer_forward(const void *x, int act_dtype, const void *Qt, in
                                 const void *W_il, int w_dtype, int64_t B, int64_t d_in,
                                 int64_t f, int64_t k, void *h, int32_t *idx_out,
                                 float *xrot_out, int mode, void *ws, size_t ws_bytes,
-                                larosa_stream_t stream);
+                                larosa_stream_t stream) LAROSA_NOEXCEPT;
 
 /* ---- Magnitude-threshold selection (the contrast to the fixed Top-K) ----
  * The R-Sparse summary page (研究流程与方法 · R-Sparse框架设计) masks every
@@ -267,7 +317,7 @@ int larosa_swiglu_layer_forward(const void *x, int act_dtype, const void *Qt, in
  * non-negative number (LAROSA_ERR_INVALID_ARG for negative or NaN). */
 
 /* Workspace bytes of larosa_calibrate_threshold (a few KB). */
-size_t larosa_calibrate_workspace_bytes(void);
+size_t larosa_calibrate_workspace_bytes(void) LAROSA_NOEXCEPT;
 
 /* *t_out (device fp32) = the keep-th largest magnitude |x_rot[i]| over the
  * n entries x_rot[0 .. n) (e.g. the rotated activations of N calibration
@@ -278,7 +328,7 @@ size_t larosa_calibrate_workspace_bytes(void);
  * larosa_calibrate_workspace_bytes() bytes, 16-byte aligned, overwritten.
  * Offline: not on the decode path. */
 int larosa_calibrate_threshold(const float *x_rot, int64_t n, int64_t keep, float *t_out,
-                               void *ws, size_t ws_bytes, larosa_stream_t stream);
+                               void *ws, size_t ws_bytes, larosa_stream_t stream) LAROSA_NOEXCEPT;
 
 /* Per-token threshold selection: for each token b the indices i with
  * |x_rot[b, i]| >= t, ascending, in idx[b·d .. b·d + count[b]) (rows of
@@ -289,7 +339,7 @@ int larosa_calibrate_threshold(const float *x_rot, int64_t n, int64_t keep, floa
 int larosa_threshold_select(const float *x_rot, int64_t B, int64_t d, float t, int32_t *idx,
                             int32_t *count, float *val, float *xs, int32_t *union_idx,
                             int32_t *union_count, float *union_coef, void *ws, size_t ws_bytes,
-                            larosa_stream_t stream);
+                            larosa_stream_t stream) LAROSA_NOEXCEPT;
 
 /* larosa_layer_forward with the threshold selection in place of the Top-K:
  * rotate, keep |x_rot| >= t per token, (row union for B > 1), product over
@@ -304,7 +354,7 @@ int larosa_threshold_layer_forward(const void *x, int act_dtype, const void *Qt,
                                    int64_t q_block, const void *W_folded, int w_dtype, int64_t B,
                                    int64_t d_in, int64_t d_out, float t, void *y,
                                    int32_t *idx_out, int32_t *count_out, float *xrot_out,
-                                   int mode, void *ws, size_t ws_bytes, larosa_stream_t stream);
+                                   int mode, void *ws, size_t ws_bytes, larosa_stream_t stream) LAROSA_NOEXCEPT;
 
 /* larosa_swiglu_layer_forward with the threshold selection (see above);
  * ws: larosa_swiglu_workspace_bytes(B, d_in, f, d_in, mode) bytes. */
@@ -313,7 +363,7 @@ int larosa_threshold_swiglu_layer_forward(const void *x, int act_dtype, const vo
                                           int64_t B, int64_t d_in, int64_t f, float t, void *h,
                                           int32_t *idx_out, int32_t *count_out, float *xrot_out,
                                           int mode, void *ws, size_t ws_bytes,
-                                          larosa_stream_t stream);
+                                          larosa_stream_t stream) LAROSA_NOEXCEPT;
 
 /* ---- Low-rank compensation of the dropped channels ---------------------
  * The R-Sparse summary page (研究流程与方法 · R-Sparse框架设计) sends the
@@ -331,7 +381,7 @@ int larosa_threshold_swiglu_layer_forward(const void *x, int act_dtype, const vo
 
 /* Workspace bytes of larosa_lowrank_layer_forward; 0 for invalid sizes. */
 size_t larosa_lowrank_workspace_bytes(int64_t B, int64_t d_in, int64_t d_out, int64_t k,
-                                      int64_t r);
+                                      int64_t r) LAROSA_NOEXCEPT;
 
 /* Rotate, keep each token's Top-k, then y [B, d_out] = xs·W' + (x_rot −
  * xs)·A_r·B_r. A_r: [d_in, r] in w_dtype (row-major); 1 <= r <= min(256,
@@ -344,7 +394,7 @@ int larosa_lowrank_layer_forward(const void *x, int act_dtype, const void *Qt, i
                                  const void *W_ext, const void *A_r, int64_t r, int w_dtype,
                                  int64_t B, int64_t d_in, int64_t d_out, int64_t k, void *y,
                                  int32_t *idx_out, float *xrot_out, int mode, void *ws,
-                                 size_t ws_bytes, larosa_stream_t stream);
+                                 size_t ws_bytes, larosa_stream_t stream) LAROSA_NOEXCEPT;
 
 /* ---- The decoder layer around the rotated linears ----------------------
  * The pages apply the rotated Top-K sparsification to every linear layer of a
@@ -356,7 +406,7 @@ int larosa_lowrank_layer_forward(const void *x, int act_dtype, const void *Qt, i
 /* RMSNorm with unit gain: out[b, :] = h[b, :] / sqrt(mean(h[b, :]²) + eps).
  * h, out: [B, d]; they may be the same buffer. */
 int larosa_rmsnorm(const void *h, void *out, int64_t B, int64_t d, float eps, int dtype,
-                   larosa_stream_t stream);
+                   larosa_stream_t stream) LAROSA_NOEXCEPT;
 
 /* Rotate-half rotary embedding at position pos: for each head, channel i
  * (i < d_head/2) pairs with i + d_head/2 and both turn by
@@ -366,11 +416,11 @@ int larosa_rmsnorm(const void *h, void *out, int64_t B, int64_t d, float eps, in
  * which must not overlap qk. */
 int larosa_rope(const void *qk, int64_t qk_stride, void *q_out, void *k_out, int64_t B,
                 int64_t n_heads, int64_t n_kv_heads, int64_t d_head, int64_t pos, float theta,
-                int dtype, larosa_stream_t stream);
+                int dtype, larosa_stream_t stream) LAROSA_NOEXCEPT;
 
 /* Workspace bytes of larosa_decode_attention (per-chunk partial results of
  * 256 positions); 0 for invalid sizes. */
-size_t larosa_decode_attention_workspace_bytes(int64_t B, int64_t T, int64_t n_heads);
+size_t larosa_decode_attention_workspace_bytes(int64_t B, int64_t T, int64_t n_heads) LAROSA_NOEXCEPT;
 
 /* Single-query softmax attention of every query head over its key/value
  * head's T cached positions plus the new token's own key and value:
@@ -387,10 +437,10 @@ int larosa_decode_attention(const void *q, const void *k_new, int64_t k_stride,
                             const void *v_new, int64_t v_stride, const void *k_cache,
                             const void *v_cache, void *out, int64_t B, int64_t T,
                             int64_t n_heads, int64_t n_kv_heads, int64_t d_head, int dtype,
-                            void *ws, size_t ws_bytes, larosa_stream_t stream);
+                            void *ws, size_t ws_bytes, larosa_stream_t stream) LAROSA_NOEXCEPT;
 
 /* Residual add in place: h[i] = h[i] + o[i] for i < n. */
-int larosa_residual_add(void *h, const void *o, int64_t n, int dtype, larosa_stream_t stream);
+int larosa_residual_add(void *h, const void *o, int64_t n, int dtype, larosa_stream_t stream) LAROSA_NOEXCEPT;
 
 #ifdef __cplusplus
 }

@@ -20,7 +20,12 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblarosa.s
 F32, BF16 = 0, 1
 UNFUSED, FUSED = 0, 1
 ROTATE_FP64 = 2  # mode flag: fp64-accumulating rotation, OR-ed into UNFUSED or FUSED
-ABI_VERSION = 6
+VALIDATE = 4     # mode flag: check the rotated input for NaN/inf (waits on the stream)
+ABI_VERSION = 7
+
+# status codes (include/larosa.h)
+OK, ERR_INVALID_ARG, ERR_SHAPE, ERR_ALIGNMENT, ERR_DTYPE, ERR_WORKSPACE = 0, 1, 2, 3, 4, 5
+ERR_NO_DEVICE, ERR_LAUNCH, ERR_NONFINITE, ERR_TIMEOUT, ERR_INTERNAL = 6, 7, 8, 9, 10
 
 _c_i64 = ctypes.c_int64
 _c_int = ctypes.c_int
@@ -33,6 +38,8 @@ SIGNATURES = {
     "larosa_status_string": (ctypes.c_char_p, [_c_int]),
     "larosa_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i64, _c_int]),
     "larosa_workspace_init": (_c_int, [_c_vp, _c_sz, _c_vp]),
+    "larosa_workspace_status": (_c_int, [_c_vp, _c_vp, _c_vp]),
+    "larosa_set_spin_limit": (ctypes.c_uint32, [ctypes.c_uint32]),
     "larosa_prepare_rotation": (_c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_vp]),
     "larosa_fold_weights": (_c_int, [_c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_vp]),
     "larosa_rotate": (_c_int, [_c_vp, _c_int, _c_vp, _c_i64, _c_int, _c_vp, _c_i64, _c_i64, _c_vp]),
@@ -155,6 +162,15 @@ def larosa_workspace_bytes(B: int, d_in: int, d_out: int, k: int, mode: int = UN
 def larosa_workspace_init(ws, stream=None) -> None:
     _check("larosa_workspace_init",
            load().larosa_workspace_init(_ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def larosa_workspace_status(ws, status_out, stream=None) -> None:
+    _check("larosa_workspace_status",
+           load().larosa_workspace_status(_ptr(ws), _ptr(status_out), _stream(stream)))
+
+
+def larosa_set_spin_limit(limit: int) -> int:
+    return int(load().larosa_set_spin_limit(limit))
 
 
 def larosa_prepare_rotation(Q, Qt, d: int, q_block: int, stream=None) -> None:

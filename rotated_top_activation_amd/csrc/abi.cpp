@@ -3,6 +3,7 @@
 // call, so an invalid call enqueues nothing and leaves outputs untouched.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "../../include/larosa.h"
@@ -32,6 +33,26 @@ int device_status() {
 
 int launched(hipError_t e) { return e == hipSuccess ? LAROSA_OK : LAROSA_ERR_LAUNCH; }
 
+// The no-throw wall of the C ABI: an exception from the host code of a call
+// (std::call_once, std::mutex, allocation inside the runtime) becomes a
+// status instead of crossing into C.
+template <typename F>
+int guard(F &&body) noexcept {
+  try {
+    return body();
+  } catch (...) {
+    return LAROSA_ERR_INTERNAL;
+  }
+}
+template <typename F>
+size_t guard_size(F &&body) noexcept {
+  try {
+    return body();
+  } catch (...) {
+    return 0;
+  }
+}
+
 hipStream_t stream_of(larosa_stream_t s) { return static_cast<hipStream_t>(s); }
 
 // Workspace carving. Every call that takes a workspace uses the same prefix,
@@ -45,8 +66,14 @@ hipStream_t stream_of(larosa_stream_t s) { return static_cast<hipStream_t>(s); }
 // larosa_layer_forward then adds its own areas, and the fused kernel's region
 // (whose synchronisation words must also stay zero) comes last.
 struct Prefix {
-  size_t mask = 0, gather = 0, mfma_coef = 0, mfma_parts = 0, end = 0;
+  size_t status = 0, mask = 0, gather = 0, mfma_coef = 0, mfma_parts = 0, end = 0;
 };
+
+// The first 256 bytes of every layer-call workspace: word 0 holds the
+// device-side status (LAROSA_ERR_TIMEOUT from a bounded wait that gave up),
+// word 1 the LAROSA_VALIDATE check's flag.
+constexpr size_t kStatusBytes = 256;
+static_assert(kStatusTimeout == LAROSA_ERR_TIMEOUT, "device status code");
 
 bool mfma_region(int64_t B, int w_dt) { return w_dt == LAROSA_BF16 && B >= kMfmaMinB && B <= kMaxB; }
 
@@ -59,6 +86,7 @@ Prefix prefix_for(int64_t B, int64_t d_in, int64_t d_out, int64_t rows_bound, in
     off += align256(bytes);
     return at;
   };
+  P.status = take(kStatusBytes);
   P.mask = take(static_cast<size_t>(B) * mask_words(static_cast<int>(d_in)) * 4);
   size_t g = gather_batch_ws_bytes(static_cast<int>(B), rows_bound, d_out, w_dt);
   if (B == 1) {
@@ -155,14 +183,31 @@ int check_rotation(int64_t d, int64_t qb, int q_dt) {
   return LAROSA_OK;
 }
 
-// The execution mode without the LAROSA_ROTATE_FP64 flag, or -1 when the
-// mode holds any other bit.
+// The execution mode without the LAROSA_ROTATE_FP64 and LAROSA_VALIDATE
+// flags, or -1 when the mode holds any other bit.
 int base_mode(int mode) {
-  const int m = mode & ~LAROSA_ROTATE_FP64;
+  const int m = mode & ~(LAROSA_ROTATE_FP64 | LAROSA_VALIDATE);
   return m == LAROSA_UNFUSED || m == LAROSA_FUSED ? m : -1;
 }
 
 bool fp64_rotation(int mode) { return (mode & LAROSA_ROTATE_FP64) != 0; }
+bool validating(int mode) { return (mode & LAROSA_VALIDATE) != 0; }
+
+// LAROSA_VALIDATE: flags any NaN or ±inf among the n rotated entries on the
+// device, then waits for the stream and reads the flag (status word 1 of
+// the workspace).
+int check_finite(const float *x_rot, int64_t n, void *ws, hipStream_t s) {
+  uint32_t *flag = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + 4);
+  hipError_t e = launch_flag_nonfinite(x_rot, n, flag, s);
+  uint32_t h = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(&h, flag, sizeof(h), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return LAROSA_ERR_LAUNCH;
+  return h ? LAROSA_ERR_NONFINITE : LAROSA_OK;
+}
+
+// Spin limit of the bounded device-side waits (larosa_set_spin_limit).
+std::atomic<uint32_t> g_spin_limit{1u << 22};
 
 }  // namespace
 
@@ -196,7 +241,8 @@ int layer_entry(const void *x, int act_dtype, const void *Qt, int64_t q_block,
     return LAROSA_ERR_ALIGNMENT;
   if ((xrot_out && !aligned16(xrot_out)) || !aligned16(ws)) return LAROSA_ERR_ALIGNMENT;
   const bool f64 = fp64_rotation(mode);
-  const bool fused = base_mode(mode) == LAROSA_FUSED && !f64 && !sel.thr &&
+  const bool check = validating(mode);
+  const bool fused = base_mode(mode) == LAROSA_FUSED && !f64 && !check && !sel.thr &&
                      fused_supported(B, d_in, act_dtype, w_dtype);
   const Layout L = fused ? layout_with_fused(B, d_in, d_out, k, w_dtype)
                          : layout_for(B, d_in, d_out, k, w_dtype);
@@ -219,6 +265,8 @@ int layer_entry(const void *x, int act_dtype, const void *Qt, int64_t q_block,
     f.idx_out = idx_out;
     f.xrot_out = xrot_out;
     f.ws = base + L.fused;
+    f.status = reinterpret_cast<uint32_t *>(base + L.p.status);
+    f.spin_limit = g_spin_limit.load();
     return launched(launch_fused_linear(f, s));
   }
   float *x_rot = xrot_out ? xrot_out : reinterpret_cast<float *>(base + L.x_rot);
@@ -239,10 +287,14 @@ int layer_entry(const void *x, int act_dtype, const void *Qt, int64_t q_block,
       : mf && q_block % 32 == 0
           ? launch_rotate_mfma(x, Qt, x_rot, static_cast<int>(B), static_cast<int>(d_in),
                                static_cast<int>(q_block), base + L.p.mfma_parts, s,
-                               B > 1 && !sel.thr ? &n_parts : nullptr)
+                               B > 1 && !sel.thr && !check ? &n_parts : nullptr)
           : launch_rotate(x, act_dtype, Qt, w_dtype, x_rot, static_cast<int>(B),
                           static_cast<int>(d_in), static_cast<int>(q_block), s);
   if (e != hipSuccess) return LAROSA_ERR_LAUNCH;
+  // (with the check the rotation sums its own k-range partials, so x_rot
+  // is complete here)
+  if (check)
+    if (int st = check_finite(x_rot, B * d_in, base + L.p.status, s)) return st;
 
   GatherArgs a;
   a.coef_mode = kCoefPacked;
@@ -343,7 +395,8 @@ int swiglu_entry(const void *x, int act_dtype, const void *Qt, int64_t q_block,
   if (!aligned16(h)) return LAROSA_ERR_ALIGNMENT;
   if (!ws || ws_bytes < need) return LAROSA_ERR_WORKSPACE;
   const size_t layer_bytes = larosa_workspace_bytes(B, d_in, 2 * f, k, mode);
-  const bool one_launch = (base_mode(mode) == LAROSA_UNFUSED || fp64_rotation(mode)) && B == 1 &&
+  const bool one_launch = (base_mode(mode) == LAROSA_UNFUSED || fp64_rotation(mode) ||
+                           validating(mode)) && B == 1 &&
                           select_gather_supported(d_in) &&
                           !(w_dtype == LAROSA_F32 && act_dtype == LAROSA_BF16);
   if (one_launch) {
@@ -367,6 +420,8 @@ int swiglu_entry(const void *x, int act_dtype, const void *Qt, int64_t q_block,
             : launch_rotate(x, act_dtype, Qt, w_dtype, x_rot, 1, static_cast<int>(d_in),
                             static_cast<int>(q_block), s);
     if (er != hipSuccess) return LAROSA_ERR_LAUNCH;
+    if (validating(mode))
+      if (int st = check_finite(x_rot, d_in, base + L.p.status, s)) return st;
     SelectGatherArgs g;
     g.x_rot = x_rot;
     g.d_in = static_cast<int>(d_in);
@@ -397,9 +452,9 @@ int swiglu_entry(const void *x, int act_dtype, const void *Qt, int64_t q_block,
 
 extern "C" {
 
-int larosa_abi_version(void) { return LAROSA_ABI_VERSION; }
+int larosa_abi_version(void) LAROSA_NOEXCEPT { return LAROSA_ABI_VERSION; }
 
-const char *larosa_status_string(int status) {
+const char *larosa_status_string(int status) LAROSA_NOEXCEPT {
   switch (status) {
     case LAROSA_OK: return "ok";
     case LAROSA_ERR_INVALID_ARG: return "invalid argument";
@@ -409,11 +464,15 @@ const char *larosa_status_string(int status) {
     case LAROSA_ERR_WORKSPACE: return "workspace missing or too small";
     case LAROSA_ERR_NO_DEVICE: return "no HIP device";
     case LAROSA_ERR_LAUNCH: return "kernel launch failed";
+    case LAROSA_ERR_NONFINITE: return "non-finite rotated input";
+    case LAROSA_ERR_TIMEOUT: return "a bounded device-side wait gave up";
+    case LAROSA_ERR_INTERNAL: return "internal error";
     default: return "unknown status";
   }
 }
 
-size_t larosa_workspace_bytes(int64_t B, int64_t d_in, int64_t d_out, int64_t k, int mode) {
+size_t larosa_workspace_bytes(int64_t B, int64_t d_in, int64_t d_out, int64_t k, int mode) LAROSA_NOEXCEPT {
+  return guard_size([&]() -> size_t {
   if (check_sizes(B < 1 ? 1 : B, d_in, k) != LAROSA_OK || d_out < 1) return 0;
   if (base_mode(mode) < 0) return 0;
   mode = base_mode(mode);
@@ -425,18 +484,33 @@ size_t larosa_workspace_bytes(int64_t B, int64_t d_in, int64_t d_out, int64_t k,
   const Layout b = mode == LAROSA_FUSED ? layout_with_fused(b1, d_in, d_out, k, LAROSA_F32)
                                         : layout_for(b1, d_in, d_out, k, LAROSA_F32);
   return a.total > b.total ? a.total : b.total;
+  });
 }
 
-int larosa_workspace_init(void *ws, size_t bytes, larosa_stream_t stream) {
+int larosa_workspace_init(void *ws, size_t bytes, larosa_stream_t stream) LAROSA_NOEXCEPT {
+  return guard([&]() -> int {
   if (!ws && bytes) return LAROSA_ERR_INVALID_ARG;
   if (bytes == 0) return LAROSA_OK;
   if (!aligned16(ws)) return LAROSA_ERR_ALIGNMENT;
   if (int st = device_status()) return st;
   return launched(launch_fill_zero(ws, bytes, stream_of(stream)));
+  });
 }
 
+int larosa_workspace_status(void *ws, int32_t *status_out, larosa_stream_t stream) LAROSA_NOEXCEPT {
+  return guard([&]() -> int {
+  if (!ws || !status_out) return LAROSA_ERR_INVALID_ARG;
+  if (!aligned16(ws) || (reinterpret_cast<uintptr_t>(status_out) & 3u)) return LAROSA_ERR_ALIGNMENT;
+  if (int st = device_status()) return st;
+  return launched(launch_take_status(static_cast<uint32_t *>(ws), status_out, stream_of(stream)));
+  });
+}
+
+uint32_t larosa_set_spin_limit(uint32_t limit) LAROSA_NOEXCEPT { return g_spin_limit.exchange(limit); }
+
 int larosa_prepare_rotation(const void *Q, void *Qt, int64_t d, int64_t q_block, int dtype,
-                            larosa_stream_t stream) {
+                            larosa_stream_t stream) LAROSA_NOEXCEPT {
+  return guard([&]() -> int {
   if (!Q || !Qt) return LAROSA_ERR_INVALID_ARG;
   if (!dtype_ok(dtype)) return LAROSA_ERR_DTYPE;
   if (d < 1) return LAROSA_ERR_SHAPE;
@@ -448,10 +522,12 @@ int larosa_prepare_rotation(const void *Q, void *Qt, int64_t d, int64_t q_block,
   if (a < b + bytes && b < a + bytes) return LAROSA_ERR_INVALID_ARG;
   if (int st = device_status()) return st;
   return launched(launch_transpose_blocks(Q, Qt, d, q_block, dtype, stream_of(stream)));
+  });
 }
 
 int larosa_fold_weights(const void *Qt, int64_t q_block, const void *W, void *W_folded,
-                        int64_t d_in, int64_t d_out, int w_dtype, larosa_stream_t stream) {
+                        int64_t d_in, int64_t d_out, int w_dtype, larosa_stream_t stream) LAROSA_NOEXCEPT {
+  return guard([&]() -> int {
   if (!Qt || !W || !W_folded) return LAROSA_ERR_INVALID_ARG;
   if (!dtype_ok(w_dtype)) return LAROSA_ERR_DTYPE;
   if (d_in < 1 || d_out < 1) return LAROSA_ERR_SHAPE;
@@ -466,10 +542,12 @@ int larosa_fold_weights(const void *Qt, int64_t q_block, const void *W, void *W_
   if ((f < w + wb && w < f + wb) || (f < q + qbts && q < f + wb)) return LAROSA_ERR_INVALID_ARG;
   if (int st = device_status()) return st;
   return launched(launch_fold(Qt, q_block, W, W_folded, d_in, d_out, w_dtype, stream_of(stream)));
+  });
 }
 
 int larosa_rotate(const void *x, int x_dtype, const void *Qt, int64_t q_block, int q_dtype,
-                  float *x_rot, int64_t B, int64_t d, larosa_stream_t stream) {
+                  float *x_rot, int64_t B, int64_t d, larosa_stream_t stream) LAROSA_NOEXCEPT {
+  return guard([&]() -> int {
   if (!dtype_ok(x_dtype) || !dtype_ok(q_dtype)) return LAROSA_ERR_DTYPE;
   if (int st = check_sizes(B, d, 1)) return st;
   if (B == 0) return LAROSA_OK;
@@ -485,10 +563,12 @@ int larosa_rotate(const void *x, int x_dtype, const void *Qt, int64_t q_block, i
   return launched(launch_rotate(x, x_dtype, Qt, q_dtype, x_rot, static_cast<int>(B),
                                 static_cast<int>(d), static_cast<int>(q_block),
                                 stream_of(stream)));
+  });
 }
 
 int larosa_rotate_fp64(const void *x, int x_dtype, const void *Qt, int64_t q_block,
-                       int q_dtype, float *x_rot, int64_t B, int64_t d, larosa_stream_t stream) {
+                       int q_dtype, float *x_rot, int64_t B, int64_t d, larosa_stream_t stream) LAROSA_NOEXCEPT {
+  return guard([&]() -> int {
   if (!dtype_ok(x_dtype) || !dtype_ok(q_dtype)) return LAROSA_ERR_DTYPE;
   if (int st = check_sizes(B, d, 1)) return st;
   if (B == 0) return LAROSA_OK;
@@ -500,11 +580,13 @@ int larosa_rotate_fp64(const void *x, int x_dtype, const void *Qt, int64_t q_blo
   return launched(launch_rotate_f64(x, x_dtype, Qt, q_dtype, x_rot, static_cast<int>(B),
                                     static_cast<int>(d), static_cast<int>(q_block),
                                     stream_of(stream)));
+  });
 }
 
 int larosa_topk_select(const float *x_rot, int64_t B, int64_t d, int64_t k, int32_t *idx,
                        float *val, float *xs, int32_t *union_idx, int32_t *union_count,
-                       float *union_coef, void *ws, size_t ws_bytes, larosa_stream_t stream) {
+                       float *union_coef, void *ws, size_t ws_bytes, larosa_stream_t stream) LAROSA_NOEXCEPT {
+  return guard([&]() -> int {
   if (int st = check_sizes(B, d, k)) return st;
   if (B == 0) return LAROSA_OK;
   if (!x_rot || !idx || !val) return LAROSA_ERR_INVALID_ARG;
@@ -513,9 +595,10 @@ int larosa_topk_select(const float *x_rot, int64_t B, int64_t d, int64_t k, int3
   if (!aligned16(x_rot)) return LAROSA_ERR_ALIGNMENT;
   uint32_t *mask = nullptr;
   if (want_union) {
-    const size_t need = static_cast<size_t>(B) * mask_words(static_cast<int>(d)) * 4;
+    const size_t need = kStatusBytes + static_cast<size_t>(B) * mask_words(static_cast<int>(d)) * 4;
     if (!ws || ws_bytes < need) return LAROSA_ERR_WORKSPACE;
-    mask = static_cast<uint32_t *>(ws);
+    if (!aligned16(ws)) return LAROSA_ERR_ALIGNMENT;
+    mask = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + kStatusBytes);
   }
   if (int st = device_status()) return st;
   hipStream_t s = stream_of(stream);
@@ -526,12 +609,14 @@ int larosa_topk_select(const float *x_rot, int64_t B, int64_t d, int64_t k, int3
     e = launch_union(mask, xs, static_cast<int>(B), static_cast<int>(d), union_idx,
                      union_count, union_coef, s);
   return launched(e);
+  });
 }
 
 int larosa_threshold_select(const float *x_rot, int64_t B, int64_t d, float t, int32_t *idx,
                             int32_t *count, float *val, float *xs, int32_t *union_idx,
                             int32_t *union_count, float *union_coef, void *ws, size_t ws_bytes,
-                            larosa_stream_t stream) {
+                            larosa_stream_t stream) LAROSA_NOEXCEPT {
+  return guard([&]() -> int {
   if (int st = check_sizes(B, d, 1)) return st;
   if (!(t >= 0.f)) return LAROSA_ERR_INVALID_ARG;  // negative or NaN
   if (B == 0) return LAROSA_OK;
@@ -541,9 +626,10 @@ int larosa_threshold_select(const float *x_rot, int64_t B, int64_t d, float t, i
   if (!aligned16(x_rot)) return LAROSA_ERR_ALIGNMENT;
   uint32_t *mask = nullptr;
   if (want_union) {
-    const size_t need = static_cast<size_t>(B) * mask_words(static_cast<int>(d)) * 4;
+    const size_t need = kStatusBytes + static_cast<size_t>(B) * mask_words(static_cast<int>(d)) * 4;
     if (!ws || ws_bytes < need) return LAROSA_ERR_WORKSPACE;
-    mask = static_cast<uint32_t *>(ws);
+    if (!aligned16(ws)) return LAROSA_ERR_ALIGNMENT;
+    mask = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + kStatusBytes);
   }
   if (int st = device_status()) return st;
   hipStream_t s = stream_of(stream);
@@ -553,12 +639,14 @@ int larosa_threshold_select(const float *x_rot, int64_t B, int64_t d, float t, i
     e = launch_union(mask, xs, static_cast<int>(B), static_cast<int>(d), union_idx,
                      union_count, union_coef, s);
   return launched(e);
+  });
 }
 
-size_t larosa_calibrate_workspace_bytes(void) { return calibrate_ws_bytes(); }
+size_t larosa_calibrate_workspace_bytes(void) LAROSA_NOEXCEPT { return calibrate_ws_bytes(); }
 
 int larosa_calibrate_threshold(const float *x_rot, int64_t n, int64_t keep, float *t_out,
-                               void *ws, size_t ws_bytes, larosa_stream_t stream) {
+                               void *ws, size_t ws_bytes, larosa_stream_t stream) LAROSA_NOEXCEPT {
+  return guard_size([&]() -> size_t {
   if (n < 1 || n > INT32_MAX) return LAROSA_ERR_SHAPE;
   if (keep < 1 || keep > n) return LAROSA_ERR_INVALID_ARG;
   if (!x_rot || !t_out) return LAROSA_ERR_INVALID_ARG;
@@ -567,23 +655,27 @@ int larosa_calibrate_threshold(const float *x_rot, int64_t n, int64_t keep, floa
   if (int st = device_status()) return st;
   return launched(launch_calibrate(x_rot, n, static_cast<uint32_t>(keep), t_out, ws,
                                    stream_of(stream)));
+  });
 }
 
 size_t larosa_lowrank_workspace_bytes(int64_t B, int64_t d_in, int64_t d_out, int64_t k,
-                                      int64_t r) {
+                                      int64_t r) LAROSA_NOEXCEPT {
+  return guard_size([&]() -> size_t {
   const int64_t b1 = B < 1 ? 1 : B;
   if (check_sizes(b1, d_in, k) != LAROSA_OK || d_out < 1) return 0;
   if (r < 1 || r > kMaxRank || r > d_in || r > d_out) return 0;
   const size_t a = lowrank_layout(b1, d_in, d_out, k, r, LAROSA_BF16).total;
   const size_t b = lowrank_layout(b1, d_in, d_out, k, r, LAROSA_F32).total;
   return a > b ? a : b;
+  });
 }
 
 int larosa_lowrank_layer_forward(const void *x, int act_dtype, const void *Qt, int64_t q_block,
                                  const void *W_ext, const void *A_r, int64_t r, int w_dtype,
                                  int64_t B, int64_t d_in, int64_t d_out, int64_t k, void *y,
                                  int32_t *idx_out, float *xrot_out, int mode, void *ws,
-                                 size_t ws_bytes, larosa_stream_t stream) {
+                                 size_t ws_bytes, larosa_stream_t stream) LAROSA_NOEXCEPT {
+  return guard([&]() -> int {
   if (!dtype_ok(act_dtype) || !dtype_ok(w_dtype)) return LAROSA_ERR_DTYPE;
   if (w_dtype == LAROSA_F32 && act_dtype == LAROSA_BF16) return LAROSA_ERR_DTYPE;
   if (int st = check_sizes(B, d_in, k)) return st;
@@ -615,8 +707,11 @@ int larosa_lowrank_layer_forward(const void *x, int act_dtype, const void *Qt, i
           ? launch_rotate_f64(x, act_dtype, Qt, w_dtype, x_rot, Bi, di, static_cast<int>(q_block), s)
       : mf && q_block % 32 == 0
           ? launch_rotate_mfma(x, Qt, x_rot, Bi, di, static_cast<int>(q_block),
-                               base + L.l.p.mfma_parts, s, &n_parts)
+                               base + L.l.p.mfma_parts, s,
+                               validating(mode) ? nullptr : &n_parts)
           : launch_rotate(x, act_dtype, Qt, w_dtype, x_rot, Bi, di, static_cast<int>(q_block), s);
+  if (e == hipSuccess && validating(mode))
+    if (int st = check_finite(x_rot, B * d_in, base + L.l.p.status, s)) return st;
   uint32_t *mask = B > 1 ? reinterpret_cast<uint32_t *>(base + L.l.p.mask) : nullptr;
   if (e == hipSuccess)
     // one token: the kept rows are the product's base list; more: the union is,
@@ -671,12 +766,14 @@ int larosa_lowrank_layer_forward(const void *x, int act_dtype, const void *Qt, i
   a.B = Bi;
   a.ws = base + L.l.p.gather;
   return launched(launch_gather(a, s));
+  });
 }
 
 int larosa_sparse_gemv(const int32_t *rows, const int32_t *n_rows, int64_t max_rows,
                        const float *coef, const void *W_folded, int w_dtype, void *y,
                        int y_dtype, int64_t B, int64_t d_in, int64_t d_out, void *ws,
-                       size_t ws_bytes, larosa_stream_t stream) {
+                       size_t ws_bytes, larosa_stream_t stream) LAROSA_NOEXCEPT {
+  return guard([&]() -> int {
   if (!dtype_ok(w_dtype) || !dtype_ok(y_dtype)) return LAROSA_ERR_DTYPE;
   if (w_dtype == LAROSA_F32 && y_dtype == LAROSA_BF16) return LAROSA_ERR_DTYPE;
   if (B < 0 || B > kMaxB) return LAROSA_ERR_INVALID_ARG;
@@ -720,11 +817,13 @@ int larosa_sparse_gemv(const int32_t *rows, const int32_t *n_rows, int64_t max_r
   a.ws = base + P.gather;
   // max_rows == 0 still runs, so y is written (as zeros).
   return launched(launch_gather(a, s));
+  });
 }
 
 int larosa_topk_gemv(const float *x_rot, int64_t d_in, int64_t k, const void *W_folded,
                      int w_dtype, void *y, int y_dtype, int64_t d_out, int32_t *idx_out,
-                     void *ws, size_t ws_bytes, larosa_stream_t stream) {
+                     void *ws, size_t ws_bytes, larosa_stream_t stream) LAROSA_NOEXCEPT {
+  return guard([&]() -> int {
   if (!dtype_ok(w_dtype) || !dtype_ok(y_dtype)) return LAROSA_ERR_DTYPE;
   if (w_dtype == LAROSA_F32 && y_dtype == LAROSA_BF16) return LAROSA_ERR_DTYPE;
   if (int st = check_sizes(1, d_in, k)) return st;
@@ -749,11 +848,13 @@ int larosa_topk_gemv(const float *x_rot, int64_t d_in, int64_t k, const void *W_
   g.idx_out = idx_out;
   g.ws = static_cast<char *>(ws) + P.gather;
   return launched(launch_select_gather(g, stream_of(stream)));
+  });
 }
 
 int larosa_dense_gemv(const void *x, int act_dtype, const void *W, int w_dtype, void *y,
                       int64_t B, int64_t d_in, int64_t d_out, void *ws, size_t ws_bytes,
-                      larosa_stream_t stream) {
+                      larosa_stream_t stream) LAROSA_NOEXCEPT {
+  return guard([&]() -> int {
   if (!dtype_ok(act_dtype) || !dtype_ok(w_dtype)) return LAROSA_ERR_DTYPE;
   if (act_dtype != w_dtype) return LAROSA_ERR_DTYPE;
   if (B < 0 || B > kMaxB) return LAROSA_ERR_INVALID_ARG;
@@ -792,23 +893,27 @@ int larosa_dense_gemv(const void *x, int act_dtype, const void *W, int w_dtype, 
   a.B = static_cast<int>(B);
   a.ws = base + P.gather;
   return launched(launch_gather(a, s));
+  });
 }
 
 int larosa_layer_forward(const void *x, int act_dtype, const void *Qt, int64_t q_block,
                          const void *W_folded, int w_dtype, int64_t B, int64_t d_in,
                          int64_t d_out, int64_t k, void *y, int32_t *idx_out, float *xrot_out,
-                         int mode, void *ws, size_t ws_bytes, larosa_stream_t stream) {
+                         int mode, void *ws, size_t ws_bytes, larosa_stream_t stream) LAROSA_NOEXCEPT {
+  return guard([&]() -> int {
   Sel sel;
   sel.k = k;
   return layer_entry(x, act_dtype, Qt, q_block, W_folded, w_dtype, B, d_in, d_out, sel, y,
                      idx_out, xrot_out, mode, ws, ws_bytes, stream);
+  });
 }
 
 int larosa_threshold_layer_forward(const void *x, int act_dtype, const void *Qt,
                                    int64_t q_block, const void *W_folded, int w_dtype, int64_t B,
                                    int64_t d_in, int64_t d_out, float t, void *y,
                                    int32_t *idx_out, int32_t *count_out, float *xrot_out,
-                                   int mode, void *ws, size_t ws_bytes, larosa_stream_t stream) {
+                                   int mode, void *ws, size_t ws_bytes, larosa_stream_t stream) LAROSA_NOEXCEPT {
+  return guard([&]() -> int {
   if (!(t >= 0.f)) return LAROSA_ERR_INVALID_ARG;  // negative or NaN
   Sel sel;
   sel.thr = true;
@@ -817,18 +922,22 @@ int larosa_threshold_layer_forward(const void *x, int act_dtype, const void *Qt,
   sel.count_out = count_out;
   return layer_entry(x, act_dtype, Qt, q_block, W_folded, w_dtype, B, d_in, d_out, sel, y,
                      idx_out, xrot_out, mode, ws, ws_bytes, stream);
+  });
 }
 
-size_t larosa_swiglu_workspace_bytes(int64_t B, int64_t d_in, int64_t f, int64_t k, int mode) {
+size_t larosa_swiglu_workspace_bytes(int64_t B, int64_t d_in, int64_t f, int64_t k, int mode) LAROSA_NOEXCEPT {
+  return guard_size([&]() -> size_t {
   if (f < 1) return 0;
   const size_t base = larosa_workspace_bytes(B, d_in, 2 * f, k, mode);
   if (base == 0) return 0;
   const int64_t b1 = B < 1 ? 1 : B;
   return base + align256(static_cast<size_t>(b1) * 2 * f * 4);  // the gate|up rows
+  });
 }
 
 int larosa_interleave_gate_up(const void *W, void *W_il, int64_t d_in, int64_t f, int dtype,
-                              larosa_stream_t stream) {
+                              larosa_stream_t stream) LAROSA_NOEXCEPT {
+  return guard([&]() -> int {
   if (!W || !W_il) return LAROSA_ERR_INVALID_ARG;
   if (!dtype_ok(dtype)) return LAROSA_ERR_DTYPE;
   if (d_in < 1 || f < 1 || f % interleave_block(dtype)) return LAROSA_ERR_SHAPE;
@@ -840,17 +949,20 @@ int larosa_interleave_gate_up(const void *W, void *W_il, int64_t d_in, int64_t f
   if (int st = device_status()) return st;
   return launched(launch_interleave(W, W_il, d_in, f, interleave_block(dtype), dtype,
                                     stream_of(stream)));
+  });
 }
 
 int larosa_swiglu_layer_forward(const void *x, int act_dtype, const void *Qt, int64_t q_block,
                                 const void *W_il, int w_dtype, int64_t B, int64_t d_in,
                                 int64_t f, int64_t k, void *h, int32_t *idx_out,
                                 float *xrot_out, int mode, void *ws, size_t ws_bytes,
-                                larosa_stream_t stream) {
+                                larosa_stream_t stream) LAROSA_NOEXCEPT {
+  return guard([&]() -> int {
   Sel sel;
   sel.k = k;
   return swiglu_entry(x, act_dtype, Qt, q_block, W_il, w_dtype, B, d_in, f, sel, h, idx_out,
                       xrot_out, mode, ws, ws_bytes, stream);
+  });
 }
 
 int larosa_threshold_swiglu_layer_forward(const void *x, int act_dtype, const void *Qt,
@@ -858,7 +970,8 @@ int larosa_threshold_swiglu_layer_forward(const void *x, int act_dtype, const vo
                                           int64_t B, int64_t d_in, int64_t f, float t, void *h,
                                           int32_t *idx_out, int32_t *count_out, float *xrot_out,
                                           int mode, void *ws, size_t ws_bytes,
-                                          larosa_stream_t stream) {
+                                          larosa_stream_t stream) LAROSA_NOEXCEPT {
+  return guard([&]() -> int {
   if (!(t >= 0.f)) return LAROSA_ERR_INVALID_ARG;
   Sel sel;
   sel.thr = true;
@@ -867,10 +980,12 @@ int larosa_threshold_swiglu_layer_forward(const void *x, int act_dtype, const vo
   sel.count_out = count_out;
   return swiglu_entry(x, act_dtype, Qt, q_block, W_il, w_dtype, B, d_in, f, sel, h, idx_out,
                       xrot_out, mode, ws, ws_bytes, stream);
+  });
 }
 
 int larosa_swiglu(const void *gu, void *h, int64_t B, int64_t f, int dtype,
-                  larosa_stream_t stream) {
+                  larosa_stream_t stream) LAROSA_NOEXCEPT {
+  return guard([&]() -> int {
   if (!dtype_ok(dtype)) return LAROSA_ERR_DTYPE;
   if (B < 0 || B > kMaxB || f < 1) return LAROSA_ERR_INVALID_ARG;
   if (B == 0) return LAROSA_OK;
@@ -879,21 +994,25 @@ int larosa_swiglu(const void *gu, void *h, int64_t B, int64_t f, int dtype,
   if (!aligned16(gu) || !aligned16(h)) return LAROSA_ERR_ALIGNMENT;
   if (int st = device_status()) return st;
   return launched(launch_swiglu(gu, h, B, f, dtype, stream_of(stream)));
+  });
 }
 
 int larosa_rmsnorm(const void *h, void *out, int64_t B, int64_t d, float eps, int dtype,
-                   larosa_stream_t stream) {
+                   larosa_stream_t stream) LAROSA_NOEXCEPT {
+  return guard([&]() -> int {
   if (!dtype_ok(dtype)) return LAROSA_ERR_DTYPE;
   if (B < 0 || B > kMaxB || d < 1 || !(eps >= 0.f)) return LAROSA_ERR_INVALID_ARG;
   if (B == 0) return LAROSA_OK;
   if (!h || !out) return LAROSA_ERR_INVALID_ARG;
   if (int st = device_status()) return st;
   return launched(launch_rmsnorm(h, out, B, d, eps, dtype, stream_of(stream)));
+  });
 }
 
 int larosa_rope(const void *qk, int64_t qk_stride, void *q_out, void *k_out, int64_t B,
                 int64_t n_heads, int64_t n_kv_heads, int64_t d_head, int64_t pos, float theta,
-                int dtype, larosa_stream_t stream) {
+                int dtype, larosa_stream_t stream) LAROSA_NOEXCEPT {
+  return guard([&]() -> int {
   if (!dtype_ok(dtype)) return LAROSA_ERR_DTYPE;
   if (B < 0 || B > kMaxB || n_heads < 1 || n_kv_heads < 1 || pos < 0 || !(theta > 0.f))
     return LAROSA_ERR_INVALID_ARG;
@@ -904,18 +1023,22 @@ int larosa_rope(const void *qk, int64_t qk_stride, void *q_out, void *k_out, int
   if (int st = device_status()) return st;
   return launched(launch_rope(qk, qk_stride, q_out, k_out, B, n_heads, n_kv_heads, d_head, pos,
                               static_cast<double>(theta), dtype, stream_of(stream)));
+  });
 }
 
-size_t larosa_decode_attention_workspace_bytes(int64_t B, int64_t T, int64_t n_heads) {
+size_t larosa_decode_attention_workspace_bytes(int64_t B, int64_t T, int64_t n_heads) LAROSA_NOEXCEPT {
+  return guard_size([&]() -> size_t {
   if (B < 1 || B > kMaxB || T < 0 || T > 16384 || n_heads < 1) return 0;
   return decode_attention_ws_bytes(B, T, n_heads);
+  });
 }
 
 int larosa_decode_attention(const void *q, const void *k_new, int64_t k_stride,
                             const void *v_new, int64_t v_stride, const void *k_cache,
                             const void *v_cache, void *out, int64_t B, int64_t T,
                             int64_t n_heads, int64_t n_kv_heads, int64_t d_head, int dtype,
-                            void *ws, size_t ws_bytes, larosa_stream_t stream) {
+                            void *ws, size_t ws_bytes, larosa_stream_t stream) LAROSA_NOEXCEPT {
+  return guard([&]() -> int {
   if (!dtype_ok(dtype)) return LAROSA_ERR_DTYPE;
   if (B < 0 || B > kMaxB || T < 0 || n_heads < 1 || n_kv_heads < 1) return LAROSA_ERR_INVALID_ARG;
   if (d_head != 128 || n_heads % n_kv_heads || T > 16384) return LAROSA_ERR_SHAPE;
@@ -933,15 +1056,18 @@ int larosa_decode_attention(const void *q, const void *k_new, int64_t k_stride,
   return launched(launch_decode_attention(q, k_new, k_stride, v_new, v_stride, k_cache, v_cache,
                                           out, B, T, n_heads, n_kv_heads, dtype, ws,
                                           stream_of(stream)));
+  });
 }
 
-int larosa_residual_add(void *h, const void *o, int64_t n, int dtype, larosa_stream_t stream) {
+int larosa_residual_add(void *h, const void *o, int64_t n, int dtype, larosa_stream_t stream) LAROSA_NOEXCEPT {
+  return guard([&]() -> int {
   if (!dtype_ok(dtype)) return LAROSA_ERR_DTYPE;
   if (n < 0) return LAROSA_ERR_INVALID_ARG;
   if (n == 0) return LAROSA_OK;
   if (!h || !o) return LAROSA_ERR_INVALID_ARG;
   if (int st = device_status()) return st;
   return launched(launch_residual_add(h, o, n, dtype, stream_of(stream)));
+  });
 }
 
 }  // extern "C"

@@ -3,14 +3,16 @@
 // Top-K select (stage 2), and the product over the kept rows of the folded
 // weight (the transfer saving named in the LaRoSA abstract).
 //
-// Every workgroup of the grid is resident at once (the grid is sized from
-// the occupancy of this kernel), and the phases hand over through memory:
+// The grid is sized from the occupancy of this kernel so that every
+// workgroup can be resident at once (an ordinary launch does not guarantee
+// it: other work on the GPU can hold CUs, and then the bounded waits below
+// give up with a status), and the phases hand over through memory:
 //   1. rotate: output channel j is owned by one wave, which writes x_rot[j]
 //      with an agent-scope atomic store. Every workgroup takes part.
-//   2. select: workgroup 0 is the selector. It waits until the other
-//      workgroups have counted themselves in (16 group counters) and tells
-//      them so, then copies the magnitude keys of x_rot into LDS and runs an
-//      exact radix select over them. After the first digit it already knows
+//   2. select: workgroup 0 is the selector. It waits until every other
+//      workgroup has written its arrival slot and tells them so, then
+//      copies the magnitude keys of x_rot into LDS and runs an exact radix
+//      select over them. After the first digit it already knows
 //      the bin B0 (key bits 30..20) holding the K-th largest key: every
 //      channel in a higher bin is kept whatever the rest of the select
 //      finds. It releases that preliminary rule at once, then finishes the
@@ -29,14 +31,21 @@
 //      rows does that for the workgroup). The last unit of a tile to finish
 //      adds the tile's partial sums in split order.
 // The bin-B0 rows go last in every unit's accumulation whatever the timing,
-// so results do not depend on when the exact rule arrives. All counters and
-// flags return to zero, so the workspace is ready for the next call. Waits
-// are bounded: a wait that runs past the limit sets an error word in the
-// workspace and continues instead of hanging.
+// so results do not depend on when the exact rule arrives.
+//
+// Every hand-over word carries the launch's epoch (a 16-bit number the host
+// gives each launch, never 0): a worker arrives by writing the epoch into its
+// own slot, and a release counts only with the current epoch. Nothing has to
+// be reset between calls, so a call that gave up a wait leaves nothing stale
+// that the next call could mistake for its own. Waits are bounded (the
+// spin limit is a kernel argument): a wait that runs past the limit writes
+// LAROSA_ERR_TIMEOUT into the workspace's status word and continues with a
+// fallback (an in-bounds but wrong result) instead of hanging.
 #include "common.hpp"
 #include "launch.hpp"
 #include "select_core.hpp"
 
+#include <atomic>
 #include <cstddef>
 #include <mutex>
 
@@ -47,22 +56,30 @@ constexpr int kFT = 512;              // threads per workgroup
 constexpr int kFW = kFT / kWave;      // waves per workgroup
 constexpr int kFRows = 8;             // rows per wave group
 constexpr int kFSplitLoads = 32;      // partial sums fetched per round trip
-constexpr int kGroups = 16;           // arrival counters
 constexpr int kChunks = kFusedMaxD / (4 * kFT);  // 16-byte key chunks per selector thread
-constexpr uint32_t kSpinLimit = 1u << 22;
 
-// Word offsets inside the synchronisation block (each on its own 128-byte
-// line): [32·(1+g)] arrival count of group g, [32·17] error word.
-constexpr int kErrWord = 32 * (kGroups + 1);
-
-// Release words: bit 63 marks a word, bits 62..61 its stage.
+// Release words: bits 63..48 the launch's epoch, bits 47..46 the stage.
 //   stage 0 (all rotations are in): nothing else
 //   stage 1 (preliminary rule):     bits 10..0 = B0
-//   stage 2 (exact rule):           bits 46..16 = T, bits 15..0 = cut-off
-//                                   (0xFFFF: every channel equal to T)
-constexpr uint64_t kWord = 1ull << 63;
-constexpr int kStageShift = 61;
-constexpr uint32_t kCutAll = 0xFFFFu;
+//   stage 2 (exact rule):           bits 45..15 = T, bits 14..0 = cut-off
+//                                   (0x7FFF: every channel equal to T;
+//                                   d <= 16384, so a real cut-off is lower)
+constexpr int kEpochShift = 48;
+constexpr int kStageShift = 46;
+constexpr uint32_t kCutAll = 0x7FFFu;
+
+__device__ __forceinline__ uint64_t make_word(uint32_t epoch, uint32_t stage, uint64_t payload) {
+  return (static_cast<uint64_t>(epoch) << kEpochShift) | (static_cast<uint64_t>(stage) << kStageShift) |
+         payload;
+}
+__device__ __forceinline__ uint32_t word_epoch(uint64_t w) { return static_cast<uint32_t>(w >> kEpochShift); }
+__device__ __forceinline__ uint32_t word_stage(uint64_t w) {
+  return static_cast<uint32_t>(w >> kStageShift) & 3u;
+}
+
+__device__ __forceinline__ void report_timeout(uint32_t *status) {
+  __hip_atomic_store(status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 struct WorkerSmem {
   float red[kFW][kWave * 8];
@@ -103,18 +120,12 @@ __device__ __forceinline__ void lds_store(uint32_t *p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
-}
-
 // Decodes a release word into sm.
 __device__ __forceinline__ void take_word(uint64_t w, FusedSmem &sm) {
-  const uint32_t stage = static_cast<uint32_t>(w >> kStageShift) & 3u;
+  const uint32_t stage = word_stage(w);
   if (stage == 2) {
-    const uint32_t T = static_cast<uint32_t>(w >> 16) & 0x7FFFFFFFu;
-    const uint32_t c = static_cast<uint32_t>(w) & 0xFFFFu;
+    const uint32_t T = static_cast<uint32_t>(w >> 15) & 0x7FFFFFFFu;
+    const uint32_t c = static_cast<uint32_t>(w) & kCutAll;
     sm.T = T;
     sm.cut = c == kCutAll ? 0xFFFFFFFFu : c;
     sm.b0 = T >> 20;
@@ -124,21 +135,21 @@ __device__ __forceinline__ void take_word(uint64_t w, FusedSmem &sm) {
   lds_store(&sm.stage, stage);
 }
 
-// Polls this workgroup's release line until a word of at least `stage`
-// arrives (bounded); decodes it into sm.
-__device__ __forceinline__ void wait_word(uint64_t *line, uint32_t stage, uint32_t *err,
-                                          FusedSmem &sm) {
+// Polls this workgroup's release line until a word of this launch's epoch
+// and at least `stage` arrives (bounded); decodes it into sm.
+__device__ __forceinline__ void wait_word(uint64_t *line, uint32_t stage, uint32_t epoch,
+                                          uint32_t spin_limit, uint32_t *status, FusedSmem &sm) {
   uint32_t spins = 0;
   uint64_t w;
   for (;;) {
     w = __hip_atomic_load(line, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((w & kWord) && (static_cast<uint32_t>(w >> kStageShift) & 3u) >= stage) break;
-    __builtin_amdgcn_s_sleep(1);
-    if (++spins > kSpinLimit) {
-      __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      w = kWord | (2ull << kStageShift);  // T = 0, cut = 0: keeps every channel of a unit
+    if (word_epoch(w) == epoch && word_stage(w) >= stage) break;
+    if (spins++ >= spin_limit) {
+      report_timeout(status);
+      w = make_word(epoch, 2, 0);  // T = 0, cut = 0: keeps every channel of a unit
       break;
     }
+    __builtin_amdgcn_s_sleep(1);
   }
   take_word(w, sm);
 }
@@ -169,32 +180,31 @@ __device__ __forceinline__ uint32_t selector_pass(int pass, const uint32_t *key,
 
 // Selector (workgroup 0): waits for the arrivals, selects, releases.
 __device__ __forceinline__ void select_and_release(const float *x_rot, int d, int k,
-                                                   uint32_t *sync, uint64_t *flags,
-                                                   int32_t *idx_out, FusedSmem &sm) {
+                                                   const uint32_t *arrive, uint64_t *flags,
+                                                   int32_t *idx_out, uint32_t epoch,
+                                                   uint32_t spin_limit, uint32_t *status,
+                                                   FusedSmem &sm) {
   const int t = threadIdx.x;
   const uint32_t G = gridDim.x;
   SelectSmem<kFT> &sel = sm.s.sel;
   uint32_t *key = sm.s.key;
   if (t < kWave) {
+    // every worker writes this launch's epoch into its own slot on arrival
     uint32_t spins = 0;
     for (;;) {
-      const uint32_t c = t < kGroups ? __hip_atomic_load(&sync[32 * (1 + t)], __ATOMIC_RELAXED,
-                                                         __HIP_MEMORY_SCOPE_AGENT)
-                                     : 0u;
-      if (wave_sum_u32(c) >= G - 1) break;
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > kSpinLimit) {
-        if (t == 0)
-          __hip_atomic_store(&sync[kErrWord], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      bool in = true;
+      for (uint32_t b = 1 + t; b < G; b += kWave)
+        in = in && __hip_atomic_load(&arrive[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch;
+      if (__all(in)) break;
+      if (spins++ >= spin_limit) {
+        if (t == 0) report_timeout(status);
         break;
       }
+      __builtin_amdgcn_s_sleep(1);
     }
-    // every worker has arrived: the counters are free for the next call
-    if (t < kGroups)
-      __hip_atomic_store(&sync[32 * (1 + t)], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
-  release_all(flags, kWord);  // stage 0: x_rot is complete
+  release_all(flags, make_word(epoch, 0, 0));  // stage 0: x_rot is complete
   // the acquire fence makes the workers' x_rot stores visible to ordinary
   // (vector) loads here
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -219,7 +229,7 @@ __device__ __forceinline__ void select_and_release(const float *x_rot, int d, in
   // first digit: bin B0 of the K-th largest key; release the preliminary rule
   uint32_t prefix = 0, pmask = kNoKey, krem = static_cast<uint32_t>(k);
   selector_pass(0, key, d, prefix, pmask, krem, sel);  // its first barrier covers the key stores
-  release_all(flags, kWord | (1ull << kStageShift) | (prefix >> 20));
+  release_all(flags, make_word(epoch, 1, prefix >> 20));
 
   // remaining digits: T, and the count of keys equal to T
   uint32_t n_eq = 0;
@@ -249,7 +259,7 @@ __device__ __forceinline__ void select_and_release(const float *x_rot, int d, in
     cut = sel.bin;
   }
   __builtin_amdgcn_s_waitcnt(0);  // earlier words are out first
-  release_all(flags, kWord | (2ull << kStageShift) | (static_cast<uint64_t>(T) << 16) | cut);
+  release_all(flags, make_word(epoch, 2, (static_cast<uint64_t>(T) << 15) | cut));
 
   // optional copy of the kept indices, ascending
   if (idx_out) {
@@ -295,9 +305,10 @@ template <typename T>
 __global__ __launch_bounds__(kFT) void fused_linear_kernel(
     const T *__restrict__ x, const T *__restrict__ qt, const T *__restrict__ wf,
     T *__restrict__ y, int d, int qb, int64_t d_out, int k, float *__restrict__ x_rot,
-    uint32_t *__restrict__ sync, uint64_t *__restrict__ flags,
+    uint32_t *__restrict__ arrive, uint64_t *__restrict__ flags,
     uint32_t *__restrict__ tile_ctr, float *__restrict__ partials,
-    int32_t *__restrict__ idx_out, int tiles, int splits, int chans_per_split) {
+    int32_t *__restrict__ idx_out, int tiles, int splits, int chans_per_split, uint32_t epoch,
+    uint32_t spin_limit, uint32_t *__restrict__ status) {
   constexpr int V = Elt<T>::kVec;
   constexpr int TILE = kWave * V;
   extern __shared__ __align__(16) unsigned char fused_lds[];
@@ -328,7 +339,7 @@ __global__ __launch_bounds__(kFT) void fused_linear_kernel(
 
   // ---- 2. selector ---------------------------------------------------------
   if (blockIdx.x == 0) {
-    select_and_release(x_rot, d, k, sync, flags, idx_out, sm);
+    select_and_release(x_rot, d, k, arrive, flags, idx_out, epoch, spin_limit, status, sm);
     return;
   }
 
@@ -336,9 +347,8 @@ __global__ __launch_bounds__(kFT) void fused_linear_kernel(
   // then the preliminary (or already the exact) rule ------------------------
   uint64_t *line = &flags[blockIdx.x * 16];
   if (t == 0) {
-    __hip_atomic_fetch_add(&sync[32 * (1 + blockIdx.x % kGroups)], 1u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    wait_word(line, 0, &sync[kErrWord], sm);
+    __hip_atomic_store(&arrive[blockIdx.x], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wait_word(line, 0, epoch, spin_limit, status, sm);
   }
   __syncthreads();
   const uint32_t W = G - 1;
@@ -356,7 +366,7 @@ __global__ __launch_bounds__(kFT) void fused_linear_kernel(
     }
   };
   if (static_cast<int>(blockIdx.x) - 1 < units) load_slice(blockIdx.x - 1);
-  if (t == 0 && lds_load(&sm.stage) < 1) wait_word(line, 1, &sync[kErrWord], sm);
+  if (t == 0 && lds_load(&sm.stage) < 1) wait_word(line, 1, epoch, spin_limit, status, sm);
   __syncthreads();
 
   // ---- 3. gather over units (column tile, channel range) -----------------
@@ -423,7 +433,8 @@ __global__ __launch_bounds__(kFT) void fused_linear_kernel(
       }
       won = __shfl(won, 0, kWave);
       if (won) {
-        if (lane == 0 && lds_load(&sm.stage) < 2) wait_word(line, 2, &sync[kErrWord], sm);
+        if (lane == 0 && lds_load(&sm.stage) < 2)
+          wait_word(line, 2, epoch, spin_limit, status, sm);
         __builtin_amdgcn_wave_barrier();
         const uint32_t Tk = __shfl(lane == 0 ? sm.T : 0u, 0, kWave);
         const uint32_t cut = __shfl(lane == 0 ? sm.cut : 0u, 0, kWave);
@@ -449,7 +460,13 @@ __global__ __launch_bounds__(kFT) void fused_linear_kernel(
         if (lane == 0) lds_store(&sm.tail, m + 1);
       }
       uint32_t tn, spins = 0;
-      while ((tn = lds_load(&sm.tail)) == 0u && ++spins < kSpinLimit) __builtin_amdgcn_s_sleep(1);
+      while ((tn = lds_load(&sm.tail)) == 0u) {
+        if (spins++ >= spin_limit) {
+          if (lane == 0) report_timeout(status);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
       n = tn > 0 ? static_cast<int>(tn - 1) : ns;
     }
     const int ng = (n + kFRows - 1) / kFRows;
@@ -508,13 +525,6 @@ __global__ __launch_bounds__(kFT) void fused_linear_kernel(
     }
     __syncthreads();  // LDS lists and reduction buffer are reused by the next unit
   }
-
-  // the exact rule always follows the preliminary one: take it before
-  // clearing the line for the next call
-  if (t == 0) {
-    if (lds_load(&sm.stage) < 2) wait_word(line, 2, &sync[kErrWord], sm);
-    __hip_atomic_store(line, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
 }
 
 // Workgroups of the kernel resident at once on the current device, for a
@@ -553,7 +563,10 @@ hipError_t launch_t(const FusedArgs &a, hipStream_t s) {
   if (capacity > kFusedMaxGrid) capacity = kFusedMaxGrid;
   const FusedPlan p = plan_fused(a.d_in, a.d_out, a.k, a.w_dt, capacity);
   char *ws = static_cast<char *>(a.ws);
-  uint32_t *sync = reinterpret_cast<uint32_t *>(ws);
+  uint32_t *arrive = reinterpret_cast<uint32_t *>(ws);
+  // 1 .. 65535, a different one for each launch (16 bits of the words)
+  static std::atomic<uint32_t> launches{0};
+  const uint32_t epoch = launches.fetch_add(1u) % 65535u + 1u;
   uint32_t *tile_ctr = reinterpret_cast<uint32_t *>(ws + p.tile_off);
   uint64_t *flags = reinterpret_cast<uint64_t *>(ws + p.flags_off);
   float *x_rot = a.xrot_out ? a.xrot_out : reinterpret_cast<float *>(ws + p.xrot_off);
@@ -561,8 +574,8 @@ hipError_t launch_t(const FusedArgs &a, hipStream_t s) {
   hipLaunchKernelGGL((fused_linear_kernel<T>), dim3(p.grid), dim3(kFT), lds, s,
                      static_cast<const T *>(a.x), static_cast<const T *>(a.qt),
                      static_cast<const T *>(a.wf), static_cast<T *>(a.y), a.d_in, a.q_block,
-                     a.d_out, a.k, x_rot, sync, flags, tile_ctr, partials, a.idx_out,
-                     p.tiles, p.splits, p.chans_per_split);
+                     a.d_out, a.k, x_rot, arrive, flags, tile_ctr, partials, a.idx_out,
+                     p.tiles, p.splits, p.chans_per_split, epoch, a.spin_limit, a.status);
   return hipGetLastError();
 }
 
@@ -587,7 +600,7 @@ FusedPlan plan_fused(int64_t d_in, int64_t d_out, int64_t k, int w_dt, int grid)
   const int64_t cps = (d_in + splits - 1) / splits;
   p.splits = static_cast<int>((d_in + cps - 1) / cps);
   p.chans_per_split = static_cast<int>(cps);
-  p.tile_off = up256(static_cast<size_t>(32 * (kGroups + 2)) * 4);
+  p.tile_off = up256(static_cast<size_t>(kFusedMaxGrid) * 4);  // arrival slots
   p.flags_off = p.tile_off + up256(static_cast<size_t>(p.tiles) * 4);
   p.xrot_off = p.flags_off + static_cast<size_t>(kFusedMaxGrid) * 128;
   p.partial_off = p.xrot_off + up256(static_cast<size_t>(d_in) * 4);

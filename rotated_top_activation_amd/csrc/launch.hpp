@@ -11,6 +11,16 @@ enum Dt { kF32 = 0, kBF16 = 1 };
 
 inline int dt_size(int dt) { return dt == kF32 ? 4 : 2; }
 
+// Status code a bounded device-side wait that gave up writes into the
+// status word of its workspace (LAROSA_ERR_TIMEOUT of the C ABI).
+constexpr uint32_t kStatusTimeout = 9;
+
+// --- status word and debug checks ---
+// *flag = 1 if any of x[0 .. n) is NaN or ±inf, else 0 (flag cleared first).
+hipError_t launch_flag_nonfinite(const float *x, int64_t n, uint32_t *flag, hipStream_t s);
+// *out = *word; *word = 0 (one thread, stream order).
+hipError_t launch_take_status(uint32_t *word, int32_t *out, hipStream_t s);
+
 // --- rotation (dot product per output channel against the prepared Qt) ---
 hipError_t launch_rotate(const void *x, int x_dt, const void *qt, int q_dt,
                          float *x_rot, int B, int d, int qb, hipStream_t s);
@@ -191,6 +201,8 @@ struct FusedArgs {
   int32_t *idx_out;   // may be NULL
   float *xrot_out;    // may be NULL (x_rot then lives in the workspace)
   void *ws;           // plan_fused(..., kFusedMaxGrid).bytes, zeroed before first use
+  uint32_t *status;   // status word: kStatusTimeout when a bounded wait gave up
+  uint32_t spin_limit = 1u << 22;  // polls before a wait gives up
 };
 hipError_t launch_fused_linear(const FusedArgs &a, hipStream_t s);
 

@@ -150,7 +150,42 @@ __global__ void fill_zero_kernel(uint8_t *__restrict__ p, size_t bytes) {
   if (blockIdx.x == 0 && threadIdx.x < tail) p[n16 * 16 + threadIdx.x] = 0;
 }
 
+// LAROSA_VALIDATE's check: the exponent field all ones marks NaN and ±inf.
+__global__ void flag_nonfinite_kernel(const float *__restrict__ x, int64_t n,
+                                      uint32_t *__restrict__ flag) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  uint32_t bad = 0;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
+    bad |= (__float_as_uint(x[i]) & 0x7F800000u) == 0x7F800000u;
+  if (__any(bad) && threadIdx.x % kWave == 0)
+    __hip_atomic_fetch_or(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ void take_status_kernel(uint32_t *__restrict__ word, int32_t *__restrict__ out) {
+  if (threadIdx.x == 0) {
+    out[0] = static_cast<int32_t>(word[0]);
+    word[0] = 0u;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_flag_nonfinite(const float *x, int64_t n, uint32_t *flag, hipStream_t s) {
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(1), dim3(64), 0, s, reinterpret_cast<uint8_t *>(flag),
+                     sizeof(uint32_t));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || n <= 0) return e;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(flag_nonfinite_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, x,
+                     n, flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_take_status(uint32_t *word, int32_t *out, hipStream_t s) {
+  hipLaunchKernelGGL(take_status_kernel, dim3(1), dim3(64), 0, s, word, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_transpose_blocks(const void *q, void *qt, int64_t d, int64_t qb,
                                    int dt, hipStream_t s) {

@@ -14,7 +14,7 @@ from rotated_top_activation_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "larosa.h")
 
-OK, INVALID, SHAPE, ALIGN, DTYPE, WS, NODEV, LAUNCH = range(8)
+OK, INVALID, SHAPE, ALIGN, DTYPE, WS, NODEV, LAUNCH, NONFINITE, TIMEOUT, INTERNAL = range(11)
 P = 0x10000          # a fake, 16-byte aligned device address
 PM = 0x10008         # a fake, misaligned one
 
@@ -44,8 +44,8 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.larosa_abi_version() == _lib.ABI_VERSION
-    for code in range(8):
-        assert lib.larosa_status_string(code)
+    for code in range(11):
+        assert lib.larosa_status_string(code) != b"unknown status"
     assert lib.larosa_status_string(99) == b"unknown status"
 
 
@@ -55,10 +55,12 @@ def test_workspace_bytes(lib):
     assert f(1, 4096, 22016, 0, 0) == 0          # k out of range
     assert f(1, 4096, 22016, 4097, 0) == 0
     assert f(1, 40000, 128, 10, 0) == 0          # d above 32768
-    assert f(1, 4096, 22016, 2457, 7) == 0       # unknown mode bit
-    assert f(1, 4096, 22016, 2457, 4) == 0
-    # the fp64-rotation flag needs no extra workspace
+    assert f(1, 4096, 22016, 2457, 8) == 0       # unknown mode bit
+    assert f(1, 4096, 22016, 2457, 9) == 0
+    # the fp64-rotation and validate flags need no extra workspace
     assert f(1, 4096, 22016, 2457, 2) == f(1, 4096, 22016, 2457, 0)
+    assert f(1, 4096, 22016, 2457, 4) == f(1, 4096, 22016, 2457, 0)
+    assert f(1, 4096, 22016, 2457, 7) == f(1, 4096, 22016, 2457, 1)
     assert f(4, 4096, 22016, 2457, 3) == f(4, 4096, 22016, 2457, 1)
     assert f(8, 4096, 22016, 2457, 0) >= f(1, 4096, 22016, 2457, 0)
 
@@ -74,9 +76,10 @@ def test_layer_forward_validation(lib):
     assert _lf(lib, k=129) == INVALID
     assert _lf(lib, B=-1) == INVALID
     assert _lf(lib, B=65) == INVALID
-    assert _lf(lib, mode=4) == INVALID
-    assert _lf(lib, mode=6) == INVALID
-    assert _lf(lib, mode=2, k=0) == INVALID      # the flag does not skip the checks
+    assert _lf(lib, mode=8) == INVALID
+    assert _lf(lib, mode=12) == INVALID
+    assert _lf(lib, mode=2, k=0) == INVALID      # the flags do not skip the checks
+    assert _lf(lib, mode=4, k=0) == INVALID
     assert _lf(lib, x=None) == INVALID
     assert _lf(lib, y=None) == INVALID
     assert _lf(lib, qb=48) == SHAPE             # does not divide 128
@@ -104,7 +107,7 @@ def test_standalone_calls_validation(lib):
     assert lib.larosa_rotate_fp64(PM, 1, P, 64, 1, P, 1, 128, None) == ALIGN
     assert lib.larosa_rotate_fp64(P, 1, P, 60, 1, P, 1, 120, None) == ALIGN  # d % 8, bf16
     assert lib.larosa_rotate_fp64(P, 1, P, 64, 1, P, 0, 128, None) == OK     # empty batch
-    assert lib.larosa_swiglu_layer_forward(P, 1, P, 64, P, 1, 1, 128, 256, 10, P, None, None, 5,
+    assert lib.larosa_swiglu_layer_forward(P, 1, P, 64, P, 1, 1, 128, 256, 10, P, None, None, 9,
                                            P, 1 << 24, None) == INVALID
     assert lib.larosa_topk_select(P, 1, 128, 0, P, P, None, None, None, None, None, 0,
                                   None) == INVALID
@@ -166,7 +169,7 @@ def test_threshold_calls_validation(lib):
     args = (P, 1, P, 64, P, 1, 1, 128, 64)
     assert tl(*args, -0.5, P, None, None, None, 0, P, 1 << 30, None) == INVALID
     assert tl(*args, nan, P, None, None, None, 0, P, 1 << 30, None) == INVALID
-    assert tl(*args, 0.5, P, None, None, None, 4, P, 1 << 30, None) == INVALID
+    assert tl(*args, 0.5, P, None, None, None, 8, P, 1 << 30, None) == INVALID
     assert tl(*args, 0.5, P, None, None, None, 0, P, 16, None) == WS
     assert tl(P, 1, P, 48, P, 1, 1, 128, 64, 0.5, P, None, None, None, 0, P, 1 << 30,
               None) == SHAPE
@@ -191,7 +194,7 @@ def test_lowrank_validation(lib):
     assert call(r=65) == INVALID                  # above d_out = 64
     assert call(a=None) == INVALID
     assert call(wext=None) == INVALID
-    assert call(mode=4) == INVALID
+    assert call(mode=8) == INVALID
     assert call(k=0) == INVALID
     assert call(qb=48) == SHAPE
     assert call(wext=PM) == ALIGN
@@ -213,3 +216,26 @@ def test_no_device_is_reported_not_crashed(lib):
     assert lib.larosa_rotate_fp64(P, 1, P, 64, 1, P + (1 << 20), 1, 128, None) == NODEV
     assert lib.larosa_swiglu(P, P + (1 << 20), 1, 64, 1, None) == NODEV
     assert lib.larosa_topk_gemv(P, 128, 10, P, 1, P, 1, 64, None, P, 1 << 20, None) == NODEV
+    assert _lf(lib, mode=_lib.VALIDATE) == NODEV
+    assert lib.larosa_workspace_status(P, P + 256, None) == NODEV
+
+
+def test_workspace_status_and_spin_limit_arguments(lib):
+    st = lib.larosa_workspace_status
+    assert st(None, P, None) == INVALID
+    assert st(P, None, None) == INVALID
+    assert st(PM, P, None) == ALIGN
+    assert st(P, P + 2, None) == ALIGN           # status_out not 4-byte aligned
+    prev = lib.larosa_set_spin_limit(7)
+    assert prev == 1 << 22                       # the documented default
+    assert lib.larosa_set_spin_limit(prev) == 7
+    assert lib.larosa_set_spin_limit(prev) == prev
+
+
+def test_entry_points_are_declared_no_throw():
+    """Every declaration in the header carries the no-throw marker, and the
+    C++ definitions repeat it (a mismatch would not compile)."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    decls = re.findall(r"\b(larosa_\w+)\s*\([^;]*\)\s*(LAROSA_NOEXCEPT)?\s*;", text)
+    assert decls
+    assert all(mark for _, mark in decls), [n for n, mark in decls if not mark]

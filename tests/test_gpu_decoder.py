@@ -134,9 +134,10 @@ def _base(cfg):
     return base, D.upload_base(base), wl.kv_cache_base(cfg, shape)
 
 
-def run_decoder(B, sparsity, n_layers, mode, n_checked=None, seed_cols=0):
+def run_decoder(B, sparsity, n_layers, mode, n_checked=None, seed_cols=0, check_every=1):
     """Run n_layers of the 7B-shaped decoder on one batch and check every
-    layer (or the first n_checked) against the oracle, teacher-forced."""
+    layer (or the first n_checked, or every check_every-th and the last)
+    against the oracle, teacher-forced."""
     cfg = 3
     shape = wl.LLAMA7B
     base, base_dev, (kb, vb) = _base(cfg)
@@ -152,7 +153,9 @@ def run_decoder(B, sparsity, n_layers, mode, n_checked=None, seed_cols=0):
         trace = {}
         D.layer_forward(layer, h, buf, mode=mode, trace=trace)
         torch.cuda.synchronize()
-        if n_checked is not None and checked >= n_checked:
+        skip = (n_checked is not None and checked >= n_checked) or \
+            (l % check_every != 0 and l != n_layers - 1)
+        if skip:
             del layer
             continue
         checked += 1
@@ -207,3 +210,19 @@ def test_decoder_layer_fused_single_token():
 def test_decoder_32_layers(B, sp):
     """The full 32-layer decode step; every layer checked."""
     run_decoder(B, sp, n_layers=32, mode=_lib.FUSED if B == 1 else _lib.UNFUSED)
+
+
+@pytest.mark.parametrize("sp", [25, 40, 50])
+def test_decoder_32_layers_single_token_unfused(sp):
+    """One token through 32 layers in the mode the benchmark reports (one
+    launch for the selection and product after each rotation); every layer
+    checked."""
+    run_decoder(1, sp, n_layers=32, mode=_lib.UNFUSED)
+
+
+@pytest.mark.parametrize("B,sp", [(4, 25), (4, 50), (16, 25), (16, 50)])
+def test_decoder_32_layers_batch_sparsity_grid(B, sp):
+    """The rest of the batch x sparsity grid of the 32-layer step (4 and 16
+    tokens at 25% and 50%): all 32 layers run, every fourth and the last are
+    checked."""
+    run_decoder(B, sp, n_layers=32, mode=_lib.UNFUSED, check_every=4)
