@@ -252,6 +252,27 @@ int larosa_layer_forward(const void *x, int act_dtype, const void *Qt,
                          void *y, int32_t *idx_out, float *xrot_out, int mode,
                          void *ws, size_t ws_bytes, larosa_stream_t stream) LAROSA_NOEXCEPT;
 
+/* larosa_layer_forward for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without the workspace, whose place takes
+ * a 16 MiB device-resident array of the library (one per GPU, held until
+ * the process ends). The call itself allocates nothing. Requests needing
+ * more than 16 MiB (larosa_workspace_bytes of the sizes) return
+ * LAROSA_ERR_WORKSPACE before any work; mode must be LAROSA_UNFUSED,
+ * optionally with LAROSA_ROTATE_FP64 or LAROSA_VALIDATE
+ * (LAROSA_ERR_INVALID_ARG otherwise: the one-launch form reports through a
+ * workspace the caller could not read). The array is zero-filled on the
+ * first call on a device and again whenever the sizes, mode or types differ
+ * from the previous call's on that device (a fill kernel on `stream`).
+ * Every call on one GPU shares its array: calls that overlap on one GPU
+ * (from two streams or two host threads) race. Other arguments, outputs
+ * and errors as larosa_layer_forward. */
+int larosa_layer_forward_noalloc(const void *x, int act_dtype, const void *Qt,
+                                 int64_t q_block, const void *W_folded, int w_dtype,
+                                 int64_t B, int64_t d_in, int64_t d_out, int64_t k,
+                                 void *y, int32_t *idx_out, float *xrot_out, int mode,
+                                 larosa_stream_t stream) LAROSA_NOEXCEPT;
+
 /* Dense reference product y = x·W over every row of W, with the same
  * streaming and fp32 accumulation as larosa_sparse_gemv. x: [B, d_in] and
  * y: [B, d_out] in act_dtype; W: [d_in, d_out] in w_dtype. The baseline that

@@ -54,6 +54,9 @@ SIGNATURES = {
     "larosa_layer_forward": (_c_int, [_c_vp, _c_int, _c_vp, _c_i64, _c_vp, _c_int, _c_i64,
                                       _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_int,
                                       _c_vp, _c_sz, _c_vp]),
+    "larosa_layer_forward_noalloc": (_c_int, [_c_vp, _c_int, _c_vp, _c_i64, _c_vp, _c_int,
+                                              _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp,
+                                              _c_vp, _c_int, _c_vp]),
     "larosa_dense_gemv": (_c_int, [_c_vp, _c_int, _c_vp, _c_int, _c_vp, _c_i64, _c_i64, _c_i64,
                                    _c_vp, _c_sz, _c_vp]),
     "larosa_swiglu": (_c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_vp]),
@@ -229,6 +232,16 @@ def larosa_layer_forward(x, Qt, q_block: int, W_folded, B: int, d_in: int, d_out
                                        _dt(W_folded), B, d_in, d_out, k, _ptr(y), _ptr(idx_out),
                                        _ptr(xrot_out), mode, _ptr(ws), _nbytes(ws),
                                        _stream(stream)))
+
+
+def larosa_layer_forward_noalloc(x, Qt, q_block: int, W_folded, B: int, d_in: int, d_out: int,
+                                 k: int, y, idx_out=None, xrot_out=None, mode: int = UNFUSED,
+                                 stream=None) -> None:
+    _check("larosa_layer_forward_noalloc",
+           load().larosa_layer_forward_noalloc(_ptr(x), _dt(x), _ptr(Qt), q_block,
+                                               _ptr(W_folded), _dt(W_folded), B, d_in, d_out, k,
+                                               _ptr(y), _ptr(idx_out), _ptr(xrot_out), mode,
+                                               _stream(stream)))
 
 
 def larosa_dense_gemv(x, W, y, B: int, d_in: int, d_out: int, ws=None, stream=None) -> None:

@@ -223,11 +223,11 @@ struct Sel {
   int32_t *count_out = nullptr;
 };
 
-int layer_entry(const void *x, int act_dtype, const void *Qt, int64_t q_block,
-                const void *W_folded, int w_dtype, int64_t B, int64_t d_in, int64_t d_out,
-                const Sel &sel, void *y, int32_t *idx_out, float *xrot_out, int mode, void *ws,
-                size_t ws_bytes, larosa_stream_t stream) {
-  const int64_t k = sel.k;
+// The argument checks of a layer call, apart from the workspace. B == 0
+// passes (the caller returns LAROSA_OK without work).
+int layer_args(const void *x, int act_dtype, const void *Qt, int64_t q_block,
+               const void *W_folded, int w_dtype, int64_t B, int64_t d_in, int64_t d_out,
+               int64_t k, const void *y, const float *xrot_out, int mode) {
   if (!dtype_ok(act_dtype) || !dtype_ok(w_dtype)) return LAROSA_ERR_DTYPE;
   if (w_dtype == LAROSA_F32 && act_dtype == LAROSA_BF16) return LAROSA_ERR_DTYPE;
   if (int st = check_sizes(B, d_in, k)) return st;
@@ -239,7 +239,20 @@ int layer_entry(const void *x, int act_dtype, const void *Qt, int64_t q_block,
   if (d_in % vec_of(act_dtype) || d_out % vec_of(w_dtype)) return LAROSA_ERR_ALIGNMENT;
   if (!aligned16(x) || !aligned16(Qt) || !aligned16(W_folded) || !aligned16(y))
     return LAROSA_ERR_ALIGNMENT;
-  if ((xrot_out && !aligned16(xrot_out)) || !aligned16(ws)) return LAROSA_ERR_ALIGNMENT;
+  if (xrot_out && !aligned16(xrot_out)) return LAROSA_ERR_ALIGNMENT;
+  return LAROSA_OK;
+}
+
+int layer_entry(const void *x, int act_dtype, const void *Qt, int64_t q_block,
+                const void *W_folded, int w_dtype, int64_t B, int64_t d_in, int64_t d_out,
+                const Sel &sel, void *y, int32_t *idx_out, float *xrot_out, int mode, void *ws,
+                size_t ws_bytes, larosa_stream_t stream) {
+  const int64_t k = sel.k;
+  if (int st = layer_args(x, act_dtype, Qt, q_block, W_folded, w_dtype, B, d_in, d_out, k, y,
+                          xrot_out, mode))
+    return st;
+  if (B == 0) return LAROSA_OK;
+  if (!aligned16(ws)) return LAROSA_ERR_ALIGNMENT;
   const bool f64 = fp64_rotation(mode);
   const bool check = validating(mode);
   const bool fused = base_mode(mode) == LAROSA_FUSED && !f64 && !check && !sel.thr &&
@@ -905,6 +918,34 @@ int larosa_layer_forward(const void *x, int act_dtype, const void *Qt, int64_t q
   sel.k = k;
   return layer_entry(x, act_dtype, Qt, q_block, W_folded, w_dtype, B, d_in, d_out, sel, y,
                      idx_out, xrot_out, mode, ws, ws_bytes, stream);
+  });
+}
+
+int larosa_layer_forward_noalloc(const void *x, int act_dtype, const void *Qt, int64_t q_block,
+                                 const void *W_folded, int w_dtype, int64_t B, int64_t d_in,
+                                 int64_t d_out, int64_t k, void *y, int32_t *idx_out,
+                                 float *xrot_out, int mode, larosa_stream_t stream) LAROSA_NOEXCEPT {
+  return guard([&]() -> int {
+  // The one-launch form reports its bounded waits through the workspace,
+  // which this caller cannot read: only the unfused steps run here.
+  if (base_mode(mode) != LAROSA_UNFUSED) return LAROSA_ERR_INVALID_ARG;
+  Sel sel;
+  sel.k = k;
+  const size_t need = larosa_workspace_bytes(B, d_in, d_out, k, mode);
+  if (need == 0 || B == 0)  // invalid sizes or an empty batch: the checks name it
+    return layer_entry(x, act_dtype, Qt, q_block, W_folded, w_dtype, B, d_in, d_out, sel, y,
+                       idx_out, xrot_out, mode, nullptr, 0, stream);
+  // every argument check of the layer call before the scratch is touched
+  if (int st = layer_args(x, act_dtype, Qt, q_block, W_folded, w_dtype, B, d_in, d_out, k, y,
+                          xrot_out, mode))
+    return st;
+  if (need > scratch_capacity()) return LAROSA_ERR_WORKSPACE;
+  if (int st = device_status()) return st;
+  ScratchShape shape{B, d_in, d_out, k, mode, act_dtype, w_dtype};
+  void *ws = nullptr;
+  if (scratch_acquire(shape, need, stream_of(stream), &ws) != hipSuccess) return LAROSA_ERR_LAUNCH;
+  return layer_entry(x, act_dtype, Qt, q_block, W_folded, w_dtype, B, d_in, d_out, sel, y,
+                     idx_out, xrot_out, mode, ws, need, stream);
   });
 }
 

@@ -206,6 +206,17 @@ struct FusedArgs {
 };
 hipError_t launch_fused_linear(const FusedArgs &a, hipStream_t s);
 
+// --- device-resident workspace of larosa_layer_forward_noalloc ---
+struct ScratchShape {
+  int64_t B, d_in, d_out, k;
+  int mode, act_dt, w_dt;
+};
+size_t scratch_capacity();
+// This device's scratch address in *out, zero-filled on `s` first when the
+// shape differs from the previous call's on this device (need bytes).
+// hipErrorInvalidValue when need exceeds scratch_capacity().
+hipError_t scratch_acquire(const ScratchShape &shape, size_t need, hipStream_t s, void **out);
+
 // --- offline preparation ---
 hipError_t launch_transpose_blocks(const void *q, void *qt, int64_t d, int64_t qb,
                                    int dt, hipStream_t s);
