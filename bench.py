@@ -52,6 +52,8 @@ def source_digest(kernel: str) -> str:
 def measured_traffic(kernel: str):
     """HBM bytes per launch from the committed counter runs, or None when the
     kernel's sources changed since the counters were taken."""
+    if kernel not in KERNEL_SOURCES:
+        return None
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f).get(kernel)
@@ -71,13 +73,13 @@ def parse():
     p.add_argument("--mode", choices=["unfused", "fused", "best"], default="best")
     p.add_argument("--sparsity", type=int, default=40)
     p.add_argument("--q2-block", type=int, default=0)
-    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-configs", action="store_true",
                    help="skip the other workloads (single linear, decoder step, layer slices)")
     p.add_argument("--config-steps", type=int, default=20)
-    p.add_argument("--kernel-only", choices=["", "gather", "topk1", "fused1", "step", "copy",
-                                             "configs"],
+    p.add_argument("--kernel-only", choices=["", "gather", "topk1", "topk1s", "topk2", "fused1",
+                                             "step", "copy", "configs"],
                    default="",
                    help="only launch that work (for profiler runs)")
     return p.parse_args()
@@ -216,6 +218,9 @@ def main():
     def topk1(i):
         _lib.larosa_topk_gemv(xr1, d, case.k1, wf1[i % copies], gu, 2 * f, ws=ws1)
 
+    def topk1s(i):  # the step's own gate|up kernel: SiLU(gate)·up folded in
+        _lib.larosa_topk_swiglu_gemv(xr1, d, case.k1, wil1[i % copies], h, f, ws=ws1)
+
     def topk2(i):
         _lib.larosa_topk_gemv(xr2, f, case.k2, wf2[i % copies], y, d, ws=ws2)
 
@@ -227,14 +232,19 @@ def main():
         c = i % copies
         _lib.larosa_layer_forward(x_d, qt1[c], l1.q_block, wf1[c], 1, d, 2 * f, case.k1, gu,
                                   mode=_lib.FUSED, ws=ws1)
-    if a.kernel_only in ("gather", "topk1", "fused1"):
-        fn = {"gather": gather, "topk1": topk1, "fused1": fused1}[a.kernel_only]
+    if a.kernel_only in ("gather", "topk1", "topk1s", "topk2", "fused1"):
+        fn = {"gather": gather, "topk1": topk1, "topk1s": topk1s, "topk2": topk2,
+              "fused1": fused1}[a.kernel_only]
         for i in range(a.steps):
             fn(i)
         torch.cuda.synchronize()
         return
     topk1_ms = timed(topk1, a.steps, a.warmup)
     topk1_bytes = case.k1 * 2 * f * 2 + d * 4 + 2 * f * 2
+    topk1s_ms = timed(topk1s, a.steps, a.warmup)
+    topk1s_bytes = case.k1 * 2 * f * 2 + d * 4 + f * 2
+    topk2_ms = timed(topk2, a.steps, a.warmup)
+    topk2_bytes = case.k2 * d * 2 + f * 4 + d * 2
     gather_ms = timed(gather, a.steps, a.warmup)
     gather_bytes = case.k1 * 2 * f * 2 + case.k1 * 8 + 2 * f * 2
     fused1_ms = timed(fused1, a.steps, a.warmup)
@@ -254,11 +264,33 @@ def main():
     def gbs(nbytes, ms_):
         return nbytes / (ms_ * 1e-3) / 1e9
 
+    # The dense MLP step on the same GPU: dense gate|up, SiLU(gate)·up, dense
+    # down, over weights of the same shapes (cycling the same copies), with
+    # the faster of this library's dense product and torch.matmul.
+    ws_d2 = torch.zeros(_lib.larosa_workspace_bytes(1, f, d, f, _lib.UNFUSED), dtype=torch.uint8,
+                        device=dev)
+
+    def dense_mlp(i, use_torch):
+        c = i % copies
+        if use_torch:
+            torch.matmul(x_d, wf1[c], out=gu)
+            _lib.larosa_swiglu(gu, h, 1, f)
+            torch.matmul(h, wf2[c], out=y)
+        else:
+            _lib.larosa_dense_gemv(x_d, wf1[c], gu, 1, d, 2 * f, ws=ws1)
+            _lib.larosa_swiglu(gu, h, 1, f)
+            _lib.larosa_dense_gemv(h, wf2[c], y, 1, f, d, ws=ws_d2)
+    dense_mlp_ms = {
+        "larosa_dense_gemv": timed(lambda i: dense_mlp(i, False), a.steps, a.warmup),
+        "torch.matmul": timed(lambda i: dense_mlp(i, True), a.steps, a.warmup),
+    }
+    copy = copy_ceiling(dev, timed, a.steps, a.warmup)
+
     # Per-stage times of the unfused step (each stage alone, cycling copies).
     stage = {}
     stage["rotate1"] = timed(lambda i: _lib.larosa_rotate(x_d, qt1[i % copies], l1.q_block, xr1,
                                                           1, d), a.steps, a.warmup)
-    stage["select_gather1"] = topk1_ms
+    stage["select_gather1"] = topk1s_ms
     stage["swiglu_alone"] = timed(lambda i: _lib.larosa_swiglu(gu, h, 1, f), a.steps, a.warmup)
     stage["rotate2"] = timed(lambda i: _lib.larosa_rotate(h, qt2[i % copies], l2.q_block, xr2,
                                                           1, f), a.steps, a.warmup)
@@ -293,10 +325,26 @@ def main():
     dense_mlp_bytes = (d * 2 * f + f * d) * 2
     best = min(step_ms, key=step_ms.get)
     ms = step_ms[best]
+    rot1_bytes = l1.Qt.numel() * 2 + d * 2 + d * 4
+    rot2_bytes = l2.Qt.numel() * 2 + f * 2 + f * 4
     kernels = {
-        "select_gather_kernel": dict(achieved=gbs(topk1_bytes, topk1_ms), bytes=topk1_bytes,
-                                     us=topk1_ms * 1e3,
-                                     what="one-token selection folded into the product, gate|up"),
+        "select_gather_kernel": dict(achieved=gbs(topk1s_bytes, topk1s_ms), bytes=topk1s_bytes,
+                                     us=topk1s_ms * 1e3,
+                                     what="one-token selection folded into the product, gate|up, "
+                                          "SiLU(gate)·up epilogue (the step's kernel)"),
+        "select_gather_kernel (no epilogue)": dict(
+            achieved=gbs(topk1_bytes, topk1_ms), bytes=topk1_bytes, us=topk1_ms * 1e3,
+            what="the same selection and product writing gate|up"),
+        "select_gather_kernel (down)": dict(
+            achieved=gbs(topk2_bytes, topk2_ms), bytes=topk2_bytes, us=topk2_ms * 1e3,
+            what="one-token selection folded into the product, down (11008 -> 4096)"),
+        "rotate_row_kernel (Q1)": dict(
+            achieved=gbs(rot1_bytes, stage["rotate1"]), bytes=rot1_bytes,
+            us=stage["rotate1"] * 1e3, what="one-token rotation, dense 4096x4096"),
+        "rotate_row_kernel (Q2)": dict(
+            achieved=gbs(rot2_bytes, stage["rotate2"]), bytes=rot2_bytes,
+            us=stage["rotate2"] * 1e3, what=f"one-token rotation, {f // case.q2_block}x"
+                                            f"{case.q2_block} blocks"),
         "gather_vec_kernel": dict(achieved=gbs(gather_bytes, gather_ms), bytes=gather_bytes,
                                   us=gather_ms * 1e3,
                                   what="product over a given kept-row list, gate|up"),
@@ -363,6 +411,16 @@ def main():
                                  "torch.matmul": round(torch_ms * 1e3, 2)},
             "gate_up_dense_GBs": round(dense_bytes / (dense_ms * 1e-3) / 1e9, 1),
             "gate_up_speedup_vs_dense": round(min(dense_ms, torch_ms) / topk1_ms, 3),
+            "down_select_gather_frac_of_peak": round(gbs(topk2_bytes, topk2_ms) / HBM_PEAK_GBS, 4),
+            "gate_up_speedup_note": "the product alone (selection folded in), without the "
+                                    "rotation; the MLP-level figure is step_speedup_vs_dense",
+            "mlp_dense_step_ms": {k: round(v, 5) for k, v in dense_mlp_ms.items()},
+            "step_speedup_vs_dense": round(min(dense_mlp_ms.values()) / ms, 3),
+            "step_speedup_vs_dense_q2_256": (
+                round(min(dense_mlp_ms.values()) / sweep["256"]["step_ms"], 3)
+                if "256" in sweep else None),
+            "copy_ceiling": copy,
+            "roofline_frac_of_copy_ceiling": round(kd["achieved"] / copy["GBs"], 4),
             "gate_up_gather_only_speedup_vs_dense": round(min(dense_ms, torch_ms) / gather_ms, 3),
             "input_gen_s": round(gen_s, 1),
             "configs": configs,
@@ -479,14 +537,30 @@ def threshold_mlp(a, case, x_d, l1, l2, qt1, wil1, qt2, wf2, copies, h, y, timed
     }
 
 
+def copy_ceiling(dev, timed, steps, warmup, nbytes=1 << 30):
+    """A plain device-to-device copy of nbytes (read once, written once):
+    the practical HBM ceiling on this part, next to the 8 TB/s peak."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    ms = timed(lambda i: dst.copy_(src), max(20, steps // 4), max(3, warmup // 4))
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes_read_plus_written": 2 * nbytes, "us": round(ms * 1e3, 2),
+            "GBs": round(2 * nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(2 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def q2_block_sweep(a, case, wd, l1, x_d, qt1, wil1, copies, h, y, timed, gbs,
-                   blocks=(256, 688, 1376, 2752, 5504, 11008)):
+                   blocks=(256, 688, 1376, 2752, 5504, 11008), steps=100, repeats=3):
     """The one-token MLP step with the down projection's rotation Q2 made of
     f / b independent b×b Haar blocks, for block widths b that divide f =
     11008 (the pages allow any orthogonal rotation, random or learned): the
     Q2 bytes fall as b shrinks. Q2 drawn on the device (QR of a seeded N(0,1)
     matrix, sign-fixed), folded into the same W_down; three copies per point
-    so the on-package cache serves none of a step's reads."""
+    so the on-package cache serves none of a step's reads. Each point is the
+    median of `repeats` timings of at least `steps` steps, whatever the
+    command line's step count."""
     import torch
     from rotated_top_activation_amd import _lib
     from rotated_top_activation_amd.device import RotatedLinear
@@ -517,13 +591,18 @@ def q2_block_sweep(a, case, wd, l1, x_d, qt1, wil1, copies, h, y, timed, gbs,
                                              h, ws=ws1)
             l2 = lins[i % 3]
             _lib.larosa_layer_forward(h, l2.Qt, b, l2.Wf, 1, f, d, case.k2, y, ws=ws2)
-        ms = timed(step, a.steps, a.warmup)
-        rot = timed(lambda i, lins=lins, b=b: _lib.larosa_rotate(h, lins[i % 3].Qt, b, xr2, 1, f),
-                    a.steps, a.warmup)
+        n_steps = max(steps, a.steps)
+        runs = sorted(timed(step, n_steps, max(a.warmup, 10)) for _ in range(repeats))
+        ms = runs[len(runs) // 2]
+        rot = sorted(timed(lambda i, lins=lins, b=b: _lib.larosa_rotate(h, lins[i % 3].Qt, b, xr2,
+                                                                        1, f),
+                           n_steps, max(a.warmup, 10)) for _ in range(repeats))[repeats // 2]
         q_bytes = l1.Qt.numel() * 2 + f * b * 2
         sparse = q_bytes + (case.k1 * 2 * f + case.k2 * d) * 2
         dense = (d * 2 * f + f * d) * 2
-        out[str(b)] = {"step_ms": round(ms, 5), "tokens_per_s": round(1.0 / (ms * 1e-3), 1),
+        out[str(b)] = {"step_ms": round(ms, 5), "step_ms_runs": [round(r, 5) for r in runs],
+                       "steps_per_run": n_steps,
+                       "tokens_per_s": round(1.0 / (ms * 1e-3), 1),
                        "rotate2_us": round(rot * 1e3, 2), "q2_bytes": f * b * 2,
                        "step_bytes": sparse, "step_GBs": round(gbs(sparse, ms), 1),
                        "dense_over_sparse_bytes": round(dense / sparse, 3)}
@@ -667,7 +746,7 @@ def other_configs(a, device):
     kv_base = tuple(torch.randn((shape.n_kv_heads, shape.ctx, shape.d_head), generator=gen,
                                 device=device).to(torch.bfloat16) for _ in range(2))
     n_layers = 32
-    for B, sps in ((1, (25, 40, 50)), (4, (40,)), (16, (40,))):
+    for B, sps in ((1, (25, 40, 50)), (4, (25, 40, 50)), (16, (25, 40, 50))):
         layers = [dec.build_layer(3, l, shape, base, kv_base, B, sps[0])[0]
                   for l in range(n_layers)]
         buf = dec.DecoderBuffers(shape, B)
@@ -682,15 +761,19 @@ def other_configs(a, device):
 
             def step():
                 h.copy_(h0)
-                for L in layers:
-                    dec.layer_forward(L, h, buf, _lib.UNFUSED)
+                _lib.larosa_rmsnorm(h, buf.a, B, d)
+                for li, L in enumerate(layers):
+                    dec.layer_forward(L, h, buf, _lib.UNFUSED, normed=True,
+                                      norm_next=li < n_layers - 1)
             ms = _timed_ms(step, steps, warm)
             # bytes: rotations + union rows (one traced step) + key/value cache
             nbytes = 0
             h.copy_(h0)
-            for L in layers:
+            _lib.larosa_rmsnorm(h, buf.a, B, d)
+            for li, L in enumerate(layers):
                 trace = {}
-                dec.layer_forward(L, h, buf, _lib.UNFUSED, trace=trace)
+                dec.layer_forward(L, h, buf, _lib.UNFUSED, trace=trace, normed=True,
+                                  norm_next=li < n_layers - 1)
                 for role in dec.ROLES:
                     lin = L.lin[role]
                     nbytes += lin.Qt.numel() * 2 + _union_rows(trace[role][1]) * lin.d_out * 2
@@ -766,27 +849,48 @@ def other_configs(a, device):
 
 def cpu_baseline(case, x, q1, wgu, q2, wd, seconds):
     """The oracle's MLP, as it stands, on the host: fold once (untimed), then
-    as many single-token steps as fit in about `seconds`."""
-    import numpy as np
+    as many single-token steps as fit in about `seconds`, once with the BLAS
+    pool at every core this process may use and once at one thread. `value`
+    is the all-cores rate; `cores` the threads that run used."""
     from oracle import larosa_ref as ref
     try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        from threadpoolctl import threadpool_info, threadpool_limits
     except Exception:
-        threads = os.cpu_count() or 1
+        threadpool_info = threadpool_limits = None
+    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None
     w1 = ref.fold(q1, wgu, "bf16")
     w2 = ref.fold(q2, wd, "bf16")
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        ref.mlp(x, q1, w1, q2, w2, case.k1, case.k2, case.f)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or n >= 1000:
-            break
-    return {"value": round(n / el, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} single-token steps of the same MLP (same x and weights), "
-                      f"{el:.1f} s; fold done once beforehand, untimed"}
+
+    def run(limit):
+        ctx = threadpool_limits(limits=limit) if threadpool_limits else None
+        if ctx is not None:
+            ctx.__enter__()
+        try:
+            threads = (max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+                       if threadpool_info else (limit or os.cpu_count() or 1))
+            ref.mlp(x, q1, w1, q2, w2, case.k1, case.k2, case.f)  # warm-up, untimed
+            n = 0
+            t0 = time.perf_counter()
+            while True:
+                ref.mlp(x, q1, w1, q2, w2, case.k1, case.k2, case.f)
+                n += 1
+                el = time.perf_counter() - t0
+                if el >= seconds or n >= 1000:
+                    break
+        finally:
+            if ctx is not None:
+                ctx.__exit__(None, None, None)
+        return n, el, threads
+    n_all, el_all, thr_all = run(affinity)
+    n_one, el_one, _ = run(1)
+    return {"value": round(n_all / el_all, 3), "unit": "tokens/s", "cores": thr_all,
+            "kind": "oracle",
+            "sample": f"{n_all} single-token steps of the same MLP (same x and weights), "
+                      f"{el_all:.1f} s, BLAS pool at {thr_all} threads; fold done once "
+                      f"beforehand, untimed",
+            "single_thread": {"value": round(n_one / el_one, 3), "unit": "tokens/s",
+                              "steps": n_one, "seconds": round(el_one, 1)},
+            "os_cpu_count": os.cpu_count(), "affinity_cores": affinity}
 
 
 if __name__ == "__main__":

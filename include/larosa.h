@@ -192,7 +192,10 @@ int larosa_rotate_fp64(const void *x, int x_dtype, const void *Qt,
  *   union_idx   [d] int32: ascending union of the tokens' kept indices
  *   union_count [1] int32: its length |U| (written on the device)
  *   union_coef  [d, B] fp32: union_coef[j·B + b] = xs[b, union_idx[j]]
- * When the union is asked for, xs is required. ws: workspace. */
+ * When the union is asked for, xs is required, and ws must hold at least
+ * larosa_workspace_bytes(B, d, d_out, k, mode) bytes for some valid d_out and
+ * mode (a status word and the tokens' bit masks come first in every
+ * layout); without the union ws may be NULL. */
 int larosa_topk_select(const float *x_rot, int64_t B, int64_t d, int64_t k,
                        int32_t *idx, float *val, float *xs, int32_t *union_idx,
                        int32_t *union_count, float *union_coef, void *ws,
@@ -229,6 +232,17 @@ int larosa_topk_gemv(const float *x_rot, int64_t d_in, int64_t k,
                      const void *W_folded, int w_dtype, void *y, int y_dtype,
                      int64_t d_out, int32_t *idx_out, void *ws, size_t ws_bytes,
                      larosa_stream_t stream) LAROSA_NOEXCEPT;
+
+/* larosa_topk_gemv with SiLU(gate)·up folded in, for one token: the
+ * selection and the product over the interleaved folded gate|up weight W_il
+ * ([d_in, 2f], see larosa_interleave_gate_up), writing h [f] = SiLU(g)·u of
+ * the sums rounded to h_dtype (the step larosa_swiglu_layer_forward runs
+ * after its rotation). f a multiple of the interleave block. ws: workspace of
+ * larosa_workspace_bytes(1, d_in, 2f, k, …). Other arguments as
+ * larosa_topk_gemv. */
+int larosa_topk_swiglu_gemv(const float *x_rot, int64_t d_in, int64_t k, const void *W_il,
+                            int w_dtype, void *h, int h_dtype, int64_t f, int32_t *idx_out,
+                            void *ws, size_t ws_bytes, larosa_stream_t stream) LAROSA_NOEXCEPT;
 
 /* One rotated sparse linear layer of the method, both online stages of the
  * LaRoSA summary page (方法详解 · 技术框架: stage 1 rotates the layer's input
@@ -459,6 +473,14 @@ int larosa_decode_attention(const void *q, const void *k_new, int64_t k_stride,
                             const void *v_cache, void *out, int64_t B, int64_t T,
                             int64_t n_heads, int64_t n_kv_heads, int64_t d_head, int dtype,
                             void *ws, size_t ws_bytes, larosa_stream_t stream) LAROSA_NOEXCEPT;
+
+/* The residual add followed by the next RMSNorm, one launch: for each token
+ * row b, h[b, :] = h[b, :] + o[b, :] (rounded to dtype, written back), then
+ * out[b, :] = RMSNorm(h[b, :]) as larosa_rmsnorm computes it from the
+ * rounded sum (the same bits as larosa_residual_add then larosa_rmsnorm).
+ * h, o, out: [B, d]; out must not overlap h or o (h and o may be equal). */
+int larosa_residual_rmsnorm(void *h, const void *o, void *out, int64_t B, int64_t d, float eps,
+                            int dtype, larosa_stream_t stream) LAROSA_NOEXCEPT;
 
 /* Residual add in place: h[i] = h[i] + o[i] for i < n. */
 int larosa_residual_add(void *h, const void *o, int64_t n, int dtype, larosa_stream_t stream) LAROSA_NOEXCEPT;

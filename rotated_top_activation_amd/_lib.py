@@ -90,6 +90,10 @@ SIGNATURES = {
                                          _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_int, _c_vp,
                                          _c_sz, _c_vp]),
     "larosa_residual_add": (_c_int, [_c_vp, _c_vp, _c_i64, _c_int, _c_vp]),
+    "larosa_residual_rmsnorm": (_c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, ctypes.c_float,
+                                         _c_int, _c_vp]),
+    "larosa_topk_swiglu_gemv": (_c_int, [_c_vp, _c_i64, _c_i64, _c_vp, _c_int, _c_vp, _c_int,
+                                         _c_i64, _c_vp, _c_vp, _c_sz, _c_vp]),
 }
 
 _lib = None
@@ -360,3 +364,17 @@ def larosa_decode_attention(q, k_new, k_stride: int, v_new, v_stride: int, k_cac
 def larosa_residual_add(h, o, n: int, stream=None) -> None:
     _check("larosa_residual_add", load().larosa_residual_add(_ptr(h), _ptr(o), n, _dt(h),
                                                              _stream(stream)))
+
+
+def larosa_residual_rmsnorm(h, o, out, B: int, d: int, eps: float = 1e-5, stream=None) -> None:
+    _check("larosa_residual_rmsnorm",
+           load().larosa_residual_rmsnorm(_ptr(h), _ptr(o), _ptr(out), B, d, eps, _dt(h),
+                                          _stream(stream)))
+
+
+def larosa_topk_swiglu_gemv(x_rot, d_in: int, k: int, W_il, h, f: int, idx_out=None, ws=None,
+                            stream=None) -> None:
+    _check("larosa_topk_swiglu_gemv",
+           load().larosa_topk_swiglu_gemv(_ptr(x_rot), d_in, k, _ptr(W_il), _dt(W_il), _ptr(h),
+                                          _dt(h), f, _ptr(idx_out), _ptr(ws), _nbytes(ws),
+                                          _stream(stream)))

@@ -1100,6 +1100,54 @@ int larosa_decode_attention(const void *q, const void *k_new, int64_t k_stride,
   });
 }
 
+int larosa_residual_rmsnorm(void *h, const void *o, void *out, int64_t B, int64_t d, float eps,
+                            int dtype, larosa_stream_t stream) LAROSA_NOEXCEPT {
+  return guard([&]() -> int {
+  if (!dtype_ok(dtype)) return LAROSA_ERR_DTYPE;
+  if (B < 0 || B > kMaxB || d < 1 || !(eps >= 0.f)) return LAROSA_ERR_INVALID_ARG;
+  if (B == 0) return LAROSA_OK;
+  if (!h || !o || !out) return LAROSA_ERR_INVALID_ARG;
+  const size_t bytes = static_cast<size_t>(B) * d * dt_size(dtype);
+  const char *hb = static_cast<const char *>(h), *ob = static_cast<const char *>(o),
+             *qb = static_cast<const char *>(out);
+  if ((qb < hb + bytes && hb < qb + bytes) || (qb < ob + bytes && ob < qb + bytes))
+    return LAROSA_ERR_INVALID_ARG;  // out must not overlap h or o
+  if (int st = device_status()) return st;
+  return launched(launch_residual_rmsnorm(h, o, out, B, d, eps, dtype, stream_of(stream)));
+  });
+}
+
+int larosa_topk_swiglu_gemv(const float *x_rot, int64_t d_in, int64_t k, const void *W_il,
+                            int w_dtype, void *h, int h_dtype, int64_t f, int32_t *idx_out,
+                            void *ws, size_t ws_bytes, larosa_stream_t stream) LAROSA_NOEXCEPT {
+  return guard([&]() -> int {
+  if (!dtype_ok(w_dtype) || !dtype_ok(h_dtype)) return LAROSA_ERR_DTYPE;
+  if (w_dtype == LAROSA_F32 && h_dtype == LAROSA_BF16) return LAROSA_ERR_DTYPE;
+  if (int st = check_sizes(1, d_in, k)) return st;
+  if (!select_gather_supported(d_in)) return LAROSA_ERR_SHAPE;
+  if (f < 1 || f % interleave_block(w_dtype)) return LAROSA_ERR_SHAPE;
+  if (!x_rot || !W_il || !h) return LAROSA_ERR_INVALID_ARG;
+  if (!aligned16(x_rot) || !aligned16(W_il) || !aligned16(h)) return LAROSA_ERR_ALIGNMENT;
+  const Prefix P = prefix_for(1, d_in, 2 * f, d_in, w_dtype);
+  if (!ws || ws_bytes < P.end) return LAROSA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return LAROSA_ERR_ALIGNMENT;
+  if (int st = device_status()) return st;
+  SelectGatherArgs g;
+  g.x_rot = x_rot;
+  g.d_in = static_cast<int>(d_in);
+  g.k = static_cast<int>(k);
+  g.w = W_il;
+  g.w_dt = w_dtype;
+  g.d_out = 2 * f;
+  g.y = h;
+  g.y_dt = h_dtype;
+  g.idx_out = idx_out;
+  g.ws = static_cast<char *>(ws) + P.gather;
+  g.swiglu = true;
+  return launched(launch_select_gather(g, stream_of(stream)));
+  });
+}
+
 int larosa_residual_add(void *h, const void *o, int64_t n, int dtype, larosa_stream_t stream) LAROSA_NOEXCEPT {
   return guard([&]() -> int {
   if (!dtype_ok(dtype)) return LAROSA_ERR_DTYPE;

@@ -58,6 +58,64 @@ __global__ __launch_bounds__(kGT) void rmsnorm_kernel(const T *__restrict__ h, T
   for (int i = threadIdx.x; i < d; i += kGT) Elt<T>::store(orow, i, Elt<T>::load(row, i) * inv);
 }
 
+// The same RMSNorm with 16-byte loads, optionally after the residual add:
+// one workgroup per token; thread t owns the 16-byte chunks t, t + 256, ...
+// of the row (at most CPT of them), loads every one of them before using
+// any, and keeps them in registers for the normalisation, so the row is read
+// once. With RESID the row is first h + o rounded to T, written back to h
+// (the residual add), and the norm is taken of that rounded sum, exactly as
+// a separate add followed by the norm would see it. The sum of squares adds
+// a thread's chunks in order, then the block's threads in a fixed tree, so
+// the standalone and the fused form give the same bits.
+template <typename T, int CPT, bool RESID>
+__global__ __launch_bounds__(kGT) void norm_vec_kernel(T *__restrict__ h, const T *__restrict__ o,
+                                                       T *__restrict__ out, int d, float eps) {
+  constexpr int V = Elt<T>::kVec;
+  __shared__ float red[kGW];
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * d;
+  const int chunks = d / V;
+  uint4 hq[CPT], oq[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int j = threadIdx.x + c * kGT;
+    const int jc = j < chunks ? j : chunks - 1;
+    hq[c] = load16(h + base + static_cast<int64_t>(jc) * V);
+    if (RESID) oq[c] = load16(o + base + static_cast<int64_t>(jc) * V);
+  }
+  float v[CPT][V];
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int j = threadIdx.x + c * kGT;
+    Elt<T>::unpack(hq[c], v[c]);
+    if (RESID) {
+      float ov[V];
+      Elt<T>::unpack(oq[c], ov);
+#pragma unroll
+      for (int e = 0; e < V; ++e) v[c][e] = Elt<T>::round(v[c][e] + ov[e]);
+    }
+    if (j < chunks) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) ss = fmaf(v[c][e], v[c][e], ss);
+      if (RESID) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) Elt<T>::store(h, base + static_cast<int64_t>(j) * V + e, v[c][e]);
+      }
+    }
+  }
+  const float tot = block_sum(ss, red);
+  const float inv = 1.0f / sqrtf(tot / static_cast<float>(d) + eps);
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int j = threadIdx.x + c * kGT;
+    if (j < chunks) {
+#pragma unroll
+      for (int e = 0; e < V; ++e)
+        Elt<T>::store(out, base + static_cast<int64_t>(j) * V + e, v[c][e] * inv);
+    }
+  }
+}
+
 // Rotate-half rotary embedding of the q and k heads of one token row:
 // channel i pairs with i + d_head/2, angle pos · theta^(−2i/d_head).
 template <typename T>
@@ -271,8 +329,43 @@ unsigned blocks_for(int64_t n) { return static_cast<unsigned>((n + kGT - 1) / kG
 
 }  // namespace
 
+template <typename T, bool RESID>
+bool launch_norm_vec(void *h, const void *o, void *out, int64_t B, int64_t d, float eps,
+                     hipStream_t s) {
+  constexpr int V = Elt<T>::kVec;
+  const auto ok16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  if (d % V || !ok16(h) || !ok16(out) || (RESID && !ok16(o))) return false;
+  const int64_t per_thread = (d / V + kGT - 1) / kGT;
+  const dim3 grid(static_cast<unsigned>(B)), block(kGT);
+  T *hp = static_cast<T *>(h);
+  const T *op = static_cast<const T *>(o);
+  T *outp = static_cast<T *>(out);
+  const int di = static_cast<int>(d);
+  if (per_thread <= 2) hipLaunchKernelGGL((norm_vec_kernel<T, 2, RESID>), grid, block, 0, s, hp, op, outp, di, eps);
+  else if (per_thread <= 4) hipLaunchKernelGGL((norm_vec_kernel<T, 4, RESID>), grid, block, 0, s, hp, op, outp, di, eps);
+  else if (per_thread <= 8) hipLaunchKernelGGL((norm_vec_kernel<T, 8, RESID>), grid, block, 0, s, hp, op, outp, di, eps);
+  else return false;
+  return true;
+}
+
+hipError_t launch_residual_rmsnorm(void *h, const void *o, void *out, int64_t B, int64_t d,
+                                   float eps, int dt, hipStream_t s) {
+  const bool vec = dt == kF32 ? launch_norm_vec<float, true>(h, o, out, B, d, eps, s)
+                              : launch_norm_vec<uint16_t, true>(h, o, out, B, d, eps, s);
+  if (vec) return hipGetLastError();
+  // ragged rows: the two separate steps
+  hipError_t e = launch_residual_add(h, o, B * d, dt, s);
+  if (e != hipSuccess) return e;
+  return launch_rmsnorm(h, out, B, d, eps, dt, s);
+}
+
 hipError_t launch_rmsnorm(const void *h, void *out, int64_t B, int64_t d, float eps, int dt,
                           hipStream_t s) {
+  // h is only read here (the residual form writes it)
+  const bool vec = dt == kF32
+                       ? launch_norm_vec<float, false>(const_cast<void *>(h), nullptr, out, B, d, eps, s)
+                       : launch_norm_vec<uint16_t, false>(const_cast<void *>(h), nullptr, out, B, d, eps, s);
+  if (vec) return hipGetLastError();
   if (dt == kF32)
     hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(static_cast<unsigned>(B)), dim3(kGT), 0, s,
                        static_cast<const float *>(h), static_cast<float *>(out),

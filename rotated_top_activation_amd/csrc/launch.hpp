@@ -250,5 +250,8 @@ hipError_t launch_decode_attention(const void *q, const void *k_new, int64_t k_s
                                    int64_t n_heads, int64_t n_kv, int dt, void *ws,
                                    hipStream_t s);
 hipError_t launch_residual_add(void *h, const void *o, int64_t n, int dt, hipStream_t s);
+// h += o (rounded to dt, written back), then out = RMSNorm(h), per token row.
+hipError_t launch_residual_rmsnorm(void *h, const void *o, void *out, int64_t B, int64_t d,
+                                   float eps, int dt, hipStream_t s);
 
 }  // namespace larosa

@@ -75,10 +75,17 @@ class DecoderBuffers:
 
 
 def layer_forward(layer: DecoderLayer, h, buf: DecoderBuffers, mode: int = _lib.UNFUSED,
-                  trace: dict | None = None):
+                  trace: dict | None = None, normed: bool = False, norm_next: bool = False):
     """One decode step through `layer`, updating h [B, d] in place. `trace`,
     if given, receives the rotated inputs and kept indices of the four
-    linears (fp32 / int32 device tensors)."""
+    linears (fp32 / int32 device tensors).
+
+    normed: buf.a already holds RMSNorm(h) (the previous layer's norm_next),
+    so the layer's first norm is skipped. norm_next: the closing residual add
+    also writes RMSNorm of the new h into buf.a, the next layer's first norm,
+    in the same launch. A stack of layers runs layer 0 with normed=False and
+    every later one with normed=True, every layer but the last with
+    norm_next=True."""
     s = layer.shape
     B = h.shape[0]
     ws = layer.workspaces(B, mode)
@@ -97,7 +104,8 @@ def layer_forward(layer: DecoderLayer, h, buf: DecoderBuffers, mode: int = _lib.
         else:
             L.forward(x, y, ws[role], idx_out=idx, xrot_out=xr, mode=mode)
 
-    _lib.larosa_rmsnorm(h, buf.a, B, s.d)
+    if not normed:
+        _lib.larosa_rmsnorm(h, buf.a, B, s.d)
     lin("attn_in", buf.a, buf.qkv)
     _lib.larosa_rope(buf.qkv, s.qkv_out, buf.q, buf.k, B, s.n_heads, s.n_kv_heads, s.d_head,
                      s.ctx)
@@ -106,11 +114,13 @@ def layer_forward(layer: DecoderLayer, h, buf: DecoderBuffers, mode: int = _lib.
                                  layer.k_cache, layer.v_cache, buf.att, B, s.ctx, s.n_heads,
                                  s.n_kv_heads, s.d_head, ws=buf.att_ws)
     lin("o_in", buf.att, buf.o)
-    _lib.larosa_residual_add(h, buf.o, B * s.d)
-    _lib.larosa_rmsnorm(h, buf.m, B, s.d)
+    _lib.larosa_residual_rmsnorm(h, buf.o, buf.m, B, s.d)  # h += o; m = RMSNorm(h)
     lin("mlp_in", buf.m, buf.hh)
     lin("down_in", buf.hh, buf.dn)
-    _lib.larosa_residual_add(h, buf.dn, B * s.d)
+    if norm_next:
+        _lib.larosa_residual_rmsnorm(h, buf.dn, buf.a, B, s.d)  # h += dn; the next layer's a
+    else:
+        _lib.larosa_residual_add(h, buf.dn, B * s.d)
 
 
 def upload_base(base: dict, dtype: str = "bf16") -> dict:

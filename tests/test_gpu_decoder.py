@@ -89,6 +89,27 @@ def test_decode_attention(B, H, Hkv, T):
     assert ref.rel_error(host(out), want) <= TOL
 
 
+@pytest.mark.parametrize("B,d", [(1, 4096), (16, 4096), (3, 520), (2, 5120), (1, 8192)])
+def test_residual_rmsnorm_matches_the_two_steps(B, d):
+    """The fused residual add + RMSNorm gives the same bits as the add and
+    the norm run one after the other, and matches the oracle."""
+    rng = np.random.default_rng(B + d)
+    a = wl.quantize(rng.standard_normal((B, d)), "bf16")
+    b = wl.quantize(rng.standard_normal((B, d)) * 0.5, "bf16")
+    h1, h2 = dev(a, "bf16"), dev(a, "bf16")
+    o = dev(b, "bf16")
+    out1 = torch.empty((B, d), dtype=torch.bfloat16, device="cuda")
+    out2 = torch.empty_like(out1)
+    _lib.larosa_residual_rmsnorm(h1, o, out1, B, d)
+    _lib.larosa_residual_add(h2, o, B * d)
+    _lib.larosa_rmsnorm(h2, out2, B, d)
+    torch.cuda.synchronize()
+    assert torch.equal(h1, h2) and torch.equal(out1, out2)
+    h_sum = dec.residual_add(a, b)
+    np.testing.assert_array_equal(host(h1), h_sum)
+    assert close_bf16(host(out1), dec.rmsnorm(h_sum), extra=1e-6)
+
+
 def test_residual_add_matches_rounded_sum():
     rng = np.random.default_rng(9)
     a = wl.quantize(rng.standard_normal((3, 4096)), "bf16")
@@ -147,11 +168,17 @@ def run_decoder(B, sparsity, n_layers, mode, n_checked=None, seed_cols=0, check_
     buf = D.DecoderBuffers(shape, B)
     rng = np.random.default_rng(seed_cols)
     checked = 0
+    # the chained form: layer l's closing residual add also writes the next
+    # layer's first RMSNorm (one launch); the first layer's norm runs here
+    _lib.larosa_rmsnorm(h, buf.a, B, shape.d)
     for l in range(n_layers):
         layer, idxs, offs = D.build_layer(cfg, l, shape, base_dev, kv_dev, B, sparsity)
+        torch.cuda.synchronize()
         h_in = host(h)
+        a = host(buf.a)
         trace = {}
-        D.layer_forward(layer, h, buf, mode=mode, trace=trace)
+        D.layer_forward(layer, h, buf, mode=mode, trace=trace, normed=True,
+                        norm_next=l < n_layers - 1)
         torch.cuda.synchronize()
         skip = (n_checked is not None and checked >= n_checked) or \
             (l % check_every != 0 and l != n_layers - 1)
@@ -159,8 +186,8 @@ def run_decoder(B, sparsity, n_layers, mode, n_checked=None, seed_cols=0, check_
             del layer
             continue
         checked += 1
-        a, qkv, att, o, m, hh, dn = (host(t) for t in (buf.a, buf.qkv, buf.att, buf.o, buf.m,
-                                                        buf.hh, buf.dn))
+        qkv, att, o, m, hh, dn = (host(t) for t in (buf.qkv, buf.att, buf.o, buf.m, buf.hh,
+                                                     buf.dn))
         q, k = host(buf.q), host(buf.k)
         h_out = host(h)
         assert close_bf16(a, dec.rmsnorm(h_in), extra=1e-6), f"layer {l} rmsnorm"
@@ -193,6 +220,8 @@ def run_decoder(B, sparsity, n_layers, mode, n_checked=None, seed_cols=0, check_
         h_mid = dec.residual_add(h_in, o)
         assert close_bf16(m, dec.rmsnorm(h_mid), extra=1e-6), f"layer {l} residual/rmsnorm"
         np.testing.assert_array_equal(h_out, dec.residual_add(h_mid, dn))
+        if l < n_layers - 1:  # the next layer's norm, written by the closing add
+            assert close_bf16(host(buf.a), dec.rmsnorm(h_out), extra=1e-6), f"layer {l} next norm"
         del layer
     assert np.all(np.isfinite(host(h)))
 

@@ -74,7 +74,8 @@ def test_threshold_select_bit_exact(d, B, kind, spec):
         u_idx = torch.full((d,), -1, dtype=torch.int32, device="cuda")
         u_cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
         u_coef = torch.empty((d * B,), dtype=torch.float32, device="cuda")
-        ws = torch.empty(B * ((d + 31) // 32) * 4, dtype=torch.uint8, device="cuda")
+        ws = torch.empty(_lib.larosa_workspace_bytes(B, d, 8, d), dtype=torch.uint8,
+                         device="cuda")
         _lib.larosa_threshold_select(xr_d, B, d, t, idx, count, val, xs, u_idx, u_cnt, u_coef,
                                      ws)
         torch.cuda.synchronize()
