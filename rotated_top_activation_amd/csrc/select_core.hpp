@@ -434,133 +434,6 @@ __device__ __forceinline__ void rule_finish(const uint32_t (&key)[EMAX], int E, 
   __syncthreads();
 }
 
-// ---- The first digit over a window around a guessed threshold ----------
-// A rotation by a random orthogonal Q spreads a token's energy evenly over
-// the channels (the point of the rotation on the LaRoSA summary page), so
-// the rotated entries look like N(0, σ²) with σ² = Σ x_rot² / d, and the K-th
-// largest magnitude lies close to σ·z, z the quantile with P(|N(0,1)| > z)
-// = K / d (the caller passes z). The first digit is then counted only over
-// the keys of a window of 2^22 key values (a quarter binade on either side)
-// around that guess, in 2048 bins of 2048 key values each: the bins are fine,
-// so the lanes of a wave rarely hit the same LDS word, and most keys need
-// only a compare. The guess only decides where to look: the counts decide
-// the rule, and when the window does not hold the K-th largest key (a
-// distribution far from the guess) the caller falls back to the full first
-// digit. So the result is the exact rule either way.
-struct WindowRule {
-  uint32_t blo, bhi;  // keys in [blo, bhi) share the boundary bin; keys >= bhi are kept
-  uint32_t krem;      // how many of the boundary bin's keys are kept
-  uint32_t n_cand;    // keys in the boundary bin
-};
-
-constexpr uint32_t kWinBinBits = 11;                   // key values per bin: 2^11
-constexpr uint32_t kWinSpan = 2048u << kWinBinBits;    // 2^22 key values
-
-// Returns false (uniformly across the block) when the window misses the
-// K-th largest key; `red` holds NT / 64 floats of scratch.
-template <int NT, int EMAX>
-__device__ __forceinline__ bool rule_window_first(const uint32_t (&key)[EMAX], int E, int d,
-                                                  uint32_t k, float z, SelectSmem<NT> &sm,
-                                                  float *red, WindowRule &wr) {
-  const int lane = threadIdx.x % kWave;
-  const int w = threadIdx.x / kWave;
-  // Σ x² in a fixed order: the thread's slots, the wave's lanes, the waves
-  float ss = 0.f;
-#pragma unroll
-  for (int e = 0; e < EMAX; ++e) {
-    if (e < E && !(key[e] & kNoKey)) {
-      const float v = __uint_as_float(key[e]);
-      ss = fmaf(v, v, ss);
-    }
-  }
-  ss = wave_sum(ss);
-  if (lane == 0) red[w] = ss;
-  radix_clear<NT>(sm);
-  if (threadIdx.x == 0) sm.above = 0u;
-  __syncthreads();
-  float tot = 0.f;
-#pragma unroll
-  for (int i = 0; i < NT / kWave; ++i) tot += red[i];
-  const float guess = sqrtf(tot / static_cast<float>(d)) * z;
-  // (NaN or inf fails this test and takes the fallback)
-  if (!(guess > 0.f && guess < 1e30f)) return false;
-  const uint32_t g = __float_as_uint(guess);
-  const uint32_t lo = (g > kWinSpan / 2 ? g - kWinSpan / 2 : 0u) & ~((1u << kWinBinBits) - 1u);
-  const uint32_t hi = lo + kWinSpan;
-  uint32_t above = 0;
-#pragma unroll
-  for (int e = 0; e < EMAX; ++e) {
-    if (e < E && !(key[e] & kNoKey)) {
-      const uint32_t kk = key[e];
-      if (kk >= hi) {
-        ++above;
-      } else if (kk >= lo) {
-        atomicAdd(&sm.hist[pad_bin(static_cast<int>((kk - lo) >> kWinBinBits))], 1u);
-      }
-    }
-  }
-  // keys above the window: one LDS atomic per wave
-  uint32_t wa = above;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) wa += __shfl_xor(wa, off, kWave);
-  __syncthreads();  // the window bins are complete (sm.above was cleared before)
-  if (lane == 0) atomicAdd(&sm.above, wa);
-  __syncthreads();
-  const uint32_t n_above = sm.above;
-  __syncthreads();  // sm.above is rewritten by the search below
-  if (n_above >= k) return false;  // the K-th key lies above the window
-  const uint32_t krem = k - n_above;
-  suffix_search<NT>(krem, sm);  // bin holding the krem-th largest window key
-  const uint32_t bin = sm.bin, in_bin = sm.count, above_bin = sm.above;
-  radix_clear<NT>(sm);  // ready for the finish
-  __syncthreads();
-  if (in_bin == 0) return false;  // fewer than krem keys in the window: the K-th lies below
-  wr.blo = lo + (bin << kWinBinBits);
-  wr.bhi = wr.blo + (1u << kWinBinBits);
-  wr.krem = krem - above_bin;
-  wr.n_cand = in_bin;
-  return true;
-}
-
-// T and the tie cut-off from the boundary bin of rule_window_first: the
-// bin's keys share all but their low 11 bits, so one more 2048-bin count of
-// those bits over the bin's keys gives T exactly.
-template <int NT, int EMAX>
-__device__ __forceinline__ void rule_window_finish(const uint32_t (&key)[EMAX], int E, int i0,
-                                                   const WindowRule &wr, SelectSmem<NT> &sm,
-                                                   uint32_t &T, uint32_t &cut) {
-  if (wr.n_cand == 1) {
-    // one key in the bin: it is T, unique, and the last one kept
-#pragma unroll
-    for (int e = 0; e < EMAX; ++e) {
-      if (e < E && key[e] >= wr.blo && key[e] < wr.bhi) {
-        sm.bin = key[e];
-        sm.above = static_cast<uint32_t>(i0 + e);
-      }
-    }
-    __syncthreads();
-    T = sm.bin;
-    cut = sm.above;
-    __syncthreads();
-    return;
-  }
-#pragma unroll
-  for (int e = 0; e < EMAX; ++e)
-    if (e < E && key[e] >= wr.blo && key[e] < wr.bhi)
-      atomicAdd(&sm.hist[pad_bin(static_cast<int>(key[e] - wr.blo))], 1u);
-  __syncthreads();
-  suffix_search<NT>(wr.krem, sm);
-  T = wr.blo + sm.bin;
-  const uint32_t krem = wr.krem - sm.above;
-  const uint32_t n_eq = sm.count;
-  __syncthreads();
-  if (n_eq == krem) {
-    cut = 0xFFFFFFFFu;  // every channel equal to T is kept
-    return;
-  }
-  cut = tie_cutoff<NT, EMAX>(key, i0, T, krem, sm);
-}
-
 template <int NT, int EMAX>
 __device__ __forceinline__ void topk_rule(const uint32_t (&key)[EMAX], int E, int i0, uint32_t k,
                                           SelectSmem<NT> &sm, CandSmem &cs, uint32_t &T,

@@ -29,8 +29,6 @@
 #include "launch.hpp"
 #include "select_core.hpp"
 
-#include <cmath>
-
 namespace larosa {
 namespace {
 
@@ -43,33 +41,10 @@ constexpr int kSgMaxSplitLoads = 32;  // partial sums fetched per round trip
 
 size_t sg_counter_bytes(int tiles) { return (static_cast<size_t>(tiles) * 4 + 255) / 256 * 256; }
 
-// z with P(|N(0,1)| > z) = k / d: where the K-th largest magnitude of an
-// evenly spread (Gaussian-like) rotated vector lies, in units of its rms.
-// Bisection on erfc(z / sqrt 2) = k / d. Only a guess for the rule's window
-// (the counts decide); 0 turns the window off (k == d).
-float window_quantile(int k, int d) {
-  if (k <= 0 || d <= 0 || k >= d) return 0.f;
-  // the last answer per host thread (a layer calls with the same k and d)
-  thread_local int last_k = -1, last_d = -1;
-  thread_local float last_z = 0.f;
-  if (k == last_k && d == last_d) return last_z;
-  const double p = static_cast<double>(k) / d;
-  double lo = 0.0, hi = 40.0;
-  for (int it = 0; it < 40; ++it) {
-    const double mid = 0.5 * (lo + hi);
-    if (std::erfc(mid / std::sqrt(2.0)) > p) lo = mid;
-    else hi = mid;
-  }
-  last_k = k;
-  last_d = d;
-  last_z = static_cast<float>(0.5 * (lo + hi));
-  return last_z;
-}
-
 template <typename WT, typename OT, int EMAX, bool SWIGLU, bool THR>
 __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
-    const float *__restrict__ x_rot, int d, int k, uint32_t thr_key, float win_z, int E,
-    int tiles, int splits, int cps, const WT *__restrict__ w, int64_t d_out, OT *__restrict__ y,
+    const float *__restrict__ x_rot, int d, int k, uint32_t thr_key, int E, int tiles,
+    int splits, int cps, const WT *__restrict__ w, int64_t d_out, OT *__restrict__ y,
     float *__restrict__ partials, uint32_t *__restrict__ counters,
     int32_t *__restrict__ idx_out, int32_t *__restrict__ count_out) {
   constexpr int V = Elt<WT>::kVec;
@@ -94,7 +69,6 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
   float(*red)[TILE] = reinterpret_cast<float(*)[TILE]>(kv);
   __shared__ uint32_t s_carry;
   __shared__ int s_last;
-  __shared__ float s_red[kSgWaves];
   __shared__ float ep[SWIGLU ? TILE : 1];  // the tile's sums, for the SwiGLU epilogue
 
   const int t = threadIdx.x;
@@ -141,29 +115,16 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
   auto key_of = [&](int i) { return kv[i] & 0x7FFFFFFFu; };
 
   // 1. First digit of the rule over all d channels (the same in every
-  //    workgroup): the boundary bin [blo, bhi) of keys, which holds the K-th
-  //    largest. A channel whose key is at or above bhi is kept whatever the
-  //    rest of the rule says. The digit is counted over a window around a
-  //    guess from the vector's norm when win_z > 0 and the window holds the
-  //    K-th key (rule_window_first), else over every key (bits 30..20).
-  //    (The threshold form has no rule: every kept channel is certain.)
+  //    workgroup): the boundary bin [blo, bhi) of keys (key bits 30..20),
+  //    which holds the K-th largest. A channel whose key is at or above bhi
+  //    is kept whatever the rest of the rule says. (The threshold form has
+  //    no rule: every kept channel is certain.)
   RuleState st{};
-  WindowRule wr{};
-  bool windowed = false;
   uint32_t blo = 0, bhi = 0;
   if constexpr (!THR) {
-    if (win_z > 0.f)
-      windowed = rule_window_first<kSgThreads, EMAX>(key, E, d, static_cast<uint32_t>(k), win_z,
-                                                     sm, s_red, wr);
-    if (windowed) {
-      blo = wr.blo;
-      bhi = wr.bhi;
-    } else {
-      st = rule_first_digit<kSgThreads, EMAX, COPIES>(key, E, static_cast<uint32_t>(k), sm,
-                                                      lists);
-      blo = (st.prefix >> radix_shift(0)) << radix_shift(0);
-      bhi = blo + (1u << radix_shift(0));
-    }
+    st = rule_first_digit<kSgThreads, EMAX, COPIES>(key, E, static_cast<uint32_t>(k), sm, lists);
+    blo = (st.prefix >> radix_shift(0)) << radix_shift(0);
+    bhi = blo + (1u << radix_shift(0));
   } else {
     __syncthreads();  // the LDS copy of the vector is complete
   }
@@ -236,8 +197,7 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
   float cb[R];
   bool has_b = false;  // the group requested after the rule
   if constexpr (!THR) {
-    if (windowed) rule_window_finish<kSgThreads, EMAX>(key, E, i0, wr, sm, T, cut);
-    else rule_finish<kSgThreads, EMAX>(key, E, i0, st, sm, cs, T, cut);
+    rule_finish<kSgThreads, EMAX>(key, E, i0, st, sm, cs, T, cut);
     if (has_a) {
       consume(qa, ca);
       has_b = wave + kSgWaves < n_cg;
@@ -376,8 +336,7 @@ void launch_sg_k(const SelectGatherArgs &a, const SelectGatherPlan &p, int E, hi
       reinterpret_cast<float *>(static_cast<char *>(a.ws) + sg_counter_bytes(p.tiles));
   const dim3 grid(static_cast<unsigned>(p.tiles * p.splits)), block(kSgThreads);
   hipLaunchKernelGGL((select_gather_kernel<WT, OT, EM, SW, TH>), grid, block, 0, s, a.x_rot,
-                     a.d_in, a.k, a.thr_key, window_quantile(a.k, a.d_in), E, p.tiles, p.splits,
-                     p.cps,
+                     a.d_in, a.k, a.thr_key, E, p.tiles, p.splits, p.cps,
                      static_cast<const WT *>(a.w), a.d_out, static_cast<OT *>(a.y), partials,
                      counters, a.idx_out, a.count_out);
 }
