@@ -145,15 +145,16 @@ def main():
     y = torch.empty((1, d), dtype=torch.bfloat16, device=dev)
     ws1 = l1.workspace(1, _lib.FUSED)
     ws2 = l2.workspace(1, _lib.FUSED)
-    ws1s = torch.zeros(_lib.larosa_swiglu_workspace_bytes(1, d, f, case.k1, _lib.FUSED),
-                       dtype=torch.uint8, device=dev)
+    ws_mlp = torch.zeros(_lib.larosa_mlp_workspace_bytes(1, d, f, case.k1, case.k2, _lib.FUSED),
+                         dtype=torch.uint8, device=dev)
 
     def step(i, mode):
+        # one call for the whole MLP: in unfused mode 4 launches (rotate x;
+        # the gate|up product with the selection and SiLU(gate)·up folded in;
+        # rotate h; the down product), in fused mode 2 one-launch layers
         c = i % copies
-        _lib.larosa_swiglu_layer_forward(x_d, qt1[c], l1.q_block, wil1[c], 1, d, f, case.k1, h,
-                                         mode=mode, ws=ws1s)
-        _lib.larosa_layer_forward(h, qt2[c], l2.q_block, wf2[c], 1, f, d, case.k2, y,
-                                  mode=mode, ws=ws2)
+        _lib.larosa_mlp_forward(x_d, qt1[c], l1.q_block, wil1[c], qt2[c], l2.q_block, wf2[c], 1,
+                                d, f, case.k1, case.k2, h, y, mode=mode, ws=ws_mlp)
 
     def timed(fn, steps, warmup):
         for i in range(warmup):
@@ -201,6 +202,9 @@ def main():
             gs = capture(modes[name])
             graph_ms[name] = timed(lambda i, g=gs: g[i % copies].replay(), a.steps, a.warmup)
             step_ms[name] = min(eager_ms[name], graph_ms[name])
+    # the chained form (the rotation of h inside the gate|up launch), eager
+    chain_ms = timed(lambda i: step(i, _lib.CHAIN), a.steps, a.warmup) \
+        if a.kernel_only == "" else None
 
     # The dominant kernels alone, gate|up (the larger linear): the one-token
     # selection folded into the product (unfused mode), the fused
@@ -218,8 +222,13 @@ def main():
     def topk1(i):
         _lib.larosa_topk_gemv(xr1, d, case.k1, wf1[i % copies], gu, 2 * f, ws=ws1)
 
-    def topk1s(i):  # the step's own gate|up kernel: SiLU(gate)·up folded in
+    def topk1s(i):  # the gate|up kernel with SiLU(gate)·up folded in
         _lib.larosa_topk_swiglu_gemv(xr1, d, case.k1, wil1[i % copies], h, f, ws=ws1)
+
+    def chain1(i):  # the chained form's gate|up kernel: SwiGLU product, then Q2's rotation
+        c = i % copies
+        _lib.larosa_topk_swiglu_rotate(xr1, d, case.k1, wil1[c], h, f, qt2[c], l2.q_block, xr2,
+                                       ws=ws1)
 
     def topk2(i):
         _lib.larosa_topk_gemv(xr2, f, case.k2, wf2[i % copies], y, d, ws=ws2)
@@ -232,9 +241,9 @@ def main():
         c = i % copies
         _lib.larosa_layer_forward(x_d, qt1[c], l1.q_block, wf1[c], 1, d, 2 * f, case.k1, gu,
                                   mode=_lib.FUSED, ws=ws1)
-    if a.kernel_only in ("gather", "topk1", "topk1s", "topk2", "fused1"):
-        fn = {"gather": gather, "topk1": topk1, "topk1s": topk1s, "topk2": topk2,
-              "fused1": fused1}[a.kernel_only]
+    if a.kernel_only in ("gather", "topk1", "topk1s", "chain1", "topk2", "fused1"):
+        fn = {"gather": gather, "topk1": topk1, "topk1s": topk1s, "chain1": chain1,
+              "topk2": topk2, "fused1": fused1}[a.kernel_only]
         for i in range(a.steps):
             fn(i)
         torch.cuda.synchronize()
@@ -245,6 +254,9 @@ def main():
     topk1s_bytes = case.k1 * 2 * f * 2 + d * 4 + f * 2
     topk2_ms = timed(topk2, a.steps, a.warmup)
     topk2_bytes = case.k2 * d * 2 + f * 4 + d * 2
+    chain1_ms = timed(chain1, a.steps, a.warmup)
+    # kept gate|up rows, x_rot, h written and read back, Q2, x_rot2
+    chain1_bytes = case.k1 * 2 * f * 2 + d * 4 + 2 * f * 2 + l2.Qt.numel() * 2 + f * 4
     gather_ms = timed(gather, a.steps, a.warmup)
     gather_bytes = case.k1 * 2 * f * 2 + case.k1 * 8 + 2 * f * 2
     fused1_ms = timed(fused1, a.steps, a.warmup)
@@ -328,10 +340,13 @@ def main():
     rot1_bytes = l1.Qt.numel() * 2 + d * 2 + d * 4
     rot2_bytes = l2.Qt.numel() * 2 + f * 2 + f * 4
     kernels = {
-        "select_gather_kernel": dict(achieved=gbs(topk1s_bytes, topk1s_ms), bytes=topk1s_bytes,
-                                     us=topk1s_ms * 1e3,
-                                     what="one-token selection folded into the product, gate|up, "
-                                          "SiLU(gate)·up epilogue (the step's kernel)"),
+        "select_gather_kernel": dict(
+            achieved=gbs(topk1s_bytes, topk1s_ms), bytes=topk1s_bytes, us=topk1s_ms * 1e3,
+            what="one-token selection folded into the gate|up product with SiLU(gate)·up "
+                 "(the step's largest kernel)"),
+        "select_gather_kernel (chained)": dict(
+            achieved=gbs(chain1_bytes, chain1_ms), bytes=chain1_bytes, us=chain1_ms * 1e3,
+            what="the same product chained into the rotation of h by Q2 (LAROSA_CHAIN)"),
         "select_gather_kernel (no epilogue)": dict(
             achieved=gbs(topk1_bytes, topk1_ms), bytes=topk1_bytes, us=topk1_ms * 1e3,
             what="the same selection and product writing gate|up"),
@@ -394,6 +409,10 @@ def main():
         "cpu_baseline": cpu,
         "detail": {
             "step_ms": {k: round(v, 5) for k, v in step_ms.items()},
+            "step": "larosa_mlp_forward (unfused: 4 launches, rotate x, gate|up product with "
+                    "the selection and SiLU(gate)·up folded in, rotate h, down product; fused: "
+                    "the two one-launch layer calls)",
+            "chain_step_ms_eager": round(chain_ms, 5) if chain_ms else None,
             "eager_step_ms": {k: round(v, 5) for k, v in eager_ms.items()},
             "graph_step_ms": {k: round(v, 5) for k, v in graph_ms.items()},
             "mlp_sparse_bytes": sparse_bytes,
@@ -567,8 +586,9 @@ def q2_block_sweep(a, case, wd, l1, x_d, qt1, wil1, copies, h, y, timed, gbs,
     dev = x_d.device
     d, f = case.d, case.f
     gen = torch.Generator(device=dev)
-    ws1 = torch.zeros(_lib.larosa_swiglu_workspace_bytes(1, d, f, case.k1, _lib.UNFUSED),
-                      dtype=torch.uint8, device=dev)
+    ws_mlp = torch.zeros(_lib.larosa_mlp_workspace_bytes(1, d, f, case.k1, case.k2,
+                                                         _lib.UNFUSED),
+                         dtype=torch.uint8, device=dev)
     w_down = None
     out = {}
     for b in blocks:
@@ -581,16 +601,13 @@ def q2_block_sweep(a, case, wd, l1, x_d, qt1, wil1, copies, h, y, timed, gbs,
             if w_down is None:
                 w_down = wl_to_dev(wd)
             lins.append(RotatedLinear(q, w_down, "bf16", case.k2, keep_w=False))
-        ws2 = torch.zeros(_lib.larosa_workspace_bytes(1, f, d, case.k2, _lib.UNFUSED),
-                          dtype=torch.uint8, device=dev)
         xr2 = torch.empty((1, f), dtype=torch.float32, device=dev)
 
-        def step(i, lins=lins, ws2=ws2, b=b):
+        def step(i, lins=lins, b=b):
             c = i % copies
-            _lib.larosa_swiglu_layer_forward(x_d, qt1[c], l1.q_block, wil1[c], 1, d, f, case.k1,
-                                             h, ws=ws1)
             l2 = lins[i % 3]
-            _lib.larosa_layer_forward(h, l2.Qt, b, l2.Wf, 1, f, d, case.k2, y, ws=ws2)
+            _lib.larosa_mlp_forward(x_d, qt1[c], l1.q_block, wil1[c], l2.Qt, b, l2.Wf, 1, d, f,
+                                    case.k1, case.k2, h, y, ws=ws_mlp)
         n_steps = max(steps, a.steps)
         runs = sorted(timed(step, n_steps, max(a.warmup, 10)) for _ in range(repeats))
         ms = runs[len(runs) // 2]

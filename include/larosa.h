@@ -101,6 +101,13 @@ enum { LAROSA_ROTATE_FP64 = 2 };
  * capture (it waits on the stream). */
 enum { LAROSA_VALIDATE = 4 };
 
+/* Mode flag of larosa_mlp_forward and larosa_mlp_workspace_bytes only (any
+ * other call takes it as an invalid mode): run the rotation of h inside the
+ * gate|up product's launch where that form applies (see larosa_mlp_forward).
+ * On MI355X this chained form measures slower than the two launches it
+ * replaces, so it is not the default. */
+enum { LAROSA_CHAIN = 8 };
+
 /* LAROSA_ABI_VERSION of the loaded library. */
 int larosa_abi_version(void) LAROSA_NOEXCEPT;
 
@@ -244,6 +251,21 @@ int larosa_topk_swiglu_gemv(const float *x_rot, int64_t d_in, int64_t k, const v
                             int w_dtype, void *h, int h_dtype, int64_t f, int32_t *idx_out,
                             void *ws, size_t ws_bytes, larosa_stream_t stream) LAROSA_NOEXCEPT;
 
+/* larosa_topk_swiglu_gemv chained into the next linear's rotation, one
+ * launch for one token: h = SiLU(gate)·up as larosa_topk_swiglu_gemv writes
+ * it, and x_rot2 [f] fp32 = h·Q2 as larosa_rotate computes it for one token
+ * (the same bits for Q2 blocks of 2056 to 4096 channels). Qt2: the down
+ * linear's prepared rotation [f, q_block2] in bf16, q_block2 a multiple of 8
+ * and at most 4096; bf16 weights and h. The launch's workgroups wait
+ * (bounded) for the blocks of h the others write; a wait that gives up
+ * records LAROSA_ERR_TIMEOUT for larosa_workspace_status. The step
+ * larosa_mlp_forward runs after its first rotation. ws: workspace of
+ * larosa_workspace_bytes(1, d_in, 2f, k, …). */
+int larosa_topk_swiglu_rotate(const float *x_rot, int64_t d_in, int64_t k, const void *W_il,
+                              int w_dtype, void *h, int64_t f, const void *Qt2, int64_t q_block2,
+                              float *x_rot2, int32_t *idx_out, void *ws, size_t ws_bytes,
+                              larosa_stream_t stream) LAROSA_NOEXCEPT;
+
 /* One rotated sparse linear layer of the method, both online stages of the
  * LaRoSA summary page (方法详解 · 技术框架: stage 1 rotates the layer's input
  * activation with its orthogonal matrix; stage 2 keeps the K entries of
@@ -339,6 +361,38 @@ int larosa_swiglu_layer_forward(const void *x, int act_dtype, const void *Qt, in
                                 int64_t f, int64_t k, void *h, int32_t *idx_out,
                                 float *xrot_out, int mode, void *ws, size_t ws_bytes,
                                 larosa_stream_t stream) LAROSA_NOEXCEPT;
+
+/* ---- A whole SwiGLU MLP: both rotated sparse linears --------------------
+ * Every linear input of the MLP is rotated and Top-K sparsified (LaRoSA
+ * summary page, 方法详解 · 技术框架): the gate|up linear reads x, h =
+ * SiLU(gate)·up, and the down linear reads h. */
+
+/* Workspace bytes of larosa_mlp_forward (0 for invalid sizes or mode). */
+size_t larosa_mlp_workspace_bytes(int64_t B, int64_t d, int64_t f, int64_t k1, int64_t k2,
+                                  int mode) LAROSA_NOEXCEPT;
+
+/* h = larosa_swiglu_layer_forward(x; Qt1, W_il, k1) and then
+ * y = larosa_layer_forward(h; Qt2, W_down, k2), with the same results as the
+ * two calls (bit for bit for Q2 blocks of 2056 to 4096 channels; within the
+ * rotation's fp32 error bound otherwise). x: [B, d], h: [B, f], y: [B, d]
+ * in act_dtype; W_il: the interleaved folded gate|up weight [d, 2f]; W_down:
+ * folded [f, d]; Qt1 [d, q_block1] and Qt2 [f, q_block2] prepared rotations;
+ * optional copies of the selections and rotated inputs as for the layer
+ * calls (NULL skips). mode: a layer-call mode, optionally OR-ed with
+ * LAROSA_CHAIN. With LAROSA_CHAIN, for one token in bf16 with the unfused
+ * steps and the fp32 rotation, and Q2 blocks of at most 4096 channels (a
+ * multiple of 8), the rotation of h runs inside the gate|up product's
+ * launch, overlapping its tail: that launch's workgroups wait (bounded) for
+ * the blocks of h written by the others, and a wait that gives up records
+ * LAROSA_ERR_TIMEOUT for larosa_workspace_status. Everything else runs the
+ * two layer calls. ws: larosa_mlp_workspace_bytes bytes (same mode),
+ * zero-filled once; h must not overlap x. */
+int larosa_mlp_forward(const void *x, int act_dtype, const void *Qt1, int64_t q_block1,
+                       const void *W_il, const void *Qt2, int64_t q_block2, const void *W_down,
+                       int w_dtype, int64_t B, int64_t d, int64_t f, int64_t k1, int64_t k2,
+                       void *h, void *y, int32_t *idx1_out, float *xrot1_out, int32_t *idx2_out,
+                       float *xrot2_out, int mode, void *ws, size_t ws_bytes,
+                       larosa_stream_t stream) LAROSA_NOEXCEPT;
 
 /* ---- Magnitude-threshold selection (the contrast to the fixed Top-K) ----
  * The R-Sparse summary page (研究流程与方法 · R-Sparse框架设计) masks every

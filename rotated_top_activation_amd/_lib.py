@@ -21,6 +21,7 @@ F32, BF16 = 0, 1
 UNFUSED, FUSED = 0, 1
 ROTATE_FP64 = 2  # mode flag: fp64-accumulating rotation, OR-ed into UNFUSED or FUSED
 VALIDATE = 4     # mode flag: check the rotated input for NaN/inf (waits on the stream)
+CHAIN = 8        # mode flag of larosa_mlp_forward: the rotation of h chained into the gate|up launch
 ABI_VERSION = 7
 
 # status codes (include/larosa.h)
@@ -65,6 +66,13 @@ SIGNATURES = {
     "larosa_swiglu_layer_forward": (_c_int, [_c_vp, _c_int, _c_vp, _c_i64, _c_vp, _c_int, _c_i64,
                                              _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_int,
                                              _c_vp, _c_sz, _c_vp]),
+    "larosa_topk_swiglu_rotate": (_c_int, [_c_vp, _c_i64, _c_i64, _c_vp, _c_int, _c_vp, _c_i64,
+                                           _c_vp, _c_i64, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
+    "larosa_mlp_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_int]),
+    "larosa_mlp_forward": (_c_int, [_c_vp, _c_int, _c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp,
+                                    _c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp,
+                                    _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_int, _c_vp, _c_sz,
+                                    _c_vp]),
     "larosa_calibrate_workspace_bytes": (_c_sz, []),
     "larosa_calibrate_threshold": (_c_int, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_sz, _c_vp]),
     "larosa_threshold_select": (_c_int, [_c_vp, _c_i64, _c_i64, ctypes.c_float, _c_vp, _c_vp,
@@ -378,3 +386,28 @@ def larosa_topk_swiglu_gemv(x_rot, d_in: int, k: int, W_il, h, f: int, idx_out=N
            load().larosa_topk_swiglu_gemv(_ptr(x_rot), d_in, k, _ptr(W_il), _dt(W_il), _ptr(h),
                                           _dt(h), f, _ptr(idx_out), _ptr(ws), _nbytes(ws),
                                           _stream(stream)))
+
+
+def larosa_mlp_workspace_bytes(B: int, d: int, f: int, k1: int, k2: int,
+                               mode: int = UNFUSED) -> int:
+    return int(load().larosa_mlp_workspace_bytes(B, d, f, k1, k2, mode))
+
+
+def larosa_mlp_forward(x, Qt1, q_block1: int, W_il, Qt2, q_block2: int, W_down, B: int, d: int,
+                       f: int, k1: int, k2: int, h, y, idx1_out=None, xrot1_out=None,
+                       idx2_out=None, xrot2_out=None, mode: int = UNFUSED, ws=None,
+                       stream=None) -> None:
+    _check("larosa_mlp_forward",
+           load().larosa_mlp_forward(_ptr(x), _dt(x), _ptr(Qt1), q_block1, _ptr(W_il), _ptr(Qt2),
+                                     q_block2, _ptr(W_down), _dt(W_il), B, d, f, k1, k2, _ptr(h),
+                                     _ptr(y), _ptr(idx1_out), _ptr(xrot1_out), _ptr(idx2_out),
+                                     _ptr(xrot2_out), mode, _ptr(ws), _nbytes(ws),
+                                     _stream(stream)))
+
+
+def larosa_topk_swiglu_rotate(x_rot, d_in: int, k: int, W_il, h, f: int, Qt2, q_block2: int,
+                              x_rot2, idx_out=None, ws=None, stream=None) -> None:
+    _check("larosa_topk_swiglu_rotate",
+           load().larosa_topk_swiglu_rotate(_ptr(x_rot), d_in, k, _ptr(W_il), _dt(W_il), _ptr(h),
+                                            f, _ptr(Qt2), q_block2, _ptr(x_rot2), _ptr(idx_out),
+                                            _ptr(ws), _nbytes(ws), _stream(stream)))

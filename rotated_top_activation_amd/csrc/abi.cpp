@@ -66,7 +66,7 @@ hipStream_t stream_of(larosa_stream_t s) { return static_cast<hipStream_t>(s); }
 // larosa_layer_forward then adds its own areas, and the fused kernel's region
 // (whose synchronisation words must also stay zero) comes last.
 struct Prefix {
-  size_t status = 0, mask = 0, gather = 0, mfma_coef = 0, mfma_parts = 0, end = 0;
+  size_t status = 0, mask = 0, gather = 0, flags = 0, mfma_coef = 0, mfma_parts = 0, end = 0;
 };
 
 // The first 256 bytes of every layer-call workspace: word 0 holds the
@@ -95,6 +95,9 @@ Prefix prefix_for(int64_t B, int64_t d_in, int64_t d_out, int64_t rows_bound, in
     g = sg > g ? sg : g;
   }
   P.gather = take(g);
+  // one token: the chained product's tile flags and control block (zero
+  // before first use; the chain keeps its epoch and queues there)
+  if (B == 1) P.flags = take(chain_flag_bytes(d_out / 2));
   if (mfma_region(B, w_dt)) {
     P.mfma_coef = take(static_cast<size_t>(B) * mfma_coef_ld(rows_bound) * 4);
     size_t parts = rotate_mfma_ws_bound(B, d_in);
@@ -459,6 +462,30 @@ int swiglu_entry(const void *x, int act_dtype, const void *Qt, int64_t q_block,
   if (st != LAROSA_OK) return st;
   return launched(launch_swiglu_il(gu, h, B, f, interleave_block(w_dtype), act_dtype,
                                    stream_of(stream)));
+}
+
+// The MLP workspace: the gate|up call's (SwiGLU) workspace, then the down
+// call's.
+struct MlpLayout {
+  size_t up = 0, down = 0, total = 0;
+  size_t up_bytes = 0, down_bytes = 0;
+};
+
+MlpLayout mlp_layout(int64_t B, int64_t d, int64_t f, int64_t k1, int64_t k2, int mode) {
+  MlpLayout M;
+  mode &= ~LAROSA_CHAIN;  // the chained form uses the unfused layout
+  M.up_bytes = larosa_swiglu_workspace_bytes(B, d, f, k1, mode);
+  M.down_bytes = larosa_workspace_bytes(B, f, d, k2, mode);
+  if (M.up_bytes == 0 || M.down_bytes == 0) return M;
+  // The down region starts at the same offset in every mode (after the
+  // larger, one-launch form of the up region), so calls in different modes
+  // can share one workspace: each region's areas keep their places.
+  const size_t up_fused = larosa_swiglu_workspace_bytes(B, d, f, k1, mode | LAROSA_FUSED);
+  if (up_fused > M.up_bytes) M.up_bytes = up_fused;
+  M.up = 0;
+  M.down = align256(M.up_bytes);
+  M.total = M.down + align256(M.down_bytes);
+  return M;
 }
 
 }  // namespace
@@ -1097,6 +1124,144 @@ int larosa_decode_attention(const void *q, const void *k_new, int64_t k_stride,
   return launched(launch_decode_attention(q, k_new, k_stride, v_new, v_stride, k_cache, v_cache,
                                           out, B, T, n_heads, n_kv_heads, dtype, ws,
                                           stream_of(stream)));
+  });
+}
+
+size_t larosa_mlp_workspace_bytes(int64_t B, int64_t d, int64_t f, int64_t k1, int64_t k2,
+                                  int mode) LAROSA_NOEXCEPT {
+  return guard_size([&]() -> size_t { return mlp_layout(B, d, f, k1, k2, mode).total; });
+}
+
+int larosa_mlp_forward(const void *x, int act_dtype, const void *Qt1, int64_t q_block1,
+                       const void *W_il, const void *Qt2, int64_t q_block2, const void *W_down,
+                       int w_dtype, int64_t B, int64_t d, int64_t f, int64_t k1, int64_t k2,
+                       void *h, void *y, int32_t *idx1_out, float *xrot1_out, int32_t *idx2_out,
+                       float *xrot2_out, int mode, void *ws, size_t ws_bytes,
+                       larosa_stream_t stream) LAROSA_NOEXCEPT {
+  return guard([&]() -> int {
+  const bool want_chain = (mode & LAROSA_CHAIN) != 0;
+  mode &= ~LAROSA_CHAIN;
+  const MlpLayout M = mlp_layout(B, d, f, k1, k2, mode);
+  // every argument of both linears first
+  if (int st = layer_args(x, act_dtype, Qt1, q_block1, W_il, w_dtype, B, d, 2 * f, k1, h,
+                          xrot1_out, mode))
+    return st;
+  if (int st = layer_args(h, act_dtype, Qt2, q_block2, W_down, w_dtype, B, f, d, k2, y,
+                          xrot2_out, mode))
+    return st;
+  if (f < 1 || f % interleave_block(w_dtype)) return LAROSA_ERR_SHAPE;
+  if (B == 0) return LAROSA_OK;
+  if (!aligned16(ws)) return LAROSA_ERR_ALIGNMENT;
+  if (!ws || M.total == 0 || ws_bytes < M.total) return LAROSA_ERR_WORKSPACE;
+  {
+    const size_t hb = static_cast<size_t>(B) * f * dt_size(act_dtype);
+    const char *hp = static_cast<const char *>(h), *xp = static_cast<const char *>(x);
+    const size_t xb = static_cast<size_t>(B) * d * dt_size(act_dtype);
+    if (hp < xp + xb && xp < hp + hb) return LAROSA_ERR_INVALID_ARG;  // h must not overlap x
+  }
+  if (int st = device_status()) return st;
+  char *base = static_cast<char *>(ws);
+  hipStream_t s = stream_of(stream);
+  const bool chain = want_chain && mode == LAROSA_UNFUSED && B == 1 && act_dtype == LAROSA_BF16 &&
+                     w_dtype == LAROSA_BF16 && select_gather_supported(d) &&
+                     select_gather_supported(f) && chain_supported(q_block2, f);
+  if (!chain) {
+    // the two layer calls (other batches, modes and types)
+    int st = swiglu_entry(x, act_dtype, Qt1, q_block1, W_il, w_dtype, B, d, f, Sel{false, k1},
+                          h, idx1_out, xrot1_out, mode, base + M.up, M.up_bytes, stream);
+    if (st != LAROSA_OK) return st;
+    return layer_entry(h, act_dtype, Qt2, q_block2, W_down, w_dtype, B, f, d, Sel{false, k2}, y,
+                       idx2_out, xrot2_out, mode, base + M.down, M.down_bytes, stream);
+  }
+  // One token: rotate x; the gate|up product with SiLU(gate)·up, chained into
+  // the rotation of h; the down product.
+  const Layout L1 = layout_for(1, d, 2 * f, k1, w_dtype);
+  const Layout L2 = layout_for(1, f, d, k2, w_dtype);
+  char *up = base + M.up;
+  char *dn = base + M.down;
+  float *xr1 = xrot1_out ? xrot1_out : reinterpret_cast<float *>(up + L1.x_rot);
+  float *xr2 = xrot2_out ? xrot2_out : reinterpret_cast<float *>(dn + L2.x_rot);
+  uint32_t *status = reinterpret_cast<uint32_t *>(up + L1.p.status);
+  const uint32_t spin = g_spin_limit.load();
+  if (launch_rotate(x, act_dtype, Qt1, w_dtype, xr1, 1, static_cast<int>(d),
+                    static_cast<int>(q_block1), s) != hipSuccess)
+    return LAROSA_ERR_LAUNCH;
+  SelectGatherArgs g;
+  g.x_rot = xr1;
+  g.d_in = static_cast<int>(d);
+  g.k = static_cast<int>(k1);
+  g.w = W_il;
+  g.w_dt = w_dtype;
+  g.d_out = 2 * f;
+  g.y = h;
+  g.y_dt = act_dtype;
+  g.idx_out = idx1_out;
+  g.ws = up + L1.p.gather;
+  g.swiglu = true;
+  g.chain.qt = static_cast<const uint16_t *>(Qt2);
+  g.chain.qb = static_cast<int>(q_block2);
+  g.chain.f = static_cast<int>(f);
+  g.chain.x_rot = xr2;
+  g.chain.tile_flag = reinterpret_cast<uint32_t *>(up + L1.p.flags);
+  g.chain.ctl = reinterpret_cast<uint64_t *>(up + L1.p.flags + chain_ctl_offset(f));
+  g.chain.status = status;
+  g.chain.spin_limit = spin;
+  if (launch_select_gather(g, s) != hipSuccess) return LAROSA_ERR_LAUNCH;
+  SelectGatherArgs g2;
+  g2.x_rot = xr2;
+  g2.d_in = static_cast<int>(f);
+  g2.k = static_cast<int>(k2);
+  g2.w = W_down;
+  g2.w_dt = w_dtype;
+  g2.d_out = d;
+  g2.y = y;
+  g2.y_dt = act_dtype;
+  g2.idx_out = idx2_out;
+  g2.ws = dn + L2.p.gather;
+  return launched(launch_select_gather(g2, s));
+  });
+}
+
+int larosa_topk_swiglu_rotate(const float *x_rot, int64_t d_in, int64_t k, const void *W_il,
+                              int w_dtype, void *h, int64_t f, const void *Qt2, int64_t q_block2,
+                              float *x_rot2, int32_t *idx_out, void *ws, size_t ws_bytes,
+                              larosa_stream_t stream) LAROSA_NOEXCEPT {
+  return guard([&]() -> int {
+  if (w_dtype != LAROSA_BF16) return LAROSA_ERR_DTYPE;
+  if (int st = check_sizes(1, d_in, k)) return st;
+  if (!select_gather_supported(d_in) || !select_gather_supported(f)) return LAROSA_ERR_SHAPE;
+  if (f < 1 || f % interleave_block(w_dtype)) return LAROSA_ERR_SHAPE;
+  if (!chain_supported(q_block2, f)) return LAROSA_ERR_SHAPE;
+  if (!x_rot || !W_il || !h || !Qt2 || !x_rot2) return LAROSA_ERR_INVALID_ARG;
+  if (!aligned16(x_rot) || !aligned16(W_il) || !aligned16(h) || !aligned16(Qt2) ||
+      !aligned16(x_rot2))
+    return LAROSA_ERR_ALIGNMENT;
+  const Prefix P = prefix_for(1, d_in, 2 * f, d_in, w_dtype);
+  if (!ws || ws_bytes < P.end) return LAROSA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return LAROSA_ERR_ALIGNMENT;
+  if (int st = device_status()) return st;
+  char *base = static_cast<char *>(ws);
+  SelectGatherArgs g;
+  g.x_rot = x_rot;
+  g.d_in = static_cast<int>(d_in);
+  g.k = static_cast<int>(k);
+  g.w = W_il;
+  g.w_dt = w_dtype;
+  g.d_out = 2 * f;
+  g.y = h;
+  g.y_dt = LAROSA_BF16;
+  g.idx_out = idx_out;
+  g.ws = base + P.gather;
+  g.swiglu = true;
+  g.chain.qt = static_cast<const uint16_t *>(Qt2);
+  g.chain.qb = static_cast<int>(q_block2);
+  g.chain.f = static_cast<int>(f);
+  g.chain.x_rot = x_rot2;
+  g.chain.tile_flag = reinterpret_cast<uint32_t *>(base + P.flags);
+  g.chain.ctl = reinterpret_cast<uint64_t *>(base + P.flags + chain_ctl_offset(f));
+  g.chain.status = reinterpret_cast<uint32_t *>(base + P.status);
+  g.chain.spin_limit = g_spin_limit.load();
+  return launched(launch_select_gather(g, stream_of(stream)));
   });
 }
 

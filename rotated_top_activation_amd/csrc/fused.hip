@@ -33,19 +33,23 @@
 // The bin-B0 rows go last in every unit's accumulation whatever the timing,
 // so results do not depend on when the exact rule arrives.
 //
-// Every hand-over word carries the launch's epoch (a 16-bit number the host
-// gives each launch, never 0): a worker arrives by writing the epoch into its
-// own slot, and a release counts only with the current epoch. Nothing has to
-// be reset between calls, so a call that gave up a wait leaves nothing stale
-// that the next call could mistake for its own. Waits are bounded (the
-// spin limit is a kernel argument): a wait that runs past the limit writes
-// LAROSA_ERR_TIMEOUT into the workspace's status word and continues with a
-// fallback (an in-bounds but wrong result) instead of hanging.
+// Every hand-over word carries the launch's epoch, a 16-bit number (never 0)
+// kept on the device, so a captured graph replays correctly. One 64-bit
+// control word holds the previous launch's epoch (high half) and a count of
+// workgroups (low half): each workgroup adds 1 once (before any wait) and so
+// reads the epoch and the count in one atomic; the last one stores the new
+// epoch with a zero count. No workgroup can read the word after that store,
+// so every workgroup of a launch has the same epoch even if waits give up.
+// A worker arrives by writing the epoch into its own slot, and a release
+// counts only with the current epoch, so nothing has to be reset between
+// calls. Waits are bounded (the spin limit is a kernel argument): a wait that
+// runs past the limit writes LAROSA_ERR_TIMEOUT into the workspace's status
+// word and continues with a fallback (an in-bounds but wrong result) instead
+// of hanging, and leaves nothing that the next launch could take as its own.
 #include "common.hpp"
 #include "launch.hpp"
 #include "select_core.hpp"
 
-#include <atomic>
 #include <cstddef>
 #include <mutex>
 
@@ -100,6 +104,7 @@ struct FusedSmem {
   uint32_t claim, tail;     // bin-B0 compaction: claimed; done (count + 1)
   uint32_t last;            // this unit is the last of its tile
   uint32_t b0, T, cut, stage;
+  uint32_t epoch;           // this launch's epoch
   alignas(16) union {
     SelectorSmem s;
     WorkerSmem w;
@@ -305,9 +310,9 @@ template <typename T>
 __global__ __launch_bounds__(kFT) void fused_linear_kernel(
     const T *__restrict__ x, const T *__restrict__ qt, const T *__restrict__ wf,
     T *__restrict__ y, int d, int qb, int64_t d_out, int k, float *__restrict__ x_rot,
-    uint32_t *__restrict__ arrive, uint64_t *__restrict__ flags,
+    uint32_t *__restrict__ arrive, uint64_t *__restrict__ ctl, uint64_t *__restrict__ flags,
     uint32_t *__restrict__ tile_ctr, float *__restrict__ partials,
-    int32_t *__restrict__ idx_out, int tiles, int splits, int chans_per_split, uint32_t epoch,
+    int32_t *__restrict__ idx_out, int tiles, int splits, int chans_per_split,
     uint32_t spin_limit, uint32_t *__restrict__ status) {
   constexpr int V = Elt<T>::kVec;
   constexpr int TILE = kWave * V;
@@ -335,7 +340,19 @@ __global__ __launch_bounds__(kFT) void fused_linear_kernel(
     if (lane == 0) __hip_atomic_store(x_rot + j, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __builtin_amdgcn_s_waitcnt(0);  // this workgroup's x_rot stores have completed
+  // this launch's epoch (1 .. 65535) and the workgroup count in one atomic;
+  // the last workgroup to count stores the epoch for the next launch
+  if (t == 0) {
+    const uint64_t old = __hip_atomic_fetch_add(ctl, uint64_t{1}, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t e = static_cast<uint32_t>(old >> 32) % 65535u + 1u;
+    sm.epoch = e;
+    if (static_cast<uint32_t>(old) == G - 1)
+      __hip_atomic_store(ctl, static_cast<uint64_t>(e) << 32, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
   __syncthreads();
+  const uint32_t epoch = sm.epoch;
 
   // ---- 2. selector ---------------------------------------------------------
   if (blockIdx.x == 0) {
@@ -564,9 +581,7 @@ hipError_t launch_t(const FusedArgs &a, hipStream_t s) {
   const FusedPlan p = plan_fused(a.d_in, a.d_out, a.k, a.w_dt, capacity);
   char *ws = static_cast<char *>(a.ws);
   uint32_t *arrive = reinterpret_cast<uint32_t *>(ws);
-  // 1 .. 65535, a different one for each launch (16 bits of the words)
-  static std::atomic<uint32_t> launches{0};
-  const uint32_t epoch = launches.fetch_add(1u) % 65535u + 1u;
+  uint64_t *ctl = reinterpret_cast<uint64_t *>(ws + static_cast<size_t>(kFusedMaxGrid) * 4);
   uint32_t *tile_ctr = reinterpret_cast<uint32_t *>(ws + p.tile_off);
   uint64_t *flags = reinterpret_cast<uint64_t *>(ws + p.flags_off);
   float *x_rot = a.xrot_out ? a.xrot_out : reinterpret_cast<float *>(ws + p.xrot_off);
@@ -574,8 +589,8 @@ hipError_t launch_t(const FusedArgs &a, hipStream_t s) {
   hipLaunchKernelGGL((fused_linear_kernel<T>), dim3(p.grid), dim3(kFT), lds, s,
                      static_cast<const T *>(a.x), static_cast<const T *>(a.qt),
                      static_cast<const T *>(a.wf), static_cast<T *>(a.y), a.d_in, a.q_block,
-                     a.d_out, a.k, x_rot, arrive, flags, tile_ctr, partials, a.idx_out,
-                     p.tiles, p.splits, p.chans_per_split, epoch, a.spin_limit, a.status);
+                     a.d_out, a.k, x_rot, arrive, ctl, flags, tile_ctr, partials, a.idx_out,
+                     p.tiles, p.splits, p.chans_per_split, a.spin_limit, a.status);
   return hipGetLastError();
 }
 
@@ -600,7 +615,7 @@ FusedPlan plan_fused(int64_t d_in, int64_t d_out, int64_t k, int w_dt, int grid)
   const int64_t cps = (d_in + splits - 1) / splits;
   p.splits = static_cast<int>((d_in + cps - 1) / cps);
   p.chans_per_split = static_cast<int>(cps);
-  p.tile_off = up256(static_cast<size_t>(kFusedMaxGrid) * 4);  // arrival slots
+  p.tile_off = up256(static_cast<size_t>(kFusedMaxGrid) * 4 + 8);  // arrival slots, control word
   p.flags_off = p.tile_off + up256(static_cast<size_t>(p.tiles) * 4);
   p.xrot_off = p.flags_off + static_cast<size_t>(kFusedMaxGrid) * 128;
   p.partial_off = p.xrot_off + up256(static_cast<size_t>(d_in) * 4);

@@ -117,6 +117,27 @@ SelectGatherPlan plan_select_gather(int64_t d_in, int64_t d_out, int w_dt);
 // partial sums.
 size_t select_gather_ws_bytes(int64_t d_in, int64_t d_out, int w_dt);
 bool select_gather_supported(int64_t d_in);
+// The chained form (see select_gather.hip): after the SwiGLU product, rotate
+// h [f] by the next linear's prepared Q (bf16, blocks of qb) into x_rot.
+// tile_flag: one word per product column tile (f / 256 of them); ctl: the
+// launch's control block (two queue words, the epoch word and the count of
+// finished tiles). Both sit in the workspace, zero-filled before first use;
+// the kernel takes its epoch from the control block and advances it.
+struct ChainArgs {
+  const uint16_t *qt = nullptr;  // NULL: no chain
+  int qb = 0;
+  int f = 0;
+  float *x_rot = nullptr;
+  uint32_t *tile_flag = nullptr;
+  uint64_t *ctl = nullptr;
+  uint32_t *status = nullptr;       // kStatusTimeout when a wait gave up (may be NULL)
+  uint32_t spin_limit = 1u << 22;
+};
+// Bytes of a chained launch's tile flags over f h channels, then its control
+// block (24 bytes, 8-byte aligned).
+inline size_t chain_flag_bytes(int64_t f) { return (static_cast<size_t>(f / 256 + 1) * 4 + 7) / 8 * 8 + 24; }
+inline size_t chain_ctl_offset(int64_t f) { return chain_flag_bytes(f) - 24; }
+bool chain_supported(int64_t q_block, int64_t f);
 struct SelectGatherArgs {
   const float *x_rot;  // [d_in] fp32
   int d_in, k;
@@ -136,6 +157,7 @@ struct SelectGatherArgs {
   bool by_threshold = false;
   uint32_t thr_key = 0;
   int32_t *count_out = nullptr;
+  ChainArgs chain;
 };
 hipError_t launch_select_gather(const SelectGatherArgs &a, hipStream_t s);
 

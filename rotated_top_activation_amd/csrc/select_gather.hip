@@ -21,6 +21,33 @@
 // The grid is sized to at most one workgroup per CU (256 on MI355X), which
 // keeps every workgroup resident for the whole launch.
 //
+// Chained form (CHAIN, the gate|up linear of a one-token MLP): after the
+// product the workgroups go on to the down linear's rotation, x_rot2 = h·Q2
+// (block-diagonal Q2, blocks of at most 4096), without a second launch and
+// without a grid-wide barrier. Each tile's finishing workgroup writes its 256
+// channels of h = SiLU(gate)·up with agent-scope atomic stores, waits for
+// them to complete and then writes this launch's epoch into the tile's flag
+// word. Every workgroup then takes 16 consecutive channels of x_rot2 at a
+// time from a work queue, one wave per channel: each wave first requests its
+// channels' Q2 rows, which do not depend on h; then one lane per workgroup
+// waits (bounded, polling gently) until every tile that covers the channels'
+// Q2 blocks carries this epoch, the workgroup copies those blocks of h into
+// LDS with agent-scope atomic loads, and the waves take their dot products.
+// So the rotation's weight traffic overlaps the product's tail (the
+// stragglers and the split reduction) instead of following it. The dot
+// products use the one-token rotation kernel's order (lane-strided 16-byte
+// chunks, then a wave sum), so x_rot2 has the same bits as that kernel's.
+//
+// The epoch is kept on the device, so a captured graph replays correctly:
+// every workgroup reads the control block's epoch word at its start and uses
+// that number + 1 (1 .. 2^31, wrapping). The workgroup that finishes the last
+// tile (so every workgroup has arrived, and has read the word) stores the new
+// epoch there. The work queue is one of two counters, chosen by the epoch's
+// parity; a launch zeroes the other one, which the previous launch used, for
+// the next. Flags of earlier launches carry other epochs, and a wait that
+// gives up leaves no state ahead of the next launch, so nothing has to be
+// reset between calls.
+//
 // Threshold form (THR): the kept channels are those with |x_rot| >= t (the
 // magnitude threshold of the R-Sparse summary page, 研究流程与方法 ·
 // R-Sparse框架设计). No rule has to be found: every workgroup compacts its
@@ -41,12 +68,15 @@ constexpr int kSgMaxSplitLoads = 32;  // partial sums fetched per round trip
 
 size_t sg_counter_bytes(int tiles) { return (static_cast<size_t>(tiles) * 4 + 255) / 256 * 256; }
 
-template <typename WT, typename OT, int EMAX, bool SWIGLU, bool THR>
+constexpr int kChainChunks = 8;  // 16-byte chunks per lane of a Q2 row: q_block <= 4096
+
+template <typename WT, typename OT, int EMAX, bool SWIGLU, bool THR, bool CHAIN>
 __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
     const float *__restrict__ x_rot, int d, int k, uint32_t thr_key, int E, int tiles,
     int splits, int cps, const WT *__restrict__ w, int64_t d_out, OT *__restrict__ y,
     float *__restrict__ partials, uint32_t *__restrict__ counters,
-    int32_t *__restrict__ idx_out, int32_t *__restrict__ count_out) {
+    int32_t *__restrict__ idx_out, int32_t *__restrict__ count_out, ChainArgs chain) {
+  static_assert(!CHAIN || (SWIGLU && !THR), "the chain follows the SwiGLU product");
   constexpr int V = Elt<WT>::kVec;
   constexpr int TILE = kWave * V;
   constexpr int R = kSgRows;  // loads in flight per lane, list positions per group
@@ -74,6 +104,19 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
   const int t = threadIdx.x;
   const int lane = t % kWave;
   const int wave = wave_id();
+  // (chain) this launch's epoch from the control block; the first workgroup
+  // zeroes the queue counter that the next launch will use
+  __shared__ uint32_t s_epoch;
+  uint32_t *const ctl32 = reinterpret_cast<uint32_t *>(chain.ctl + 2);  // [epoch word, tiles done]
+  if constexpr (CHAIN)
+    if (t == 0) {
+      const uint32_t e =
+          __hip_atomic_load(&ctl32[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 0x7fffffffu;
+      s_epoch = e + 1u;
+      if (blockIdx.x == 0)
+        __hip_atomic_store(&chain.ctl[(e + 2u) & 1u], uint64_t{0}, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
   const int tile = blockIdx.x % tiles;
   const int split = blockIdx.x / tiles;
   const int c0 = split * cps < d ? split * cps : d;
@@ -268,6 +311,33 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
   auto epilogue = [&]() {
     if (!SWIGLU) return;
     __syncthreads();
+    if constexpr (CHAIN) {
+      // h with agent-scope atomic stores (two bf16 per word), then the tile's
+      // flag once every store has completed
+      uint32_t *h32 = reinterpret_cast<uint32_t *>(y) + static_cast<int64_t>(tile) * (TILE / 4);
+      for (int e = t; e < TILE / 4; e += kSgThreads) {
+        const float h0 = silu_mul(Elt<OT>::round(ep[2 * e]), Elt<OT>::round(ep[TILE / 2 + 2 * e]));
+        const float h1 =
+            silu_mul(Elt<OT>::round(ep[2 * e + 1]), Elt<OT>::round(ep[TILE / 2 + 2 * e + 1]));
+        const uint32_t word = static_cast<uint32_t>(f32_to_bf16(h0)) |
+                              (static_cast<uint32_t>(f32_to_bf16(h1)) << 16);
+        __hip_atomic_store(h32 + e, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (t == 0) {
+        const uint32_t epoch = s_epoch;
+        __hip_atomic_store(&chain.tile_flag[tile], epoch, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        // the last tile finished: every workgroup has read the epoch word
+        if (__hip_atomic_fetch_add(&ctl32[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            static_cast<uint32_t>(tiles - 1)) {
+          __hip_atomic_store(&ctl32[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(&ctl32[0], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      return;
+    }
     for (int e = t; e < TILE / 2; e += kSgThreads)
       Elt<OT>::store(y, static_cast<int64_t>(tile) * (TILE / 2) + e,
                      silu_mul(Elt<OT>::round(ep[e]), Elt<OT>::round(ep[TILE / 2 + e])));
@@ -291,64 +361,187 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
   }
   if (splits == 1) {
     epilogue();
-    return;
-  }
-
-  // The tile's last workgroup to arrive adds the partial sums in split
-  // order (the result does not depend on arrival order) and resets the
-  // tile's counter for the next call.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (t == 0) {
-    const uint32_t prev =
-        __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = prev == static_cast<uint32_t>(splits - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  for (int e = t; e < TILE; e += kSgThreads) {
-    const int64_t cg = tile_col0 + e;
-    if (cg >= d_out) continue;
-    const float *p = partials + cg;
-    float sum = 0.f;
-    for (int r0 = 0; r0 < splits; r0 += kSgMaxSplitLoads) {
-      float pv[kSgMaxSplitLoads];
-#pragma unroll
-      for (int i = 0; i < kSgMaxSplitLoads; ++i)
-        pv[i] = r0 + i < splits ? __hip_atomic_load(p + (r0 + i) * d_out, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT)
-                                : 0.f;
-#pragma unroll
-      for (int i = 0; i < kSgMaxSplitLoads; ++i)
-        if (r0 + i < splits) sum += pv[i];
+  } else {
+    // The tile's last workgroup to arrive adds the partial sums in split
+    // order (the result does not depend on arrival order) and resets the
+    // tile's counter for the next call.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t == 0) {
+      const uint32_t prev =
+          __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = prev == static_cast<uint32_t>(splits - 1);
     }
-    finish(e, sum);
+    __syncthreads();
+    if (s_last) {
+      for (int e = t; e < TILE; e += kSgThreads) {
+        const int64_t cg = tile_col0 + e;
+        if (cg >= d_out) continue;
+        const float *p = partials + cg;
+        float sum = 0.f;
+        for (int r0 = 0; r0 < splits; r0 += kSgMaxSplitLoads) {
+          float pv[kSgMaxSplitLoads];
+#pragma unroll
+          for (int i = 0; i < kSgMaxSplitLoads; ++i)
+            pv[i] = r0 + i < splits ? __hip_atomic_load(p + (r0 + i) * d_out, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT)
+                                    : 0.f;
+#pragma unroll
+          for (int i = 0; i < kSgMaxSplitLoads; ++i)
+            if (r0 + i < splits) sum += pv[i];
+        }
+        finish(e, sum);
+      }
+      epilogue();
+      if (t == 0)
+        __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
-  epilogue();
-  if (t == 0)
-    __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if constexpr (!CHAIN) return;
+
+  // 8. (chain) x_rot2[j] = h[blk(j)·qb ..]·Qt2[j, :]. Workgroups take chunks
+  //    of 16 consecutive channels (one per wave) from the launch's queue as
+  //    they finish the product, so the ones that finish early (not a tile's
+  //    last split) do most of the rotation. A chunk's Q2 rows are requested
+  //    at once, before its block of h is known to be complete; then one lane
+  //    waits (bounded) until every product tile of the block has written its
+  //    flag, the workgroup copies the block of h into LDS with agent-scope
+  //    loads, and the waves take their dot products. The next chunk is
+  //    grabbed, and its rows requested, before the current one is summed.
+  //    Barriers here are bare s_barrier after an LDS wait, so they do not
+  //    wait for the rows in flight.
+  const int qb2 = chain.qb;
+  const int chunks = qb2 / 8;
+  const int n_chunks = (chain.f + kSgWaves - 1) / kSgWaves;
+  __shared__ int s_next[2];  // the chunk after the current one, by iteration parity
+  __shared__ int s_hblk[2];  // blocks of h staged in LDS: [first, last], -1 when none
+  uint64_t *hs = reinterpret_cast<uint64_t *>(kv);  // staged h (two blocks at most)
+  const uint64_t *h64 = reinterpret_cast<const uint64_t *>(y);
+  auto bar = [&]() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS traffic is done
+    __builtin_amdgcn_s_barrier();
+  };
+  const uint32_t epoch = s_epoch;
+  uint64_t *const queue = chain.ctl + (epoch & 1u);
+  // A grab is issued by thread 0 and its result read one iteration later, so
+  // the round trip overlaps a chunk's work.
+  auto grab = [&]() {
+    return __hip_atomic_fetch_add(queue, uint64_t{1}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto chunk_of = [&](uint64_t w) {
+    return w < static_cast<uint64_t>(n_chunks) ? static_cast<int>(w) : n_chunks;
+  };
+  auto load_row = [&](int j, uint4(&q)[kChainChunks]) {
+    const uint16_t *row = chain.qt + static_cast<int64_t>(j < chain.f ? j : chain.f - 1) * qb2;
+#pragma unroll
+    for (int i = 0; i < kChainChunks; ++i) {
+      const int cc = lane + kWave * i;
+      q[i] = cc < chunks ? load16(row + cc * 8) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  uint64_t pending = 0;  // thread 0: the grab in flight
+  if (t == 0) {
+    s_hblk[0] = -1;
+    s_hblk[1] = -1;
+    s_next[0] = chunk_of(grab());  // the first chunk (waits once)
+    pending = grab();
+  }
+  bar();  // also: every wave is past the product's last use of LDS
+  int cur = s_next[0];
+  uint4 rq[kChainChunks], rn[kChainChunks];
+  if (cur < n_chunks) load_row(cur * kSgWaves + wave, rq);
+  bool gave_up = false;
+  int par = 1;
+  while (cur < n_chunks) {
+    const int jc0 = cur * kSgWaves;
+    const int jc1 = jc0 + kSgWaves < chain.f ? jc0 + kSgWaves : chain.f;
+    const int b_lo = jc0 / qb2, b_hi = (jc1 - 1) / qb2;
+    if (b_lo != s_hblk[0] || b_hi != s_hblk[1]) {
+      // wait for every product tile of these blocks, then stage them (the
+      // barrier first: no wave still reads the blocks staged before)
+      const int hlo = b_lo * qb2, hhi = (b_hi + 1) * qb2;
+      const int t_lo = hlo / (TILE / 2), t_hi = (hhi - 1) / (TILE / 2);
+      if (wave == 0) {
+        uint32_t spins = 0;
+        for (;;) {
+          bool in = true;
+          for (int tt = t_lo + lane; tt <= t_hi; tt += kWave)
+            in = in && __hip_atomic_load(&chain.tile_flag[tt], __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT) == epoch;
+          if (__all(in)) break;
+          if (spins++ >= chain.spin_limit) {
+            gave_up = true;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(8);
+        }
+      }
+      bar();
+      for (int i = t; i < (hhi - hlo) / 4; i += kSgThreads)
+        hs[i] = __hip_atomic_load(h64 + hlo / 4 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (t == 0) {
+        s_hblk[0] = b_lo;
+        s_hblk[1] = b_hi;
+      }
+    }
+    if (t == 0) s_next[par] = chunk_of(pending);
+    bar();  // the staged h, s_hblk and s_next[par] are visible
+    const int nxt = s_next[par];
+    par ^= 1;
+    if (t == 0 && nxt < n_chunks) pending = grab();
+    if (nxt < n_chunks) load_row(nxt * kSgWaves + wave, rn);  // in flight during this chunk
+    const int j = jc0 + wave;
+    if (j < jc1) {
+      const uint4 *hb = reinterpret_cast<const uint4 *>(hs) + ((j / qb2) * qb2 - b_lo * qb2) / 8;
+      float accr = 0.f;
+#pragma unroll
+      for (int i = 0; i < kChainChunks; ++i) {
+        const int cc = lane + kWave * i;
+        const uint4 hx = cc < chunks ? hb[cc] : make_uint4(0, 0, 0, 0);
+        float xf[8], qf[8];
+        Elt<uint16_t>::unpack(hx, xf);
+        Elt<uint16_t>::unpack(rq[i], qf);
+#pragma unroll
+        for (int v = 0; v < 8; ++v) accr = fmaf(xf[v], qf[v], accr);
+      }
+      const float sum = wave_sum(accr);
+      if (lane == 0) chain.x_rot[j] = sum;
+    }
+    cur = nxt;
+#pragma unroll
+    for (int i = 0; i < kChainChunks; ++i) rq[i] = rn[i];
+  }
+  if (gave_up && lane == 0 && chain.status != nullptr)
+    __hip_atomic_store(chain.status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <typename WT, typename OT, int EM, bool SW, bool TH>
+template <typename WT, typename OT, int EM, bool SW, bool TH, bool CH>
 void launch_sg_k(const SelectGatherArgs &a, const SelectGatherPlan &p, int E, hipStream_t s) {
   uint32_t *counters = static_cast<uint32_t *>(a.ws);
   float *partials =
       reinterpret_cast<float *>(static_cast<char *>(a.ws) + sg_counter_bytes(p.tiles));
   const dim3 grid(static_cast<unsigned>(p.tiles * p.splits)), block(kSgThreads);
-  hipLaunchKernelGGL((select_gather_kernel<WT, OT, EM, SW, TH>), grid, block, 0, s, a.x_rot,
+  const ChainArgs &chain = a.chain;
+  hipLaunchKernelGGL((select_gather_kernel<WT, OT, EM, SW, TH, CH>), grid, block, 0, s, a.x_rot,
                      a.d_in, a.k, a.thr_key, E, p.tiles, p.splits, p.cps,
                      static_cast<const WT *>(a.w), a.d_out, static_cast<OT *>(a.y), partials,
-                     counters, a.idx_out, a.count_out);
+                     counters, a.idx_out, a.count_out, chain);
 }
 
 template <typename WT, typename OT, int EM>
 void launch_sg_em(const SelectGatherArgs &a, const SelectGatherPlan &p, int E, hipStream_t s) {
   if (a.by_threshold) {
-    if (a.swiglu) launch_sg_k<WT, OT, EM, true, true>(a, p, E, s);
-    else launch_sg_k<WT, OT, EM, false, true>(a, p, E, s);
+    if (a.swiglu) launch_sg_k<WT, OT, EM, true, true, false>(a, p, E, s);
+    else launch_sg_k<WT, OT, EM, false, true, false>(a, p, E, s);
   } else {
-    if (a.swiglu) launch_sg_k<WT, OT, EM, true, false>(a, p, E, s);
-    else launch_sg_k<WT, OT, EM, false, false>(a, p, E, s);
+    if constexpr (sizeof(WT) == 2 && sizeof(OT) == 2) {
+      if (a.chain.qt != nullptr) {
+        launch_sg_k<WT, OT, EM, true, false, true>(a, p, E, s);
+        return;
+      }
+    }
+    if (a.swiglu) launch_sg_k<WT, OT, EM, true, false, false>(a, p, E, s);
+    else launch_sg_k<WT, OT, EM, false, false, false>(a, p, E, s);
   }
 }
 
@@ -388,9 +581,18 @@ size_t select_gather_ws_bytes(int64_t d_in, int64_t d_out, int w_dt) {
 
 bool select_gather_supported(int64_t d_in) { return d_in >= 1 && d_in <= kSgKeysMax; }
 
+bool chain_supported(int64_t q_block, int64_t f) {
+  return q_block >= 8 && q_block % 8 == 0 && q_block <= 8 * kWave * kChainChunks && f % q_block == 0;
+}
+
 hipError_t launch_select_gather(const SelectGatherArgs &a, hipStream_t s) {
   const SelectGatherPlan p = plan_select_gather(a.d_in, a.d_out, a.w_dt);
   if (p.cps > kSgListMax) return hipErrorInvalidValue;
+  if (a.chain.qt != nullptr &&
+      (!a.swiglu || a.by_threshold || a.w_dt != kBF16 || a.y_dt != kBF16 ||
+       !chain_supported(a.chain.qb, a.chain.f) || a.d_out != 2 * a.chain.f ||
+       a.chain.tile_flag == nullptr || a.chain.ctl == nullptr || a.chain.x_rot == nullptr))
+    return hipErrorInvalidValue;
   if (a.w_dt == kBF16 && a.y_dt == kBF16) return launch_sg_t<uint16_t, uint16_t>(a, p, s);
   if (a.w_dt == kBF16 && a.y_dt == kF32) return launch_sg_t<uint16_t, float>(a, p, s);
   if (a.w_dt == kF32 && a.y_dt == kF32) return launch_sg_t<float, float>(a, p, s);

@@ -65,6 +65,22 @@ def test_workspace_bytes(lib):
     assert f(8, 4096, 22016, 2457, 0) >= f(1, 4096, 22016, 2457, 0)
 
 
+def test_mlp_workspace_bytes(lib):
+    m = lib.larosa_mlp_workspace_bytes
+    args = (1, 4096, 11008, 2457, 6604)
+    unf = m(*args, 0)
+    assert unf > 0
+    # the chained form takes the unfused layout; any mode's workspace holds
+    # the one-launch up region, so the down region sits at one offset
+    assert m(*args, 8) == unf
+    assert m(*args, 8 | 2) == unf
+    assert m(*args, 1) >= unf
+    assert unf >= (lib.larosa_swiglu_workspace_bytes(1, 4096, 11008, 2457, 1) +
+                   lib.larosa_workspace_bytes(1, 11008, 4096, 6604, 0))
+    assert m(*args, 16) == 0          # unknown mode bit
+    assert m(*args, 9 | 16) == 0
+
+
 def _lf(lib, x=P, act=1, qt=P, qb=64, wf=P, wdt=1, B=1, d_in=128, d_out=64, k=32, y=P,
         idx=None, xr=None, mode=0, ws=P, wsb=1 << 30):
     return lib.larosa_layer_forward(x, act, qt, qb, wf, wdt, B, d_in, d_out, k, y, idx, xr,

@@ -280,6 +280,41 @@ def test_graph_replay_matches_eager(B, mode):
 
 
 @pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("B", [1, 4])
+def test_graph_replay_with_changing_inputs(B, mode):
+    """A captured layer_forward replayed on new inputs written into its input
+    buffer: every replay equals the eager call on the same input. Any state a
+    launch keeps between calls (the one-launch kernel's epoch) has to live on
+    the device for this to hold."""
+    case = wl.LinearCase(cfg=3, batch=B, d_in=2048, d_out=4104, q_block=512, sparsity_pct=40,
+                         dtype="bf16")
+    x, q, w = wl.linear_case_inputs(case, w_std=0.02)
+    lin = RotatedLinear(q, w, "bf16", case.k)
+    ws = lin.workspace(B, mode)
+    x_static = dev(x, "bf16")
+    y_g = torch.zeros((B, case.d_out), dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        lin.forward(x_static, y_g, ws, mode=mode)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lin.forward(x_static, y_g, ws, mode=mode)
+    rng = np.random.default_rng(100 + B + mode)
+    ws_eager = lin.workspace(B, mode)
+    for rep in range(5):
+        xn = dev(wl.quantize(x * rng.uniform(0.25, 4.0, x.shape), "bf16"), "bf16")
+        x_static.copy_(xn)
+        y_g.zero_()
+        g.replay()
+        y_e = torch.empty_like(y_g)
+        lin.forward(xn, y_e, ws_eager, mode=mode)
+        torch.cuda.synchronize()
+        assert torch.equal(y_g, y_e), f"replay {rep} differs"
+
+
+@pytest.mark.parametrize("mode", MODES)
 def test_changing_inputs_through_one_workspace(mode):
     """Different inputs through one workspace, call after call: every output
     matches the oracle (a stale partial sum from an earlier call would not)."""
