@@ -78,6 +78,9 @@ def parse():
     p.add_argument("--no-configs", action="store_true",
                    help="skip the other workloads (single linear, decoder step, layer slices)")
     p.add_argument("--config-steps", type=int, default=20)
+    p.add_argument("--only-config", default="",
+                   help="with --kernel-only configs: only the workloads whose name starts so "
+                        "(e.g. decoder32_7b_b1_s40, slice_13b)")
     p.add_argument("--kernel-only", choices=["", "gather", "topk1", "topk1s", "topk2", "fused1",
                                              "step", "copy", "configs"],
                    default="",
@@ -724,14 +727,11 @@ def _entry(B, ms, nbytes, extra=None):
     return out
 
 
-def other_configs(a, device):
+def _single_linear_f32(res, device):
+    """The fp32 512 -> 1536 single linear at batch 1, 40%, both modes."""
     import torch
-    from rotated_top_activation_amd import _lib, decoder as dec, workloads as wl
+    from rotated_top_activation_amd import _lib, workloads as wl
     from rotated_top_activation_amd.device import RotatedLinear
-    steps, warm = a.config_steps, 3
-    res = {}
-
-    # single linear, fp32, 512 -> 1536, batch 1, 40%
     case, x, q, w = wl.single_linear_f32()
     lin = RotatedLinear(q, w, "f32", case.k)
     x_d = wl.to_torch(x, "f32")
@@ -746,65 +746,88 @@ def other_configs(a, device):
     res["single_linear_f32_512x1536_b1_s40"] = _entry(1, best[0], nbytes, {"mode": best[1]})
     del lin
 
-    # 32-layer 7B decoder step
-    shape = wl.LLAMA7B
-    gen = torch.Generator(device=device)
-    gen.manual_seed(3)
-    d, f = shape.d, shape.f
-    base = {
-        "q_attn": _dev_haar(gen, d, 1, device), "q_o": _dev_haar(gen, d, 1, device),
-        "q_mlp": _dev_haar(gen, d, 1, device),
-        "q_down": _dev_haar(gen, shape.q2_block, f // shape.q2_block, device),
-        "w_qkv": _dev_weight(gen, d, shape.qkv_out, shape.w_std, device),
-        "w_o": _dev_weight(gen, d, d, shape.w_std, device),
-        "w_gu": _dev_weight(gen, d, 2 * f, shape.w_std, device),
-        "w_down": _dev_weight(gen, f, d, shape.w_std, device),
-    }
-    kv_base = tuple(torch.randn((shape.n_kv_heads, shape.ctx, shape.d_head), generator=gen,
-                                device=device).to(torch.bfloat16) for _ in range(2))
-    n_layers = 32
-    for B, sps in ((1, (25, 40, 50)), (4, (25, 40, 50)), (16, (25, 40, 50))):
-        layers = [dec.build_layer(3, l, shape, base, kv_base, B, sps[0])[0]
-                  for l in range(n_layers)]
-        buf = dec.DecoderBuffers(shape, B)
-        h0 = wl.to_torch(wl.decoder_hidden(3, B, d), "bf16")
-        h = h0.clone()
-        for sp in sps:
-            for L in layers:
-                for role in dec.ROLES:
-                    lin = L.lin[role]
-                    lin.k = wl.k_for(lin.d_in, sp)
-                L.ws = {}
 
-            def step():
+def other_configs(a, device):
+    import torch
+    from rotated_top_activation_amd import _lib, decoder as dec, workloads as wl
+    from rotated_top_activation_amd.device import RotatedLinear
+    steps, warm = a.config_steps, 3
+    res = {}
+    only = getattr(a, "only_config", "")
+
+    def want(name):
+        return not only or name.startswith(only)
+
+    # single linear, fp32, 512 -> 1536, batch 1, 40%
+    if want("single_linear_f32_512x1536_b1_s40"):
+        _single_linear_f32(res, device)
+
+    # 32-layer 7B decoder step
+    if any(want(f"decoder32_7b_b{B}_s{sp}") for B in (1, 4, 16) for sp in (25, 40, 50)):
+        shape = wl.LLAMA7B
+        gen = torch.Generator(device=device)
+        gen.manual_seed(3)
+        d, f = shape.d, shape.f
+        base = {
+            "q_attn": _dev_haar(gen, d, 1, device), "q_o": _dev_haar(gen, d, 1, device),
+            "q_mlp": _dev_haar(gen, d, 1, device),
+            "q_down": _dev_haar(gen, shape.q2_block, f // shape.q2_block, device),
+            "w_qkv": _dev_weight(gen, d, shape.qkv_out, shape.w_std, device),
+            "w_o": _dev_weight(gen, d, d, shape.w_std, device),
+            "w_gu": _dev_weight(gen, d, 2 * f, shape.w_std, device),
+            "w_down": _dev_weight(gen, f, d, shape.w_std, device),
+        }
+        kv_base = tuple(torch.randn((shape.n_kv_heads, shape.ctx, shape.d_head), generator=gen,
+                                    device=device).to(torch.bfloat16) for _ in range(2))
+        n_layers = 32
+        for B, sps in ((1, (25, 40, 50)), (4, (25, 40, 50)), (16, (25, 40, 50))):
+            sps = tuple(sp for sp in sps if want(f"decoder32_7b_b{B}_s{sp}"))
+            if not sps:
+                continue
+            layers = [dec.build_layer(3, l, shape, base, kv_base, B, sps[0])[0]
+                      for l in range(n_layers)]
+            buf = dec.DecoderBuffers(shape, B)
+            h0 = wl.to_torch(wl.decoder_hidden(3, B, d), "bf16")
+            h = h0.clone()
+            for sp in sps:
+                for L in layers:
+                    for role in dec.ROLES:
+                        lin = L.lin[role]
+                        lin.k = wl.k_for(lin.d_in, sp)
+                    L.ws = {}
+
+                def step():
+                    h.copy_(h0)
+                    _lib.larosa_rmsnorm(h, buf.a, B, d)
+                    for li, L in enumerate(layers):
+                        dec.layer_forward(L, h, buf, _lib.UNFUSED, normed=True,
+                                          norm_next=li < n_layers - 1)
+                ms = _timed_ms(step, steps, warm)
+                # bytes: rotations + union rows (one traced step) + key/value cache
+                nbytes = 0
                 h.copy_(h0)
                 _lib.larosa_rmsnorm(h, buf.a, B, d)
                 for li, L in enumerate(layers):
-                    dec.layer_forward(L, h, buf, _lib.UNFUSED, normed=True,
+                    trace = {}
+                    dec.layer_forward(L, h, buf, _lib.UNFUSED, trace=trace, normed=True,
                                       norm_next=li < n_layers - 1)
-            ms = _timed_ms(step, steps, warm)
-            # bytes: rotations + union rows (one traced step) + key/value cache
-            nbytes = 0
-            h.copy_(h0)
-            _lib.larosa_rmsnorm(h, buf.a, B, d)
-            for li, L in enumerate(layers):
-                trace = {}
-                dec.layer_forward(L, h, buf, _lib.UNFUSED, trace=trace, normed=True,
-                                  norm_next=li < n_layers - 1)
-                for role in dec.ROLES:
-                    lin = L.lin[role]
-                    nbytes += lin.Qt.numel() * 2 + _union_rows(trace[role][1]) * lin.d_out * 2
-                nbytes += B * 2 * shape.n_kv_heads * shape.ctx * shape.d_head * 2
-            res[f"decoder32_7b_b{B}_s{sp}"] = _entry(B, ms, nbytes, {"layers": n_layers})
-        del layers, buf
+                    for role in dec.ROLES:
+                        lin = L.lin[role]
+                        nbytes += lin.Qt.numel() * 2 + _union_rows(trace[role][1]) * lin.d_out * 2
+                    nbytes += B * 2 * shape.n_kv_heads * shape.ctx * shape.d_head * 2
+                res[f"decoder32_7b_b{B}_s{sp}"] = _entry(B, ms, nbytes, {"layers": n_layers})
+            del layers, buf
+            torch.cuda.empty_cache()
+        del base, kv_base
         torch.cuda.empty_cache()
-    del base, kv_base
-    torch.cuda.empty_cache()
 
     # layer slices: the four rotated linears of one layer (no attention core)
+    gen = torch.Generator(device=device)
     slices = (("13b", 4, 5120, 13824, 40, 40, 0.02, "outlier", 40, (8,)),
               ("70b", 5, 8192, 28672, 64, 8, 0.01, "heavy", 50, (32, 64)))
     for name, cfg, d, f, H, Hkv, wstd, act, sp, Bs in slices:
+        if not any(want(f"slice_{name}_b{B}_s{sp}") for B in Bs):
+            continue
         q2 = wl.ffn_q_block(f)
         qkv_out = (H + 2 * Hkv) * 128
         gen.manual_seed(cfg)
@@ -822,6 +845,9 @@ def other_configs(a, device):
                                      wl.k_for(f, sp), keep_w=False),
         }
         for B in Bs:
+            if not want(f"slice_{name}_b{B}_s{sp}"):
+                continue
+
             def acts(role):
                 if act == "outlier":
                     return wl.to_torch(wl.outlier_activations(cfg, 0, role, B, d, d // 100, 30.0,
