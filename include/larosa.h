@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define LAROSA_ABI_VERSION 7
+#define LAROSA_ABI_VERSION 8
 
 /* Every entry point is a no-throw C function: exceptions never cross the
  * ABI (a caught one is reported as LAROSA_ERR_INTERNAL). */
@@ -499,13 +499,36 @@ int larosa_rmsnorm(const void *h, void *out, int64_t B, int64_t d, float eps, in
 
 /* Rotate-half rotary embedding at position pos: for each head, channel i
  * (i < d_head/2) pairs with i + d_head/2 and both turn by
- * pos · theta^(−2i/d_head). Row b of qk holds n_heads query heads, then
+ * pos · theta^(−2i/d_head) (the angle in fp64 on the host, its cosine and
+ * sine rounded to fp32; d_head even and at most 256). Row b of qk holds n_heads query heads, then
  * n_kv_heads key heads (d_head channels each) at qk + b·qk_stride; the
  * results go to q_out [B, n_heads·d_head] and k_out [B, n_kv_heads·d_head],
  * which must not overlap qk. */
 int larosa_rope(const void *qk, int64_t qk_stride, void *q_out, void *k_out, int64_t B,
                 int64_t n_heads, int64_t n_kv_heads, int64_t d_head, int64_t pos, float theta,
                 int dtype, larosa_stream_t stream) LAROSA_NOEXCEPT;
+
+/* The q|k|v linear of a decoder layer with the rotary embedding applied:
+ * y = larosa_layer_forward(x; Qt, W_folded, k) over d_out = (n_heads +
+ * 2·n_kv_heads)·d_head columns (the q heads, then the k heads, then v),
+ * after which the q and k heads of every token's row are rotated in place
+ * at position pos as larosa_rope computes it (same rounding: each output
+ * is rounded to act_dtype before the rotation). The LaRoSA summary page
+ * (方法详解 · 技术框架) rotates and sparsifies the input of the attention
+ * projections like every other linear; the embedding is the decoder's own
+ * step. For one token in bf16 with the one-token product (unfused modes)
+ * the rotation runs in that product's epilogue, so no extra launch is made;
+ * otherwise a second kernel applies it. y: [B, d_out] in act_dtype. Other
+ * arguments, the workspace (larosa_workspace_bytes(B, d_in, d_out, k,
+ * mode)) and errors as larosa_layer_forward; LAROSA_ERR_INVALID_ARG for
+ * head counts outside 1..4096, pos < 0 or theta <= 0; LAROSA_ERR_SHAPE for
+ * a d_head that is odd or above 256. */
+int larosa_qkv_rope_layer_forward(const void *x, int act_dtype, const void *Qt, int64_t q_block,
+                                  const void *W_folded, int w_dtype, int64_t B, int64_t d_in,
+                                  int64_t k, int64_t n_heads, int64_t n_kv_heads, int64_t d_head,
+                                  int64_t pos, float theta, void *y, int32_t *idx_out,
+                                  float *xrot_out, int mode, void *ws, size_t ws_bytes,
+                                  larosa_stream_t stream) LAROSA_NOEXCEPT;
 
 /* Workspace bytes of larosa_decode_attention (per-chunk partial results of
  * 256 positions); 0 for invalid sizes. */

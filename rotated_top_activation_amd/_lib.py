@@ -22,7 +22,7 @@ UNFUSED, FUSED = 0, 1
 ROTATE_FP64 = 2  # mode flag: fp64-accumulating rotation, OR-ed into UNFUSED or FUSED
 VALIDATE = 4     # mode flag: check the rotated input for NaN/inf (waits on the stream)
 CHAIN = 8        # mode flag of larosa_mlp_forward: the rotation of h chained into the gate|up launch
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 # status codes (include/larosa.h)
 OK, ERR_INVALID_ARG, ERR_SHAPE, ERR_ALIGNMENT, ERR_DTYPE, ERR_WORKSPACE = 0, 1, 2, 3, 4, 5
@@ -93,6 +93,10 @@ SIGNATURES = {
     "larosa_rmsnorm": (_c_int, [_c_vp, _c_vp, _c_i64, _c_i64, ctypes.c_float, _c_int, _c_vp]),
     "larosa_rope": (_c_int, [_c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                              ctypes.c_float, _c_int, _c_vp]),
+    "larosa_qkv_rope_layer_forward": (_c_int, [_c_vp, _c_int, _c_vp, _c_i64, _c_vp, _c_int,
+                                               _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                               _c_i64, ctypes.c_float, _c_vp, _c_vp, _c_vp,
+                                               _c_int, _c_vp, _c_sz, _c_vp]),
     "larosa_decode_attention_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64]),
     "larosa_decode_attention": (_c_int, [_c_vp, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp, _c_vp, _c_vp,
                                          _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_int, _c_vp,
@@ -353,6 +357,18 @@ def larosa_rope(qk, qk_stride: int, q_out, k_out, B: int, n_heads: int, n_kv_hea
     _check("larosa_rope", load().larosa_rope(_ptr(qk), qk_stride, _ptr(q_out), _ptr(k_out), B,
                                              n_heads, n_kv_heads, d_head, pos, theta, _dt(qk),
                                              _stream(stream)))
+
+
+def larosa_qkv_rope_layer_forward(x, Qt, q_block: int, W_folded, B: int, d_in: int, k: int,
+                                  n_heads: int, n_kv_heads: int, d_head: int, pos: int, y,
+                                  theta: float = 10000.0, idx_out=None, xrot_out=None,
+                                  mode: int = UNFUSED, ws=None, stream=None) -> None:
+    _check("larosa_qkv_rope_layer_forward",
+           load().larosa_qkv_rope_layer_forward(_ptr(x), _dt(x), _ptr(Qt), q_block,
+                                                _ptr(W_folded), _dt(W_folded), B, d_in, k,
+                                                n_heads, n_kv_heads, d_head, pos, theta, _ptr(y),
+                                                _ptr(idx_out), _ptr(xrot_out), mode, _ptr(ws),
+                                                _nbytes(ws), _stream(stream)))
 
 
 def larosa_decode_attention_workspace_bytes(B: int, T: int, n_heads: int) -> int:

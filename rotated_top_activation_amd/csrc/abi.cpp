@@ -249,7 +249,10 @@ int layer_args(const void *x, int act_dtype, const void *Qt, int64_t q_block,
 int layer_entry(const void *x, int act_dtype, const void *Qt, int64_t q_block,
                 const void *W_folded, int w_dtype, int64_t B, int64_t d_in, int64_t d_out,
                 const Sel &sel, void *y, int32_t *idx_out, float *xrot_out, int mode, void *ws,
-                size_t ws_bytes, larosa_stream_t stream) {
+                size_t ws_bytes, larosa_stream_t stream, const RopeArgs *rope = nullptr,
+                bool *rope_done = nullptr) {
+  // rope: RoPE to fold into the one-token product's epilogue where that
+  // product runs (bf16); *rope_done says whether it was.
   const int64_t k = sel.k;
   if (int st = layer_args(x, act_dtype, Qt, q_block, W_folded, w_dtype, B, d_in, d_out, k, y,
                           xrot_out, mode))
@@ -339,7 +342,12 @@ int layer_entry(const void *x, int act_dtype, const void *Qt, int64_t q_block,
     g.by_threshold = sel.thr;
     g.thr_key = sel.thr_key;
     g.count_out = sel.count_out;
-    return launched(launch_select_gather(g, s));
+    const bool fold_rope = rope != nullptr && !sel.thr && act_dtype == LAROSA_BF16 &&
+                           w_dtype == LAROSA_BF16;
+    if (fold_rope) g.rope = *rope;
+    const int st = launched(launch_select_gather(g, s));
+    if (st == LAROSA_OK && fold_rope && rope_done) *rope_done = true;
+    return st;
   }
   if (B == 1) {
     if (sel.thr) {
@@ -1084,13 +1092,45 @@ int larosa_rope(const void *qk, int64_t qk_stride, void *q_out, void *k_out, int
   if (!dtype_ok(dtype)) return LAROSA_ERR_DTYPE;
   if (B < 0 || B > kMaxB || n_heads < 1 || n_kv_heads < 1 || pos < 0 || !(theta > 0.f))
     return LAROSA_ERR_INVALID_ARG;
-  if (d_head < 2 || d_head % 2 || qk_stride < (n_heads + n_kv_heads) * d_head)
+  if (d_head < 2 || d_head % 2 || d_head > 2 * kRopeMaxHalf ||
+      qk_stride < (n_heads + n_kv_heads) * d_head)
     return LAROSA_ERR_SHAPE;
   if (B == 0) return LAROSA_OK;
   if (!qk || !q_out || !k_out) return LAROSA_ERR_INVALID_ARG;
   if (int st = device_status()) return st;
-  return launched(launch_rope(qk, qk_stride, q_out, k_out, B, n_heads, n_kv_heads, d_head, pos,
-                              static_cast<double>(theta), dtype, stream_of(stream)));
+  return launched(launch_rope(qk, qk_stride, q_out, k_out, B, n_heads, n_kv_heads,
+                              rope_table(d_head, static_cast<double>(pos),
+                                         static_cast<double>(theta)),
+                              dtype, stream_of(stream)));
+  });
+}
+
+int larosa_qkv_rope_layer_forward(const void *x, int act_dtype, const void *Qt, int64_t q_block,
+                                  const void *W_folded, int w_dtype, int64_t B, int64_t d_in,
+                                  int64_t k, int64_t n_heads, int64_t n_kv_heads, int64_t d_head,
+                                  int64_t pos, float theta, void *y, int32_t *idx_out,
+                                  float *xrot_out, int mode, void *ws, size_t ws_bytes,
+                                  larosa_stream_t stream) LAROSA_NOEXCEPT {
+  return guard([&]() -> int {
+  if (n_heads < 1 || n_kv_heads < 1 || pos < 0 || !(theta > 0.f) || n_heads > 4096 ||
+      n_kv_heads > 4096)
+    return LAROSA_ERR_INVALID_ARG;
+  if (d_head < 2 || d_head % 2 || d_head > 2 * kRopeMaxHalf) return LAROSA_ERR_SHAPE;
+  const int64_t d_out = (n_heads + 2 * n_kv_heads) * d_head;
+  RopeArgs r;
+  r.rot_cols = static_cast<int>((n_heads + n_kv_heads) * d_head);
+  r.tab = rope_table(d_head, static_cast<double>(pos), static_cast<double>(theta));
+  // folded only where whole heads fill the product's 512-column tiles
+  const bool foldable = 512 % d_head == 0;
+  Sel sel;
+  sel.k = k;
+  bool done = false;
+  const int st = layer_entry(x, act_dtype, Qt, q_block, W_folded, w_dtype, B, d_in, d_out, sel,
+                             y, idx_out, xrot_out, mode, ws, ws_bytes, stream,
+                             foldable ? &r : nullptr, &done);
+  if (st != LAROSA_OK || done || B == 0) return st;
+  return launched(launch_rope_inplace(y, d_out, B, n_heads + n_kv_heads, r.tab, act_dtype,
+                                      stream_of(stream)));
   });
 }
 

@@ -28,6 +28,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // that applies it, so they agree bit for bit).
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
+// Rotary position embedding of one pair (a, b) = (x[i], x[i + dh/2]) of a
+// head with the pair's cosine c and sine s: (a·c − b·s, b·c + a·s) in fp32
+// with fixed fused multiply-adds (one definition for every kernel that
+// applies it).
+__device__ __forceinline__ float rope_lo(float a, float b, float c, float s) { return fmaf(-b, s, a * c); }
+__device__ __forceinline__ float rope_hi(float a, float b, float c, float s) { return fmaf(a, s, b * c); }
+
 // Element access by type tag: float or uint16_t (bf16).
 template <typename T> struct Elt;
 template <> struct Elt<float> {

@@ -10,6 +10,8 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#include <cmath>
+
 namespace larosa {
 namespace {
 
@@ -121,9 +123,8 @@ __global__ __launch_bounds__(kGT) void norm_vec_kernel(T *__restrict__ h, const 
 template <typename T>
 __global__ __launch_bounds__(kGT) void rope_kernel(const T *__restrict__ qk, int64_t stride,
                                                    T *__restrict__ q_out, T *__restrict__ k_out,
-                                                   int B, int n_heads, int n_kv, int dh,
-                                                   double pos, double theta) {
-  const int half = dh / 2;
+                                                   int B, int n_heads, int n_kv, RopeTable tab) {
+  const int dh = tab.dh, half = dh / 2;
   const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t per_tok = static_cast<int64_t>(n_heads + n_kv) * half;
   if (e >= per_tok * B) return;
@@ -133,13 +134,29 @@ __global__ __launch_bounds__(kGT) void rope_kernel(const T *__restrict__ qk, int
   const T *src = qk + b * stride + static_cast<int64_t>(head) * dh;
   T *dst = head < n_heads ? q_out + (static_cast<int64_t>(b) * n_heads + head) * dh
                           : k_out + (static_cast<int64_t>(b) * n_kv + (head - n_heads)) * dh;
-  const double ang = pos * pow(theta, -2.0 * i / dh);
-  double sd, cd;
-  sincos(ang, &sd, &cd);
-  const float s = static_cast<float>(sd), c = static_cast<float>(cd);
+  const float cs = tab.cs[i], sn = tab.sn[i];
   const float a = Elt<T>::load(src, i), bb = Elt<T>::load(src, i + half);
-  Elt<T>::store(dst, i, a * c - bb * s);
-  Elt<T>::store(dst, i + half, bb * c + a * s);
+  Elt<T>::store(dst, i, rope_lo(a, bb, cs, sn));
+  Elt<T>::store(dst, i + half, rope_hi(a, bb, cs, sn));
+}
+
+// The same rotation in place on the first n_rot heads of each token's row
+// (row b at qk + b·stride), one thread per pair.
+template <typename T>
+__global__ __launch_bounds__(kGT) void rope_inplace_kernel(T *__restrict__ qk, int64_t stride,
+                                                           int B, int n_rot, RopeTable tab) {
+  const int dh = tab.dh, half = dh / 2;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t per_tok = static_cast<int64_t>(n_rot) * half;
+  if (e >= per_tok * B) return;
+  const int b = static_cast<int>(e / per_tok);
+  const int r = static_cast<int>(e % per_tok);
+  const int head = r / half, i = r % half;
+  T *row = qk + b * stride + static_cast<int64_t>(head) * dh;
+  const float cs = tab.cs[i], sn = tab.sn[i];
+  const float a = Elt<T>::load(row, i), bb = Elt<T>::load(row, i + half);
+  Elt<T>::store(row, i, rope_lo(a, bb, cs, sn));
+  Elt<T>::store(row, i + half, rope_hi(a, bb, cs, sn));
 }
 
 // One workgroup per (query head, token). The cache is [B, n_kv, T, 128];
@@ -378,22 +395,47 @@ hipError_t launch_rmsnorm(const void *h, void *out, int64_t B, int64_t d, float 
 }
 
 hipError_t launch_rope(const void *qk, int64_t stride, void *q_out, void *k_out, int64_t B,
-                       int64_t n_heads, int64_t n_kv, int64_t dh, int64_t pos, double theta,
-                       int dt, hipStream_t s) {
-  const int64_t n = B * (n_heads + n_kv) * (dh / 2);
+                       int64_t n_heads, int64_t n_kv, const RopeTable &tab, int dt,
+                       hipStream_t s) {
+  const int64_t n = B * (n_heads + n_kv) * (tab.dh / 2);
+  if (n == 0) return hipSuccess;
   if (dt == kF32)
     hipLaunchKernelGGL(rope_kernel<float>, dim3(blocks_for(n)), dim3(kGT), 0, s,
                        static_cast<const float *>(qk), stride, static_cast<float *>(q_out),
                        static_cast<float *>(k_out), static_cast<int>(B), static_cast<int>(n_heads),
-                       static_cast<int>(n_kv), static_cast<int>(dh), static_cast<double>(pos),
-                       theta);
+                       static_cast<int>(n_kv), tab);
   else
     hipLaunchKernelGGL(rope_kernel<uint16_t>, dim3(blocks_for(n)), dim3(kGT), 0, s,
                        static_cast<const uint16_t *>(qk), stride, static_cast<uint16_t *>(q_out),
                        static_cast<uint16_t *>(k_out), static_cast<int>(B),
-                       static_cast<int>(n_heads), static_cast<int>(n_kv), static_cast<int>(dh),
-                       static_cast<double>(pos), theta);
+                       static_cast<int>(n_heads), static_cast<int>(n_kv), tab);
   return hipGetLastError();
+}
+
+hipError_t launch_rope_inplace(void *qk, int64_t stride, int64_t B, int64_t n_rot,
+                               const RopeTable &tab, int dt, hipStream_t s) {
+  const int64_t n = B * n_rot * (tab.dh / 2);
+  if (n == 0) return hipSuccess;
+  if (dt == kF32)
+    hipLaunchKernelGGL(rope_inplace_kernel<float>, dim3(blocks_for(n)), dim3(kGT), 0, s,
+                       static_cast<float *>(qk), stride, static_cast<int>(B),
+                       static_cast<int>(n_rot), tab);
+  else
+    hipLaunchKernelGGL(rope_inplace_kernel<uint16_t>, dim3(blocks_for(n)), dim3(kGT), 0, s,
+                       static_cast<uint16_t *>(qk), stride, static_cast<int>(B),
+                       static_cast<int>(n_rot), tab);
+  return hipGetLastError();
+}
+
+RopeTable rope_table(int64_t dh, double pos, double theta) {
+  RopeTable t;
+  t.dh = static_cast<int>(dh);
+  for (int i = 0; i < kRopeMaxHalf; ++i) {
+    const double ang = i < dh / 2 ? pos * std::pow(theta, -2.0 * i / static_cast<double>(dh)) : 0.0;
+    t.cs[i] = static_cast<float>(std::cos(ang));
+    t.sn[i] = static_cast<float>(std::sin(ang));
+  }
+  return t;
 }
 
 size_t decode_attention_ws_bytes(int64_t B, int64_t Tlen, int64_t n_heads) {

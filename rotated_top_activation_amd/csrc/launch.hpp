@@ -138,6 +138,26 @@ struct ChainArgs {
 inline size_t chain_flag_bytes(int64_t f) { return (static_cast<size_t>(f / 256 + 1) * 4 + 7) / 8 * 8 + 24; }
 inline size_t chain_ctl_offset(int64_t f) { return chain_flag_bytes(f) - 24; }
 bool chain_supported(int64_t q_block, int64_t f);
+// The rotary embedding's per-pair cosine and sine at one position, for
+// heads of dh <= 2·kRopeMaxHalf channels: angle pos·theta^(-2i/dh) in fp64
+// on the host, its cosine and sine rounded to fp32. Every RoPE kernel takes
+// the same table (by value), so they agree bit for bit.
+constexpr int kRopeMaxHalf = 128;
+struct RopeTable {
+  int dh = 0;
+  float cs[kRopeMaxHalf];
+  float sn[kRopeMaxHalf];
+};
+RopeTable rope_table(int64_t dh, double pos, double theta);  // host
+// RoPE folded into a one-token product's epilogue (the q|k|v linear of a
+// decoder layer): output columns below rot_cols are heads of tab.dh channels
+// (dividing the 512-column tile) rotated with the table, pairing channel i
+// with i + dh/2 (the split-half form of larosa_rope); the rest (v) are
+// stored as they are.
+struct RopeArgs {
+  int rot_cols = 0;  // 0: no RoPE
+  RopeTable tab;
+};
 struct SelectGatherArgs {
   const float *x_rot;  // [d_in] fp32
   int d_in, k;
@@ -158,6 +178,7 @@ struct SelectGatherArgs {
   uint32_t thr_key = 0;
   int32_t *count_out = nullptr;
   ChainArgs chain;
+  RopeArgs rope;
 };
 hipError_t launch_select_gather(const SelectGatherArgs &a, hipStream_t s);
 
@@ -262,8 +283,11 @@ hipError_t launch_interleave(const void *w, void *out, int64_t d_in, int64_t f, 
 hipError_t launch_rmsnorm(const void *h, void *out, int64_t B, int64_t d, float eps, int dt,
                           hipStream_t s);
 hipError_t launch_rope(const void *qk, int64_t stride, void *q_out, void *k_out, int64_t B,
-                       int64_t n_heads, int64_t n_kv, int64_t dh, int64_t pos, double theta,
-                       int dt, hipStream_t s);
+                       int64_t n_heads, int64_t n_kv, const RopeTable &tab, int dt,
+                       hipStream_t s);
+// RoPE in place on the first n_rot heads of each row (row b at qk + b·stride).
+hipError_t launch_rope_inplace(void *qk, int64_t stride, int64_t B, int64_t n_rot,
+                               const RopeTable &tab, int dt, hipStream_t s);
 // ws: decode_attention_ws_bytes (per-chunk partial results)
 size_t decode_attention_ws_bytes(int64_t B, int64_t Tlen, int64_t n_heads);
 hipError_t launch_decode_attention(const void *q, const void *k_new, int64_t k_stride,

@@ -56,6 +56,8 @@
 #include "launch.hpp"
 #include "select_core.hpp"
 
+#include <type_traits>
+
 namespace larosa {
 namespace {
 
@@ -70,13 +72,27 @@ size_t sg_counter_bytes(int tiles) { return (static_cast<size_t>(tiles) * 4 + 25
 
 constexpr int kChainChunks = 8;  // 16-byte chunks per lane of a Q2 row: q_block <= 4096
 
-template <typename WT, typename OT, int EMAX, bool SWIGLU, bool THR, bool CHAIN>
+// Epilogue forms of the product.
+constexpr int kEpiPlain = 0;  // y stored as summed (or SwiGLU, with SWIGLU)
+constexpr int kEpiChain = 1;  // the SwiGLU product chained into the next rotation
+constexpr int kEpiRope = 2;   // RoPE on the q and k heads of a q|k|v product
+
+// The RoPE table travels only with the RoPE form (a 1 KB kernel argument).
+struct NoRope {};
+template <int EPI>
+using RopeParam = std::conditional_t<EPI == kEpiRope, RopeArgs, NoRope>;
+
+template <typename WT, typename OT, int EMAX, bool SWIGLU, bool THR, int EPI>
 __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
     const float *__restrict__ x_rot, int d, int k, uint32_t thr_key, int E, int tiles,
     int splits, int cps, const WT *__restrict__ w, int64_t d_out, OT *__restrict__ y,
     float *__restrict__ partials, uint32_t *__restrict__ counters,
-    int32_t *__restrict__ idx_out, int32_t *__restrict__ count_out, ChainArgs chain) {
+    int32_t *__restrict__ idx_out, int32_t *__restrict__ count_out, ChainArgs chain,
+    RopeParam<EPI> rope) {
+  constexpr bool CHAIN = EPI == kEpiChain;
+  constexpr bool ROPE = EPI == kEpiRope;
   static_assert(!CHAIN || (SWIGLU && !THR), "the chain follows the SwiGLU product");
+  static_assert(!ROPE || (!SWIGLU && !THR), "RoPE follows a plain product");
   constexpr int V = Elt<WT>::kVec;
   constexpr int TILE = kWave * V;
   constexpr int R = kSgRows;  // loads in flight per lane, list positions per group
@@ -99,7 +115,7 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
   float(*red)[TILE] = reinterpret_cast<float(*)[TILE]>(kv);
   __shared__ uint32_t s_carry;
   __shared__ int s_last;
-  __shared__ float ep[SWIGLU ? TILE : 1];  // the tile's sums, for the SwiGLU epilogue
+  __shared__ float ep[SWIGLU || ROPE ? TILE : 1];  // the tile's sums, for the epilogue
 
   const int t = threadIdx.x;
   const int lane = t % kWave;
@@ -305,10 +321,32 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
   // pairs gate column e with up column e + TILE/2 of the tile (rounded to
   // the output type first, as a separate SwiGLU step would see them).
   auto finish = [&](int e, float v) {
-    if (SWIGLU) ep[e] = v;
+    if (SWIGLU || ROPE) ep[e] = v;
     else Elt<OT>::store(y, tile_col0 + e, v);
   };
   auto epilogue = [&]() {
+    if constexpr (ROPE) {
+      // The tile holds whole heads (dh divides TILE). Each sum is rounded to
+      // the output type first, as a separate RoPE step would read it; the
+      // table and the arithmetic are larosa_rope's.
+      __syncthreads();
+      const int dh = rope.tab.dh, half = dh / 2;
+      for (int e = t; e < TILE; e += kSgThreads) {
+        const int64_t col = tile_col0 + e;
+        if (col >= d_out) continue;
+        if (col >= rope.rot_cols) {
+          Elt<OT>::store(y, col, Elt<OT>::round(ep[e]));
+          continue;
+        }
+        const int j = static_cast<int>(col % dh);
+        const int i = j % half;
+        const int h0 = e - j;  // the head's first column in the tile
+        const float a = Elt<OT>::round(ep[h0 + i]), bb = Elt<OT>::round(ep[h0 + i + half]);
+        const float cs = rope.tab.cs[i], sn = rope.tab.sn[i];
+        Elt<OT>::store(y, col, j < half ? rope_lo(a, bb, cs, sn) : rope_hi(a, bb, cs, sn));
+      }
+      return;
+    }
     if (!SWIGLU) return;
     __syncthreads();
     if constexpr (CHAIN) {
@@ -515,33 +553,39 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
     __hip_atomic_store(chain.status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <typename WT, typename OT, int EM, bool SW, bool TH, bool CH>
+template <typename WT, typename OT, int EM, bool SW, bool TH, int EPI>
 void launch_sg_k(const SelectGatherArgs &a, const SelectGatherPlan &p, int E, hipStream_t s) {
   uint32_t *counters = static_cast<uint32_t *>(a.ws);
   float *partials =
       reinterpret_cast<float *>(static_cast<char *>(a.ws) + sg_counter_bytes(p.tiles));
   const dim3 grid(static_cast<unsigned>(p.tiles * p.splits)), block(kSgThreads);
   const ChainArgs &chain = a.chain;
-  hipLaunchKernelGGL((select_gather_kernel<WT, OT, EM, SW, TH, CH>), grid, block, 0, s, a.x_rot,
+  RopeParam<EPI> rope{};
+  if constexpr (EPI == kEpiRope) rope = a.rope;
+  hipLaunchKernelGGL((select_gather_kernel<WT, OT, EM, SW, TH, EPI>), grid, block, 0, s, a.x_rot,
                      a.d_in, a.k, a.thr_key, E, p.tiles, p.splits, p.cps,
                      static_cast<const WT *>(a.w), a.d_out, static_cast<OT *>(a.y), partials,
-                     counters, a.idx_out, a.count_out, chain);
+                     counters, a.idx_out, a.count_out, chain, rope);
 }
 
 template <typename WT, typename OT, int EM>
 void launch_sg_em(const SelectGatherArgs &a, const SelectGatherPlan &p, int E, hipStream_t s) {
   if (a.by_threshold) {
-    if (a.swiglu) launch_sg_k<WT, OT, EM, true, true, false>(a, p, E, s);
-    else launch_sg_k<WT, OT, EM, false, true, false>(a, p, E, s);
+    if (a.swiglu) launch_sg_k<WT, OT, EM, true, true, kEpiPlain>(a, p, E, s);
+    else launch_sg_k<WT, OT, EM, false, true, kEpiPlain>(a, p, E, s);
   } else {
     if constexpr (sizeof(WT) == 2 && sizeof(OT) == 2) {
       if (a.chain.qt != nullptr) {
-        launch_sg_k<WT, OT, EM, true, false, true>(a, p, E, s);
+        launch_sg_k<WT, OT, EM, true, false, kEpiChain>(a, p, E, s);
+        return;
+      }
+      if (a.rope.rot_cols > 0) {
+        launch_sg_k<WT, OT, EM, false, false, kEpiRope>(a, p, E, s);
         return;
       }
     }
-    if (a.swiglu) launch_sg_k<WT, OT, EM, true, false, false>(a, p, E, s);
-    else launch_sg_k<WT, OT, EM, false, false, false>(a, p, E, s);
+    if (a.swiglu) launch_sg_k<WT, OT, EM, true, false, kEpiPlain>(a, p, E, s);
+    else launch_sg_k<WT, OT, EM, false, false, kEpiPlain>(a, p, E, s);
   }
 }
 
@@ -592,6 +636,12 @@ hipError_t launch_select_gather(const SelectGatherArgs &a, hipStream_t s) {
       (!a.swiglu || a.by_threshold || a.w_dt != kBF16 || a.y_dt != kBF16 ||
        !chain_supported(a.chain.qb, a.chain.f) || a.d_out != 2 * a.chain.f ||
        a.chain.tile_flag == nullptr || a.chain.ctl == nullptr || a.chain.x_rot == nullptr))
+    return hipErrorInvalidValue;
+  if (a.rope.rot_cols > 0 &&
+      (a.swiglu || a.by_threshold || a.chain.qt != nullptr || a.w_dt != kBF16 ||
+       a.y_dt != kBF16 || a.rope.tab.dh < 2 || a.rope.tab.dh % 2 ||
+       a.rope.tab.dh > 2 * kRopeMaxHalf || (kWave * 8) % a.rope.tab.dh ||
+       a.rope.rot_cols % a.rope.tab.dh || a.rope.rot_cols > a.d_out))
     return hipErrorInvalidValue;
   if (a.w_dt == kBF16 && a.y_dt == kBF16) return launch_sg_t<uint16_t, uint16_t>(a, p, s);
   if (a.w_dt == kBF16 && a.y_dt == kF32) return launch_sg_t<uint16_t, float>(a, p, s);

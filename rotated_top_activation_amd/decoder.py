@@ -106,13 +106,31 @@ def layer_forward(layer: DecoderLayer, h, buf: DecoderBuffers, mode: int = _lib.
 
     if not normed:
         _lib.larosa_rmsnorm(h, buf.a, B, s.d)
-    lin("attn_in", buf.a, buf.qkv)
-    _lib.larosa_rope(buf.qkv, s.qkv_out, buf.q, buf.k, B, s.n_heads, s.n_kv_heads, s.d_head,
-                     s.ctx)
-    v_new = buf.qkv[:, (s.n_heads + s.n_kv_heads) * s.d_head:]
-    _lib.larosa_decode_attention(buf.q, buf.k, s.n_kv_heads * s.d_head, v_new, s.qkv_out,
-                                 layer.k_cache, layer.v_cache, buf.att, B, s.ctx, s.n_heads,
-                                 s.n_kv_heads, s.d_head, ws=buf.att_ws)
+    Hd, Kd = s.n_heads * s.d_head, s.n_kv_heads * s.d_head
+    if B == 1:
+        # one token: q and k are rotated in place inside qkv, in the q|k|v
+        # product's epilogue (no RoPE launch); attention reads them there
+        L = layer.lin["attn_in"]
+        xr = idx = None
+        if trace is not None:
+            xr = torch.empty((B, L.d_in), dtype=torch.float32, device=h.device)
+            idx = torch.empty((B, L.k), dtype=torch.int32, device=h.device)
+            trace["attn_in"] = (xr, idx)
+            trace["rope_in_qkv"] = True
+        _lib.larosa_qkv_rope_layer_forward(buf.a, L.Qt, L.q_block, L.Wf, B, L.d_in, L.k,
+                                           s.n_heads, s.n_kv_heads, s.d_head, s.ctx, buf.qkv,
+                                           idx_out=idx, xrot_out=xr, mode=mode,
+                                           ws=ws["attn_in"])
+        q, k, k_stride = buf.qkv[:, :Hd], buf.qkv[:, Hd:Hd + Kd], s.qkv_out
+    else:
+        lin("attn_in", buf.a, buf.qkv)
+        _lib.larosa_rope(buf.qkv, s.qkv_out, buf.q, buf.k, B, s.n_heads, s.n_kv_heads,
+                         s.d_head, s.ctx)
+        q, k, k_stride = buf.q, buf.k, Kd
+    v_new = buf.qkv[:, Hd + Kd:]
+    _lib.larosa_decode_attention(q, k, k_stride, v_new, s.qkv_out, layer.k_cache,
+                                 layer.v_cache, buf.att, B, s.ctx, s.n_heads, s.n_kv_heads,
+                                 s.d_head, ws=buf.att_ws)
     lin("o_in", buf.att, buf.o)
     _lib.larosa_residual_rmsnorm(h, buf.o, buf.m, B, s.d)  # h += o; m = RMSNorm(h)
     lin("mlp_in", buf.m, buf.hh)

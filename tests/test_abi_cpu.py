@@ -111,6 +111,30 @@ def test_layer_forward_validation(lib):
     assert _lf(lib, B=0) == OK                   # empty batch: nothing to do
 
 
+def _qkv(lib, x=P, H=2, Hkv=1, dh=16, pos=5, theta=10000.0, B=1, k=32, ws=P, wsb=1 << 30,
+         mode=0):
+    # d_in 128, d_out (H + 2·Hkv)·dh
+    return lib.larosa_qkv_rope_layer_forward(x, 1, P, 64, P, 1, B, 128, k, H, Hkv, dh, pos,
+                                             ctypes.c_float(theta), P, None, None, mode, ws,
+                                             wsb, None)
+
+
+def test_qkv_rope_layer_validation(lib):
+    assert _qkv(lib, H=0) == INVALID
+    assert _qkv(lib, Hkv=0) == INVALID
+    assert _qkv(lib, pos=-1) == INVALID
+    assert _qkv(lib, theta=0.0) == INVALID
+    assert _qkv(lib, theta=float("nan")) == INVALID
+    assert _qkv(lib, dh=15) == SHAPE
+    assert _qkv(lib, dh=0) == SHAPE
+    assert _qkv(lib, dh=258) == SHAPE           # above 256
+    assert _qkv(lib, k=0) == INVALID            # the layer's own checks follow
+    assert _qkv(lib, x=PM) == ALIGN
+    assert _qkv(lib, ws=None) == WS
+    assert _qkv(lib, mode=9) == INVALID
+    assert _qkv(lib, B=0) == OK
+
+
 def test_standalone_calls_validation(lib):
     assert lib.larosa_rotate(P, 1, P, 48, 1, P, 1, 128, None) == SHAPE
     assert lib.larosa_rotate(P, 9, P, 64, 1, P, 1, 128, None) == DTYPE

@@ -19,6 +19,7 @@ from oracle import larosa_ref as ref
 from rotated_top_activation_amd import _lib
 from rotated_top_activation_amd import decoder as D
 from rotated_top_activation_amd import workloads as wl
+from rotated_top_activation_amd.device import RotatedLinear
 
 from gpu_helpers import dev, host, host_f32, ulp_bf16
 from test_gpu_parity import rotation_bound
@@ -64,6 +65,44 @@ def test_rope(B, H, Hkv):
     want_k = dec.rope(qkv[:, H * dh:(H + Hkv) * dh], Hkv, dh, 2048)
     assert close_bf16(host(q), want_q, extra=1e-6)
     assert close_bf16(host(k), want_k, extra=1e-6)
+
+
+@pytest.mark.parametrize("B,H,Hkv,mode,pos", [
+    (1, 8, 8, _lib.UNFUSED, 2048), (1, 16, 4, _lib.UNFUSED, 777), (1, 8, 8, _lib.UNFUSED, 0),
+    (4, 8, 8, _lib.UNFUSED, 2048), (1, 8, 8, _lib.FUSED, 2048),
+    (1, 8, 2, _lib.UNFUSED | _lib.ROTATE_FP64, 5)])
+def test_qkv_rope_layer_equals_layer_then_rope(B, H, Hkv, mode, pos):
+    """larosa_qkv_rope_layer_forward: RoPE folded into the one-token
+    product's epilogue (or applied in place after the other paths) gives the
+    bits of larosa_layer_forward followed by larosa_rope."""
+    d, dh = 1024, 128
+    d_out = (H + 2 * Hkv) * dh
+    k = wl.k_for(d, 40)
+    rng = np.random.default_rng(H * 31 + Hkv + pos)
+    q = wl.quantize(wl.rotation_fp64(4, 1, "attn_in", d, 512), "bf16")
+    w = wl.quantize(rng.standard_normal((d, d_out)) * 0.02, "bf16")
+    x = wl.quantize(rng.standard_normal((B, d)), "bf16")
+    lin = RotatedLinear(q, w, "bf16", k, keep_w=False)
+    x_d = dev(x, "bf16")
+    y1 = torch.empty((B, d_out), dtype=torch.bfloat16, device="cuda")
+    idx1 = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    _lib.larosa_qkv_rope_layer_forward(x_d, lin.Qt, lin.q_block, lin.Wf, B, d, k, H, Hkv, dh,
+                                       pos, y1, idx_out=idx1, mode=mode,
+                                       ws=lin.workspace(B, mode))
+    y2 = torch.empty_like(y1)
+    idx2 = torch.empty_like(idx1)
+    lin.forward(x_d, y2, lin.workspace(B, mode), idx_out=idx2, mode=mode)
+    qo = torch.empty((B, H * dh), dtype=torch.bfloat16, device="cuda")
+    ko = torch.empty((B, Hkv * dh), dtype=torch.bfloat16, device="cuda")
+    _lib.larosa_rope(y2, d_out, qo, ko, B, H, Hkv, dh, pos)
+    torch.cuda.synchronize()
+    Hd, Kd = H * dh, Hkv * dh
+    assert torch.equal(idx1, idx2)
+    assert torch.equal(y1[:, :Hd], qo)
+    assert torch.equal(y1[:, Hd:Hd + Kd], ko)
+    assert torch.equal(y1[:, Hd + Kd:], y2[:, Hd + Kd:])
+    if pos == 0:  # angle 0: the plain product
+        assert torch.equal(y1, y2)
 
 
 @pytest.mark.parametrize("B,H,Hkv,T", [(1, 32, 32, 2048), (4, 32, 32, 2048), (2, 64, 8, 300),
@@ -133,6 +172,29 @@ def _check_linear(x_in, q_blocks, xr_gpu, idx_gpu, y_gpu, wf_dev, k, cols):
     assert ref.rel_error(y_gpu[:, cols], want) <= TOL
 
 
+def _check_qkv_rope_linear(x_in, q_blocks, xr_gpu, idx_gpu, qkv_gpu, wf_dev, k, shape, rng):
+    """The q|k|v linear with RoPE folded in (one token): 6 sampled q and k
+    heads against the oracle's RoPE of the product over the GPU's kept rows,
+    and 256 sampled v columns against the product, teacher-forced."""
+    bound, exact = rotation_bound(x_in, q_blocks)
+    assert np.all(np.abs(xr_gpu.astype(np.float64) - exact) <= bound), "rotation bound"
+    want_idx = ref.select(xr_gpu, k)
+    np.testing.assert_array_equal(idx_gpu, want_idx)
+    dh = shape.d_head
+    n_rot = shape.n_heads + shape.n_kv_heads
+    heads = np.sort(rng.choice(n_rot, size=6, replace=False))
+    cols = np.concatenate([np.arange(hd * dh, (hd + 1) * dh) for hd in heads])
+    wf_cols = host(wf_dev[:, torch.from_numpy(cols).cuda()])
+    prod = ref.round_to(ref.gather_product(xr_gpu, want_idx, wf_cols), "bf16")
+    want = dec.rope(prod, len(heads), dh, shape.ctx)
+    assert ref.rel_error(qkv_gpu[:, cols], want) <= TOL, "q|k heads with RoPE"
+    v0 = n_rot * dh
+    vcols = np.sort(rng.choice(np.arange(v0, shape.qkv_out), size=256, replace=False))
+    wf_v = host(wf_dev[:, torch.from_numpy(vcols).cuda()])
+    want_v = ref.round_to(ref.gather_product(xr_gpu, want_idx, wf_v), "bf16")
+    assert ref.rel_error(qkv_gpu[:, vcols], want_v) <= TOL, "v columns"
+
+
 def _check_swiglu_linear(x_in, q_blocks, xr_gpu, idx_gpu, h_gpu, wf_dev, k, f, cols):
     """The gate|up linear with SiLU(gate)·up folded in: h on gate columns
     `cols` (each paired with up column f + c) against the oracle's SwiGLU of
@@ -188,7 +250,13 @@ def run_decoder(B, sparsity, n_layers, mode, n_checked=None, seed_cols=0, check_
         checked += 1
         qkv, att, o, m, hh, dn = (host(t) for t in (buf.qkv, buf.att, buf.o, buf.m, buf.hh,
                                                      buf.dn))
-        q, k = host(buf.q), host(buf.k)
+        Hd = shape.n_heads * shape.d_head
+        Kd = shape.n_kv_heads * shape.d_head
+        rope_in_qkv = trace.get("rope_in_qkv", False)
+        if rope_in_qkv:  # q and k rotated in place inside qkv
+            q, k = qkv[:, :Hd], qkv[:, Hd:Hd + Kd]
+        else:
+            q, k = host(buf.q), host(buf.k)
         h_out = host(h)
         assert close_bf16(a, dec.rmsnorm(h_in), extra=1e-6), f"layer {l} rmsnorm"
         lin_in = {"attn_in": a, "o_in": att, "mlp_in": m, "down_in": hh}
@@ -203,15 +271,18 @@ def run_decoder(B, sparsity, n_layers, mode, n_checked=None, seed_cols=0, check_
                 _check_swiglu_linear(m, q_host, host_f32(xr), host(idx), hh, L.Wf, L.k,
                                      shape.f, cols)
                 continue
+            if role == "attn_in" and rope_in_qkv:
+                _check_qkv_rope_linear(a, q_host, host_f32(xr), host(idx), qkv, L.Wf, L.k,
+                                       shape, rng)
+                continue
             cols = np.sort(rng.choice(L.d_out, size=min(256, L.d_out), replace=False))
             _check_linear(lin_in[role], q_host, host_f32(xr), host(idx), lin_out[role], L.Wf,
                           L.k, cols)
-        Hd = shape.n_heads * shape.d_head
-        Kd = shape.n_kv_heads * shape.d_head
-        assert close_bf16(q, dec.rope(qkv[:, :Hd], shape.n_heads, shape.d_head, shape.ctx),
-                          extra=1e-6), f"layer {l} rope q"
-        assert close_bf16(k, dec.rope(qkv[:, Hd:Hd + Kd], shape.n_kv_heads, shape.d_head,
-                                      shape.ctx), extra=1e-6), f"layer {l} rope k"
+        if not rope_in_qkv:
+            assert close_bf16(q, dec.rope(qkv[:, :Hd], shape.n_heads, shape.d_head, shape.ctx),
+                              extra=1e-6), f"layer {l} rope q"
+            assert close_bf16(k, dec.rope(qkv[:, Hd:Hd + Kd], shape.n_kv_heads, shape.d_head,
+                                          shape.ctx), extra=1e-6), f"layer {l} rope k"
         kc = np.stack([np.roll(kb, int(o_), axis=1) for o_ in offs])
         vc = np.stack([np.roll(vb, int(o_), axis=1) for o_ in offs])
         want_att = dec.decode_attention(q, k, qkv[:, Hd + Kd:], kc, vc, shape.n_heads,
