@@ -201,8 +201,11 @@ int larosa_rotate_fp64(const void *x, int x_dtype, const void *Qt,
  *   union_coef  [d, B] fp32: union_coef[j·B + b] = xs[b, union_idx[j]]
  * When the union is asked for, xs is required, and ws must hold at least
  * larosa_workspace_bytes(B, d, d_out, k, mode) bytes for some valid d_out and
- * mode (a status word and the tokens' bit masks come first in every
- * layout); without the union ws may be NULL. */
+ * mode (a status area and the tokens' bit masks come first in every
+ * layout), zero-filled once before first use like any layer workspace: the
+ * union list is taken by the selection launch itself (its last workgroup to
+ * finish), through an arrival counter in the status area that each call
+ * leaves at zero. Without the union ws may be NULL. */
 int larosa_topk_select(const float *x_rot, int64_t B, int64_t d, int64_t k,
                        int32_t *idx, float *val, float *xs, int32_t *union_idx,
                        int32_t *union_count, float *union_coef, void *ws,

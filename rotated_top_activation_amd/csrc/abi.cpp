@@ -71,8 +71,16 @@ struct Prefix {
 
 // The first 256 bytes of every layer-call workspace: word 0 holds the
 // device-side status (LAROSA_ERR_TIMEOUT from a bounded wait that gave up),
-// word 1 the LAROSA_VALIDATE check's flag.
+// word 1 the LAROSA_VALIDATE check's flag, word 2 the selection launch's
+// arrival counter for the row union (zero between calls).
 constexpr size_t kStatusBytes = 256;
+UnionTail union_tail(char *status_area, int32_t *u_idx, int32_t *u_count) {
+  UnionTail ut;
+  ut.counter = reinterpret_cast<uint32_t *>(status_area) + 2;
+  ut.u_idx = u_idx;
+  ut.u_count = u_count;
+  return ut;
+}
 static_assert(kStatusTimeout == LAROSA_ERR_TIMEOUT, "device status code");
 
 bool mfma_region(int64_t B, int w_dt) { return w_dt == LAROSA_BF16 && B >= kMfmaMinB && B <= kMaxB; }
@@ -370,16 +378,23 @@ int layer_entry(const void *x, int act_dtype, const void *Qt, int64_t q_block,
     int32_t *u_idx = reinterpret_cast<int32_t *>(base + L.u_idx);
     int32_t *u_cnt = reinterpret_cast<int32_t *>(base + L.u_cnt);
     float *u_coef = reinterpret_cast<float *>(base + L.u_coef);
-    e = sel.thr ? launch_threshold_select(x_rot, static_cast<int>(B), static_cast<int>(d_in),
-                                          sel.thr_key, idx, sel.count_out, val, xs, mask, s)
-                // the union and the product read xs and the masks only: the
-                // index list is written when asked for, the values not at all
-                : launch_select(x_rot, static_cast<int>(B), static_cast<int>(d_in),
-                                static_cast<int>(k), idx_out, nullptr, xs, mask, s, parts,
-                                n_parts);
-    if (e == hipSuccess)
-      e = launch_union(mask, xs, static_cast<int>(B), static_cast<int>(d_in), u_idx, u_cnt,
-                       mf ? nullptr : u_coef, s);
+    if (sel.thr) {
+      e = launch_threshold_select(x_rot, static_cast<int>(B), static_cast<int>(d_in),
+                                  sel.thr_key, idx, sel.count_out, val, xs, mask, s);
+      if (e == hipSuccess)
+        e = launch_union(mask, xs, static_cast<int>(B), static_cast<int>(d_in), u_idx, u_cnt,
+                         mf ? nullptr : u_coef, s);
+    } else {
+      // the union and the product read xs and the masks only: the index
+      // list is written when asked for, the values not at all; the union
+      // list is taken by the selection launch itself
+      e = launch_select(x_rot, static_cast<int>(B), static_cast<int>(d_in), static_cast<int>(k),
+                        idx_out, nullptr, xs, mask, s, parts, n_parts,
+                        union_tail(base + L.p.status, u_idx, u_cnt));
+      if (e == hipSuccess && !mf)
+        e = launch_union_coef(u_idx, u_cnt, xs, static_cast<int>(B), static_cast<int>(d_in),
+                              u_coef, s);
+    }
     if (e != hipSuccess) return LAROSA_ERR_LAUNCH;
     const int64_t bk = B * k;  // the threshold form's k is d_in
     const int64_t max_rows = bk < d_in ? bk : d_in;
@@ -651,11 +666,17 @@ int larosa_topk_select(const float *x_rot, int64_t B, int64_t d, int64_t k, int3
   if (int st = device_status()) return st;
   hipStream_t s = stream_of(stream);
   // x_rot is only read (no partial sums are passed)
+  const bool tail = want_union && B > 1;  // the union list taken by the selection launch
   hipError_t e = launch_select(const_cast<float *>(x_rot), static_cast<int>(B),
-                               static_cast<int>(d), static_cast<int>(k), idx, val, xs, mask, s);
+                               static_cast<int>(d), static_cast<int>(k), idx, val, xs, mask, s,
+                               nullptr, 1,
+                               tail ? union_tail(static_cast<char *>(ws), union_idx, union_count)
+                                    : UnionTail{});
   if (e == hipSuccess && want_union)
-    e = launch_union(mask, xs, static_cast<int>(B), static_cast<int>(d), union_idx,
-                     union_count, union_coef, s);
+    e = tail ? launch_union_coef(union_idx, union_count, xs, static_cast<int>(B),
+                                 static_cast<int>(d), union_coef, s)
+             : launch_union(mask, xs, static_cast<int>(B), static_cast<int>(d), union_idx,
+                            union_count, union_coef, s);
   return launched(e);
   });
 }
@@ -766,15 +787,19 @@ int larosa_lowrank_layer_forward(const void *x, int act_dtype, const void *Qt, i
     // and the index list is written only when asked for. Coefficients come
     // from xs, so the values are not written.
     e = launch_select(x_rot, Bi, di, static_cast<int>(k), B == 1 ? idx : idx_out, nullptr, xs,
-                      mask, s, parts, n_parts);
-  // the base row list: the token's kept rows, or the batch's union
+                      mask, s, parts, n_parts,
+                      B > 1 ? union_tail(base + L.l.p.status,
+                                         reinterpret_cast<int32_t *>(base + L.l.u_idx),
+                                         reinterpret_cast<int32_t *>(base + L.l.u_cnt))
+                            : UnionTail{});
+  // the base row list: the token's kept rows, or the batch's union (taken by
+  // the selection launch)
   const int32_t *list = idx;
   const int32_t *n_dev = nullptr;
   int64_t max_rows = k;
   if (e == hipSuccess && B > 1) {
     int32_t *u_idx = reinterpret_cast<int32_t *>(base + L.l.u_idx);
     int32_t *u_cnt = reinterpret_cast<int32_t *>(base + L.l.u_cnt);
-    e = launch_union(mask, xs, Bi, di, u_idx, u_cnt, nullptr, s);
     list = u_idx;
     n_dev = u_cnt;
     max_rows = B * k < d_in ? B * k : d_in;

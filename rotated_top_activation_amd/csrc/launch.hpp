@@ -59,15 +59,26 @@ hipError_t launch_rotate_f64(const void *x, int x_dt, const void *qt, int q_dt, 
 // rotation (slice p at parts + p·B·d, added in order p = 0, 1, ...) and is
 // written here; select_takes_parts says whether this d allows n_parts.
 bool select_takes_parts(int d, int n_parts);
+// With counter != NULL (B > 1, masks written) the launch also takes the row
+// union: the last workgroup to arrive writes u_idx and *u_count and resets
+// the counter (a word that is zero before the call and after it).
+struct UnionTail {
+  uint32_t *counter = nullptr;
+  int32_t *u_idx = nullptr;
+  int32_t *u_count = nullptr;
+};
 hipError_t launch_select(float *x_rot, int B, int d, int k, int32_t *idx, float *val, float *xs,
                          uint32_t *mask, hipStream_t s, const float *parts = nullptr,
-                         int n_parts = 1);
+                         int n_parts = 1, const UnionTail &ut = UnionTail{});
 
 // --- row union of B > 1 selections (from the per-token bit masks); with
 // u_coef == NULL only the list and its count are written ---
 hipError_t launch_union(const uint32_t *mask, const float *xs, int B, int d,
                         int32_t *u_idx, int32_t *u_count, float *u_coef,
                         hipStream_t s);
+// the coefficients alone, for a list taken by the selection launch
+hipError_t launch_union_coef(const int32_t *u_idx, const int32_t *u_count, const float *xs, int B,
+                             int d, float *u_coef, hipStream_t s);
 
 inline int mask_words(int d) { return (d + 31) / 32; }
 

@@ -13,9 +13,14 @@
 // ascending without a sort.
 //
 // Row union for B > 1: each token also writes a d-bit mask of its kept
-// channels; a single workgroup ORs the B masks word by word and compacts the
-// set bits in index order, and a grid kernel gathers each token's
-// coefficient for every union row.
+// channels; one workgroup ORs the B masks word by word and compacts the set
+// bits in index order, and a grid kernel gathers each token's coefficient
+// for every union row. In the layer calls the union list is taken by the
+// selection launch itself: every token's workgroup writes its mask with
+// write-through (agent-scope) stores, waits for them to complete and takes
+// an arrival counter; the last to arrive ORs the masks (agent-scope loads,
+// which read the device-coherent point) and writes the list, then resets the
+// counter. That saves the union launch.
 #include "common.hpp"
 #include "launch.hpp"
 #include "select_core.hpp"
@@ -78,13 +83,69 @@ __device__ __forceinline__ void load_keys_parts(const float *part_row, int64_t p
   }
 }
 
+// OR of word t over the B tokens' masks, C words in flight per round trip.
+// Positions past B repeat the last token's word (OR is idempotent), so the
+// loads are unconditional and a batch of up to C tokens takes one round trip.
+// With COHERENT the loads are agent-scope (the device-coherent point), for
+// masks written by other workgroups of the same launch.
+template <int C, bool COHERENT = false>
+__device__ __forceinline__ uint32_t or_words(const uint32_t *__restrict__ mask, int B, int nw,
+                                             int t) {
+  uint32_t word = 0u;
+  for (int b = 0; b < B; b += C) {
+    uint32_t w[C];
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+      const uint32_t *p = mask + static_cast<int64_t>(b + i < B ? b + i : B - 1) * nw + t;
+      if constexpr (COHERENT)
+        w[i] = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        w[i] = *p;
+    }
+#pragma unroll
+    for (int i = 0; i < C; ++i) word |= w[i];
+  }
+  return word;
+}
+
+// The union list of the B masks by one workgroup of kThreads (one mask word
+// per thread, d <= 32768): the set bits in index order go to u_idx through
+// `stage` (at least d words of LDS), the count to *u_count.
+template <bool COHERENT>
+__device__ __forceinline__ void union_compact(const uint32_t *__restrict__ mask, int B, int d,
+                                              int32_t *__restrict__ u_idx,
+                                              int32_t *__restrict__ u_count, uint32_t *stage,
+                                              uint32_t *wave_tot) {
+  const int t = threadIdx.x;
+  const int nw = (d + 31) / 32;
+  uint32_t word = 0u;
+  if (t < nw)
+    word = B <= 16 ? or_words<16, COHERENT>(mask, B, nw, t) : or_words<32, COHERENT>(mask, B, nw, t);
+  const uint32_t c = __popc(word);
+  const uint32_t incl = block_incl_scan<kThreads>(c, wave_tot);
+  uint32_t pos = incl - c;
+  while (word) {
+    const int bit = __ffs(word) - 1;
+    stage[pos++] = static_cast<uint32_t>(t * 32 + bit);
+    word &= word - 1u;
+  }
+  // the total: the wave totals left by the scan
+  uint32_t total = 0;
+#pragma unroll
+  for (int i = 0; i < kThreads / kWave; ++i) total += wave_tot[i];
+  __syncthreads();
+  for (int j = t; j < static_cast<int>(total); j += kThreads)
+    u_idx[j] = static_cast<int32_t>(stage[j]);
+  if (t == kThreads - 1) *u_count = static_cast<int32_t>(incl);
+}
+
 // x_rot is either given (n_parts <= 1) or summed here from n_parts partial
 // sums (and written).
 template <int EMAX>
 __global__ __launch_bounds__(kThreads) void topk_select_kernel(
     float *__restrict__ x_rot, int d, int k, int E, int32_t *__restrict__ idx,
     float *__restrict__ val, float *__restrict__ xs, uint32_t *__restrict__ mask,
-    const float *__restrict__ parts, int n_parts) {
+    const float *__restrict__ parts, int n_parts, UnionTail ut) {
   __shared__ SelectSmem<kThreads> sm;
   __shared__ uint32_t bitmap[kThreads];  // up to 32768 channels
   __shared__ __align__(16) uint32_t stage[EMAX * kThreads];  // one output row
@@ -158,26 +219,28 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
   if (mask) {
     __syncthreads();
     const int nw = (d + 31) / 32;
-    if (t < nw) mask[static_cast<int64_t>(b) * nw + t] = bitmap[t];
+    if (t < nw) {
+      uint32_t *mp = mask + static_cast<int64_t>(b) * nw + t;
+      if (ut.counter)  // read by the last workgroup of this launch
+        __hip_atomic_store(mp, bitmap[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        *mp = bitmap[t];
+    }
   }
-}
-
-// OR of word t over the B tokens' masks, C words in flight per round trip.
-// Positions past B repeat the last token's word (OR is idempotent), so the
-// loads are unconditional and a batch of up to C tokens takes one round trip.
-template <int C>
-__device__ __forceinline__ uint32_t or_words(const uint32_t *__restrict__ mask, int B, int nw,
-                                             int t) {
-  uint32_t word = 0u;
-  for (int b = 0; b < B; b += C) {
-    uint32_t w[C];
-#pragma unroll
-    for (int i = 0; i < C; ++i)
-      w[i] = mask[static_cast<int64_t>(b + i < B ? b + i : B - 1) * nw + t];
-#pragma unroll
-    for (int i = 0; i < C; ++i) word |= w[i];
-  }
-  return word;
+  if (ut.counter == nullptr) return;
+  // The union list, by the last token to arrive: every mask store of this
+  // workgroup has completed before its arrival is counted.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  __shared__ int s_last;
+  if (t == 0)
+    s_last = __hip_atomic_fetch_add(ut.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             static_cast<uint32_t>(gridDim.x - 1);
+  __syncthreads();
+  if (!s_last) return;
+  union_compact<true>(mask, static_cast<int>(gridDim.x), d, ut.u_idx, ut.u_count, stage,
+                      sm.wave_tot);
+  if (t == 0) __hip_atomic_store(ut.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Union of the B masks: one workgroup, one mask word per thread (d <= 32768).
@@ -186,26 +249,7 @@ __global__ __launch_bounds__(kThreads) void union_list_kernel(
     int32_t *__restrict__ u_count) {
   __shared__ uint32_t wave_tot[kThreads / kWave];
   __shared__ uint32_t stage[32 * kThreads];  // the list, copied out coalesced
-  const int t = threadIdx.x;
-  const int nw = (d + 31) / 32;
-  uint32_t word = 0u;
-  if (t < nw) word = B <= 16 ? or_words<16>(mask, B, nw, t) : or_words<32>(mask, B, nw, t);
-  const uint32_t c = __popc(word);
-  const uint32_t incl = block_incl_scan<kThreads>(c, wave_tot);
-  uint32_t pos = incl - c;
-  while (word) {
-    const int bit = __ffs(word) - 1;
-    stage[pos++] = static_cast<uint32_t>(t * 32 + bit);
-    word &= word - 1u;
-  }
-  // the total: the wave totals left by the scan
-  uint32_t total = 0;
-#pragma unroll
-  for (int i = 0; i < kThreads / kWave; ++i) total += wave_tot[i];
-  __syncthreads();
-  for (int j = t; j < static_cast<int>(total); j += kThreads)
-    u_idx[j] = static_cast<int32_t>(stage[j]);
-  if (t == kThreads - 1) *u_count = static_cast<int32_t>(incl);
+  union_compact<false>(mask, B, d, u_idx, u_count, stage, wave_tot);
 }
 
 // coef[j·B + b] = xs[b, u_idx[j]] for j < |U|; rows past |U| get zeros
@@ -264,10 +308,10 @@ __global__ void coef_transpose_kernel(const float *__restrict__ coef, int B, int
 template <int EMAX>
 hipError_t launch_sel(float *x_rot, int B, int d, int k, int E, int32_t *idx, float *val,
                       float *xs, uint32_t *mask, const float *parts, int n_parts,
-                      hipStream_t s) {
+                      const UnionTail &ut, hipStream_t s) {
   if (n_parts > kMaxPartLoads / (EMAX / 4)) return hipErrorInvalidValue;
   hipLaunchKernelGGL((topk_select_kernel<EMAX>), dim3(B), dim3(kThreads), 0, s, x_rot,
-                     d, k, E, idx, val, xs, mask, parts, n_parts);
+                     d, k, E, idx, val, xs, mask, parts, n_parts, ut);
   return hipGetLastError();
 }
 
@@ -283,13 +327,17 @@ bool select_takes_parts(int d, int n_parts) {
 }
 
 hipError_t launch_select(float *x_rot, int B, int d, int k, int32_t *idx, float *val, float *xs,
-                         uint32_t *mask, hipStream_t s, const float *parts, int n_parts) {
+                         uint32_t *mask, hipStream_t s, const float *parts, int n_parts,
+                         const UnionTail &ut) {
   const int E = slots_per_thread(d, kThreads);
   if (n_parts <= 1) parts = nullptr;
-  if (E <= 4) return launch_sel<4>(x_rot, B, d, k, E, idx, val, xs, mask, parts, n_parts, s);
-  if (E <= 8) return launch_sel<8>(x_rot, B, d, k, E, idx, val, xs, mask, parts, n_parts, s);
-  if (E <= 16) return launch_sel<16>(x_rot, B, d, k, E, idx, val, xs, mask, parts, n_parts, s);
-  if (E <= 32) return launch_sel<32>(x_rot, B, d, k, E, idx, val, xs, mask, parts, n_parts, s);
+  if (ut.counter != nullptr && (B < 2 || mask == nullptr || ut.u_idx == nullptr ||
+                                ut.u_count == nullptr))
+    return hipErrorInvalidValue;
+  if (E <= 4) return launch_sel<4>(x_rot, B, d, k, E, idx, val, xs, mask, parts, n_parts, ut, s);
+  if (E <= 8) return launch_sel<8>(x_rot, B, d, k, E, idx, val, xs, mask, parts, n_parts, ut, s);
+  if (E <= 16) return launch_sel<16>(x_rot, B, d, k, E, idx, val, xs, mask, parts, n_parts, ut, s);
+  if (E <= 32) return launch_sel<32>(x_rot, B, d, k, E, idx, val, xs, mask, parts, n_parts, ut, s);
   return hipErrorInvalidValue;
 }
 
@@ -300,6 +348,13 @@ hipError_t launch_union(const uint32_t *mask, const float *xs, int B, int d,
                      u_idx, u_count);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !u_coef) return e;
+  hipLaunchKernelGGL(union_coef_kernel, dim3(static_cast<unsigned>((d + kUcRows - 1) / kUcRows)),
+                     dim3(kUcThreads), 0, s, u_idx, u_count, xs, B, d, u_coef);
+  return hipGetLastError();
+}
+
+hipError_t launch_union_coef(const int32_t *u_idx, const int32_t *u_count, const float *xs, int B,
+                             int d, float *u_coef, hipStream_t s) {
   hipLaunchKernelGGL(union_coef_kernel, dim3(static_cast<unsigned>((d + kUcRows - 1) / kUcRows)),
                      dim3(kUcThreads), 0, s, u_idx, u_count, xs, B, d, u_coef);
   return hipGetLastError();
