@@ -124,6 +124,75 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void rotate_row_kernel(
   if (lane == 0) x_rot[j] = sum;
 }
 
+// A few tokens (2 to 8 per group), x and Qt of one element type: one output
+// channel per wave, every 16-byte chunk of its Qt row requested at once (NC
+// per lane). The workgroup's 8 waves take 8 consecutive channels, which
+// share one Q block (q_block is a multiple of 8), so the group's x segments
+// of that block are staged once in LDS (NB·q_block elements) while the rows
+// are in flight; then each wave reads them from LDS. Qt is read once per group of NB tokens. A token's sum
+// runs in the order of the one-token kernel for rows of more than 32 chunks
+// (the same lane chunks, the same zero chunks past the row, the same wave
+// sum), so there its x_rot does not depend on the batch it came in.
+constexpr int kBatchWaves = 8;
+
+template <int NC, int NB, typename T>
+__global__ __launch_bounds__(kBatchWaves * kWave) void rotate_rows_batch_kernel(
+    const T *__restrict__ x, const T *__restrict__ qt, float *__restrict__ x_rot, int B, int d,
+    int qb) {
+  constexpr int V = Elt<T>::kVec;
+  extern __shared__ __align__(16) unsigned char rot_lds[];
+  T *xs = reinterpret_cast<T *>(rot_lds);  // [NB][qb]
+  const int t = threadIdx.x;
+  const int lane = t % kWave;
+  const int j0 = blockIdx.x * kBatchWaves;
+  const int j = j0 + wave_id();
+  const int b0 = blockIdx.y * NB;
+  const int64_t xoff = static_cast<int64_t>(j0 / qb) * qb;
+  const int chunks = qb / V;
+  uint4 q[NC];
+  {
+    const T *row = qt + static_cast<int64_t>(j < d ? j : d - 1) * qb;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c = lane + kWave * i;
+      q[i] = c < chunks ? load16(row + c * V) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  // the group's x segments (tokens past B: the last token's, never stored)
+  for (int e = t; e < NB * chunks; e += kBatchWaves * kWave) {
+    const int b = e / chunks, c = e % chunks;
+    const int bb = b0 + b < B ? b0 + b : B - 1;
+    *reinterpret_cast<uint4 *>(xs + b * qb + c * V) =
+        load16(x + static_cast<int64_t>(bb) * d + xoff + c * V);
+  }
+  __syncthreads();
+  if (j >= d) return;  // after the only barrier
+  float acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = 0.f;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = lane + kWave * i;
+    const bool ok = c < chunks;
+    float qf[V];
+    Elt<T>::unpack(q[i], qf);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const uint4 xq = ok ? *reinterpret_cast<const uint4 *>(xs + b * qb + c * V)
+                          : make_uint4(0, 0, 0, 0);
+      float xf[V];
+      Elt<T>::unpack(xq, xf);
+#pragma unroll
+      for (int v = 0; v < V; ++v) acc[b] = fmaf(xf[v], qf[v], acc[b]);
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const float sum = wave_sum(acc[b]);
+    if (lane == 0 && b0 + b < B) x_rot[static_cast<int64_t>(b0 + b) * d + j] = sum;
+  }
+}
+
 // One token, short rotation blocks (a row of Qt is at most LPR 16-byte
 // chunks, LPR <= 32): each wave computes 64 / LPR output channels, LPR lanes
 // per channel, so every lane has a chunk to load; the lane groups are summed
@@ -174,6 +243,51 @@ bool launch_row(const void *x, const void *qt, float *x_rot, int d, int qb, hipS
   else if (nc <= 8) hipLaunchKernelGGL((rotate_row_kernel<8, T>), grid, block, 0, s, xp, qp, x_rot, d, qb);
   else if (nc <= 16) hipLaunchKernelGGL((rotate_row_kernel<16, T>), grid, block, 0, s, xp, qp, x_rot, d, qb);
   else return false;
+  return true;
+}
+
+constexpr size_t kBatchLdsMax = 128 * 1024;  // staged x per workgroup
+
+template <int NC, int NB, typename T>
+void launch_batch_k(const T *x, const T *qt, float *x_rot, int B, int d, int qb, hipStream_t s) {
+  const dim3 grid((d + kBatchWaves - 1) / kBatchWaves, (B + NB - 1) / NB);
+  const size_t lds = static_cast<size_t>(NB) * qb * sizeof(T);
+  auto k = rotate_rows_batch_kernel<NC, NB, T>;
+  if (lds > 64 * 1024)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(k),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  hipLaunchKernelGGL(k, grid, dim3(kBatchWaves * kWave), lds, s, x, qt, x_rot, B, d, qb);
+}
+
+template <int NC, typename T>
+void launch_batch_nb(const T *x, const T *qt, float *x_rot, int B, int d, int qb, hipStream_t s) {
+  // tokens per group: the batch (up to 8), as far as the staged x fits and
+  // the row chunks and sums stay in registers (NC·NB <= 32)
+  int nb = B <= 2 ? 2 : (B <= 4 ? 4 : 8);
+  while (nb > 2 && (static_cast<size_t>(nb) * qb * sizeof(T) > kBatchLdsMax || NC * nb > 32))
+    nb /= 2;
+  if constexpr (NC * 4 <= 32)
+    if (nb == 4) return launch_batch_k<NC, 4, T>(x, qt, x_rot, B, d, qb, s);
+  if constexpr (NC * 8 <= 32)
+    if (nb == 8) return launch_batch_k<NC, 8, T>(x, qt, x_rot, B, d, qb, s);
+  launch_batch_k<NC, 2, T>(x, qt, x_rot, B, d, qb, s);
+}
+
+// Tokens in groups of up to 8 (each group reads Qt once); false when the
+// form does not apply (a row of more than 512 chunks, a workgroup's 8
+// channels spanning two Q blocks, or two tokens' x segments beyond the LDS).
+template <typename T>
+bool launch_rows_batch(const void *x, const void *qt, float *x_rot, int B, int d, int qb,
+                       hipStream_t s) {
+  constexpr int V = Elt<T>::kVec;
+  const int nc = (qb / V + kWave - 1) / kWave;
+  if (qb % kBatchWaves || 2 * static_cast<size_t>(qb) * sizeof(T) > kBatchLdsMax) return false;
+  const auto *xp = static_cast<const T *>(x);
+  const auto *qp = static_cast<const T *>(qt);
+  if (nc <= 2) launch_batch_nb<2, T>(xp, qp, x_rot, B, d, qb, s);
+  else if (nc <= 4) launch_batch_nb<4, T>(xp, qp, x_rot, B, d, qb, s);
+  else if (nc <= 8) launch_batch_nb<8, T>(xp, qp, x_rot, B, d, qb, s);
+  else return false;  // longer rows: the row and two tokens' sums would spill
   return true;
 }
 
@@ -367,7 +481,12 @@ hipError_t launch_rotate(const void *x, int x_dt, const void *qt, int q_dt,
                                     : launch_row<float>(x, qt, x_rot, d, qb, s);
     if (done) return hipGetLastError();
   }
-  // Tokens are processed four at a time; each group re-reads Qt.
+  if (B > 1 && x_dt == q_dt) {
+    const bool done = x_dt == kBF16 ? launch_rows_batch<uint16_t>(x, qt, x_rot, B, d, qb, s)
+                                    : launch_rows_batch<float>(x, qt, x_rot, B, d, qb, s);
+    if (done) return hipGetLastError();
+  }
+  // Mixed types: tokens four at a time; each group re-reads Qt.
   const int xs = dt_size(x_dt);
   for (int b0 = 0; b0 < B; b0 += 4) {
     const int nb = B - b0 < 4 ? B - b0 : 4;

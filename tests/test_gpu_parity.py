@@ -117,6 +117,10 @@ ROTATE_CASES = [
     ("f32", "f32", 512, 512, 1), ("bf16", "bf16", 4096, 4096, 1),
     ("bf16", "bf16", 11008, 2752, 1), ("bf16", "bf16", 1024, 256, 5),
     ("f32", "bf16", 768, 768, 2), ("bf16", "f32", 256, 64, 3), ("bf16", "bf16", 13824, 3456, 8),
+    # 2 to 4 tokens over blocks of 4096 or more, and fp32 batches: the
+    # one-wave-per-channel form with the tokens' x staged in LDS
+    ("bf16", "bf16", 4096, 4096, 2), ("bf16", "bf16", 4096, 4096, 3),
+    ("bf16", "bf16", 5120, 5120, 4), ("f32", "f32", 512, 512, 4), ("f32", "f32", 2048, 1024, 7),
     # batches of 16 and more in bf16 take the matrix-core form
     ("bf16", "bf16", 4096, 4096, 16), ("bf16", "bf16", 11008, 2752, 33),
     ("bf16", "bf16", 8192, 8192, 64), ("bf16", "bf16", 1152, 96, 17),
@@ -142,6 +146,26 @@ def test_rotate_within_rigorous_bound(xdt, qdt, d, qb, B):
     assert np.all(np.abs(got - exact) <= bound)
     assert ref.rel_error(got, ref.rotate(x, q)) < 1e-5
     assert ok()
+
+
+@pytest.mark.parametrize("dt,d,qb,B", [("bf16", 4096, 4096, 3), ("f32", 1024, 1024, 4),
+                                        ("f32", 2048, 512, 7)])
+def test_batched_rotation_is_batch_invariant(dt, d, qb, B):
+    """The few-token form sums each token in the one-token kernel's order:
+    every token's x_rot equals its own one-token call bit for bit."""
+    q = wl.rotation(4, 2, "single", d, qb, dt)
+    x = wl.heavy_tailed_activations(4, 2, "single", B, d, dt)
+    q_d = dev(q.reshape(d, qb), dt)
+    qt = torch.empty_like(q_d)
+    _lib.larosa_prepare_rotation(q_d, qt, d, qb)
+    x_d = dev(x, dt)
+    xr = torch.empty((B, d), device="cuda")
+    _lib.larosa_rotate(x_d, qt, qb, xr, B, d)
+    one = torch.empty((B, d), device="cuda")
+    for b in range(B):
+        _lib.larosa_rotate(x_d[b:b + 1], qt, qb, one[b:b + 1], 1, d)
+    torch.cuda.synchronize()
+    assert torch.equal(xr, one)
 
 
 def test_rotate_exact_for_signed_permutation_and_identity():
