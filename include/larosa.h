@@ -335,8 +335,8 @@ int larosa_swiglu(const void *gu, void *h, int64_t B, int64_t f, int dtype,
  * input, and their outputs meet only in h = SiLU(gate)·up, which is the
  * input of the down projection. Storing the folded [W'_gate | W'_up] with
  * the two halves' columns interleaved in blocks (256 columns for bf16
- * weights, 128 for fp32: half a product column tile) lets the product write
- * h directly. */
+ * weights, 128 for fp32) puts matching gate and up columns in every column
+ * tile of the product, which can then write h directly. */
 
 /* W_il[r, (i / b)·2b + i mod b] = W[r, i] (gate) and W_il[r, (i / b)·2b + b
  * + i mod b] = W[r, f + i] (up) for the block b above; W: [d_in, 2f] =

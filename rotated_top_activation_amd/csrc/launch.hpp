@@ -119,7 +119,8 @@ hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
 
 // --- selection folded into the product, one token ---
 struct SelectGatherPlan {
-  int tiles;   // column tiles of 64·V columns
+  int lpr;     // lanes per row: tiles of lpr·V columns (64, or 32 for narrow bf16 outputs)
+  int tiles;   // column tiles
   int splits;  // channel ranges per tile (partial sums when > 1)
   int cps;     // channels per range
 };
@@ -145,8 +146,9 @@ struct ChainArgs {
   uint32_t spin_limit = 1u << 22;
 };
 // Bytes of a chained launch's tile flags over f h channels, then its control
-// block (24 bytes, 8-byte aligned).
-inline size_t chain_flag_bytes(int64_t f) { return (static_cast<size_t>(f / 256 + 1) * 4 + 7) / 8 * 8 + 24; }
+// block (24 bytes, 8-byte aligned). One flag per product column tile:
+// f / 64 + 1 words cover tiles of 512, 256 or 128 columns.
+inline size_t chain_flag_bytes(int64_t f) { return (static_cast<size_t>(f / 64 + 1) * 4 + 7) / 8 * 8 + 24; }
 inline size_t chain_ctl_offset(int64_t f) { return chain_flag_bytes(f) - 24; }
 bool chain_supported(int64_t q_block, int64_t f);
 // The rotary embedding's per-pair cosine and sine at one position, for

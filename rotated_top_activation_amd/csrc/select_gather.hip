@@ -10,13 +10,24 @@
 // no index list goes through memory; each workgroup builds the list of its
 // own kept channels in LDS and starts streaming their rows at once.
 //
-// Work split: workgroup (tile, split) owns one column tile of 64·V columns
-// (V = 8 bf16 or 4 fp32 per 16-byte load) and the kept channels of the
-// channel range [split·cps, split·cps + cps). Its 16 waves take interleaved
-// groups of eight kept rows, one 16-byte load per lane and row, all eight in
-// flight. The waves' sums are combined in LDS; with more than one split the
+// Work split: workgroup (tile, split) owns one column tile of LPR·V columns
+// (V = 8 bf16 or 4 fp32 per 16-byte load; LPR lanes per row, 64 or 32) and
+// the kept channels of the channel range [split·cps, split·cps + cps). Its
+// 16 waves take interleaved groups of 8·(64 / LPR) kept rows: every lane
+// holds eight 16-byte loads in flight, and one wave load covers 64 / LPR
+// rows. The waves' sums are combined in LDS; with more than one split the
 // partial sums of a tile are added in split order by the tile's
 // last-arriving workgroup, as in the standalone product.
+//
+// Narrow tiles (LPR = 32: 256 bf16 columns, one 512-byte segment per row)
+// serve outputs of at most 8192 columns: 4096 columns then make 16 tiles of
+// 16 channel ranges instead of 8 tiles of 32, so a tile's split reduction
+// adds 16 partial sums instead of 32 and each workgroup hands over 256 of
+// them instead of 512 (11008 → 4096 down product: 20.4 against 21.1 µs;
+// 128-column tiles measured 21.7). Wide outputs keep 512-column tiles,
+// which stream faster there. With the SwiGLU epilogue a narrow tile takes
+// 128 gate and the matching 128 up columns of the interleaved layout, so it
+// still finishes whole channels of h.
 //
 // The grid is sized to at most one workgroup per CU (256 on MI355X), which
 // keeps every workgroup resident for the whole launch.
@@ -82,7 +93,7 @@ struct NoRope {};
 template <int EPI>
 using RopeParam = std::conditional_t<EPI == kEpiRope, RopeArgs, NoRope>;
 
-template <typename WT, typename OT, int EMAX, bool SWIGLU, bool THR, int EPI>
+template <typename WT, typename OT, int EMAX, bool SWIGLU, bool THR, int EPI, int LPR>
 __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
     const float *__restrict__ x_rot, int d, int k, uint32_t thr_key, int E, int tiles,
     int splits, int cps, const WT *__restrict__ w, int64_t d_out, OT *__restrict__ y,
@@ -93,9 +104,19 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
   constexpr bool ROPE = EPI == kEpiRope;
   static_assert(!CHAIN || (SWIGLU && !THR), "the chain follows the SwiGLU product");
   static_assert(!ROPE || (!SWIGLU && !THR), "RoPE follows a plain product");
+  static_assert(LPR == kWave || LPR == 32, "lanes per row");
   constexpr int V = Elt<WT>::kVec;
-  constexpr int TILE = kWave * V;
-  constexpr int R = kSgRows;  // loads in flight per lane, list positions per group
+  constexpr int RPW = kWave / LPR;  // rows per wave load
+  constexpr int TILE = LPR * V;     // columns per tile
+  constexpr int R = kSgRows;        // loads in flight per lane
+  constexpr int GP = R * RPW;       // list positions per group
+  // SwiGLU tiles: the first half of a tile's columns are gate columns, the
+  // second half the matching up columns. In the interleaved layout (blocks of
+  // IB = 32·V columns, gate and up alternating) a tile of SEG + SEG columns
+  // is segment (tile % TPP) of the interleaved pair (tile / TPP).
+  constexpr int SEG = TILE / 2;
+  constexpr int IB = 32 * V;
+  constexpr int TPP = IB / SEG;
   __shared__ SelectSmem<kSgThreads> sm;
   __shared__ CandSmem cs;
   // The row list (indices, then coefficients). Before the list is built the
@@ -120,6 +141,7 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
   const int t = threadIdx.x;
   const int lane = t % kWave;
   const int wave = wave_id();
+  const int sub = lane / LPR;  // the lane's row slot within a wave load
   // (chain) this launch's epoch from the control block; the first workgroup
   // zeroes the queue counter that the next launch will use
   __shared__ uint32_t s_epoch;
@@ -135,6 +157,14 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
     }
   const int tile = blockIdx.x % tiles;
   const int split = blockIdx.x / tiles;
+  // global column of the tile's column e
+  auto gcol = [&](int e) -> int64_t {
+    if constexpr (SWIGLU)
+      return static_cast<int64_t>(tile / TPP) * (2 * IB) + (tile % TPP) * SEG + (e / SEG) * IB +
+             e % SEG;
+    else
+      return static_cast<int64_t>(tile) * TILE + e;
+  };
   const int c0 = split * cps < d ? split * cps : d;
   const int c1 = c0 + cps < d ? c0 + cps : d;
   const int i0 = t * E;
@@ -200,32 +230,34 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
         l_val[pos] = __uint_as_float(kv[i]);
       }));
 
-  // 3. Start streaming. The row list is read in groups of R positions:
+  // 3. Start streaming. The row list is read in groups of GP positions:
   //    first the certain rows (groups 0 .. CG − 1), then the boundary rows
   //    (the tail, known once the rule is resolved); wave w takes groups w,
-  //    w + 16, w + 32, ... This wave's first group of certain rows is
+  //    w + 16, w + 32, ... Within a group, lane slot `sub` takes positions
+  //    sub, sub + RPW, ... This wave's first group of certain rows is
   //    requested now, so the rest of the rule is resolved while it is in
   //    flight. Lanes past the last column read a valid column and store
   //    nothing.
-  const int64_t col_raw = static_cast<int64_t>(tile) * TILE + lane * V;
+  const int64_t col_raw = gcol((lane % LPR) * V);
   const int64_t col = col_raw < d_out ? col_raw : d_out - V;
-  const int n_cg = (n_cert + R - 1) / R;  // CG
+  const int n_cg = (n_cert + GP - 1) / GP;  // CG
   int n_list = n_cert;
-  // A group's list entries are all read first, then its R rows requested
-  // back to back. Positions past the group's end (the last group of a
-  // segment) repeat the group's last row with coefficient 0: the repeated
-  // request hits the same lines as the real one, so it costs no HBM
-  // traffic, and no load is conditional.
+  // A group's list entries are all read first, then the lane's R rows
+  // requested back to back. Positions past the group's end (the last group
+  // of a segment) repeat the group's last row with coefficient 0: the
+  // repeated request hits the same lines as the real one, so it costs no
+  // HBM traffic, and no load is conditional.
   auto load_group = [&](int G, uint4(&q)[R], float(&c)[R]) {
-    const int lo = G < n_cg ? G * R : n_cert + (G - n_cg) * R;
-    const int hi = G < n_cg ? (lo + R < n_cert ? lo + R : n_cert) : (lo + R < n_list ? lo + R : n_list);
+    const int lo = G < n_cg ? G * GP : n_cert + (G - n_cg) * GP;
+    const int hi = G < n_cg ? (lo + GP < n_cert ? lo + GP : n_cert) : (lo + GP < n_list ? lo + GP : n_list);
     int rows[R];
 #pragma unroll
     for (int u = 0; u < R; ++u) {
-      const int j = lo + u < hi ? lo + u : hi - 1;  // hi > lo for every group read
+      const int pos = lo + u * RPW + sub;
+      const int j = pos < hi ? pos : hi - 1;  // hi > lo for every group read
       rows[u] = l_idx[j];
       const float cv = l_val[j];
-      c[u] = lo + u < hi ? cv : 0.f;
+      c[u] = pos < hi ? cv : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < R; ++u) q[u] = load16(w + static_cast<int64_t>(rows[u]) * d_out + col);
@@ -291,7 +323,7 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
 
   // 6. Stream the rest of this wave's groups: the one in flight (if any),
   //    then one group of R rows at a time, all R loads in flight.
-  const int n_groups = n_cg + (n_list - n_cert + R - 1) / R;
+  const int n_groups = n_cg + (n_list - n_cert + GP - 1) / GP;
   int G = wave;
   if constexpr (THR) {
     if (has_a) {  // still in flight
@@ -312,9 +344,17 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
     consume(q, c);
   }
 
-  // 7. Combine the waves; with one split finish the tile, else partial sums.
+  // 7. Combine the row slots of each wave (lane butterflies), then the
+  //    waves; with one split finish the tile, else partial sums.
+  if constexpr (RPW > 1) {
 #pragma unroll
-  for (int q = 0; q < V; ++q) red[wave][lane * V + q] = acc[q];
+    for (int off = LPR; off < kWave; off <<= 1)
+#pragma unroll
+      for (int q = 0; q < V; ++q) acc[q] += __shfl_xor(acc[q], off, kWave);
+  }
+  if (lane < LPR)
+#pragma unroll
+    for (int q = 0; q < V; ++q) red[wave][lane * V + q] = acc[q];
   __syncthreads();
   const int64_t tile_col0 = static_cast<int64_t>(tile) * TILE;
   // A finished column sum: stored, or staged for the SwiGLU epilogue, which
@@ -322,7 +362,7 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
   // the output type first, as a separate SwiGLU step would see them).
   auto finish = [&](int e, float v) {
     if (SWIGLU || ROPE) ep[e] = v;
-    else Elt<OT>::store(y, tile_col0 + e, v);
+    else Elt<OT>::store(y, gcol(e), v);
   };
   auto epilogue = [&]() {
     if constexpr (ROPE) {
@@ -382,7 +422,7 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
   };
   float *part = partials + static_cast<int64_t>(split) * d_out;
   for (int e = t; e < TILE; e += kSgThreads) {
-    const int64_t cg = tile_col0 + e;
+    const int64_t cg = gcol(e);
     if (cg >= d_out) continue;
     float sum = 0.f;
 #pragma unroll
@@ -413,7 +453,7 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
     __syncthreads();
     if (s_last) {
       for (int e = t; e < TILE; e += kSgThreads) {
-        const int64_t cg = tile_col0 + e;
+        const int64_t cg = gcol(e);
         if (cg >= d_out) continue;
         const float *p = partials + cg;
         float sum = 0.f;
@@ -553,8 +593,8 @@ __global__ __launch_bounds__(kSgThreads) void select_gather_kernel(
     __hip_atomic_store(chain.status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <typename WT, typename OT, int EM, bool SW, bool TH, int EPI>
-void launch_sg_k(const SelectGatherArgs &a, const SelectGatherPlan &p, int E, hipStream_t s) {
+template <typename WT, typename OT, int EM, bool SW, bool TH, int EPI, int LPR>
+void launch_sg_l(const SelectGatherArgs &a, const SelectGatherPlan &p, int E, hipStream_t s) {
   uint32_t *counters = static_cast<uint32_t *>(a.ws);
   float *partials =
       reinterpret_cast<float *>(static_cast<char *>(a.ws) + sg_counter_bytes(p.tiles));
@@ -562,10 +602,18 @@ void launch_sg_k(const SelectGatherArgs &a, const SelectGatherPlan &p, int E, hi
   const ChainArgs &chain = a.chain;
   RopeParam<EPI> rope{};
   if constexpr (EPI == kEpiRope) rope = a.rope;
-  hipLaunchKernelGGL((select_gather_kernel<WT, OT, EM, SW, TH, EPI>), grid, block, 0, s, a.x_rot,
+  hipLaunchKernelGGL((select_gather_kernel<WT, OT, EM, SW, TH, EPI, LPR>), grid, block, 0, s, a.x_rot,
                      a.d_in, a.k, a.thr_key, E, p.tiles, p.splits, p.cps,
                      static_cast<const WT *>(a.w), a.d_out, static_cast<OT *>(a.y), partials,
                      counters, a.idx_out, a.count_out, chain, rope);
+}
+
+// Narrow tiles exist for bf16 weights only.
+template <typename WT, typename OT, int EM, bool SW, bool TH, int EPI>
+void launch_sg_k(const SelectGatherArgs &a, const SelectGatherPlan &p, int E, hipStream_t s) {
+  if constexpr (sizeof(WT) == 2)
+    if (p.lpr == 32) return launch_sg_l<WT, OT, EM, SW, TH, EPI, 32>(a, p, E, s);
+  launch_sg_l<WT, OT, EM, SW, TH, EPI, kWave>(a, p, E, s);
 }
 
 template <typename WT, typename OT, int EM>
@@ -603,7 +651,9 @@ hipError_t launch_sg_t(const SelectGatherArgs &a, const SelectGatherPlan &p, hip
 
 SelectGatherPlan plan_select_gather(int64_t d_in, int64_t d_out, int w_dt) {
   SelectGatherPlan p;
-  const int64_t tile_cols = static_cast<int64_t>(kWave) * (w_dt == kF32 ? 4 : 8);
+  // narrow tiles (256 columns) for bf16 outputs of at most 8192 columns
+  p.lpr = w_dt == kBF16 && d_out <= 8192 ? 32 : kWave;
+  const int64_t tile_cols = static_cast<int64_t>(p.lpr) * (w_dt == kF32 ? 4 : 8);
   p.tiles = static_cast<int>((d_out + tile_cols - 1) / tile_cols);
   int64_t splits = 256 / p.tiles;                          // one workgroup per CU
   const int64_t by_list = (d_in + kSgListMax - 1) / kSgListMax;  // LDS list bound
@@ -635,12 +685,13 @@ hipError_t launch_select_gather(const SelectGatherArgs &a, hipStream_t s) {
   if (a.chain.qt != nullptr &&
       (!a.swiglu || a.by_threshold || a.w_dt != kBF16 || a.y_dt != kBF16 ||
        !chain_supported(a.chain.qb, a.chain.f) || a.d_out != 2 * a.chain.f ||
-       a.chain.tile_flag == nullptr || a.chain.ctl == nullptr || a.chain.x_rot == nullptr))
+       a.chain.tile_flag == nullptr || a.chain.ctl == nullptr || a.chain.x_rot == nullptr ||
+       p.tiles > a.chain.f / 64 + 1))  // the flag words chain_flag_bytes(f) provides
     return hipErrorInvalidValue;
   if (a.rope.rot_cols > 0 &&
       (a.swiglu || a.by_threshold || a.chain.qt != nullptr || a.w_dt != kBF16 ||
        a.y_dt != kBF16 || a.rope.tab.dh < 2 || a.rope.tab.dh % 2 ||
-       a.rope.tab.dh > 2 * kRopeMaxHalf || (kWave * 8) % a.rope.tab.dh ||
+       a.rope.tab.dh > 2 * kRopeMaxHalf || (p.lpr * 8) % a.rope.tab.dh ||
        a.rope.rot_cols % a.rope.tab.dh || a.rope.rot_cols > a.d_out))
     return hipErrorInvalidValue;
   if (a.w_dt == kBF16 && a.y_dt == kBF16) return launch_sg_t<uint16_t, uint16_t>(a, p, s);
