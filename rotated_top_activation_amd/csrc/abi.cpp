@@ -381,16 +381,18 @@ int layer_entry(const void *x, int act_dtype, const void *Qt, int64_t q_block,
     if (sel.thr) {
       e = launch_threshold_select(x_rot, static_cast<int>(B), static_cast<int>(d_in),
                                   sel.thr_key, idx, sel.count_out, val, xs, mask, s);
-      if (e == hipSuccess)
+      if (e == hipSuccess && !mf)
         e = launch_union(mask, xs, static_cast<int>(B), static_cast<int>(d_in), u_idx, u_cnt,
-                         mf ? nullptr : u_coef, s);
+                         u_coef, s);
     } else {
       // the union and the product read xs and the masks only: the index
-      // list is written when asked for, the values not at all; the union
-      // list is taken by the selection launch itself
+      // list is written when asked for, the values not at all. For the
+      // vector product the union list is taken by the selection launch
+      // itself; the matrix-core product's coefficient launch takes it from
+      // the masks.
       e = launch_select(x_rot, static_cast<int>(B), static_cast<int>(d_in), static_cast<int>(k),
                         idx_out, nullptr, xs, mask, s, parts, n_parts,
-                        union_tail(base + L.p.status, u_idx, u_cnt));
+                        mf ? UnionTail{} : union_tail(base + L.p.status, u_idx, u_cnt));
       if (e == hipSuccess && !mf)
         e = launch_union_coef(u_idx, u_cnt, xs, static_cast<int>(B), static_cast<int>(d_in),
                               u_coef, s);
@@ -401,8 +403,8 @@ int layer_entry(const void *x, int act_dtype, const void *Qt, int64_t q_block,
     if (mf) {
       const int64_t ldc = mfma_coef_ld(max_rows);
       void *coefT = base + L.p.mfma_coef;
-      e = launch_union_coef_t(u_idx, u_cnt, xs, static_cast<int>(B), static_cast<int>(d_in), ldc,
-                              coefT, s);
+      e = launch_union_coef_mask(mask, xs, static_cast<int>(B), static_cast<int>(d_in), ldc, coefT,
+                                 u_idx, u_cnt, s);
       if (e == hipSuccess)
         e = launch_gather_mfma(u_idx, u_cnt, max_rows, d_in, coefT, ldc, W_folded, y,
                                static_cast<int>(B), d_out, base + L.p.mfma_parts, s);

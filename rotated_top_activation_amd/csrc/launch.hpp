@@ -221,9 +221,12 @@ int64_t mfma_coef_ld(int64_t max_rows);
 hipError_t launch_gather_mfma(const int32_t *rows, const int32_t *n_rows, int64_t max_rows,
                               int64_t d_in, const void *coef_hl, int64_t ldc, const void *w,
                               void *y, int B, int64_t d_out, void *ws, hipStream_t s);
-// Split coefficients of xs[b, u_idx[j]] for j < |U|, zero for j in [|U|, ldc).
-hipError_t launch_union_coef_t(const int32_t *u_idx, const int32_t *u_count, const float *xs,
-                               int B, int d, int64_t ldc, void *coef_hl, hipStream_t s);
+// The union of the B masks ([B, ceil(d/32)] words, d <= 32768) as u_idx
+// (ascending) and *u_count, and the split coefficients of xs[b, u_idx[j]]
+// for j < |U|, zero for j in [|U|, ldc), in one launch.
+hipError_t launch_union_coef_mask(const uint32_t *mask, const float *xs, int B, int d,
+                                  int64_t ldc, void *coef_hl, int32_t *u_idx, int32_t *u_count,
+                                  hipStream_t s);
 // Split coefficients of coef[j · B + b] for j < max_rows, zero up to ldc.
 hipError_t launch_coef_transpose(const float *coef, int B, int64_t max_rows, int64_t ldc,
                                  void *coef_hl, hipStream_t s);

@@ -281,18 +281,50 @@ __global__ __launch_bounds__(kUcThreads) void union_coef_kernel(
   }
 }
 
-// Split coefficients (store_coef_hl) of xs[b, u_idx[j]] for j < |U|; zero
-// for j in [|U|, ldc).
-__global__ void union_coef_t_kernel(const int32_t *__restrict__ u_idx,
-                                    const int32_t *__restrict__ u_count,
-                                    const float *__restrict__ xs, int B, int d, int64_t ldc,
-                                    uint16_t *__restrict__ coef_hl) {
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (e >= ldc * B) return;
-  const int b = static_cast<int>(e / ldc);
-  const int64_t j = e % ldc;
-  const int n = *u_count;
-  store_coef_hl(coef_hl, ldc, b, j, j < n ? xs[static_cast<int64_t>(b) * d + u_idx[j]] : 0.f);
+// The union and its split coefficients in one launch, from the B masks: every
+// workgroup ORs the masks (one word per thread), counts the set bits with a
+// block scan, and so knows the whole union list; it then takes its own
+// kUmRows list positions j: u_idx[j], and the coefficients xs[b, u_idx[j]]
+// of every token (zero for j in [|U|, ldc)). Workgroup 0 writes |U|. This
+// replaces the selection launch's union tail (an arrival counter and the
+// last token's OR, three device round trips after the slowest token) plus a
+// coefficient launch.
+constexpr int kUmRows = 256;
+__global__ __launch_bounds__(kThreads) void union_coef_mask_kernel(
+    const uint32_t *__restrict__ mask, const float *__restrict__ xs, int B, int d, int64_t ldc,
+    uint16_t *__restrict__ coef_hl, int32_t *__restrict__ u_idx, int32_t *__restrict__ u_count) {
+  __shared__ uint32_t wave_tot[kThreads / kWave];
+  __shared__ int32_t rows[kUmRows];
+  const int t = threadIdx.x;
+  const int nw = (d + 31) / 32;
+  const int64_t j0 = static_cast<int64_t>(blockIdx.x) * kUmRows;
+  uint32_t word = 0u;
+  if (t < nw) word = B <= 16 ? or_words<16>(mask, B, nw, t) : or_words<32>(mask, B, nw, t);
+  const uint32_t c = __popc(word);
+  const uint32_t incl = block_incl_scan<kThreads>(c, wave_tot);
+  uint32_t total = 0;
+#pragma unroll
+  for (int i = 0; i < kThreads / kWave; ++i) total += wave_tot[i];
+  int64_t pos = incl - c;
+  if (pos < j0 + kUmRows && pos + c > j0) {
+    while (word) {
+      const int bit = __ffs(word) - 1;
+      if (pos >= j0 && pos < j0 + kUmRows) rows[pos - j0] = t * 32 + bit;
+      ++pos;
+      word &= word - 1u;
+    }
+  }
+  __syncthreads();
+  const int64_t n = total;
+  if (blockIdx.x == 0 && t == 0) *u_count = static_cast<int32_t>(n);
+  for (int r = t; r < kUmRows; r += kThreads)
+    if (j0 + r < n) u_idx[j0 + r] = rows[r];
+  for (int e = t; e < B * kUmRows; e += kThreads) {
+    const int b = e / kUmRows, r = e % kUmRows;
+    const int64_t j = j0 + r;
+    if (j >= ldc) continue;
+    store_coef_hl(coef_hl, ldc, b, j, j < n ? xs[static_cast<int64_t>(b) * d + rows[r]] : 0.f);
+  }
 }
 
 // Split coefficients of coef[j·B + b] for j < rows; zero for j in [rows, ldc).
@@ -360,11 +392,13 @@ hipError_t launch_union_coef(const int32_t *u_idx, const int32_t *u_count, const
   return hipGetLastError();
 }
 
-hipError_t launch_union_coef_t(const int32_t *u_idx, const int32_t *u_count, const float *xs,
-                               int B, int d, int64_t ldc, void *coefT, hipStream_t s) {
-  const int64_t n = ldc * B;
-  hipLaunchKernelGGL(union_coef_t_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
-                     0, s, u_idx, u_count, xs, B, d, ldc, static_cast<uint16_t *>(coefT));
+hipError_t launch_union_coef_mask(const uint32_t *mask, const float *xs, int B, int d,
+                                  int64_t ldc, void *coefT, int32_t *u_idx, int32_t *u_count,
+                                  hipStream_t s) {
+  if (d > 32 * kThreads || B < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(union_coef_mask_kernel, dim3(static_cast<unsigned>((ldc + kUmRows - 1) / kUmRows)),
+                     dim3(kThreads), 0, s, mask, xs, B, d, ldc, static_cast<uint16_t *>(coefT),
+                     u_idx, u_count);
   return hipGetLastError();
 }
 
