@@ -165,15 +165,24 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
   if (mask) bitmap[t] = 0u;
 
   // The first digit counts into histogram copies laid out in `stage`, which
-  // is free until the outputs; the later digits continue from it.
+  // is free until the outputs; the rest of the rule works on the channels
+  // of the boundary digit, listed in the same free words (the one-token
+  // product's rule: T and the index cut-off of the keys equal to T).
+  static_assert(EMAX * kThreads * sizeof(uint32_t) >= sizeof(CandSmem), "candidates fit in stage");
   constexpr int kCopies = EMAX >= 8 ? hist_copies_for(EMAX * kThreads) : 1;
   const RuleState st =
       rule_first_digit<kThreads, EMAX, kCopies>(key, E, static_cast<uint32_t>(k), sm, stage);
-  uint32_t T, krem, n_eq;
-  radix_threshold_from<kThreads, EMAX>(key, 1, st.prefix, st.pmask, st.krem, sm, T, krem, n_eq);
+  uint32_t T, cut;
+  rule_finish<kThreads, EMAX>(key, E, i0, st, sm, *reinterpret_cast<CandSmem *>(stage), T, cut);
   bool kept[EMAX];
-  uint32_t pos;
-  kept_flags<kThreads, EMAX>(key, T, krem, sm, kept, pos);
+  uint32_t n_kept = 0;
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) {
+    kept[e] = rule_keeps<EMAX>(key, e, E, i0, T, cut);
+    n_kept += kept[e];
+  }
+  // the position of the thread's first kept channel in the ascending list
+  const uint32_t pos = block_incl_scan<kThreads>(n_kept, sm.wave_tot) - n_kept;
 
   // Outputs go through LDS: a thread's slots are E consecutive channels, so
   // storing them straight to memory would put a wave's 64 lanes 4·E bytes

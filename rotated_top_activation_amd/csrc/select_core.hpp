@@ -162,15 +162,6 @@ __device__ __forceinline__ void radix_threshold_from(const uint32_t (&key)[EMAX]
   eq_count = last_count;
 }
 
-// Finds T and krem for the top k of the keys held by the block, and the
-// number of keys equal to T.
-template <int NT, int EMAX>
-__device__ __forceinline__ void radix_threshold(const uint32_t (&key)[EMAX], uint32_t k,
-                                                SelectSmem<NT> &sm, uint32_t &T,
-                                                uint32_t &krem_out, uint32_t &eq_count) {
-  radix_threshold_from<NT, EMAX>(key, 0, 0u, kNoKey, k, sm, T, krem_out, eq_count);
-}
-
 // Index of the krem-th (1-based) channel, in index order, whose key equals
 // T, over slots holding consecutive channels from i0 = t·E. Every thread
 // gets the result. Channels with key == T are kept iff their index is at
@@ -225,41 +216,6 @@ __device__ __forceinline__ void load_keys4(const float *row, int d, int E, uint3
 // Slots per thread for d channels over NT threads: a multiple of 4.
 __host__ __device__ constexpr int slots_per_thread(int d, int NT) {
   return (((d + NT - 1) / NT) + 3) / 4 * 4;
-}
-
-// Kept flags and ascending output positions of the thread's slots, which
-// hold consecutive channels. Slot e is kept iff key > T, or key == T and
-// fewer than krem equal keys precede it. Returns the number of kept
-// channels owned by lower threads (the position of the first kept slot).
-template <int NT, int EMAX>
-__device__ __forceinline__ void kept_flags(const uint32_t (&key)[EMAX], uint32_t T, uint32_t krem,
-                                           SelectSmem<NT> &sm, bool (&kept)[EMAX],
-                                           uint32_t &pos0) {
-  uint32_t gt = 0, eq = 0;
-#pragma unroll
-  for (int e = 0; e < EMAX; ++e) {
-    if (key[e] & kNoKey) continue;
-    gt += key[e] > T;
-    eq += key[e] == T;
-  }
-  const uint32_t packed = (gt << 16) | eq;  // each count <= 32768
-  const uint32_t excl = block_incl_scan<NT>(packed, sm.wave_tot) - packed;
-  const uint32_t g0 = excl >> 16;
-  uint32_t qe = excl & 0xFFFFu;
-  pos0 = g0 + (qe < krem ? qe : krem);
-#pragma unroll
-  for (int e = 0; e < EMAX; ++e) {
-    bool kp = false;
-    if (!(key[e] & kNoKey)) {
-      if (key[e] > T) {
-        kp = true;
-      } else if (key[e] == T) {
-        kp = qe < krem;
-        ++qe;
-      }
-    }
-    kept[e] = kp;
-  }
 }
 
 // ---- Exact rule from a short candidate list ------------------------------
@@ -432,14 +388,6 @@ __device__ __forceinline__ void rule_finish(const uint32_t (&key)[EMAX], int E, 
   __syncthreads();
   cut = sm.bin;
   __syncthreads();
-}
-
-template <int NT, int EMAX>
-__device__ __forceinline__ void topk_rule(const uint32_t (&key)[EMAX], int E, int i0, uint32_t k,
-                                          SelectSmem<NT> &sm, CandSmem &cs, uint32_t &T,
-                                          uint32_t &cut) {
-  const RuleState st = rule_first_digit<NT, EMAX>(key, E, k, sm);
-  rule_finish<NT, EMAX>(key, E, i0, st, sm, cs, T, cut);
 }
 
 // Whether slot e (channel i0 + e) is kept under the rule (T, cut).
