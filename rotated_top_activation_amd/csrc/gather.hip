@@ -22,7 +22,11 @@
 namespace larosa {
 namespace {
 
-constexpr int kRows = 8;  // rows per wave group (loads in flight per lane)
+// Rows per wave group (loads in flight per lane). Four measured faster than
+// eight or six: the 7B gate|up product over a given list of 2457 rows takes
+// 22.4 µs against 26.7 µs (and the dense product over all 4096 rows 33.7
+// against 34.9 µs), one process on one box.
+constexpr int kRows = 4;
 
 size_t counter_bytes(int tiles) { return (static_cast<size_t>(tiles) * 4 + 255) / 256 * 256; }
 constexpr int kMaxSplitLoads = 16;  // partial sums fetched per round trip
