@@ -360,8 +360,10 @@ def test_fused_and_unfused_share_one_workspace():
 
 
 @pytest.mark.parametrize("B,d,qb,n", [(32, 2048, 512, 2056), (64, 1024, 1024, 1032),
-                                      (11, 4096, 4096, 520)])
+                                      (11, 4096, 4096, 520), (6, 1000, 200, 264)])
 def test_large_batches(B, d, qb, n):
+    """Matrix-core batches, including d = 1000, whose last mask word of the
+    row union is partly past the channels."""
     case = wl.LinearCase(cfg=5, batch=B, d_in=d, d_out=n, q_block=qb, sparsity_pct=50,
                          dtype="bf16", role="mlp_in")
     x, q, w = wl.linear_case_inputs(case, w_std=0.01)
