@@ -798,19 +798,14 @@ def other_configs(a, device):
 
                 def step():
                     h.copy_(h0)
-                    _lib.larosa_rmsnorm(h, buf.a, B, d)
-                    for li, L in enumerate(layers):
-                        dec.layer_forward(L, h, buf, _lib.UNFUSED, normed=True,
-                                          norm_next=li < n_layers - 1)
+                    dec.decoder_step(layers, h, buf, _lib.UNFUSED)
                 ms = _timed_ms(step, steps, warm)
                 # bytes: rotations + union rows (one traced step) + key/value cache
                 nbytes = 0
                 h.copy_(h0)
-                _lib.larosa_rmsnorm(h, buf.a, B, d)
-                for li, L in enumerate(layers):
-                    trace = {}
-                    dec.layer_forward(L, h, buf, _lib.UNFUSED, trace=trace, normed=True,
-                                      norm_next=li < n_layers - 1)
+                traces = [{} for _ in layers]
+                dec.decoder_step(layers, h, buf, _lib.UNFUSED, traces=traces)
+                for L, trace in zip(layers, traces):
                     for role in dec.ROLES:
                         lin = L.lin[role]
                         nbytes += lin.Qt.numel() * 2 + _union_rows(trace[role][1]) * lin.d_out * 2

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define LAROSA_ABI_VERSION 8
+#define LAROSA_ABI_VERSION 9
 
 /* Every entry point is a no-throw C function: exceptions never cross the
  * ABI (a caught one is reported as LAROSA_ERR_INTERNAL). */
@@ -107,6 +107,18 @@ enum { LAROSA_VALIDATE = 4 };
  * On MI355X this chained form measures slower than the two launches it
  * replaces, so it is not the default. */
 enum { LAROSA_CHAIN = 8 };
+
+/* Mode flag of larosa_layer_forward, larosa_swiglu_layer_forward,
+ * larosa_qkv_rope_layer_forward and their workspace-size calls: x already
+ * holds the rotated input x_rot = x·Q, fp32 [B, d_in] (for instance from
+ * larosa_residual_rmsnorm_rotate), so the rotation step is skipped and Qt
+ * is not read (it may be NULL; q_block must still be valid). act_dtype
+ * names the element type of y only. The remaining steps (select, union,
+ * product and the epilogues) are those of the call without the flag, on
+ * the same x_rot, so y has the same bits. xrot_out must be NULL; the flag
+ * cannot be combined with LAROSA_ROTATE_FP64, and LAROSA_FUSED with it runs
+ * the unfused steps. */
+enum { LAROSA_PREROTATED = 16 };
 
 /* LAROSA_ABI_VERSION of the loaded library. */
 int larosa_abi_version(void) LAROSA_NOEXCEPT;
@@ -534,7 +546,7 @@ int larosa_qkv_rope_layer_forward(const void *x, int act_dtype, const void *Qt, 
                                   larosa_stream_t stream) LAROSA_NOEXCEPT;
 
 /* Workspace bytes of larosa_decode_attention (per-chunk partial results of
- * 256 positions); 0 for invalid sizes. */
+ * 64 positions); 0 for invalid sizes. */
 size_t larosa_decode_attention_workspace_bytes(int64_t B, int64_t T, int64_t n_heads) LAROSA_NOEXCEPT;
 
 /* Single-query softmax attention of every query head over its key/value
@@ -544,10 +556,10 @@ size_t larosa_decode_attention_workspace_bytes(int64_t B, int64_t T, int64_t n_h
  * the new key and value of token b start at k_new + b·k_stride and
  * v_new + b·v_stride (n_kv_heads·128 channels each); caches are
  * [B, n_kv_heads, T, 128] (head-major). d_head must be 128; T <= 16384.
- * The positions are taken in chunks of 256 whose partial softmax results
- * are combined in chunk order (deterministic); ws: at least
- * larosa_decode_attention_workspace_bytes(B, T, n_heads) bytes, 16-byte
- * aligned, overwritten by each call. */
+ * The positions are taken in chunks of 64 whose partial softmax results
+ * are combined in chunk order (deterministic) by a second launch; ws: at
+ * least larosa_decode_attention_workspace_bytes(B, T, n_heads) bytes,
+ * 16-byte aligned, overwritten by each call. */
 int larosa_decode_attention(const void *q, const void *k_new, int64_t k_stride,
                             const void *v_new, int64_t v_stride, const void *k_cache,
                             const void *v_cache, void *out, int64_t B, int64_t T,
@@ -561,6 +573,24 @@ int larosa_decode_attention(const void *q, const void *k_new, int64_t k_stride,
  * h, o, out: [B, d]; out must not overlap h or o (h and o may be equal). */
 int larosa_residual_rmsnorm(void *h, const void *o, void *out, int64_t B, int64_t d, float eps,
                             int dtype, larosa_stream_t stream) LAROSA_NOEXCEPT;
+
+/* One token: the residual add and RMSNorm folded into the rotation of the
+ * normalised row (stage 1 of the method, LaRoSA summary page, 方法详解 ·
+ * 技术框架: each linear input is rotated by its layer's Q), in one launch:
+ *   v = o ? bf16(h + o) : h;  a = bf16(v / sqrt(mean(v²) + eps));
+ *   x_rot = a·Q  (fp32 [d]),
+ * with the bits of larosa_residual_rmsnorm (or larosa_rmsnorm when o is
+ * NULL) followed by larosa_rotate. With o, the residual sum v is written to
+ * h_out, which must not overlap h or o (every workgroup reads h and o whole,
+ * so the sum cannot be written in place); a_out, if not NULL, receives a.
+ * Qt: the prepared rotation of a dense Q, [d, d] (q_block == d). bf16 only
+ * (LAROSA_ERR_DTYPE otherwise); d a multiple of 8 above 256 and at most
+ * 8192 (the sizes whose one-token rotation takes one wave per channel;
+ * LAROSA_ERR_SHAPE otherwise); every pointer 16-byte aligned. The decoder glue uses
+ * it with LAROSA_PREROTATED layer calls. */
+int larosa_residual_rmsnorm_rotate(const void *h, const void *o, void *h_out, void *a_out,
+                                   const void *Qt, int64_t d, float eps, float *x_rot, int dtype,
+                                   larosa_stream_t stream) LAROSA_NOEXCEPT;
 
 /* Residual add in place: h[i] = h[i] + o[i] for i < n. */
 int larosa_residual_add(void *h, const void *o, int64_t n, int dtype, larosa_stream_t stream) LAROSA_NOEXCEPT;

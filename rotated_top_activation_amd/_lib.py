@@ -22,7 +22,8 @@ UNFUSED, FUSED = 0, 1
 ROTATE_FP64 = 2  # mode flag: fp64-accumulating rotation, OR-ed into UNFUSED or FUSED
 VALIDATE = 4     # mode flag: check the rotated input for NaN/inf (waits on the stream)
 CHAIN = 8        # mode flag of larosa_mlp_forward: the rotation of h chained into the gate|up launch
-ABI_VERSION = 8
+PREROTATED = 16  # mode flag of the layer calls: x is the rotated input x_rot (fp32)
+ABI_VERSION = 9
 
 # status codes (include/larosa.h)
 OK, ERR_INVALID_ARG, ERR_SHAPE, ERR_ALIGNMENT, ERR_DTYPE, ERR_WORKSPACE = 0, 1, 2, 3, 4, 5
@@ -104,6 +105,8 @@ SIGNATURES = {
     "larosa_residual_add": (_c_int, [_c_vp, _c_vp, _c_i64, _c_int, _c_vp]),
     "larosa_residual_rmsnorm": (_c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, ctypes.c_float,
                                          _c_int, _c_vp]),
+    "larosa_residual_rmsnorm_rotate": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64,
+                                                ctypes.c_float, _c_vp, _c_int, _c_vp]),
     "larosa_topk_swiglu_gemv": (_c_int, [_c_vp, _c_i64, _c_i64, _c_vp, _c_int, _c_vp, _c_int,
                                          _c_i64, _c_vp, _c_vp, _c_sz, _c_vp]),
 }
@@ -146,6 +149,11 @@ def _check(name: str, status: int) -> None:
 
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _act_dt(x, y, mode: int) -> int:
+    """act_dtype of a layer call: y's type when x is the fp32 rotated input."""
+    return _dt(y) if mode & PREROTATED else _dt(x)
 
 
 def _dt(t) -> int:
@@ -244,7 +252,7 @@ def larosa_layer_forward(x, Qt, q_block: int, W_folded, B: int, d_in: int, d_out
                          y, idx_out=None, xrot_out=None, mode: int = UNFUSED, ws=None,
                          stream=None) -> None:
     _check("larosa_layer_forward",
-           load().larosa_layer_forward(_ptr(x), _dt(x), _ptr(Qt), q_block, _ptr(W_folded),
+           load().larosa_layer_forward(_ptr(x), _act_dt(x, y, mode), _ptr(Qt), q_block, _ptr(W_folded),
                                        _dt(W_folded), B, d_in, d_out, k, _ptr(y), _ptr(idx_out),
                                        _ptr(xrot_out), mode, _ptr(ws), _nbytes(ws),
                                        _stream(stream)))
@@ -254,7 +262,7 @@ def larosa_layer_forward_noalloc(x, Qt, q_block: int, W_folded, B: int, d_in: in
                                  k: int, y, idx_out=None, xrot_out=None, mode: int = UNFUSED,
                                  stream=None) -> None:
     _check("larosa_layer_forward_noalloc",
-           load().larosa_layer_forward_noalloc(_ptr(x), _dt(x), _ptr(Qt), q_block,
+           load().larosa_layer_forward_noalloc(_ptr(x), _act_dt(x, y, mode), _ptr(Qt), q_block,
                                                _ptr(W_folded), _dt(W_folded), B, d_in, d_out, k,
                                                _ptr(y), _ptr(idx_out), _ptr(xrot_out), mode,
                                                _stream(stream)))
@@ -284,7 +292,7 @@ def larosa_swiglu_layer_forward(x, Qt, q_block: int, W_il, B: int, d_in: int, f:
                                 h, idx_out=None, xrot_out=None, mode: int = UNFUSED, ws=None,
                                 stream=None) -> None:
     _check("larosa_swiglu_layer_forward",
-           load().larosa_swiglu_layer_forward(_ptr(x), _dt(x), _ptr(Qt), q_block, _ptr(W_il),
+           load().larosa_swiglu_layer_forward(_ptr(x), _act_dt(x, h, mode), _ptr(Qt), q_block, _ptr(W_il),
                                               _dt(W_il), B, d_in, f, k, _ptr(h), _ptr(idx_out),
                                               _ptr(xrot_out), mode, _ptr(ws), _nbytes(ws),
                                               _stream(stream)))
@@ -364,7 +372,7 @@ def larosa_qkv_rope_layer_forward(x, Qt, q_block: int, W_folded, B: int, d_in: i
                                   theta: float = 10000.0, idx_out=None, xrot_out=None,
                                   mode: int = UNFUSED, ws=None, stream=None) -> None:
     _check("larosa_qkv_rope_layer_forward",
-           load().larosa_qkv_rope_layer_forward(_ptr(x), _dt(x), _ptr(Qt), q_block,
+           load().larosa_qkv_rope_layer_forward(_ptr(x), _act_dt(x, y, mode), _ptr(Qt), q_block,
                                                 _ptr(W_folded), _dt(W_folded), B, d_in, k,
                                                 n_heads, n_kv_heads, d_head, pos, theta, _ptr(y),
                                                 _ptr(idx_out), _ptr(xrot_out), mode, _ptr(ws),
@@ -388,6 +396,14 @@ def larosa_decode_attention(q, k_new, k_stride: int, v_new, v_stride: int, k_cac
 def larosa_residual_add(h, o, n: int, stream=None) -> None:
     _check("larosa_residual_add", load().larosa_residual_add(_ptr(h), _ptr(o), n, _dt(h),
                                                              _stream(stream)))
+
+
+def larosa_residual_rmsnorm_rotate(h, o, h_out, Qt, x_rot, d: int, a_out=None, eps: float = 1e-5,
+                                   stream=None) -> None:
+    _check("larosa_residual_rmsnorm_rotate",
+           load().larosa_residual_rmsnorm_rotate(_ptr(h), _ptr(o), _ptr(h_out), _ptr(a_out),
+                                                 _ptr(Qt), d, eps, _ptr(x_rot), _dt(h),
+                                                 _stream(stream)))
 
 
 def larosa_residual_rmsnorm(h, o, out, B: int, d: int, eps: float = 1e-5, stream=None) -> None:

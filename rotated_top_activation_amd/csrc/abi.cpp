@@ -197,11 +197,13 @@ int check_rotation(int64_t d, int64_t qb, int q_dt) {
 // The execution mode without the LAROSA_ROTATE_FP64 and LAROSA_VALIDATE
 // flags, or -1 when the mode holds any other bit.
 int base_mode(int mode) {
-  const int m = mode & ~(LAROSA_ROTATE_FP64 | LAROSA_VALIDATE);
+  if ((mode & LAROSA_PREROTATED) && (mode & LAROSA_ROTATE_FP64)) return -1;
+  const int m = mode & ~(LAROSA_ROTATE_FP64 | LAROSA_VALIDATE | LAROSA_PREROTATED);
   return m == LAROSA_UNFUSED || m == LAROSA_FUSED ? m : -1;
 }
 
 bool fp64_rotation(int mode) { return (mode & LAROSA_ROTATE_FP64) != 0; }
+bool prerotated(int mode) { return (mode & LAROSA_PREROTATED) != 0; }
 bool validating(int mode) { return (mode & LAROSA_VALIDATE) != 0; }
 
 // LAROSA_VALIDATE: flags any NaN or ±inf among the n rotated entries on the
@@ -245,7 +247,10 @@ int layer_args(const void *x, int act_dtype, const void *Qt, int64_t q_block,
   if (base_mode(mode) < 0) return LAROSA_ERR_INVALID_ARG;
   if (d_out < 1) return LAROSA_ERR_SHAPE;
   if (B == 0) return LAROSA_OK;
-  if (!x || !Qt || !W_folded || !y) return LAROSA_ERR_INVALID_ARG;
+  // with LAROSA_PREROTATED x is fp32 x_rot and Qt is not read
+  const bool pre = prerotated(mode);
+  if (!x || (!Qt && !pre) || !W_folded || !y) return LAROSA_ERR_INVALID_ARG;
+  if (pre && xrot_out) return LAROSA_ERR_INVALID_ARG;
   if (int st = check_rotation(d_in, q_block, w_dtype)) return st;
   if (d_in % vec_of(act_dtype) || d_out % vec_of(w_dtype)) return LAROSA_ERR_ALIGNMENT;
   if (!aligned16(x) || !aligned16(Qt) || !aligned16(W_folded) || !aligned16(y))
@@ -269,7 +274,8 @@ int layer_entry(const void *x, int act_dtype, const void *Qt, int64_t q_block,
   if (!aligned16(ws)) return LAROSA_ERR_ALIGNMENT;
   const bool f64 = fp64_rotation(mode);
   const bool check = validating(mode);
-  const bool fused = base_mode(mode) == LAROSA_FUSED && !f64 && !check && !sel.thr &&
+  const bool pre = prerotated(mode);
+  const bool fused = base_mode(mode) == LAROSA_FUSED && !f64 && !check && !sel.thr && !pre &&
                      fused_supported(B, d_in, act_dtype, w_dtype);
   const Layout L = fused ? layout_with_fused(B, d_in, d_out, k, w_dtype)
                          : layout_for(B, d_in, d_out, k, w_dtype);
@@ -296,7 +302,9 @@ int layer_entry(const void *x, int act_dtype, const void *Qt, int64_t q_block,
     f.spin_limit = g_spin_limit.load();
     return launched(launch_fused_linear(f, s));
   }
-  float *x_rot = xrot_out ? xrot_out : reinterpret_cast<float *>(base + L.x_rot);
+  float *x_rot = pre        ? const_cast<float *>(static_cast<const float *>(x))
+                 : xrot_out ? xrot_out
+                            : reinterpret_cast<float *>(base + L.x_rot);
   int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(base + L.idx);
   float *val = reinterpret_cast<float *>(base + L.val);
 
@@ -309,7 +317,8 @@ int layer_entry(const void *x, int act_dtype, const void *Qt, int64_t q_block,
   int n_parts = 1;
   const float *parts = reinterpret_cast<const float *>(base + L.p.mfma_parts);
   hipError_t e =
-      f64   ? launch_rotate_f64(x, act_dtype, Qt, w_dtype, x_rot, static_cast<int>(B),
+      pre   ? hipSuccess
+      : f64 ? launch_rotate_f64(x, act_dtype, Qt, w_dtype, x_rot, static_cast<int>(B),
                                 static_cast<int>(d_in), static_cast<int>(q_block), s)
       : mf && q_block % 32 == 0
           ? launch_rotate_mfma(x, Qt, x_rot, static_cast<int>(B), static_cast<int>(d_in),
@@ -437,13 +446,15 @@ int swiglu_entry(const void *x, int act_dtype, const void *Qt, int64_t q_block,
   if (!ws || ws_bytes < need) return LAROSA_ERR_WORKSPACE;
   const size_t layer_bytes = larosa_workspace_bytes(B, d_in, 2 * f, k, mode);
   const bool one_launch = (base_mode(mode) == LAROSA_UNFUSED || fp64_rotation(mode) ||
-                           validating(mode)) && B == 1 &&
+                           validating(mode) || prerotated(mode)) && B == 1 &&
                           select_gather_supported(d_in) &&
                           !(w_dtype == LAROSA_F32 && act_dtype == LAROSA_BF16);
   if (one_launch) {
     // rotation, then the selection, product and SiLU(gate)·up in one launch
+    const bool pre = prerotated(mode);
     if (int st = check_sizes(B, d_in, k)) return st;
-    if (!x || !Qt || !W_il) return LAROSA_ERR_INVALID_ARG;
+    if (!x || (!Qt && !pre) || !W_il) return LAROSA_ERR_INVALID_ARG;
+    if (pre && xrot_out) return LAROSA_ERR_INVALID_ARG;
     if (int st = check_rotation(d_in, q_block, w_dtype)) return st;
     if (d_in % vec_of(act_dtype)) return LAROSA_ERR_ALIGNMENT;
     if (!aligned16(x) || !aligned16(Qt) || !aligned16(W_il) || !aligned16(ws))
@@ -452,10 +463,13 @@ int swiglu_entry(const void *x, int act_dtype, const void *Qt, int64_t q_block,
     if (int st = device_status()) return st;
     const Layout L = layout_for(B, d_in, 2 * f, k, w_dtype);
     char *base = static_cast<char *>(ws);
-    float *x_rot = xrot_out ? xrot_out : reinterpret_cast<float *>(base + L.x_rot);
+    float *x_rot = pre        ? const_cast<float *>(static_cast<const float *>(x))
+                   : xrot_out ? xrot_out
+                              : reinterpret_cast<float *>(base + L.x_rot);
     hipStream_t s = stream_of(stream);
     const hipError_t er =
-        fp64_rotation(mode)
+        pre ? hipSuccess
+        : fp64_rotation(mode)
             ? launch_rotate_f64(x, act_dtype, Qt, w_dtype, x_rot, 1, static_cast<int>(d_in),
                                 static_cast<int>(q_block), s)
             : launch_rotate(x, act_dtype, Qt, w_dtype, x_rot, 1, static_cast<int>(d_in),
@@ -498,6 +512,7 @@ struct MlpLayout {
 
 MlpLayout mlp_layout(int64_t B, int64_t d, int64_t f, int64_t k1, int64_t k2, int mode) {
   MlpLayout M;
+  if (mode & LAROSA_PREROTATED) return M;  // not a flag of the MLP call
   mode &= ~LAROSA_CHAIN;  // the chained form uses the unfused layout
   M.up_bytes = larosa_swiglu_workspace_bytes(B, d, f, k1, mode);
   M.down_bytes = larosa_workspace_bytes(B, f, d, k2, mode);
@@ -752,7 +767,7 @@ int larosa_lowrank_layer_forward(const void *x, int act_dtype, const void *Qt, i
   if (!dtype_ok(act_dtype) || !dtype_ok(w_dtype)) return LAROSA_ERR_DTYPE;
   if (w_dtype == LAROSA_F32 && act_dtype == LAROSA_BF16) return LAROSA_ERR_DTYPE;
   if (int st = check_sizes(B, d_in, k)) return st;
-  if (base_mode(mode) < 0) return LAROSA_ERR_INVALID_ARG;
+  if (base_mode(mode) < 0 || prerotated(mode)) return LAROSA_ERR_INVALID_ARG;
   if (d_out < 1) return LAROSA_ERR_SHAPE;
   if (r < 1 || r > kMaxRank || r > d_in || r > d_out) return LAROSA_ERR_INVALID_ARG;
   if (B == 0) return LAROSA_OK;
@@ -1212,6 +1227,8 @@ int larosa_mlp_forward(const void *x, int act_dtype, const void *Qt1, int64_t q_
   return guard([&]() -> int {
   const bool want_chain = (mode & LAROSA_CHAIN) != 0;
   mode &= ~LAROSA_CHAIN;
+  // both linears rotate their own inputs here
+  if (prerotated(mode)) return LAROSA_ERR_INVALID_ARG;
   const MlpLayout M = mlp_layout(B, d, f, k1, k2, mode);
   // every argument of both linears first
   if (int st = layer_args(x, act_dtype, Qt1, q_block1, W_il, w_dtype, B, d, 2 * f, k1, h,
@@ -1333,6 +1350,34 @@ int larosa_topk_swiglu_rotate(const float *x_rot, int64_t d_in, int64_t k, const
   g.chain.status = reinterpret_cast<uint32_t *>(base + P.status);
   g.chain.spin_limit = g_spin_limit.load();
   return launched(launch_select_gather(g, stream_of(stream)));
+  });
+}
+
+int larosa_residual_rmsnorm_rotate(const void *h, const void *o, void *h_out, void *a_out,
+                                   const void *Qt, int64_t d, float eps, float *x_rot, int dtype,
+                                   larosa_stream_t stream) LAROSA_NOEXCEPT {
+  return guard([&]() -> int {
+  if (!dtype_ok(dtype)) return LAROSA_ERR_DTYPE;
+  if (dtype != LAROSA_BF16) return LAROSA_ERR_DTYPE;
+  if (d <= 256 || d > 8192 || d % 8) return LAROSA_ERR_SHAPE;
+  if (!(eps >= 0.f)) return LAROSA_ERR_INVALID_ARG;
+  if (!h || !Qt || !x_rot || (o && !h_out)) return LAROSA_ERR_INVALID_ARG;
+  if (!aligned16(h) || !aligned16(Qt) || !aligned16(x_rot) || !aligned16(o) ||
+      !aligned16(h_out) || !aligned16(a_out))
+    return LAROSA_ERR_ALIGNMENT;
+  const size_t bytes = static_cast<size_t>(d) * 2;
+  auto overlap = [&](const void *p, const void *q) {
+    const char *a = static_cast<const char *>(p), *b = static_cast<const char *>(q);
+    return a && b && a < b + bytes && b < a + bytes;
+  };
+  // the outputs are written while every workgroup still reads h and o
+  const void *outs[2] = {o ? h_out : nullptr, a_out};
+  for (const void *w : outs)
+    if (overlap(w, h) || overlap(w, o)) return LAROSA_ERR_INVALID_ARG;
+  if (overlap(outs[0], a_out)) return LAROSA_ERR_INVALID_ARG;
+  if (int st = device_status()) return st;
+  return launched(launch_norm_rotate(h, o, o ? h_out : nullptr, a_out, Qt, x_rot, d, eps,
+                                     stream_of(stream)));
   });
 }
 

@@ -118,6 +118,114 @@ __global__ __launch_bounds__(kGT) void norm_vec_kernel(T *__restrict__ h, const 
   }
 }
 
+// One token: the RMSNorm above (after the residual add with RESID) folded
+// into the one-token rotation of the normalised row by a dense Q (q_block
+// == d), bf16 only. A 256-thread workgroup first takes the norm exactly as
+// norm_vec_kernel does (thread t owns chunks t, t + 256, ...; the same
+// rounding of the residual sum, the same order of the sum of squares and the
+// same block sum) and lays the normalised row out in LDS as bf16; then each
+// of its 4 waves computes one output channel of x_rot as the one-token
+// rotation does (lane chunks lane + 64·i, the Qt row requested before the
+// norm is taken, the same wave sum). So x_rot, the new residual h_out and the
+// normalised row a_out have the bits of larosa_residual_rmsnorm followed by
+// larosa_rotate. Workgroup 0 writes h_out and a_out; every workgroup reads h
+// and o, so h_out must be another buffer.
+constexpr int kNRWaves = kGW;               // one output channel per wave
+constexpr int kNRMaxChunks = 8192 / 8;      // d <= 8192 (bf16)
+
+// Eight floats, each already a bf16 value, as one 16-byte chunk.
+__device__ __forceinline__ uint4 pack_bf16x8(const float (&f)[8]) {
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    w[e] = static_cast<uint32_t>(f32_to_bf16(f[2 * e])) |
+           (static_cast<uint32_t>(f32_to_bf16(f[2 * e + 1])) << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <int NC, int CPT, bool RESID>
+__global__ __launch_bounds__(kGT) void norm_rotate_row_kernel(
+    const uint16_t *__restrict__ h, const uint16_t *__restrict__ o, uint16_t *__restrict__ h_out,
+    uint16_t *__restrict__ a_out, const uint16_t *__restrict__ qt, float *__restrict__ x_rot,
+    int d, float eps) {
+  constexpr int V = 8;
+  __shared__ float red[kGW];
+  __shared__ uint4 arow[kNRMaxChunks];
+  const int lane = threadIdx.x % kWave;
+  const int j = blockIdx.x * kNRWaves + static_cast<int>(threadIdx.x / kWave);  // < d: d % 4 == 0
+  const uint16_t *row = qt + static_cast<int64_t>(j) * d;
+  const int chunks = d / V;
+  // The residual row first: a wave's loads return in issue order, so the
+  // norm (row from L2) then runs while the Qt row is still on its way.
+  uint4 hq[CPT], oq[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int jj = threadIdx.x + c * kGT;
+    const int jc = jj < chunks ? jj : chunks - 1;
+    hq[c] = load16(h + jc * V);
+    if (RESID) oq[c] = load16(o + jc * V);
+  }
+  // keep those loads ahead of the Qt row's (no memory access moves across)
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  // Every lane issues all NC loads (past the row: its last chunk again), so
+  // no load sits under a branch and the wait before the norm covers the
+  // residual row only.
+  uint4 q[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = lane + kWave * i;
+    q[i] = load16(row + (c < chunks ? c : chunks - 1) * V);
+  }
+  // the norm, as norm_vec_kernel takes it
+  float v[CPT][V];
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int jj = threadIdx.x + c * kGT;
+    Elt<uint16_t>::unpack(hq[c], v[c]);
+    if (RESID) {
+      float ov[V];
+      Elt<uint16_t>::unpack(oq[c], ov);
+#pragma unroll
+      for (int e = 0; e < V; ++e) v[c][e] = Elt<uint16_t>::round(v[c][e] + ov[e]);
+    }
+    if (jj < chunks) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) ss = fmaf(v[c][e], v[c][e], ss);
+      if (RESID && blockIdx.x == 0 && h_out != nullptr)
+        *reinterpret_cast<uint4 *>(h_out + jj * V) = pack_bf16x8(v[c]);
+    }
+  }
+  const float tot = block_sum(ss, red);
+  const float inv = 1.0f / sqrtf(tot / static_cast<float>(d) + eps);
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int jj = threadIdx.x + c * kGT;
+    if (jj < chunks) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) v[c][e] = v[c][e] * inv;
+      const uint4 a = pack_bf16x8(v[c]);  // rounded once, as the norm kernel stores it
+      arow[jj] = a;
+      if (blockIdx.x == 0 && a_out != nullptr) *reinterpret_cast<uint4 *>(a_out + jj * V) = a;
+    }
+  }
+  __syncthreads();
+  // the one-token rotation of the normalised row
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = lane + kWave * i;
+    float af[V], qf[V];
+    Elt<uint16_t>::unpack(c < chunks ? arow[c] : make_uint4(0, 0, 0, 0), af);
+    Elt<uint16_t>::unpack(c < chunks ? q[i] : make_uint4(0, 0, 0, 0), qf);
+#pragma unroll
+    for (int e = 0; e < V; ++e) acc = fmaf(af[e], qf[e], acc);
+  }
+  const float sum = wave_sum(acc);
+  if (lane == 0) x_rot[j] = sum;
+}
+
 // Rotate-half rotary embedding of the q and k heads of one token row:
 // channel i pairs with i + d_head/2, angle pos · theta^(−2i/d_head).
 template <typename T>
@@ -391,6 +499,35 @@ hipError_t launch_rmsnorm(const void *h, void *out, int64_t B, int64_t d, float 
     hipLaunchKernelGGL(rmsnorm_kernel<uint16_t>, dim3(static_cast<unsigned>(B)), dim3(kGT), 0, s,
                        static_cast<const uint16_t *>(h), static_cast<uint16_t *>(out),
                        static_cast<int>(d), eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_rotate(const void *h, const void *o, void *h_out, void *a_out,
+                              const void *qt, float *x_rot, int64_t d, float eps, hipStream_t s) {
+  // d % 8 == 0, 256 < d <= 8192 (host-checked): d / 4 whole workgroups
+  const int chunks = static_cast<int>(d / 8);
+  const int nc = (chunks + kWave - 1) / kWave;
+  const int cpt = (chunks + kGT - 1) / kGT;
+  if (d % 8 || chunks > kNRMaxChunks || nc > 16) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(d / kNRWaves)), block(kGT);
+  const auto *hp = static_cast<const uint16_t *>(h);
+  const auto *op = static_cast<const uint16_t *>(o);
+  auto *hop = static_cast<uint16_t *>(h_out);
+  auto *ap = static_cast<uint16_t *>(a_out);
+  const auto *qp = static_cast<const uint16_t *>(qt);
+  const int di = static_cast<int>(d);
+#define LAROSA_NR(NC, CPT)                                                                         \
+  do {                                                                                             \
+    if (o)                                                                                         \
+      hipLaunchKernelGGL((norm_rotate_row_kernel<NC, CPT, true>), grid, block, 0, s, hp, op, hop,  \
+                         ap, qp, x_rot, di, eps);                                                  \
+    else                                                                                           \
+      hipLaunchKernelGGL((norm_rotate_row_kernel<NC, CPT, false>), grid, block, 0, s, hp, op, hop, \
+                         ap, qp, x_rot, di, eps);                                                  \
+  } while (0)
+  if (nc <= 8 && cpt <= 2) LAROSA_NR(8, 2);
+  else LAROSA_NR(16, 4);
+#undef LAROSA_NR
   return hipGetLastError();
 }
 

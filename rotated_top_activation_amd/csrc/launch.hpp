@@ -312,6 +312,12 @@ hipError_t launch_decode_attention(const void *q, const void *k_new, int64_t k_s
                                    int64_t n_heads, int64_t n_kv, int dt, void *ws,
                                    hipStream_t s);
 hipError_t launch_residual_add(void *h, const void *o, int64_t n, int dt, hipStream_t s);
+// One token, bf16, dense Q (q_block == d <= 8192, d % 8 == 0): x_rot =
+// RMSNorm(h [+ o])·Q with the norm folded into the rotation; with o the
+// rounded residual sum goes to h_out (another buffer); a_out (optional)
+// receives the normalised row.
+hipError_t launch_norm_rotate(const void *h, const void *o, void *h_out, void *a_out,
+                              const void *qt, float *x_rot, int64_t d, float eps, hipStream_t s);
 // h += o (rounded to dt, written back), then out = RMSNorm(h), per token row.
 hipError_t launch_residual_rmsnorm(void *h, const void *o, void *out, int64_t B, int64_t d,
                                    float eps, int dt, hipStream_t s);

@@ -72,10 +72,27 @@ class DecoderBuffers:
         self.dn = torch.empty((B, s.d), **bf)
         n = _lib.larosa_decode_attention_workspace_bytes(B, s.ctx, s.n_heads)
         self.att_ws = torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+        # one token, norms folded into the rotations: the second residual
+        # buffer, a zero row (the residual sum of a first layer) and the two
+        # rotated norm outputs
+        self.h2 = torch.empty((B, s.d), **bf)
+        self.zero = torch.zeros((B, s.d), **bf)
+        self.xr_attn = torch.empty((B, s.d), dtype=torch.float32, device=device)
+        self.xr_mlp = torch.empty((B, s.d), dtype=torch.float32, device=device)
+
+
+def folds_norms(layer: DecoderLayer, B: int, mode: int) -> bool:
+    """Whether layer_forward folds the two RMSNorms (with their residual adds)
+    into the rotations of the q|k|v and gate|up inputs: one token, unfused
+    steps, dense rotations of those inputs (larosa_residual_rmsnorm_rotate)."""
+    s = layer.shape
+    return (B == 1 and mode == _lib.UNFUSED and s.d % 8 == 0 and 256 < s.d <= 8192 and
+            all(layer.lin[r].q_block == s.d for r in ("attn_in", "mlp_in")))
 
 
 def layer_forward(layer: DecoderLayer, h, buf: DecoderBuffers, mode: int = _lib.UNFUSED,
-                  trace: dict | None = None, normed: bool = False, norm_next: bool = False):
+                  trace: dict | None = None, normed: bool = False, norm_next: bool = False,
+                  pending: bool = False, defer: bool = False):
     """One decode step through `layer`, updating h [B, d] in place. `trace`,
     if given, receives the rotated inputs and kept indices of the four
     linears (fp32 / int32 device tensors).
@@ -85,10 +102,22 @@ def layer_forward(layer: DecoderLayer, h, buf: DecoderBuffers, mode: int = _lib.
     also writes RMSNorm of the new h into buf.a, the next layer's first norm,
     in the same launch. A stack of layers runs layer 0 with normed=False and
     every later one with normed=True, every layer but the last with
-    norm_next=True."""
+    norm_next=True.
+
+    Where folds_norms holds (one token, unfused), the two norms run inside
+    the rotations instead, and normed / norm_next are not used: pending says
+    that buf.dn holds the previous layer's down output, still to be added to
+    h (it is added inside the first folded norm); defer leaves this layer's
+    down output in buf.dn for the next layer, so h ends the layer as the
+    residual after attention. A stack runs layer 0 with pending=False and
+    later ones with pending=True, every layer but the last with defer=True.
+    buf.a and buf.m still receive the two norms' outputs."""
     s = layer.shape
     B = h.shape[0]
     ws = layer.workspaces(B, mode)
+    if folds_norms(layer, B, mode):
+        _layer_forward_folded(layer, h, buf, ws, trace, pending, defer)
+        return
 
     def lin(role, x, y):
         L = layer.lin[role]
@@ -139,6 +168,79 @@ def layer_forward(layer: DecoderLayer, h, buf: DecoderBuffers, mode: int = _lib.
         _lib.larosa_residual_rmsnorm(h, buf.dn, buf.a, B, s.d)  # h += dn; the next layer's a
     else:
         _lib.larosa_residual_add(h, buf.dn, B * s.d)
+
+
+def _layer_forward_folded(layer: DecoderLayer, h, buf: DecoderBuffers, ws: dict,
+                          trace: dict | None, pending: bool, defer: bool):
+    """layer_forward for one token with the norms folded into the rotations.
+    The residual moves h -> buf.h2 (the first norm's sum) -> h (the second),
+    since a folded norm cannot write its sum in place."""
+    s = layer.shape
+    B = 1
+    Hd, Kd = s.n_heads * s.d_head, s.n_kv_heads * s.d_head
+    pre = _lib.UNFUSED | _lib.PREROTATED
+
+    def rotated(role, default):
+        L = layer.lin[role]
+        if trace is None:
+            return default, None
+        xr = torch.empty((B, L.d_in), dtype=torch.float32, device=h.device)
+        idx = torch.empty((B, L.k), dtype=torch.int32, device=h.device)
+        trace[role] = (xr, idx)
+        return xr, idx
+
+    # h + dn (or + 0 for a first layer) -> h2; x_rot of RMSNorm(h2)
+    La = layer.lin["attn_in"]
+    xr, idx = rotated("attn_in", buf.xr_attn)
+    _lib.larosa_residual_rmsnorm_rotate(h, buf.dn if pending else buf.zero, buf.h2, La.Qt, xr,
+                                        s.d, a_out=buf.a)
+    if trace is not None:
+        trace["rope_in_qkv"] = True
+    _lib.larosa_qkv_rope_layer_forward(xr, None, La.q_block, La.Wf, B, La.d_in, La.k, s.n_heads,
+                                       s.n_kv_heads, s.d_head, s.ctx, buf.qkv, idx_out=idx,
+                                       mode=pre, ws=ws["attn_in"])
+    q, k = buf.qkv[:, :Hd], buf.qkv[:, Hd:Hd + Kd]
+    _lib.larosa_decode_attention(q, k, s.qkv_out, buf.qkv[:, Hd + Kd:], s.qkv_out,
+                                 layer.k_cache, layer.v_cache, buf.att, B, s.ctx, s.n_heads,
+                                 s.n_kv_heads, s.d_head, ws=buf.att_ws)
+    Lo = layer.lin["o_in"]
+    xr_o = idx_o = None
+    if trace is not None:
+        xr_o, idx_o = rotated("o_in", None)
+    Lo.forward(buf.att, buf.o, ws["o_in"], idx_out=idx_o, xrot_out=xr_o, mode=_lib.UNFUSED)
+    # h2 + o -> h; x_rot of RMSNorm(h)
+    Lm = layer.lin["mlp_in"]
+    xr, idx = rotated("mlp_in", buf.xr_mlp)
+    _lib.larosa_residual_rmsnorm_rotate(buf.h2, buf.o, h, Lm.Qt, xr, s.d, a_out=buf.m)
+    _lib.larosa_swiglu_layer_forward(xr, None, Lm.q_block, layer.w_il, B, Lm.d_in, s.f, Lm.k,
+                                     buf.hh, idx_out=idx, mode=pre, ws=ws["mlp_in"])
+    Ld = layer.lin["down_in"]
+    xr_d = idx_d = None
+    if trace is not None:
+        xr_d, idx_d = rotated("down_in", None)
+    Ld.forward(buf.hh, buf.dn, ws["down_in"], idx_out=idx_d, xrot_out=xr_d, mode=_lib.UNFUSED)
+    if not defer:
+        _lib.larosa_residual_add(h, buf.dn, B * s.d)
+
+
+def decoder_step(layers: list, h, buf: DecoderBuffers, mode: int = _lib.UNFUSED,
+                 traces: list | None = None):
+    """One decode step through a stack of layers, h [B, d] updated in place
+    (the chained norms of layer_forward). traces: one dict per layer, or
+    None."""
+    n = len(layers)
+    if n == 0:
+        return
+    B = h.shape[0]
+    folded = folds_norms(layers[0], B, mode)
+    if not folded:
+        _lib.larosa_rmsnorm(h, buf.a, B, layers[0].shape.d)
+    for i, L in enumerate(layers):
+        tr = traces[i] if traces is not None else None
+        if folded:
+            layer_forward(L, h, buf, mode, trace=tr, pending=i > 0, defer=i < n - 1)
+        else:
+            layer_forward(L, h, buf, mode, trace=tr, normed=True, norm_next=i < n - 1)
 
 
 def upload_base(base: dict, dtype: str = "bf16") -> dict:

@@ -279,3 +279,38 @@ def test_entry_points_are_declared_no_throw():
     decls = re.findall(r"\b(larosa_\w+)\s*\([^;]*\)\s*(LAROSA_NOEXCEPT)?\s*;", text)
     assert decls
     assert all(mark for _, mark in decls), [n for n, mark in decls if not mark]
+
+
+def test_prerotated_flag_rules(lib):
+    """LAROSA_PREROTATED (16): x is x_rot and Qt may be NULL; xrot_out must be
+    NULL and the fp64 rotation flag cannot join it. Valid calls get past
+    every argument check (to the device check, which fails here)."""
+    assert _lf(lib, qt=None) == INVALID                 # a rotating call needs Qt
+    assert _lf(lib, qt=None, mode=16) == NODEV
+    assert _lf(lib, mode=16 | 1) == NODEV               # FUSED runs the unfused steps
+    assert _lf(lib, mode=16, xr=P) == INVALID
+    assert _lf(lib, mode=16 | 2) == INVALID
+    assert _lf(lib, mode=16, k=0) == INVALID
+    assert lib.larosa_workspace_bytes(1, 4096, 22016, 2457, 16) == \
+        lib.larosa_workspace_bytes(1, 4096, 22016, 2457, 0)
+
+
+def test_residual_rmsnorm_rotate_validation(lib):
+    f = lib.larosa_residual_rmsnorm_rotate
+    H, O, HO, A, Q, X = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x60000
+    d = 4096
+    assert f(H, O, HO, A, Q, d, 1e-5, X, 1, None) == NODEV     # every check passed
+    assert f(H, None, None, None, Q, d, 1e-5, X, 1, None) == NODEV
+    assert f(H, O, HO, A, Q, d, 1e-5, X, 0, None) == DTYPE      # bf16 only
+    assert f(H, O, HO, A, Q, 256, 1e-5, X, 1, None) == SHAPE
+    assert f(H, O, HO, A, Q, 8200, 1e-5, X, 1, None) == SHAPE
+    assert f(H, O, HO, A, Q, 4100, 1e-5, X, 1, None) == SHAPE   # d % 8
+    assert f(H, O, None, A, Q, d, 1e-5, X, 1, None) == INVALID  # o needs h_out
+    assert f(H, O, H, A, Q, d, 1e-5, X, 1, None) == INVALID     # not in place
+    assert f(H, O, H + 4096, A, Q, d, 1e-5, X, 1, None) == INVALID   # overlaps h
+    assert f(H, O, HO, O, Q, d, 1e-5, X, 1, None) == INVALID    # a_out overlaps o
+    assert f(H, O, HO, HO, Q, d, 1e-5, X, 1, None) == INVALID   # a_out overlaps h_out
+    assert f(None, O, HO, A, Q, d, 1e-5, X, 1, None) == INVALID
+    assert f(H, O, HO, A, None, d, 1e-5, X, 1, None) == INVALID
+    assert f(H, O, HO, A, Q, d, -1.0, X, 1, None) == INVALID
+    assert f(H + 8, O, HO, A, Q, d, 1e-5, X, 1, None) == ALIGN

@@ -119,13 +119,145 @@ def test_decode_attention(B, H, Hkv, T):
     out = torch.empty((B, H * dh), dtype=torch.bfloat16, device="cuda")
     kc_d = dev(kc.reshape(-1), "bf16") if T else torch.empty(8, dtype=torch.bfloat16, device="cuda")
     vc_d = dev(vc.reshape(-1), "bf16") if T else torch.empty(8, dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(_lib.larosa_decode_attention_workspace_bytes(B, T, H), dtype=torch.uint8,
+    ws = torch.zeros(_lib.larosa_decode_attention_workspace_bytes(B, T, H), dtype=torch.uint8,
                      device="cuda")
-    _lib.larosa_decode_attention(dev(q, "bf16"), dev(kn, "bf16"), Hkv * dh, dev(vn, "bf16"),
-                                 Hkv * dh, kc_d, vc_d, out, B, T, H, Hkv, dh, ws=ws)
+    args = (dev(q, "bf16"), dev(kn, "bf16"), Hkv * dh, dev(vn, "bf16"), Hkv * dh, kc_d, vc_d)
+    _lib.larosa_decode_attention(*args, out, B, T, H, Hkv, dh, ws=ws)
     torch.cuda.synchronize()
     want = dec.decode_attention(q, kn, vn, kc, vc, H, Hkv, dh)
     assert ref.rel_error(host(out), want) <= TOL
+    # the chunks are combined in chunk order: a second call gives the same bits
+    out2 = torch.empty_like(out)
+    _lib.larosa_decode_attention(*args, out2, B, T, H, Hkv, dh, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+
+
+def test_decode_attention_workspace_reused_across_shapes():
+    """One workspace serves calls of changing context length, batch and head
+    count in a row."""
+    dh = 128
+    ws = torch.empty(_lib.larosa_decode_attention_workspace_bytes(4, 2048, 32), dtype=torch.uint8,
+                     device="cuda")
+    for B, H, Hkv, T in [(2, 32, 8, 2048), (2, 32, 8, 100), (2, 32, 8, 0), (2, 32, 8, 1500),
+                         (4, 32, 32, 2000), (1, 8, 8, 300)]:
+        rng = np.random.default_rng(7 * T + H + B)
+        q = wl.quantize(rng.standard_normal((B, H * dh)), "bf16")
+        kn = wl.quantize(rng.standard_normal((B, Hkv * dh)), "bf16")
+        vn = wl.quantize(rng.standard_normal((B, Hkv * dh)), "bf16")
+        kc = wl.quantize(rng.standard_normal((B, Hkv, T, dh)), "bf16")
+        vc = wl.quantize(rng.standard_normal((B, Hkv, T, dh)), "bf16")
+        out = torch.empty((B, H * dh), dtype=torch.bfloat16, device="cuda")
+        kc_d = dev(kc.reshape(-1), "bf16") if T else torch.empty(8, dtype=torch.bfloat16,
+                                                                  device="cuda")
+        vc_d = dev(vc.reshape(-1), "bf16") if T else torch.empty(8, dtype=torch.bfloat16,
+                                                                  device="cuda")
+        _lib.larosa_decode_attention(dev(q, "bf16"), dev(kn, "bf16"), Hkv * dh, dev(vn, "bf16"),
+                                     Hkv * dh, kc_d, vc_d, out, B, T, H, Hkv, dh, ws=ws)
+        torch.cuda.synchronize()
+        want = dec.decode_attention(q, kn, vn, kc, vc, H, Hkv, dh)
+        assert ref.rel_error(host(out), want) <= TOL, (B, H, Hkv, T)
+
+
+def _rand_qt(d, seed):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    return (torch.randn((d, d), generator=g, device="cuda") / d ** 0.5).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("d,resid", [(4096, True), (4096, False), (5120, True), (520, True),
+                                     (8192, True), (264, False)])
+def test_residual_rmsnorm_rotate_equals_the_two_steps(d, resid):
+    """The norm folded into the one-token rotation gives the bits of the
+    residual add + RMSNorm launch followed by the rotation launch: the new
+    residual, the normalised row and x_rot."""
+    rng = np.random.default_rng(d + resid)
+    h = dev(wl.quantize(rng.standard_normal((1, d)) * 3, "bf16"), "bf16")
+    o = dev(wl.quantize(rng.standard_normal((1, d)), "bf16"), "bf16")
+    qt = _rand_qt(d, d)
+    h1, a1 = h.clone(), torch.empty_like(h)
+    xr1 = torch.empty((1, d), dtype=torch.float32, device="cuda")
+    if resid:
+        _lib.larosa_residual_rmsnorm(h1, o, a1, 1, d)
+    else:
+        _lib.larosa_rmsnorm(h1, a1, 1, d)
+    _lib.larosa_rotate(a1, qt, d, xr1, 1, d)
+    h2, a2 = torch.full_like(h, 7.0), torch.empty_like(h)
+    xr2 = torch.empty_like(xr1)
+    _lib.larosa_residual_rmsnorm_rotate(h, o if resid else None, h2 if resid else None, qt, xr2,
+                                        d, a_out=a2)
+    torch.cuda.synchronize()
+    assert torch.equal(a2, a1)
+    assert torch.equal(xr2, xr1)
+    if resid:
+        assert torch.equal(h2, h1)
+    else:
+        assert bool((h2 == 7.0).all())  # no residual sum without o
+    # and against the oracle: the norm within one bf16 spacing, x_rot in its bound
+    want_a = dec.rmsnorm(host(h1))
+    assert close_bf16(host(a2), want_a, extra=1e-6)
+
+
+def test_residual_rmsnorm_rotate_rejects_in_place_and_bad_sizes():
+    d = 4096
+    h = torch.zeros((1, d), dtype=torch.bfloat16, device="cuda")
+    o = torch.zeros_like(h)
+    qt = torch.zeros((d, d), dtype=torch.bfloat16, device="cuda")
+    xr = torch.empty((1, d), dtype=torch.float32, device="cuda")
+    for args, code in [((h, o, h, qt, xr, d), 1), ((h, o, o, qt, xr, d), 1),
+                       ((h, o, None, qt, xr, d), 1), ((h, o, torch.empty_like(h), qt, xr, 256), 2),
+                       ((h, o, torch.empty_like(h), qt, xr, 8200), 2)]:
+        with pytest.raises(_lib.LarosaError) as err:
+            _lib.larosa_residual_rmsnorm_rotate(*args)
+        assert err.value.status == code
+
+
+@pytest.mark.parametrize("B", [1, 4, 16])
+def test_prerotated_layer_calls_equal_the_rotating_calls(B):
+    """LAROSA_PREROTATED: the layer calls given x_rot give the bits of the
+    calls that rotate x themselves (plain, SwiGLU-folded and RoPE-folded)."""
+    shape = wl.LLAMA7B
+    d, f = shape.d, 1024
+    case = wl.LinearCase(cfg=3, batch=B, d_in=d, d_out=2 * f, q_block=d, sparsity_pct=40,
+                         dtype="bf16")
+    x, q, w = wl.linear_case_inputs(case, w_std=0.02)
+    lin = RotatedLinear(q, w, "bf16", case.k)
+    x_d = wl.to_torch(x, "bf16")
+    xr = torch.empty((B, d), dtype=torch.float32, device="cuda")
+    ws = lin.workspace(B)
+    pre = _lib.UNFUSED | _lib.PREROTATED
+    y1 = torch.empty((B, 2 * f), dtype=torch.bfloat16, device="cuda")
+    y2 = torch.empty_like(y1)
+    i1 = torch.empty((B, case.k), dtype=torch.int32, device="cuda")
+    i2 = torch.empty_like(i1)
+    lin.forward(x_d, y1, ws, idx_out=i1, xrot_out=xr)
+    lin.forward(xr, y2, ws, idx_out=i2, mode=pre)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2) and torch.equal(y1, y2)
+    # SwiGLU folded (interleaved gate|up)
+    w_il = torch.empty_like(lin.Wf)
+    _lib.larosa_interleave_gate_up(lin.Wf, w_il, d, f)
+    n = _lib.larosa_swiglu_workspace_bytes(B, d, f, case.k, _lib.UNFUSED)
+    sws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    _lib.larosa_workspace_init(sws)
+    h1 = torch.empty((B, f), dtype=torch.bfloat16, device="cuda")
+    h2 = torch.empty_like(h1)
+    _lib.larosa_swiglu_layer_forward(x_d, lin.Qt, d, w_il, B, d, f, case.k, h1, ws=sws)
+    _lib.larosa_swiglu_layer_forward(xr, None, d, w_il, B, d, f, case.k, h2, mode=pre, ws=sws)
+    torch.cuda.synchronize()
+    assert torch.equal(h1, h2)
+    # RoPE folded: 2 f columns as 16 heads of 128
+    H, Hkv = 8, 4
+    _lib.larosa_qkv_rope_layer_forward(x_d, lin.Qt, d, lin.Wf, B, d, case.k, H, Hkv, 128, 2048,
+                                       y1, ws=ws)
+    _lib.larosa_qkv_rope_layer_forward(xr, None, d, lin.Wf, B, d, case.k, H, Hkv, 128, 2048, y2,
+                                       mode=pre, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    # the flag's argument rules
+    with pytest.raises(RuntimeError):
+        lin.forward(xr, y2, ws, xrot_out=xr, mode=pre)
+    with pytest.raises(RuntimeError):
+        lin.forward(xr, y2, ws, mode=pre | _lib.ROTATE_FP64)
 
 
 @pytest.mark.parametrize("B,d", [(1, 4096), (16, 4096), (3, 520), (2, 5120), (1, 8192)])
@@ -230,18 +362,30 @@ def run_decoder(B, sparsity, n_layers, mode, n_checked=None, seed_cols=0, check_
     buf = D.DecoderBuffers(shape, B)
     rng = np.random.default_rng(seed_cols)
     checked = 0
-    # the chained form: layer l's closing residual add also writes the next
-    # layer's first RMSNorm (one launch); the first layer's norm runs here
-    _lib.larosa_rmsnorm(h, buf.a, B, shape.d)
+    folded = None
     for l in range(n_layers):
         layer, idxs, offs = D.build_layer(cfg, l, shape, base_dev, kv_dev, B, sparsity)
+        if folded is None:
+            # one token, unfused: the norms run inside the rotations, and each
+            # layer's down output is added to h by the next layer's first
+            # folded norm. Otherwise the chained form: layer l's closing
+            # residual add also writes the next layer's first RMSNorm (one
+            # launch); the first layer's norm runs here.
+            folded = D.folds_norms(layer, B, mode)
+            if not folded:
+                _lib.larosa_rmsnorm(h, buf.a, B, shape.d)
         torch.cuda.synchronize()
         h_in = host(h)
-        a = host(buf.a)
+        if folded and l > 0:  # the previous layer's down output, still pending
+            h_in = dec.residual_add(h_in, host(buf.dn))
+        a = None if folded else host(buf.a)
         trace = {}
-        D.layer_forward(layer, h, buf, mode=mode, trace=trace, normed=True,
-                        norm_next=l < n_layers - 1)
+        last = l == n_layers - 1
+        D.layer_forward(layer, h, buf, mode=mode, trace=trace, normed=True, norm_next=not last,
+                        pending=l > 0, defer=not last)
         torch.cuda.synchronize()
+        if folded:
+            a = host(buf.a)  # written by the layer's first folded norm
         skip = (n_checked is not None and checked >= n_checked) or \
             (l % check_every != 0 and l != n_layers - 1)
         if skip:
@@ -290,8 +434,11 @@ def run_decoder(B, sparsity, n_layers, mode, n_checked=None, seed_cols=0, check_
         assert ref.rel_error(att, want_att) <= TOL, f"layer {l} attention"
         h_mid = dec.residual_add(h_in, o)
         assert close_bf16(m, dec.rmsnorm(h_mid), extra=1e-6), f"layer {l} residual/rmsnorm"
-        np.testing.assert_array_equal(h_out, dec.residual_add(h_mid, dn))
-        if l < n_layers - 1:  # the next layer's norm, written by the closing add
+        if folded and not last:  # dn is added by the next layer
+            np.testing.assert_array_equal(h_out, h_mid)
+        else:
+            np.testing.assert_array_equal(h_out, dec.residual_add(h_mid, dn))
+        if l < n_layers - 1 and not folded:  # the next layer's norm, written by the closing add
             assert close_bf16(host(buf.a), dec.rmsnorm(h_out), extra=1e-6), f"layer {l} next norm"
         del layer
     assert np.all(np.isfinite(host(h)))
