@@ -490,3 +490,40 @@ def test_batched_selection_adds_the_rotation_parts_in_order(B, d, qb, n):
     assert ok_y() and ok_i() and ok_x()
     assert torch.equal(xr, xr_t)
     np.testing.assert_array_equal(host(idx), ref.select(host_f32(xr), case.k))
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("B", [1, 2, 3, 8, 16, 33, 64])
+def test_exact_arithmetic_end_to_end(B, dt, mode):
+    """Signed-permutation rotations with small-integer x and W make every step
+    exact: x_rot = x·Q is a signed permutation of x, the fold only permutes and
+    negates W's rows, and every partial sum of the product is an integer below
+    2^24, so no summation order can change it. The kept index sets are then
+    the oracle's on its own x_rot (end to end, not teacher-forced; the
+    integer magnitudes tie heavily at the K-th key, so the lowest-index rule
+    decides), and y is the oracle's exact product rounded to the output type,
+    bit for bit, through the one-token, vector and matrix-core paths and the
+    one-launch form."""
+    d, qb, n, k = 1024, 256, 1544, 410
+    rng = np.random.default_rng(1000 * B + (dt == "f32"))
+    q = np.zeros((d // qb, qb, qb))
+    for c in range(d // qb):
+        perm, sign = wl.signed_permutation(rng, qb)
+        q[c, np.arange(qb), perm] = sign
+    x = rng.integers(-8, 9, (B, d)).astype(np.float64)
+    w = rng.integers(-4, 5, (d, n)).astype(np.float64)
+    lin = RotatedLinear(q, w, dt, k)
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    y, ok_y = guarded((B, n), tdt)
+    idx, ok_i = guarded((B, k), torch.int32, fill=-3)
+    xr, ok_x = guarded((B, d), torch.float32)
+    lin.forward(dev(x, dt), y, lin.workspace(B, mode), idx_out=idx, xrot_out=xr, mode=mode)
+    torch.cuda.synchronize()
+    assert ok_y() and ok_i() and ok_x()
+    want_y, want_xr, want_idx = ref.linear(x, q, ref.fold(q, w, dt), k, dt)
+    np.testing.assert_array_equal(host_f32(xr), want_xr.astype(np.float32))
+    np.testing.assert_array_equal(host(idx), want_idx)
+    np.testing.assert_array_equal(host(y), want_y)
+    key = np.abs(want_xr[0])
+    assert np.sum(key == np.sort(key)[::-1][k - 1]) > 1  # the K-th key is tied
