@@ -637,9 +637,12 @@ int larosa_rotate(const void *x, int x_dtype, const void *Qt, int64_t q_block, i
   if (!aligned16(x) || !aligned16(Qt) || !aligned16(x_rot)) return LAROSA_ERR_ALIGNMENT;
   if (int st = device_status()) return st;
   // Without a workspace the matrix-core form runs unsplit over each block;
-  // up to 4 tokens over blocks of 4096 or more the vector forms are faster
-  // (d = 4096: 11.0 / 14.4 µs at 2 / 4 tokens against 26.6 µs).
-  if (!(B <= 4 && q_block >= 4096) && mfma_supported(B, x_dtype, q_dtype) && q_block % 32 == 0)
+  // up to 4 tokens over blocks of 4096 or more, and up to 8 over blocks of
+  // 4096 (which the few-token kernel takes in one pass), the vector forms are
+  // faster (d = 4096: 11.0 / 14.4 / 23.7 µs at 2 / 4 / 8 tokens against
+  // 26.6 µs).
+  const bool vec = (B <= 4 && q_block >= 4096) || (B <= 8 && q_block == 4096);
+  if (!vec && mfma_supported(B, x_dtype, q_dtype) && q_block % 32 == 0)
     return launched(launch_rotate_mfma(x, Qt, x_rot, static_cast<int>(B), static_cast<int>(d),
                                        static_cast<int>(q_block), nullptr, stream_of(stream)));
   return launched(launch_rotate(x, x_dtype, Qt, q_dtype, x_rot, static_cast<int>(B),

@@ -117,10 +117,11 @@ ROTATE_CASES = [
     ("f32", "f32", 512, 512, 1), ("bf16", "bf16", 4096, 4096, 1),
     ("bf16", "bf16", 11008, 2752, 1), ("bf16", "bf16", 1024, 256, 5),
     ("f32", "bf16", 768, 768, 2), ("bf16", "f32", 256, 64, 3), ("bf16", "bf16", 13824, 3456, 8),
-    # 2 to 4 tokens over blocks of 4096 or more, and fp32 batches: the
+    # 2 to 8 tokens over blocks of 4096 or more, and fp32 batches: the
     # one-wave-per-channel form with the tokens' x staged in LDS
     ("bf16", "bf16", 4096, 4096, 2), ("bf16", "bf16", 4096, 4096, 3),
     ("bf16", "bf16", 5120, 5120, 4), ("f32", "f32", 512, 512, 4), ("f32", "f32", 2048, 1024, 7),
+    ("bf16", "bf16", 4096, 4096, 8), ("bf16", "bf16", 8192, 8192, 6),
     # batches of 16 and more in bf16 take the matrix-core form
     ("bf16", "bf16", 4096, 4096, 16), ("bf16", "bf16", 11008, 2752, 33),
     ("bf16", "bf16", 8192, 8192, 64), ("bf16", "bf16", 1152, 96, 17),
@@ -149,7 +150,7 @@ def test_rotate_within_rigorous_bound(xdt, qdt, d, qb, B):
 
 
 @pytest.mark.parametrize("dt,d,qb,B", [("bf16", 4096, 4096, 3), ("f32", 1024, 1024, 4),
-                                        ("f32", 2048, 512, 7)])
+                                        ("f32", 2048, 512, 7), ("bf16", 4096, 4096, 8)])
 def test_batched_rotation_is_batch_invariant(dt, d, qb, B):
     """The few-token form sums each token in the one-token kernel's order:
     every token's x_rot equals its own one-token call bit for bit."""
