@@ -209,6 +209,25 @@ def main():
     chain_ms = timed(lambda i: step(i, _lib.CHAIN), a.steps, a.warmup) \
         if a.kernel_only == "" else None
 
+    def per_step_us(fn, steps):
+        # an event pair around every step (the steps still run back to back):
+        # the spread of single-step device times
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for i, (s0, s1) in enumerate(evs):
+            s0.record(stream)
+            fn(i)
+            s1.record(stream)
+        torch.cuda.synchronize()
+        t = sorted(s0.elapsed_time(s1) * 1e3 for s0, s1 in evs)
+
+        def pct(p):
+            return round(t[min(len(t) - 1, int(round(p / 100 * (len(t) - 1))))], 2)
+        return {"median": pct(50), "p10": pct(10), "p90": pct(90), "steps": steps}
+
+    step_dist = {name: per_step_us(lambda i, m=modes[name]: step(i, m), max(a.steps, 100))
+                 for name in eager_ms} if a.kernel_only == "" else {}
+
     # The dominant kernels alone, gate|up (the larger linear): the one-token
     # selection folded into the product (unfused mode), the fused
     # rotate-select-gather, and for reference the product over a given row list.
@@ -418,6 +437,7 @@ def main():
             "chain_step_ms_eager": round(chain_ms, 5) if chain_ms else None,
             "eager_step_ms": {k: round(v, 5) for k, v in eager_ms.items()},
             "graph_step_ms": {k: round(v, 5) for k, v in graph_ms.items()},
+            "eager_step_us_per_step_events": step_dist,
             "mlp_sparse_bytes": sparse_bytes,
             "mlp_dense_weight_bytes": dense_mlp_bytes,
             "mlp_achieved_GBs": round(sparse_bytes / (ms * 1e-3) / 1e9, 1),
