@@ -252,9 +252,9 @@ def larosa_layer_forward(x, Qt, q_block: int, W_folded, B: int, d_in: int, d_out
                          y, idx_out=None, xrot_out=None, mode: int = UNFUSED, ws=None,
                          stream=None) -> None:
     _check("larosa_layer_forward",
-           load().larosa_layer_forward(_ptr(x), _act_dt(x, y, mode), _ptr(Qt), q_block, _ptr(W_folded),
-                                       _dt(W_folded), B, d_in, d_out, k, _ptr(y), _ptr(idx_out),
-                                       _ptr(xrot_out), mode, _ptr(ws), _nbytes(ws),
+           load().larosa_layer_forward(_ptr(x), _act_dt(x, y, mode), _ptr(Qt), q_block,
+                                       _ptr(W_folded), _dt(W_folded), B, d_in, d_out, k, _ptr(y),
+                                       _ptr(idx_out), _ptr(xrot_out), mode, _ptr(ws), _nbytes(ws),
                                        _stream(stream)))
 
 
@@ -292,10 +292,10 @@ def larosa_swiglu_layer_forward(x, Qt, q_block: int, W_il, B: int, d_in: int, f:
                                 h, idx_out=None, xrot_out=None, mode: int = UNFUSED, ws=None,
                                 stream=None) -> None:
     _check("larosa_swiglu_layer_forward",
-           load().larosa_swiglu_layer_forward(_ptr(x), _act_dt(x, h, mode), _ptr(Qt), q_block, _ptr(W_il),
-                                              _dt(W_il), B, d_in, f, k, _ptr(h), _ptr(idx_out),
-                                              _ptr(xrot_out), mode, _ptr(ws), _nbytes(ws),
-                                              _stream(stream)))
+           load().larosa_swiglu_layer_forward(_ptr(x), _act_dt(x, h, mode), _ptr(Qt), q_block,
+                                              _ptr(W_il), _dt(W_il), B, d_in, f, k, _ptr(h),
+                                              _ptr(idx_out), _ptr(xrot_out), mode, _ptr(ws),
+                                              _nbytes(ws), _stream(stream)))
 
 
 def larosa_calibrate_workspace_bytes() -> int:
