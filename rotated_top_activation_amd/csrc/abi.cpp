@@ -1168,7 +1168,7 @@ int larosa_qkv_rope_layer_forward(const void *x, int act_dtype, const void *Qt, 
   r.rot_cols = static_cast<int>((n_heads + n_kv_heads) * d_head);
   r.tab = rope_table(d_head, static_cast<double>(pos), static_cast<double>(theta));
   // folded only where whole heads fill the one-token product's column tiles
-  // (512 columns, or 256 for outputs of at most 8192 columns)
+  // (512 columns, or 256 for outputs of at most 12288 columns)
   const SelectGatherPlan sgp = plan_select_gather(d_in, d_out, w_dtype);
   const bool foldable = (static_cast<int64_t>(sgp.lpr) * 8) % d_head == 0;
   Sel sel;

@@ -20,12 +20,14 @@
 // last-arriving workgroup, as in the standalone product.
 //
 // Narrow tiles (LPR = 32: 256 bf16 columns, one 512-byte segment per row)
-// serve outputs of at most 8192 columns: 4096 columns then make 16 tiles of
+// serve outputs of at most 12288 columns: 4096 columns then make 16 tiles of
 // 16 channel ranges instead of 8 tiles of 32, so a tile's split reduction
 // adds 16 partial sums instead of 32 and each workgroup hands over 256 of
 // them instead of 512 (11008 → 4096 down product: 20.4 against 21.1 µs;
-// 128-column tiles measured 21.7). Wide outputs keep 512-column tiles,
-// which stream faster there. With the SwiGLU epilogue a narrow tile takes
+// 128-column tiles measured 21.7); the 7B q|k|v product (12288 columns)
+// takes 48 tiles of 5 ranges instead of 24 of 10 (the 32-layer decoder step
+// 4280 against 4306 µs). Wider outputs keep 512-column tiles, which stream
+// faster there. With the SwiGLU epilogue a narrow tile takes
 // 128 gate and the matching 128 up columns of the interleaved layout, so it
 // still finishes whole channels of h.
 //
@@ -655,8 +657,8 @@ hipError_t launch_sg_t(const SelectGatherArgs &a, const SelectGatherPlan &p, hip
 
 SelectGatherPlan plan_select_gather(int64_t d_in, int64_t d_out, int w_dt) {
   SelectGatherPlan p;
-  // narrow tiles (256 columns) for bf16 outputs of at most 8192 columns
-  p.lpr = w_dt == kBF16 && d_out <= 8192 ? 32 : kWave;
+  // narrow tiles (256 columns) for bf16 outputs of at most 12288 columns
+  p.lpr = w_dt == kBF16 && d_out <= 12288 ? 32 : kWave;
   const int64_t tile_cols = static_cast<int64_t>(p.lpr) * (w_dt == kF32 ? 4 : 8);
   p.tiles = static_cast<int>((d_out + tile_cols - 1) / tile_cols);
   int64_t splits = 256 / p.tiles;                          // one workgroup per CU
