@@ -311,8 +311,9 @@ int larosa_layer_forward(const void *x, int act_dtype, const void *Qt,
  * more than 16 MiB (larosa_workspace_bytes of the sizes) return
  * LAROSA_ERR_WORKSPACE before any work; mode must be LAROSA_UNFUSED,
  * optionally with LAROSA_ROTATE_FP64 or LAROSA_VALIDATE
- * (LAROSA_ERR_INVALID_ARG otherwise: the one-launch form reports through a
- * workspace the caller could not read). The array is zero-filled on the
+ * (LAROSA_ERR_INVALID_ARG otherwise, LAROSA_PREROTATED included: the
+ * one-launch form reports through a workspace the caller could not read).
+ * The array is zero-filled on the
  * first call on a device and again whenever the sizes, mode or types differ
  * from the previous call's on that device (a fill kernel on `stream`).
  * Every call on one GPU shares its array: calls that overlap on one GPU

@@ -1009,8 +1009,9 @@ int larosa_layer_forward_noalloc(const void *x, int act_dtype, const void *Qt, i
                                  float *xrot_out, int mode, larosa_stream_t stream) LAROSA_NOEXCEPT {
   return guard([&]() -> int {
   // The one-launch form reports its bounded waits through the workspace,
-  // which this caller cannot read: only the unfused steps run here.
-  if (base_mode(mode) != LAROSA_UNFUSED) return LAROSA_ERR_INVALID_ARG;
+  // which this caller cannot read: only the unfused steps run here, on x
+  // itself (the modes the declaration lists).
+  if (base_mode(mode) != LAROSA_UNFUSED || prerotated(mode)) return LAROSA_ERR_INVALID_ARG;
   Sel sel;
   sel.k = k;
   const size_t need = larosa_workspace_bytes(B, d_in, d_out, k, mode);

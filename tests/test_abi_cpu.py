@@ -293,6 +293,10 @@ def test_prerotated_flag_rules(lib):
     assert _lf(lib, mode=16, k=0) == INVALID
     assert lib.larosa_workspace_bytes(1, 4096, 22016, 2457, 16) == \
         lib.larosa_workspace_bytes(1, 4096, 22016, 2457, 0)
+    # the no-alloc call runs on x itself only
+    na = lib.larosa_layer_forward_noalloc
+    assert na(P, 1, P, 64, P, 1, 1, 128, 64, 32, P, None, None, 16, None) == INVALID
+    assert na(P, 1, P, 64, P, 1, 1, 128, 64, 32, P, None, None, 0, None) == NODEV
 
 
 def test_residual_rmsnorm_rotate_validation(lib):
