@@ -1369,16 +1369,20 @@ int larosa_residual_rmsnorm_rotate(const void *h, const void *o, void *h_out, vo
   if (!aligned16(h) || !aligned16(Qt) || !aligned16(x_rot) || !aligned16(o) ||
       !aligned16(h_out) || !aligned16(a_out))
     return LAROSA_ERR_ALIGNMENT;
-  const size_t bytes = static_cast<size_t>(d) * 2;
-  auto overlap = [&](const void *p, const void *q) {
+  const size_t bytes = static_cast<size_t>(d) * 2;  // a bf16 row; x_rot is twice that
+  auto overlap = [&](const void *p, size_t pn, const void *q, size_t qn) {
     const char *a = static_cast<const char *>(p), *b = static_cast<const char *>(q);
-    return a && b && a < b + bytes && b < a + bytes;
+    return a && b && a < b + qn && b < a + pn;
   };
   // the outputs are written while every workgroup still reads h and o
   const void *outs[2] = {o ? h_out : nullptr, a_out};
   for (const void *w : outs)
-    if (overlap(w, h) || overlap(w, o)) return LAROSA_ERR_INVALID_ARG;
-  if (overlap(outs[0], a_out)) return LAROSA_ERR_INVALID_ARG;
+    if (overlap(w, bytes, h, bytes) || overlap(w, bytes, o, bytes) ||
+        overlap(w, bytes, x_rot, 2 * bytes))
+      return LAROSA_ERR_INVALID_ARG;
+  if (overlap(outs[0], bytes, a_out, bytes) || overlap(x_rot, 2 * bytes, h, bytes) ||
+      overlap(x_rot, 2 * bytes, o, bytes))
+    return LAROSA_ERR_INVALID_ARG;
   if (int st = device_status()) return st;
   return launched(launch_norm_rotate(h, o, o ? h_out : nullptr, a_out, Qt, x_rot, d, eps,
                                      stream_of(stream)));

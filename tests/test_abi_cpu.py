@@ -318,3 +318,7 @@ def test_residual_rmsnorm_rotate_validation(lib):
     assert f(H, O, HO, A, None, d, 1e-5, X, 1, None) == INVALID
     assert f(H, O, HO, A, Q, d, -1.0, X, 1, None) == INVALID
     assert f(H + 8, O, HO, A, Q, d, 1e-5, X, 1, None) == ALIGN
+    assert f(H, O, HO, A, Q, d, 1e-5, H + 4096, 1, None) == INVALID  # x_rot overlaps h
+    assert f(H, O, HO, A, Q, d, 1e-5, O - 8192, 1, None) == INVALID  # x_rot (fp32) reaches o
+    assert f(H, O, HO, A, Q, d, 1e-5, A - 16384, 1, None) == NODEV   # x_rot ends where a_out starts
+    assert f(H, O, HO, A, Q, d, 1e-5, A - 16368, 1, None) == INVALID  # ... and one chunk more
