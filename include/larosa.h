@@ -584,6 +584,8 @@ int larosa_residual_rmsnorm(void *h, const void *o, void *out, int64_t B, int64_
  * NULL) followed by larosa_rotate. With o, the residual sum v is written to
  * h_out, which must not overlap h or o (every workgroup reads h and o whole,
  * so the sum cannot be written in place); a_out, if not NULL, receives a.
+ * No output (h_out, a_out, x_rot) may overlap h, o or another output
+ * (LAROSA_ERR_INVALID_ARG).
  * Qt: the prepared rotation of a dense Q, [d, d] (q_block == d). bf16 only
  * (LAROSA_ERR_DTYPE otherwise); d a multiple of 8 above 256 and at most
  * 8192 (the sizes whose one-token rotation takes one wave per channel;
